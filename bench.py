@@ -1,0 +1,218 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention forward on one MI355X.
+
+One step = one full forward over one batch of resident synthetic inputs:
+block_pool -> coarse_score (+ topk_select, per panel chunk) -> sparse_flash_fwd.
+Prints ONE JSON line: forward tokens/s (batch * n / step time), effective
+TFLOP/s, the roofline of the dominant kernel (timed with HIP events on the
+launch stream inside this run) and the fp64 CPU oracle's throughput on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+METRIC = "fwd tokens/s and effective TFLOP/s at N=32k,H=8,D=64,B=64,k=16; % roofline"
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
+KERNEL_SOURCES = {
+    "block_pool": "block_pool.hip",
+    "coarse_score": "coarse_score.hip",
+    "topk_select": "topk_select.hip",
+    "sparse_flash_fwd": "sparse_flash_fwd.hip",
+}
+
+
+def visible_pairs(w: W.Workload) -> int:
+    """Closed form of the (query, key) pairs the fine stage visits."""
+    nb = w.nb
+    if not w.causal:
+        return w.bh * w.n * min(w.topk, nb) * w.block
+    i = np.arange(w.n, dtype=np.int64)
+    qb = i // w.block
+    keff = np.minimum(w.topk, qb + 1)
+    return int(w.bh * ((keff - 1) * w.block + (i % w.block) + 1).sum())
+
+
+def candidate_pairs(w: W.Workload) -> int:
+    if not w.causal:
+        return w.bh * w.n * w.nb
+    i = np.arange(w.n, dtype=np.int64)
+    return int(w.bh * (i // w.block + 1).sum())
+
+
+def stage_work(w: W.Workload):
+    """Algorithmic work per launch of each kernel over the whole problem:
+    (bound, flops, bytes).  Bytes count each compulsory read/write once."""
+    s = 2 if w.dtype == "bf16" else 4
+    qkv = w.bh * w.n * w.d * s
+    repr_b = w.bh * w.nb * w.d * 4
+    cand = candidate_pairs(w)
+    panel = cand * 4
+    idx = w.bh * w.n * w.topk * 4
+    fine_flops = 4 * w.d * visible_pairs(w)
+    return {
+        "block_pool": ("hbm", 0, qkv + repr_b),
+        "coarse_score": ("hbm", 2 * w.d * cand, qkv + repr_b + panel),
+        "topk_select": ("hbm", 0, panel + idx),
+        "sparse_flash_fwd": ("mfma", fine_flops, 3 * qkv + w.bh * w.n * w.d * 4 + idx),
+    }
+
+
+def source_sha(kernel: str) -> str:
+    p = os.path.join(ROOT, "content_dependent_block_amd", "csrc", KERNEL_SOURCES[kernel])
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        c = json.load(f)
+    if c.get("source_sha") != source_sha(kernel):
+        return None
+    return c.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w: W.Workload, inp, positions: int):
+    import oracle
+    n_pos = min(positions, w.n)
+    pos = np.linspace(0, w.n - 1, n_pos).astype(np.int64)
+    rows = (np.arange(w.bh, dtype=np.int64)[:, None] * w.n + pos[None, :]).ravel()
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    t0 = time.perf_counter()
+    oracle.forward(inp.q, inp.k, inp.v, w.block, w.topk, w.causal, w.scale, rows)
+    dt = time.perf_counter() - t0
+    return {"value": n_pos * w.batch / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_pos} of {w.n} query positions (evenly spaced) x all {w.bh} heads; "
+                      f"pool + coarse scores + top-k + two-pass softmax attention in fp64; "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-positions", type=int, default=16384)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
+              "(heads shard with no communication; see the sharding notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import content_dependent_block_amd as m
+
+    w = W.WORKLOADS[args.workload]
+    if w.static:
+        raise SystemExit("bench.py times the dynamic two-stage forward; pick a dynamic workload")
+    inp = W.generate(w)
+    dev = torch.device("cuda:0")
+    if w.dtype == "bf16":
+        q, k, v = (torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+                   for b in (inp.q_bits, inp.k_bits, inp.v_bits))
+    else:
+        q, k, v = (torch.from_numpy(x).to(dev) for x in (inp.q, inp.k, inp.v))
+    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    idx = torch.empty(q.shape[:3] + (w.topk,), dtype=torch.int32, device=dev)
+    lib = m.BlockSparseAttention(0)
+    h = lib.handle
+
+    def step():
+        m.bsa_forward(h, q, k, v, out, idx, topk=w.topk, scale=w.scale, causal=w.causal)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # Second pass: per-kernel HIP events on the launch stream.
+    m.bsa_profile_read(h, reset=True)
+    m.bsa_profile_enable(h, True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms, launches = m.bsa_profile_read(h, reset=True)
+    m.bsa_profile_enable(h, False)
+    per_step = {name: ms[i] / args.steps for i, name in enumerate(m.STAGE_NAMES)}
+    per_launch = {name: (ms[i] / launches[i] if launches[i] else 0.0)
+                  for i, name in enumerate(m.STAGE_NAMES)}
+    launches_per_step = {name: launches[i] // args.steps for i, name in enumerate(m.STAGE_NAMES)}
+
+    work = stage_work(w)
+    dom = max(per_step, key=per_step.get)
+    bound, flops, nbytes = work[dom]
+    t_launch = per_launch[dom] * 1e-3
+    n_launch = launches_per_step[dom]
+    if bound == "mfma":
+        achieved = flops / n_launch / t_launch / 1e12
+        peak, unit = MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
+    else:
+        achieved = nbytes / n_launch / t_launch / 1e9
+        peak, unit = HBM_PEAK_GBS, "GB/s"
+    roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 5), "traffic": measured_traffic(dom, w.name),
+                "kernel": dom, "avg_launch_ms": round(per_launch[dom], 5),
+                "launches_per_step": n_launch}
+
+    total_flops = sum(f for (_, f, _) in work.values())
+    tokens = w.batch * w.n
+    result = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_per_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded N(0,1) q/k/v plus per-block key offsets N(0,0.5^2), "
+                "rounded to bf16 (no dataset)" if w.key_offsets else "synthetic: seeded N(0,1)",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n": w.n, "d": w.d,
+                   "block": w.block, "topk": w.topk, "causal": w.causal},
+        "effective_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 3),
+        "algorithmic_gflop": round(total_flops / 1e9, 3),
+        "stage_ms_per_step": {k_: round(v_, 5) for k_, v_ in per_step.items()},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_positions)
+    lib.close()
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

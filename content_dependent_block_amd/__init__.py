@@ -1,0 +1,62 @@
+"""Two-stage, content-dependent block-sparse attention forward for AMD MI355X.
+
+Stage 1 mean-pools each 64-key block, scores every query against every block
+representative and keeps each query's top-k blocks; stage 2 runs fused
+online-softmax attention over only those blocks.  All of it runs in the gfx950
+kernels of ``libbsa.so`` behind the C ABI in ``include/bsa.h``; this package is
+a thin binding with the same names (see ``_binding``).
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from ._binding import *  # noqa: F401,F403  (bsa_* functions and constants)
+from ._binding import (BSA_OPT_PANEL_CHUNK_BYTES, EXPORTED, STAGE_NAMES, BsaError, bsa_create,
+                       bsa_destroy, bsa_forward, bsa_forward_static, bsa_set_option)
+
+
+class BlockSparseAttention:
+    """Owns a library handle (and its workspace) on one device."""
+
+    def __init__(self, device: int = 0):
+        self.device = device
+        self.handle = bsa_create(device)
+
+    def close(self):
+        if self.handle is not None:
+            bsa_destroy(self.handle)
+            self.handle = None
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def forward(self, q, k, v, *, topk: int, block: int = 64, scale: float | None = None,
+                causal: bool = False, return_indices: bool = False, stream=None):
+        """out (float32, same shape as q), and optionally the int32 block indices."""
+        b, h, n, d = q.shape
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        idx = torch.empty((b, h, n, topk), dtype=torch.int32, device=q.device) if return_indices else None
+        bsa_forward(self.handle, q, k, v, out, idx, block=block, topk=topk, scale=scale,
+                    causal=causal, stream=stream)
+        return (out, idx) if return_indices else out
+
+    def forward_static(self, q, k, v, tile_row_ptr, tile_col, tile_rowmask=None, *,
+                       scale: float | None = None, stream=None):
+        d = q.shape[-1]
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        bsa_forward_static(self.handle, q, k, v, out, tile_row_ptr, tile_col, tile_rowmask,
+                           scale=scale, stream=stream)
+        return out

@@ -1,0 +1,271 @@
+"""ctypes binding of libbsa.so (include/bsa.h), same names as the C ABI.
+
+Argument marshalling only: tensors are checked for shape, dtype, device and
+contiguity (the C side cannot see sizes), then their device pointers and the
+current HIP stream are passed through.  Every step of the computation runs in
+the gfx950 kernels of libbsa.so; there is no fallback.  If the library has not
+been built, importing this module raises ImportError.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+import numpy as np
+import torch
+
+_LIB_PATH = Path(__file__).resolve().parent / "libbsa.so"
+if not _LIB_PATH.exists():
+    raise ImportError(f"{_LIB_PATH} is not built; run `python -m content_dependent_block_amd.build`")
+_lib = ctypes.CDLL(str(_LIB_PATH))
+
+BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED = 0, 1, 2
+BSA_ERR_NO_DEVICE, BSA_ERR_OUT_OF_MEMORY, BSA_ERR_LAUNCH = 3, 4, 5
+BSA_FP32, BSA_BF16 = 0, 1
+BSA_STAGE_POOL, BSA_STAGE_COARSE, BSA_STAGE_TOPK, BSA_STAGE_FINE, BSA_NUM_STAGES = 0, 1, 2, 3, 4
+STAGE_NAMES = ("block_pool", "coarse_score", "topk_select", "sparse_flash_fwd")
+BSA_OPT_PANEL_CHUNK_BYTES = 0
+
+_P, _I, _I64, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+
+
+def _sig(name, args, res=ctypes.c_int):
+    f = getattr(_lib, name)
+    f.argtypes, f.restype = args, res
+    return f
+
+
+_sig("bsa_create", [_I, ctypes.POINTER(_P)])
+_sig("bsa_destroy", [_P])
+_sig("bsa_status_string", [_I], ctypes.c_char_p)
+_sig("bsa_last_error", [_P], ctypes.c_char_p)
+_sig("bsa_set_option", [_P, _I, _I64])
+_sig("bsa_workspace_bytes", [_P, ctypes.POINTER(ctypes.c_size_t)])
+_sig("bsa_forward", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P])
+_sig("bsa_fine_forward", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P])
+_sig("bsa_block_pool", [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P])
+_sig("bsa_coarse_score", [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P])
+_sig("bsa_topk_select", [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P])
+_sig("bsa_forward_static", [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I64, _F, _P])
+_sig("bsa_tiles_from_mask", [_P, _I, _I, _P, _P, _P, ctypes.POINTER(_I64)])
+_sig("bsa_tiles_window_stride", [_I, _I, _I, _I, _P, _P, _P, ctypes.POINTER(_I64)])
+_sig("bsa_tiles_validate", [_P, _P, _I64, _I, _I])
+_sig("bsa_profile_enable", [_P, _I])
+_sig("bsa_profile_read", [_P, _P, _P, _I])
+
+EXPORTED = ("bsa_create", "bsa_destroy", "bsa_status_string", "bsa_last_error", "bsa_set_option",
+            "bsa_workspace_bytes", "bsa_forward", "bsa_fine_forward", "bsa_block_pool",
+            "bsa_coarse_score", "bsa_topk_select", "bsa_forward_static", "bsa_tiles_from_mask",
+            "bsa_tiles_window_stride", "bsa_tiles_validate", "bsa_profile_enable",
+            "bsa_profile_read")
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{bsa_status_string(status)}: {message}")
+        self.status = status
+
+
+def bsa_status_string(status: int) -> str:
+    return _lib.bsa_status_string(status).decode()
+
+
+def bsa_last_error(h=None) -> str:
+    return _lib.bsa_last_error(h).decode()
+
+
+def _check(status: int, h=None):
+    if status != BSA_OK:
+        raise BsaError(status, bsa_last_error(h))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BSA_BF16
+    if t.dtype == torch.float32:
+        return BSA_FP32
+    raise TypeError(f"unsupported dtype {t.dtype}; use torch.bfloat16 or torch.float32")
+
+
+def _stream(stream, device):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _need(t, name, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _qkv(q, k, v):
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, heads, n, d]")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    pq = _need(q, "q", q.shape, None, dev)
+    pk = _need(k, "k", q.shape, q.dtype, dev)
+    pv = _need(v, "v", q.shape, q.dtype, dev)
+    return pq, pk, pv, dev
+
+
+# ------------------------------------------------------------- lifetime --
+def bsa_create(device: int = 0):
+    h = ctypes.c_void_p()
+    _check(_lib.bsa_create(device, ctypes.byref(h)))
+    return h
+
+
+def bsa_destroy(h) -> None:
+    _check(_lib.bsa_destroy(h), h)
+
+
+def bsa_set_option(h, option: int, value: int) -> None:
+    _check(_lib.bsa_set_option(h, option, value), h)
+
+
+def bsa_workspace_bytes(h) -> int:
+    out = ctypes.c_size_t()
+    _check(_lib.bsa_workspace_bytes(h, ctypes.byref(out)), h)
+    return int(out.value)
+
+
+# -------------------------------------------------------------- forward --
+def bsa_forward(h, q, k, v, out, block_idx_out=None, *, block: int = 64, topk: int,
+                scale: float, causal: bool = False, stream=None) -> None:
+    pq, pk, pv, dev = _qkv(q, k, v)
+    b, hh, n, d = q.shape
+    po = _need(out, "out", q.shape, torch.float32, dev)
+    pi = None
+    if block_idx_out is not None:
+        pi = _need(block_idx_out, "block_idx_out", (b, hh, n, topk), torch.int32, dev)
+    _check(_lib.bsa_forward(h, pq, pk, pv, po, pi, b, hh, n, d, _dtype_code(q), block, topk,
+                            float(scale), int(causal), _stream(stream, dev)), h)
+
+
+def bsa_fine_forward(h, q, k, v, out, block_idx, *, block: int = 64, scale: float,
+                     causal: bool = False, stream=None) -> None:
+    pq, pk, pv, dev = _qkv(q, k, v)
+    b, hh, n, d = q.shape
+    if block_idx.dim() != 4:
+        raise ValueError("block_idx must be [batch, heads, n, topk]")
+    topk = block_idx.shape[-1]
+    po = _need(out, "out", q.shape, torch.float32, dev)
+    pi = _need(block_idx, "block_idx", (b, hh, n, topk), torch.int32, dev)
+    _check(_lib.bsa_fine_forward(h, pq, pk, pv, po, pi, b, hh, n, d, _dtype_code(q), block, topk,
+                                 float(scale), int(causal), _stream(stream, dev)), h)
+
+
+def bsa_block_pool(h, k, repr_out, *, block: int = 64, stream=None) -> None:
+    if k.dim() != 4:
+        raise ValueError("k must be [batch, heads, n, d]")
+    b, hh, n, d = k.shape
+    dev = k.device
+    pk = _need(k, "k", k.shape, None, dev)
+    pr = _need(repr_out, "repr_out", (b, hh, n // block, d), torch.float32, dev)
+    _check(_lib.bsa_block_pool(h, pk, pr, b, hh, n, d, _dtype_code(k), block, _stream(stream, dev)), h)
+
+
+def bsa_coarse_score(h, q, repr_, panel_out, *, block: int = 64, causal: bool = False,
+                     stream=None) -> None:
+    if q.dim() != 4:
+        raise ValueError("q must be [batch, heads, n, d]")
+    b, hh, n, d = q.shape
+    dev = q.device
+    pq = _need(q, "q", q.shape, None, dev)
+    pr = _need(repr_, "repr", (b, hh, n // block, d), torch.float32, dev)
+    pp = _need(panel_out, "panel_out", (b, hh, n, n // block), torch.float32, dev)
+    _check(_lib.bsa_coarse_score(h, pq, pr, pp, b, hh, n, d, _dtype_code(q), block, int(causal),
+                                 _stream(stream, dev)), h)
+
+
+def bsa_topk_select(h, panel, block_idx_out, *, block: int = 64, causal: bool = False,
+                    stream=None) -> None:
+    if panel.dim() != 4:
+        raise ValueError("panel must be [batch, heads, n, n/block]")
+    b, hh, n, nb = panel.shape
+    dev = panel.device
+    if nb * block != n:
+        raise ValueError("panel's last dimension must be n / block")
+    pp = _need(panel, "panel", panel.shape, torch.float32, dev)
+    topk = block_idx_out.shape[-1]
+    pi = _need(block_idx_out, "block_idx_out", (b, hh, n, topk), torch.int32, dev)
+    _check(_lib.bsa_topk_select(h, pp, pi, b, hh, n, block, topk, int(causal),
+                                _stream(stream, dev)), h)
+
+
+# --------------------------------------------------------------- static --
+def bsa_forward_static(h, q, k, v, out, tile_row_ptr, tile_col, tile_rowmask=None, *,
+                       scale: float, stream=None) -> None:
+    pq, pk, pv, dev = _qkv(q, k, v)
+    b, hh, n, d = q.shape
+    po = _need(out, "out", q.shape, torch.float32, dev)
+    prp = _need(tile_row_ptr, "tile_row_ptr", (n // 64 + 1,), torch.int32, dev)
+    nnz = int(tile_col.numel())
+    pc = _need(tile_col, "tile_col", (nnz,), torch.int32, dev)
+    pm = None
+    if tile_rowmask is not None:
+        pm = _need(tile_rowmask, "tile_rowmask", (nnz, 64), None, dev)
+        if tile_rowmask.element_size() != 8:
+            raise TypeError("tile_rowmask must hold 64-bit masks")
+    _check(_lib.bsa_forward_static(h, pq, pk, pv, po, b, hh, n, d, _dtype_code(q), prp, pc, pm,
+                                   nnz, float(scale), _stream(stream, dev)), h)
+
+
+def _tiles(fn, n, *head_args):
+    row_ptr = np.zeros(n // 64 + 1, dtype=np.int32)
+    nnz = ctypes.c_int64(0)
+    _check(fn(*head_args, row_ptr.ctypes.data, None, None, ctypes.byref(nnz)))
+    col = np.zeros(max(nnz.value, 1), dtype=np.int32)
+    rowmask = np.zeros((max(nnz.value, 1), 64), dtype=np.uint64)
+    _check(fn(*head_args, row_ptr.ctypes.data, col.ctypes.data, rowmask.ctypes.data,
+              ctypes.byref(nnz)))
+    return row_ptr, col[: nnz.value].copy(), rowmask[: nnz.value].copy()
+
+
+def bsa_tiles_from_mask(mask: np.ndarray, tile: int = 64):
+    """Host CSR tile list (row_ptr, col, rowmask) of a dense [n, n] mask."""
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    n = mask.shape[0]
+    if mask.shape != (n, n):
+        raise ValueError("mask must be square")
+    return _tiles(_lib.bsa_tiles_from_mask, n, mask.ctypes.data, n, tile)
+
+
+def bsa_tiles_window_stride(n: int, window: int, stride: int, tile: int = 64):
+    """Host CSR tile list of the window+stride pattern."""
+    return _tiles(_lib.bsa_tiles_window_stride, n, n, window, stride, tile)
+
+
+def bsa_tiles_validate(row_ptr: np.ndarray, col: np.ndarray, n: int, tile: int = 64) -> bool:
+    row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    col = np.ascontiguousarray(col, dtype=np.int32)
+    if row_ptr.size != n // tile + 1:
+        return False
+    return _lib.bsa_tiles_validate(row_ptr.ctypes.data, col.ctypes.data if col.size else None,
+                                   col.size, n, tile) == BSA_OK
+
+
+# --------------------------------------------------------------- timing --
+def bsa_profile_enable(h, on: bool = True) -> None:
+    _check(_lib.bsa_profile_enable(h, int(on)), h)
+
+
+def bsa_profile_read(h, reset: bool = True):
+    """Per-stage summed kernel milliseconds and launch counts."""
+    ms = (ctypes.c_double * BSA_NUM_STAGES)()
+    launches = (ctypes.c_int64 * BSA_NUM_STAGES)()
+    _check(_lib.bsa_profile_read(h, ms, launches, int(reset)), h)
+    return list(ms), list(launches)

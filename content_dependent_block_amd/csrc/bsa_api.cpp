@@ -1,0 +1,451 @@
+// bsa_api.cpp -- the C ABI declared in include/bsa.h: argument validation,
+// the per-handle workspace, the order of the kernel launches, per-stage
+// timing.  Every step of the computation runs in the gfx950 kernels; this
+// file only checks, allocates and enqueues.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "bsa.h"
+#include "bsa_launch.hpp"
+
+#define BSA_API extern "C" __attribute__((visibility("default")))
+
+struct bsa_handle_s {
+  int device = 0;
+  char err[512] = {0};
+  // workspace
+  float* repr = nullptr;
+  size_t repr_bytes = 0;
+  float* panel = nullptr;
+  size_t panel_bytes = 0;
+  int32_t* idx = nullptr;
+  size_t idx_bytes = 0;
+  int64_t panel_chunk_bytes = int64_t(128) << 20;
+  // timing
+  bool profiling = false;
+  struct Rec {
+    int stage;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> free_events;
+};
+
+namespace {
+
+thread_local char g_err[512] = {0};
+
+bsa_status fail(bsa_handle h, bsa_status s, const char* fmt, ...) {
+  char* buf = h ? h->err : g_err;
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, 512, fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+class DeviceGuard {
+ public:
+  explicit DeviceGuard(int dev) {
+    if (hipGetDevice(&prev_) != hipSuccess) prev_ = -1;
+    if (prev_ != dev) (void)hipSetDevice(dev);
+  }
+  ~DeviceGuard() {
+    int cur = -1;
+    if (prev_ >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev_) (void)hipSetDevice(prev_);
+  }
+
+ private:
+  int prev_ = -1;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bsa_status grow(bsa_handle h, void** ptr, size_t* have, size_t need, const char* what) {
+  if (*have >= need) return BSA_OK;
+  if (*ptr) {
+    (void)hipFree(*ptr);
+    *ptr = nullptr;
+    *have = 0;
+  }
+  if (getenv("BSA_TEST_FAIL_ALLOC") && std::strcmp(getenv("BSA_TEST_FAIL_ALLOC"), "1") == 0)
+    return fail(h, BSA_ERR_OUT_OF_MEMORY, "%s: allocation of %zu bytes refused (BSA_TEST_FAIL_ALLOC)",
+                what, need);
+  if (hipMalloc(ptr, need) != hipSuccess) {
+    (void)hipGetLastError();
+    *ptr = nullptr;
+    return fail(h, BSA_ERR_OUT_OF_MEMORY, "%s: hipMalloc(%zu) failed", what, need);
+  }
+  *have = need;
+  return BSA_OK;
+}
+
+hipEvent_t take_event(bsa_handle h) {
+  if (!h->free_events.empty()) {
+    hipEvent_t e = h->free_events.back();
+    h->free_events.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Launch `fn` (returning hipError_t) for `stage`, bracketed by events when
+// timing is on.
+template <typename F>
+bsa_status timed_launch(bsa_handle h, int stage, hipStream_t s, const char* what, F&& fn) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (h->profiling) {
+    a = take_event(h);
+    b = take_event(h);
+    if (!a || !b || hipEventRecord(a, s) != hipSuccess)
+      return fail(h, BSA_ERR_LAUNCH, "%s: could not record a timing event", what);
+  }
+  const hipError_t e = fn();
+  if (e != hipSuccess)
+    return fail(h, BSA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  if (h->profiling) {
+    if (hipEventRecord(b, s) != hipSuccess)
+      return fail(h, BSA_ERR_LAUNCH, "%s: could not record a timing event", what);
+    h->recs.push_back({stage, a, b});
+  }
+  return BSA_OK;
+}
+
+struct Shape {
+  int batch, heads, n, d;
+  int64_t bh() const { return int64_t(batch) * heads; }
+  int64_t elems() const { return bh() * n * d; }
+};
+
+bsa_status check_shape(bsa_handle h, const char* fn, const Shape& s, bsa_dtype dtype, int block) {
+  if (s.batch < 1 || s.heads < 1 || s.n < 1 || s.d < 1)
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: batch, heads, n and d must be >= 1 (got %d, %d, %d, %d)",
+                fn, s.batch, s.heads, s.n, s.d);
+  if (dtype != BSA_FP32 && dtype != BSA_BF16)
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, int(dtype));
+  if (block != 64)
+    return fail(h, BSA_ERR_UNSUPPORTED, "%s: block must be 64 (got %d)", fn, block);
+  if (s.d != 64 && s.d != 128)
+    return fail(h, BSA_ERR_UNSUPPORTED, "%s: d must be 64 or 128 (got %d)", fn, s.d);
+  if (s.n % 64 != 0)
+    return fail(h, BSA_ERR_UNSUPPORTED, "%s: n must be a multiple of 64 (got %d)", fn, s.n);
+  if (s.bh() * s.n > (int64_t(1) << 31) / 1 || s.elems() > (int64_t(1) << 40))
+    return fail(h, BSA_ERR_UNSUPPORTED, "%s: problem too large (batch*heads*n = %lld)", fn,
+                (long long)(s.bh() * s.n));
+  return BSA_OK;
+}
+
+bsa_status check_ptr(bsa_handle h, const char* fn, const char* name, const void* p) {
+  if (!p) return fail(h, BSA_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
+  if (!aligned16(p)) return fail(h, BSA_ERR_INVALID_ARG, "%s: %s is not 16-byte aligned", fn, name);
+  return BSA_OK;
+}
+
+bsa_status check_scale(bsa_handle h, const char* fn, float scale) {
+  if (!(std::isfinite(scale) && scale > 0.f))
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: scale must be finite and > 0 (got %g)", fn, double(scale));
+  return BSA_OK;
+}
+
+bsa_status check_dynamic(bsa_handle h, const char* fn, const Shape& s, int topk, int causal) {
+  if (topk < 1) return fail(h, BSA_ERR_INVALID_ARG, "%s: topk must be >= 1 (got %d)", fn, topk);
+  if (causal != 0 && causal != 1)
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: causal must be 0 or 1 (got %d)", fn, causal);
+  if (s.n / 64 > 2048)
+    return fail(h, BSA_ERR_UNSUPPORTED, "%s: n/64 must be <= 2048 (got %d)", fn, s.n / 64);
+  return BSA_OK;
+}
+
+#define TRY(expr)                     \
+  do {                                \
+    const bsa_status _st = (expr);    \
+    if (_st != BSA_OK) return _st;    \
+  } while (0)
+
+}  // namespace
+
+// ------------------------------------------------------------- lifetime --
+
+BSA_API const char* bsa_status_string(bsa_status s) {
+  switch (s) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_INVALID_ARG: return "invalid argument";
+    case BSA_ERR_UNSUPPORTED: return "unsupported";
+    case BSA_ERR_NO_DEVICE: return "no gfx950 device";
+    case BSA_ERR_OUT_OF_MEMORY: return "out of device memory";
+    case BSA_ERR_LAUNCH: return "launch failed";
+  }
+  return "unknown status";
+}
+
+BSA_API const char* bsa_last_error(bsa_handle h) { return h ? h->err : g_err; }
+
+BSA_API bsa_status bsa_create(int device, bsa_handle* out) {
+  if (!out) return fail(nullptr, BSA_ERR_INVALID_ARG, "bsa_create: out is NULL");
+  *out = nullptr;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count < 1) {
+    (void)hipGetLastError();
+    return fail(nullptr, BSA_ERR_NO_DEVICE, "bsa_create: no HIP device");
+  }
+  if (device < 0 || device >= count)
+    return fail(nullptr, BSA_ERR_NO_DEVICE, "bsa_create: device %d out of range (count %d)", device, count);
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess)
+    return fail(nullptr, BSA_ERR_NO_DEVICE, "bsa_create: cannot query device %d", device);
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(nullptr, BSA_ERR_NO_DEVICE, "bsa_create: device %d is %s, not gfx950", device,
+                prop.gcnArchName);
+  bsa_handle h = new (std::nothrow) bsa_handle_s();
+  if (!h) return fail(nullptr, BSA_ERR_OUT_OF_MEMORY, "bsa_create: host allocation failed");
+  h->device = device;
+  *out = h;
+  return BSA_OK;
+}
+
+BSA_API bsa_status bsa_destroy(bsa_handle h) {
+  if (!h) return BSA_OK;
+  DeviceGuard dg(h->device);
+  for (auto& r : h->recs) {
+    (void)hipEventDestroy(r.a);
+    (void)hipEventDestroy(r.b);
+  }
+  for (auto e : h->free_events) (void)hipEventDestroy(e);
+  if (h->repr) (void)hipFree(h->repr);
+  if (h->panel) (void)hipFree(h->panel);
+  if (h->idx) (void)hipFree(h->idx);
+  delete h;
+  return BSA_OK;
+}
+
+BSA_API bsa_status bsa_set_option(bsa_handle h, int option, int64_t value) {
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "bsa_set_option: handle is NULL");
+  switch (option) {
+    case BSA_OPT_PANEL_CHUNK_BYTES:
+      if (value < 1) return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: panel chunk must be > 0");
+      h->panel_chunk_bytes = value;
+      return BSA_OK;
+    default:
+      return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: unknown option %d", option);
+  }
+}
+
+BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
+  if (!h || !bytes) return fail(h, BSA_ERR_INVALID_ARG, "bsa_workspace_bytes: NULL argument");
+  *bytes = h->repr_bytes + h->panel_bytes + h->idx_bytes;
+  return BSA_OK;
+}
+
+// ----------------------------------------------------------- stage 1 ----
+
+namespace {
+
+bsa_status run_pool(bsa_handle h, const void* k, float* repr, const Shape& s, bsa_dtype dt,
+                    hipStream_t st) {
+  return timed_launch(h, BSA_STAGE_POOL, st, "block_pool", [&] {
+    return bsa::launch_block_pool(k, repr, s.bh(), s.n, s.d, dt, st);
+  });
+}
+
+// coarse_score + topk_select over all rows, in panel chunks of at most
+// panel_chunk_bytes.
+bsa_status run_select(bsa_handle h, const void* q, const float* repr, int32_t* idx, const Shape& s,
+                      bsa_dtype dt, int topk, int causal, hipStream_t st) {
+  const int64_t nb = s.n / 64;
+  const int64_t total = s.bh() * s.n;
+  int64_t chunk = h->panel_chunk_bytes / (nb * 4) / 64 * 64;
+  if (chunk < 64) chunk = 64;
+  if (chunk > total) chunk = total;
+  TRY(grow(h, reinterpret_cast<void**>(&h->panel), &h->panel_bytes, size_t(chunk) * nb * 4,
+           "panel workspace"));
+  for (int64_t r0 = 0; r0 < total; r0 += chunk) {
+    const int64_t rows = (total - r0) < chunk ? (total - r0) : chunk;
+    TRY(timed_launch(h, BSA_STAGE_COARSE, st, "coarse_score", [&] {
+      return bsa::launch_coarse_score(q, repr, h->panel, r0, rows, s.n, s.d, dt, causal, st);
+    }));
+    TRY(timed_launch(h, BSA_STAGE_TOPK, st, "topk_select", [&] {
+      return bsa::launch_topk_select(h->panel, idx, r0, rows, s.n, topk, causal, st);
+    }));
+  }
+  return BSA_OK;
+}
+
+}  // namespace
+
+BSA_API bsa_status bsa_block_pool(bsa_handle h, const void* k, float* repr_out, int batch,
+                                  int heads, int n, int d, bsa_dtype dtype, int block,
+                                  void* stream) {
+  const char* fn = "bsa_block_pool";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const Shape s{batch, heads, n, d};
+  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_ptr(h, fn, "k", k));
+  TRY(check_ptr(h, fn, "repr_out", repr_out));
+  DeviceGuard dg(h->device);
+  return run_pool(h, k, repr_out, s, dtype, static_cast<hipStream_t>(stream));
+}
+
+BSA_API bsa_status bsa_coarse_score(bsa_handle h, const void* q, const float* repr,
+                                    float* panel_out, int batch, int heads, int n, int d,
+                                    bsa_dtype dtype, int block, int causal, void* stream) {
+  const char* fn = "bsa_coarse_score";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const Shape s{batch, heads, n, d};
+  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_dynamic(h, fn, s, 1, causal));
+  TRY(check_ptr(h, fn, "q", q));
+  TRY(check_ptr(h, fn, "repr", repr));
+  TRY(check_ptr(h, fn, "panel_out", panel_out));
+  DeviceGuard dg(h->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return timed_launch(h, BSA_STAGE_COARSE, st, "coarse_score", [&] {
+    return bsa::launch_coarse_score(q, repr, panel_out, 0, s.bh() * s.n, s.n, s.d, dtype, causal, st);
+  });
+}
+
+BSA_API bsa_status bsa_topk_select(bsa_handle h, const float* panel, int32_t* block_idx_out,
+                                   int batch, int heads, int n, int block, int topk, int causal,
+                                   void* stream) {
+  const char* fn = "bsa_topk_select";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const Shape s{batch, heads, n, 64};
+  TRY(check_shape(h, fn, s, BSA_FP32, block));
+  TRY(check_dynamic(h, fn, s, topk, causal));
+  TRY(check_ptr(h, fn, "panel", panel));
+  if (!block_idx_out) return fail(h, BSA_ERR_INVALID_ARG, "%s: block_idx_out is NULL", fn);
+  DeviceGuard dg(h->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return timed_launch(h, BSA_STAGE_TOPK, st, "topk_select", [&] {
+    return bsa::launch_topk_select(panel, block_idx_out, 0, s.bh() * s.n, s.n, topk, causal, st);
+  });
+}
+
+// ----------------------------------------------------------- stage 2 ----
+
+BSA_API bsa_status bsa_fine_forward(bsa_handle h, const void* q, const void* k, const void* v,
+                                    float* out, const int32_t* block_idx, int batch, int heads,
+                                    int n, int d, bsa_dtype dtype, int block, int topk,
+                                    float scale, int causal, void* stream) {
+  const char* fn = "bsa_fine_forward";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const Shape s{batch, heads, n, d};
+  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_dynamic(h, fn, s, topk, causal));
+  TRY(check_scale(h, fn, scale));
+  TRY(check_ptr(h, fn, "q", q));
+  TRY(check_ptr(h, fn, "k", k));
+  TRY(check_ptr(h, fn, "v", v));
+  TRY(check_ptr(h, fn, "out", out));
+  if (!block_idx) return fail(h, BSA_ERR_INVALID_ARG, "%s: block_idx is NULL", fn);
+  DeviceGuard dg(h->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
+    return bsa::launch_sparse_flash_dynamic(q, k, v, out, block_idx, s.bh(), s.n, s.d, topk, scale,
+                                            causal, dtype, st);
+  });
+}
+
+BSA_API bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const void* v,
+                               float* out, int32_t* block_idx_out, int batch, int heads, int n,
+                               int d, bsa_dtype dtype, int block, int topk, float scale,
+                               int causal, void* stream) {
+  const char* fn = "bsa_forward";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const Shape s{batch, heads, n, d};
+  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_dynamic(h, fn, s, topk, causal));
+  TRY(check_scale(h, fn, scale));
+  TRY(check_ptr(h, fn, "q", q));
+  TRY(check_ptr(h, fn, "k", k));
+  TRY(check_ptr(h, fn, "v", v));
+  TRY(check_ptr(h, fn, "out", out));
+  if (block_idx_out && (reinterpret_cast<uintptr_t>(block_idx_out) & 3u))
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: block_idx_out is not 4-byte aligned", fn);
+  DeviceGuard dg(h->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t nb = s.n / 64;
+  TRY(grow(h, reinterpret_cast<void**>(&h->repr), &h->repr_bytes, size_t(s.bh() * nb * s.d) * 4,
+           "repr workspace"));
+  int32_t* idx = block_idx_out;
+  if (!idx) {
+    TRY(grow(h, reinterpret_cast<void**>(&h->idx), &h->idx_bytes, size_t(s.bh() * s.n * topk) * 4,
+             "index workspace"));
+    idx = h->idx;
+  }
+  TRY(run_pool(h, k, h->repr, s, dtype, st));
+  TRY(run_select(h, q, h->repr, idx, s, dtype, topk, causal, st));
+  return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
+    return bsa::launch_sparse_flash_dynamic(q, k, v, out, idx, s.bh(), s.n, s.d, topk, scale,
+                                            causal, dtype, st);
+  });
+}
+
+BSA_API bsa_status bsa_forward_static(bsa_handle h, const void* q, const void* k, const void* v,
+                                      float* out, int batch, int heads, int n, int d,
+                                      bsa_dtype dtype, const int32_t* tile_row_ptr,
+                                      const int32_t* tile_col, const uint64_t* tile_rowmask,
+                                      int64_t nnz, float scale, void* stream) {
+  const char* fn = "bsa_forward_static";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const Shape s{batch, heads, n, d};
+  TRY(check_shape(h, fn, s, dtype, 64));
+  TRY(check_scale(h, fn, scale));
+  TRY(check_ptr(h, fn, "q", q));
+  TRY(check_ptr(h, fn, "k", k));
+  TRY(check_ptr(h, fn, "v", v));
+  TRY(check_ptr(h, fn, "out", out));
+  if (!tile_row_ptr) return fail(h, BSA_ERR_INVALID_ARG, "%s: tile_row_ptr is NULL", fn);
+  if (nnz < 0) return fail(h, BSA_ERR_INVALID_ARG, "%s: nnz must be >= 0", fn);
+  if (nnz > 0 && !tile_col) return fail(h, BSA_ERR_INVALID_ARG, "%s: tile_col is NULL", fn);
+  if (tile_rowmask && (reinterpret_cast<uintptr_t>(tile_rowmask) & 7u))
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: tile_rowmask is not 8-byte aligned", fn);
+  DeviceGuard dg(h->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
+    return bsa::launch_sparse_flash_static(q, k, v, out, tile_row_ptr, tile_col, tile_rowmask, nnz,
+                                           s.bh(), s.n, s.d, scale, dtype, st);
+  });
+}
+
+// ------------------------------------------------------------- timing ---
+
+BSA_API bsa_status bsa_profile_enable(bsa_handle h, int on) {
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "bsa_profile_enable: handle is NULL");
+  h->profiling = on != 0;
+  return BSA_OK;
+}
+
+BSA_API bsa_status bsa_profile_read(bsa_handle h, double* ms, int64_t* launches, int reset) {
+  if (!h || !ms) return fail(h, BSA_ERR_INVALID_ARG, "bsa_profile_read: NULL argument");
+  DeviceGuard dg(h->device);
+  for (int i = 0; i < BSA_NUM_STAGES; ++i) {
+    ms[i] = 0.0;
+    if (launches) launches[i] = 0;
+  }
+  for (auto& r : h->recs) {
+    if (hipEventSynchronize(r.b) != hipSuccess)
+      return fail(h, BSA_ERR_LAUNCH, "bsa_profile_read: event wait failed");
+    float t = 0.f;
+    if (hipEventElapsedTime(&t, r.a, r.b) != hipSuccess)
+      return fail(h, BSA_ERR_LAUNCH, "bsa_profile_read: elapsed-time query failed");
+    ms[r.stage] += t;
+    if (launches) launches[r.stage] += 1;
+  }
+  if (reset) {
+    for (auto& r : h->recs) {
+      h->free_events.push_back(r.a);
+      h->free_events.push_back(r.b);
+    }
+    h->recs.clear();
+  }
+  return BSA_OK;
+}

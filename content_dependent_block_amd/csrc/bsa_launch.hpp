@@ -1,0 +1,42 @@
+// bsa_launch.hpp -- host-side launchers of the gfx950 kernels.  Each kernel
+// file defines its launcher; the C ABI (bsa_api.cpp) validates arguments and
+// calls these.  Launchers assume validated arguments: n % 64 == 0, d in
+// {64, 128}, n / 64 <= 2048 where stated, 16-byte aligned pointers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "bsa.h"
+
+namespace bsa {
+
+// block_pool: k [bh][n][d] -> repr float [bh][n/64][d].
+hipError_t launch_block_pool(const void* k, float* repr, int64_t bh, int n, int d,
+                             bsa_dtype dtype, hipStream_t stream);
+
+// coarse_score over panel rows [row0, row0 + rows) of the flattened
+// [bh * n] query rows; row0 and rows multiples of 64.  panel row r holds
+// query row0 + r, nb = n / 64 columns.
+hipError_t launch_coarse_score(const void* q, const float* repr, float* panel, int64_t row0,
+                               int64_t rows, int n, int d, bsa_dtype dtype, int causal,
+                               hipStream_t stream);
+
+// topk_select over the same rows: idx[(row0 + r) * topk + t].
+hipError_t launch_topk_select(const float* panel, int32_t* idx, int64_t row0, int64_t rows,
+                              int n, int topk, int causal, hipStream_t stream);
+
+// sparse_flash_fwd, dynamic: per 64-query tile the union of its rows'
+// selected blocks, each row masked to its own selection.
+hipError_t launch_sparse_flash_dynamic(const void* q, const void* k, const void* v, float* out,
+                                       const int32_t* idx, int64_t bh, int n, int d, int topk,
+                                       float scale, int causal, bsa_dtype dtype,
+                                       hipStream_t stream);
+
+// sparse_flash_fwd, static tile list.
+hipError_t launch_sparse_flash_static(const void* q, const void* k, const void* v, float* out,
+                                      const int32_t* row_ptr, const int32_t* col,
+                                      const uint64_t* rowmask, int64_t nnz, int64_t bh, int n,
+                                      int d, float scale, bsa_dtype dtype, hipStream_t stream);
+
+}  // namespace bsa

@@ -1,0 +1,440 @@
+// sparse_flash_fwd.hip -- Stage 2, fused fine attention over a per-query-tile
+// list of 64-key tiles with per-row masks.
+//
+// What it computes (nishantmodi.me "sparse-attention-triton-bench", sections
+// "Stage 2: fine attention" and "The Triton kernel"): for each query i,
+// o_i = sum_j softmax_j(scale * q_i . k_j) v_j over the keys j visible to i,
+// with an online softmax: running max m, running sum l and an unnormalised
+// accumulator, rescaled as each key tile arrives, so no score ever leaves the
+// chip.  Invisible keys take no part (score -inf; yayme/CUDA-kernel README,
+// the note on masked keys).  A row with no visible key gets zeros.
+//
+// Tile sources:
+//   dynamic -- the tile list of a 64-query tile is the union of its rows'
+//     selected blocks (ascending), and row r sees block beta iff beta is in
+//     its own selection; in the causal variant keys after the query are
+//     hidden (only the diagonal block can hold such keys).
+//   static  -- a CSR list of key tiles per query tile plus optional per-row
+//     64-bit key masks, built on the host (the README's plan of precomputing
+//     the active (row tile, column tile) list; infra.bea.ai "Block-Sparse &
+//     Linear Attention Kernels", the loop over K/V blocks where the mask is set).
+//
+// Work layout (gfx950): a 256-thread workgroup owns 64 queries, 16 per wave.
+// Each key tile (64 keys) is staged once into LDS for all four waves: K in its
+// natural [key][d] layout, V transposed to [d][key] for bf16.  A wave whose 16
+// rows see nothing in a tile skips its MFMA work for that tile.  With
+// S^T = K * Q^T on v_mfma_f32_16x16x32_bf16 a lane ends up holding scores of
+// ONE query (column lane%16) for 16 keys, so the row max / sum need only
+// in-lane work plus two xor shuffles, and the bf16-rounded probabilities are
+// already laid out as the B operand of O^T = V^T * P^T.  l is summed from the
+// same rounded probabilities that feed the PV product.  fp32 inputs use
+// v_mfma_f32_16x16x4_f32 the same way with float probabilities.  The next
+// tile's global loads are issued into registers before the current tile's
+// MFMA work (register double buffering).
+#include "bsa_device.hpp"
+#include "bsa_launch.hpp"
+
+namespace bsa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+template <typename T, int D>
+struct FineLayout {
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  static constexpr int KPITCH = D + (kBf16 ? 8 : 4);        // elements per K row
+  static constexpr int VROWS = kBf16 ? D : kTile;           // bf16: V^T rows are d
+  static constexpr int VPITCH = kBf16 ? kTile + 4 : D + 4;  // elements per V row
+  static constexpr int K_BYTES = kTile * KPITCH * sizeof(T);
+  static constexpr int V_BYTES = VROWS * VPITCH * sizeof(T);
+  static constexpr int TILE_BYTES = (K_BYTES + V_BYTES + 15) / 16 * 16;
+  // Global->register chunks (16 B) per thread.
+  static constexpr int KCH = kBf16 ? D / 32 : D / 16;
+  static constexpr int VCH = kBf16 ? D / 32 : D / 16;  // bf16: D/64 key pairs x 2 rows
+};
+
+template <typename T, int D>
+struct TileRegs {
+  uint4 kr[FineLayout<T, D>::KCH];
+  uint4 vr[FineLayout<T, D>::VCH];
+};
+
+// Issue the global loads of key tile `kt` of head base pointers kb / vb.
+template <typename T, int D>
+__device__ __forceinline__ void load_tile(TileRegs<T, D>& r, const T* __restrict__ kb,
+                                          const T* __restrict__ vb, int kt, int tid) {
+  using L = FineLayout<T, D>;
+  const int64_t key0 = static_cast<int64_t>(kt) * kTile;
+  if constexpr (L::kBf16) {
+#pragma unroll
+    for (int u = 0; u < L::KCH; ++u) {
+      const int c = tid + 256 * u, c8 = c % (D / 8), row = c / (D / 8);
+      r.kr[u] = ld16(kb + (key0 + row) * D + c8 * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < L::VCH / 2; ++u) {
+      const int it = tid + 256 * u, c8 = it % (D / 8), p = it / (D / 8);
+      r.vr[2 * u] = ld16(vb + (key0 + 2 * p) * D + c8 * 8);
+      r.vr[2 * u + 1] = ld16(vb + (key0 + 2 * p + 1) * D + c8 * 8);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < L::KCH; ++u) {
+      const int c = tid + 256 * u, c4 = c % (D / 4), row = c / (D / 4);
+      r.kr[u] = ld16(kb + (key0 + row) * D + c4 * 4);
+      r.vr[u] = ld16(vb + (key0 + row) * D + c4 * 4);
+    }
+  }
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void store_tile(const TileRegs<T, D>& r, T* ks, T* vs, int tid) {
+  using L = FineLayout<T, D>;
+  if constexpr (L::kBf16) {
+#pragma unroll
+    for (int u = 0; u < L::KCH; ++u) {
+      const int c = tid + 256 * u, c8 = c % (D / 8), row = c / (D / 8);
+      *reinterpret_cast<uint4*>(ks + row * L::KPITCH + c8 * 8) = r.kr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < L::VCH / 2; ++u) {
+      const int it = tid + 256 * u, c8 = it % (D / 8), p = it / (D / 8);
+      const uint32_t a[4] = {r.vr[2 * u].x, r.vr[2 * u].y, r.vr[2 * u].z, r.vr[2 * u].w};
+      const uint32_t b[4] = {r.vr[2 * u + 1].x, r.vr[2 * u + 1].y, r.vr[2 * u + 1].z,
+                             r.vr[2 * u + 1].w};
+      uint32_t* dst = reinterpret_cast<uint32_t*>(vs + (c8 * 8) * L::VPITCH + 2 * p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // d = c8*8 + 2e (low halves) and + 2e + 1 (high halves); keys 2p, 2p+1.
+        dst[(2 * e) * (L::VPITCH / 2)] = (a[e] & 0xFFFFu) | (b[e] << 16);
+        dst[(2 * e + 1) * (L::VPITCH / 2)] = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < L::KCH; ++u) {
+      const int c = tid + 256 * u, c4 = c % (D / 4), row = c / (D / 4);
+      *reinterpret_cast<uint4*>(ks + row * L::KPITCH + c4 * 4) = r.kr[u];
+      *reinterpret_cast<uint4*>(vs + row * L::VPITCH + c4 * 4) = r.vr[u];
+    }
+  }
+}
+
+// Per-lane online-softmax state: query row = lane % 16 of this wave; the lane
+// accumulates O[row][16*dt + 4*(lane/16) + jj].
+template <int D>
+struct RowState {
+  f32x4 acc[D / 16];
+  float m;  // running max of log2-scaled scores (identical in the row's 4 lanes)
+  float l;  // this lane's share of the running sum
+};
+
+// One key tile for one wave.  `vis` gives the visibility of the lane's 16
+// keys (bit 4*t + jj for key 16*t + 4*(lane/16) + jj).
+template <typename T, int D>
+__device__ __forceinline__ void tile_step(RowState<D>& st, const T* ks, const T* vs,
+                                          const void* qreg, uint32_t vis, float scale_log2,
+                                          int lane) {
+  using L = FineLayout<T, D>;
+  const int g = lane >> 4, c16 = lane & 15;
+  f32x4 s[4];
+  if constexpr (L::kBf16) {
+    const bf16x8* qb = static_cast<const bf16x8*>(qreg);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (16 * t + c16) * L::KPITCH + 8 * g + 32 * kk);
+        s[t] = mfma_16x16x32_bf16(a, qb[kk], s[t]);
+      }
+    }
+  } else {
+    const float* qf = static_cast<const float*>(qreg);
+    constexpr int KS = D / 4;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const float* kr = ks + (16 * t + c16) * L::KPITCH + KS * g;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) s[t] = mfma_16x16x4_f32(kr[kk], qf[kk], s[t]);
+    }
+  }
+  // Scale into log2 units and mask.
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float z = ((vis >> (4 * t + jj)) & 1u) ? s[t][jj] * scale_log2 : -INFINITY;
+      s[t][jj] = z;
+      mx = fmaxf(mx, z);
+    }
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float m_new = fmaxf(st.m, mx);
+  const float m_use = m_new == -INFINITY ? 0.f : m_new;  // all hidden so far: keep zeros
+  const float alpha = __builtin_amdgcn_exp2f(st.m - m_use);
+  st.m = m_new;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) st.acc[dt] *= alpha;
+  float lsum = 0.f;
+  if constexpr (L::kBf16) {
+    __bf16 pb[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        pb[t][jj] = f32_to_bf16(__builtin_amdgcn_exp2f(s[t][jj] - m_use));
+        lsum += static_cast<float>(pb[t][jj]);
+      }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8 bp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bp[i] = pb[2 * kk][i];
+        bp[4 + i] = pb[2 * kk + 1][i];
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const T* vr = vs + (16 * dt + c16) * L::VPITCH + 32 * kk + 4 * g;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        st.acc[dt] = mfma_16x16x32_bf16(a, bp, st.acc[dt]);
+      }
+    }
+  } else {
+    float p[4][4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        p[t][jj] = __builtin_amdgcn_exp2f(s[t][jj] - m_use);
+        lsum += p[t][jj];
+      }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const T* vr = vs + (16 * t + 4 * g + jj) * L::VPITCH + c16;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt)
+          st.acc[dt] = mfma_16x16x4_f32(vr[16 * dt], p[t][jj], st.acc[dt]);
+      }
+  }
+  st.l = st.l * alpha + lsum;
+}
+
+template <typename T, int D, bool STATIC, bool CAUSAL>
+__global__ __launch_bounds__(256) void sparse_flash_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    float* __restrict__ out, const int32_t* __restrict__ idx, int topk,
+    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
+    const uint64_t* __restrict__ rowmask, int64_t nnz, int n, float scale_log2) {
+  using L = FineLayout<T, D>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* ks = reinterpret_cast<T*>(smem);
+  T* vs = reinterpret_cast<T*>(smem + L::K_BYTES);
+  uint64_t* rm = reinterpret_cast<uint64_t*>(smem + L::TILE_BYTES);  // dynamic: per-block row bits
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int nqt = n / kTile;
+  const int nb = nqt;
+  const int64_t bh = blockIdx.x / nqt;
+  int qt = static_cast<int>(blockIdx.x % nqt);
+  if (CAUSAL) qt = nqt - 1 - qt;  // heaviest query tiles first
+  const int64_t tile_row = bh * n + static_cast<int64_t>(qt) * kTile;
+  const T* kb = k + bh * static_cast<int64_t>(n) * D;
+  const T* vb = v + bh * static_cast<int64_t>(n) * D;
+
+  // ---- the tile list
+  int nlist = 0;
+  int64_t list_base = 0;
+  int32_t* list = nullptr;
+  if constexpr (!STATIC) {
+    const int nbc = CAUSAL ? qt + 1 : nb;  // blocks that can be visible to this tile
+    list = reinterpret_cast<int32_t*>(rm + nb);
+    int* count = reinterpret_cast<int*>(list + nb);
+    for (int c = tid; c < nbc; c += 256) rm[c] = 0ull;
+    __syncthreads();
+    const int32_t* ib = idx + tile_row * topk;
+    for (int e = tid; e < kTile * topk; e += 256) {
+      const int b = ib[e];
+      if (b >= 0 && b < nbc) atomicOr(reinterpret_cast<unsigned long long*>(&rm[b]), 1ull << (e / topk));
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int cnt = 0;
+      for (int c0 = 0; c0 < nbc; c0 += 64) {
+        const int c = c0 + lane;
+        const bool f = c < nbc && rm[c] != 0ull;
+        const uint64_t m = ballot(f);
+        if (f) list[cnt + static_cast<int>(lanes_below(m))] = c;
+        cnt += __popcll(m);
+      }
+      if (lane == 0) *count = cnt;
+    }
+    __syncthreads();
+    nlist = *count;
+  } else {
+    int64_t s0 = row_ptr[qt], s1 = row_ptr[qt + 1];
+    if (s0 < 0) s0 = 0;
+    if (s1 > nnz) s1 = nnz;
+    list_base = s0;
+    nlist = s1 > s0 ? static_cast<int>(s1 - s0) : 0;
+  }
+  auto tile_at = [&](int it) -> int {
+    int kt;
+    if constexpr (STATIC) kt = col[list_base + it];
+    else kt = list[it];
+    return (kt >= 0 && kt < nqt) ? kt : -1;
+  };
+
+  // ---- this lane's query row in registers (B operand of S^T = K Q^T)
+  const int64_t qrow = tile_row + wave * 16 + c16;
+  const int qlocal = wave * 16 + c16;
+  union {
+    bf16x8 b[D / 32];
+    float f[D / 4];
+  } qreg;
+  if constexpr (L::kBf16) {
+    const T* qp = q + qrow * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) qreg.b[kk] = as_bf16x8(ld16(qp + 32 * kk));
+  } else {
+    const T* qp = q + qrow * D + (D / 4) * g;
+#pragma unroll
+    for (int e = 0; e < D / 4; e += 4) {
+      const uint4 u = ld16(qp + e);
+      qreg.f[e] = __uint_as_float(u.x);
+      qreg.f[e + 1] = __uint_as_float(u.y);
+      qreg.f[e + 2] = __uint_as_float(u.z);
+      qreg.f[e + 3] = __uint_as_float(u.w);
+    }
+  }
+
+  RowState<D> st;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  TileRegs<T, D> regs;
+  int cur = nlist > 0 ? tile_at(0) : -1;
+  if (cur >= 0) load_tile<T, D>(regs, kb, vb, cur, tid);
+  for (int it = 0; it < nlist; ++it) {
+    __syncthreads();
+    if (cur >= 0) store_tile<T, D>(regs, ks, vs, tid);
+    __syncthreads();
+    const int nxt = it + 1 < nlist ? tile_at(it + 1) : -1;
+    if (nxt >= 0) load_tile<T, D>(regs, kb, vb, nxt, tid);
+    if (cur >= 0) {
+      uint32_t vis;
+      bool any;
+      if constexpr (!STATIC) {
+        const uint64_t bits = rm[cur];
+        any = ((bits >> (16 * wave)) & 0xFFFFull) != 0ull;
+        vis = ((bits >> qlocal) & 1ull) ? 0xFFFFu : 0u;
+        if (CAUSAL && cur == qt) {
+          // diagonal tile: key 16t + 4g + jj visible iff it is <= the query
+          uint32_t cm = 0u;
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              if (16 * t + 4 * g + jj <= qlocal) cm |= 1u << (4 * t + jj);
+          vis &= cm;
+        }
+      } else {
+        uint64_t m64 = ~0ull;
+        if (rowmask) m64 = rowmask[(list_base + it) * kTile + qlocal];
+        any = ballot(m64 != 0ull) != 0ull;
+        vis = 0u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj)
+            vis |= static_cast<uint32_t>((m64 >> (16 * t + 4 * g + jj)) & 1ull) << (4 * t + jj);
+      }
+      if (any) tile_step<T, D>(st, ks, vs, &qreg, vis, scale_log2, lane);
+    }
+    cur = nxt;
+  }
+
+  // ---- normalise and store
+  float lt = st.l + __shfl_xor(st.l, 16);
+  lt += __shfl_xor(lt, 32);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  float* op = out + qrow * D + 4 * g;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const f32x4 a = st.acc[dt] * inv;
+    *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(a[0], a[1], a[2], a[3]);
+  }
+}
+
+template <typename T, int D, bool STATIC, bool CAUSAL>
+hipError_t launch_one(const void* q, const void* k, const void* v, float* out, const int32_t* idx,
+                      int topk, const int32_t* row_ptr, const int32_t* col,
+                      const uint64_t* rowmask, int64_t nnz, int64_t bh, int n, float scale,
+                      hipStream_t s) {
+  using L = FineLayout<T, D>;
+  const int nb = n / kTile;
+  size_t smem = L::TILE_BYTES;
+  if (!STATIC) smem += static_cast<size_t>(nb) * 8 + static_cast<size_t>(nb) * 4 + 16;
+  const auto kern = sparse_flash_kernel<T, D, STATIC, CAUSAL>;
+  if (smem > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(smem));
+    if (e != hipSuccess) return e;
+  }
+  const dim3 grid(static_cast<unsigned>(bh * (n / kTile)));
+  hipLaunchKernelGGL(kern, grid, dim3(256), smem, s, static_cast<const T*>(q),
+                     static_cast<const T*>(k), static_cast<const T*>(v), out, idx, topk, row_ptr,
+                     col, rowmask, nnz, n, scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t dispatch_dynamic(const void* q, const void* k, const void* v, float* out,
+                            const int32_t* idx, int64_t bh, int n, int topk, float scale,
+                            int causal, hipStream_t s) {
+  return causal ? launch_one<T, D, false, true>(q, k, v, out, idx, topk, nullptr, nullptr, nullptr,
+                                                0, bh, n, scale, s)
+                : launch_one<T, D, false, false>(q, k, v, out, idx, topk, nullptr, nullptr,
+                                                 nullptr, 0, bh, n, scale, s);
+}
+
+}  // namespace
+
+hipError_t launch_sparse_flash_dynamic(const void* q, const void* k, const void* v, float* out,
+                                       const int32_t* idx, int64_t bh, int n, int d, int topk,
+                                       float scale, int causal, bsa_dtype dtype,
+                                       hipStream_t stream) {
+  if (dtype == BSA_BF16)
+    return d == 64 ? dispatch_dynamic<bf16_bits, 64>(q, k, v, out, idx, bh, n, topk, scale, causal, stream)
+                   : dispatch_dynamic<bf16_bits, 128>(q, k, v, out, idx, bh, n, topk, scale, causal, stream);
+  return d == 64 ? dispatch_dynamic<float, 64>(q, k, v, out, idx, bh, n, topk, scale, causal, stream)
+                 : dispatch_dynamic<float, 128>(q, k, v, out, idx, bh, n, topk, scale, causal, stream);
+}
+
+hipError_t launch_sparse_flash_static(const void* q, const void* k, const void* v, float* out,
+                                      const int32_t* row_ptr, const int32_t* col,
+                                      const uint64_t* rowmask, int64_t nnz, int64_t bh, int n,
+                                      int d, float scale, bsa_dtype dtype, hipStream_t stream) {
+  if (dtype == BSA_BF16)
+    return d == 64 ? launch_one<bf16_bits, 64, true, false>(q, k, v, out, nullptr, 0, row_ptr, col,
+                                                            rowmask, nnz, bh, n, scale, stream)
+                   : launch_one<bf16_bits, 128, true, false>(q, k, v, out, nullptr, 0, row_ptr, col,
+                                                             rowmask, nnz, bh, n, scale, stream);
+  return d == 64 ? launch_one<float, 64, true, false>(q, k, v, out, nullptr, 0, row_ptr, col,
+                                                      rowmask, nnz, bh, n, scale, stream)
+                 : launch_one<float, 128, true, false>(q, k, v, out, nullptr, 0, row_ptr, col,
+                                                       rowmask, nnz, bh, n, scale, stream);
+}
+
+}  // namespace bsa

@@ -1,0 +1,221 @@
+/*
+ * bsa.h -- C ABI of libbsa, a two-stage, content-dependent block-sparse
+ * attention forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * The method (nishantmodi.me post "sparse-attention-triton-bench"):
+ *   Stage 1 ("Two-stage block indexer", "Stage 1: coarse scoring"): split the
+ *     keys into blocks of B, mean-pool each block into a representative, score
+ *     every query against every representative, and keep each query's top-k
+ *     blocks.  The choice is made at run time, per query and per head.
+ *   Stage 2 ("Stage 2: fine attention", "The Triton kernel"): softmax
+ *     attention of each query over only the k*B keys of its selected blocks,
+ *     with an online softmax (running max m, running sum l, unnormalised
+ *     accumulator) so that no score matrix is written to memory.
+ * The static mode runs the same fine kernel over a precomputed list of active
+ * 64x64 (query tile, key tile) pairs (yayme/CUDA-kernel README: the tile
+ * list is built on the CPU and the kernel walks it instead of scanning a
+ * mask; masked keys take no part, i.e. score -inf).
+ *
+ * Conventions shared by every entry point:
+ *  - Tensors are row-major [batch][heads][n][d] with d innermost, contiguous,
+ *    16-byte aligned, in device memory owned by the caller.  The library never
+ *    frees caller memory.
+ *  - dtype BSA_BF16: q, k, v hold bfloat16 bit patterns (uint16).  BSA_FP32:
+ *    float32.  Outputs are always float32; block indices are always int32.
+ *  - "stream" is a hipStream_t (NULL = the null stream).  Work is enqueued on
+ *    it and the call returns without waiting: BSA_OK means "validated and
+ *    enqueued".  A device fault surfaces at the caller's next synchronisation.
+ *  - Validation is synchronous and happens before anything is enqueued; a
+ *    failing call enqueues nothing, returns a specific status and leaves a
+ *    message readable with bsa_last_error().  Calls never abort or print.
+ *  - A handle is not thread-safe: use one handle per host thread / stream.
+ *    Two calls on one handle that overlap on different streams race on the
+ *    handle's workspace.
+ *  - Supported today: block (= tile) 64; d in {64, 128}; n a multiple of 64;
+ *    n/64 <= 2048 for the dynamic path.  Anything else returns
+ *    BSA_ERR_UNSUPPORTED.
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct bsa_handle_s* bsa_handle;
+
+typedef enum {
+  BSA_OK = 0,
+  BSA_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad scale, misaligned pointer, bad CSR */
+  BSA_ERR_UNSUPPORTED = 2,   /* valid request outside what is implemented (d, block, n) */
+  BSA_ERR_NO_DEVICE = 3,     /* no HIP device, or the device is not gfx950 */
+  BSA_ERR_OUT_OF_MEMORY = 4, /* workspace allocation failed */
+  BSA_ERR_LAUNCH = 5         /* the HIP runtime refused a launch or an event/copy call */
+} bsa_status;
+
+typedef enum { BSA_FP32 = 0, BSA_BF16 = 1 } bsa_dtype;
+
+/* Stages, for the per-stage timer below. */
+typedef enum {
+  BSA_STAGE_POOL = 0,   /* block_pool       */
+  BSA_STAGE_COARSE = 1, /* coarse_score     */
+  BSA_STAGE_TOPK = 2,   /* topk_select      */
+  BSA_STAGE_FINE = 3,   /* sparse_flash_fwd */
+  BSA_NUM_STAGES = 4
+} bsa_stage;
+
+/* Tunables for bsa_set_option. */
+typedef enum {
+  /* Upper bound in bytes of the fp32 coarse-score panel that stage 1 keeps at
+   * once; queries are processed in chunks of at most this many bytes of panel.
+   * Default 128 MiB.  Minimum one 64-query tile. */
+  BSA_OPT_PANEL_CHUNK_BYTES = 0
+} bsa_option;
+
+/* ----------------------------------------------------------- lifetime -- */
+
+/* Create a handle bound to HIP device `device`.  *out receives the handle.
+ * BSA_ERR_NO_DEVICE if there is no HIP device, `device` is out of range, or
+ * the device is not gfx950.  The library loads (and this call fails cleanly)
+ * on a machine without a GPU. */
+bsa_status bsa_create(int device, bsa_handle* out);
+
+/* Free the handle and its workspace.  The caller must make sure no work that
+ * uses the handle is still running.  NULL is accepted. */
+bsa_status bsa_destroy(bsa_handle h);
+
+/* Static text for a status.  Never NULL. */
+const char* bsa_status_string(bsa_status s);
+
+/* Detail of the last failing call on h (or, for h == NULL, of the last
+ * failing call on this thread that had no handle).  Never NULL. */
+const char* bsa_last_error(bsa_handle h);
+
+/* Set a tunable (see bsa_option).  BSA_ERR_INVALID_ARG for an unknown option
+ * or a value out of range. */
+bsa_status bsa_set_option(bsa_handle h, int option, int64_t value);
+
+/* Bytes of device workspace the handle holds right now (repr, panel chunk,
+ * internal index buffer). */
+bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes);
+
+/* --------------------------------------------------- dynamic forward -- */
+
+/* Both stages: block_pool -> coarse_score -> topk_select -> sparse_flash_fwd.
+ *  q, k, v        device, [batch][heads][n][d], dtype.
+ *  out            device, float32 [batch][heads][n][d].
+ *  block_idx_out  device, int32 [batch][heads][n][topk] or NULL.  When given,
+ *                 it receives each query's selected blocks in ascending order,
+ *                 padded with -1 (k_eff = min(topk, #candidate blocks)).  When
+ *                 NULL the handle uses an internal buffer.
+ *  block          key-block size B; must be 64.
+ *  topk           k >= 1; k above the number of candidate blocks keeps them all.
+ *  scale          softmax scale (finite, > 0), typically 1/sqrt(d).
+ *  causal         0: every block is a candidate.  1: candidates are the blocks
+ *                 up to the query's own block, the own block is always kept
+ *                 (as one of the k), and inside kept blocks only keys j <= i
+ *                 are visible.
+ * Coarse scores are q . mean(block keys), unscaled; equal scores go to the
+ * lower block index, and -0 equals +0. */
+bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const void* v,
+                       float* out, int32_t* block_idx_out, int batch, int heads,
+                       int n, int d, bsa_dtype dtype, int block, int topk,
+                       float scale, int causal, void* stream);
+
+/* Stage 2 alone on caller-supplied selections (same layout as block_idx_out;
+ * each row must hold distinct indices; entries outside [0, n/block), and in
+ * causal mode blocks after the query's own block, count as padding).  Useful
+ * to test or reuse a selection. */
+bsa_status bsa_fine_forward(bsa_handle h, const void* q, const void* k,
+                            const void* v, float* out, const int32_t* block_idx,
+                            int batch, int heads, int n, int d, bsa_dtype dtype,
+                            int block, int topk, float scale, int causal,
+                            void* stream);
+
+/* ---------------------------------------------------- stage 1 pieces -- */
+
+/* block_pool: repr_out[b][h][beta][:] = mean of keys beta*B .. beta*B+B-1, as
+ * float32 [batch][heads][n/B][d]. */
+bsa_status bsa_block_pool(bsa_handle h, const void* k, float* repr_out,
+                          int batch, int heads, int n, int d, bsa_dtype dtype,
+                          int block, void* stream);
+
+/* coarse_score: panel_out[b][h][i][beta] = q_i . repr[beta], float32
+ * [batch][heads][n][n/B].  repr is float32 as produced by bsa_block_pool.  In
+ * causal mode entries with beta > i/B are unspecified. */
+bsa_status bsa_coarse_score(bsa_handle h, const void* q, const float* repr,
+                            float* panel_out, int batch, int heads, int n, int d,
+                            bsa_dtype dtype, int block, int causal, void* stream);
+
+/* topk_select: per row of the float32 panel [batch][heads][n][n/B], the
+ * selection exactly as described for bsa_forward, into block_idx_out int32
+ * [batch][heads][n][topk]. */
+bsa_status bsa_topk_select(bsa_handle h, const float* panel,
+                           int32_t* block_idx_out, int batch, int heads, int n,
+                           int block, int topk, int causal, void* stream);
+
+/* ------------------------------------------------------ static forward -- */
+
+/* Fine attention over a precomputed tile list, the same for every batch and
+ * head.  Query tile t (rows 64t .. 64t+63) visits key tiles
+ * tile_col[tile_row_ptr[t] .. tile_row_ptr[t+1]) in that order.
+ *  tile_row_ptr  device int32 [n/64 + 1], non-decreasing, tile_row_ptr[0] = 0.
+ *  tile_col      device int32 [nnz], key-tile ids in [0, n/64).
+ *  tile_rowmask  device uint64 [nnz][64] or NULL: bit c of entry (p, r) says
+ *                whether query row r of the tile sees key c of tile p.  NULL
+ *                means every listed tile is fully visible.
+ *  nnz           number of listed tiles (= tile_row_ptr[n/64]).
+ * Device-side list content is not read on the host; the kernel skips entries
+ * outside the stated ranges instead of reading out of bounds.  Use
+ * bsa_tiles_validate on the host copy to check a list.  A row that sees no
+ * key gets zeros. */
+bsa_status bsa_forward_static(bsa_handle h, const void* q, const void* k,
+                              const void* v, float* out, int batch, int heads,
+                              int n, int d, bsa_dtype dtype,
+                              const int32_t* tile_row_ptr,
+                              const int32_t* tile_col,
+                              const uint64_t* tile_rowmask, int64_t nnz,
+                              float scale, void* stream);
+
+/* Host helper: tile list of a dense element mask.  mask is host uint8 [n][n]
+ * (nonzero = visible).  row_ptr: host int32 [n/tile + 1].  col: host int32
+ * [*nnz_inout] or NULL; rowmask: host uint64 [*nnz_inout][tile] or NULL.
+ * With col == NULL only counts: *nnz_inout receives the number of active tiles.
+ * Otherwise *nnz_inout must be >= that number on entry and receives it on
+ * return.  tile must be 64; n a multiple of 64. */
+bsa_status bsa_tiles_from_mask(const uint8_t* mask, int n, int tile,
+                               int32_t* row_ptr, int32_t* col,
+                               uint64_t* rowmask, int64_t* nnz_inout);
+
+/* Host helper: the same for the window+stride pattern (query i sees key j iff
+ * |i-j| <= window or j mod stride == 0) without materialising the mask. */
+bsa_status bsa_tiles_window_stride(int n, int window, int stride, int tile,
+                                   int32_t* row_ptr, int32_t* col,
+                                   uint64_t* rowmask, int64_t* nnz_inout);
+
+/* Host helper: BSA_OK iff (row_ptr, col) is a well-formed list for n and tile:
+ * row_ptr[0] == 0, non-decreasing, row_ptr[n/tile] == nnz, every col in
+ * [0, n/tile). */
+bsa_status bsa_tiles_validate(const int32_t* row_ptr, const int32_t* col,
+                              int64_t nnz, int n, int tile);
+
+/* ------------------------------------------------------------ timing -- */
+
+/* Enable (1) or disable (0) per-stage timing.  While enabled every kernel
+ * launch is bracketed by two HIP events on the launch stream. */
+bsa_status bsa_profile_enable(bsa_handle h, int on);
+
+/* Wait for the recorded events and return, per bsa_stage, the summed kernel
+ * time in milliseconds (ms[BSA_NUM_STAGES]) and the number of launches
+ * (launches[BSA_NUM_STAGES], may be NULL).  reset != 0 clears the record. */
+bsa_status bsa_profile_read(bsa_handle h, double* ms, int64_t* launches,
+                            int reset);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

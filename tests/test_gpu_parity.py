@@ -1,0 +1,390 @@
+"""GPU parity: every stage of the HIP path against the fp64 oracle, through the
+C ABI (Python binding).  Marked gpu; run on an MI355X.
+
+Acceptance (per query row):
+  * block indices equal the oracle's bit for bit, except when the oracle's
+    k-th and (k+1)-th coarse scores lie within 1e-4 relative of each other
+    (tie band); there the GPU set must still be a valid top-k of the oracle's
+    scores (distinct candidates, every kept block scoring >= s_{k+1} and every
+    dropped candidate <= s_k);
+  * outputs within 1e-2 (bf16 inputs) / 1e-4 (fp32 inputs) max abs of the
+    oracle's fine attention over the GPU's own selection.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TOL = {"bf16": 1e-2, "fp32": 1e-4}
+TIE_REL = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def bsa():
+    import content_dependent_block_amd as m
+    lib = m.BlockSparseAttention(0)
+    yield m, lib
+    lib.close()
+
+
+def to_dev(inp, dtype):
+    if dtype == "bf16":
+        conv = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+        return conv(inp.q_bits), conv(inp.k_bits), conv(inp.v_bits)
+    return (torch.from_numpy(inp.q).cuda(), torch.from_numpy(inp.k).cuda(),
+            torch.from_numpy(inp.v).cuda())
+
+
+def check_selection(gpu_idx, ora_idx, kth, nxt, scores, rows, n, block, causal):
+    """Returns the boolean mask of tie-band rows; asserts the rest match."""
+    band = np.zeros(rows.size, dtype=bool)
+    fin = np.isfinite(kth) & np.isfinite(nxt)
+    band[fin] = np.abs(kth[fin] - nxt[fin]) <= TIE_REL * np.maximum(np.abs(kth[fin]), np.abs(nxt[fin]))
+    same = (gpu_idx == ora_idx).all(axis=1)
+    bad = ~same & ~band
+    assert not bad.any(), (
+        f"{bad.sum()} rows select different blocks outside the tie band, e.g. row {rows[bad][0]}: "
+        f"gpu {gpu_idx[bad][0].tolist()} oracle {ora_idx[bad][0].tolist()}")
+    for r in np.nonzero(~same)[0]:
+        g = gpu_idx[r]
+        keff = int((ora_idx[r] >= 0).sum())
+        sel = g[g >= 0]
+        assert sel.size == keff and np.unique(sel).size == keff and (np.diff(sel) > 0).all()
+        qb = (rows[r] % n) // block
+        cand = np.arange(qb + 1 if causal else scores.shape[1])
+        assert np.isin(sel, cand).all()
+        s = scores[r].copy()
+        if causal:
+            s[qb] = np.inf
+        assert (s[sel] >= nxt[r]).all()
+        dropped = np.setdiff1d(cand, sel)
+        assert (s[dropped] <= kth[r]).all()
+    return band
+
+
+def sample_rows(w, count, seed=0, extra=()):
+    total = w.bh * w.n
+    if count >= total:
+        return np.arange(total, dtype=np.int64)
+    rng = np.random.default_rng(seed)
+    r = set(rng.choice(total, size=count, replace=False).tolist())
+    r.update(int(x) for x in extra)
+    return np.array(sorted(r), dtype=np.int64)
+
+
+def run_forward(m, lib, w, inp, *, topk=None, causal=None, n=None):
+    q, k, v = to_dev(inp, w.dtype)
+    topk = topk or w.topk
+    causal = w.causal if causal is None else causal
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    idx = torch.empty(q.shape[:3] + (topk,), dtype=torch.int32, device="cuda")
+    m.bsa_forward(lib.handle, q, k, v, out, idx, topk=topk, scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), idx.cpu().numpy()
+
+
+def end_to_end(m, lib, w, inp, rows, *, topk=None, causal=None):
+    topk = topk or w.topk
+    causal = w.causal if causal is None else causal
+    b, h, n, d = inp.q.shape
+    say(f"[gpu] bsa_forward {w.name} b={b} h={h} n={n} d={d} k={topk} causal={causal} dtype={w.dtype}")
+    out, idx = run_forward(m, lib, w, inp, topk=topk, causal=causal)
+    out = out.reshape(-1, d)[rows]
+    gidx = idx.reshape(-1, topk)[rows]
+    r = oracle.pool(inp.k, w.block)
+    s = oracle.scores(inp.q, r, w.block, rows)
+    oidx, kth, nxt = oracle.topk(s, n, w.block, topk, causal, rows)
+    band = check_selection(gidx, oidx, kth, nxt, s, rows, n, w.block, causal)
+    ref = oracle.attend(inp.q, inp.k, inp.v, gidx, w.block, causal, w.scale, rows)
+    err = np.abs(out - ref).max()
+    say(f"    rows={rows.size} tie-band rows={int(band.sum())} "
+        f"index mismatches={int((gidx != oidx).any(axis=1).sum())} max|err|={err:.3g}")
+    assert err <= TOL[w.dtype]
+    return out, gidx, band
+
+
+# ------------------------------------------------------------- block_pool --
+@pytest.mark.parametrize("name,dd", [("tiny_fp32_n1k", 64), ("dyn_bf16_n4k", 64),
+                                     ("dyn_bf16_n4k", 128), ("tiny_fp32_n1k", 128)])
+def test_block_pool(bsa, name, dd):
+    m, lib = bsa
+    w = W.WORKLOADS[name]
+    w = W.Workload(w.name, w.batch, w.heads, w.n, dd, w.dtype, w.seed, topk=w.topk,
+                   key_offsets=w.key_offsets)
+    inp = W.generate(w)
+    say(f"[gpu] bsa_block_pool {name} d={dd}")
+    _, k, _ = to_dev(inp, w.dtype)
+    rep = torch.empty((w.batch, w.heads, w.nb, dd), dtype=torch.float32, device="cuda")
+    m.bsa_block_pool(lib.handle, k, rep)
+    torch.cuda.synchronize()
+    ref = oracle.pool(inp.k, w.block).reshape(rep.shape)
+    np.testing.assert_allclose(rep.cpu().numpy(), ref, rtol=0, atol=2e-6)
+
+
+# ----------------------------------------------------------- coarse_score --
+@pytest.mark.parametrize("name,causal", [("tiny_fp32_n1k", False), ("dyn_bf16_n4k", False),
+                                         ("dyn_bf16_n4k", True)])
+def test_coarse_score(bsa, name, causal):
+    """GPU scores from the oracle's representatives (rounded to fp32) against
+    the oracle's fp64 scores.  Bound: the 3-term bf16 split carries r to
+    ~2^-24 relative and the MFMA accumulates in fp32, so the error is a few
+    2^-24 of sum_d |q_d r_d| (1e-6 of it is asserted)."""
+    m, lib = bsa
+    w = W.WORKLOADS[name]
+    inp = W.generate(w)
+    say(f"[gpu] bsa_coarse_score {name} causal={causal}")
+    q, _, _ = to_dev(inp, w.dtype)
+    r = oracle.pool(inp.k, w.block)
+    r32 = r.astype(np.float32)
+    rep = torch.from_numpy(r32.reshape(w.batch, w.heads, w.nb, w.d)).cuda()
+    panel = torch.full((w.batch, w.heads, w.n, w.nb), float("nan"), dtype=torch.float32, device="cuda")
+    m.bsa_coarse_score(lib.handle, q, rep, panel, causal=causal)
+    torch.cuda.synchronize()
+    got = panel.cpu().numpy().reshape(-1, w.nb)
+    ref = oracle.scores(inp.q, r32.astype(np.float64), w.block)
+    qa = np.abs(inp.q.reshape(w.bh, w.n, w.d)).astype(np.float64)
+    ra = np.abs(r32.reshape(w.bh, w.nb, w.d)).astype(np.float64)
+    bound = np.concatenate([qa[h] @ ra[h].T for h in range(w.bh)])
+    valid = np.ones_like(got, dtype=bool)
+    if causal:
+        i = np.arange(w.bh * w.n) % w.n
+        valid = np.arange(w.nb)[None, :] <= (i // w.block)[:, None]
+    err = np.abs(got - ref)[valid]
+    assert (err <= 1e-6 * bound[valid] + 1e-7).all(), f"max err {err.max():.3g}"
+
+
+# ------------------------------------------------------------ topk_select --
+@pytest.mark.parametrize("nb,k,causal", [(16, 4, False), (16, 32, False), (64, 16, False),
+                                         (512, 16, False), (2048, 32, False), (128, 5, True),
+                                         (2048, 32, True), (64, 1, True)])
+def test_topk_select_bit_exact(bsa, nb, k, causal):
+    """topk_select on a float32 panel with many exact ties and signed zeros,
+    against the oracle's selection on the same float32 values."""
+    m, lib = bsa
+    n = nb * 64
+    rows_total = min(4096, n)
+    rng = np.random.default_rng(nb * 31 + k)
+    panel = np.round(rng.standard_normal((1, 1, rows_total, nb)) * 4).astype(np.float32) / 4
+    panel[..., ::7] = -0.0
+    panel[..., 3::11] = 0.0
+    # place the rows at the end of the sequence so causal rows see many blocks
+    say(f"[gpu] bsa_topk_select nb={nb} k={k} causal={causal}")
+    full = np.zeros((1, 1, n, nb), dtype=np.float32)
+    full[:, :, n - rows_total:] = panel
+    dev = torch.from_numpy(full).cuda()
+    idx = torch.empty((1, 1, n, k), dtype=torch.int32, device="cuda")
+    m.bsa_topk_select(lib.handle, dev, idx, causal=causal)
+    torch.cuda.synchronize()
+    rows = np.arange(n - rows_total, n, dtype=np.int64)
+    got = idx.cpu().numpy().reshape(n, k)[rows]
+    ref, _, _ = oracle.topk(full.reshape(n, nb)[rows].astype(np.float64), n, 64, k, causal, rows)
+    np.testing.assert_array_equal(got, ref)
+
+
+# --------------------------------------------------------- fine attention --
+@pytest.mark.parametrize("name,causal,dd", [("tiny_fp32_n1k", False, 64), ("dyn_bf16_n4k", False, 64),
+                                            ("dyn_bf16_n4k", True, 64), ("dyn_bf16_n4k", False, 128),
+                                            ("tiny_fp32_n1k", True, 128)])
+def test_fine_forward_on_oracle_indices(bsa, name, causal, dd):
+    m, lib = bsa
+    w0 = W.WORKLOADS[name]
+    w = W.Workload(w0.name, w0.batch, w0.heads, w0.n, dd, w0.dtype, w0.seed, topk=w0.topk,
+                   causal=causal, key_offsets=w0.key_offsets)
+    inp = W.generate(w)
+    rows = sample_rows(w, 4096, seed=1)
+    oidx_rows, _, _ = oracle.select(inp.q, inp.k, w.block, w.topk, causal)
+    say(f"[gpu] bsa_fine_forward {name} causal={causal} d={dd}")
+    q, k, v = to_dev(inp, w.dtype)
+    idx = torch.from_numpy(oidx_rows.reshape(w.batch, w.heads, w.n, w.topk)).cuda()
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    m.bsa_fine_forward(lib.handle, q, k, v, out, idx, scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().reshape(-1, dd)[rows]
+    ref = oracle.attend(inp.q, inp.k, inp.v, oidx_rows[rows], w.block, causal, w.scale, rows)
+    assert np.abs(got - ref).max() <= TOL[w.dtype]
+
+
+# ------------------------------------------------------------ end to end --
+@pytest.mark.parametrize("name", ["tiny_fp32_n1k", "dyn_bf16_n4k"])
+def test_forward_small_workloads_all_rows(bsa, name):
+    m, lib = bsa
+    w = W.WORKLOADS[name]
+    inp = W.generate(w)
+    end_to_end(m, lib, w, inp, np.arange(w.bh * w.n, dtype=np.int64))
+
+
+def test_forward_headline_sampled(bsa):
+    """N=32768, 8 heads, bf16, k=16 in the launch configuration the benchmark
+    times; sampled rows against the oracle, plus properties of every row."""
+    m, lib = bsa
+    w = W.WORKLOADS["dyn_bf16_n32k"]
+    inp = W.generate(w)
+    rows = sample_rows(w, 3000, seed=2, extra=[0, 63, w.n - 1, w.n, w.bh * w.n - 1])
+    end_to_end(m, lib, w, inp, rows)
+    _, idx = run_forward(m, lib, w, inp)
+    idx = idx.reshape(-1, w.topk)
+    assert (np.diff(idx, axis=1) > 0).all() and idx.min() >= 0 and idx.max() < w.nb
+
+
+def test_forward_causal_long_sampled(bsa):
+    """N=131072, 8 heads, D=128, bf16, k=32, causal: all rows of the first 32
+    query blocks of two heads plus random rows; every row's properties."""
+    m, lib = bsa
+    w = W.WORKLOADS["causal_bf16_n128k"]
+    inp = W.generate(w)
+    early = np.concatenate([h * w.n + np.arange(32 * 64) for h in (0, 5)])
+    rows = sample_rows(w, 1500, seed=4, extra=early)
+    end_to_end(m, lib, w, inp, rows)
+    _, idx = run_forward(m, lib, w, inp)
+    idx = idx.reshape(w.bh, w.n, w.topk)
+    qb = np.arange(w.n) // 64
+    keff = np.minimum(w.topk, qb + 1)
+    for h in range(w.bh):
+        valid = idx[h] >= 0
+        assert (valid.sum(axis=1) == keff).all()
+        assert ((idx[h] == qb[:, None]).any(axis=1)).all()   # own block kept
+        assert (np.where(valid, idx[h], 0) <= qb[:, None]).all()
+
+
+def test_static_window_stride(bsa):
+    m, lib = bsa
+    w = W.WORKLOADS["static_fp32_n8k"]
+    inp = W.generate(w)
+    rp, col, rm = m.bsa_tiles_window_stride(w.n, w.window, w.stride)
+    say(f"[gpu] bsa_forward_static {w.name} nnz={col.size}")
+    q, k, v = to_dev(inp, w.dtype)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    m.bsa_forward_static(lib.handle, q, k, v, out, torch.from_numpy(rp).cuda(),
+                         torch.from_numpy(col).cuda(), torch.from_numpy(rm.view(np.int64)).cuda(),
+                         scale=w.scale)
+    torch.cuda.synchronize()
+    mask = oracle.window_stride_mask(w.n, w.window, w.stride)
+    ref = oracle.attend_mask(inp.q, inp.k, inp.v, mask, w.scale)
+    err = np.abs(out.cpu().numpy().reshape(-1, w.d) - ref).max()
+    say(f"    max|err|={err:.3g}")
+    assert err <= TOL["fp32"]
+
+
+# ------------------------------------------------------------- edge cases --
+@pytest.mark.parametrize("case", [
+    dict(batch=1, heads=1, n=1024, d=64, dtype="fp32", topk=32, causal=False),   # k > n/64: all blocks, -1 pad
+    dict(batch=2, heads=1, n=1024, d=64, dtype="bf16", topk=1, causal=False),    # k = 1, batch 2
+    dict(batch=1, heads=1, n=64, d=64, dtype="bf16", topk=4, causal=True),       # single block, causal
+    dict(batch=1, heads=2, n=2048, d=128, dtype="bf16", topk=5, causal=True),    # D=128 causal, small k
+    dict(batch=1, heads=3, n=2048, d=64, dtype="fp32", topk=7, causal=True),     # fp32 causal
+    dict(batch=2, heads=1, n=1024, d=128, dtype="fp32", topk=3, causal=False),   # fp32 D=128
+    dict(batch=1, heads=2, n=4096, d=64, dtype="bf16", topk=64, causal=False),   # k = n/64: dense
+])
+def test_forward_edge_cases(bsa, case):
+    m, lib = bsa
+    w = W.Workload("edge", case["batch"], case["heads"], case["n"], case["d"], case["dtype"],
+                   seed=77, topk=case["topk"], causal=case["causal"],
+                   key_offsets=case["dtype"] == "bf16")
+    inp = W.generate(w)
+    end_to_end(m, lib, w, inp, np.arange(w.bh * w.n, dtype=np.int64))
+
+
+def test_static_edge_cases(bsa):
+    """Static list with empty query tiles (zeros), no rowmask (full tiles) and a
+    dense-mask source; bf16 inputs; batch 2."""
+    m, lib = bsa
+    n, d = 1024, 64
+    w = W.Workload("static_edge", 2, 1, n, d, "bf16", seed=9, window=8, stride=300)
+    inp = W.generate(w)
+    rng = np.random.default_rng(5)
+    mask = (rng.random((n, n)) < 0.02).astype(np.uint8)
+    mask[128:256] = 0                       # two empty query tiles
+    mask[512:576, 64:128] = 1               # one fully visible tile
+    rp, col, rm = m.bsa_tiles_from_mask(mask)
+    assert m.bsa_tiles_validate(rp, col, n)
+    q, k, v = to_dev(inp, "bf16")
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    say(f"[gpu] bsa_forward_static random mask n={n} nnz={col.size}")
+    m.bsa_forward_static(lib.handle, q, k, v, out, torch.from_numpy(rp).cuda(),
+                         torch.from_numpy(col).cuda(), torch.from_numpy(rm.view(np.int64)).cuda(),
+                         scale=0.125)
+    torch.cuda.synchronize()
+    ref = oracle.attend_mask(inp.q, inp.k, inp.v, mask, 0.125)
+    got = out.cpu().numpy().reshape(-1, d)
+    assert np.abs(got - ref).max() <= TOL["bf16"]
+    assert (got.reshape(2, n, d)[:, 128:256] == 0).all()
+    # no rowmask: every listed tile fully visible
+    full = np.zeros((n, n), dtype=np.uint8)
+    for t in range(n // 64):
+        for kt in col[rp[t]:rp[t + 1]]:
+            full[t * 64:(t + 1) * 64, kt * 64:(kt + 1) * 64] = 1
+    say("[gpu] bsa_forward_static without rowmask")
+    m.bsa_forward_static(lib.handle, q, k, v, out, torch.from_numpy(rp).cuda(),
+                         torch.from_numpy(col).cuda(), None, scale=0.125)
+    torch.cuda.synchronize()
+    ref = oracle.attend_mask(inp.q, inp.k, inp.v, full, 0.125)
+    assert np.abs(out.cpu().numpy().reshape(-1, d) - ref).max() <= TOL["bf16"]
+
+
+def test_deterministic(bsa):
+    m, lib = bsa
+    w = W.WORKLOADS["dyn_bf16_n4k"]
+    inp = W.generate(w)
+    say("[gpu] determinism dyn_bf16_n4k x2")
+    o1, i1 = run_forward(m, lib, w, inp)
+    o2, i2 = run_forward(m, lib, w, inp)
+    assert np.array_equal(i1, i2) and np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
+def test_panel_chunking_does_not_change_results(bsa):
+    m, lib = bsa
+    w = W.WORKLOADS["dyn_bf16_n4k"]
+    inp = W.generate(w)
+    o1, i1 = run_forward(m, lib, w, inp)
+    say("[gpu] small panel chunks")
+    m.bsa_set_option(lib.handle, m.BSA_OPT_PANEL_CHUNK_BYTES, 64 * 64 * 4 * 3)
+    try:
+        o2, i2 = run_forward(m, lib, w, inp)
+    finally:
+        m.bsa_set_option(lib.handle, m.BSA_OPT_PANEL_CHUNK_BYTES, 128 << 20)
+    assert np.array_equal(i1, i2) and np.array_equal(o1, o2)
+
+
+# ------------------------------------------------------------- validation --
+def test_validation_statuses(bsa):
+    m, lib = bsa
+    h = lib.handle
+    L = m._binding._lib
+    q = torch.zeros((1, 1, 128, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((1, 1, 128, 64), dtype=torch.float32, device="cuda")
+    P = lambda t: t.data_ptr()
+    def fwd(**kw):
+        a = dict(q=P(q), k=P(q), v=P(q), out=P(out), idx=None, b=1, h=1, n=128, d=64, dt=1,
+                 block=64, topk=2, scale=0.125, causal=0)
+        a.update(kw)
+        return L.bsa_forward(h, a["q"], a["k"], a["v"], a["out"], a["idx"], a["b"], a["h"], a["n"],
+                             a["d"], a["dt"], a["block"], a["topk"], a["scale"], a["causal"], None)
+    assert fwd() == m.BSA_OK
+    assert fwd(q=None) == m.BSA_ERR_INVALID_ARG
+    assert fwd(q=P(q) + 2) == m.BSA_ERR_INVALID_ARG          # misaligned
+    assert fwd(n=0) == m.BSA_ERR_INVALID_ARG
+    assert fwd(topk=0) == m.BSA_ERR_INVALID_ARG
+    assert fwd(scale=float("nan")) == m.BSA_ERR_INVALID_ARG
+    assert fwd(scale=-1.0) == m.BSA_ERR_INVALID_ARG
+    assert fwd(causal=2) == m.BSA_ERR_INVALID_ARG
+    assert fwd(dt=7) == m.BSA_ERR_INVALID_ARG
+    assert fwd(d=96) == m.BSA_ERR_UNSUPPORTED
+    assert fwd(block=32) == m.BSA_ERR_UNSUPPORTED
+    assert fwd(n=100) == m.BSA_ERR_UNSUPPORTED
+    assert fwd(n=64 * 4096) == m.BSA_ERR_UNSUPPORTED
+    assert "d must be 64 or 128" in (fwd(d=96), m.bsa_last_error(h))[1]
+    assert L.bsa_forward(None, P(q), P(q), P(q), P(out), None, 1, 1, 128, 64, 1, 64, 2, 0.125, 0,
+                         None) == m.BSA_ERR_INVALID_ARG
+    torch.cuda.synchronize()
