@@ -10,8 +10,8 @@
  *
  * What it follows (pages as published; section names in quotes):
  *
- *  [P1] "How I Built a Sparse Attention Kernel ..." (nishantmodi.me,
- *       sparse-attention-triton-bench), section "Two-stage block indexer":
+ *  [P1] the nishantmodi.me post "sparse-attention-triton-bench", section
+ *       "Two-stage block indexer":
  *       Stage 1 splits the keys into blocks of B, mean-pools each block into a
  *       representative vector, and scores every query against every
  *       representative (Q times the transposed representatives), which costs
