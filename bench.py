@@ -33,7 +33,9 @@ KERNEL_SOURCES = {
     "block_pool": "block_pool.hip",
     "coarse_score": "coarse_score.hip",
     "topk_select": "topk_select.hip",
-    "sparse_flash_fwd": "sparse_flash_fwd.hip",
+    "sparse_flash_fwd": "fine_gather.hip",
+    "gather_index": "fine_gather.hip",
+    "gather_combine": "fine_gather.hip",
 }
 
 
@@ -65,11 +67,20 @@ def stage_work(w: W.Workload):
     panel = cand * 4
     idx = w.bh * w.n * w.topk * 4
     fine_flops = 4 * w.d * visible_pairs(w)
+    sel_pairs = w.bh * w.n * min(w.topk, w.nb) if not w.causal else None
+    if sel_pairs is None:
+        i = np.arange(w.n, dtype=np.int64)
+        sel_pairs = int(w.bh * np.minimum(w.topk, i // w.block + 1).sum())
+    partial = sel_pairs * (w.d * (2 if w.dtype == "bf16" else 4) + 8)
+    out_b = w.bh * w.n * w.d * 4
     return {
         "block_pool": ("hbm", 0, qkv + repr_b),
         "coarse_score": ("hbm", 2 * w.d * cand, qkv + repr_b + panel),
         "topk_select": ("hbm", 0, panel + idx),
-        "sparse_flash_fwd": ("mfma", fine_flops, 3 * qkv + w.bh * w.n * w.d * 4 + idx),
+        # block-gather attention kernel: reads Q, K, V once, writes the partials
+        "sparse_flash_fwd": ("mfma", fine_flops, 3 * qkv + idx + partial),
+        "gather_index": ("hbm", 0, 2 * idx + 3 * sel_pairs * 4),
+        "gather_combine": ("hbm", 0, partial + idx + out_b),
     }
 
 
@@ -114,7 +125,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-positions", type=int, default=16384)
+    ap.add_argument("--cpu-positions", type=int, default=32768)
+    ap.add_argument("--fine-strategy", choices=["block_gather", "query_tile"], default="block_gather")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB -> 1 GiB device copy (3 times), the reference "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
@@ -122,6 +137,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 4,
+                          "copy_calibration_bytes_written": dst.numel() * 4, "launches": 3}))
+        return
 
     import content_dependent_block_amd as m
 
@@ -139,6 +164,8 @@ def main():
     idx = torch.empty(q.shape[:3] + (w.topk,), dtype=torch.int32, device=dev)
     lib = m.BlockSparseAttention(0)
     h = lib.handle
+    m.bsa_set_option(h, m.BSA_OPT_FINE_STRATEGY,
+                     m.BSA_FINE_BLOCK_GATHER if args.fine_strategy == "block_gather" else m.BSA_FINE_QUERY_TILE)
 
     def step():
         m.bsa_forward(h, q, k, v, out, idx, topk=w.topk, scale=w.scale, causal=w.causal)
@@ -164,10 +191,10 @@ def main():
     torch.cuda.synchronize()
     ms, launches = m.bsa_profile_read(h, reset=True)
     m.bsa_profile_enable(h, False)
-    per_step = {name: ms[i] / args.steps for i, name in enumerate(m.STAGE_NAMES)}
-    per_launch = {name: (ms[i] / launches[i] if launches[i] else 0.0)
-                  for i, name in enumerate(m.STAGE_NAMES)}
-    launches_per_step = {name: launches[i] // args.steps for i, name in enumerate(m.STAGE_NAMES)}
+    per_step = {name: ms[i] / args.steps for i, name in enumerate(m.STAGE_NAMES) if launches[i]}
+    per_launch = {name: ms[i] / launches[i] for i, name in enumerate(m.STAGE_NAMES) if launches[i]}
+    launches_per_step = {name: launches[i] // args.steps for i, name in enumerate(m.STAGE_NAMES)
+                         if launches[i]}
 
     work = stage_work(w)
     dom = max(per_step, key=per_step.get)
@@ -185,7 +212,7 @@ def main():
                 "kernel": dom, "avg_launch_ms": round(per_launch[dom], 5),
                 "launches_per_step": n_launch}
 
-    total_flops = sum(f for (_, f, _) in work.values())
+    total_flops = sum(f for (_, f, _) in work.values())  # matmul-only: coarse + fine
     tokens = w.batch * w.n
     result = {
         "metric": METRIC,
@@ -202,7 +229,8 @@ def main():
         "data": "synthetic: seeded N(0,1) q/k/v plus per-block key offsets N(0,0.5^2), "
                 "rounded to bf16 (no dataset)" if w.key_offsets else "synthetic: seeded N(0,1)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n": w.n, "d": w.d,
-                   "block": w.block, "topk": w.topk, "causal": w.causal},
+                   "block": w.block, "topk": w.topk, "causal": w.causal,
+                   "fine_strategy": args.fine_strategy},
         "effective_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 3),
         "algorithmic_gflop": round(total_flops / 1e9, 3),
         "stage_ms_per_step": {k_: round(v_, 5) for k_, v_ in per_step.items()},

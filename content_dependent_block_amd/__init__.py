@@ -13,8 +13,8 @@ import math
 import torch
 
 from ._binding import *  # noqa: F401,F403  (bsa_* functions and constants)
-from ._binding import (BSA_OPT_PANEL_CHUNK_BYTES, EXPORTED, STAGE_NAMES, BsaError, bsa_create,
-                       bsa_destroy, bsa_forward, bsa_forward_static, bsa_set_option)
+from ._binding import (EXPORTED, STAGE_NAMES, BsaError, bsa_create, bsa_destroy, bsa_forward,
+                       bsa_forward_static)
 
 
 class BlockSparseAttention:

@@ -22,9 +22,12 @@ _lib = ctypes.CDLL(str(_LIB_PATH))
 BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED = 0, 1, 2
 BSA_ERR_NO_DEVICE, BSA_ERR_OUT_OF_MEMORY, BSA_ERR_LAUNCH = 3, 4, 5
 BSA_FP32, BSA_BF16 = 0, 1
-BSA_STAGE_POOL, BSA_STAGE_COARSE, BSA_STAGE_TOPK, BSA_STAGE_FINE, BSA_NUM_STAGES = 0, 1, 2, 3, 4
-STAGE_NAMES = ("block_pool", "coarse_score", "topk_select", "sparse_flash_fwd")
-BSA_OPT_PANEL_CHUNK_BYTES = 0
+BSA_STAGE_POOL, BSA_STAGE_COARSE, BSA_STAGE_TOPK, BSA_STAGE_FINE = 0, 1, 2, 3
+BSA_STAGE_GATHER_INDEX, BSA_STAGE_GATHER_COMBINE, BSA_NUM_STAGES = 4, 5, 6
+STAGE_NAMES = ("block_pool", "coarse_score", "topk_select", "sparse_flash_fwd", "gather_index",
+               "gather_combine")
+BSA_OPT_PANEL_CHUNK_BYTES, BSA_OPT_FINE_STRATEGY, BSA_OPT_FINE_CHUNK_BYTES = 0, 1, 2
+BSA_FINE_BLOCK_GATHER, BSA_FINE_QUERY_TILE = 0, 1
 
 _P, _I, _I64, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
 

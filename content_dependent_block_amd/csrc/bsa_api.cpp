@@ -28,6 +28,14 @@ struct bsa_handle_s {
   int32_t* idx = nullptr;
   size_t idx_bytes = 0;
   int64_t panel_chunk_bytes = int64_t(128) << 20;
+  // block-gather workspace
+  int fine_strategy = BSA_FINE_BLOCK_GATHER;
+  int64_t fine_chunk_bytes = int64_t(1) << 30;
+  struct Buf {
+    void* p = nullptr;
+    size_t bytes = 0;
+  };
+  Buf g_count, g_offsets, g_items, g_rank, g_list, g_po, g_pml;
   // timing
   bool profiling = false;
   struct Rec {
@@ -223,6 +231,8 @@ BSA_API bsa_status bsa_destroy(bsa_handle h) {
   if (h->repr) (void)hipFree(h->repr);
   if (h->panel) (void)hipFree(h->panel);
   if (h->idx) (void)hipFree(h->idx);
+  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml})
+    if (b->p) (void)hipFree(b->p);
   delete h;
   return BSA_OK;
 }
@@ -234,6 +244,15 @@ BSA_API bsa_status bsa_set_option(bsa_handle h, int option, int64_t value) {
       if (value < 1) return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: panel chunk must be > 0");
       h->panel_chunk_bytes = value;
       return BSA_OK;
+    case BSA_OPT_FINE_STRATEGY:
+      if (value != BSA_FINE_BLOCK_GATHER && value != BSA_FINE_QUERY_TILE)
+        return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: unknown fine strategy %lld", (long long)value);
+      h->fine_strategy = static_cast<int>(value);
+      return BSA_OK;
+    case BSA_OPT_FINE_CHUNK_BYTES:
+      if (value < 1) return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: fine chunk must be > 0");
+      h->fine_chunk_bytes = value;
+      return BSA_OK;
     default:
       return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: unknown option %d", option);
   }
@@ -242,6 +261,8 @@ BSA_API bsa_status bsa_set_option(bsa_handle h, int option, int64_t value) {
 BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
   if (!h || !bytes) return fail(h, BSA_ERR_INVALID_ARG, "bsa_workspace_bytes: NULL argument");
   *bytes = h->repr_bytes + h->panel_bytes + h->idx_bytes;
+  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml})
+    *bytes += b->bytes;
   return BSA_OK;
 }
 
@@ -275,6 +296,54 @@ bsa_status run_select(bsa_handle h, const void* q, const float* repr, int32_t* i
     TRY(timed_launch(h, BSA_STAGE_TOPK, st, "topk_select", [&] {
       return bsa::launch_topk_select(h->panel, idx, r0, rows, s.n, topk, causal, st);
     }));
+  }
+  return BSA_OK;
+}
+
+bsa_status grow_buf(bsa_handle h, bsa_handle_s::Buf& b, size_t need, const char* what) {
+  return grow(h, &b.p, &b.bytes, need, what);
+}
+
+// Stage 2 for the dynamic path, with the handle's fine strategy.
+bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, float* out,
+                    const int32_t* idx, const Shape& s, bsa_dtype dt, int topk, float scale,
+                    int causal, hipStream_t st) {
+  if (h->fine_strategy == BSA_FINE_QUERY_TILE)
+    return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
+      return bsa::launch_sparse_flash_dynamic(q, k, v, out, idx, s.bh(), s.n, s.d, topk, scale,
+                                              causal, dt, st);
+    });
+  const int64_t total = s.bh() * s.n;
+  const size_t per_row = bsa::gather_pair_bytes(s.d, dt) * size_t(topk);
+  int64_t chunk = h->fine_chunk_bytes / int64_t(per_row) / 64 * 64;
+  if (chunk < 64) chunk = 64;
+  if (chunk > total) chunk = total;
+  const int64_t pairs = chunk * topk;
+  const int64_t nb = s.n / 64;
+  const int64_t buckets = (s.bh() < (chunk + s.n - 1) / s.n + 1 ? s.bh() : (chunk + s.n - 1) / s.n + 1) * nb;
+  TRY(grow_buf(h, h->g_count, size_t(buckets) * 4, "bucket counts"));
+  TRY(grow_buf(h, h->g_offsets, size_t(buckets + 1) * 4, "bucket offsets"));
+  TRY(grow_buf(h, h->g_items, size_t(buckets + 1) * 4, "bucket work items"));
+  TRY(grow_buf(h, h->g_rank, size_t(pairs) * 4, "pair ranks"));
+  TRY(grow_buf(h, h->g_list, size_t(pairs) * 4, "pair lists"));
+  TRY(grow_buf(h, h->g_po, size_t(pairs) * s.d * (dt == BSA_BF16 ? 2 : 4), "partial outputs"));
+  TRY(grow_buf(h, h->g_pml, size_t(pairs) * 8, "partial max/sum"));
+  bsa::GatherArgs a{q, k, v, out, idx, s.n, s.d, topk, causal, scale, dt, {}};
+  a.ws.count = static_cast<int32_t*>(h->g_count.p);
+  a.ws.offsets = static_cast<int32_t*>(h->g_offsets.p);
+  a.ws.items = static_cast<int32_t*>(h->g_items.p);
+  a.ws.rank = static_cast<int32_t*>(h->g_rank.p);
+  a.ws.list = static_cast<int32_t*>(h->g_list.p);
+  a.ws.partial_o = h->g_po.p;
+  a.ws.partial_ml = static_cast<float2*>(h->g_pml.p);
+  for (int64_t r0 = 0; r0 < total; r0 += chunk) {
+    const int64_t rows = (total - r0) < chunk ? (total - r0) : chunk;
+    TRY(timed_launch(h, BSA_STAGE_GATHER_INDEX, st, "block-gather bucketing",
+                     [&] { return bsa::launch_gather_index(a, r0, rows, st); }));
+    TRY(timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd",
+                     [&] { return bsa::launch_gather_partial(a, r0, rows, st); }));
+    TRY(timed_launch(h, BSA_STAGE_GATHER_COMBINE, st, "block-gather combine",
+                     [&] { return bsa::launch_gather_combine(a, r0, rows, st); }));
   }
   return BSA_OK;
 }
@@ -347,11 +416,8 @@ BSA_API bsa_status bsa_fine_forward(bsa_handle h, const void* q, const void* k, 
   TRY(check_ptr(h, fn, "out", out));
   if (!block_idx) return fail(h, BSA_ERR_INVALID_ARG, "%s: block_idx is NULL", fn);
   DeviceGuard dg(h->device);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
-    return bsa::launch_sparse_flash_dynamic(q, k, v, out, block_idx, s.bh(), s.n, s.d, topk, scale,
-                                            causal, dtype, st);
-  });
+  return run_fine(h, q, k, v, out, block_idx, s, dtype, topk, scale, causal,
+                  static_cast<hipStream_t>(stream));
 }
 
 BSA_API bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const void* v,
@@ -383,10 +449,7 @@ BSA_API bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const
   }
   TRY(run_pool(h, k, h->repr, s, dtype, st));
   TRY(run_select(h, q, h->repr, idx, s, dtype, topk, causal, st));
-  return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
-    return bsa::launch_sparse_flash_dynamic(q, k, v, out, idx, s.bh(), s.n, s.d, topk, scale,
-                                            causal, dtype, st);
-  });
+  return run_fine(h, q, k, v, out, idx, s, dtype, topk, scale, causal, st);
 }
 
 BSA_API bsa_status bsa_forward_static(bsa_handle h, const void* q, const void* k, const void* v,

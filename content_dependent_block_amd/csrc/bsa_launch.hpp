@@ -39,4 +39,34 @@ hipError_t launch_sparse_flash_static(const void* q, const void* k, const void* 
                                       const uint64_t* rowmask, int64_t nnz, int64_t bh, int n,
                                       int d, float scale, bsa_dtype dtype, hipStream_t stream);
 
+// sparse_flash_fwd, block-gather strategy: pairs grouped by key block,
+// split-softmax partials, merged per query.  Three launch groups per chunk of
+// query rows [row0, row0 + rows) (row0, rows multiples of 64).
+struct GatherWorkspace {
+  int32_t* count = nullptr;    // [buckets]      buckets = heads spanned by a chunk * n/64
+  int32_t* offsets = nullptr;  // [buckets + 1]
+  int32_t* items = nullptr;    // [buckets + 1]
+  int32_t* rank = nullptr;     // [chunk pairs]  pairs = rows * topk
+  int32_t* list = nullptr;     // [chunk pairs]
+  void* partial_o = nullptr;   // [chunk pairs][d]  fp16 for bf16 inputs, fp32 for fp32 inputs
+  float2* partial_ml = nullptr;  // [chunk pairs]  (log2-domain max, sum)
+};
+
+struct GatherArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  float* out;
+  const int32_t* idx;
+  int n, d, topk, causal;
+  float scale;
+  bsa_dtype dtype;
+  GatherWorkspace ws;
+};
+
+size_t gather_pair_bytes(int d, bsa_dtype dtype);  // partial bytes per (query, block) pair
+hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s);
+hipError_t launch_gather_partial(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s);
+hipError_t launch_gather_combine(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s);
+
 }  // namespace bsa

@@ -60,19 +60,37 @@ typedef enum { BSA_FP32 = 0, BSA_BF16 = 1 } bsa_dtype;
 
 /* Stages, for the per-stage timer below. */
 typedef enum {
-  BSA_STAGE_POOL = 0,   /* block_pool       */
-  BSA_STAGE_COARSE = 1, /* coarse_score     */
-  BSA_STAGE_TOPK = 2,   /* topk_select      */
-  BSA_STAGE_FINE = 3,   /* sparse_flash_fwd */
-  BSA_NUM_STAGES = 4
+  BSA_STAGE_POOL = 0,    /* block_pool                                         */
+  BSA_STAGE_COARSE = 1,  /* coarse_score                                       */
+  BSA_STAGE_TOPK = 2,    /* topk_select                                        */
+  BSA_STAGE_FINE = 3,    /* sparse_flash_fwd (the MFMA attention kernel)       */
+  BSA_STAGE_GATHER_INDEX = 4,   /* block-gather: bucketing of (query, block) pairs */
+  BSA_STAGE_GATHER_COMBINE = 5, /* block-gather: merge of per-block partials       */
+  BSA_NUM_STAGES = 6
 } bsa_stage;
+
+/* How the dynamic fine stage visits the selected blocks. */
+typedef enum {
+  /* Group the (query, block) pairs by key block, run 16 pairs per MFMA tile,
+   * write split-softmax partials (m, l, o) and merge them per query.  Every
+   * selected pair is computed once.  Default. */
+  BSA_FINE_BLOCK_GATHER = 0,
+  /* Per 64-query tile, walk the union of the rows' selected blocks with the
+   * online softmax in registers, masking each row to its own selection. */
+  BSA_FINE_QUERY_TILE = 1
+} bsa_fine_strategy;
 
 /* Tunables for bsa_set_option. */
 typedef enum {
   /* Upper bound in bytes of the fp32 coarse-score panel that stage 1 keeps at
    * once; queries are processed in chunks of at most this many bytes of panel.
    * Default 128 MiB.  Minimum one 64-query tile. */
-  BSA_OPT_PANEL_CHUNK_BYTES = 0
+  BSA_OPT_PANEL_CHUNK_BYTES = 0,
+  /* bsa_fine_strategy for the dynamic fine stage.  Default BSA_FINE_BLOCK_GATHER. */
+  BSA_OPT_FINE_STRATEGY = 1,
+  /* Upper bound in bytes of the block-gather partial buffer; query rows are
+   * processed in chunks that fit.  Default 1 GiB.  Minimum one 64-query tile. */
+  BSA_OPT_FINE_CHUNK_BYTES = 2
 } bsa_option;
 
 /* ----------------------------------------------------------- lifetime -- */

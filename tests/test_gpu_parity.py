@@ -31,12 +31,27 @@ def say(*a):
     sys.stdout.flush()
 
 
+STRATEGIES = ["block_gather", "query_tile"]
+
+
 @pytest.fixture(scope="module")
 def bsa():
     import content_dependent_block_amd as m
     lib = m.BlockSparseAttention(0)
     yield m, lib
     lib.close()
+
+
+def use_strategy(m, lib, strategy):
+    code = {"block_gather": m.BSA_FINE_BLOCK_GATHER, "query_tile": m.BSA_FINE_QUERY_TILE}[strategy]
+    m.bsa_set_option(lib.handle, m.BSA_OPT_FINE_STRATEGY, code)
+
+
+@pytest.fixture(autouse=True)
+def _default_strategy(bsa):
+    yield
+    m, lib = bsa
+    use_strategy(m, lib, "block_gather")
 
 
 def to_dev(inp, dtype):
@@ -194,18 +209,20 @@ def test_topk_select_bit_exact(bsa, nb, k, causal):
 
 
 # --------------------------------------------------------- fine attention --
+@pytest.mark.parametrize("strategy", STRATEGIES)
 @pytest.mark.parametrize("name,causal,dd", [("tiny_fp32_n1k", False, 64), ("dyn_bf16_n4k", False, 64),
                                             ("dyn_bf16_n4k", True, 64), ("dyn_bf16_n4k", False, 128),
                                             ("tiny_fp32_n1k", True, 128)])
-def test_fine_forward_on_oracle_indices(bsa, name, causal, dd):
+def test_fine_forward_on_oracle_indices(bsa, name, causal, dd, strategy):
     m, lib = bsa
+    use_strategy(m, lib, strategy)
     w0 = W.WORKLOADS[name]
     w = W.Workload(w0.name, w0.batch, w0.heads, w0.n, dd, w0.dtype, w0.seed, topk=w0.topk,
                    causal=causal, key_offsets=w0.key_offsets)
     inp = W.generate(w)
     rows = sample_rows(w, 4096, seed=1)
     oidx_rows, _, _ = oracle.select(inp.q, inp.k, w.block, w.topk, causal)
-    say(f"[gpu] bsa_fine_forward {name} causal={causal} d={dd}")
+    say(f"[gpu] bsa_fine_forward {name} causal={causal} d={dd} strategy={strategy}")
     q, k, v = to_dev(inp, w.dtype)
     idx = torch.from_numpy(oidx_rows.reshape(w.batch, w.heads, w.n, w.topk)).cuda()
     out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
@@ -217,18 +234,23 @@ def test_fine_forward_on_oracle_indices(bsa, name, causal, dd):
 
 
 # ------------------------------------------------------------ end to end --
+@pytest.mark.parametrize("strategy", STRATEGIES)
 @pytest.mark.parametrize("name", ["tiny_fp32_n1k", "dyn_bf16_n4k"])
-def test_forward_small_workloads_all_rows(bsa, name):
+def test_forward_small_workloads_all_rows(bsa, name, strategy):
     m, lib = bsa
+    use_strategy(m, lib, strategy)
     w = W.WORKLOADS[name]
     inp = W.generate(w)
     end_to_end(m, lib, w, inp, np.arange(w.bh * w.n, dtype=np.int64))
 
 
-def test_forward_headline_sampled(bsa):
+@pytest.mark.parametrize("strategy", STRATEGIES)
+def test_forward_headline_sampled(bsa, strategy):
     """N=32768, 8 heads, bf16, k=16 in the launch configuration the benchmark
-    times; sampled rows against the oracle, plus properties of every row."""
+    times (block_gather); sampled rows against the oracle, plus properties of
+    every row."""
     m, lib = bsa
+    use_strategy(m, lib, strategy)
     w = W.WORKLOADS["dyn_bf16_n32k"]
     inp = W.generate(w)
     rows = sample_rows(w, 3000, seed=2, extra=[0, 63, w.n - 1, w.n, w.bh * w.n - 1])
@@ -287,8 +309,10 @@ def test_static_window_stride(bsa):
     dict(batch=2, heads=1, n=1024, d=128, dtype="fp32", topk=3, causal=False),   # fp32 D=128
     dict(batch=1, heads=2, n=4096, d=64, dtype="bf16", topk=64, causal=False),   # k = n/64: dense
 ])
-def test_forward_edge_cases(bsa, case):
+@pytest.mark.parametrize("strategy", STRATEGIES)
+def test_forward_edge_cases(bsa, case, strategy):
     m, lib = bsa
+    use_strategy(m, lib, strategy)
     w = W.Workload("edge", case["batch"], case["heads"], case["n"], case["d"], case["dtype"],
                    seed=77, topk=case["topk"], causal=case["causal"],
                    key_offsets=case["dtype"] == "bf16")
@@ -333,11 +357,29 @@ def test_static_edge_cases(bsa):
     assert np.abs(out.cpu().numpy().reshape(-1, d) - ref).max() <= TOL["bf16"]
 
 
-def test_deterministic(bsa):
+def test_fine_chunking_does_not_change_results(bsa):
+    """Block-gather partial buffer split into many chunks, some spanning two
+    heads (chunk of 3 query tiles with n = 4096), gives bit-identical output."""
     m, lib = bsa
     w = W.WORKLOADS["dyn_bf16_n4k"]
     inp = W.generate(w)
-    say("[gpu] determinism dyn_bf16_n4k x2")
+    o1, i1 = run_forward(m, lib, w, inp)
+    say("[gpu] small fine chunks")
+    m.bsa_set_option(lib.handle, m.BSA_OPT_FINE_CHUNK_BYTES, 3 * 64 * w.topk * (w.d * 2 + 8))
+    try:
+        o2, i2 = run_forward(m, lib, w, inp)
+    finally:
+        m.bsa_set_option(lib.handle, m.BSA_OPT_FINE_CHUNK_BYTES, 1 << 30)
+    assert np.array_equal(i1, i2) and np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
+@pytest.mark.parametrize("strategy", STRATEGIES)
+def test_deterministic(bsa, strategy):
+    m, lib = bsa
+    use_strategy(m, lib, strategy)
+    w = W.WORKLOADS["dyn_bf16_n4k"]
+    inp = W.generate(w)
+    say(f"[gpu] determinism dyn_bf16_n4k x2 strategy={strategy}")
     o1, i1 = run_forward(m, lib, w, inp)
     o2, i2 = run_forward(m, lib, w, inp)
     assert np.array_equal(i1, i2) and np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
