@@ -2,7 +2,8 @@
 """Benchmark of the block-sparse attention forward on one MI355X.
 
 One step = one full forward over one batch of resident synthetic inputs:
-block_pool -> coarse_score (+ topk_select, per panel chunk) -> sparse_flash_fwd.
+block_pool -> coarse_select (coarse scores and top-k in one kernel) ->
+block-gather sparse_flash_fwd (gather_index, attention, gather_combine).
 Prints ONE JSON line: forward tokens/s (batch * n / step time), effective
 TFLOP/s, the roofline of the dominant kernel (timed with HIP events on the
 launch stream inside this run) and the fp64 CPU oracle's throughput on a
@@ -33,6 +34,7 @@ KERNEL_SOURCES = {
     "block_pool": "block_pool.hip",
     "coarse_score": "coarse_score.hip",
     "topk_select": "topk_select.hip",
+    "coarse_select": "coarse_score.hip",
     "sparse_flash_fwd": "fine_gather.hip",
     "gather_index": "fine_gather.hip",
     "gather_combine": "fine_gather.hip",
@@ -77,6 +79,8 @@ def stage_work(w: W.Workload):
         "block_pool": ("hbm", 0, qkv + repr_b),
         "coarse_score": ("hbm", 2 * w.d * cand, qkv + repr_b + panel),
         "topk_select": ("hbm", 0, panel + idx),
+        # fused scoring + selection: q and the representatives in, indices out
+        "coarse_select": ("mfma", 2 * w.d * cand, qkv + repr_b + idx),
         # block-gather attention kernel: reads Q, K, V once, writes the partials
         "sparse_flash_fwd": ("mfma", fine_flops, 3 * qkv + idx + partial),
         "gather_index": ("hbm", 0, 2 * idx + 3 * sel_pairs * 4),
@@ -127,6 +131,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-positions", type=int, default=32768)
     ap.add_argument("--fine-strategy", choices=["block_gather", "query_tile"], default="block_gather")
+    ap.add_argument("--select-strategy", choices=["fused", "panel"], default="fused")
+    ap.add_argument("--panel-chunk-mb", type=int, default=0, help="coarse-score panel chunk (0 = default)")
+    ap.add_argument("--fine-chunk-mb", type=int, default=0, help="block-gather partial chunk (0 = default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB -> 1 GiB device copy (3 times), the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -166,6 +173,12 @@ def main():
     h = lib.handle
     m.bsa_set_option(h, m.BSA_OPT_FINE_STRATEGY,
                      m.BSA_FINE_BLOCK_GATHER if args.fine_strategy == "block_gather" else m.BSA_FINE_QUERY_TILE)
+    m.bsa_set_option(h, m.BSA_OPT_SELECT_STRATEGY,
+                     m.BSA_SELECT_FUSED if args.select_strategy == "fused" else m.BSA_SELECT_PANEL)
+    if args.panel_chunk_mb:
+        m.bsa_set_option(h, m.BSA_OPT_PANEL_CHUNK_BYTES, args.panel_chunk_mb << 20)
+    if args.fine_chunk_mb:
+        m.bsa_set_option(h, m.BSA_OPT_FINE_CHUNK_BYTES, args.fine_chunk_mb << 20)
 
     def step():
         m.bsa_forward(h, q, k, v, out, idx, topk=w.topk, scale=w.scale, causal=w.causal)
@@ -212,7 +225,7 @@ def main():
                 "kernel": dom, "avg_launch_ms": round(per_launch[dom], 5),
                 "launches_per_step": n_launch}
 
-    total_flops = sum(f for (_, f, _) in work.values())  # matmul-only: coarse + fine
+    total_flops = sum(work[k_][1] for k_ in per_step)  # matmul-only: coarse + fine, stages that ran
     tokens = w.batch * w.n
     result = {
         "metric": METRIC,
@@ -230,7 +243,8 @@ def main():
                 "rounded to bf16 (no dataset)" if w.key_offsets else "synthetic: seeded N(0,1)",
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n": w.n, "d": w.d,
                    "block": w.block, "topk": w.topk, "causal": w.causal,
-                   "fine_strategy": args.fine_strategy},
+                   "select_strategy": args.select_strategy, "fine_strategy": args.fine_strategy,
+                   "panel_chunk_mb": args.panel_chunk_mb or 128, "fine_chunk_mb": args.fine_chunk_mb or 1024},
         "effective_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 3),
         "algorithmic_gflop": round(total_flops / 1e9, 3),
         "stage_ms_per_step": {k_: round(v_, 5) for k_, v_ in per_step.items()},

@@ -23,11 +23,14 @@ BSA_OK, BSA_ERR_INVALID_ARG, BSA_ERR_UNSUPPORTED = 0, 1, 2
 BSA_ERR_NO_DEVICE, BSA_ERR_OUT_OF_MEMORY, BSA_ERR_LAUNCH = 3, 4, 5
 BSA_FP32, BSA_BF16 = 0, 1
 BSA_STAGE_POOL, BSA_STAGE_COARSE, BSA_STAGE_TOPK, BSA_STAGE_FINE = 0, 1, 2, 3
-BSA_STAGE_GATHER_INDEX, BSA_STAGE_GATHER_COMBINE, BSA_NUM_STAGES = 4, 5, 6
+BSA_STAGE_GATHER_INDEX, BSA_STAGE_GATHER_COMBINE, BSA_STAGE_COARSE_TOPK = 4, 5, 6
+BSA_NUM_STAGES = 7
 STAGE_NAMES = ("block_pool", "coarse_score", "topk_select", "sparse_flash_fwd", "gather_index",
-               "gather_combine")
+               "gather_combine", "coarse_select")
 BSA_OPT_PANEL_CHUNK_BYTES, BSA_OPT_FINE_STRATEGY, BSA_OPT_FINE_CHUNK_BYTES = 0, 1, 2
+BSA_OPT_SELECT_STRATEGY = 3
 BSA_FINE_BLOCK_GATHER, BSA_FINE_QUERY_TILE = 0, 1
+BSA_SELECT_FUSED, BSA_SELECT_PANEL = 0, 1
 
 _P, _I, _I64, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
 
@@ -189,21 +192,20 @@ def bsa_coarse_score(h, q, repr_, panel_out, *, block: int = 64, causal: bool = 
     dev = q.device
     pq = _need(q, "q", q.shape, None, dev)
     pr = _need(repr_, "repr", (b, hh, n // block, d), torch.float32, dev)
-    pp = _need(panel_out, "panel_out", (b, hh, n, n // block), torch.float32, dev)
+    pp = _need(panel_out, "panel_out", (n // block, b * hh * n), torch.float32, dev)
     _check(_lib.bsa_coarse_score(h, pq, pr, pp, b, hh, n, d, _dtype_code(q), block, int(causal),
                                  _stream(stream, dev)), h)
 
 
 def bsa_topk_select(h, panel, block_idx_out, *, block: int = 64, causal: bool = False,
                     stream=None) -> None:
-    if panel.dim() != 4:
-        raise ValueError("panel must be [batch, heads, n, n/block]")
-    b, hh, n, nb = panel.shape
+    """panel: block-major [n/block, batch*heads*n] as bsa_coarse_score writes it;
+    block_idx_out: [batch, heads, n, topk]."""
+    if block_idx_out.dim() != 4:
+        raise ValueError("block_idx_out must be [batch, heads, n, topk]")
+    b, hh, n, topk = block_idx_out.shape
     dev = panel.device
-    if nb * block != n:
-        raise ValueError("panel's last dimension must be n / block")
-    pp = _need(panel, "panel", panel.shape, torch.float32, dev)
-    topk = block_idx_out.shape[-1]
+    pp = _need(panel, "panel", (n // block, b * hh * n), torch.float32, dev)
     pi = _need(block_idx_out, "block_idx_out", (b, hh, n, topk), torch.int32, dev)
     _check(_lib.bsa_topk_select(h, pp, pi, b, hh, n, block, topk, int(causal),
                                 _stream(stream, dev)), h)

@@ -25,6 +25,7 @@ SOURCES = ["block_pool.hip", "coarse_score.hip", "topk_select.hip", "sparse_flas
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-mfma-vgpr-form",
          "-Wno-unused-result", f"-I{ROOT / 'include'}", f"-I{CSRC}"]
 
 

@@ -28,6 +28,7 @@ struct bsa_handle_s {
   int32_t* idx = nullptr;
   size_t idx_bytes = 0;
   int64_t panel_chunk_bytes = int64_t(128) << 20;
+  int select_strategy = BSA_SELECT_FUSED;
   // block-gather workspace
   int fine_strategy = BSA_FINE_BLOCK_GATHER;
   int64_t fine_chunk_bytes = int64_t(1) << 30;
@@ -35,7 +36,7 @@ struct bsa_handle_s {
     void* p = nullptr;
     size_t bytes = 0;
   };
-  Buf g_count, g_offsets, g_items, g_rank, g_list, g_po, g_pml;
+  Buf g_count, g_offsets, g_items, g_item_rec, g_rank, g_list, g_po, g_pml;
   // timing
   bool profiling = false;
   struct Rec {
@@ -231,7 +232,7 @@ BSA_API bsa_status bsa_destroy(bsa_handle h) {
   if (h->repr) (void)hipFree(h->repr);
   if (h->panel) (void)hipFree(h->panel);
   if (h->idx) (void)hipFree(h->idx);
-  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml})
+  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml})
     if (b->p) (void)hipFree(b->p);
   delete h;
   return BSA_OK;
@@ -249,6 +250,11 @@ BSA_API bsa_status bsa_set_option(bsa_handle h, int option, int64_t value) {
         return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: unknown fine strategy %lld", (long long)value);
       h->fine_strategy = static_cast<int>(value);
       return BSA_OK;
+    case BSA_OPT_SELECT_STRATEGY:
+      if (value != BSA_SELECT_FUSED && value != BSA_SELECT_PANEL)
+        return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: unknown select strategy %lld", (long long)value);
+      h->select_strategy = static_cast<int>(value);
+      return BSA_OK;
     case BSA_OPT_FINE_CHUNK_BYTES:
       if (value < 1) return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: fine chunk must be > 0");
       h->fine_chunk_bytes = value;
@@ -261,7 +267,7 @@ BSA_API bsa_status bsa_set_option(bsa_handle h, int option, int64_t value) {
 BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
   if (!h || !bytes) return fail(h, BSA_ERR_INVALID_ARG, "bsa_workspace_bytes: NULL argument");
   *bytes = h->repr_bytes + h->panel_bytes + h->idx_bytes;
-  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml})
+  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml})
     *bytes += b->bytes;
   return BSA_OK;
 }
@@ -277,12 +283,17 @@ bsa_status run_pool(bsa_handle h, const void* k, float* repr, const Shape& s, bs
   });
 }
 
-// coarse_score + topk_select over all rows, in panel chunks of at most
-// panel_chunk_bytes.
+// Stage 1 selection over all rows: one fused coarse_score + topk_select
+// kernel (k <= 32, fused strategy), else coarse_score and topk_select through
+// a panel, in chunks of at most panel_chunk_bytes of panel.
 bsa_status run_select(bsa_handle h, const void* q, const float* repr, int32_t* idx, const Shape& s,
                       bsa_dtype dt, int topk, int causal, hipStream_t st) {
   const int64_t nb = s.n / 64;
   const int64_t total = s.bh() * s.n;
+  if (h->select_strategy == BSA_SELECT_FUSED && topk <= bsa::kFusedSelectMaxK)
+    return timed_launch(h, BSA_STAGE_COARSE_TOPK, st, "coarse_select", [&] {
+      return bsa::launch_coarse_select(q, repr, idx, total, s.n, s.d, dt, topk, causal, st);
+    });
   int64_t chunk = h->panel_chunk_bytes / (nb * 4) / 64 * 64;
   if (chunk < 64) chunk = 64;
   if (chunk > total) chunk = total;
@@ -315,8 +326,9 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
     });
   const int64_t total = s.bh() * s.n;
   const size_t per_row = bsa::gather_pair_bytes(s.d, dt) * size_t(topk);
-  int64_t chunk = h->fine_chunk_bytes / int64_t(per_row) / 64 * 64;
-  if (chunk < 64) chunk = 64;
+  const int64_t align = (s.n % 256 == 0) ? 256 : 64;  // keeps bucketing workgroups inside one head
+  int64_t chunk = h->fine_chunk_bytes / int64_t(per_row) / align * align;
+  if (chunk < align) chunk = align;
   if (chunk > total) chunk = total;
   const int64_t pairs = chunk * topk;
   const int64_t nb = s.n / 64;
@@ -324,6 +336,8 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   TRY(grow_buf(h, h->g_count, size_t(buckets) * 4, "bucket counts"));
   TRY(grow_buf(h, h->g_offsets, size_t(buckets + 1) * 4, "bucket offsets"));
   TRY(grow_buf(h, h->g_items, size_t(buckets + 1) * 4, "bucket work items"));
+  TRY(grow_buf(h, h->g_item_rec, size_t(bsa::gather_grid(chunk, topk, buckets)) * 16,
+               "work-item records"));
   TRY(grow_buf(h, h->g_rank, size_t(pairs) * 4, "pair ranks"));
   TRY(grow_buf(h, h->g_list, size_t(pairs) * 4, "pair lists"));
   TRY(grow_buf(h, h->g_po, size_t(pairs) * s.d * (dt == BSA_BF16 ? 2 : 4), "partial outputs"));
@@ -332,6 +346,7 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   a.ws.count = static_cast<int32_t*>(h->g_count.p);
   a.ws.offsets = static_cast<int32_t*>(h->g_offsets.p);
   a.ws.items = static_cast<int32_t*>(h->g_items.p);
+  a.ws.item_rec = static_cast<int4*>(h->g_item_rec.p);
   a.ws.rank = static_cast<int32_t*>(h->g_rank.p);
   a.ws.list = static_cast<int32_t*>(h->g_list.p);
   a.ws.partial_o = h->g_po.p;
@@ -377,7 +392,8 @@ BSA_API bsa_status bsa_coarse_score(bsa_handle h, const void* q, const float* re
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
   return timed_launch(h, BSA_STAGE_COARSE, st, "coarse_score", [&] {
-    return bsa::launch_coarse_score(q, repr, panel_out, 0, s.bh() * s.n, s.n, s.d, dtype, causal, st);
+    return bsa::launch_coarse_score(q, repr, panel_out, 0, s.bh() * s.n, s.n, s.d, dtype, causal,
+                                    st);
   });
 }
 

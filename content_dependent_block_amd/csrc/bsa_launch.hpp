@@ -17,14 +17,21 @@ hipError_t launch_block_pool(const void* k, float* repr, int64_t bh, int n, int 
 
 // coarse_score over panel rows [row0, row0 + rows) of the flattened
 // [bh * n] query rows; row0 and rows multiples of 64.  panel row r holds
-// query row0 + r, nb = n / 64 columns.
+// query row0 + r, nb = n / 64 columns, block-major: panel[beta * rows + r].
 hipError_t launch_coarse_score(const void* q, const float* repr, float* panel, int64_t row0,
                                int64_t rows, int n, int d, bsa_dtype dtype, int causal,
                                hipStream_t stream);
 
-// topk_select over the same rows: idx[(row0 + r) * topk + t].
-hipError_t launch_topk_select(const float* panel, int32_t* idx, int64_t row0, int64_t rows,
-                              int n, int topk, int causal, hipStream_t stream);
+// coarse_score and topk_select in one kernel (topk <= 32) over all `rows`
+// query rows: idx[row * topk + t], no panel.
+hipError_t launch_coarse_select(const void* q, const float* repr, int32_t* idx, int64_t rows,
+                                int n, int d, bsa_dtype dtype, int topk, int causal,
+                                hipStream_t stream);
+constexpr int kFusedSelectMaxK = 32;
+
+// topk_select over panel rows [row0, row0 + rows): idx[(row0 + r) * topk + t].
+hipError_t launch_topk_select(const float* panel, int32_t* idx, int64_t row0, int64_t rows, int n,
+                              int topk, int causal, hipStream_t stream);
 
 // sparse_flash_fwd, dynamic: per 64-query tile the union of its rows'
 // selected blocks, each row masked to its own selection.
@@ -46,6 +53,7 @@ struct GatherWorkspace {
   int32_t* count = nullptr;    // [buckets]      buckets = heads spanned by a chunk * n/64
   int32_t* offsets = nullptr;  // [buckets + 1]
   int32_t* items = nullptr;    // [buckets + 1]
+  int4* item_rec = nullptr;    // [gather_grid(...)]  per-workgroup work-item records
   int32_t* rank = nullptr;     // [chunk pairs]  pairs = rows * topk
   int32_t* list = nullptr;     // [chunk pairs]
   void* partial_o = nullptr;   // [chunk pairs][d]  fp16 for bf16 inputs, fp32 for fp32 inputs
@@ -65,6 +73,7 @@ struct GatherArgs {
 };
 
 size_t gather_pair_bytes(int d, bsa_dtype dtype);  // partial bytes per (query, block) pair
+int64_t gather_grid(int64_t rows, int topk, int64_t nbuckets);  // attention-kernel workgroups
 hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s);
 hipError_t launch_gather_partial(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s);
 hipError_t launch_gather_combine(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s);

@@ -36,6 +36,7 @@
 
 #include "bsa_device.hpp"
 #include "bsa_launch.hpp"
+#include "kv_tile.hpp"
 
 namespace bsa {
 namespace {
@@ -59,15 +60,15 @@ __global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, 
   if (i < count) p[i] = 0;
 }
 
-// One workgroup per 64 query rows (never straddles a head because n % 64 == 0).
+// One workgroup per `rpw` query rows of one head (rpw divides n and row0).
 __global__ __launch_bounds__(256) void bucket_count_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ count, int32_t* __restrict__ rank,
-    int64_t row0, int64_t rows, int n, int topk, int causal, int64_t bh0) {
+    int64_t row0, int64_t rows, int n, int topk, int causal, int64_t bh0, int rpw) {
   extern __shared__ int32_t hist[];  // [nb] local counts, then [nb] global bases
   const int nb = n / kTile;
   int32_t* base = hist + nb;
-  const int64_t r_begin = row0 + static_cast<int64_t>(blockIdx.x) * kTile;
-  const int64_t nrows = (row0 + rows - r_begin) < kTile ? (row0 + rows - r_begin) : kTile;
+  const int64_t r_begin = row0 + static_cast<int64_t>(blockIdx.x) * rpw;
+  const int64_t nrows = (row0 + rows - r_begin) < rpw ? (row0 + rows - r_begin) : rpw;
   const int npairs = static_cast<int>(nrows) * topk;
   const int64_t p_begin = (r_begin - row0) * topk;  // chunk-relative pair id of the first pair
   const int64_t bucket0 = (r_begin / n - bh0) * nb;
@@ -128,11 +129,29 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const int32_t* __rest
   }
 }
 
+// Pair ids into per-bucket lists.  Threads p < nbuckets also write, for each
+// work item of bucket p, the record {bucket, first list position, pair count}
+// at the slot of the workgroup that will run it: items are spread so that
+// consecutive items (one head, neighbouring blocks) go to one XCD, i.e.
+// item = xcd * per_xcd + j runs as workgroup j * 8 + xcd.
 __global__ __launch_bounds__(256) void bucket_fill_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
-    const int32_t* __restrict__ offsets, int32_t* __restrict__ list, int64_t row0, int64_t npairs,
-    int n, int topk, int64_t bh0) {
+    const int32_t* __restrict__ offsets, const int32_t* __restrict__ items,
+    int4* __restrict__ item_rec, int nbuckets, int64_t max_slots, int32_t* __restrict__ list,
+    int64_t row0, int64_t npairs, int n, int topk, int64_t bh0) {
   const int64_t p = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (p < nbuckets) {
+    const int32_t total = items[nbuckets];
+    const int32_t per_xcd = (total + kXcds - 1) / kXcds;
+    const int32_t cnt = offsets[p + 1] - offsets[p];
+    for (int32_t i = items[p], u = 0; i < items[p + 1]; ++i, ++u) {
+      const int64_t slot = static_cast<int64_t>(i % per_xcd) * kXcds + i / per_xcd;
+      const int32_t left = cnt - u * kItemPairs;
+      if (slot < max_slots)
+        item_rec[slot] = make_int4(static_cast<int32_t>(p), offsets[p] + u * kItemPairs,
+                                   left < kItemPairs ? left : kItemPairs, 0);
+    }
+  }
   if (p >= npairs) return;
   const int32_t rk = rank[p];
   if (rk < 0) return;
@@ -144,274 +163,311 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(
   if (pos < npairs) list[pos] = static_cast<int32_t>(p);
 }
 
-template <typename T, int D>
-struct GatherLayout {
-  static constexpr bool kBf16 = sizeof(T) == 2;
-  static constexpr int KPITCH = D + (kBf16 ? 8 : 4);
-  static constexpr int VROWS = kBf16 ? D : kTile;
-  static constexpr int VPITCH = kBf16 ? kTile + 4 : D + 4;
-  static constexpr int K_BYTES = kTile * KPITCH * sizeof(T);
-  static constexpr int V_BYTES = VROWS * VPITCH * sizeof(T);
-  static constexpr int BYTES = K_BYTES + V_BYTES;
-};
-
-// Stage key block `beta` of head base pointers kb / vb into LDS (K as is,
-// V transposed for bf16).
-template <typename T, int D>
-__device__ __forceinline__ void stage_block(const T* __restrict__ kb, const T* __restrict__ vb,
-                                            int beta, T* ks, T* vs, int tid) {
-  using L = GatherLayout<T, D>;
-  const int64_t key0 = static_cast<int64_t>(beta) * kTile;
-  if constexpr (L::kBf16) {
-    for (int c = tid; c < kTile * D / 8; c += 256) {
-      const int c8 = c % (D / 8), row = c / (D / 8);
-      *reinterpret_cast<uint4*>(ks + row * L::KPITCH + c8 * 8) = ld16(kb + (key0 + row) * D + c8 * 8);
-    }
-    for (int it = tid; it < (kTile / 2) * (D / 8); it += 256) {
-      const int c8 = it % (D / 8), p = it / (D / 8);
-      const uint4 ra = ld16(vb + (key0 + 2 * p) * D + c8 * 8);
-      const uint4 rb = ld16(vb + (key0 + 2 * p + 1) * D + c8 * 8);
-      const uint32_t a[4] = {ra.x, ra.y, ra.z, ra.w};
-      const uint32_t b[4] = {rb.x, rb.y, rb.z, rb.w};
-      uint32_t* dst = reinterpret_cast<uint32_t*>(vs + (c8 * 8) * L::VPITCH + 2 * p);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dst[(2 * e) * (L::VPITCH / 2)] = (a[e] & 0xFFFFu) | (b[e] << 16);
-        dst[(2 * e + 1) * (L::VPITCH / 2)] = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
-      }
-    }
-  } else {
-    for (int c = tid; c < kTile * D / 4; c += 256) {
-      const int c4 = c % (D / 4), row = c / (D / 4);
-      *reinterpret_cast<uint4*>(ks + row * L::KPITCH + c4 * 4) = ld16(kb + (key0 + row) * D + c4 * 4);
-      *reinterpret_cast<uint4*>(vs + row * L::VPITCH + c4 * 4) = ld16(vb + (key0 + row) * D + c4 * 4);
-    }
-  }
-}
-
 // bf16 inputs keep partial outputs as fp16 (|o| <= max |v|, relative error
 // 2^-11), fp32 inputs as fp32.
 template <typename T>
 using PartialT = typename std::conditional<sizeof(T) == 2, f16, float>::type;
 
+// Query operand of S^T = K Q^T for one lane: its pair's query row, the d
+// slots of MFMA k-group lane/16.
+template <typename T, int D>
+union QOperand {
+  bf16x8 b[D / 32];
+  float f[D / 4];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void load_q(QOperand<T, D>& qo, const T* __restrict__ q, int64_t row,
+                                       bool live, int g) {
+  if constexpr (sizeof(T) == 2) {
+    const T* qp = q + row * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) qo.b[kk] = live ? as_bf16x8(ld16(qp + 32 * kk)) : bf16x8{};
+  } else {
+    constexpr int KS = D / 4;
+    const T* qp = q + row * D + KS * g;
+#pragma unroll
+    for (int e = 0; e < KS; e += 4) {
+      const uint4 u = live ? ld16(qp + e) : uint4{0u, 0u, 0u, 0u};
+      qo.f[e] = __uint_as_float(u.x);
+      qo.f[e + 1] = __uint_as_float(u.y);
+      qo.f[e + 2] = __uint_as_float(u.z);
+      qo.f[e + 3] = __uint_as_float(u.w);
+    }
+  }
+}
+
+// Output dim carried by row m of PV output tile dt (bf16 path).  The V^T
+// rows fed to each MFMA tile are permuted so that the lanes of row group
+// g = m/4 end up holding 8 consecutive dims per pair of tiles: tiles 2u and
+// 2u+1 cover dims 32u .. 32u+31, group g takes 32u + 8g .. 32u + 8g + 7, the
+// first tile of the pair the lower 4 of those.  A bijection on 0 .. D-1.
+template <int D>
+__device__ __forceinline__ int out_dim(int dt, int m) {
+  return 32 * (dt / 2) + 8 * (m / 4) + 4 * (dt % 2) + (m % 4);
+}
+
+// One group of 16 pairs sharing key block `beta` (K, V^T in LDS): the lane
+// computes column lane%16 (its pair) and writes the pair's partial
+// (m in log2 units, l, o = sum 2^(z-m) v / l).  The softmax scale is folded
+// into the exp2 argument (the max is taken on raw scores; the scale is > 0),
+// and for bf16 inputs l comes out of the PV MFMA itself: one more 16-row
+// output tile whose A operand is a row of ones multiplies the same rounded
+// probabilities, so l sums exactly the weights that enter o.
+template <typename T, int D, bool CAUSAL>
+__device__ __forceinline__ void pair_group(const T* ks, const T* vs, const QOperand<T, D>& qo,
+                                           int64_t row, int beta, int n, bool live, int32_t pair,
+                                           float scale_log2, PartialT<T>* __restrict__ po,
+                                           float2* __restrict__ pml, int lane) {
+  using L = KvLayout<T, D>;
+  const int g = lane >> 4, c16 = lane & 15;
+  f32x4 s[4];
+  if constexpr (L::kBf16) {
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (16 * tt + c16) * L::KPITCH + 8 * g + 32 * kk);
+        s[tt] = mfma_16x16x32_bf16(a, qo.b[kk], s[tt]);
+      }
+    }
+  } else {
+    constexpr int KS = D / 4;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+      s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const T* kr = ks + (16 * tt + c16) * L::KPITCH + KS * g;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) s[tt] = mfma_16x16x4_f32(kr[kk], qo.f[kk], s[tt]);
+    }
+  }
+  if (CAUSAL) {
+    const int qi = static_cast<int>(row % n);
+    if (beta == qi / kTile) {  // diagonal block: keys after the query are hidden
+      const int qlocal = qi % kTile;
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+          if (16 * tt + 4 * g + jj > qlocal) s[tt][jj] = -INFINITY;
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt)
+    mx = fmaxf(mx, fmaxf(fmaxf(s[tt][0], s[tt][1]), fmaxf(s[tt][2], s[tt][3])));
+  mx = fmaxf(mx, __shfl_xor(mx, 16));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));  // a live pair has >= 1 visible key: finite
+  const float m = mx * scale_log2;     // log2-domain max
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float lt;
+  if constexpr (L::kBf16) {
+    bf16x8 bp[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        bp[kk][i] = f32_to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * kk][i], scale_log2, -m)));
+        bp[kk][4 + i] = f32_to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * kk + 1][i], scale_log2, -m)));
+      }
+    const __bf16 one = static_cast<__bf16>(c16 == 0 ? 1.0f : 0.0f);
+    const bf16x8 ones = {one, one, one, one, one, one, one, one};
+    f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const T* vr = vs + out_dim<D>(dt, c16) * L::VPITCH + 32 * kk + 4 * g;
+        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
+        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[dt] = mfma_16x16x32_bf16(a, bp[kk], acc[dt]);
+      }
+      lacc = mfma_16x16x32_bf16(ones, bp[kk], lacc);
+    }
+    // row 0 of the ones tile (lane c16, element 0) holds l of query c16
+    lt = __shfl(lacc[0], c16);
+  } else {
+    float p[4][4];
+    float lsum = 0.f;
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        p[tt][jj] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][jj], scale_log2, -m));
+        lsum += p[tt][jj];
+      }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const T* vr = vs + (16 * tt + 4 * g + jj) * L::VPITCH + c16;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma_16x16x4_f32(vr[16 * dt], p[tt][jj], acc[dt]);
+      }
+    lt = lsum + __shfl_xor(lsum, 16);
+    lt += __shfl_xor(lt, 32);
+  }
+  if (!live) return;
+  const float inv = 1.0f / lt;
+  PartialT<T>* op = po + static_cast<int64_t>(pair) * D;
+  if constexpr (L::kBf16) {
+    // tiles 2u, 2u+1 hold dims 32u*(D/64) + 8g .. +7: one 16-byte store each,
+    // the 4 lanes of a pair writing 64 contiguous bytes per instruction
+#pragma unroll
+    for (int u = 0; u < D / 32; ++u) {
+      const f32x4 a0 = acc[2 * u] * inv, a1 = acc[2 * u + 1] * inv;
+      typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+      const f16x8 h = {static_cast<f16>(a0[0]), static_cast<f16>(a0[1]), static_cast<f16>(a0[2]),
+                       static_cast<f16>(a0[3]), static_cast<f16>(a1[0]), static_cast<f16>(a1[1]),
+                       static_cast<f16>(a1[2]), static_cast<f16>(a1[3])};
+      *reinterpret_cast<f16x8*>(op + out_dim<D>(2 * u, 4 * g)) = h;
+    }
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const f32x4 a = acc[dt] * inv;
+      *reinterpret_cast<float4*>(op + 16 * dt + 4 * g) = make_float4(a[0], a[1], a[2], a[3]);
+    }
+  }
+  if (g == 0) pml[pair] = make_float2(m, lt);
+}
+
+// One work item = up to kItemPairs pairs of one bucket (head, key block),
+// described by the record the fill kernel left at this workgroup's slot.
+// Every load the item needs is issued before any is waited on: the wave's
+// list entries, the block's K/V into registers, then (as the list entries
+// arrive) the pairs' query rows; then K/V go to LDS and the MFMA work runs.
+// row = pair / topk uses a precomputed multiply-shift (exact for pair < 2^31).
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void gather_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const int32_t* __restrict__ list, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ items, int nbuckets, int64_t row0, int64_t npairs, int n,
-    int topk, int64_t bh0, float scale_log2, PartialT<T>* __restrict__ po,
-    float2* __restrict__ pml) {
-  using L = GatherLayout<T, D>;
+    const int32_t* __restrict__ list, const int32_t* __restrict__ items,
+    const int4* __restrict__ item_rec, int nbuckets, int64_t row0, int64_t npairs, int n,
+    uint64_t div_magic, int div_shift, int64_t bh0, float scale_log2,
+    PartialT<T>* __restrict__ po, float2* __restrict__ pml) {
+  using L = KvLayout<T, D>;
+  constexpr int GPW = kItemPairs / 16 / 4;  // 16-pair groups per wave
   __shared__ __align__(16) unsigned char smem[L::BYTES];
-  __shared__ int s_bucket;
   T* ks = reinterpret_cast<T*>(smem);
   T* vs = reinterpret_cast<T*>(smem + L::K_BYTES);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
 
-  // Work item of this workgroup: consecutive items go to one XCD.
   const int total = items[nbuckets];
+  const int4 rec = item_rec[blockIdx.x];
   const int per_xcd = (total + kXcds - 1) / kXcds;
   const int slot = static_cast<int>(blockIdx.x) / kXcds;
-  if (slot >= per_xcd) return;
   const int item = (static_cast<int>(blockIdx.x) % kXcds) * per_xcd + slot;
-  if (item >= total) return;
-  if (tid == 0) {
-    int lo = 0, hi = nbuckets - 1;  // last bucket with items[b] <= item
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (items[mid] <= item) lo = mid;
-      else hi = mid - 1;
-    }
-    s_bucket = lo;
-  }
-  __syncthreads();
-  const int b = s_bucket;
+  if (slot >= per_xcd || item >= total) return;  // no item for this workgroup
+  const int b = rec.x;
+  if (b < 0 || b >= nbuckets) return;
+  const int64_t first = rec.y;
+  int cnt = rec.z;
+  if (cnt > kItemPairs) cnt = kItemPairs;
+  if (first + cnt > npairs) cnt = first < npairs ? static_cast<int>(npairs - first) : 0;
   const int nb = n / kTile;
   const int beta = b % nb;
   const int64_t bh = bh0 + b / nb;
-  const int64_t first = static_cast<int64_t>(offsets[b]) + static_cast<int64_t>(item - items[b]) * kItemPairs;
-  int64_t last = offsets[b + 1];
-  if (last > npairs) last = npairs;
-  const int cnt = first < last ? static_cast<int>((last - first) < kItemPairs ? (last - first) : kItemPairs) : 0;
-  const T* kb = k + bh * static_cast<int64_t>(n) * D;
-  const T* vb = v + bh * static_cast<int64_t>(n) * D;
-  stage_block<T, D>(kb, vb, beta, ks, vs, tid);
-  __syncthreads();
 
-  for (int grp = wave; grp * 16 < cnt; grp += 4) {
-    const int t = grp * 16 + c16;
-    const bool live = t < cnt;
-    int32_t pair = 0;
-    if (live) pair = list[first + t];
-    if (pair < 0 || pair >= npairs) pair = 0;
-    const int64_t row = row0 + pair / topk;
-    const int qi = static_cast<int>(row % n);
-    // S^T = K Q^T: lane holds scores of its pair's query for keys 16t+4g+jj.
-    f32x4 s[4];
-    if constexpr (L::kBf16) {
-      bf16x8 qb[D / 32];
-      const T* qp = q + row * D + 8 * g;
+  int32_t pair[GPW];
+  bool live[GPW];
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) qb[kk] = live ? as_bf16x8(ld16(qp + 32 * kk)) : bf16x8{};
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int t = (wave + 4 * gi) * 16 + c16;
+    live[gi] = t < cnt;
+    pair[gi] = live[gi] ? list[first + t] : 0;
+  }
+  KvRegs<T, D> kv;
+  kv_load<T, D>(kv, k + bh * static_cast<int64_t>(n) * D, v + bh * static_cast<int64_t>(n) * D,
+                beta, tid);
+  QOperand<T, D> qo[GPW];
+  int64_t row[GPW];
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (16 * tt + c16) * L::KPITCH + 8 * g + 32 * kk);
-          s[tt] = mfma_16x16x32_bf16(a, qb[kk], s[tt]);
-        }
-      }
-    } else {
-      constexpr int KS = D / 4;
-      float qf[KS];
-      const T* qp = q + row * D + KS * g;
-#pragma unroll
-      for (int e = 0; e < KS; e += 4) {
-        const uint4 u = live ? ld16(qp + e) : uint4{0u, 0u, 0u, 0u};
-        qf[e] = __uint_as_float(u.x);
-        qf[e + 1] = __uint_as_float(u.y);
-        qf[e + 2] = __uint_as_float(u.z);
-        qf[e + 3] = __uint_as_float(u.w);
-      }
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const T* kr = ks + (16 * tt + c16) * L::KPITCH + KS * g;
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) s[tt] = mfma_16x16x4_f32(kr[kk], qf[kk], s[tt]);
-      }
+  for (int gi = 0; gi < GPW; ++gi) {
+    if (pair[gi] < 0 || pair[gi] >= npairs) {
+      pair[gi] = 0;
+      live[gi] = false;
     }
-    const bool diag = CAUSAL && beta == qi / kTile;
-    const int qlocal = qi % kTile;
-    float mx = -INFINITY;
+    row[gi] = row0 + static_cast<int64_t>((static_cast<uint64_t>(pair[gi]) * div_magic) >> div_shift);
+    load_q<T, D>(qo[gi], q, row[gi], live[gi], g);
+  }
+  kv_store<T, D>(kv, ks, vs, tid);
+  __syncthreads();
 #pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const bool vis = !diag || (16 * tt + 4 * g + jj) <= qlocal;
-        const float z = vis ? s[tt][jj] * scale_log2 : -INFINITY;
-        s[tt][jj] = z;
-        mx = fmaxf(mx, z);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));  // >= 1 visible key per pair: finite
-    f32x4 acc[D / 16];
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.f;
-    if constexpr (L::kBf16) {
-      __bf16 pb[4][4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          pb[tt][jj] = f32_to_bf16(__builtin_amdgcn_exp2f(s[tt][jj] - mx));
-          lsum += static_cast<float>(pb[tt][jj]);
-        }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 bp;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          bp[i] = pb[2 * kk][i];
-          bp[4 + i] = pb[2 * kk + 1][i];
-        }
-#pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const T* vr = vs + (16 * dt + c16) * L::VPITCH + 32 * kk + 4 * g;
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vr);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vr + 16);
-          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[dt] = mfma_16x16x32_bf16(a, bp, acc[dt]);
-        }
-      }
-    } else {
-      float p[4][4];
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          p[tt][jj] = __builtin_amdgcn_exp2f(s[tt][jj] - mx);
-          lsum += p[tt][jj];
-        }
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const T* vr = vs + (16 * tt + 4 * g + jj) * L::VPITCH + c16;
-#pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma_16x16x4_f32(vr[16 * dt], p[tt][jj], acc[dt]);
-        }
-    }
-    float lt = lsum + __shfl_xor(lsum, 16);
-    lt += __shfl_xor(lt, 32);
-    if (live) {
-      const float inv = 1.0f / lt;
-      PartialT<T>* op = po + static_cast<int64_t>(pair) * D + 4 * g;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const f32x4 a = acc[dt] * inv;
-        if constexpr (L::kBf16) {
-          const f16x4 h = {static_cast<f16>(a[0]), static_cast<f16>(a[1]), static_cast<f16>(a[2]),
-                           static_cast<f16>(a[3])};
-          *reinterpret_cast<f16x4*>(op + 16 * dt) = h;
-        } else {
-          *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(a[0], a[1], a[2], a[3]);
-        }
-      }
-      if (g == 0) pml[pair] = make_float2(mx, lt);
-    }
+  for (int gi = 0; gi < GPW; ++gi) {
+    if ((wave + 4 * gi) * 16 >= cnt) break;  // wave-uniform
+    pair_group<T, D, CAUSAL>(ks, vs, qo[gi], row[gi], beta, n, live[gi], pair[gi], scale_log2, po,
+                             pml, lane);
   }
 }
 
-// One group of 16 lanes per query row; lane holds D/16 consecutive dims.
+// One group of 16 lanes per query row.  Lane c reads the (m, l) of slots
+// c, c + 16, ... so a row's partial headers arrive together; the row max and
+// the weight sum are 16-lane shuffle reductions.  Then, 16 slots at a time,
+// every lane issues the loads of its D/16 dims of all 16 partials before
+// using any (slot index clamped into the row, so every load is in bounds;
+// padding slots carry weight 0 and are zeroed by a select, since their buffer
+// entries were never written), and accumulates in slot order.  Any topk.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ idx,
                                                       const PartialT<T>* __restrict__ po,
                                                       const float2* __restrict__ pml,
                                                       float* __restrict__ out, int64_t row0,
                                                       int64_t rows, int n, int topk, int causal) {
-  constexpr int E = D / 16;
+  constexpr int E = D / 16;  // dims per lane
+  constexpr int V = E / 4;   // 4-element loads per lane and slot
+  typedef typename std::conditional<sizeof(T) == 2, f16x4, f32x4>::type Vec;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   if (r >= rows) return;
   const int c = threadIdx.x & 15;
+  const int gbase = (threadIdx.x & 63) & ~15;
   const int64_t row = row0 + r;
   const int nb = n / kTile;
   const int32_t* sel = idx + row * topk;
+  const float2* ml = pml + r * topk;
   float mmax = -INFINITY;
-  for (int s = 0; s < topk; ++s)
-    if (pair_valid(sel[s], nb, row, n, causal)) mmax = fmaxf(mmax, pml[r * topk + s].x);
+  for (int s = c; s < topk; s += 16)
+    if (pair_valid(sel[s], nb, row, n, causal)) mmax = fmaxf(mmax, ml[s].x);
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off, 16));
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float wsum = 0.f;
-  for (int s = 0; s < topk; ++s) {
-    if (!pair_valid(sel[s], nb, row, n, causal)) continue;
-    const int64_t p = r * topk + s;
-    const float2 ml = pml[p];
-    const float w = ml.y * __builtin_amdgcn_exp2f(ml.x - mmax);
-    wsum += w;
-    const PartialT<T>* src = po + p * D + c * E;
-    if constexpr (sizeof(T) == 2) {
+  const PartialT<T>* src = po + r * topk * D + c * E;
+  for (int s0 = 0; s0 < topk; s0 += 16) {
+    Vec x[16][V];
 #pragma unroll
-      for (int e = 0; e < E; e += 4) {
-        const f16x4 h = *reinterpret_cast<const f16x4*>(src + e);
+    for (int t = 0; t < 16; ++t) {
+      const int st = s0 + t < topk ? s0 + t : topk - 1;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) acc[e + u] += w * static_cast<float>(h[u]);
-      }
-    } else {
+      for (int u = 0; u < V; ++u)
+        x[t][u] = __builtin_nontemporal_load(reinterpret_cast<const Vec*>(src + static_cast<int64_t>(st) * D) + u);
+    }
+    float wl = 0.f;  // weight of slot s0 + c
+    if (s0 + c < topk && pair_valid(sel[s0 + c], nb, row, n, causal)) {
+      const float2 v = ml[s0 + c];
+      wl = v.y * __builtin_amdgcn_exp2f(v.x - mmax);
+    }
+    wsum += wl;
 #pragma unroll
-      for (int e = 0; e < E; e += 4) {
-        const float4 f = *reinterpret_cast<const float4*>(src + e);
-        acc[e] += w * f.x;
-        acc[e + 1] += w * f.y;
-        acc[e + 2] += w * f.z;
-        acc[e + 3] += w * f.w;
-      }
+    for (int t = 0; t < 16; ++t) {
+      const float ws = __shfl(wl, gbase + t);
+#pragma unroll
+      for (int u = 0; u < V; ++u)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float xv = static_cast<float>(x[t][u][q4]);
+          acc[4 * u + q4] += ws != 0.f ? ws * xv : 0.f;
+        }
     }
   }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off, 16);
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   float* dst = out + row * D + c * E;
 #pragma unroll
@@ -435,20 +491,25 @@ struct ChunkGeom {
 template <typename T, int D>
 hipError_t partial_chunk(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
   const ChunkGeom c(a, row0, rows);
-  const int64_t max_items = (c.npairs + kItemPairs - 1) / kItemPairs + c.nbuckets;
-  const int64_t grid = (max_items + kXcds - 1) / kXcds * kXcds;
+  const int64_t grid = gather_grid(rows, a.topk, c.nbuckets);
   const float sl2 = a.scale * kLog2e;
   auto* po = reinterpret_cast<PartialT<T>*>(a.ws.partial_o);
+  // pair / topk as (pair * magic) >> shift: shift = 32 + ceil(log2 topk),
+  // magic = ceil(2^shift / topk); exact for every pair < 2^31.
+  int lg = 0;
+  while ((1 << lg) < a.topk) ++lg;
+  const int shift = 32 + lg;
+  const uint64_t magic = ((uint64_t(1) << shift) + uint64_t(a.topk) - 1) / uint64_t(a.topk);
   if (a.causal)
     hipLaunchKernelGGL((gather_partial_kernel<T, D, true>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), a.ws.list, a.ws.offsets, a.ws.items, c.nbuckets,
-                       row0, c.npairs, a.n, a.topk, c.bh0, sl2, po, a.ws.partial_ml);
+                       static_cast<const T*>(a.v), a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets,
+                       row0, c.npairs, a.n, magic, shift, c.bh0, sl2, po, a.ws.partial_ml);
   else
     hipLaunchKernelGGL((gather_partial_kernel<T, D, false>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
-                       static_cast<const T*>(a.v), a.ws.list, a.ws.offsets, a.ws.items, c.nbuckets,
-                       row0, c.npairs, a.n, a.topk, c.bh0, sl2, po, a.ws.partial_ml);
+                       static_cast<const T*>(a.v), a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets,
+                       row0, c.npairs, a.n, magic, shift, c.bh0, sl2, po, a.ws.partial_ml);
   return hipGetLastError();
 }
 
@@ -462,6 +523,11 @@ hipError_t combine_chunk(const GatherArgs& a, int64_t row0, int64_t rows, hipStr
 
 }  // namespace
 
+int64_t gather_grid(int64_t rows, int topk, int64_t nbuckets) {
+  const int64_t max_items = (rows * topk + kItemPairs - 1) / kItemPairs + nbuckets;
+  return (max_items + kXcds - 1) / kXcds * kXcds;
+}
+
 size_t gather_pair_bytes(int d, bsa_dtype dtype) {
   return static_cast<size_t>(d) * (dtype == BSA_BF16 ? 2 : 4) + sizeof(float2);
 }
@@ -470,13 +536,16 @@ hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, 
   const ChunkGeom c(a, row0, rows);
   hipLaunchKernelGGL(zero_i32_kernel, dim3(static_cast<unsigned>((c.nbuckets + 255) / 256)), dim3(256),
                      0, s, a.ws.count, static_cast<int64_t>(c.nbuckets));
-  hipLaunchKernelGGL(bucket_count_kernel, dim3(static_cast<unsigned>((rows + kTile - 1) / kTile)),
+  const int rpw = (a.n % 256 == 0 && row0 % 256 == 0) ? 256 : kTile;
+  hipLaunchKernelGGL(bucket_count_kernel, dim3(static_cast<unsigned>((rows + rpw - 1) / rpw)),
                      dim3(256), static_cast<size_t>(c.nb) * 8, s, a.idx, a.ws.count, a.ws.rank, row0,
-                     rows, a.n, a.topk, a.causal, c.bh0);
+                     rows, a.n, a.topk, a.causal, c.bh0, rpw);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, a.ws.count, a.ws.offsets,
                      a.ws.items, c.nbuckets);
-  hipLaunchKernelGGL(bucket_fill_kernel, dim3(static_cast<unsigned>((c.npairs + 255) / 256)), dim3(256),
-                     0, s, a.idx, a.ws.rank, a.ws.offsets, a.ws.list, row0, c.npairs, a.n, a.topk,
+  const int64_t nthreads = c.npairs > c.nbuckets ? c.npairs : c.nbuckets;
+  hipLaunchKernelGGL(bucket_fill_kernel, dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256),
+                     0, s, a.idx, a.ws.rank, a.ws.offsets, a.ws.items, a.ws.item_rec, c.nbuckets,
+                     gather_grid(rows, a.topk, c.nbuckets), a.ws.list, row0, c.npairs, a.n, a.topk,
                      c.bh0);
   return hipGetLastError();
 }

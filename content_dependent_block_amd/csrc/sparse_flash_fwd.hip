@@ -33,92 +33,12 @@
 // MFMA work (register double buffering).
 #include "bsa_device.hpp"
 #include "bsa_launch.hpp"
+#include "kv_tile.hpp"
 
 namespace bsa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-
-template <typename T, int D>
-struct FineLayout {
-  static constexpr bool kBf16 = sizeof(T) == 2;
-  static constexpr int KPITCH = D + (kBf16 ? 8 : 4);        // elements per K row
-  static constexpr int VROWS = kBf16 ? D : kTile;           // bf16: V^T rows are d
-  static constexpr int VPITCH = kBf16 ? kTile + 4 : D + 4;  // elements per V row
-  static constexpr int K_BYTES = kTile * KPITCH * sizeof(T);
-  static constexpr int V_BYTES = VROWS * VPITCH * sizeof(T);
-  static constexpr int TILE_BYTES = (K_BYTES + V_BYTES + 15) / 16 * 16;
-  // Global->register chunks (16 B) per thread.
-  static constexpr int KCH = kBf16 ? D / 32 : D / 16;
-  static constexpr int VCH = kBf16 ? D / 32 : D / 16;  // bf16: D/64 key pairs x 2 rows
-};
-
-template <typename T, int D>
-struct TileRegs {
-  uint4 kr[FineLayout<T, D>::KCH];
-  uint4 vr[FineLayout<T, D>::VCH];
-};
-
-// Issue the global loads of key tile `kt` of head base pointers kb / vb.
-template <typename T, int D>
-__device__ __forceinline__ void load_tile(TileRegs<T, D>& r, const T* __restrict__ kb,
-                                          const T* __restrict__ vb, int kt, int tid) {
-  using L = FineLayout<T, D>;
-  const int64_t key0 = static_cast<int64_t>(kt) * kTile;
-  if constexpr (L::kBf16) {
-#pragma unroll
-    for (int u = 0; u < L::KCH; ++u) {
-      const int c = tid + 256 * u, c8 = c % (D / 8), row = c / (D / 8);
-      r.kr[u] = ld16(kb + (key0 + row) * D + c8 * 8);
-    }
-#pragma unroll
-    for (int u = 0; u < L::VCH / 2; ++u) {
-      const int it = tid + 256 * u, c8 = it % (D / 8), p = it / (D / 8);
-      r.vr[2 * u] = ld16(vb + (key0 + 2 * p) * D + c8 * 8);
-      r.vr[2 * u + 1] = ld16(vb + (key0 + 2 * p + 1) * D + c8 * 8);
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < L::KCH; ++u) {
-      const int c = tid + 256 * u, c4 = c % (D / 4), row = c / (D / 4);
-      r.kr[u] = ld16(kb + (key0 + row) * D + c4 * 4);
-      r.vr[u] = ld16(vb + (key0 + row) * D + c4 * 4);
-    }
-  }
-}
-
-template <typename T, int D>
-__device__ __forceinline__ void store_tile(const TileRegs<T, D>& r, T* ks, T* vs, int tid) {
-  using L = FineLayout<T, D>;
-  if constexpr (L::kBf16) {
-#pragma unroll
-    for (int u = 0; u < L::KCH; ++u) {
-      const int c = tid + 256 * u, c8 = c % (D / 8), row = c / (D / 8);
-      *reinterpret_cast<uint4*>(ks + row * L::KPITCH + c8 * 8) = r.kr[u];
-    }
-#pragma unroll
-    for (int u = 0; u < L::VCH / 2; ++u) {
-      const int it = tid + 256 * u, c8 = it % (D / 8), p = it / (D / 8);
-      const uint32_t a[4] = {r.vr[2 * u].x, r.vr[2 * u].y, r.vr[2 * u].z, r.vr[2 * u].w};
-      const uint32_t b[4] = {r.vr[2 * u + 1].x, r.vr[2 * u + 1].y, r.vr[2 * u + 1].z,
-                             r.vr[2 * u + 1].w};
-      uint32_t* dst = reinterpret_cast<uint32_t*>(vs + (c8 * 8) * L::VPITCH + 2 * p);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // d = c8*8 + 2e (low halves) and + 2e + 1 (high halves); keys 2p, 2p+1.
-        dst[(2 * e) * (L::VPITCH / 2)] = (a[e] & 0xFFFFu) | (b[e] << 16);
-        dst[(2 * e + 1) * (L::VPITCH / 2)] = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int u = 0; u < L::KCH; ++u) {
-      const int c = tid + 256 * u, c4 = c % (D / 4), row = c / (D / 4);
-      *reinterpret_cast<uint4*>(ks + row * L::KPITCH + c4 * 4) = r.kr[u];
-      *reinterpret_cast<uint4*>(vs + row * L::VPITCH + c4 * 4) = r.vr[u];
-    }
-  }
-}
 
 // Per-lane online-softmax state: query row = lane % 16 of this wave; the lane
 // accumulates O[row][16*dt + 4*(lane/16) + jj].
@@ -135,7 +55,7 @@ template <typename T, int D>
 __device__ __forceinline__ void tile_step(RowState<D>& st, const T* ks, const T* vs,
                                           const void* qreg, uint32_t vis, float scale_log2,
                                           int lane) {
-  using L = FineLayout<T, D>;
+  using L = KvLayout<T, D>;
   const int g = lane >> 4, c16 = lane & 15;
   f32x4 s[4];
   if constexpr (L::kBf16) {
@@ -233,11 +153,11 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
     float* __restrict__ out, const int32_t* __restrict__ idx, int topk,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
     const uint64_t* __restrict__ rowmask, int64_t nnz, int n, float scale_log2) {
-  using L = FineLayout<T, D>;
+  using L = KvLayout<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   T* ks = reinterpret_cast<T*>(smem);
   T* vs = reinterpret_cast<T*>(smem + L::K_BYTES);
-  uint64_t* rm = reinterpret_cast<uint64_t*>(smem + L::TILE_BYTES);  // dynamic: per-block row bits
+  uint64_t* rm = reinterpret_cast<uint64_t*>(smem + L::BYTES);  // dynamic: per-block row bits
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
@@ -322,15 +242,15 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
   st.m = -INFINITY;
   st.l = 0.f;
 
-  TileRegs<T, D> regs;
+  KvRegs<T, D> regs;
   int cur = nlist > 0 ? tile_at(0) : -1;
-  if (cur >= 0) load_tile<T, D>(regs, kb, vb, cur, tid);
+  if (cur >= 0) kv_load<T, D>(regs, kb, vb, cur, tid);
   for (int it = 0; it < nlist; ++it) {
     __syncthreads();
-    if (cur >= 0) store_tile<T, D>(regs, ks, vs, tid);
+    if (cur >= 0) kv_store<T, D>(regs, ks, vs, tid);
     __syncthreads();
     const int nxt = it + 1 < nlist ? tile_at(it + 1) : -1;
-    if (nxt >= 0) load_tile<T, D>(regs, kb, vb, nxt, tid);
+    if (nxt >= 0) kv_load<T, D>(regs, kb, vb, nxt, tid);
     if (cur >= 0) {
       uint32_t vis;
       bool any;
@@ -381,9 +301,9 @@ hipError_t launch_one(const void* q, const void* k, const void* v, float* out, c
                       int topk, const int32_t* row_ptr, const int32_t* col,
                       const uint64_t* rowmask, int64_t nnz, int64_t bh, int n, float scale,
                       hipStream_t s) {
-  using L = FineLayout<T, D>;
+  using L = KvLayout<T, D>;
   const int nb = n / kTile;
-  size_t smem = L::TILE_BYTES;
+  size_t smem = L::BYTES;
   if (!STATIC) smem += static_cast<size_t>(nb) * 8 + static_cast<size_t>(nb) * 4 + 16;
   const auto kern = sparse_flash_kernel<T, D, STATIC, CAUSAL>;
   if (smem > 64 * 1024) {

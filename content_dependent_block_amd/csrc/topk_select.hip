@@ -1,24 +1,29 @@
-// topk_select.hip -- Stage 1 selection: each query keeps its k highest-scoring
-// blocks (nishantmodi.me "sparse-attention-triton-bench", section "Stage 2:
-// fine attention": take the top-k highest-scoring blocks per query; the
-// indices are int32, section "Two things I wish I knew").
+// topk_select.hip -- Stage 1 selection from a stored score panel: each query
+// keeps its k highest-scoring blocks (nishantmodi.me
+// "sparse-attention-triton-bench", section "Stage 2: fine attention": take the
+// top-k highest-scoring blocks per query; indices are int32, section "Two
+// things I wish I knew").  bsa_forward normally selects inside the coarse
+// scoring kernel instead (coarse_score.hip); this kernel serves the
+// stage-level entry point and the panel strategy.
 //
 // Semantics: candidates are all n/64 blocks, or in the causal variant the
 // blocks up to the query's own block, which is always kept.  k_eff =
 // min(k, #candidates).  Equal scores go to the lower block index and -0 equals
 // +0.  Output: the k_eff indices in ascending order, then -1 up to k.
 //
-// One wavefront per query row; lane l holds the scores of blocks l + 64*j.
-// Scores become order-preserving uint32 keys (-0 folded onto +0; the forced
-// own block gets 0xFFFFFFFF, above every float; non-candidates get 0, below
-// every float).  A binary radix search over the 32 key bits finds the k_eff-th
-// largest key T with one ballot + popcount per bit and per register; it stops
-// early as soon as exactly k_eff keys are >= the current prefix.  The keys
-// above T, plus the lowest-indexed keys equal to T, are then written in
-// ascending index order with ballot / mbcnt prefix counts, so no sort is
-// needed.  All control flow is wave-uniform.
+// Input: the panel of a chunk of query rows, block-major (panel[beta][row]).
+//   k <= 32: one lane per query row (64 rows per wave, 256 contiguous bytes
+//     per block across the wave) offers every candidate, in ascending block
+//     order, to an exact register top-KL list (topk_list.hpp), KL >= k.
+//   k > 32: the whole wave takes one row at a time: lane l holds blocks
+//     l + 64 j, a binary radix search over the 32-bit score keys (ballot +
+//     popcount per bit, stopping once exactly k_eff keys reach the prefix)
+//     finds the k_eff-th largest key T, and ballot / mbcnt prefix counts write
+//     the keys above T, then the lowest-index keys equal to T, in ascending
+//     block order.
 #include "bsa_device.hpp"
 #include "bsa_launch.hpp"
+#include "topk_list.hpp"
 
 namespace bsa {
 namespace {
@@ -28,88 +33,134 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-template <int NPER>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ panel,
-                                                   int32_t* __restrict__ idx, int64_t row0,
-                                                   int64_t rows, int n, int topk, int causal) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
+template <int KL>
+__global__ __launch_bounds__(64) void topk_lane_kernel(const float* __restrict__ panel,
+                                                       int32_t* __restrict__ idx, int64_t row0,
+                                                       int64_t prows, int n, int topk, int causal) {
+  const int lane = threadIdx.x;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 64 + lane;  // prows % 64 == 0
   const int nb = n / kTile;
   const int64_t grow = row0 + r;
-  const int qb = static_cast<int>(grow % n) / kTile;
-  const int nvalid = causal ? (qb + 1 < nb ? qb + 1 : nb) : nb;
+  const int qb = static_cast<int>(grow % n) / kTile;  // the same in all 64 rows
+  const int nvalid = causal ? qb + 1 : nb;
   const int keff = topk < nvalid ? topk : nvalid;
-  const float* src = panel + r * nb;
+  const float* col = panel + r;
+  const int forced = causal ? qb : -1;
 
-  uint32_t key[NPER];
+  TopList<KL> l;
+  l.init();
+  int beta = 0;
+  for (; beta + 8 <= nvalid; beta += 8) {
+    float v[8];
 #pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    const int e = lane + 64 * j;
-    uint32_t kk = 0u;
-    if (e < nvalid) kk = (causal && e == qb) ? 0xFFFFFFFFu : order_key(src[e]);
-    key[j] = kk;
+    for (int u = 0; u < 8; ++u) v[u] = col[static_cast<int64_t>(beta + u) * prows];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) l.offer(beta + u == forced ? INFINITY : v[u], beta + u);
   }
+  for (; beta < nvalid; ++beta) {
+    const float v = col[static_cast<int64_t>(beta) * prows];
+    l.offer(beta == forced ? INFINITY : v, beta);
+  }
+  emit_ascending<KL>(l, keff, topk, idx + grow * topk);
+}
 
-  // Radix search for the threshold.
-  uint32_t prefix = 0u, thr = 0u;
-  bool exact = false;
+// Binary radix search for the k-th largest key over NV keys per lane.
+// Returns P with #{key >= P} >= k; `early` means exactly k keys are >= P,
+// otherwise P is the k-th largest key itself.
+template <int NV>
+__device__ __forceinline__ uint32_t radix_kth(const uint32_t (&key)[NV], int k, bool& early) {
+  uint32_t prefix = 0u;
+  early = false;
   for (int b = 31; b >= 0; --b) {
     const uint32_t cand = prefix | (1u << b);
     int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < NPER; ++j) cnt += __popcll(ballot(key[j] >= cand));
-    if (cnt >= keff) {
+    for (int j = 0; j < NV; ++j) cnt += __popcll(ballot(key[j] >= cand));
+    if (cnt >= k) {
       prefix = cand;
-      if (cnt == keff) {
-        thr = cand - 1u;  // exactly keff keys are > thr
-        exact = true;
+      if (cnt == k) {
+        early = true;
         break;
       }
     }
   }
-  if (!exact) thr = prefix;  // the keff-th largest key
-  int gt = 0;
-#pragma unroll
-  for (int j = 0; j < NPER; ++j) gt += __popcll(ballot(key[j] > thr));
-  const int need = keff - gt;  // how many keys equal to thr to keep (lowest index first)
+  return prefix;
+}
 
-  int32_t* dst = idx + grow * topk;
-  int out_base = 0, eq_base = 0;
+// One wave per row, rows taken in turn; 4 waves per workgroup of 64 rows.
+template <int NPER>
+__global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ panel,
+                                                        int32_t* __restrict__ idx, int64_t row0,
+                                                        int64_t prows, int n, int topk, int causal) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int nb = n / kTile;
+  for (int rr = 0; rr < 16; ++rr) {
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * 64 + wave * 16 + rr;
+    const int64_t grow = row0 + r;
+    const int qb = static_cast<int>(grow % n) / kTile;
+    const int nvalid = causal ? qb + 1 : nb;
+    const int keff = topk < nvalid ? topk : nvalid;
+    int32_t* dst = idx + grow * topk;
+    uint32_t key[NPER];
 #pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    const bool is_eq = key[j] == thr;
-    const uint64_t eqm = ballot(is_eq);
-    const int eq_rank = eq_base + static_cast<int>(lanes_below(eqm));
-    const bool sel = key[j] > thr || (is_eq && eq_rank < need);
-    const uint64_t selm = ballot(sel);
-    if (sel) dst[out_base + static_cast<int>(lanes_below(selm))] = lane + 64 * j;
-    out_base += __popcll(selm);
-    eq_base += __popcll(eqm);
+    for (int j = 0; j < NPER; ++j) {
+      const int e = lane + 64 * j;
+      uint32_t kk = 0u;  // not a candidate: below every score
+      if (e < nvalid)
+        kk = (causal && e == qb) ? 0xffffffffu : order_key(panel[static_cast<int64_t>(e) * prows + r]);
+      key[j] = kk;
+    }
+    bool early;
+    const uint32_t P = radix_kth<NPER>(key, keff, early);
+    const uint32_t thr = early ? P - 1u : P;  // keys > thr are in; ties at thr fill up
+    int gt = 0;
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) gt += __popcll(ballot(key[j] > thr));
+    const int need = keff - gt;
+    int out_base = 0, eq_base = 0;
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      const bool is_eq = key[j] == thr;
+      const uint64_t eqm = ballot(is_eq);
+      const int eq_rank = eq_base + static_cast<int>(lanes_below(eqm));
+      const bool sel = key[j] > thr || (is_eq && eq_rank < need);
+      const uint64_t selm = ballot(sel);
+      if (sel) dst[out_base + static_cast<int>(lanes_below(selm))] = lane + 64 * j;
+      out_base += __popcll(selm);
+      eq_base += __popcll(eqm);
+    }
+    for (int t = keff + lane; t < topk; t += 64) dst[t] = -1;
   }
-  for (int t = keff + lane; t < topk; t += 64) dst[t] = -1;
 }
 
 template <int NPER>
-hipError_t launch(const float* panel, int32_t* idx, int64_t row0, int64_t rows, int n, int topk,
-                  int causal, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
-  hipLaunchKernelGGL(topk_kernel<NPER>, grid, dim3(256), 0, s, panel, idx, row0, rows, n, topk,
-                     causal);
-  return hipGetLastError();
+void launch_wave(const float* panel, int32_t* idx, int64_t row0, int64_t rows, int n, int topk,
+                 int causal, hipStream_t s) {
+  hipLaunchKernelGGL((topk_wave_kernel<NPER>), dim3(static_cast<unsigned>(rows / 64)), dim3(256), 0, s,
+                     panel, idx, row0, rows, n, topk, causal);
 }
 
 }  // namespace
 
 hipError_t launch_topk_select(const float* panel, int32_t* idx, int64_t row0, int64_t rows, int n,
-                              int topk, int causal, hipStream_t stream) {
-  const int nb = n / kTile;
-  if (nb <= 64) return launch<1>(panel, idx, row0, rows, n, topk, causal, stream);
-  if (nb <= 128) return launch<2>(panel, idx, row0, rows, n, topk, causal, stream);
-  if (nb <= 256) return launch<4>(panel, idx, row0, rows, n, topk, causal, stream);
-  if (nb <= 512) return launch<8>(panel, idx, row0, rows, n, topk, causal, stream);
-  if (nb <= 1024) return launch<16>(panel, idx, row0, rows, n, topk, causal, stream);
-  return launch<32>(panel, idx, row0, rows, n, topk, causal, stream);
+                              int topk, int causal, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(rows / 64));
+  if (topk <= 8) {
+    hipLaunchKernelGGL((topk_lane_kernel<8>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, causal);
+  } else if (topk <= 16) {
+    hipLaunchKernelGGL((topk_lane_kernel<16>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, causal);
+  } else if (topk <= 32) {
+    hipLaunchKernelGGL((topk_lane_kernel<32>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, causal);
+  } else {
+    const int nb = n / kTile;
+    if (nb <= 64) launch_wave<1>(panel, idx, row0, rows, n, topk, causal, s);
+    else if (nb <= 128) launch_wave<2>(panel, idx, row0, rows, n, topk, causal, s);
+    else if (nb <= 256) launch_wave<4>(panel, idx, row0, rows, n, topk, causal, s);
+    else if (nb <= 512) launch_wave<8>(panel, idx, row0, rows, n, topk, causal, s);
+    else if (nb <= 1024) launch_wave<16>(panel, idx, row0, rows, n, topk, causal, s);
+    else launch_wave<32>(panel, idx, row0, rows, n, topk, causal, s);
+  }
+  return hipGetLastError();
 }
 
 }  // namespace bsa

@@ -66,7 +66,8 @@ typedef enum {
   BSA_STAGE_FINE = 3,    /* sparse_flash_fwd (the MFMA attention kernel)       */
   BSA_STAGE_GATHER_INDEX = 4,   /* block-gather: bucketing of (query, block) pairs */
   BSA_STAGE_GATHER_COMBINE = 5, /* block-gather: merge of per-block partials       */
-  BSA_NUM_STAGES = 6
+  BSA_STAGE_COARSE_TOPK = 6,    /* coarse_score and topk_select fused in one kernel  */
+  BSA_NUM_STAGES = 7
 } bsa_stage;
 
 /* How the dynamic fine stage visits the selected blocks. */
@@ -80,6 +81,18 @@ typedef enum {
   BSA_FINE_QUERY_TILE = 1
 } bsa_fine_strategy;
 
+/* How bsa_forward runs stage 1 (the selection is the same either way). */
+typedef enum {
+  /* For k <= 32: one kernel scores each 64-query tile against every block
+   * representative and keeps each query's top k in registers, so the score
+   * panel is never stored.  Larger k falls back to BSA_SELECT_PANEL.
+   * Default. */
+  BSA_SELECT_FUSED = 0,
+  /* coarse_score writes the float32 panel (in chunks, see
+   * BSA_OPT_PANEL_CHUNK_BYTES), topk_select reads it back. */
+  BSA_SELECT_PANEL = 1
+} bsa_select_strategy;
+
 /* Tunables for bsa_set_option. */
 typedef enum {
   /* Upper bound in bytes of the fp32 coarse-score panel that stage 1 keeps at
@@ -90,7 +103,9 @@ typedef enum {
   BSA_OPT_FINE_STRATEGY = 1,
   /* Upper bound in bytes of the block-gather partial buffer; query rows are
    * processed in chunks that fit.  Default 1 GiB.  Minimum one 64-query tile. */
-  BSA_OPT_FINE_CHUNK_BYTES = 2
+  BSA_OPT_FINE_CHUNK_BYTES = 2,
+  /* bsa_select_strategy for stage 1 of bsa_forward.  Default BSA_SELECT_FUSED. */
+  BSA_OPT_SELECT_STRATEGY = 3
 } bsa_option;
 
 /* ----------------------------------------------------------- lifetime -- */
@@ -122,7 +137,8 @@ bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes);
 
 /* --------------------------------------------------- dynamic forward -- */
 
-/* Both stages: block_pool -> coarse_score -> topk_select -> sparse_flash_fwd.
+/* Both stages: block_pool -> coarse_score -> topk_select -> sparse_flash_fwd
+ * (coarse_score and topk_select fused for k <= 32, see bsa_select_strategy).
  *  q, k, v        device, [batch][heads][n][d], dtype.
  *  out            device, float32 [batch][heads][n][d].
  *  block_idx_out  device, int32 [batch][heads][n][topk] or NULL.  When given,
@@ -161,16 +177,18 @@ bsa_status bsa_block_pool(bsa_handle h, const void* k, float* repr_out,
                           int batch, int heads, int n, int d, bsa_dtype dtype,
                           int block, void* stream);
 
-/* coarse_score: panel_out[b][h][i][beta] = q_i . repr[beta], float32
- * [batch][heads][n][n/B].  repr is float32 as produced by bsa_block_pool.  In
- * causal mode entries with beta > i/B are unspecified. */
+/* coarse_score: the float32 score panel, stored block-major: with
+ * rows = batch*heads*n and row = (b*heads + h)*n + i,
+ * panel_out[beta * rows + row] = q_i . repr[b][h][beta]  (beta < n/B).
+ * repr is float32 as produced by bsa_block_pool.  In causal mode entries with
+ * beta > i/B are unspecified. */
 bsa_status bsa_coarse_score(bsa_handle h, const void* q, const float* repr,
                             float* panel_out, int batch, int heads, int n, int d,
                             bsa_dtype dtype, int block, int causal, void* stream);
 
-/* topk_select: per row of the float32 panel [batch][heads][n][n/B], the
- * selection exactly as described for bsa_forward, into block_idx_out int32
- * [batch][heads][n][topk]. */
+/* topk_select: per row of the block-major float32 panel laid out as
+ * bsa_coarse_score writes it, the selection exactly as described for
+ * bsa_forward, into block_idx_out int32 [batch][heads][n][topk]. */
 bsa_status bsa_topk_select(bsa_handle h, const float* panel,
                            int32_t* block_idx_out, int batch, int heads, int n,
                            int block, int topk, int causal, void* stream);

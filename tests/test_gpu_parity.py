@@ -32,6 +32,8 @@ def say(*a):
 
 
 STRATEGIES = ["block_gather", "query_tile"]
+# (stage-1 strategy, fine strategy) combinations run end to end
+PATHS = [("fused", "block_gather"), ("panel", "block_gather"), ("fused", "query_tile")]
 
 
 @pytest.fixture(scope="module")
@@ -42,16 +44,18 @@ def bsa():
     lib.close()
 
 
-def use_strategy(m, lib, strategy):
+def use_strategy(m, lib, strategy, select="fused"):
     code = {"block_gather": m.BSA_FINE_BLOCK_GATHER, "query_tile": m.BSA_FINE_QUERY_TILE}[strategy]
     m.bsa_set_option(lib.handle, m.BSA_OPT_FINE_STRATEGY, code)
+    code = {"fused": m.BSA_SELECT_FUSED, "panel": m.BSA_SELECT_PANEL}[select]
+    m.bsa_set_option(lib.handle, m.BSA_OPT_SELECT_STRATEGY, code)
 
 
 @pytest.fixture(autouse=True)
 def _default_strategy(bsa):
     yield
     m, lib = bsa
-    use_strategy(m, lib, "block_gather")
+    use_strategy(m, lib, "block_gather", "fused")
 
 
 def to_dev(inp, dtype):
@@ -164,10 +168,10 @@ def test_coarse_score(bsa, name, causal):
     r = oracle.pool(inp.k, w.block)
     r32 = r.astype(np.float32)
     rep = torch.from_numpy(r32.reshape(w.batch, w.heads, w.nb, w.d)).cuda()
-    panel = torch.full((w.batch, w.heads, w.n, w.nb), float("nan"), dtype=torch.float32, device="cuda")
+    panel = torch.full((w.nb, w.bh * w.n), float("nan"), dtype=torch.float32, device="cuda")
     m.bsa_coarse_score(lib.handle, q, rep, panel, causal=causal)
     torch.cuda.synchronize()
-    got = panel.cpu().numpy().reshape(-1, w.nb)
+    got = panel.cpu().numpy().T  # block-major -> [row, block]
     ref = oracle.scores(inp.q, r32.astype(np.float64), w.block)
     qa = np.abs(inp.q.reshape(w.bh, w.n, w.d)).astype(np.float64)
     ra = np.abs(r32.reshape(w.bh, w.nb, w.d)).astype(np.float64)
@@ -183,7 +187,8 @@ def test_coarse_score(bsa, name, causal):
 # ------------------------------------------------------------ topk_select --
 @pytest.mark.parametrize("nb,k,causal", [(16, 4, False), (16, 32, False), (64, 16, False),
                                          (512, 16, False), (2048, 32, False), (128, 5, True),
-                                         (2048, 32, True), (64, 1, True)])
+                                         (2048, 32, True), (64, 1, True), (512, 64, False),
+                                         (1024, 48, True), (2048, 100, True), (256, 3, False)])
 def test_topk_select_bit_exact(bsa, nb, k, causal):
     """topk_select on a float32 panel with many exact ties and signed zeros,
     against the oracle's selection on the same float32 values."""
@@ -198,7 +203,7 @@ def test_topk_select_bit_exact(bsa, nb, k, causal):
     say(f"[gpu] bsa_topk_select nb={nb} k={k} causal={causal}")
     full = np.zeros((1, 1, n, nb), dtype=np.float32)
     full[:, :, n - rows_total:] = panel
-    dev = torch.from_numpy(full).cuda()
+    dev = torch.from_numpy(np.ascontiguousarray(full.reshape(n, nb).T)).cuda()  # block-major
     idx = torch.empty((1, 1, n, k), dtype=torch.int32, device="cuda")
     m.bsa_topk_select(lib.handle, dev, idx, causal=causal)
     torch.cuda.synchronize()
@@ -234,23 +239,23 @@ def test_fine_forward_on_oracle_indices(bsa, name, causal, dd, strategy):
 
 
 # ------------------------------------------------------------ end to end --
-@pytest.mark.parametrize("strategy", STRATEGIES)
+@pytest.mark.parametrize("select,strategy", PATHS)
 @pytest.mark.parametrize("name", ["tiny_fp32_n1k", "dyn_bf16_n4k"])
-def test_forward_small_workloads_all_rows(bsa, name, strategy):
+def test_forward_small_workloads_all_rows(bsa, name, select, strategy):
     m, lib = bsa
-    use_strategy(m, lib, strategy)
+    use_strategy(m, lib, strategy, select)
     w = W.WORKLOADS[name]
     inp = W.generate(w)
     end_to_end(m, lib, w, inp, np.arange(w.bh * w.n, dtype=np.int64))
 
 
-@pytest.mark.parametrize("strategy", STRATEGIES)
-def test_forward_headline_sampled(bsa, strategy):
+@pytest.mark.parametrize("select,strategy", PATHS)
+def test_forward_headline_sampled(bsa, select, strategy):
     """N=32768, 8 heads, bf16, k=16 in the launch configuration the benchmark
-    times (block_gather); sampled rows against the oracle, plus properties of
-    every row."""
+    times (fused selection, block_gather); sampled rows against the oracle,
+    plus properties of every row."""
     m, lib = bsa
-    use_strategy(m, lib, strategy)
+    use_strategy(m, lib, strategy, select)
     w = W.WORKLOADS["dyn_bf16_n32k"]
     inp = W.generate(w)
     rows = sample_rows(w, 3000, seed=2, extra=[0, 63, w.n - 1, w.n, w.bh * w.n - 1])
@@ -309,10 +314,10 @@ def test_static_window_stride(bsa):
     dict(batch=2, heads=1, n=1024, d=128, dtype="fp32", topk=3, causal=False),   # fp32 D=128
     dict(batch=1, heads=2, n=4096, d=64, dtype="bf16", topk=64, causal=False),   # k = n/64: dense
 ])
-@pytest.mark.parametrize("strategy", STRATEGIES)
-def test_forward_edge_cases(bsa, case, strategy):
+@pytest.mark.parametrize("select,strategy", PATHS)
+def test_forward_edge_cases(bsa, case, select, strategy):
     m, lib = bsa
-    use_strategy(m, lib, strategy)
+    use_strategy(m, lib, strategy, select)
     w = W.Workload("edge", case["batch"], case["heads"], case["n"], case["d"], case["dtype"],
                    seed=77, topk=case["topk"], causal=case["causal"],
                    key_offsets=case["dtype"] == "bf16")
@@ -357,11 +362,14 @@ def test_static_edge_cases(bsa):
     assert np.abs(out.cpu().numpy().reshape(-1, d) - ref).max() <= TOL["bf16"]
 
 
-def test_fine_chunking_does_not_change_results(bsa):
-    """Block-gather partial buffer split into many chunks, some spanning two
-    heads (chunk of 3 query tiles with n = 4096), gives bit-identical output."""
+@pytest.mark.parametrize("n", [4096, 4160])
+def test_fine_chunking_does_not_change_results(bsa, n):
+    """Block-gather partial buffer split into many chunks gives bit-identical
+    output; with n = 4160 (not a multiple of 256) the 3-tile chunks straddle
+    head boundaries."""
     m, lib = bsa
-    w = W.WORKLOADS["dyn_bf16_n4k"]
+    w0 = W.WORKLOADS["dyn_bf16_n4k"]
+    w = W.Workload("chunks", 1, 4, n, 64, "bf16", seed=11, topk=16, key_offsets=True)
     inp = W.generate(w)
     o1, i1 = run_forward(m, lib, w, inp)
     say("[gpu] small fine chunks")
@@ -387,6 +395,7 @@ def test_deterministic(bsa, strategy):
 
 def test_panel_chunking_does_not_change_results(bsa):
     m, lib = bsa
+    use_strategy(m, lib, "block_gather", "panel")
     w = W.WORKLOADS["dyn_bf16_n4k"]
     inp = W.generate(w)
     o1, i1 = run_forward(m, lib, w, inp)
@@ -397,6 +406,51 @@ def test_panel_chunking_does_not_change_results(bsa):
     finally:
         m.bsa_set_option(lib.handle, m.BSA_OPT_PANEL_CHUNK_BYTES, 128 << 20)
     assert np.array_equal(i1, i2) and np.array_equal(o1, o2)
+
+
+@pytest.mark.parametrize("name,causal,topk", [("dyn_bf16_n4k", False, 16), ("dyn_bf16_n4k", True, 16),
+                                              ("tiny_fp32_n1k", True, 4), ("dyn_bf16_n4k", False, 32),
+                                              ("dyn_bf16_n4k", True, 9)])
+def test_fused_and_panel_selection_identical(bsa, name, causal, topk):
+    """Both stage-1 strategies rank the same MFMA scores, so their selections
+    and outputs agree bit for bit."""
+    m, lib = bsa
+    w = W.WORKLOADS[name]
+    inp = W.generate(w)
+    say(f"[gpu] fused vs panel selection {name} causal={causal} k={topk}")
+    use_strategy(m, lib, "block_gather", "fused")
+    o1, i1 = run_forward(m, lib, w, inp, topk=topk, causal=causal)
+    use_strategy(m, lib, "block_gather", "panel")
+    o2, i2 = run_forward(m, lib, w, inp, topk=topk, causal=causal)
+    assert np.array_equal(i1, i2) and np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
+@pytest.mark.parametrize("select", ["fused", "panel"])
+@pytest.mark.parametrize("causal", [False, True])
+def test_selection_exact_ties(bsa, select, causal):
+    """Small-integer fp32 inputs: every coarse score is exact in fp32 and many
+    are equal, so tie-breaking (lower block index first) and the causal own
+    block are checked bit for bit against the oracle, with no tie band."""
+    m, lib = bsa
+    use_strategy(m, lib, "block_gather", select)
+    n, d, topk = 2048, 64, 6
+    rng = np.random.default_rng(123)
+    q = rng.integers(-2, 3, size=(1, 2, n, d)).astype(np.float32)
+    k = rng.integers(-2, 3, size=(1, 2, n, d)).astype(np.float32)
+    k[:, :, 64 * 5:64 * 9] = k[:, :, 64 * 1:64 * 5]      # duplicate blocks: equal representatives
+    v = rng.standard_normal((1, 2, n, d)).astype(np.float32)
+    say(f"[gpu] exact ties select={select} causal={causal}")
+    dq, dk, dv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    out = torch.empty(dq.shape, dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, 2, n, topk), dtype=torch.int32, device="cuda")
+    m.bsa_forward(lib.handle, dq, dk, dv, out, idx, topk=topk, scale=0.125, causal=causal)
+    torch.cuda.synchronize()
+    r = oracle.pool(k.astype(np.float64), 64)
+    s = oracle.scores(q.astype(np.float64), r, 64)
+    ref, kth, nxt = oracle.topk(s, n, 64, topk, causal)
+    ties = np.isfinite(kth) & (kth == nxt)
+    assert ties.mean() > 0.05   # the case really has ties at the boundary
+    np.testing.assert_array_equal(idx.cpu().numpy().reshape(-1, topk), ref)
 
 
 # ------------------------------------------------------------- validation --
