@@ -7,6 +7,12 @@
 // lanes that share a column chunk are then reduced with xor shuffles.  The
 // kernel reads K exactly once and writes the float32 representatives, so it is
 // bound by HBM bandwidth.
+//
+// Optionally it also writes each representative r as three bfloat16 terms
+// hi + mid + lo (hi = bf16(r), mid = bf16(r - hi), lo = bf16(r - hi - mid)),
+// laid out as one plane per term and head, split[bh][term][beta][d], the form
+// the fused scoring kernel feeds to the bf16 MFMA (coarse_score.hip explains
+// the split).
 #include "bsa_device.hpp"
 #include "bsa_launch.hpp"
 
@@ -16,7 +22,8 @@ namespace {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k,
                                                          float* __restrict__ repr,
-                                                         int64_t total_blocks) {
+                                                         bf16_bits* __restrict__ split,
+                                                         int64_t total_blocks, int nb) {
   constexpr int E = 16 / sizeof(T);     // elements per 16-byte chunk
   constexpr int LPR = D / E;            // lanes per key row
   constexpr int RPL = kWave / LPR;      // rows per wave-wide load
@@ -54,34 +61,60 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k
     for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], s);
   }
   if (ro == 0) {
-    float* dst = repr + blk * D + c * E;
     constexpr float inv = 1.0f / kTile;  // exact: a power of two
 #pragma unroll
-    for (int e = 0; e < E; e += 4)
-      *reinterpret_cast<float4*>(dst + e) =
-          make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+    for (int e = 0; e < E; ++e) acc[e] *= inv;
+    if (repr) {
+      float* dst = repr + blk * D + c * E;
+#pragma unroll
+      for (int e = 0; e < E; e += 4)
+        *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+    }
+    if (split) {
+      // E consecutive d per lane; the planes of one head are nb * D apart.
+      const int64_t bhi = blk / nb;
+      bf16_bits* dst = split + (blk + 2 * bhi * nb) * D + c * E;
+#pragma unroll
+      for (int t = 0; t < 3; ++t) {
+        uint32_t w[E / 2];
+#pragma unroll
+        for (int e = 0; e < E; e += 2) {
+          const __bf16 h0 = f32_to_bf16(acc[e]), h1 = f32_to_bf16(acc[e + 1]);
+          acc[e] -= static_cast<float>(h0);
+          acc[e + 1] -= static_cast<float>(h1);
+          w[e / 2] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
+                     (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h1)) << 16);
+        }
+        if constexpr (E == 8) {
+          *reinterpret_cast<uint4*>(dst + static_cast<int64_t>(t) * nb * D) = make_uint4(w[0], w[1], w[2], w[3]);
+        } else {
+          *reinterpret_cast<uint2*>(dst + static_cast<int64_t>(t) * nb * D) = make_uint2(w[0], w[1]);
+        }
+      }
+    }
   }
 }
 
 template <typename T, int D>
-hipError_t launch(const void* k, float* repr, int64_t blocks, hipStream_t s) {
+hipError_t launch(const void* k, float* repr, bf16_bits* split, int64_t blocks, int nb, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((blocks + 3) / 4));
   hipLaunchKernelGGL((block_pool_kernel<T, D>), grid, dim3(256), 0, s,
-                     static_cast<const T*>(k), repr, blocks);
+                     static_cast<const T*>(k), repr, split, blocks, nb);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_block_pool(const void* k, float* repr, int64_t bh, int n, int d,
+hipError_t launch_block_pool(const void* k, float* repr, uint16_t* split, int64_t bh, int n, int d,
                              bsa_dtype dtype, hipStream_t stream) {
-  const int64_t blocks = bh * (n / kTile);
+  const int nb = n / kTile;
+  const int64_t blocks = bh * nb;
   if (dtype == BSA_BF16) {
-    return d == 64 ? launch<bf16_bits, 64>(k, repr, blocks, stream)
-                   : launch<bf16_bits, 128>(k, repr, blocks, stream);
+    return d == 64 ? launch<bf16_bits, 64>(k, repr, split, blocks, nb, stream)
+                   : launch<bf16_bits, 128>(k, repr, split, blocks, nb, stream);
   }
-  return d == 64 ? launch<float, 64>(k, repr, blocks, stream)
-                 : launch<float, 128>(k, repr, blocks, stream);
+  return d == 64 ? launch<float, 64>(k, repr, split, blocks, nb, stream)
+                 : launch<float, 128>(k, repr, split, blocks, nb, stream);
 }
 
 }  // namespace bsa

@@ -23,6 +23,8 @@ struct bsa_handle_s {
   // workspace
   float* repr = nullptr;
   size_t repr_bytes = 0;
+  uint16_t* split = nullptr;  // bf16 three-term split of repr, for the fused selection
+  size_t split_bytes = 0;
   float* panel = nullptr;
   size_t panel_bytes = 0;
   int32_t* idx = nullptr;
@@ -230,6 +232,7 @@ BSA_API bsa_status bsa_destroy(bsa_handle h) {
   }
   for (auto e : h->free_events) (void)hipEventDestroy(e);
   if (h->repr) (void)hipFree(h->repr);
+  if (h->split) (void)hipFree(h->split);
   if (h->panel) (void)hipFree(h->panel);
   if (h->idx) (void)hipFree(h->idx);
   for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml})
@@ -266,7 +269,7 @@ BSA_API bsa_status bsa_set_option(bsa_handle h, int option, int64_t value) {
 
 BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
   if (!h || !bytes) return fail(h, BSA_ERR_INVALID_ARG, "bsa_workspace_bytes: NULL argument");
-  *bytes = h->repr_bytes + h->panel_bytes + h->idx_bytes;
+  *bytes = h->repr_bytes + h->split_bytes + h->panel_bytes + h->idx_bytes;
   for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml})
     *bytes += b->bytes;
   return BSA_OK;
@@ -276,23 +279,28 @@ BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
 
 namespace {
 
-bsa_status run_pool(bsa_handle h, const void* k, float* repr, const Shape& s, bsa_dtype dt,
-                    hipStream_t st) {
+bsa_status run_pool(bsa_handle h, const void* k, float* repr, uint16_t* split, const Shape& s,
+                    bsa_dtype dt, hipStream_t st) {
   return timed_launch(h, BSA_STAGE_POOL, st, "block_pool", [&] {
-    return bsa::launch_block_pool(k, repr, s.bh(), s.n, s.d, dt, st);
+    return bsa::launch_block_pool(k, repr, split, s.bh(), s.n, s.d, dt, st);
   });
+}
+
+bool fused_select(bsa_handle h, int topk) {
+  return h->select_strategy == BSA_SELECT_FUSED && topk <= bsa::kFusedSelectMaxK;
 }
 
 // Stage 1 selection over all rows: one fused coarse_score + topk_select
 // kernel (k <= 32, fused strategy), else coarse_score and topk_select through
 // a panel, in chunks of at most panel_chunk_bytes of panel.
-bsa_status run_select(bsa_handle h, const void* q, const float* repr, int32_t* idx, const Shape& s,
-                      bsa_dtype dt, int topk, int causal, hipStream_t st) {
+bsa_status run_select(bsa_handle h, const void* q, const float* repr, const uint16_t* split,
+                      int32_t* idx, const Shape& s, bsa_dtype dt, int topk, int causal,
+                      hipStream_t st) {
   const int64_t nb = s.n / 64;
   const int64_t total = s.bh() * s.n;
-  if (h->select_strategy == BSA_SELECT_FUSED && topk <= bsa::kFusedSelectMaxK)
+  if (fused_select(h, topk))
     return timed_launch(h, BSA_STAGE_COARSE_TOPK, st, "coarse_select", [&] {
-      return bsa::launch_coarse_select(q, repr, idx, total, s.n, s.d, dt, topk, causal, st);
+      return bsa::launch_coarse_select(q, repr, split, idx, total, s.n, s.d, dt, topk, causal, st);
     });
   int64_t chunk = h->panel_chunk_bytes / (nb * 4) / 64 * 64;
   if (chunk < 64) chunk = 64;
@@ -375,7 +383,7 @@ BSA_API bsa_status bsa_block_pool(bsa_handle h, const void* k, float* repr_out, 
   TRY(check_ptr(h, fn, "k", k));
   TRY(check_ptr(h, fn, "repr_out", repr_out));
   DeviceGuard dg(h->device);
-  return run_pool(h, k, repr_out, s, dtype, static_cast<hipStream_t>(stream));
+  return run_pool(h, k, repr_out, nullptr, s, dtype, static_cast<hipStream_t>(stream));
 }
 
 BSA_API bsa_status bsa_coarse_score(bsa_handle h, const void* q, const float* repr,
@@ -455,16 +463,24 @@ BSA_API bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t nb = s.n / 64;
-  TRY(grow(h, reinterpret_cast<void**>(&h->repr), &h->repr_bytes, size_t(s.bh() * nb * s.d) * 4,
-           "repr workspace"));
+  // The fused bf16 selection reads the split representatives only.
+  const bool want_split = fused_select(h, topk) && dtype == BSA_BF16;
+  if (want_split)
+    TRY(grow(h, reinterpret_cast<void**>(&h->split), &h->split_bytes,
+             size_t(s.bh() * nb * s.d) * 3 * 2, "split repr workspace"));
+  else
+    TRY(grow(h, reinterpret_cast<void**>(&h->repr), &h->repr_bytes, size_t(s.bh() * nb * s.d) * 4,
+             "repr workspace"));
+  float* repr = want_split ? nullptr : h->repr;
+  uint16_t* split = want_split ? h->split : nullptr;
   int32_t* idx = block_idx_out;
   if (!idx) {
     TRY(grow(h, reinterpret_cast<void**>(&h->idx), &h->idx_bytes, size_t(s.bh() * s.n * topk) * 4,
              "index workspace"));
     idx = h->idx;
   }
-  TRY(run_pool(h, k, h->repr, s, dtype, st));
-  TRY(run_select(h, q, h->repr, idx, s, dtype, topk, causal, st));
+  TRY(run_pool(h, k, repr, split, s, dtype, st));
+  TRY(run_select(h, q, repr, split, idx, s, dtype, topk, causal, st));
   return run_fine(h, q, k, v, out, idx, s, dtype, topk, scale, causal, st);
 }
 

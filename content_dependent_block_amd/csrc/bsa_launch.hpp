@@ -11,8 +11,10 @@
 
 namespace bsa {
 
-// block_pool: k [bh][n][d] -> repr float [bh][n/64][d].
-hipError_t launch_block_pool(const void* k, float* repr, int64_t bh, int n, int d,
+// block_pool: k [bh][n][d] -> repr float [bh][n/64][d] (if repr != NULL) and
+// the three-term bf16 split of each representative, split [bh][3][n/64][d]
+// (if split != NULL).
+hipError_t launch_block_pool(const void* k, float* repr, uint16_t* split, int64_t bh, int n, int d,
                              bsa_dtype dtype, hipStream_t stream);
 
 // coarse_score over panel rows [row0, row0 + rows) of the flattened
@@ -23,10 +25,12 @@ hipError_t launch_coarse_score(const void* q, const float* repr, float* panel, i
                                hipStream_t stream);
 
 // coarse_score and topk_select in one kernel (topk <= 32) over all `rows`
-// query rows: idx[row * topk + t], no panel.
-hipError_t launch_coarse_select(const void* q, const float* repr, int32_t* idx, int64_t rows,
-                                int n, int d, bsa_dtype dtype, int topk, int causal,
-                                hipStream_t stream);
+// query rows: idx[row * topk + t], no panel.  Representatives: for bf16
+// inputs the split form from block_pool (repr_split), for fp32 inputs the
+// float32 repr.
+hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t* repr_split,
+                                int32_t* idx, int64_t rows, int n, int d, bsa_dtype dtype,
+                                int topk, int causal, hipStream_t stream);
 constexpr int kFusedSelectMaxK = 32;
 
 // topk_select over panel rows [row0, row0 + rows): idx[(row0 + r) * topk + t].

@@ -17,20 +17,36 @@
 // scores of blocks 4*(l/16) + j of each 16-block tile.  In the causal variant
 // block tiles entirely after the query tile are skipped.
 //
-// Two sinks for the scores:
-//   panel mode: the float32 panel, block-major (panel[beta][row]), 16 lanes
-//     storing 64 contiguous bytes of one block row.
-//   select mode (k <= 32, the path bsa_forward takes): the scores never leave
-//     the chip.  Each lane offers its scores, in ascending block order, to an
-//     exact register top-KL list (topk_list.hpp, KL >= k); the query's answer
-//     is contained in the union of its 4 lanes' lists, from which k_eff
-//     rounds of a cross-lane tournament take it in rank order.  It is written
-//     in ascending block order (topk_select.hip states the selection
-//     semantics).
+// The panel kernel (bsa_coarse_score, and the panel strategy of bsa_forward)
+// writes the float32 scores block-major, panel[beta][row], 16 lanes storing
+// 64 contiguous bytes of one block row.
+//
+// The select kernel (bsa_forward, k <= 32) never stores a score.  It walks
+// the representatives twice:
+//   pass 1: every lane keeps the maximum of each of its score groups, group =
+//     beta mod G with G = 64 * GM (16 * GM groups per lane, the 4 lanes of a
+//     query hold them all).  tau = the k_eff-th largest of the G group maxima
+//     (each lane sorts its own, then k_eff rounds of a 4-lane tournament).
+//     The k_eff groups whose maxima are >= tau each hold a score >= tau, so at
+//     least k_eff scores are >= tau, and every score of the answer is >= tau.
+//   pass 2: the same scores again; those >= tau (typically k + a few) are
+//     appended to the lane's LDS slots in ascending block order.
+//   The lane offers its slots to an exact register top-KL list (topk_list.hpp,
+//     KL >= k) and k_eff rounds of a cross-lane tournament between the 4
+//     lists take the answer in rank order; it is written in ascending block
+//     order.  Because the answer is ranked from pass 2's scores alone and
+//     pass 2 checks it holds >= k_eff candidates, the result is exact.
+//   A workgroup in which some lane has more candidates than slots (or fewer
+//     than k_eff candidates) redoes the walk offering every score to the
+//     lists: the same answer, slower.
+// topk_select.hip states the selection semantics.
+//
 // Workgroups are issued XCD-major: consecutive workgroup ids go round-robin
 // over the 8 XCDs, so tile t runs on XCD t / (tiles / 8) and each XCD's L2
 // sees the representatives of as few heads as possible; in the causal
 // variant each XCD takes its tiles heaviest first.
+#include <type_traits>
+
 #include "bsa_device.hpp"
 #include "bsa_launch.hpp"
 #include "topk_list.hpp"
@@ -47,124 +63,50 @@ __device__ __forceinline__ int64_t xcd_tile(int causal) {
   return (bid % 8) * per + (causal ? per - 1 - local : local);
 }
 
-// Is (va, ba) ranked above (vb, bb)?  Higher score first, then lower block.
-__device__ __forceinline__ bool ranks_above(float va, int ba, float vb, int bb) {
-  return va > vb || (va == vb && ba < bb);
+// ------------------------------------------------------ score tiles ----
+// One lane's 4 scores of a 16-block MFMA tile from the 3-term R tile in LDS
+// ([term][64 blocks][D + 8] bf16) and its query's B operand.
+template <int D>
+__device__ __forceinline__ f32x4 bf16_tile(const unsigned char* lds, const bf16x8 (&qb)[D / 32], int mt,
+                                           int g, int c16) {
+  constexpr int PITCH = D + 8;
+  const __bf16* rs = reinterpret_cast<const __bf16*>(lds);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) {
+#pragma unroll
+    for (int t = 0; t < kTerms; ++t) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(rs + (t * kTile + mt * 16 + c16) * PITCH + 8 * g + 32 * ks);
+      acc = mfma_16x16x32_bf16(a, qb[ks], acc);
+    }
+  }
+  return acc;
 }
+// A producer stages 64 representatives in LDS (stage) and returns one lane's
+// 4 scores of a 16-block MFMA tile (tile): C[block 4g + j][query c16].
 
-// Consumer of the score tiles of one lane (query c16 of the wave; acc[j] is
-// the score of block beta0 + j).
-template <int KL>
-struct Sink {
-  TopList<KL> list;
-  __device__ __forceinline__ void init() { list.init(); }
-  __device__ __forceinline__ void take(const f32x4& acc, int beta0, int nb, int nvalid, int forced,
-                                       float* __restrict__ panel, int64_t prows, int64_t prow) {
-    if constexpr (KL == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (beta0 + j < nb) panel[static_cast<int64_t>(beta0 + j) * prows + prow] = acc[j];
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int beta = beta0 + j;
-        float x = beta == forced ? INFINITY : acc[j];
-        x = beta < nvalid ? x : -INFINITY;
-        list.offer(x, beta);
-      }
-    }
-  }
-  // Merge the 4 lists of each query and write its selection: k_eff rounds of
-  // a 4-lane tournament between the lists' heads; the winner's lane drops
-  // its head.  sel: LDS [4 waves][KL][16] receives the winners in rank order.
-  __device__ __forceinline__ void finish(int* sel, int wave, int g, int c16, int keff, int topk,
-                                         int32_t* __restrict__ dst) {
-    if constexpr (KL > 0) {
-      int* ws = sel + wave * KL * 16;
-      for (int t = 0; t < keff; ++t) {
-        float mv = list.v[0];
-        int mb = list.b[0];
-#pragma unroll
-        for (int m = 16; m <= 32; m *= 2) {
-          const float ov = __shfl_xor(mv, m);
-          const int ob = __shfl_xor(mb, m);
-          const bool take = ranks_above(ov, ob, mv, mb);
-          mv = take ? ov : mv;
-          mb = take ? ob : mb;
-        }
-        if (list.b[0] == mb) {
-#pragma unroll
-          for (int j = 0; j + 1 < KL; ++j) {
-            list.v[j] = list.v[j + 1];
-            list.b[j] = list.b[j + 1];
-          }
-          list.v[KL - 1] = -INFINITY;
-          list.b[KL - 1] = -1;
-        }
-        if (g == 0) ws[t * 16 + c16] = mb;
-      }
-      __syncthreads();
-      int b[KL];
-#pragma unroll
-      for (int u = 0; u < KL; ++u) b[u] = u < keff ? ws[u * 16 + c16] : 0x7fffffff;
-#pragma unroll
-      for (int t0 = 0; t0 < KL; t0 += 4) {
-        const int t = t0 + g;
-        if (t < keff) {
-          int me = b[t0];
-#pragma unroll
-          for (int e = 1; e < 4; ++e) me = g == e ? b[t0 + e] : me;
-          int pos = 0;
-#pragma unroll
-          for (int u = 0; u < KL; ++u) pos += b[u] < me ? 1 : 0;
-          dst[pos] = me;
-        }
-      }
-      for (int t = keff + g; t < topk; t += 4) dst[t] = -1;
-    }
-  }
-};
+// bf16 inputs, float32 representatives [block][d] split here into three bf16
+// terms (the same split block_pool writes for the select kernel).
+template <int D>
+struct Bf16Tiles {
+  using QT = bf16_bits;
+  using Src = float;
+  static constexpr int KS = D / 32;      // MFMA k-steps over d
+  static constexpr int PITCH = D + 8;    // bf16 per LDS row (16 B pad)
+  static constexpr int LDS_BYTES = kTerms * kTile * PITCH * 2;
+  bf16x8 qb[KS];  // B operand: this lane's query, d = 8g + 32ks .. +7
 
-// Panel rows: prows = rows of the chunk; panel[beta * prows + prow].
-template <int D, int KL>
-__global__ __launch_bounds__(256) void coarse_bf16_kernel(const bf16_bits* __restrict__ q,
-                                                          const float* __restrict__ repr,
-                                                          float* __restrict__ panel,
-                                                          int32_t* __restrict__ idx, int64_t row0,
-                                                          int64_t prows, int n, int topk, int causal) {
-  constexpr int KS = D / 32;        // MFMA k-steps over d
-  constexpr int PITCH = D + 8;      // bf16 elements per LDS row (16 B pad)
-  __shared__ __bf16 rs[kTerms][kTile][PITCH];
-  __shared__ int sel[4][KL > 0 ? KL : 1][16];
-
-  const int nb = n / kTile;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int64_t tile_row = row0 + xcd_tile(causal) * kTile;  // first query row
-  const int64_t bh = tile_row / n;
-  const int i0 = static_cast<int>(tile_row % n);
-  const int64_t qrow = tile_row + wave * 16 + c16;  // this lane's query
-  const int64_t prow = qrow - row0;
-
-  // B operand: this lane's query row, d = 8g + 32ks .. +7.
-  bf16x8 qb[KS];
-  {
-    const bf16_bits* qr = q + qrow * D + 8 * g;
+  __device__ __forceinline__ void load_q(const QT* __restrict__ q, int64_t qrow, int g) {
+    const QT* qr = q + qrow * D + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) qb[ks] = as_bf16x8(ld16(qr + 32 * ks));
   }
-
-  const float* rbase = repr + bh * static_cast<int64_t>(nb) * D;
-  const int nbt_all = (nb + kTile - 1) / kTile;
-  const int nbt = causal ? (i0 / kTile) / kTile + 1 : nbt_all;
-  const int qblk = i0 / kTile;  // query block of all 64 rows
-  const int nvalid = causal ? qblk + 1 : nb;
-  const int forced = causal ? qblk : -1;
-  Sink<KL> sink;
-  sink.init();
-  for (int bt = 0; bt < nbt; ++bt) {
-    __syncthreads();
-    // Stage 64 representatives as three bf16 terms.
+  __device__ __forceinline__ static const Src* head_base(const Src* r, int64_t bh, int nb) {
+    return r + bh * nb * D;
+  }
+  __device__ __forceinline__ static void stage(unsigned char* lds, const Src* __restrict__ rbase, int bt,
+                                               int nb, int tid) {
+    __bf16* rs = reinterpret_cast<__bf16*>(lds);
     for (int c = tid; c < kTile * D / 4; c += 256) {
       const int r = c / (D / 4), col = (c % (D / 4)) * 4;
       const int beta = bt * kTile + r;
@@ -176,56 +118,81 @@ __global__ __launch_bounds__(256) void coarse_bf16_kernel(const bf16_bits* __res
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const __bf16 h = f32_to_bf16(v[e]);
-          rs[t][r][col + e] = h;
+          rs[(t * kTile + r) * PITCH + col + e] = h;
           v[e] -= static_cast<float>(h);
         }
       }
     }
-    __syncthreads();
+  }
+  __device__ __forceinline__ f32x4 tile(const unsigned char* lds, int mt, int g, int c16) const {
+    return bf16_tile<D>(lds, qb, mt, g, c16);
+  }
+};
+
+// bf16 inputs, representatives pre-split by block_pool into term planes
+// [term][beta][d] per head.  fetch() issues the global loads of a tile into
+// registers, put() writes them to LDS: the loads of tile bt + 1 are in flight
+// while tile bt is computed.  Rows past the last block repeat the last block
+// (their scores are never used).
+template <int D>
+struct Bf16PlaneTiles {
+  using QT = bf16_bits;
+  using Src = bf16_bits;
+  static constexpr int KS = D / 32;
+  static constexpr int PITCH = D + 8;
+  static constexpr int LDS_BYTES = kTerms * kTile * PITCH * 2;
+  static constexpr int CPR = D / 8;               // 16-byte chunks per block row
+  static constexpr int PER = kTile * CPR / 256;   // chunks per thread and term
+  bf16x8 qb[KS];
+  uint4 pf[kTerms][PER];
+
+  __device__ __forceinline__ void load_q(const QT* __restrict__ q, int64_t qrow, int g) {
+    const QT* qr = q + qrow * D + 8 * g;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if (bt * kTile + mt * 16 >= nb) break;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks) qb[ks] = as_bf16x8(ld16(qr + 32 * ks));
+  }
+  __device__ __forceinline__ static const Src* head_base(const Src* r, int64_t bh, int nb) {
+    return r + bh * kTerms * nb * D;
+  }
+  __device__ __forceinline__ void fetch(const Src* __restrict__ rbase, int nb, int bt, int tid) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 8;
+      const int beta = min(bt * kTile + r, nb - 1);
 #pragma unroll
-        for (int t = 0; t < kTerms; ++t) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&rs[t][mt * 16 + c16][8 * g + 32 * ks]);
-          acc = mfma_16x16x32_bf16(a, qb[ks], acc);
-        }
-      }
-      // lane holds C[block 4g + j][query c16]
-      sink.take(acc, bt * kTile + mt * 16 + 4 * g, nb, nvalid, forced, panel, prows, prow);
+      for (int t = 0; t < kTerms; ++t)
+        pf[t][u] = ld16(rbase + static_cast<uint32_t>((t * nb + beta) * D + col));
     }
   }
-  if constexpr (KL > 0) {
-    const int keff = topk < nvalid ? topk : nvalid;
-    sink.finish(&sel[0][0][0], wave, g, c16, keff, topk, idx + qrow * topk);
+  __device__ __forceinline__ void put(unsigned char* lds, int tid) const {
+    __bf16* rs = reinterpret_cast<__bf16*>(lds);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 8;
+#pragma unroll
+      for (int t = 0; t < kTerms; ++t) *reinterpret_cast<uint4*>(rs + (t * kTile + r) * PITCH + col) = pf[t][u];
+    }
   }
-}
+  __device__ __forceinline__ f32x4 tile(const unsigned char* lds, int mt, int g, int c16) const {
+    return bf16_tile<D>(lds, qb, mt, g, c16);
+  }
+};
 
-template <int D, int KL>
-__global__ __launch_bounds__(256) void coarse_f32_kernel(const float* __restrict__ q,
-                                                         const float* __restrict__ repr,
-                                                         float* __restrict__ panel,
-                                                         int32_t* __restrict__ idx, int64_t row0,
-                                                         int64_t prows, int n, int topk, int causal) {
-  constexpr int KS = D / 4;     // MFMA k-steps; slot (ks, g) carries d = KS*g + ks
-  constexpr int PITCH = D + 4;
-  __shared__ float rs[kTile][PITCH];
-  __shared__ int sel[4][KL > 0 ? KL : 1][16];
-
-  const int nb = n / kTile;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
-  const int64_t tile_row = row0 + xcd_tile(causal) * kTile;
-  const int64_t bh = tile_row / n;
-  const int i0 = static_cast<int>(tile_row % n);
-  const int64_t qrow = tile_row + wave * 16 + c16;
-  const int64_t prow = qrow - row0;
-
+// fp32 inputs: v_mfma_f32_16x16x4_f32; slot (ks, g) carries d = KS*g + ks.
+// stage() for the panel kernel; fetch()/put() as for Bf16PlaneTiles.
+template <int D>
+struct F32Tiles {
+  using QT = float;
+  using Src = float;
+  static constexpr int KS = D / 4;
+  static constexpr int PITCH = D + 4;
+  static constexpr int LDS_BYTES = kTile * PITCH * 4;
+  static constexpr int CPR = D / 4;               // 16-byte chunks per block row
+  static constexpr int PER = kTile * CPR / 256;
   float qf[KS];
-  {
+  float4 pf[PER];
+
+  __device__ __forceinline__ void load_q(const QT* __restrict__ q, int64_t qrow, int g) {
     const float* qr = q + qrow * D + KS * g;
 #pragma unroll
     for (int e = 0; e < KS; e += 4) {
@@ -233,57 +200,384 @@ __global__ __launch_bounds__(256) void coarse_f32_kernel(const float* __restrict
       qf[e] = x.x; qf[e + 1] = x.y; qf[e + 2] = x.z; qf[e + 3] = x.w;
     }
   }
-  const float* rbase = repr + bh * static_cast<int64_t>(nb) * D;
-  const int nbt_all = (nb + kTile - 1) / kTile;
-  const int nbt = causal ? (i0 / kTile) / kTile + 1 : nbt_all;
-  const int qblk = i0 / kTile;
-  const int nvalid = causal ? qblk + 1 : nb;
-  const int forced = causal ? qblk : -1;
-  Sink<KL> sink;
-  sink.init();
-  for (int bt = 0; bt < nbt; ++bt) {
-    __syncthreads();
+  __device__ __forceinline__ static const Src* head_base(const Src* r, int64_t bh, int nb) {
+    return r + bh * nb * D;
+  }
+  __device__ __forceinline__ static void stage(unsigned char* lds, const Src* __restrict__ rbase, int bt,
+                                               int nb, int tid) {
+    float* rs = reinterpret_cast<float*>(lds);
     for (int c = tid; c < kTile * D / 4; c += 256) {
       const int r = c / (D / 4), col = (c % (D / 4)) * 4;
       const int beta = bt * kTile + r;
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       if (beta < nb) x = *reinterpret_cast<const float4*>(rbase + static_cast<int64_t>(beta) * D + col);
-      *reinterpret_cast<float4*>(&rs[r][col]) = x;
+      *reinterpret_cast<float4*>(rs + r * PITCH + col) = x;
     }
+  }
+  __device__ __forceinline__ void fetch(const Src* __restrict__ rbase, int nb, int bt, int tid) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 4;
+      const int beta = min(bt * kTile + r, nb - 1);
+      pf[u] = *reinterpret_cast<const float4*>(rbase + static_cast<uint32_t>(beta * D + col));
+    }
+  }
+  __device__ __forceinline__ void put(unsigned char* lds, int tid) const {
+    float* rs = reinterpret_cast<float*>(lds);
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 4;
+      *reinterpret_cast<float4*>(rs + r * PITCH + col) = pf[u];
+    }
+  }
+  __device__ __forceinline__ f32x4 tile(const unsigned char* lds, int mt, int g, int c16) const {
+    const float* rr = reinterpret_cast<const float*>(lds) + (mt * 16 + c16) * PITCH + KS * g;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = mfma_16x16x4_f32(rr[ks], qf[ks], acc);
+    return acc;
+  }
+};
+
+// Where a workgroup's 64 query rows sit, and which blocks they may select.
+struct TileInfo {
+  int64_t tile_row, bh, qrow;
+  int nb, nbt, nvalid, forced;
+  int tid, lane, wave, g, c16;
+  __device__ __forceinline__ TileInfo(int64_t row0, int n, int causal) {
+    nb = n / kTile;
+    tid = threadIdx.x;
+    lane = tid & 63;
+    wave = tid >> 6;
+    g = lane >> 4;
+    c16 = lane & 15;
+    tile_row = row0 + xcd_tile(causal) * kTile;
+    bh = tile_row / n;
+    const int i0 = static_cast<int>(tile_row % n);
+    qrow = tile_row + wave * 16 + c16;
+    const int qblk = i0 / kTile;  // query block of all 64 rows
+    nbt = causal ? qblk / kTile + 1 : (nb + kTile - 1) / kTile;
+    nvalid = causal ? qblk + 1 : nb;
+    forced = causal ? qblk : -1;
+  }
+  // The score as the selection sees it: -inf for a block that is not a
+  // candidate, +inf for the causal own block.
+  __device__ __forceinline__ float cand(float s, int beta) const {
+    const float x = beta == forced ? INFINITY : s;
+    return beta < nvalid ? x : -INFINITY;
+  }
+};
+
+// --------------------------------------------------------- panel mode ----
+// panel rows: prows = rows of the chunk; panel[beta * prows + (qrow - row0)].
+template <typename TL>
+__global__ __launch_bounds__(256) void coarse_panel_kernel(const typename TL::QT* __restrict__ q,
+                                                           const typename TL::Src* __restrict__ rsrc,
+                                                           float* __restrict__ panel, int64_t row0,
+                                                           int64_t prows, int n, int causal) {
+  __shared__ __attribute__((aligned(16))) unsigned char rs[TL::LDS_BYTES];
+  const TileInfo ti(row0, n, causal);
+  TL sc;
+  sc.load_q(q, ti.qrow, ti.g);
+  const auto* rbase = TL::head_base(rsrc, ti.bh, ti.nb);
+  const int64_t prow = ti.qrow - row0;
+  for (int bt = 0; bt < ti.nbt; ++bt) {
+    __syncthreads();
+    TL::stage(rs, rbase, bt, ti.nb, ti.tid);
     __syncthreads();
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      if (bt * kTile + mt * 16 >= nb) break;
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      const float* rr = &rs[mt * 16 + c16][KS * g];
+      if (bt * kTile + mt * 16 >= ti.nb) break;
+      const f32x4 acc = sc.tile(rs, mt, ti.g, ti.c16);
+      const int beta0 = bt * kTile + mt * 16 + 4 * ti.g;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = mfma_16x16x4_f32(rr[ks], qf[ks], acc);
-      sink.take(acc, bt * kTile + mt * 16 + 4 * g, nb, nvalid, forced, panel, prows, prow);
+      for (int j = 0; j < 4; ++j)
+        if (beta0 + j < ti.nb) panel[static_cast<int64_t>(beta0 + j) * prows + prow] = acc[j];
     }
   }
-  if constexpr (KL > 0) {
-    const int keff = topk < nvalid ? topk : nvalid;
-    sink.finish(&sel[0][0][0], wave, g, c16, keff, topk, idx + qrow * topk);
+}
+
+// -------------------------------------------------------- select mode ----
+// Is (va, ba) ranked above (vb, bb)?  Higher value first, then lower id.
+__device__ __forceinline__ bool ranks_above(float va, int ba, float vb, int bb) {
+  return va > vb || (va == vb && ba < bb);
+}
+
+// The value lane l ^ 16 (row pair swap) or l ^ 32 (half swap) holds, with the
+// gfx950 permlane swaps: called with the same register twice, the swap
+// returns the partner's value in the second result for rows 0 and 2 (lower
+// half) and in the first result for rows 1 and 3 (upper half).
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
   }
 }
 
-template <int D, int KL>
-void launch_kl(const void* q, const float* repr, float* panel, int32_t* idx, int64_t row0,
-               int64_t rows, int n, bsa_dtype dtype, int topk, int causal, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(rows / kTile)), block(256);
-  if (dtype == BSA_BF16)
-    hipLaunchKernelGGL((coarse_bf16_kernel<D, KL>), grid, block, 0, stream,
-                       static_cast<const bf16_bits*>(q), repr, panel, idx, row0, rows, n, topk, causal);
-  else
-    hipLaunchKernelGGL((coarse_f32_kernel<D, KL>), grid, block, 0, stream,
-                       static_cast<const float*>(q), repr, panel, idx, row0, rows, n, topk, causal);
+// Compare-exchanges, descending.  Plain values: larger first.  (value,
+// block) pairs: ranks_above order.
+template <int N>
+__device__ __forceinline__ void cx(float (&a)[N], int i, int j) {  // a[i] >= a[j] afterwards
+  const float hi = fmaxf(a[i], a[j]), lo = fminf(a[i], a[j]);
+  a[i] = hi;
+  a[j] = lo;
+}
+template <int N>
+__device__ __forceinline__ void cx(float (&v)[N], int (&b)[N], int i, int j) {
+  const bool sw = ranks_above(v[j], b[j], v[i], b[i]);
+  const float vi = v[i];
+  const int bi = b[i];
+  v[i] = sw ? v[j] : vi;
+  b[i] = sw ? b[j] : bi;
+  v[j] = sw ? vi : v[j];
+  b[j] = sw ? bi : b[j];
 }
 
+// Bitonic sort of N values, descending.
+template <int N>
+__device__ __forceinline__ void sort_desc(float (&a)[N]) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          if ((i & size) == 0) cx(a, i, j);
+          else cx(a, j, i);
+        }
+      }
+    }
+  }
+}
+
+// A bitonic sequence -> sorted descending.
+template <int N>
+__device__ __forceinline__ void bitonic_clean(float (&a)[N]) {
+#pragma unroll
+  for (int stride = N / 2; stride > 0; stride >>= 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((i ^ stride) > i) cx(a, i, i ^ stride);
+}
+template <int N>
+__device__ __forceinline__ void bitonic_clean(float (&v)[N], int (&b)[N]) {
+#pragma unroll
+  for (int stride = N / 2; stride > 0; stride >>= 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((i ^ stride) > i) cx(v, b, i, i ^ stride);
+}
+
+// Both lanes of a pair (l, l ^ M) hold a sorted list; afterwards both hold
+// the N largest of the two lists, sorted: c[i] = the larger of a[i] and the
+// partner's a[N-1-i] is bitonic and holds the N largest.
+template <int M, int N>
+__device__ __forceinline__ void merge_top(float (&a)[N], int lane) {
+  float p[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) p[i] = __uint_as_float(lane_xor<M>(__float_as_uint(a[N - 1 - i]), lane));
+#pragma unroll
+  for (int i = 0; i < N; ++i) a[i] = fmaxf(a[i], p[i]);
+  bitonic_clean<N>(a);
+}
+template <int M, int N>
+__device__ __forceinline__ void merge_top(float (&v)[N], int (&b)[N], int lane) {
+  float pv[N];
+  int pb[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    pv[i] = __uint_as_float(lane_xor<M>(__float_as_uint(v[N - 1 - i]), lane));
+    pb[i] = static_cast<int>(lane_xor<M>(static_cast<uint32_t>(b[N - 1 - i]), lane));
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const bool take = ranks_above(pv[i], pb[i], v[i], b[i]);
+    v[i] = take ? pv[i] : v[i];
+    b[i] = take ? pb[i] : b[i];
+  }
+  bitonic_clean<N>(v, b);
+}
+
+// The keff-th largest of the values held by the 4 lanes g = 0..3 of one
+// query (lanes c16 + 16 g), each sorted descending: after two pairwise
+// merges every lane holds the N largest of the 4 N, sorted.  keff <= N.
+template <int N>
+__device__ __forceinline__ float kth_of_lanes(float (&a)[N], int keff, int lane) {
+  merge_top<16, N>(a, lane);
+  merge_top<32, N>(a, lane);
+  float r = a[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) r = keff - 1 == i ? a[i] : r;
+  return r;
+}
+
+// The query's 4 lanes each hold a sorted top-KL list of their own candidates;
+// after two pairwise merges every one of them holds the query's top KL.  The
+// first keff entries are the selection: lane g writes entries g, g + 4, ...
+// at their places in ascending block order, and -1 from keff up to topk.
 template <int KL>
-void launch_d(const void* q, const float* repr, float* panel, int32_t* idx, int64_t row0,
-              int64_t rows, int n, int d, bsa_dtype dtype, int topk, int causal, hipStream_t stream) {
-  if (d == 64) launch_kl<64, KL>(q, repr, panel, idx, row0, rows, n, dtype, topk, causal, stream);
-  else launch_kl<128, KL>(q, repr, panel, idx, row0, rows, n, dtype, topk, causal, stream);
+__device__ __forceinline__ void finish_select(TopList<KL>& l, const TileInfo& ti, int keff, int topk,
+                                              int32_t* __restrict__ dst) {
+  merge_top<16, KL>(l.v, l.b, ti.lane);
+  merge_top<32, KL>(l.v, l.b, ti.lane);
+#pragma unroll
+  for (int t0 = 0; t0 < KL; t0 += 4) {
+    if (t0 + ti.g < keff) {
+      int me = l.b[t0];
+#pragma unroll
+      for (int e = 1; e < 4; ++e) me = ti.g == e ? l.b[t0 + e] : me;
+      int pos = 0;
+#pragma unroll
+      for (int u = 0; u < KL; ++u) pos += (u < keff && l.b[u] < me) ? 1 : 0;
+      dst[pos] = me;
+    }
+  }
+  for (int t = keff + ti.g; t < topk; t += 4) dst[t] = -1;
+}
+
+// Stream the tiles of the workgroup's representatives through LDS, register-
+// prefetching tile bt + 1 while tile bt is computed, and hand each 16-block
+// MFMA tile to fast(bt, mt, b0, acc) or slow(...) (b0 = first block of the
+// MFMA tile).  Every block of a tile before the last is an ordinary
+// candidate (below the last candidate and not the causal own block, which
+// both lie in the last tile), so only the last tile takes the checked slow().
+template <typename TL, typename FF, typename FS>
+__device__ __forceinline__ void walk(TL& sc, unsigned char* rs, const typename TL::Src* rbase,
+                                     const TileInfo& ti, FF&& fast, FS&& slow) {
+  sc.fetch(rbase, ti.nb, 0, ti.tid);
+  for (int bt = 0; bt < ti.nbt; ++bt) {
+    __syncthreads();
+    sc.put(rs, ti.tid);
+    const bool last = bt + 1 == ti.nbt;
+    if (!last) sc.fetch(rbase, ti.nb, bt + 1, ti.tid);
+    __syncthreads();
+    if (!last) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) fast(bt, mt, bt * kTile + mt * 16, sc.tile(rs, mt, ti.g, ti.c16));
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const int b0 = bt * kTile + mt * 16;
+        if (b0 >= ti.nb) break;
+        slow(bt, mt, b0, sc.tile(rs, mt, ti.g, ti.c16));
+      }
+    }
+  }
+}
+
+template <typename TL, int KL, int GM, int CAP>
+__global__ __launch_bounds__(256) void coarse_select_kernel(const typename TL::QT* __restrict__ q,
+                                                            const typename TL::Src* __restrict__ rsrc,
+                                                            int32_t* __restrict__ idx, int n, int topk,
+                                                            int causal) {
+  __shared__ __attribute__((aligned(16))) unsigned char rs[TL::LDS_BYTES];
+  // per lane: candidate (score, block bits); slot CAP takes the discarded
+  // writes.
+  __shared__ float2 cvb[4][CAP + 1][64];
+  const TileInfo ti(0, n, causal);
+  TL sc;
+  sc.load_q(q, ti.qrow, ti.g);
+  const auto* rbase = TL::head_base(rsrc, ti.bh, ti.nb);
+  const int keff = topk < ti.nvalid ? topk : ti.nvalid;
+
+  // pass 1: group maxima; the lane's group of block 64 bt + 16 mt + 4 g + j
+  // is slot 16 (bt mod GM) + 4 mt + j.
+  float a[16 * GM];
+#pragma unroll
+  for (int u = 0; u < 16 * GM; ++u) a[u] = -INFINITY;
+  auto group_max = [&](bool checked, int bt, int mt, int b0, const f32x4& acc) {
+    const int h = GM == 1 ? 0 : (bt & (GM - 1));
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh) {
+      if (hh == h) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float x = checked ? ti.cand(acc[j], b0 + 4 * ti.g + j) : acc[j];
+          a[16 * hh + 4 * mt + j] = fmaxf(a[16 * hh + 4 * mt + j], x);
+        }
+      }
+    }
+  };
+  walk(sc, rs, rbase, ti,
+       [&](int bt, int mt, int b0, const f32x4& acc) { group_max(false, bt, mt, b0, acc); },
+       [&](int bt, int mt, int b0, const f32x4& acc) { group_max(true, bt, mt, b0, acc); });
+  sort_desc<16 * GM>(a);
+  const float tau = kth_of_lanes<16 * GM>(a, keff, ti.lane);
+
+  // pass 2: the candidates >= tau, in ascending block order
+  int cnt = 0;
+  auto append = [&](bool checked, int b0, const f32x4& acc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int beta = b0 + 4 * ti.g + j;
+      const float x = checked ? ti.cand(acc[j], beta) : acc[j];
+      const bool c = x >= tau;
+      const int slot = c ? min(cnt, CAP) : CAP;
+      cvb[ti.wave][slot][ti.lane] = make_float2(x, __int_as_float(beta));
+      cnt += c ? 1 : 0;
+    }
+  };
+  walk(sc, rs, rbase, ti, [&](int, int, int b0, const f32x4& acc) { append(false, b0, acc); },
+       [&](int, int, int b0, const f32x4& acc) { append(true, b0, acc); });
+  int tot = cnt + __shfl_xor(cnt, 16);
+  tot += __shfl_xor(tot, 32);
+  const int redo = __syncthreads_or(cnt > CAP || tot < keff);
+
+  TopList<KL> l;
+  l.init();
+  if (!redo) {
+    int mc = cnt;
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) mc = max(mc, __shfl_xor(mc, m));
+    mc = __builtin_amdgcn_readfirstlane(mc);
+    for (int i = 0; i < mc; ++i) {
+      const float2 e = cvb[ti.wave][i][ti.lane];
+      l.offer(i < cnt ? e.x : -INFINITY, __float_as_int(e.y));
+    }
+  } else {
+    // slots overflowed somewhere in the workgroup: offer every score
+    walk(sc, rs, rbase, ti,
+         [&](int, int, int b0, const f32x4& acc) {
+#pragma unroll
+           for (int j = 0; j < 4; ++j) l.offer(acc[j], b0 + 4 * ti.g + j);
+         },
+         [&](int, int, int b0, const f32x4& acc) {
+#pragma unroll
+           for (int j = 0; j < 4; ++j) l.offer(ti.cand(acc[j], b0 + 4 * ti.g + j), b0 + 4 * ti.g + j);
+         });
+  }
+  finish_select<KL>(l, ti, keff, topk, idx + ti.qrow * topk);
+}
+
+// ------------------------------------------------------------ launch ----
+template <typename TL>
+void launch_panel(const void* q, const void* rsrc, float* panel, int64_t row0, int64_t rows, int n,
+                  int causal, hipStream_t s) {
+  hipLaunchKernelGGL((coarse_panel_kernel<TL>), dim3(static_cast<unsigned>(rows / kTile)), dim3(256), 0, s,
+                     static_cast<const typename TL::QT*>(q), static_cast<const typename TL::Src*>(rsrc),
+                     panel, row0, rows, n, causal);
+}
+
+template <typename TL, int KL, int GM, int CAP>
+void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
+                   int causal, hipStream_t s) {
+  hipLaunchKernelGGL((coarse_select_kernel<TL, KL, GM, CAP>), dim3(static_cast<unsigned>(rows / kTile)), dim3(256),
+                     0, s, static_cast<const typename TL::QT*>(q), static_cast<const typename TL::Src*>(rsrc),
+                     idx, n, topk, causal);
+}
+
+template <typename TL>
+void launch_select_k(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
+                     int causal, hipStream_t s) {
+  if (topk <= 8) launch_select<TL, 8, 1, 8>(q, rsrc, idx, rows, n, topk, causal, s);
+  else if (topk <= 16) launch_select<TL, 16, 1, 16>(q, rsrc, idx, rows, n, topk, causal, s);
+  else launch_select<TL, 32, 2, 32>(q, rsrc, idx, rows, n, topk, causal, s);
 }
 
 }  // namespace
@@ -291,16 +585,26 @@ void launch_d(const void* q, const float* repr, float* panel, int32_t* idx, int6
 hipError_t launch_coarse_score(const void* q, const float* repr, float* panel, int64_t row0,
                                int64_t rows, int n, int d, bsa_dtype dtype, int causal,
                                hipStream_t stream) {
-  launch_d<0>(q, repr, panel, nullptr, row0, rows, n, d, dtype, 1, causal, stream);
+  if (dtype == BSA_BF16) {
+    if (d == 64) launch_panel<Bf16Tiles<64>>(q, repr, panel, row0, rows, n, causal, stream);
+    else launch_panel<Bf16Tiles<128>>(q, repr, panel, row0, rows, n, causal, stream);
+  } else {
+    if (d == 64) launch_panel<F32Tiles<64>>(q, repr, panel, row0, rows, n, causal, stream);
+    else launch_panel<F32Tiles<128>>(q, repr, panel, row0, rows, n, causal, stream);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_coarse_select(const void* q, const float* repr, int32_t* idx, int64_t rows,
-                                int n, int d, bsa_dtype dtype, int topk, int causal,
-                                hipStream_t stream) {
-  if (topk <= 8) launch_d<8>(q, repr, nullptr, idx, 0, rows, n, d, dtype, topk, causal, stream);
-  else if (topk <= 16) launch_d<16>(q, repr, nullptr, idx, 0, rows, n, d, dtype, topk, causal, stream);
-  else launch_d<32>(q, repr, nullptr, idx, 0, rows, n, d, dtype, topk, causal, stream);
+hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t* repr_split,
+                                int32_t* idx, int64_t rows, int n, int d, bsa_dtype dtype,
+                                int topk, int causal, hipStream_t stream) {
+  if (dtype == BSA_BF16) {
+    if (d == 64) launch_select_k<Bf16PlaneTiles<64>>(q, repr_split, idx, rows, n, topk, causal, stream);
+    else launch_select_k<Bf16PlaneTiles<128>>(q, repr_split, idx, rows, n, topk, causal, stream);
+  } else {
+    if (d == 64) launch_select_k<F32Tiles<64>>(q, repr, idx, rows, n, topk, causal, stream);
+    else launch_select_k<F32Tiles<128>>(q, repr, idx, rows, n, topk, causal, stream);
+  }
   return hipGetLastError();
 }
 

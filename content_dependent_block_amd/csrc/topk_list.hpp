@@ -31,18 +31,19 @@ struct TopList {
       b[j] = -1;
     }
   }
-  // A score of -inf or NaN is never kept.
+  // A score of -inf or NaN is never kept.  Slots are updated from the bottom
+  // up, so only two compare masks are live at a time.
   __device__ __forceinline__ void offer(float x, int beta) {
-    bool gt[KL];
-#pragma unroll
-    for (int j = 0; j < KL; ++j) gt[j] = x > v[j];
+    bool below = x > v[KL - 1];
 #pragma unroll
     for (int j = KL - 1; j >= 1; --j) {
-      v[j] = gt[j - 1] ? v[j - 1] : (gt[j] ? x : v[j]);
-      b[j] = gt[j - 1] ? b[j - 1] : (gt[j] ? beta : b[j]);
+      const bool above = x > v[j - 1];
+      v[j] = above ? v[j - 1] : (below ? x : v[j]);
+      b[j] = above ? b[j - 1] : (below ? beta : b[j]);
+      below = above;
     }
-    v[0] = gt[0] ? x : v[0];
-    b[0] = gt[0] ? beta : b[0];
+    v[0] = below ? x : v[0];
+    b[0] = below ? beta : b[0];
   }
 };
 
