@@ -64,9 +64,12 @@ __device__ __forceinline__ int64_t xcd_tile(int causal) {
 }
 
 // ------------------------------------------------------ score tiles ----
-// One lane's 4 scores of a 16-block MFMA tile from the 3-term R tile in LDS
-// ([term][64 blocks][D + 8] bf16) and its query's B operand.
-template <int D>
+// A producer stages TB representatives in LDS and returns one lane's 4
+// scores of a 16-block MFMA tile (tile): C[block 4g + j][query c16].
+
+// One lane's 4 scores of MFMA tile mt from the 3-term R tile in LDS
+// ([term][TB blocks][D + 8] bf16) and its query's B operand.
+template <int D, int TB>
 __device__ __forceinline__ f32x4 bf16_tile(const unsigned char* lds, const bf16x8 (&qb)[D / 32], int mt,
                                            int g, int c16) {
   constexpr int PITCH = D + 8;
@@ -76,30 +79,35 @@ __device__ __forceinline__ f32x4 bf16_tile(const unsigned char* lds, const bf16x
   for (int ks = 0; ks < D / 32; ++ks) {
 #pragma unroll
     for (int t = 0; t < kTerms; ++t) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(rs + (t * kTile + mt * 16 + c16) * PITCH + 8 * g + 32 * ks);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(rs + (t * TB + mt * 16 + c16) * PITCH + 8 * g + 32 * ks);
       acc = mfma_16x16x32_bf16(a, qb[ks], acc);
     }
   }
   return acc;
 }
-// A producer stages 64 representatives in LDS (stage) and returns one lane's
-// 4 scores of a 16-block MFMA tile (tile): C[block 4g + j][query c16].
+
+template <int D>
+__device__ __forceinline__ void load_q_bf16(bf16x8 (&qb)[D / 32], const bf16_bits* __restrict__ q,
+                                            int64_t qrow, int g) {
+  const bf16_bits* qr = q + qrow * D + 8 * g;  // B operand: d = 8g + 32ks .. +7
+#pragma unroll
+  for (int ks = 0; ks < D / 32; ++ks) qb[ks] = as_bf16x8(ld16(qr + 32 * ks));
+}
 
 // bf16 inputs, float32 representatives [block][d] split here into three bf16
-// terms (the same split block_pool writes for the select kernel).
+// terms (the same split block_pool writes for the select kernel).  Panel
+// kernel.
 template <int D>
 struct Bf16Tiles {
   using QT = bf16_bits;
   using Src = float;
-  static constexpr int KS = D / 32;      // MFMA k-steps over d
+  static constexpr int TB = 64;
   static constexpr int PITCH = D + 8;    // bf16 per LDS row (16 B pad)
-  static constexpr int LDS_BYTES = kTerms * kTile * PITCH * 2;
-  bf16x8 qb[KS];  // B operand: this lane's query, d = 8g + 32ks .. +7
+  static constexpr int LDS_BYTES = kTerms * TB * PITCH * 2;
+  bf16x8 qb[D / 32];
 
   __device__ __forceinline__ void load_q(const QT* __restrict__ q, int64_t qrow, int g) {
-    const QT* qr = q + qrow * D + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = as_bf16x8(ld16(qr + 32 * ks));
+    load_q_bf16<D>(qb, q, qrow, g);
   }
   __device__ __forceinline__ static const Src* head_base(const Src* r, int64_t bh, int nb) {
     return r + bh * nb * D;
@@ -107,9 +115,9 @@ struct Bf16Tiles {
   __device__ __forceinline__ static void stage(unsigned char* lds, const Src* __restrict__ rbase, int bt,
                                                int nb, int tid) {
     __bf16* rs = reinterpret_cast<__bf16*>(lds);
-    for (int c = tid; c < kTile * D / 4; c += 256) {
+    for (int c = tid; c < TB * D / 4; c += 256) {
       const int r = c / (D / 4), col = (c % (D / 4)) * 4;
-      const int beta = bt * kTile + r;
+      const int beta = bt * TB + r;
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       if (beta < nb) x = *reinterpret_cast<const float4*>(rbase + static_cast<int64_t>(beta) * D + col);
       float v[4] = {x.x, x.y, x.z, x.w};
@@ -118,38 +126,36 @@ struct Bf16Tiles {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const __bf16 h = f32_to_bf16(v[e]);
-          rs[(t * kTile + r) * PITCH + col + e] = h;
+          rs[(t * TB + r) * PITCH + col + e] = h;
           v[e] -= static_cast<float>(h);
         }
       }
     }
   }
   __device__ __forceinline__ f32x4 tile(const unsigned char* lds, int mt, int g, int c16) const {
-    return bf16_tile<D>(lds, qb, mt, g, c16);
+    return bf16_tile<D, TB>(lds, qb, mt, g, c16);
   }
 };
 
 // bf16 inputs, representatives pre-split by block_pool into term planes
-// [term][beta][d] per head.  fetch() issues the global loads of a tile into
-// registers, put() writes them to LDS: the loads of tile bt + 1 are in flight
-// while tile bt is computed.  Rows past the last block repeat the last block
-// (their scores are never used).
+// [term][beta][d] per head.  Select kernel: fetch() issues the global loads
+// of a tile into registers, put() writes them to LDS, so the loads of tile
+// bt + 1 are in flight while tile bt is computed.  Rows past the last block
+// repeat the last block (their scores are never used).
 template <int D>
 struct Bf16PlaneTiles {
   using QT = bf16_bits;
   using Src = bf16_bits;
-  static constexpr int KS = D / 32;
+  static constexpr int TB = 32;
   static constexpr int PITCH = D + 8;
-  static constexpr int LDS_BYTES = kTerms * kTile * PITCH * 2;
-  static constexpr int CPR = D / 8;               // 16-byte chunks per block row
-  static constexpr int PER = kTile * CPR / 256;   // chunks per thread and term
-  bf16x8 qb[KS];
+  static constexpr int LDS_BYTES = kTerms * TB * PITCH * 2;
+  static constexpr int CPR = D / 8;             // 16-byte chunks per block row
+  static constexpr int PER = TB * CPR / 256;    // chunks per thread and term
+  bf16x8 qb[D / 32];
   uint4 pf[kTerms][PER];
 
   __device__ __forceinline__ void load_q(const QT* __restrict__ q, int64_t qrow, int g) {
-    const QT* qr = q + qrow * D + 8 * g;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qb[ks] = as_bf16x8(ld16(qr + 32 * ks));
+    load_q_bf16<D>(qb, q, qrow, g);
   }
   __device__ __forceinline__ static const Src* head_base(const Src* r, int64_t bh, int nb) {
     return r + bh * kTerms * nb * D;
@@ -158,7 +164,7 @@ struct Bf16PlaneTiles {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 8;
-      const int beta = min(bt * kTile + r, nb - 1);
+      const int beta = min(bt * TB + r, nb - 1);
 #pragma unroll
       for (int t = 0; t < kTerms; ++t)
         pf[t][u] = ld16(rbase + static_cast<uint32_t>((t * nb + beta) * D + col));
@@ -170,25 +176,26 @@ struct Bf16PlaneTiles {
     for (int u = 0; u < PER; ++u) {
       const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 8;
 #pragma unroll
-      for (int t = 0; t < kTerms; ++t) *reinterpret_cast<uint4*>(rs + (t * kTile + r) * PITCH + col) = pf[t][u];
+      for (int t = 0; t < kTerms; ++t) *reinterpret_cast<uint4*>(rs + (t * TB + r) * PITCH + col) = pf[t][u];
     }
   }
   __device__ __forceinline__ f32x4 tile(const unsigned char* lds, int mt, int g, int c16) const {
-    return bf16_tile<D>(lds, qb, mt, g, c16);
+    return bf16_tile<D, TB>(lds, qb, mt, g, c16);
   }
 };
 
 // fp32 inputs: v_mfma_f32_16x16x4_f32; slot (ks, g) carries d = KS*g + ks.
 // stage() for the panel kernel; fetch()/put() as for Bf16PlaneTiles.
-template <int D>
+template <int D, int TB_>
 struct F32Tiles {
   using QT = float;
   using Src = float;
+  static constexpr int TB = TB_;
   static constexpr int KS = D / 4;
   static constexpr int PITCH = D + 4;
-  static constexpr int LDS_BYTES = kTile * PITCH * 4;
-  static constexpr int CPR = D / 4;               // 16-byte chunks per block row
-  static constexpr int PER = kTile * CPR / 256;
+  static constexpr int LDS_BYTES = TB * PITCH * 4;
+  static constexpr int CPR = D / 4;             // 16-byte chunks per block row
+  static constexpr int PER = TB * CPR / 256;
   float qf[KS];
   float4 pf[PER];
 
@@ -206,9 +213,9 @@ struct F32Tiles {
   __device__ __forceinline__ static void stage(unsigned char* lds, const Src* __restrict__ rbase, int bt,
                                                int nb, int tid) {
     float* rs = reinterpret_cast<float*>(lds);
-    for (int c = tid; c < kTile * D / 4; c += 256) {
+    for (int c = tid; c < TB * D / 4; c += 256) {
       const int r = c / (D / 4), col = (c % (D / 4)) * 4;
-      const int beta = bt * kTile + r;
+      const int beta = bt * TB + r;
       float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
       if (beta < nb) x = *reinterpret_cast<const float4*>(rbase + static_cast<int64_t>(beta) * D + col);
       *reinterpret_cast<float4*>(rs + r * PITCH + col) = x;
@@ -218,7 +225,7 @@ struct F32Tiles {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 4;
-      const int beta = min(bt * kTile + r, nb - 1);
+      const int beta = min(bt * TB + r, nb - 1);
       pf[u] = *reinterpret_cast<const float4*>(rbase + static_cast<uint32_t>(beta * D + col));
     }
   }
@@ -239,12 +246,13 @@ struct F32Tiles {
   }
 };
 
-// Where a workgroup's 64 query rows sit, and which blocks they may select.
+// Where a workgroup's 64 query rows sit, and which blocks they may select;
+// nbt = number of TB-block tiles to walk.
 struct TileInfo {
   int64_t tile_row, bh, qrow;
   int nb, nbt, nvalid, forced;
   int tid, lane, wave, g, c16;
-  __device__ __forceinline__ TileInfo(int64_t row0, int n, int causal) {
+  __device__ __forceinline__ TileInfo(int64_t row0, int n, int causal, int TB) {
     nb = n / kTile;
     tid = threadIdx.x;
     lane = tid & 63;
@@ -256,7 +264,7 @@ struct TileInfo {
     const int i0 = static_cast<int>(tile_row % n);
     qrow = tile_row + wave * 16 + c16;
     const int qblk = i0 / kTile;  // query block of all 64 rows
-    nbt = causal ? qblk / kTile + 1 : (nb + kTile - 1) / kTile;
+    nbt = causal ? qblk / TB + 1 : (nb + TB - 1) / TB;
     nvalid = causal ? qblk + 1 : nb;
     forced = causal ? qblk : -1;
   }
@@ -276,7 +284,7 @@ __global__ __launch_bounds__(256) void coarse_panel_kernel(const typename TL::QT
                                                            float* __restrict__ panel, int64_t row0,
                                                            int64_t prows, int n, int causal) {
   __shared__ __attribute__((aligned(16))) unsigned char rs[TL::LDS_BYTES];
-  const TileInfo ti(row0, n, causal);
+  const TileInfo ti(row0, n, causal, TL::TB);
   TL sc;
   sc.load_q(q, ti.qrow, ti.g);
   const auto* rbase = TL::head_base(rsrc, ti.bh, ti.nb);
@@ -286,10 +294,10 @@ __global__ __launch_bounds__(256) void coarse_panel_kernel(const typename TL::QT
     TL::stage(rs, rbase, bt, ti.nb, ti.tid);
     __syncthreads();
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      if (bt * kTile + mt * 16 >= ti.nb) break;
+    for (int mt = 0; mt < TL::TB / 16; ++mt) {
+      if (bt * TL::TB + mt * 16 >= ti.nb) break;
       const f32x4 acc = sc.tile(rs, mt, ti.g, ti.c16);
-      const int beta0 = bt * kTile + mt * 16 + 4 * ti.g;
+      const int beta0 = bt * TL::TB + mt * 16 + 4 * ti.g;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (beta0 + j < ti.nb) panel[static_cast<int64_t>(beta0 + j) * prows + prow] = acc[j];
@@ -376,30 +384,35 @@ __device__ __forceinline__ void bitonic_clean(float (&v)[N], int (&b)[N]) {
 
 // Both lanes of a pair (l, l ^ M) hold a sorted list; afterwards both hold
 // the N largest of the two lists, sorted: c[i] = the larger of a[i] and the
-// partner's a[N-1-i] is bitonic and holds the N largest.
+// partner's a[N-1-i] is bitonic and holds the N largest.  Positions i and
+// N-1-i are done together, before either is overwritten in both lanes, so no
+// copy of the lists is needed.
 template <int M, int N>
 __device__ __forceinline__ void merge_top(float (&a)[N], int lane) {
-  float p[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) p[i] = __uint_as_float(lane_xor<M>(__float_as_uint(a[N - 1 - i]), lane));
-#pragma unroll
-  for (int i = 0; i < N; ++i) a[i] = fmaxf(a[i], p[i]);
+  for (int i = 0; i < N / 2; ++i) {
+    const float pi = __uint_as_float(lane_xor<M>(__float_as_uint(a[N - 1 - i]), lane));
+    const float pj = __uint_as_float(lane_xor<M>(__float_as_uint(a[i]), lane));
+    a[i] = fmaxf(a[i], pi);
+    a[N - 1 - i] = fmaxf(a[N - 1 - i], pj);
+  }
   bitonic_clean<N>(a);
 }
 template <int M, int N>
 __device__ __forceinline__ void merge_top(float (&v)[N], int (&b)[N], int lane) {
-  float pv[N];
-  int pb[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    pv[i] = __uint_as_float(lane_xor<M>(__float_as_uint(v[N - 1 - i]), lane));
-    pb[i] = static_cast<int>(lane_xor<M>(static_cast<uint32_t>(b[N - 1 - i]), lane));
-  }
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const bool take = ranks_above(pv[i], pb[i], v[i], b[i]);
-    v[i] = take ? pv[i] : v[i];
-    b[i] = take ? pb[i] : b[i];
+  for (int i = 0; i < N / 2; ++i) {
+    const int j = N - 1 - i;
+    const float pvi = __uint_as_float(lane_xor<M>(__float_as_uint(v[j]), lane));
+    const int pbi = static_cast<int>(lane_xor<M>(static_cast<uint32_t>(b[j]), lane));
+    const float pvj = __uint_as_float(lane_xor<M>(__float_as_uint(v[i]), lane));
+    const int pbj = static_cast<int>(lane_xor<M>(static_cast<uint32_t>(b[i]), lane));
+    const bool ti = ranks_above(pvi, pbi, v[i], b[i]);
+    const bool tj = ranks_above(pvj, pbj, v[j], b[j]);
+    v[i] = ti ? pvi : v[i];
+    b[i] = ti ? pbi : b[i];
+    v[j] = tj ? pvj : v[j];
+    b[j] = tj ? pbj : b[j];
   }
   bitonic_clean<N>(v, b);
 }
@@ -443,72 +456,78 @@ __device__ __forceinline__ void finish_select(TopList<KL>& l, const TileInfo& ti
 
 // Stream the tiles of the workgroup's representatives through LDS, register-
 // prefetching tile bt + 1 while tile bt is computed, and hand each 16-block
-// MFMA tile to fast(bt, mt, b0, acc) or slow(...) (b0 = first block of the
-// MFMA tile).  Every block of a tile before the last is an ordinary
-// candidate (below the last candidate and not the causal own block, which
-// both lie in the last tile), so only the last tile takes the checked slow().
-template <typename TL, typename FF, typename FS>
+// MFMA tile to fast(h, mt, b0, acc) or slow(...) (b0 = first block of the
+// MFMA tile, h = bt mod NH as a compile-time value: the loop is unrolled by
+// NH).  Every block of a tile before the last is an ordinary candidate (below
+// the last candidate and not the causal own block, which both lie in the
+// last tile), so only the last tile takes the checked slow().
+template <int NH, typename TL, typename FF, typename FS>
 __device__ __forceinline__ void walk(TL& sc, unsigned char* rs, const typename TL::Src* rbase,
                                      const TileInfo& ti, FF&& fast, FS&& slow) {
+  constexpr int MT = TL::TB / 16;
   sc.fetch(rbase, ti.nb, 0, ti.tid);
-  for (int bt = 0; bt < ti.nbt; ++bt) {
-    __syncthreads();
-    sc.put(rs, ti.tid);
-    const bool last = bt + 1 == ti.nbt;
-    if (!last) sc.fetch(rbase, ti.nb, bt + 1, ti.tid);
-    __syncthreads();
-    if (!last) {
+  for (int bt0 = 0; bt0 < ti.nbt; bt0 += NH) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) fast(bt, mt, bt * kTile + mt * 16, sc.tile(rs, mt, ti.g, ti.c16));
-    } else {
+    for (int h = 0; h < NH; ++h) {
+      const int bt = bt0 + h;
+      if (bt < ti.nbt) {
+        __syncthreads();
+        sc.put(rs, ti.tid);
+        const bool last = bt + 1 == ti.nbt;
+        if (!last) sc.fetch(rbase, ti.nb, bt + 1, ti.tid);
+        __syncthreads();
+        if (!last) {
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const int b0 = bt * kTile + mt * 16;
-        if (b0 >= ti.nb) break;
-        slow(bt, mt, b0, sc.tile(rs, mt, ti.g, ti.c16));
+          for (int mt = 0; mt < MT; ++mt) fast(h, mt, bt * TL::TB + mt * 16, sc.tile(rs, mt, ti.g, ti.c16));
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const int b0 = bt * TL::TB + mt * 16;
+            if (b0 >= ti.nb) break;
+            slow(h, mt, b0, sc.tile(rs, mt, ti.g, ti.c16));
+          }
+        }
       }
     }
   }
 }
 
-template <typename TL, int KL, int GM, int CAP>
-__global__ __launch_bounds__(256) void coarse_select_kernel(const typename TL::QT* __restrict__ q,
-                                                            const typename TL::Src* __restrict__ rsrc,
-                                                            int32_t* __restrict__ idx, int n, int topk,
-                                                            int causal) {
+// MINW: waves per SIMD the register budget is sized for.
+template <typename TL, int KL, int GM, int CAP, int MINW>
+__global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename TL::QT* __restrict__ q,
+                                                                  const typename TL::Src* __restrict__ rsrc,
+                                                                  int32_t* __restrict__ idx, int n,
+                                                                  int topk, int causal) {
+  constexpr int MT = TL::TB / 16;     // MFMA tiles per R tile
+  constexpr int NS = 16 * GM;         // group slots per lane
+  constexpr int NH = NS / (4 * MT);   // R tiles per cycle of slots
   __shared__ __attribute__((aligned(16))) unsigned char rs[TL::LDS_BYTES];
-  // per lane: candidate (score, block bits); slot CAP takes the discarded
-  // writes.
-  __shared__ float2 cvb[4][CAP + 1][64];
-  const TileInfo ti(0, n, causal);
+  // per lane: candidate scores and blocks; slot CAP takes the discarded writes
+  __shared__ float cv[4][CAP + 1][64];
+  __shared__ uint16_t cb[4][CAP + 1][64];
+  const TileInfo ti(0, n, causal, TL::TB);
   TL sc;
   sc.load_q(q, ti.qrow, ti.g);
   const auto* rbase = TL::head_base(rsrc, ti.bh, ti.nb);
   const int keff = topk < ti.nvalid ? topk : ti.nvalid;
 
-  // pass 1: group maxima; the lane's group of block 64 bt + 16 mt + 4 g + j
-  // is slot 16 (bt mod GM) + 4 mt + j.
-  float a[16 * GM];
+  // pass 1: group maxima.  The lane's block 16 (MT bt + mt) + 4 g + j goes to
+  // slot 4 ((MT bt + mt) mod 4 GM) + j: G = 64 GM groups over the 4 lanes.
+  float a[NS];
 #pragma unroll
-  for (int u = 0; u < 16 * GM; ++u) a[u] = -INFINITY;
-  auto group_max = [&](bool checked, int bt, int mt, int b0, const f32x4& acc) {
-    const int h = GM == 1 ? 0 : (bt & (GM - 1));
+  for (int u = 0; u < NS; ++u) a[u] = -INFINITY;
+  auto group_max = [&](bool checked, int h, int mt, int b0, const f32x4& acc) {
 #pragma unroll
-    for (int hh = 0; hh < GM; ++hh) {
-      if (hh == h) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float x = checked ? ti.cand(acc[j], b0 + 4 * ti.g + j) : acc[j];
-          a[16 * hh + 4 * mt + j] = fmaxf(a[16 * hh + 4 * mt + j], x);
-        }
-      }
+    for (int j = 0; j < 4; ++j) {
+      const float x = checked ? ti.cand(acc[j], b0 + 4 * ti.g + j) : acc[j];
+      a[4 * (MT * h + mt) + j] = fmaxf(a[4 * (MT * h + mt) + j], x);
     }
   };
-  walk(sc, rs, rbase, ti,
-       [&](int bt, int mt, int b0, const f32x4& acc) { group_max(false, bt, mt, b0, acc); },
-       [&](int bt, int mt, int b0, const f32x4& acc) { group_max(true, bt, mt, b0, acc); });
-  sort_desc<16 * GM>(a);
-  const float tau = kth_of_lanes<16 * GM>(a, keff, ti.lane);
+  walk<NH>(sc, rs, rbase, ti,
+           [&](int h, int mt, int b0, const f32x4& acc) { group_max(false, h, mt, b0, acc); },
+           [&](int h, int mt, int b0, const f32x4& acc) { group_max(true, h, mt, b0, acc); });
+  sort_desc<NS>(a);
+  const float tau = kth_of_lanes<NS>(a, keff, ti.lane);
 
   // pass 2: the candidates >= tau, in ascending block order
   int cnt = 0;
@@ -519,12 +538,13 @@ __global__ __launch_bounds__(256) void coarse_select_kernel(const typename TL::Q
       const float x = checked ? ti.cand(acc[j], beta) : acc[j];
       const bool c = x >= tau;
       const int slot = c ? min(cnt, CAP) : CAP;
-      cvb[ti.wave][slot][ti.lane] = make_float2(x, __int_as_float(beta));
+      cv[ti.wave][slot][ti.lane] = x;
+      cb[ti.wave][slot][ti.lane] = static_cast<uint16_t>(beta);
       cnt += c ? 1 : 0;
     }
   };
-  walk(sc, rs, rbase, ti, [&](int, int, int b0, const f32x4& acc) { append(false, b0, acc); },
-       [&](int, int, int b0, const f32x4& acc) { append(true, b0, acc); });
+  walk<1>(sc, rs, rbase, ti, [&](int, int, int b0, const f32x4& acc) { append(false, b0, acc); },
+          [&](int, int, int b0, const f32x4& acc) { append(true, b0, acc); });
   int tot = cnt + __shfl_xor(cnt, 16);
   tot += __shfl_xor(tot, 32);
   const int redo = __syncthreads_or(cnt > CAP || tot < keff);
@@ -536,13 +556,11 @@ __global__ __launch_bounds__(256) void coarse_select_kernel(const typename TL::Q
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) mc = max(mc, __shfl_xor(mc, m));
     mc = __builtin_amdgcn_readfirstlane(mc);
-    for (int i = 0; i < mc; ++i) {
-      const float2 e = cvb[ti.wave][i][ti.lane];
-      l.offer(i < cnt ? e.x : -INFINITY, __float_as_int(e.y));
-    }
+    for (int i = 0; i < mc; ++i)
+      l.offer(i < cnt ? cv[ti.wave][i][ti.lane] : -INFINITY, cb[ti.wave][i][ti.lane]);
   } else {
     // slots overflowed somewhere in the workgroup: offer every score
-    walk(sc, rs, rbase, ti,
+    walk<1>(sc, rs, rbase, ti,
          [&](int, int, int b0, const f32x4& acc) {
 #pragma unroll
            for (int j = 0; j < 4; ++j) l.offer(acc[j], b0 + 4 * ti.g + j);
@@ -564,20 +582,20 @@ void launch_panel(const void* q, const void* rsrc, float* panel, int64_t row0, i
                      panel, row0, rows, n, causal);
 }
 
-template <typename TL, int KL, int GM, int CAP>
+template <typename TL, int KL, int GM, int CAP, int MINW>
 void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
                    int causal, hipStream_t s) {
-  hipLaunchKernelGGL((coarse_select_kernel<TL, KL, GM, CAP>), dim3(static_cast<unsigned>(rows / kTile)), dim3(256),
-                     0, s, static_cast<const typename TL::QT*>(q), static_cast<const typename TL::Src*>(rsrc),
-                     idx, n, topk, causal);
+  hipLaunchKernelGGL((coarse_select_kernel<TL, KL, GM, CAP, MINW>), dim3(static_cast<unsigned>(rows / kTile)),
+                     dim3(256), 0, s, static_cast<const typename TL::QT*>(q),
+                     static_cast<const typename TL::Src*>(rsrc), idx, n, topk, causal);
 }
 
 template <typename TL>
 void launch_select_k(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
                      int causal, hipStream_t s) {
-  if (topk <= 8) launch_select<TL, 8, 1, 8>(q, rsrc, idx, rows, n, topk, causal, s);
-  else if (topk <= 16) launch_select<TL, 16, 1, 16>(q, rsrc, idx, rows, n, topk, causal, s);
-  else launch_select<TL, 32, 2, 32>(q, rsrc, idx, rows, n, topk, causal, s);
+  if (topk <= 8) launch_select<TL, 8, 1, 8, 4>(q, rsrc, idx, rows, n, topk, causal, s);
+  else if (topk <= 16) launch_select<TL, 16, 1, 16, 4>(q, rsrc, idx, rows, n, topk, causal, s);
+  else launch_select<TL, 32, 2, 32, 2>(q, rsrc, idx, rows, n, topk, causal, s);
 }
 
 }  // namespace
@@ -589,8 +607,8 @@ hipError_t launch_coarse_score(const void* q, const float* repr, float* panel, i
     if (d == 64) launch_panel<Bf16Tiles<64>>(q, repr, panel, row0, rows, n, causal, stream);
     else launch_panel<Bf16Tiles<128>>(q, repr, panel, row0, rows, n, causal, stream);
   } else {
-    if (d == 64) launch_panel<F32Tiles<64>>(q, repr, panel, row0, rows, n, causal, stream);
-    else launch_panel<F32Tiles<128>>(q, repr, panel, row0, rows, n, causal, stream);
+    if (d == 64) launch_panel<F32Tiles<64, 64>>(q, repr, panel, row0, rows, n, causal, stream);
+    else launch_panel<F32Tiles<128, 64>>(q, repr, panel, row0, rows, n, causal, stream);
   }
   return hipGetLastError();
 }
@@ -602,8 +620,8 @@ hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t
     if (d == 64) launch_select_k<Bf16PlaneTiles<64>>(q, repr_split, idx, rows, n, topk, causal, stream);
     else launch_select_k<Bf16PlaneTiles<128>>(q, repr_split, idx, rows, n, topk, causal, stream);
   } else {
-    if (d == 64) launch_select_k<F32Tiles<64>>(q, repr, idx, rows, n, topk, causal, stream);
-    else launch_select_k<F32Tiles<128>>(q, repr, idx, rows, n, topk, causal, stream);
+    if (d == 64) launch_select_k<F32Tiles<64, 32>>(q, repr, idx, rows, n, topk, causal, stream);
+    else launch_select_k<F32Tiles<128, 32>>(q, repr, idx, rows, n, topk, causal, stream);
   }
   return hipGetLastError();
 }
