@@ -67,12 +67,19 @@ __device__ __forceinline__ int64_t xcd_tile(int causal) {
 // A producer stages TB representatives in LDS and returns one lane's 4
 // scores of a 16-block MFMA tile (tile): C[block 4g + j][query c16].
 
+// LDS row pitch of the bf16 R tiles, in elements.  The A-operand read (16
+// lanes, 16 rows, 16 bytes each) runs without bank conflicts at D + 16 (160 B
+// rows for d = 64, 288 B for d = 128, measured on gfx950); at D + 8 half of
+// the LDS cycles are conflicts.
+template <int D>
+constexpr int kRPitch = D + 16;
+
 // One lane's 4 scores of MFMA tile mt from the 3-term R tile in LDS
-// ([term][TB blocks][D + 8] bf16) and its query's B operand.
+// ([term][TB blocks][kRPitch] bf16) and its query's B operand.
 template <int D, int TB>
 __device__ __forceinline__ f32x4 bf16_tile(const unsigned char* lds, const bf16x8 (&qb)[D / 32], int mt,
                                            int g, int c16) {
-  constexpr int PITCH = D + 8;
+  constexpr int PITCH = kRPitch<D>;
   const __bf16* rs = reinterpret_cast<const __bf16*>(lds);
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -102,7 +109,7 @@ struct Bf16Tiles {
   using QT = bf16_bits;
   using Src = float;
   static constexpr int TB = 64;
-  static constexpr int PITCH = D + 8;    // bf16 per LDS row (16 B pad)
+  static constexpr int PITCH = kRPitch<D>;
   static constexpr int LDS_BYTES = kTerms * TB * PITCH * 2;
   bf16x8 qb[D / 32];
 
@@ -147,7 +154,7 @@ struct Bf16PlaneTiles {
   using QT = bf16_bits;
   using Src = bf16_bits;
   static constexpr int TB = 32;
-  static constexpr int PITCH = D + 8;
+  static constexpr int PITCH = kRPitch<D>;
   static constexpr int LDS_BYTES = kTerms * TB * PITCH * 2;
   static constexpr int CPR = D / 8;             // 16-byte chunks per block row
   static constexpr int PER = TB * CPR / 256;    // chunks per thread and term
@@ -417,6 +424,17 @@ __device__ __forceinline__ void merge_top(float (&v)[N], int (&b)[N], int lane) 
   bitonic_clean<N>(v, b);
 }
 
+// The t-th entry (t >= 1) of a descending array = the smallest of its first
+// t entries; a reduction keeps the array in registers (a select chain on a
+// dynamic index can be turned into a scratch-memory load).
+template <int N>
+__device__ __forceinline__ float kth_desc(const float (&a)[N], int t) {
+  float r = a[0];
+#pragma unroll
+  for (int i = 1; i < N; ++i) r = fminf(r, i < t ? a[i] : INFINITY);
+  return r;
+}
+
 // The keff-th largest of the values held by the 4 lanes g = 0..3 of one
 // query (lanes c16 + 16 g), each sorted descending: after two pairwise
 // merges every lane holds the N largest of the 4 N, sorted.  keff <= N.
@@ -424,34 +442,35 @@ template <int N>
 __device__ __forceinline__ float kth_of_lanes(float (&a)[N], int keff, int lane) {
   merge_top<16, N>(a, lane);
   merge_top<32, N>(a, lane);
-  float r = a[0];
-#pragma unroll
-  for (int i = 1; i < N; ++i) r = keff - 1 == i ? a[i] : r;
-  return r;
+  return kth_desc<N>(a, keff);
 }
 
-// The query's 4 lanes each hold a sorted top-KL list of their own candidates;
-// after two pairwise merges every one of them holds the query's top KL.  The
-// first keff entries are the selection: lane g writes entries g, g + 4, ...
-// at their places in ascending block order, and -1 from keff up to topk.
+// Write a query's selection in ascending block order: b[0 .. keff) are the
+// selected blocks in any order (entries from keff on are ignored); lane g of
+// the query's 4 writes entries g, g + 4, ... at their places, and -1 from keff
+// up to topk.
 template <int KL>
-__device__ __forceinline__ void finish_select(TopList<KL>& l, const TileInfo& ti, int keff, int topk,
-                                              int32_t* __restrict__ dst) {
-  merge_top<16, KL>(l.v, l.b, ti.lane);
-  merge_top<32, KL>(l.v, l.b, ti.lane);
+__device__ __forceinline__ void emit_selection(const int (&b)[KL], int g, int keff, int topk,
+                                               int32_t* __restrict__ dst) {
 #pragma unroll
   for (int t0 = 0; t0 < KL; t0 += 4) {
-    if (t0 + ti.g < keff) {
-      int me = l.b[t0];
+    if (t0 + g < keff) {
+      int me = b[t0];
 #pragma unroll
-      for (int e = 1; e < 4; ++e) me = ti.g == e ? l.b[t0 + e] : me;
+      for (int e = 1; e < 4; ++e) me = g == e ? b[t0 + e] : me;
       int pos = 0;
 #pragma unroll
-      for (int u = 0; u < KL; ++u) pos += (u < keff && l.b[u] < me) ? 1 : 0;
+      for (int u = 0; u < KL; ++u) pos += (u < keff && b[u] < me) ? 1 : 0;
       dst[pos] = me;
     }
   }
-  for (int t = keff + ti.g; t < topk; t += 4) dst[t] = -1;
+  for (int t = keff + g; t < topk; t += 4) dst[t] = -1;
+}
+
+// Sum over the query's 4 lanes.
+__device__ __forceinline__ int sum4(int x, int lane) {
+  x += static_cast<int>(lane_xor<16>(static_cast<uint32_t>(x), lane));
+  return x + static_cast<int>(lane_xor<32>(static_cast<uint32_t>(x), lane));
 }
 
 // Stream the tiles of the workgroup's representatives through LDS, register-
@@ -501,8 +520,10 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
   constexpr int MT = TL::TB / 16;     // MFMA tiles per R tile
   constexpr int NS = 16 * GM;         // group slots per lane
   constexpr int NH = NS / (4 * MT);   // R tiles per cycle of slots
+  static_assert(TL::LDS_BYTES >= 64 * 33 * 4, "the R tile buffer also holds the selection lists");
+  static_assert(CAP <= 32, "candidate slots are tracked in a 32-bit mask");
   __shared__ __attribute__((aligned(16))) unsigned char rs[TL::LDS_BYTES];
-  // per lane: candidate scores and blocks; slot CAP takes the discarded writes
+  // per lane: candidate scores and blocks (the last slot is never read)
   __shared__ float cv[4][CAP + 1][64];
   __shared__ uint16_t cb[4][CAP + 1][64];
   const TileInfo ti(0, n, causal, TL::TB);
@@ -536,30 +557,89 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
     for (int j = 0; j < 4; ++j) {
       const int beta = b0 + 4 * ti.g + j;
       const float x = checked ? ti.cand(acc[j], beta) : acc[j];
-      const bool c = x >= tau;
-      const int slot = c ? min(cnt, CAP) : CAP;
-      cv[ti.wave][slot][ti.lane] = x;
-      cb[ti.wave][slot][ti.lane] = static_cast<uint16_t>(beta);
-      cnt += c ? 1 : 0;
+      if (x >= tau) {
+        const int slot = min(cnt, CAP);
+        cv[ti.wave][slot][ti.lane] = x;
+        cb[ti.wave][slot][ti.lane] = static_cast<uint16_t>(beta);
+        ++cnt;
+      }
     }
   };
   walk<1>(sc, rs, rbase, ti, [&](int, int, int b0, const f32x4& acc) { append(false, b0, acc); },
           [&](int, int, int b0, const f32x4& acc) { append(true, b0, acc); });
-  int tot = cnt + __shfl_xor(cnt, 16);
-  tot += __shfl_xor(tot, 32);
-  const int redo = __syncthreads_or(cnt > CAP || tot < keff);
+  const int redo = __syncthreads_or(cnt > CAP || sum4(cnt, ti.lane) < keff);
+  int32_t* dst = idx + ti.qrow * topk;
 
-  TopList<KL> l;
-  l.init();
   if (!redo) {
+    // T = the keff-th largest candidate score of the query: every lane sorts
+    // its candidates' scores, two pairwise merges give all 4 lanes the
+    // query's top CAP.
     int mc = cnt;
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) mc = max(mc, __shfl_xor(mc, m));
     mc = __builtin_amdgcn_readfirstlane(mc);
+    const float(&lv)[CAP + 1][64] = cv[ti.wave];
+    const uint16_t(&lb)[CAP + 1][64] = cb[ti.wave];
+    float c[CAP];
+#pragma unroll
+    for (int i = 0; i < CAP; ++i) c[i] = i < cnt ? lv[i][ti.lane] : -INFINITY;
+    sort_desc<CAP>(c);
+    merge_top<16, CAP>(c, ti.lane);
+    merge_top<32, CAP>(c, ti.lane);
+    const float T = kth_desc<CAP>(c, keff);
+    // Selected: scores above T, and the lowest-index `need` of those equal to
+    // T.  A tie's rank among the query's ties = ties before it in its own
+    // lane (ascending blocks) + ties with lower blocks in the other 3 lanes.
+    int gt = 0, eq = 0;
+    for (int i = 0; i < mc; ++i) {
+      const float x = i < cnt ? lv[i][ti.lane] : -INFINITY;
+      gt += x > T ? 1 : 0;
+      eq += x == T ? 1 : 0;
+    }
+    const int need = keff - sum4(gt, ti.lane);
+    const bool all_ties = sum4(eq, ti.lane) == need;
+    const int cnt16 = static_cast<int>(lane_xor<16>(static_cast<uint32_t>(cnt), ti.lane));
+    const int cnt32 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(cnt), ti.lane));
+    const int cnt48 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(cnt16), ti.lane));
+    uint32_t selbits = 0u;
+    int ties_before = 0;
+    for (int i = 0; i < mc; ++i) {
+      const float x = i < cnt ? lv[i][ti.lane] : -INFINITY;
+      bool s = x > T;
+      if (x == T) {
+        int r = ties_before++;
+        if (!all_ties) {
+          const int beta = lb[i][ti.lane];
+          for (int m = 1; m < 4; ++m) {
+            const int ln = ti.lane ^ (16 * m);
+            const int cn = m == 1 ? cnt16 : m == 2 ? cnt32 : cnt48;
+            for (int jj = 0; jj < cn; ++jj) r += (lv[jj][ln] == T && lb[jj][ln] < beta) ? 1 : 0;
+          }
+        }
+        s = r < need;
+      }
+      selbits |= s ? (1u << i) : 0u;
+    }
+    // The query's selection into its row of an LDS list (the R tile buffer
+    // is free now), this lane's part after those of lanes g' < g.
+    const int ns = __popc(selbits);
+    const int n16 = static_cast<int>(lane_xor<16>(static_cast<uint32_t>(ns), ti.lane));
+    const int n32 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(ns), ti.lane));
+    const int n48 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(n16), ti.lane));
+    int p = ((ti.g & 1) ? n16 : 0) + ((ti.g & 2) ? n32 + n48 : 0);
+    int* list = reinterpret_cast<int*>(rs) + (ti.wave * 16 + ti.c16) * 33;  // odd pitch: no bank conflicts
     for (int i = 0; i < mc; ++i)
-      l.offer(i < cnt ? cv[ti.wave][i][ti.lane] : -INFINITY, cb[ti.wave][i][ti.lane]);
+      if ((selbits >> i) & 1u) list[p++] = lb[i][ti.lane];
+    __syncthreads();
+    int b[KL];
+#pragma unroll
+    for (int u = 0; u < KL; ++u) b[u] = u < keff ? list[u] : 0x7fffffff;
+    emit_selection<KL>(b, ti.g, keff, topk, dst);
   } else {
-    // slots overflowed somewhere in the workgroup: offer every score
+    // slots overflowed somewhere in the workgroup: offer every score to
+    // exact register lists and merge them pairwise
+    TopList<KL> l;
+    l.init();
     walk<1>(sc, rs, rbase, ti,
          [&](int, int, int b0, const f32x4& acc) {
 #pragma unroll
@@ -569,8 +649,10 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
 #pragma unroll
            for (int j = 0; j < 4; ++j) l.offer(ti.cand(acc[j], b0 + 4 * ti.g + j), b0 + 4 * ti.g + j);
          });
+    merge_top<16, KL>(l.v, l.b, ti.lane);
+    merge_top<32, KL>(l.v, l.b, ti.lane);
+    emit_selection<KL>(l.b, ti.g, keff, topk, dst);
   }
-  finish_select<KL>(l, ti, keff, topk, idx + ti.qrow * topk);
 }
 
 // ------------------------------------------------------------ launch ----
