@@ -14,7 +14,6 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,17 +29,6 @@ import workloads as W  # noqa: E402
 METRIC = "fwd tokens/s and effective TFLOP/s at N=32k,H=8,D=64,B=64,k=16; % roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
-KERNEL_SOURCES = {
-    "block_pool": "block_pool.hip",
-    "coarse_score": "coarse_score.hip",
-    "topk_select": "topk_select.hip",
-    "coarse_select": "coarse_score.hip",
-    "sparse_flash_fwd": "fine_gather.hip",
-    "gather_index": "fine_gather.hip",
-    "gather_combine": "fine_gather.hip",
-}
-
-
 def visible_pairs(w: W.Workload) -> int:
     """Closed form of the (query, key) pairs the fine stage visits."""
     nb = w.nb
@@ -88,15 +76,10 @@ def stage_work(w: W.Workload):
     }
 
 
-def source_sha(kernel: str) -> str:
-    p = os.path.join(ROOT, "content_dependent_block_amd", "csrc", KERNEL_SOURCES[kernel])
-    with open(p, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
+    from content_dependent_block_amd.rocprof_summary import source_sha
     p = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
     if not os.path.exists(p):
         return None
