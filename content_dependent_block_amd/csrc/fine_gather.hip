@@ -197,6 +197,11 @@ __device__ __forceinline__ void load_q(QOperand<T, D>& qo, const T* __restrict__
   }
 }
 
+// Row pitch (fp16 elements) of a wave's LDS staging rows for the partial
+// outputs: 16 bytes of padding between rows.
+template <int D>
+constexpr int kStagePitch = D + 8;
+
 // Output dim carried by row m of PV output tile dt (bf16 path).  The V^T
 // rows fed to each MFMA tile are permuted so that the lanes of row group
 // g = m/4 end up holding 8 consecutive dims per pair of tiles: tiles 2u and
@@ -215,7 +220,7 @@ __device__ __forceinline__ int out_dim(int dt, int m) {
 // output tile whose A operand is a row of ones multiplies the same rounded
 // probabilities, so l sums exactly the weights that enter o.
 template <typename T, int D, bool CAUSAL>
-__device__ __forceinline__ void pair_group(const T* ks, const T* vs, const QOperand<T, D>& qo,
+__device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage, const QOperand<T, D>& qo,
                                            int64_t row, int beta, int n, bool live, int32_t pair,
                                            float scale_log2, PartialT<T>* __restrict__ po,
                                            float2* __restrict__ pml, int lane) {
@@ -311,29 +316,45 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, const QOper
     lt = lsum + __shfl_xor(lsum, 16);
     lt += __shfl_xor(lt, 32);
   }
-  if (!live) return;
   const float inv = 1.0f / lt;
-  PartialT<T>* op = po + static_cast<int64_t>(pair) * D;
   if constexpr (L::kBf16) {
-    // tiles 2u, 2u+1 hold dims 32u*(D/64) + 8g .. +7: one 16-byte store each,
-    // the 4 lanes of a pair writing 64 contiguous bytes per instruction
+    // Through the wave's LDS staging rows (16 pairs x D fp16) so that every
+    // partial row leaves as whole 128-byte lines: CPR lanes write one row's
+    // CPR 16-byte chunks in one instruction.  Non-temporal stores: the rows
+    // are read back only by the combine, and keeping them out of L2 leaves
+    // it to the gathered query rows.
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 #pragma unroll
     for (int u = 0; u < D / 32; ++u) {
       const f32x4 a0 = acc[2 * u] * inv, a1 = acc[2 * u + 1] * inv;
-      typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
       const f16x8 h = {static_cast<f16>(a0[0]), static_cast<f16>(a0[1]), static_cast<f16>(a0[2]),
                        static_cast<f16>(a0[3]), static_cast<f16>(a1[0]), static_cast<f16>(a1[1]),
                        static_cast<f16>(a1[2]), static_cast<f16>(a1[3])};
-      *reinterpret_cast<f16x8*>(op + out_dim<D>(2 * u, 4 * g)) = h;
+      *reinterpret_cast<f16x8*>(stage + c16 * kStagePitch<D> + out_dim<D>(2 * u, 4 * g)) = h;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int CPR = D * 2 / 16;  // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;    // rows per store instruction
+#pragma unroll
+    for (int i = 0; i < 16 / RPI; ++i) {
+      const int r = i * RPI + lane / CPR, ch = lane % CPR;
+      const int32_t pr = __shfl(pair, r);
+      const bool lv = __shfl(static_cast<int>(live), r) != 0;
+      const f16x8 h = *reinterpret_cast<const f16x8*>(stage + r * kStagePitch<D> + ch * 8);
+      if (lv) __builtin_nontemporal_store(h, reinterpret_cast<f16x8*>(po + static_cast<int64_t>(pr) * D) + ch);
     }
   } else {
+    if (!live) return;
+    PartialT<T>* op = po + static_cast<int64_t>(pair) * D;
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const f32x4 a = acc[dt] * inv;
       *reinterpret_cast<float4*>(op + 16 * dt + 4 * g) = make_float4(a[0], a[1], a[2], a[3]);
     }
   }
-  if (g == 0) pml[pair] = make_float2(m, lt);
+  if (live && g == 0) pml[pair] = make_float2(m, lt);
 }
 
 // One work item = up to kItemPairs pairs of one bucket (head, key block),
@@ -351,10 +372,12 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
     PartialT<T>* __restrict__ po, float2* __restrict__ pml) {
   using L = KvLayout<T, D>;
   constexpr int GPW = kItemPairs / 16 / 4;  // 16-pair groups per wave
-  __shared__ __align__(16) unsigned char smem[L::BYTES];
+  constexpr int STAGE_BYTES = L::kBf16 ? 16 * kStagePitch<D> * 2 : 0;  // per wave
+  __shared__ __align__(16) unsigned char smem[L::BYTES + 4 * STAGE_BYTES];
   T* ks = reinterpret_cast<T*>(smem);
   T* vs = reinterpret_cast<T*>(smem + L::K_BYTES);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  f16* stage = reinterpret_cast<f16*>(smem + L::BYTES + wave * STAGE_BYTES);
   const int g = lane >> 4, c16 = lane & 15;
 
   const int total = items[nbuckets];
@@ -400,8 +423,8 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     if ((wave + 4 * gi) * 16 >= cnt) break;  // wave-uniform
-    pair_group<T, D, CAUSAL>(ks, vs, qo[gi], row[gi], beta, n, live[gi], pair[gi], scale_log2, po,
-                             pml, lane);
+    pair_group<T, D, CAUSAL>(ks, vs, stage, qo[gi], row[gi], beta, n, live[gi], pair[gi], scale_log2,
+                             po, pml, lane);
   }
 }
 

@@ -3,8 +3,10 @@
 // early, so the loads overlap other work) and a register->LDS half.
 //
 // LDS layout:
-//   K: [64 keys][D + pad], natural layout; the pad (16 B for bf16, 16 B for
-//      fp32) staggers rows across banks for the 16-byte A-operand reads.
+//   K: [64 keys][D + pad], natural layout.  bf16: pad 16 elements (32 B); the
+//      16-byte A-operand reads of 16 rows then run without bank conflicts on
+//      gfx950 (with a 16-byte pad half the LDS cycles were conflicts).  fp32:
+//      pad 4 elements.
 //   V, bf16: transposed to [D][64 + 4 keys] so the A operand of
 //      O^T = V^T P^T is two 8-byte reads per lane; two keys are packed per
 //      32-bit LDS write.
@@ -20,7 +22,7 @@ namespace bsa {
 template <typename T, int D>
 struct KvLayout {
   static constexpr bool kBf16 = sizeof(T) == 2;
-  static constexpr int KPITCH = D + (kBf16 ? 8 : 4);        // elements per K row
+  static constexpr int KPITCH = D + (kBf16 ? 16 : 4);       // elements per K row
   static constexpr int VROWS = kBf16 ? D : kTile;           // bf16: V^T rows are d
   static constexpr int VPITCH = kBf16 ? kTile + 4 : D + 4;  // elements per V row
   static constexpr int K_BYTES = kTile * KPITCH * sizeof(T);
