@@ -29,6 +29,10 @@
 //     (each lane sorts its own, then k_eff rounds of a 4-lane tournament).
 //     The k_eff groups whose maxima are >= tau each hold a score >= tau, so at
 //     least k_eff scores are >= tau, and every score of the answer is >= tau.
+//     For bf16 inputs pass 1 multiplies only the hi term of the split; tau is
+//     then lowered by a bound E on |exact - hi-only| (relative 2^-8 per
+//     representative element, plus rounding; see pass1_error), which keeps
+//     it a bound for the exact scores at a third of the MFMA and LDS work.
 //   pass 2: the same scores again; those >= tau (typically k + a few) are
 //     appended to the lane's LDS slots in ascending block order.
 //   The lane offers its slots to an exact register top-KL list (topk_list.hpp,
@@ -63,6 +67,21 @@ __device__ __forceinline__ int64_t xcd_tile(int causal) {
   return (bid % 8) * per + (causal ? per - 1 - local : local);
 }
 
+// The value lane l ^ 16 (row pair swap) or l ^ 32 (half swap) holds, with the
+// gfx950 permlane swaps: called with the same register twice, the swap
+// returns the partner's value in the second result for rows 0 and 2 (lower
+// half) and in the first result for rows 1 and 3 (upper half).
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+
 // ------------------------------------------------------ score tiles ----
 // A producer stages TB representatives in LDS and returns one lane's 4
 // scores of a 16-block MFMA tile (tile): C[block 4g + j][query c16].
@@ -76,7 +95,7 @@ constexpr int kRPitch = D + 16;
 
 // One lane's 4 scores of MFMA tile mt from the 3-term R tile in LDS
 // ([term][TB blocks][kRPitch] bf16) and its query's B operand.
-template <int D, int TB>
+template <int D, int TB, int NT = kTerms>
 __device__ __forceinline__ f32x4 bf16_tile(const unsigned char* lds, const bf16x8 (&qb)[D / 32], int mt,
                                            int g, int c16) {
   constexpr int PITCH = kRPitch<D>;
@@ -85,7 +104,7 @@ __device__ __forceinline__ f32x4 bf16_tile(const unsigned char* lds, const bf16x
 #pragma unroll
   for (int ks = 0; ks < D / 32; ++ks) {
 #pragma unroll
-    for (int t = 0; t < kTerms; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(rs + (t * TB + mt * 16 + c16) * PITCH + 8 * g + 32 * ks);
       acc = mfma_16x16x32_bf16(a, qb[ks], acc);
     }
@@ -139,6 +158,7 @@ struct Bf16Tiles {
       }
     }
   }
+  template <int NT>
   __device__ __forceinline__ f32x4 tile(const unsigned char* lds, int mt, int g, int c16) const {
     return bf16_tile<D, TB>(lds, qb, mt, g, c16);
   }
@@ -148,7 +168,9 @@ struct Bf16Tiles {
 // [term][beta][d] per head.  Select kernel: fetch() issues the global loads
 // of a tile into registers, put() writes them to LDS, so the loads of tile
 // bt + 1 are in flight while tile bt is computed.  Rows past the last block
-// repeat the last block (their scores are never used).
+// repeat the last block (their scores are never used).  NT = number of terms
+// staged and multiplied: 3 (exact scores) or 1 (hi only, for the selection
+// bound; put<1>() also tracks max |hi| per column for its error bound).
 template <int D>
 struct Bf16PlaneTiles {
   using QT = bf16_bits;
@@ -158,36 +180,82 @@ struct Bf16PlaneTiles {
   static constexpr int LDS_BYTES = kTerms * TB * PITCH * 2;
   static constexpr int CPR = D / 8;             // 16-byte chunks per block row
   static constexpr int PER = TB * CPR / 256;    // chunks per thread and term
+  static_assert(256 % CPR == 0, "a thread keeps one column chunk");
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
   bf16x8 qb[D / 32];
   uint4 pf[kTerms][PER];
+  u16x2 amax[4];  // max |hi| bit patterns of this thread's 8 columns
 
   __device__ __forceinline__ void load_q(const QT* __restrict__ q, int64_t qrow, int g) {
     load_q_bf16<D>(qb, q, qrow, g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax[i] = u16x2{0, 0};
   }
   __device__ __forceinline__ static const Src* head_base(const Src* r, int64_t bh, int nb) {
     return r + bh * kTerms * nb * D;
   }
+  template <int NT>
   __device__ __forceinline__ void fetch(const Src* __restrict__ rbase, int nb, int bt, int tid) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 8;
       const int beta = min(bt * TB + r, nb - 1);
 #pragma unroll
-      for (int t = 0; t < kTerms; ++t)
+      for (int t = 0; t < NT; ++t)
         pf[t][u] = ld16(rbase + static_cast<uint32_t>((t * nb + beta) * D + col));
     }
   }
-  __device__ __forceinline__ void put(unsigned char* lds, int tid) const {
+  template <int NT>
+  __device__ __forceinline__ void put(unsigned char* lds, int tid) {
     __bf16* rs = reinterpret_cast<__bf16*>(lds);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 8;
 #pragma unroll
-      for (int t = 0; t < kTerms; ++t) *reinterpret_cast<uint4*>(rs + (t * TB + r) * PITCH + col) = pf[t][u];
+      for (int t = 0; t < NT; ++t) *reinterpret_cast<uint4*>(rs + (t * TB + r) * PITCH + col) = pf[t][u];
+      if constexpr (NT == 1) {
+        const uint32_t w[4] = {pf[0][u].x, pf[0][u].y, pf[0][u].z, pf[0][u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          amax[i] = __builtin_elementwise_max(amax[i], __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
+      }
     }
   }
+  template <int NT>
   __device__ __forceinline__ f32x4 tile(const unsigned char* lds, int mt, int g, int c16) const {
-    return bf16_tile<D, TB>(lds, qb, mt, g, c16);
+    return bf16_tile<D, TB, NT>(lds, qb, mt, g, c16);
+  }
+  // E >= |exact score - hi-only score| for this lane's query and every block
+  // of the head: (2^-8 + 2^-15) sum_d |q_d| R_d with R_d >= max_beta |r_beta,d|
+  // (hi is r rounded to 8 significant bits, |r - hi| <= 2^-8 |r|; 2^-15 covers
+  // the fp32 rounding of both sums).  The query's 4 lanes return the same E.
+  // lds: at least 256 * 16 + D * 4 bytes, free; a barrier precedes reuse.
+  __device__ __forceinline__ float pass1_error(unsigned char* lds, int tid, int lane, int g) const {
+    uint32_t* part = reinterpret_cast<uint32_t*>(lds);              // [256][4]
+    float* rmax = reinterpret_cast<float*>(lds + 256 * 16);         // [D]
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[tid * 4 + i] = __builtin_bit_cast(uint32_t, amax[i]);
+    __syncthreads();
+    if (tid < D) {
+      const int cc = tid / 8, e = tid % 8;  // column chunk, element in it
+      uint32_t m = 0u;
+      for (int t = cc; t < 256; t += CPR) {
+        const uint32_t w = part[t * 4 + e / 2];
+        m = max(m, (e & 1) ? (w >> 16) : (w & 0xffffu));
+      }
+      rmax[tid] = __uint_as_float(m << 16) * (1.0f + 0x1.0p-8f);
+    }
+    __syncthreads();
+    float sum = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        sum += fabsf(static_cast<float>(qb[ks][e])) * rmax[8 * g + 32 * ks + e];
+    sum += __uint_as_float(lane_xor<16>(__float_as_uint(sum), lane));
+    sum += __uint_as_float(lane_xor<32>(__float_as_uint(sum), lane));
+    return sum * (0x1.0p-8f + 0x1.0p-15f);
   }
 };
 
@@ -228,6 +296,7 @@ struct F32Tiles {
       *reinterpret_cast<float4*>(rs + r * PITCH + col) = x;
     }
   }
+  template <int NT>
   __device__ __forceinline__ void fetch(const Src* __restrict__ rbase, int nb, int bt, int tid) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -236,7 +305,8 @@ struct F32Tiles {
       pf[u] = *reinterpret_cast<const float4*>(rbase + static_cast<uint32_t>(beta * D + col));
     }
   }
-  __device__ __forceinline__ void put(unsigned char* lds, int tid) const {
+  template <int NT>
+  __device__ __forceinline__ void put(unsigned char* lds, int tid) {
     float* rs = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -244,6 +314,7 @@ struct F32Tiles {
       *reinterpret_cast<float4*>(rs + r * PITCH + col) = pf[u];
     }
   }
+  template <int NT>
   __device__ __forceinline__ f32x4 tile(const unsigned char* lds, int mt, int g, int c16) const {
     const float* rr = reinterpret_cast<const float*>(lds) + (mt * 16 + c16) * PITCH + KS * g;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -251,6 +322,8 @@ struct F32Tiles {
     for (int ks = 0; ks < KS; ++ks) acc = mfma_16x16x4_f32(rr[ks], qf[ks], acc);
     return acc;
   }
+  // Pass 1 computes the same scores as pass 2 here.
+  __device__ __forceinline__ float pass1_error(unsigned char*, int, int, int) const { return 0.f; }
 };
 
 // Where a workgroup's 64 query rows sit, and which blocks they may select;
@@ -303,7 +376,7 @@ __global__ __launch_bounds__(256) void coarse_panel_kernel(const typename TL::QT
 #pragma unroll
     for (int mt = 0; mt < TL::TB / 16; ++mt) {
       if (bt * TL::TB + mt * 16 >= ti.nb) break;
-      const f32x4 acc = sc.tile(rs, mt, ti.g, ti.c16);
+      const f32x4 acc = sc.template tile<kTerms>(rs, mt, ti.g, ti.c16);
       const int beta0 = bt * TL::TB + mt * 16 + 4 * ti.g;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
@@ -316,21 +389,6 @@ __global__ __launch_bounds__(256) void coarse_panel_kernel(const typename TL::QT
 // Is (va, ba) ranked above (vb, bb)?  Higher value first, then lower id.
 __device__ __forceinline__ bool ranks_above(float va, int ba, float vb, int bb) {
   return va > vb || (va == vb && ba < bb);
-}
-
-// The value lane l ^ 16 (row pair swap) or l ^ 32 (half swap) holds, with the
-// gfx950 permlane swaps: called with the same register twice, the swap
-// returns the partner's value in the second result for rows 0 and 2 (lower
-// half) and in the first result for rows 1 and 3 (upper half).
-template <int M>
-__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
-  if constexpr (M == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return (lane & 16) ? r[0] : r[1];
-  } else {
-    const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return (lane & 32) ? r[0] : r[1];
-  }
 }
 
 // Compare-exchanges, descending.  Plain values: larger first.  (value,
@@ -480,30 +538,31 @@ __device__ __forceinline__ int sum4(int x, int lane) {
 // NH).  Every block of a tile before the last is an ordinary candidate (below
 // the last candidate and not the causal own block, which both lie in the
 // last tile), so only the last tile takes the checked slow().
-template <int NH, typename TL, typename FF, typename FS>
+template <int NH, int NT, typename TL, typename FF, typename FS>
 __device__ __forceinline__ void walk(TL& sc, unsigned char* rs, const typename TL::Src* rbase,
                                      const TileInfo& ti, FF&& fast, FS&& slow) {
   constexpr int MT = TL::TB / 16;
-  sc.fetch(rbase, ti.nb, 0, ti.tid);
+  sc.template fetch<NT>(rbase, ti.nb, 0, ti.tid);
   for (int bt0 = 0; bt0 < ti.nbt; bt0 += NH) {
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const int bt = bt0 + h;
       if (bt < ti.nbt) {
         __syncthreads();
-        sc.put(rs, ti.tid);
+        sc.template put<NT>(rs, ti.tid);
         const bool last = bt + 1 == ti.nbt;
-        if (!last) sc.fetch(rbase, ti.nb, bt + 1, ti.tid);
+        if (!last) sc.template fetch<NT>(rbase, ti.nb, bt + 1, ti.tid);
         __syncthreads();
         if (!last) {
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) fast(h, mt, bt * TL::TB + mt * 16, sc.tile(rs, mt, ti.g, ti.c16));
+          for (int mt = 0; mt < MT; ++mt)
+            fast(h, mt, bt * TL::TB + mt * 16, sc.template tile<NT>(rs, mt, ti.g, ti.c16));
         } else {
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
             const int b0 = bt * TL::TB + mt * 16;
             if (b0 >= ti.nb) break;
-            slow(h, mt, b0, sc.tile(rs, mt, ti.g, ti.c16));
+            slow(h, mt, b0, sc.template tile<NT>(rs, mt, ti.g, ti.c16));
           }
         }
       }
@@ -521,11 +580,12 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
   constexpr int NS = 16 * GM;         // group slots per lane
   constexpr int NH = NS / (4 * MT);   // R tiles per cycle of slots
   static_assert(TL::LDS_BYTES >= 64 * 33 * 4, "the R tile buffer also holds the selection lists");
+  static_assert(TL::LDS_BYTES >= 256 * 16 + 128 * 4, "and the scratch of the pass-1 error bound");
   static_assert(CAP <= 32, "candidate slots are tracked in a 32-bit mask");
   __shared__ __attribute__((aligned(16))) unsigned char rs[TL::LDS_BYTES];
-  // per lane: candidate scores and blocks (the last slot is never read)
-  __shared__ float cv[4][CAP + 1][64];
-  __shared__ uint16_t cb[4][CAP + 1][64];
+  // per lane: candidate scores and blocks
+  __shared__ float cv[4][CAP][64];
+  __shared__ uint16_t cb[4][CAP][64];
   const TileInfo ti(0, n, causal, TL::TB);
   TL sc;
   sc.load_q(q, ti.qrow, ti.g);
@@ -544,11 +604,14 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
       a[4 * (MT * h + mt) + j] = fmaxf(a[4 * (MT * h + mt) + j], x);
     }
   };
-  walk<NH>(sc, rs, rbase, ti,
-           [&](int h, int mt, int b0, const f32x4& acc) { group_max(false, h, mt, b0, acc); },
-           [&](int h, int mt, int b0, const f32x4& acc) { group_max(true, h, mt, b0, acc); });
+  walk<NH, 1>(sc, rs, rbase, ti,
+              [&](int h, int mt, int b0, const f32x4& acc) { group_max(false, h, mt, b0, acc); },
+              [&](int h, int mt, int b0, const f32x4& acc) { group_max(true, h, mt, b0, acc); });
   sort_desc<NS>(a);
-  const float tau = kth_of_lanes<NS>(a, keff, ti.lane);
+  // pass 1 may run on approximate scores (bf16: the hi term alone); lowering
+  // the bound by their error keeps it a bound for the exact scores
+  const float err = sc.pass1_error(rs, ti.tid, ti.lane, ti.g);
+  const float tau = kth_of_lanes<NS>(a, keff, ti.lane) - err;
 
   // pass 2: the candidates >= tau, in ascending block order
   int cnt = 0;
@@ -558,15 +621,16 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
       const int beta = b0 + 4 * ti.g + j;
       const float x = checked ? ti.cand(acc[j], beta) : acc[j];
       if (x >= tau) {
-        const int slot = min(cnt, CAP);
-        cv[ti.wave][slot][ti.lane] = x;
-        cb[ti.wave][slot][ti.lane] = static_cast<uint16_t>(beta);
+        if (cnt < CAP) {
+          cv[ti.wave][cnt][ti.lane] = x;
+          cb[ti.wave][cnt][ti.lane] = static_cast<uint16_t>(beta);
+        }
         ++cnt;
       }
     }
   };
-  walk<1>(sc, rs, rbase, ti, [&](int, int, int b0, const f32x4& acc) { append(false, b0, acc); },
-          [&](int, int, int b0, const f32x4& acc) { append(true, b0, acc); });
+  walk<1, kTerms>(sc, rs, rbase, ti, [&](int, int, int b0, const f32x4& acc) { append(false, b0, acc); },
+                  [&](int, int, int b0, const f32x4& acc) { append(true, b0, acc); });
   const int redo = __syncthreads_or(cnt > CAP || sum4(cnt, ti.lane) < keff);
   int32_t* dst = idx + ti.qrow * topk;
 
@@ -578,8 +642,8 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
 #pragma unroll
     for (int m = 1; m < 64; m <<= 1) mc = max(mc, __shfl_xor(mc, m));
     mc = __builtin_amdgcn_readfirstlane(mc);
-    const float(&lv)[CAP + 1][64] = cv[ti.wave];
-    const uint16_t(&lb)[CAP + 1][64] = cb[ti.wave];
+    const float(&lv)[CAP][64] = cv[ti.wave];
+    const uint16_t(&lb)[CAP][64] = cb[ti.wave];
     float c[CAP];
 #pragma unroll
     for (int i = 0; i < CAP; ++i) c[i] = i < cnt ? lv[i][ti.lane] : -INFINITY;
@@ -640,7 +704,7 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
     // exact register lists and merge them pairwise
     TopList<KL> l;
     l.init();
-    walk<1>(sc, rs, rbase, ti,
+    walk<1, kTerms>(sc, rs, rbase, ti,
          [&](int, int, int b0, const f32x4& acc) {
 #pragma unroll
            for (int j = 0; j < 4; ++j) l.offer(acc[j], b0 + 4 * ti.g + j);
