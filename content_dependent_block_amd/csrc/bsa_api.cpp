@@ -340,7 +340,9 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   if (chunk > total) chunk = total;
   const int64_t pairs = chunk * topk;
   const int64_t nb = s.n / 64;
-  const int64_t buckets = (s.bh() < (chunk + s.n - 1) / s.n + 1 ? s.bh() : (chunk + s.n - 1) / s.n + 1) * nb;
+  const int qsegs = bsa::gather_segments(s.n, s.d, topk, dt);
+  const int64_t heads_spanned = s.bh() < (chunk + s.n - 1) / s.n + 1 ? s.bh() : (chunk + s.n - 1) / s.n + 1;
+  const int64_t buckets = heads_spanned * qsegs * nb;
   TRY(grow_buf(h, h->g_count, size_t(buckets) * 4, "bucket counts"));
   TRY(grow_buf(h, h->g_offsets, size_t(buckets + 1) * 4, "bucket offsets"));
   TRY(grow_buf(h, h->g_items, size_t(buckets + 1) * 4, "bucket work items"));
@@ -350,7 +352,7 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   TRY(grow_buf(h, h->g_list, size_t(pairs) * 4, "pair lists"));
   TRY(grow_buf(h, h->g_po, size_t(pairs) * s.d * (dt == BSA_BF16 ? 2 : 4), "partial outputs"));
   TRY(grow_buf(h, h->g_pml, size_t(pairs) * 8, "partial max/sum"));
-  bsa::GatherArgs a{q, k, v, out, idx, s.n, s.d, topk, causal, scale, dt, {}};
+  bsa::GatherArgs a{q, k, v, out, idx, s.n, s.d, topk, causal, scale, dt, qsegs, {}};
   a.ws.count = static_cast<int32_t*>(h->g_count.p);
   a.ws.offsets = static_cast<int32_t*>(h->g_offsets.p);
   a.ws.items = static_cast<int32_t*>(h->g_items.p);

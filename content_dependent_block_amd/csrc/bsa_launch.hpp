@@ -73,8 +73,14 @@ struct GatherArgs {
   int n, d, topk, causal;
   float scale;
   bsa_dtype dtype;
+  int qsegs;  // query segments per head (gather_segments); buckets = heads x qsegs x n/64
   GatherWorkspace ws;
 };
+
+// Query segments per head for the bucketing: the pairs of one (head, key
+// block) are split by query range so that the work items of one segment,
+// which run together, gather query rows from about 1 MB of Q.
+int gather_segments(int n, int d, int topk, bsa_dtype dtype);
 
 size_t gather_pair_bytes(int d, bsa_dtype dtype);  // partial bytes per (query, block) pair
 int64_t gather_grid(int64_t rows, int topk, int64_t nbuckets);  // attention-kernel workgroups

@@ -18,7 +18,8 @@
 // tiles and reads each K/V block once per 128 pairs.
 //
 // Kernels, per chunk of query rows (the chunk bounds the partial buffer):
-//   bucket_count   -- histogram of the chunk's pairs by (head, block); each pair
+//   bucket_count   -- histogram of the chunk's pairs by (head, query segment,
+//                     key block); each pair
 //                     gets its rank inside its bucket (LDS histogram per 64 rows,
 //                     one global atomic per (workgroup, block)).
 //   bucket_scan    -- one workgroup: exclusive prefix of the counts (pair offsets)
@@ -28,7 +29,9 @@
 //                     of the block in LDS, the pairs' query rows gathered into
 //                     MFMA operands, S^T = K Q^T and O^T = V^T P^T on MFMA,
 //                     partial (m, l, o) out.  Work items are laid out so that
-//                     consecutive items of one head land on one XCD.
+//                     consecutive items (one head, one query segment,
+//                     neighbouring blocks) land on one XCD, whose L2 then holds
+//                     the segment's query rows (about 1 MB, gather_segments).
 //   combine        -- per query row, merge its partials in slot order.
 // The order of pairs inside a bucket (set by atomics) does not affect any
 // result: every MFMA column is computed independently of the others.
@@ -55,15 +58,23 @@ __device__ __forceinline__ bool pair_valid(int beta, int nb, int64_t row, int n,
   return !causal || beta <= static_cast<int>(row % n) / kTile;
 }
 
+// Bucket of pair (row, beta): (head, query segment, key block), so that the
+// buckets of one segment of one head are consecutive.
+__device__ __forceinline__ int64_t bucket_of(int64_t row, int beta, int n, int nb, int qsegs, int64_t bh0) {
+  const int seg = static_cast<int>(row % n) / (n / qsegs);
+  return ((row / n - bh0) * qsegs + seg) * nb + beta;
+}
+
 __global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, int64_t count) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i < count) p[i] = 0;
 }
 
-// One workgroup per `rpw` query rows of one head (rpw divides n and row0).
+// One workgroup per `rpw` query rows of one query segment (rpw divides the
+// segment length and row0).
 __global__ __launch_bounds__(256) void bucket_count_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ count, int32_t* __restrict__ rank,
-    int64_t row0, int64_t rows, int n, int topk, int causal, int64_t bh0, int rpw) {
+    int64_t row0, int64_t rows, int n, int topk, int causal, int64_t bh0, int rpw, int qsegs) {
   extern __shared__ int32_t hist[];  // [nb] local counts, then [nb] global bases
   const int nb = n / kTile;
   int32_t* base = hist + nb;
@@ -71,7 +82,7 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
   const int64_t nrows = (row0 + rows - r_begin) < rpw ? (row0 + rows - r_begin) : rpw;
   const int npairs = static_cast<int>(nrows) * topk;
   const int64_t p_begin = (r_begin - row0) * topk;  // chunk-relative pair id of the first pair
-  const int64_t bucket0 = (r_begin / n - bh0) * nb;
+  const int64_t bucket0 = bucket_of(r_begin, 0, n, nb, qsegs, bh0);  // rpw divides the segment
   for (int c = threadIdx.x; c < nb; c += 256) hist[c] = 0;
   __syncthreads();
   for (int e = threadIdx.x; e < npairs; e += 256) {
@@ -90,42 +101,89 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
 // Single workgroup of 1024 threads.  offsets[b] / items[b] are exclusive
-// prefixes; entry nbuckets holds the totals.
+// prefixes; entry nbuckets holds the totals.  Passes of 1024 x 16 buckets:
+// the counts are loaded coalesced into LDS, each thread sums a contiguous run
+// of 16, one block-wide scan of the run sums (waves, then the 16 wave totals)
+// gives every run its base, and the prefixes go back through LDS to
+// coalesced stores.  Runs are padded to 17 words (no bank conflicts).
+constexpr int kScanRun = 16;
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(const int32_t* __restrict__ count,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ items,
                                                            int nbuckets) {
-  __shared__ int32_t s_pairs[1024], s_items[1024];
-  const int t = threadIdx.x;
-  const int per = (nbuckets + 1023) / 1024;
-  const int b0 = t * per;
-  int32_t sp = 0, si = 0;
-  for (int b = b0; b < b0 + per && b < nbuckets; ++b) {
-    sp += count[b];
-    si += (count[b] + kItemPairs - 1) / kItemPairs;
-  }
-  s_pairs[t] = sp;
-  s_items[t] = si;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {  // Hillis-Steele inclusive scan
-    const int32_t ap = t >= off ? s_pairs[t - off] : 0;
-    const int32_t ai = t >= off ? s_items[t - off] : 0;
+  constexpr int PASS = 1024 * kScanRun, RP = kScanRun + 1;
+  __shared__ int32_t s_c[1024 * RP], s_i[1024 * RP];
+  __shared__ int32_t s_wp[16], s_wi[16], s_tot[2];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int32_t carry_p = 0, carry_i = 0;
+  for (int base = 0; base < nbuckets; base += PASS) {
+#pragma unroll
+    for (int j = 0; j < kScanRun; ++j) {
+      const int e = j * 1024 + t, b = base + e;  // element e of the pass lives in run e / 16
+      s_c[(e / kScanRun) * RP + e % kScanRun] = b < nbuckets ? count[b] : 0;
+    }
     __syncthreads();
-    s_pairs[t] += ap;
-    s_items[t] += ai;
+    int32_t v[kScanRun], sp = 0, si = 0;
+#pragma unroll
+    for (int j = 0; j < kScanRun; ++j) {
+      v[j] = s_c[t * RP + j];
+      sp += v[j];
+      si += (v[j] + kItemPairs - 1) / kItemPairs;
+    }
+    const int32_t ip = wave_incl_scan(sp, lane), ii = wave_incl_scan(si, lane);
+    if (lane == 63) {
+      s_wp[wave] = ip;
+      s_wi[wave] = ii;
+    }
+    __syncthreads();
+    if (wave == 0) {
+      const int32_t wp = lane < 16 ? s_wp[lane] : 0, wi = lane < 16 ? s_wi[lane] : 0;
+      const int32_t xp = wave_incl_scan(wp, lane), xi = wave_incl_scan(wi, lane);
+      if (lane < 16) {
+        s_wp[lane] = xp - wp;
+        s_wi[lane] = xi - wi;
+      }
+      if (lane == 15) {
+        s_tot[0] = xp;
+        s_tot[1] = xi;
+      }
+    }
+    __syncthreads();
+    int32_t ep = carry_p + s_wp[wave] + ip - sp, ei = carry_i + s_wi[wave] + ii - si;
+#pragma unroll
+    for (int j = 0; j < kScanRun; ++j) {
+      s_c[t * RP + j] = ep;
+      s_i[t * RP + j] = ei;
+      ep += v[j];
+      ei += (v[j] + kItemPairs - 1) / kItemPairs;
+    }
+    carry_p += s_tot[0];
+    carry_i += s_tot[1];
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kScanRun; ++j) {
+      const int e = j * 1024 + t, b = base + e;
+      if (b < nbuckets) {
+        offsets[b] = s_c[(e / kScanRun) * RP + e % kScanRun];
+        items[b] = s_i[(e / kScanRun) * RP + e % kScanRun];
+      }
+    }
     __syncthreads();
   }
-  int32_t rp = s_pairs[t] - sp, ri = s_items[t] - si;  // exclusive
-  for (int b = b0; b < b0 + per && b < nbuckets; ++b) {
-    offsets[b] = rp;
-    items[b] = ri;
-    rp += count[b];
-    ri += (count[b] + kItemPairs - 1) / kItemPairs;
-  }
-  if (t == 1023) {
-    offsets[nbuckets] = s_pairs[1023];
-    items[nbuckets] = s_items[1023];
+  if (t == 0) {
+    offsets[nbuckets] = carry_p;
+    items[nbuckets] = carry_i;
   }
 }
 
@@ -138,7 +196,7 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ items,
     int4* __restrict__ item_rec, int nbuckets, int64_t max_slots, int32_t* __restrict__ list,
-    int64_t row0, int64_t npairs, int n, int topk, int64_t bh0) {
+    int64_t row0, int64_t npairs, int n, int topk, int64_t bh0, int qsegs) {
   const int64_t p = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (p < nbuckets) {
     const int32_t total = items[nbuckets];
@@ -158,7 +216,7 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(
   const int nb = n / kTile;
   const int64_t row = row0 + p / topk;
   const int beta = idx[row * topk + (p % topk)];
-  const int64_t b = (row / n - bh0) * nb + beta;
+  const int64_t b = bucket_of(row, beta, n, nb, qsegs, bh0);
   const int64_t pos = static_cast<int64_t>(offsets[b]) + rk;
   if (pos < npairs) list[pos] = static_cast<int32_t>(p);
 }
@@ -368,7 +426,7 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ list, const int32_t* __restrict__ items,
     const int4* __restrict__ item_rec, int nbuckets, int64_t row0, int64_t npairs, int n,
-    uint64_t div_magic, int div_shift, int64_t bh0, float scale_log2,
+    uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, float scale_log2,
     PartialT<T>* __restrict__ po, float2* __restrict__ pml) {
   using L = KvLayout<T, D>;
   constexpr int GPW = kItemPairs / 16 / 4;  // 16-pair groups per wave
@@ -394,7 +452,7 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
   if (first + cnt > npairs) cnt = first < npairs ? static_cast<int>(npairs - first) : 0;
   const int nb = n / kTile;
   const int beta = b % nb;
-  const int64_t bh = bh0 + b / nb;
+  const int64_t bh = bh0 + b / (nb * qsegs);
 
   int32_t pair[GPW];
   bool live[GPW];
@@ -506,7 +564,7 @@ struct ChunkGeom {
     nb = a.n / kTile;
     bh0 = row0 / a.n;
     const int64_t bh1 = (row0 + rows - 1) / a.n;
-    nbuckets = static_cast<int>((bh1 - bh0 + 1) * nb);
+    nbuckets = static_cast<int>((bh1 - bh0 + 1) * a.qsegs * nb);
     npairs = rows * a.topk;
   }
 };
@@ -527,12 +585,12 @@ hipError_t partial_chunk(const GatherArgs& a, int64_t row0, int64_t rows, hipStr
     hipLaunchKernelGGL((gather_partial_kernel<T, D, true>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets,
-                       row0, c.npairs, a.n, magic, shift, c.bh0, sl2, po, a.ws.partial_ml);
+                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, sl2, po, a.ws.partial_ml);
   else
     hipLaunchKernelGGL((gather_partial_kernel<T, D, false>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets,
-                       row0, c.npairs, a.n, magic, shift, c.bh0, sl2, po, a.ws.partial_ml);
+                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, sl2, po, a.ws.partial_ml);
   return hipGetLastError();
 }
 
@@ -551,6 +609,19 @@ int64_t gather_grid(int64_t rows, int topk, int64_t nbuckets) {
   return (max_items + kXcds - 1) / kXcds * kXcds;
 }
 
+int gather_segments(int n, int d, int topk, bsa_dtype dtype) {
+  if (n % 256 != 0) return 1;
+  const int nb = n / kTile;
+  const int64_t qbytes = static_cast<int64_t>(n) * d * (dtype == BSA_BF16 ? 2 : 4);
+  int qs = 1;
+  // halve the segment while its Q is over 1 MB, its length stays a multiple
+  // of 256 rows, and a (segment, block) bucket still averages >= 256 pairs
+  while (n % (qs * 2 * 256) == 0 && qbytes / qs > (int64_t(1) << 20) &&
+         static_cast<int64_t>(n / (qs * 2)) * topk / nb >= 256)
+    qs *= 2;
+  return qs;
+}
+
 size_t gather_pair_bytes(int d, bsa_dtype dtype) {
   return static_cast<size_t>(d) * (dtype == BSA_BF16 ? 2 : 4) + sizeof(float2);
 }
@@ -559,17 +630,18 @@ hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, 
   const ChunkGeom c(a, row0, rows);
   hipLaunchKernelGGL(zero_i32_kernel, dim3(static_cast<unsigned>((c.nbuckets + 255) / 256)), dim3(256),
                      0, s, a.ws.count, static_cast<int64_t>(c.nbuckets));
-  const int rpw = (a.n % 256 == 0 && row0 % 256 == 0) ? 256 : kTile;
+  const int seg = a.n / a.qsegs;
+  const int rpw = (seg % 256 == 0 && row0 % 256 == 0) ? 256 : kTile;
   hipLaunchKernelGGL(bucket_count_kernel, dim3(static_cast<unsigned>((rows + rpw - 1) / rpw)),
                      dim3(256), static_cast<size_t>(c.nb) * 8, s, a.idx, a.ws.count, a.ws.rank, row0,
-                     rows, a.n, a.topk, a.causal, c.bh0, rpw);
+                     rows, a.n, a.topk, a.causal, c.bh0, rpw, a.qsegs);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, a.ws.count, a.ws.offsets,
                      a.ws.items, c.nbuckets);
   const int64_t nthreads = c.npairs > c.nbuckets ? c.npairs : c.nbuckets;
   hipLaunchKernelGGL(bucket_fill_kernel, dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256),
                      0, s, a.idx, a.ws.rank, a.ws.offsets, a.ws.items, a.ws.item_rec, c.nbuckets,
                      gather_grid(rows, a.topk, c.nbuckets), a.ws.list, row0, c.npairs, a.n, a.topk,
-                     c.bh0);
+                     c.bh0, a.qsegs);
   return hipGetLastError();
 }
 
