@@ -44,7 +44,7 @@
 namespace bsa {
 namespace {
 
-constexpr int kItemPairs = 128;  // pairs per work item (8 groups of 16)
+constexpr int kItemPairs = 256;  // pairs per work item (16 groups of 16)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kXcds = 8;
 
