@@ -79,7 +79,7 @@ struct GatherArgs {
 
 // Query segments per head for the bucketing: the pairs of one (head, key
 // block) are split by query range so that the work items of one segment,
-// which run together, gather query rows from about 1 MB of Q.
+// which run together, gather query rows from at most 2 MB of Q.
 int gather_segments(int n, int d, int topk, bsa_dtype dtype);
 
 size_t gather_pair_bytes(int d, bsa_dtype dtype);  // partial bytes per (query, block) pair

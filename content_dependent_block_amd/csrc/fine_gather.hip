@@ -31,7 +31,7 @@
 //                     partial (m, l, o) out.  Work items are laid out so that
 //                     consecutive items (one head, one query segment,
 //                     neighbouring blocks) land on one XCD, whose L2 then holds
-//                     the segment's query rows (about 1 MB, gather_segments).
+//                     the segment's query rows (at most 2 MB, gather_segments).
 //   combine        -- per query row, merge its partials in slot order.
 // The order of pairs inside a bucket (set by atomics) does not affect any
 // result: every MFMA column is computed independently of the others.
@@ -614,9 +614,12 @@ int gather_segments(int n, int d, int topk, bsa_dtype dtype) {
   const int nb = n / kTile;
   const int64_t qbytes = static_cast<int64_t>(n) * d * (dtype == BSA_BF16 ? 2 : 4);
   int qs = 1;
-  // halve the segment while its Q is over 1 MB, its length stays a multiple
-  // of 256 rows, and a (segment, block) bucket still averages >= 256 pairs
-  while (n % (qs * 2 * 256) == 0 && qbytes / qs > (int64_t(1) << 20) &&
+  // halve the segment while its Q is over 2 MB, its length stays a multiple
+  // of 256 rows, and a (segment, block) bucket still averages >= 256 pairs.
+  // (Measured at N = 32k, d = 64: 4 MB segments fetch 554 MB per launch,
+  // 2 MB 434 MB, 1 MB 451 MB with twice the buckets, 512 KB 792 MB: smaller
+  // segments trade query-row misses for re-reads of the key blocks.)
+  while (n % (qs * 2 * 256) == 0 && qbytes / qs > (int64_t(2) << 20) &&
          static_cast<int64_t>(n / (qs * 2)) * topk / nb >= 256)
     qs *= 2;
   return qs;
