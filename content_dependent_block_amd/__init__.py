@@ -14,7 +14,7 @@ import torch
 
 from ._binding import *  # noqa: F401,F403  (bsa_* functions and constants)
 from ._binding import (EXPORTED, STAGE_NAMES, BsaError, bsa_create, bsa_destroy, bsa_forward,
-                       bsa_forward_static)
+                       bsa_forward_budgets, bsa_forward_static)
 
 
 class BlockSparseAttention:
@@ -41,15 +41,24 @@ class BlockSparseAttention:
         except Exception:
             pass
 
-    def forward(self, q, k, v, *, topk: int, block: int = 64, scale: float | None = None,
+    def forward(self, q, k, v, *, topk, block: int = 64, scale: float | None = None,
                 causal: bool = False, return_indices: bool = False, stream=None):
-        """out (float32, same shape as q), and optionally the int32 block indices."""
+        """out (float32, same shape as q), and optionally the int32 block indices.
+
+        topk: one budget for every head, or a sequence with one per head (the
+        index rows then have max(topk) entries, -1 padded)."""
         b, h, n, d = q.shape
         scale = 1.0 / math.sqrt(d) if scale is None else scale
+        per_head = not isinstance(topk, int)
+        kmax = int(max(topk)) if per_head else topk
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        idx = torch.empty((b, h, n, topk), dtype=torch.int32, device=q.device) if return_indices else None
-        bsa_forward(self.handle, q, k, v, out, idx, block=block, topk=topk, scale=scale,
-                    causal=causal, stream=stream)
+        idx = torch.empty((b, h, n, kmax), dtype=torch.int32, device=q.device) if return_indices else None
+        if per_head:
+            bsa_forward_budgets(self.handle, q, k, v, out, idx, head_topk=list(topk), topk_max=kmax,
+                                block=block, scale=scale, causal=causal, stream=stream)
+        else:
+            bsa_forward(self.handle, q, k, v, out, idx, block=block, topk=topk, scale=scale,
+                        causal=causal, stream=stream)
         return (out, idx) if return_indices else out
 
     def forward_static(self, q, k, v, tile_row_ptr, tile_col, tile_rowmask=None, *,

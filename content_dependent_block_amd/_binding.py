@@ -48,6 +48,7 @@ _sig("bsa_last_error", [_P], ctypes.c_char_p)
 _sig("bsa_set_option", [_P, _I, _I64])
 _sig("bsa_workspace_bytes", [_P, ctypes.POINTER(ctypes.c_size_t)])
 _sig("bsa_forward", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P])
+_sig("bsa_forward_budgets", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _F, _I, _P])
 _sig("bsa_fine_forward", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P])
 _sig("bsa_block_pool", [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P])
 _sig("bsa_coarse_score", [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P])
@@ -60,7 +61,8 @@ _sig("bsa_profile_enable", [_P, _I])
 _sig("bsa_profile_read", [_P, _P, _P, _I])
 
 EXPORTED = ("bsa_create", "bsa_destroy", "bsa_status_string", "bsa_last_error", "bsa_set_option",
-            "bsa_workspace_bytes", "bsa_forward", "bsa_fine_forward", "bsa_block_pool",
+            "bsa_workspace_bytes", "bsa_forward", "bsa_forward_budgets", "bsa_fine_forward",
+            "bsa_block_pool",
             "bsa_coarse_score", "bsa_topk_select", "bsa_forward_static", "bsa_tiles_from_mask",
             "bsa_tiles_window_stride", "bsa_tiles_validate", "bsa_profile_enable",
             "bsa_profile_read")
@@ -159,6 +161,25 @@ def bsa_forward(h, q, k, v, out, block_idx_out=None, *, block: int = 64, topk: i
         pi = _need(block_idx_out, "block_idx_out", (b, hh, n, topk), torch.int32, dev)
     _check(_lib.bsa_forward(h, pq, pk, pv, po, pi, b, hh, n, d, _dtype_code(q), block, topk,
                             float(scale), int(causal), _stream(stream, dev)), h)
+
+
+def bsa_forward_budgets(h, q, k, v, out, block_idx_out=None, *, head_topk, topk_max: int = None,
+                        block: int = 64, scale: float, causal: bool = False, stream=None) -> None:
+    """bsa_forward with one top-k budget per head (head_topk: ints, one per head)."""
+    pq, pk, pv, dev = _qkv(q, k, v)
+    b, hh, n, d = q.shape
+    ks = np.ascontiguousarray(np.asarray(head_topk, dtype=np.int32).reshape(-1))
+    if ks.size != hh:
+        raise ValueError(f"head_topk needs {hh} entries, got {ks.size}")
+    if topk_max is None:
+        topk_max = int(ks.max())
+    po = _need(out, "out", q.shape, torch.float32, dev)
+    pi = None
+    if block_idx_out is not None:
+        pi = _need(block_idx_out, "block_idx_out", (b, hh, n, topk_max), torch.int32, dev)
+    _check(_lib.bsa_forward_budgets(h, pq, pk, pv, po, pi, b, hh, n, d, _dtype_code(q), block,
+                                    ks.ctypes.data, int(topk_max), float(scale), int(causal),
+                                    _stream(stream, dev)), h)
 
 
 def bsa_fine_forward(h, q, k, v, out, block_idx, *, block: int = 64, scale: float,

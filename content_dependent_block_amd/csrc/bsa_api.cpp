@@ -290,17 +290,24 @@ bool fused_select(bsa_handle h, int topk) {
   return h->select_strategy == BSA_SELECT_FUSED && topk <= bsa::kFusedSelectMaxK;
 }
 
+bsa::HeadBudget uniform_budget(int topk) {
+  bsa::HeadBudget hb;
+  hb.heads = 1;
+  hb.k[0] = topk;
+  return hb;
+}
+
 // Stage 1 selection over all rows: one fused coarse_score + topk_select
 // kernel (k <= 32, fused strategy), else coarse_score and topk_select through
 // a panel, in chunks of at most panel_chunk_bytes of panel.
 bsa_status run_select(bsa_handle h, const void* q, const float* repr, const uint16_t* split,
-                      int32_t* idx, const Shape& s, bsa_dtype dt, int topk, int causal,
-                      hipStream_t st) {
+                      int32_t* idx, const Shape& s, bsa_dtype dt, int topk,
+                      const bsa::HeadBudget& hb, int causal, hipStream_t st) {
   const int64_t nb = s.n / 64;
   const int64_t total = s.bh() * s.n;
   if (fused_select(h, topk))
     return timed_launch(h, BSA_STAGE_COARSE_TOPK, st, "coarse_select", [&] {
-      return bsa::launch_coarse_select(q, repr, split, idx, total, s.n, s.d, dt, topk, causal, st);
+      return bsa::launch_coarse_select(q, repr, split, idx, total, s.n, s.d, dt, topk, hb, causal, st);
     });
   int64_t chunk = h->panel_chunk_bytes / (nb * 4) / 64 * 64;
   if (chunk < 64) chunk = 64;
@@ -313,7 +320,7 @@ bsa_status run_select(bsa_handle h, const void* q, const float* repr, const uint
       return bsa::launch_coarse_score(q, repr, h->panel, r0, rows, s.n, s.d, dt, causal, st);
     }));
     TRY(timed_launch(h, BSA_STAGE_TOPK, st, "topk_select", [&] {
-      return bsa::launch_topk_select(h->panel, idx, r0, rows, s.n, topk, causal, st);
+      return bsa::launch_topk_select(h->panel, idx, r0, rows, s.n, topk, hb, causal, st);
     }));
   }
   return BSA_OK;
@@ -420,7 +427,8 @@ BSA_API bsa_status bsa_topk_select(bsa_handle h, const float* panel, int32_t* bl
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
   return timed_launch(h, BSA_STAGE_TOPK, st, "topk_select", [&] {
-    return bsa::launch_topk_select(panel, block_idx_out, 0, s.bh() * s.n, s.n, topk, causal, st);
+    return bsa::launch_topk_select(panel, block_idx_out, 0, s.bh() * s.n, s.n, topk,
+                                   uniform_budget(topk), causal, st);
   });
 }
 
@@ -446,15 +454,12 @@ BSA_API bsa_status bsa_fine_forward(bsa_handle h, const void* q, const void* k, 
                   static_cast<hipStream_t>(stream));
 }
 
-BSA_API bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const void* v,
-                               float* out, int32_t* block_idx_out, int batch, int heads, int n,
-                               int d, bsa_dtype dtype, int block, int topk, float scale,
-                               int causal, void* stream) {
-  const char* fn = "bsa_forward";
-  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
-  const Shape s{batch, heads, n, d};
-  TRY(check_shape(h, fn, s, dtype, block));
-  TRY(check_dynamic(h, fn, s, topk, causal));
+namespace {
+// bsa_forward and bsa_forward_budgets after their own argument checks;
+// topk = index row length (the largest budget).
+bsa_status forward_impl(bsa_handle h, const char* fn, const void* q, const void* k, const void* v,
+                        float* out, int32_t* block_idx_out, const Shape& s, bsa_dtype dtype,
+                        int topk, const bsa::HeadBudget& hb, float scale, int causal, void* stream) {
   TRY(check_scale(h, fn, scale));
   TRY(check_ptr(h, fn, "q", q));
   TRY(check_ptr(h, fn, "k", k));
@@ -482,8 +487,48 @@ BSA_API bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const
     idx = h->idx;
   }
   TRY(run_pool(h, k, repr, split, s, dtype, st));
-  TRY(run_select(h, q, repr, split, idx, s, dtype, topk, causal, st));
+  TRY(run_select(h, q, repr, split, idx, s, dtype, topk, hb, causal, st));
   return run_fine(h, q, k, v, out, idx, s, dtype, topk, scale, causal, st);
+}
+}  // namespace
+
+BSA_API bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const void* v,
+                               float* out, int32_t* block_idx_out, int batch, int heads, int n,
+                               int d, bsa_dtype dtype, int block, int topk, float scale,
+                               int causal, void* stream) {
+  const char* fn = "bsa_forward";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const Shape s{batch, heads, n, d};
+  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_dynamic(h, fn, s, topk, causal));
+  return forward_impl(h, fn, q, k, v, out, block_idx_out, s, dtype, topk, uniform_budget(topk), scale,
+                      causal, stream);
+}
+
+BSA_API bsa_status bsa_forward_budgets(bsa_handle h, const void* q, const void* k, const void* v,
+                                       float* out, int32_t* block_idx_out, int batch, int heads,
+                                       int n, int d, bsa_dtype dtype, int block,
+                                       const int32_t* head_topk, int topk_max, float scale,
+                                       int causal, void* stream) {
+  const char* fn = "bsa_forward_budgets";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const Shape s{batch, heads, n, d};
+  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_dynamic(h, fn, s, topk_max, causal));
+  if (!head_topk) return fail(h, BSA_ERR_INVALID_ARG, "%s: head_topk is NULL", fn);
+  if (heads > bsa::kMaxBudgetHeads)
+    return fail(h, BSA_ERR_UNSUPPORTED, "%s: at most %d heads with per-head budgets (got %d)", fn,
+                bsa::kMaxBudgetHeads, heads);
+  bsa::HeadBudget hb;
+  hb.heads = heads;
+  for (int i = 0; i < heads; ++i) {
+    if (head_topk[i] < 1 || head_topk[i] > topk_max)
+      return fail(h, BSA_ERR_INVALID_ARG, "%s: head_topk[%d] = %d is outside [1, topk_max = %d]", fn, i,
+                  head_topk[i], topk_max);
+    hb.k[i] = head_topk[i];
+  }
+  return forward_impl(h, fn, q, k, v, out, block_idx_out, s, dtype, topk_max, hb, scale, causal,
+                      stream);
 }
 
 BSA_API bsa_status bsa_forward_static(bsa_handle h, const void* q, const void* k, const void* v,

@@ -24,18 +24,27 @@ hipError_t launch_coarse_score(const void* q, const float* repr, float* panel, i
                                int64_t rows, int n, int d, bsa_dtype dtype, int causal,
                                hipStream_t stream);
 
+// Selection budgets: the query rows of (batch, head) bh keep
+// k[bh % heads] blocks; a uniform budget is heads = 1.  Passed by value as a
+// kernel argument.  Index rows have `topk` (>= every k) entries, -1 padded.
+constexpr int kMaxBudgetHeads = 256;
+struct HeadBudget {
+  int heads;
+  int32_t k[kMaxBudgetHeads];
+};
+
 // coarse_score and topk_select in one kernel (topk <= 32) over all `rows`
 // query rows: idx[row * topk + t], no panel.  Representatives: for bf16
 // inputs the split form from block_pool (repr_split), for fp32 inputs the
 // float32 repr.
 hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t* repr_split,
                                 int32_t* idx, int64_t rows, int n, int d, bsa_dtype dtype,
-                                int topk, int causal, hipStream_t stream);
+                                int topk, const HeadBudget& budget, int causal, hipStream_t stream);
 constexpr int kFusedSelectMaxK = 32;
 
 // topk_select over panel rows [row0, row0 + rows): idx[(row0 + r) * topk + t].
 hipError_t launch_topk_select(const float* panel, int32_t* idx, int64_t row0, int64_t rows, int n,
-                              int topk, int causal, hipStream_t stream);
+                              int topk, const HeadBudget& budget, int causal, hipStream_t stream);
 
 // sparse_flash_fwd, dynamic: per 64-query tile the union of its rows'
 // selected blocks, each row masked to its own selection.

@@ -575,7 +575,8 @@ template <typename TL, int KL, int GM, int CAP, int MINW>
 __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename TL::QT* __restrict__ q,
                                                                   const typename TL::Src* __restrict__ rsrc,
                                                                   int32_t* __restrict__ idx, int n,
-                                                                  int topk, int causal) {
+                                                                  int topk, const HeadBudget budget,
+                                                                  int causal) {
   constexpr int MT = TL::TB / 16;     // MFMA tiles per R tile
   constexpr int NS = 16 * GM;         // group slots per lane
   constexpr int NH = NS / (4 * MT);   // R tiles per cycle of slots
@@ -590,7 +591,8 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
   TL sc;
   sc.load_q(q, ti.qrow, ti.g);
   const auto* rbase = TL::head_base(rsrc, ti.bh, ti.nb);
-  const int keff = topk < ti.nvalid ? topk : ti.nvalid;
+  const int kh = budget.k[ti.bh % budget.heads];  // this head's budget (<= topk <= KL)
+  const int keff = kh < ti.nvalid ? kh : ti.nvalid;
 
   // pass 1: group maxima.  The lane's block 16 (MT bt + mt) + 4 g + j goes to
   // slot 4 ((MT bt + mt) mod 4 GM) + j: G = 64 GM groups over the 4 lanes.
@@ -730,18 +732,18 @@ void launch_panel(const void* q, const void* rsrc, float* panel, int64_t row0, i
 
 template <typename TL, int KL, int GM, int CAP, int MINW>
 void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
-                   int causal, hipStream_t s) {
+                   const HeadBudget& hb, int causal, hipStream_t s) {
   hipLaunchKernelGGL((coarse_select_kernel<TL, KL, GM, CAP, MINW>), dim3(static_cast<unsigned>(rows / kTile)),
                      dim3(256), 0, s, static_cast<const typename TL::QT*>(q),
-                     static_cast<const typename TL::Src*>(rsrc), idx, n, topk, causal);
+                     static_cast<const typename TL::Src*>(rsrc), idx, n, topk, hb, causal);
 }
 
 template <typename TL>
 void launch_select_k(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
-                     int causal, hipStream_t s) {
-  if (topk <= 8) launch_select<TL, 8, 1, 8, 4>(q, rsrc, idx, rows, n, topk, causal, s);
-  else if (topk <= 16) launch_select<TL, 16, 1, 16, 4>(q, rsrc, idx, rows, n, topk, causal, s);
-  else launch_select<TL, 32, 2, 32, 2>(q, rsrc, idx, rows, n, topk, causal, s);
+                     const HeadBudget& hb, int causal, hipStream_t s) {
+  if (topk <= 8) launch_select<TL, 8, 1, 8, 4>(q, rsrc, idx, rows, n, topk, hb, causal, s);
+  else if (topk <= 16) launch_select<TL, 16, 1, 16, 4>(q, rsrc, idx, rows, n, topk, hb, causal, s);
+  else launch_select<TL, 32, 2, 32, 2>(q, rsrc, idx, rows, n, topk, hb, causal, s);
 }
 
 }  // namespace
@@ -761,13 +763,13 @@ hipError_t launch_coarse_score(const void* q, const float* repr, float* panel, i
 
 hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t* repr_split,
                                 int32_t* idx, int64_t rows, int n, int d, bsa_dtype dtype,
-                                int topk, int causal, hipStream_t stream) {
+                                int topk, const HeadBudget& hb, int causal, hipStream_t stream) {
   if (dtype == BSA_BF16) {
-    if (d == 64) launch_select_k<Bf16PlaneTiles<64>>(q, repr_split, idx, rows, n, topk, causal, stream);
-    else launch_select_k<Bf16PlaneTiles<128>>(q, repr_split, idx, rows, n, topk, causal, stream);
+    if (d == 64) launch_select_k<Bf16PlaneTiles<64>>(q, repr_split, idx, rows, n, topk, hb, causal, stream);
+    else launch_select_k<Bf16PlaneTiles<128>>(q, repr_split, idx, rows, n, topk, hb, causal, stream);
   } else {
-    if (d == 64) launch_select_k<F32Tiles<64, 32>>(q, repr, idx, rows, n, topk, causal, stream);
-    else launch_select_k<F32Tiles<128, 32>>(q, repr, idx, rows, n, topk, causal, stream);
+    if (d == 64) launch_select_k<F32Tiles<64, 32>>(q, repr, idx, rows, n, topk, hb, causal, stream);
+    else launch_select_k<F32Tiles<128, 32>>(q, repr, idx, rows, n, topk, hb, causal, stream);
   }
   return hipGetLastError();
 }

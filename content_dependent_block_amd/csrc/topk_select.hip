@@ -8,7 +8,10 @@
 //
 // Semantics: candidates are all n/64 blocks, or in the causal variant the
 // blocks up to the query's own block, which is always kept.  k_eff =
-// min(k, #candidates).  Equal scores go to the lower block index and -0 equals
+// min(k, #candidates), where k is the head's budget (one k for all heads
+// unless per-head budgets are given; nishantmodi.me
+// "sparse-attention-triton-bench", section "What's next": per-head sparsity
+// budgets).  Equal scores go to the lower block index and -0 equals
 // +0.  Output: the k_eff indices in ascending order, then -1 up to k.
 //
 // Input: the panel of a chunk of query rows, block-major (panel[beta][row]).
@@ -36,14 +39,16 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 template <int KL>
 __global__ __launch_bounds__(64) void topk_lane_kernel(const float* __restrict__ panel,
                                                        int32_t* __restrict__ idx, int64_t row0,
-                                                       int64_t prows, int n, int topk, int causal) {
+                                                       int64_t prows, int n, int topk,
+                                                       const HeadBudget budget, int causal) {
   const int lane = threadIdx.x;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 64 + lane;  // prows % 64 == 0
   const int nb = n / kTile;
   const int64_t grow = row0 + r;
   const int qb = static_cast<int>(grow % n) / kTile;  // the same in all 64 rows
   const int nvalid = causal ? qb + 1 : nb;
-  const int keff = topk < nvalid ? topk : nvalid;
+  const int kh = budget.k[(grow / n) % budget.heads];  // the same in all 64 rows
+  const int keff = kh < nvalid ? kh : nvalid;
   const float* col = panel + r;
   const int forced = causal ? qb : -1;
 
@@ -91,7 +96,8 @@ __device__ __forceinline__ uint32_t radix_kth(const uint32_t (&key)[NV], int k, 
 template <int NPER>
 __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ panel,
                                                         int32_t* __restrict__ idx, int64_t row0,
-                                                        int64_t prows, int n, int topk, int causal) {
+                                                        int64_t prows, int n, int topk,
+                                                        const HeadBudget budget, int causal) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nb = n / kTile;
   for (int rr = 0; rr < 16; ++rr) {
@@ -99,7 +105,8 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
     const int64_t grow = row0 + r;
     const int qb = static_cast<int>(grow % n) / kTile;
     const int nvalid = causal ? qb + 1 : nb;
-    const int keff = topk < nvalid ? topk : nvalid;
+    const int kh = budget.k[(grow / n) % budget.heads];
+    const int keff = kh < nvalid ? kh : nvalid;
     int32_t* dst = idx + grow * topk;
     uint32_t key[NPER];
 #pragma unroll
@@ -135,30 +142,30 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
 
 template <int NPER>
 void launch_wave(const float* panel, int32_t* idx, int64_t row0, int64_t rows, int n, int topk,
-                 int causal, hipStream_t s) {
+                 const HeadBudget& hb, int causal, hipStream_t s) {
   hipLaunchKernelGGL((topk_wave_kernel<NPER>), dim3(static_cast<unsigned>(rows / 64)), dim3(256), 0, s,
-                     panel, idx, row0, rows, n, topk, causal);
+                     panel, idx, row0, rows, n, topk, hb, causal);
 }
 
 }  // namespace
 
 hipError_t launch_topk_select(const float* panel, int32_t* idx, int64_t row0, int64_t rows, int n,
-                              int topk, int causal, hipStream_t s) {
+                              int topk, const HeadBudget& hb, int causal, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(rows / 64));
   if (topk <= 8) {
-    hipLaunchKernelGGL((topk_lane_kernel<8>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, causal);
+    hipLaunchKernelGGL((topk_lane_kernel<8>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, hb, causal);
   } else if (topk <= 16) {
-    hipLaunchKernelGGL((topk_lane_kernel<16>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, causal);
+    hipLaunchKernelGGL((topk_lane_kernel<16>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, hb, causal);
   } else if (topk <= 32) {
-    hipLaunchKernelGGL((topk_lane_kernel<32>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, causal);
+    hipLaunchKernelGGL((topk_lane_kernel<32>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, hb, causal);
   } else {
     const int nb = n / kTile;
-    if (nb <= 64) launch_wave<1>(panel, idx, row0, rows, n, topk, causal, s);
-    else if (nb <= 128) launch_wave<2>(panel, idx, row0, rows, n, topk, causal, s);
-    else if (nb <= 256) launch_wave<4>(panel, idx, row0, rows, n, topk, causal, s);
-    else if (nb <= 512) launch_wave<8>(panel, idx, row0, rows, n, topk, causal, s);
-    else if (nb <= 1024) launch_wave<16>(panel, idx, row0, rows, n, topk, causal, s);
-    else launch_wave<32>(panel, idx, row0, rows, n, topk, causal, s);
+    if (nb <= 64) launch_wave<1>(panel, idx, row0, rows, n, topk, hb, causal, s);
+    else if (nb <= 128) launch_wave<2>(panel, idx, row0, rows, n, topk, hb, causal, s);
+    else if (nb <= 256) launch_wave<4>(panel, idx, row0, rows, n, topk, hb, causal, s);
+    else if (nb <= 512) launch_wave<8>(panel, idx, row0, rows, n, topk, hb, causal, s);
+    else if (nb <= 1024) launch_wave<16>(panel, idx, row0, rows, n, topk, hb, causal, s);
+    else launch_wave<32>(panel, idx, row0, rows, n, topk, hb, causal, s);
   }
   return hipGetLastError();
 }

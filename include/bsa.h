@@ -159,6 +159,26 @@ bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const void* v
                        int n, int d, bsa_dtype dtype, int block, int topk,
                        float scale, int causal, void* stream);
 
+/* Like bsa_forward with a top-k budget per head (nishantmodi.me
+ * "sparse-attention-triton-bench", section "What's next": each head keeps
+ * its own number of blocks, chosen at run time).
+ *  head_topk      host, int32 [heads]: head h of every batch keeps
+ *                 k_eff = min(head_topk[h], #candidate blocks) blocks;
+ *                 1 <= head_topk[h] <= topk_max, else BSA_ERR_INVALID_ARG.
+ *                 Read during the call only.
+ *  topk_max       row length of block_idx_out: int32
+ *                 [batch][heads][n][topk_max], each row's k_eff indices in
+ *                 ascending order, then -1.
+ *  heads          at most 256 (BSA_ERR_UNSUPPORTED above).
+ * Everything else as for bsa_forward; with every head_topk[h] = topk_max
+ * the result equals bsa_forward's with topk = topk_max. */
+bsa_status bsa_forward_budgets(bsa_handle h, const void* q, const void* k,
+                               const void* v, float* out, int32_t* block_idx_out,
+                               int batch, int heads, int n, int d,
+                               bsa_dtype dtype, int block,
+                               const int32_t* head_topk, int topk_max,
+                               float scale, int causal, void* stream);
+
 /* Stage 2 alone on caller-supplied selections (same layout as block_idx_out;
  * each row must hold distinct indices; entries outside [0, n/block), and in
  * causal mode blocks after the query's own block, count as padding).  Useful
