@@ -53,8 +53,10 @@ def _load():
     lib.oracle_attend_mask.argtypes = [P, P, P, I, I, I, ctypes.c_double, P, P, I, P]
     lib.oracle_visible_pairs.argtypes = [P, P, I, I, I, I, ctypes.c_int]
     lib.oracle_visible_pairs.restype = ctypes.c_int64
+    lib.oracle_attend_backward.argtypes = [P, P, P, P, I, I, I, I, I, ctypes.c_int, ctypes.c_double,
+                                           P, P, I, P, P, P, I, P, P]
     for name in ("oracle_pool", "oracle_scores", "oracle_topk", "oracle_attend",
-                 "oracle_window_stride_mask", "oracle_attend_mask"):
+                 "oracle_window_stride_mask", "oracle_attend_mask", "oracle_attend_backward"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -173,6 +175,35 @@ def window_stride_mask(n, window, stride):
     m = np.empty((n, n), dtype=np.uint8)
     _check(lib.oracle_window_stride_mask(n, window, stride, _ptr(m)), "oracle_window_stride_mask")
     return m
+
+
+def attend_backward(q, k, v, dout, idx, block, causal, scale, rows=None, key_blocks=None):
+    """Gradients of the fine attention with the selection idx held fixed.
+
+    idx: int32 selections of ALL bh*n rows ([bh*n, topk], -1 padded).
+    rows: query rows for dq and lse (default all); key_blocks: flattened
+    (head * nb + beta) ids for dk and dv (default all).
+    Returns (dq [rows, d], lse [rows], dk [blocks, block, d], dv [same]), fp64."""
+    lib = _load()
+    bh, n, d = _shape(q)
+    nb = -(-n // block)
+    q, qp = _f32(q)
+    k, kp = _f32(k)
+    v, vp = _f32(v)
+    dout, dp = _f32(dout)
+    rows = _rows(rows, bh * n)
+    kb = np.arange(bh * nb, dtype=np.int64) if key_blocks is None else \
+        np.ascontiguousarray(key_blocks, dtype=np.int64)
+    idx = np.ascontiguousarray(idx, dtype=np.int32).reshape(bh * n, -1)
+    dq = np.empty((rows.size, d), dtype=np.float64)
+    lse = np.empty(rows.size, dtype=np.float64)
+    dk = np.empty((kb.size, block, d), dtype=np.float64)
+    dv = np.empty((kb.size, block, d), dtype=np.float64)
+    _check(lib.oracle_attend_backward(qp, kp, vp, dp, bh, n, d, block, idx.shape[1], int(causal),
+                                      float(scale), _ptr(idx), _ptr(rows), rows.size, _ptr(dq),
+                                      _ptr(lse), _ptr(kb), kb.size, _ptr(dk), _ptr(dv)),
+           "oracle_attend_backward")
+    return dq, lse, dk, dv
 
 
 def attend_mask(q, k, v, mask, scale, rows=None):

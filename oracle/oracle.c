@@ -326,3 +326,203 @@ ORACLE_EXPORT int64_t oracle_visible_pairs(const int32_t* idx,
   }
   return total;
 }
+
+/* ------------------------------------------------------------------------
+ * Backward of the fine stage [P1 "What's next": a backward pass that
+ * differentiates through the softmax-weighted sum over the selected blocks,
+ * with FlashAttention-2's backward as the dense model].
+ *
+ * Reading R7: the selection is a discrete choice and carries no gradient; it
+ * is held fixed (the idx the forward used), so the gradients are those of
+ * softmax attention over each row's visible key set J(i).  With
+ * z_ij = scale * q_i.k_j, p_ij = softmax_j(z_ij) over J(i) and an incoming
+ * gradient dO_i of o_i = sum_j p_ij v_j:
+ *   dp_ij = dO_i . v_j
+ *   ds_ij = p_ij (dp_ij - sum_l p_il dp_il)      (softmax Jacobian)
+ *   dq_i  = scale * sum_j ds_ij k_j
+ *   dk_j  = scale * sum_{i : j in J(i)} ds_ij q_i
+ *   dv_j  = sum_{i : j in J(i)} p_ij dO_i
+ * and lse_i = log sum_{j in J(i)} exp(z_ij) (natural log, scale included).
+ * ------------------------------------------------------------------------ */
+
+/* Visible keys of row i of one head: the keys of its selected blocks
+ * (entries < 0 are padding), j <= i if causal (R4).  Returns the count. */
+static int64_t row_keys(const int32_t* sel, int64_t topk, int64_t i, int64_t n,
+                        int64_t B, int causal, int64_t* keys) {
+  int64_t nk = 0;
+  for (int64_t t = 0; t < topk; ++t) {
+    const int64_t beta = sel[t];
+    if (beta < 0) continue;
+    for (int64_t j = beta * B; j < beta * B + B && j < n; ++j) {
+      if (causal && j > i) continue;
+      keys[nk++] = j;
+    }
+  }
+  return nk;
+}
+
+/* Softmax of one row over its key list: p[t] for keys[t], the row's lse,
+ * and delta = sum_t p[t] (dO . v_keys[t]).  An empty list gives lse = -inf,
+ * delta = 0 (R6). */
+static void row_softmax(const float* qi, const float* dOi, const float* kh,
+                        const float* vh, int64_t d, double scale,
+                        const int64_t* keys, int64_t nk, double* p,
+                        double* lse, double* delta) {
+  *lse = -INFINITY;
+  *delta = 0.0;
+  if (nk == 0) return;
+  double zmax = -INFINITY;
+  for (int64_t t = 0; t < nk; ++t) {
+    const float* kj = kh + keys[t] * d;
+    double s = 0.0;
+    for (int64_t c = 0; c < d; ++c) s += (double)qi[c] * (double)kj[c];
+    p[t] = scale * s;
+    if (p[t] > zmax) zmax = p[t];
+  }
+  double den = 0.0;
+  for (int64_t t = 0; t < nk; ++t) {
+    p[t] = exp(p[t] - zmax);
+    den += p[t];
+  }
+  for (int64_t t = 0; t < nk; ++t) p[t] /= den;
+  *lse = zmax + log(den);
+  double dl = 0.0;
+  for (int64_t t = 0; t < nk; ++t) {
+    const float* vj = vh + keys[t] * d;
+    double dp = 0.0;
+    for (int64_t c = 0; c < d; ++c) dp += (double)dOi[c] * (double)vj[c];
+    dl += p[t] * dp;
+  }
+  *delta = dl;
+}
+
+/* Gradients for the requested query rows (dq, lse) and the requested key
+ * blocks (dk, dv: kblocks[b] = head * nb + beta, rows of the block past n are
+ * zero).  idx holds the selections of ALL bh*n rows ([bh*n][topk]): a key's
+ * gradient sums over every row that sees it. */
+ORACLE_EXPORT int oracle_attend_backward(
+    const float* q, const float* k, const float* v, const float* dout,
+    int64_t bh, int64_t n, int64_t d, int64_t B, int64_t topk, int causal,
+    double scale, const int32_t* idx, const int64_t* rows, int64_t nrows,
+    double* dq, double* lse, const int64_t* kblocks, int64_t nkb, double* dk,
+    double* dv) {
+  if (!q || !k || !v || !dout || !idx || bh < 1 || n < 1 || d < 1 || B < 1 ||
+      topk < 1 || (nrows > 0 && (!rows || !dq || !lse)) ||
+      (nkb > 0 && (!kblocks || !dk || !dv)))
+    return -1;
+  const int64_t nb = ceil_div(n, B);
+  for (int64_t r = 0; r < bh * n * topk; ++r)
+    if (idx[r] >= nb) return -2;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (rows[r] < 0 || rows[r] >= bh * n) return -2;
+  for (int64_t b = 0; b < nkb; ++b)
+    if (kblocks[b] < 0 || kblocks[b] >= bh * nb) return -2;
+  int bad = 0;
+
+  /* dq and lse, one row at a time. */
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+  for (int64_t r = 0; r < nrows; ++r) {
+    const int64_t row = rows[r], h = row / n, i = row % n;
+    const float* kh = k + h * n * d;
+    const float* vh = v + h * n * d;
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)(topk * B));
+    double* p = (double*)malloc(sizeof(double) * (size_t)(topk * B));
+    if (!keys || !p) {
+      bad = 1;
+      free(keys);
+      free(p);
+      continue;
+    }
+    const int64_t nk = row_keys(idx + row * topk, topk, i, n, B, causal, keys);
+    double delta;
+    row_softmax(q + row * d, dout + row * d, kh, vh, d, scale, keys, nk, p,
+                &lse[r], &delta);
+    double* g = dq + r * d;
+    for (int64_t c = 0; c < d; ++c) g[c] = 0.0;
+    for (int64_t t = 0; t < nk; ++t) {
+      const float* vj = vh + keys[t] * d;
+      const float* kj = kh + keys[t] * d;
+      double dp = 0.0;
+      for (int64_t c = 0; c < d; ++c) dp += (double)dout[row * d + c] * (double)vj[c];
+      const double ds = p[t] * (dp - delta);
+      for (int64_t c = 0; c < d; ++c) g[c] += scale * ds * (double)kj[c];
+    }
+    free(keys);
+    free(p);
+  }
+  if (bad) return -3;
+
+  /* dk and dv.  First lse_i and delta_i of every row that selects one of
+   * the requested blocks (each over its whole key list); then, one requested
+   * block at a time, the sum over the rows of its head in ascending order,
+   * with p_ij = exp(z_ij - lse_i). */
+  if (nkb == 0) return 0;
+  char* want = (char*)calloc((size_t)(bh * n), 1);
+  double* rl = (double*)malloc(sizeof(double) * (size_t)(bh * n));
+  double* rd = (double*)malloc(sizeof(double) * (size_t)(bh * n));
+  if (!want || !rl || !rd) {
+    free(want);
+    free(rl);
+    free(rd);
+    return -3;
+  }
+  for (int64_t b = 0; b < nkb; ++b) {
+    const int64_t h = kblocks[b] / nb, beta = kblocks[b] % nb;
+    for (int64_t i = 0; i < n; ++i)
+      for (int64_t t = 0; t < topk; ++t)
+        if (idx[(h * n + i) * topk + t] == beta) want[h * n + i] = 1;
+  }
+#pragma omp parallel for schedule(dynamic, 16) reduction(| : bad)
+  for (int64_t row = 0; row < bh * n; ++row) {
+    if (!want[row]) continue;
+    const int64_t h = row / n, i = row % n;
+    int64_t* keys = (int64_t*)malloc(sizeof(int64_t) * (size_t)(topk * B));
+    double* p = (double*)malloc(sizeof(double) * (size_t)(topk * B));
+    if (!keys || !p) {
+      bad = 1;
+      free(keys);
+      free(p);
+      continue;
+    }
+    const int64_t nk = row_keys(idx + row * topk, topk, i, n, B, causal, keys);
+    row_softmax(q + row * d, dout + row * d, k + h * n * d, v + h * n * d, d,
+                scale, keys, nk, p, &rl[row], &rd[row]);
+    free(keys);
+    free(p);
+  }
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t b = 0; b < nkb; ++b) {
+    const int64_t h = kblocks[b] / nb, beta = kblocks[b] % nb;
+    const float* kh = k + h * n * d;
+    const float* vh = v + h * n * d;
+    double* gk = dk + b * B * d;
+    double* gv = dv + b * B * d;
+    for (int64_t e = 0; e < B * d; ++e) gk[e] = gv[e] = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t row = h * n + i;
+      int64_t hits = 0;
+      for (int64_t t = 0; t < topk; ++t) hits += idx[row * topk + t] == beta;
+      for (int64_t j = beta * B; j < beta * B + B && j < n; ++j) {
+        if (hits == 0 || (causal && j > i)) continue;
+        const float* kj = kh + j * d;
+        const float* vj = vh + j * d;
+        double s = 0.0, dp = 0.0;
+        for (int64_t c = 0; c < d; ++c) {
+          s += (double)q[row * d + c] * (double)kj[c];
+          dp += (double)dout[row * d + c] * (double)vj[c];
+        }
+        const double pij = exp(scale * s - rl[row]);
+        const double ds = pij * (dp - rd[row]);
+        /* a block listed twice in a row is two copies of its keys in J(i) */
+        for (int64_t c = 0; c < d; ++c) {
+          gk[(j - beta * B) * d + c] += (double)hits * scale * ds * (double)q[row * d + c];
+          gv[(j - beta * B) * d + c] += (double)hits * pij * (double)dout[row * d + c];
+        }
+      }
+    }
+  }
+  free(want);
+  free(rl);
+  free(rd);
+  return bad ? -3 : 0;
+}

@@ -309,3 +309,128 @@ def test_flop_counts_reproduce_the_page():
     assert round(100 * sparse_page / dense_page, 1) == g["sparse_fraction_printed_percent"]
     assert sparse_mm == pytest.approx(85.899e9, rel=1e-4)
     assert dense_mm == pytest.approx(2.199e12, rel=1e-3)
+
+
+# ---------------------------------------------------------------- backward --
+# oracle.attend_backward follows nishantmodi.me "sparse-attention-triton-bench",
+# section "What's next" (a backward pass through the softmax-weighted sum over
+# the selected blocks, FlashAttention-2's backward as the dense model), with
+# the selection held fixed.
+
+def _torch_dense_grads(q, k, v, dout, scale, causal):
+    """Autograd of textbook attention in fp64 (torch CPU), per head [n, d]."""
+    torch = pytest.importorskip("torch")
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    z = tq @ tk.transpose(-1, -2) * scale
+    if causal:
+        n = q.shape[-2]
+        z = z.masked_fill(torch.triu(torch.ones(n, n, dtype=torch.bool), 1), float("-inf"))
+    lse = torch.logsumexp(z, dim=-1)
+    o = torch.softmax(z, dim=-1) @ tv
+    o.backward(torch.tensor(dout, dtype=torch.float64))
+    return tq.grad.numpy(), tk.grad.numpy(), tv.grad.numpy(), lse.detach().numpy()
+
+
+def _all_blocks_idx(bh, n, block, topk):
+    nb = -(-n // block)
+    idx = np.full((bh * n, topk), -1, np.int32)
+    idx[:, :nb] = np.arange(nb, dtype=np.int32)
+    return idx
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_equals_dense_autograd_when_every_block_is_kept(causal):
+    """Every block selected (k*B >= n): the gradients are those of dense
+    (causal) attention, computed here by torch autograd in fp64."""
+    rng = np.random.default_rng(11)
+    bh, n, d, block, scale = 2, 256, 32, 64, 0.2
+    q, k, v, dout = (rng.standard_normal((bh, n, d)).astype(np.float32) for _ in range(4))
+    idx = _all_blocks_idx(bh, n, block, 5)          # 4 blocks + one -1 pad
+    dq, lse, dk, dv = oracle.attend_backward(q, k, v, dout, idx, block, causal, scale)
+    for h in range(bh):
+        gq, gk, gv, gl = _torch_dense_grads(q[h], k[h], v[h], dout[h], scale, causal)
+        np.testing.assert_allclose(dq[h * n:(h + 1) * n], gq, rtol=0, atol=1e-11)
+        np.testing.assert_allclose(lse[h * n:(h + 1) * n], gl, rtol=0, atol=1e-11)
+        np.testing.assert_allclose(dk[h * 4:(h + 1) * 4].reshape(n, d), gk, rtol=0, atol=1e-11)
+        np.testing.assert_allclose(dv[h * 4:(h + 1) * 4].reshape(n, d), gv, rtol=0, atol=1e-11)
+
+
+def _random_selection(rng, bh, n, block, topk, causal):
+    nb = -(-n // block)
+    idx = np.full((bh * n, topk), -1, np.int32)
+    for r in range(bh * n):
+        qb = (r % n) // block
+        cand = np.arange(qb + 1) if causal else np.arange(nb)
+        kk = rng.integers(1, topk + 1)                 # some rows padded with -1
+        sel = rng.choice(cand, size=min(kk, cand.size), replace=False)
+        if causal and qb not in sel:
+            sel[0] = qb
+        idx[r, :sel.size] = np.sort(sel)
+    return idx
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_matches_finite_differences_of_the_forward(causal):
+    """Sparse, padded selections: every gradient entry checked is the central
+    difference of the loss sum(dout * attend(...)), where attend is the
+    oracle's forward (independent code: two-pass softmax over key lists)."""
+    rng = np.random.default_rng(5 + causal)
+    bh, n, d, block, topk, scale = 1, 64, 8, 16, 3, 0.4
+    q, k, v, dout = (rng.standard_normal((bh, n, d)).astype(np.float32) for _ in range(4))
+    idx = _random_selection(rng, bh, n, block, topk, causal)
+    dq, _, dk, dv = oracle.attend_backward(q, k, v, dout, idx, block, causal, scale)
+    grads = {"q": dq.reshape(bh, n, d), "k": dk.reshape(bh, n, d), "v": dv.reshape(bh, n, d)}
+
+    def loss(qq, kk, vv):
+        o = oracle.attend(qq, kk, vv, idx, block, causal, scale)
+        return float(np.sum(o * dout.reshape(-1, d).astype(np.float64)))
+
+    h = 2.0 ** -9
+    for name in ("q", "k", "v"):
+        for _ in range(12):
+            i, c = int(rng.integers(n)), int(rng.integers(d))
+            args = {"q": q, "k": k, "v": v}
+            plus = {a: x.copy() for a, x in args.items()}
+            minus = {a: x.copy() for a, x in args.items()}
+            plus[name][0, i, c] += np.float32(h)       # exact in float32 for |x| < 2^14 h
+            minus[name][0, i, c] -= np.float32(h)
+            step = float(plus[name][0, i, c]) - float(minus[name][0, i, c])
+            fd = (loss(plus["q"], plus["k"], plus["v"]) - loss(minus["q"], minus["k"], minus["v"])) / step
+            assert abs(fd - grads[name][0, i, c]) <= 1e-5 * max(1.0, abs(fd)), (name, i, c, fd,
+                                                                                grads[name][0, i, c])
+
+
+def test_backward_invariants():
+    """For any selection: sum_j dv_j = sum_i dO_i (each row's weights sum to
+    one) and sum_j dk_j = 0 (each row's ds sums to zero), per head; a zero
+    incoming gradient gives zero gradients; key blocks nobody selects get 0."""
+    rng = np.random.default_rng(21)
+    bh, n, d, block, topk, scale = 2, 256, 16, 32, 3, 0.3
+    q, k, v, dout = (rng.standard_normal((bh, n, d)).astype(np.float32) for _ in range(4))
+    idx = _random_selection(rng, bh, n, block, topk, False)
+    idx[idx == 7] = 6                                   # block 7 never selected (dups allowed)
+    dq, lse, dk, dv = oracle.attend_backward(q, k, v, dout, idx, block, False, scale)
+    nb = n // block
+    for h in range(bh):
+        np.testing.assert_allclose(dv[h * nb:(h + 1) * nb].reshape(n, d).sum(0),
+                                   dout[h].astype(np.float64).sum(0), atol=1e-10)
+        np.testing.assert_allclose(dk[h * nb:(h + 1) * nb].reshape(n, d).sum(0), 0.0, atol=1e-10)
+        assert not dk[h * nb + 7].any() and not dv[h * nb + 7].any()
+    z = oracle.attend_backward(q, k, v, np.zeros_like(dout), idx, block, False, scale)
+    assert not z[0].any() and not z[2].any() and not z[3].any()
+    np.testing.assert_array_equal(z[1], lse)
+
+
+def test_backward_row_and_block_subsets_agree_with_the_full_call():
+    rng = np.random.default_rng(3)
+    bh, n, d, block, topk, scale = 2, 128, 16, 32, 2, 0.25
+    q, k, v, dout = (rng.standard_normal((bh, n, d)).astype(np.float32) for _ in range(4))
+    idx = _random_selection(rng, bh, n, block, topk, True)
+    full = oracle.attend_backward(q, k, v, dout, idx, block, True, scale)
+    rows = np.array([3, 130, 255])
+    blocks = np.array([7, 0, 5])
+    sub = oracle.attend_backward(q, k, v, dout, idx, block, True, scale, rows=rows, key_blocks=blocks)
+    np.testing.assert_array_equal(sub[0], full[0][rows])
+    np.testing.assert_array_equal(sub[1], full[1][rows])
+    np.testing.assert_array_equal(sub[2], full[2][blocks])
+    np.testing.assert_array_equal(sub[3], full[3][blocks])
