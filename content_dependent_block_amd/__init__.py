@@ -2,9 +2,11 @@
 
 Stage 1 mean-pools each 64-key block, scores every query against every block
 representative and keeps each query's top-k blocks; stage 2 runs fused
-online-softmax attention over only those blocks.  All of it runs in the gfx950
-kernels of ``libbsa.so`` behind the C ABI in ``include/bsa.h``; this package is
-a thin binding with the same names (see ``_binding``).
+online-softmax attention over only those blocks.  ``block_sparse_attention``
+is the differentiable form (the selection is held fixed in the backward).  All
+of it runs in the gfx950 kernels of ``libbsa.so`` behind the C ABI in
+``include/bsa.h``; this package is a thin binding with the same names (see
+``_binding``).
 """
 from __future__ import annotations
 
@@ -13,8 +15,8 @@ import math
 import torch
 
 from ._binding import *  # noqa: F401,F403  (bsa_* functions and constants)
-from ._binding import (EXPORTED, STAGE_NAMES, BsaError, bsa_create, bsa_destroy, bsa_forward,
-                       bsa_forward_budgets, bsa_forward_static)
+from ._binding import (EXPORTED, STAGE_NAMES, BsaError, bsa_backward, bsa_create, bsa_destroy,
+                       bsa_forward, bsa_forward_budgets, bsa_forward_static, bsa_forward_train)
 
 
 class BlockSparseAttention:
@@ -69,3 +71,45 @@ class BlockSparseAttention:
         bsa_forward_static(self.handle, q, k, v, out, tile_row_ptr, tile_col, tile_rowmask,
                            scale=scale, stream=stream)
         return out
+
+
+class _BlockSparseAttentionFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, lib, topk, head_topk, block, scale, causal):
+        b, h, n, _ = q.shape
+        q, k, v = q.contiguous(), k.contiguous(), v.contiguous()
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        idx = torch.empty((b, h, n, topk), dtype=torch.int32, device=q.device)
+        lse = torch.empty((b, h, n), dtype=torch.float32, device=q.device)
+        bsa_forward_train(lib.handle, q, k, v, out, idx, lse, topk=topk, head_topk=head_topk,
+                          block=block, scale=scale, causal=causal)
+        ctx.save_for_backward(q, k, v, out, idx, lse)
+        ctx.lib, ctx.block, ctx.scale, ctx.causal = lib, block, scale, causal
+        ctx.mark_non_differentiable(idx)
+        return out, idx
+
+    @staticmethod
+    def backward(ctx, dout, _didx):
+        q, k, v, out, idx, lse = ctx.saved_tensors
+        dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        dk = torch.empty_like(dq)
+        dv = torch.empty_like(dq)
+        bsa_backward(ctx.lib.handle, q, k, v, out, dout.contiguous().float(), idx, lse, dq, dk, dv,
+                     block=ctx.block, scale=ctx.scale, causal=ctx.causal)
+        return dq, dk, dv, None, None, None, None, None, None
+
+
+def block_sparse_attention(q, k, v, topk, *, lib: BlockSparseAttention, block: int = 64,
+                           scale: float | None = None, causal: bool = False,
+                           return_indices: bool = False):
+    """Differentiable two-stage block-sparse attention: float32 out (and the
+    int32 selection).  topk: an int, or one int per head (rows then hold
+    max(topk) indices, -1 padded).  Gradients reach q, k, v through the fine
+    stage; the selection is a discrete choice and is held fixed."""
+    d = q.shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    per_head = not isinstance(topk, int)
+    kmax = int(max(topk)) if per_head else int(topk)
+    out, idx = _BlockSparseAttentionFn.apply(q, k, v, lib, kmax, list(topk) if per_head else None,
+                                             block, scale, causal)
+    return (out, idx) if return_indices else out

@@ -24,9 +24,10 @@ BSA_ERR_NO_DEVICE, BSA_ERR_OUT_OF_MEMORY, BSA_ERR_LAUNCH = 3, 4, 5
 BSA_FP32, BSA_BF16 = 0, 1
 BSA_STAGE_POOL, BSA_STAGE_COARSE, BSA_STAGE_TOPK, BSA_STAGE_FINE = 0, 1, 2, 3
 BSA_STAGE_GATHER_INDEX, BSA_STAGE_GATHER_COMBINE, BSA_STAGE_COARSE_TOPK = 4, 5, 6
-BSA_NUM_STAGES = 7
+BSA_STAGE_BWD_PREP, BSA_STAGE_BWD_INDEX, BSA_STAGE_BWD_PAIRS, BSA_STAGE_BWD_REDUCE = 7, 8, 9, 10
+BSA_NUM_STAGES = 11
 STAGE_NAMES = ("block_pool", "coarse_score", "topk_select", "sparse_flash_fwd", "gather_index",
-               "gather_combine", "coarse_select")
+               "gather_combine", "coarse_select", "bwd_prep", "bwd_index", "bwd_pairs", "bwd_reduce")
 BSA_OPT_PANEL_CHUNK_BYTES, BSA_OPT_FINE_STRATEGY, BSA_OPT_FINE_CHUNK_BYTES = 0, 1, 2
 BSA_OPT_SELECT_STRATEGY = 3
 BSA_FINE_BLOCK_GATHER, BSA_FINE_QUERY_TILE = 0, 1
@@ -49,6 +50,9 @@ _sig("bsa_set_option", [_P, _I, _I64])
 _sig("bsa_workspace_bytes", [_P, ctypes.POINTER(ctypes.c_size_t)])
 _sig("bsa_forward", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P])
 _sig("bsa_forward_budgets", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _F, _I, _P])
+_sig("bsa_forward_train", [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _F, _I, _P])
+_sig("bsa_backward", [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                      _P])
 _sig("bsa_fine_forward", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P])
 _sig("bsa_block_pool", [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P])
 _sig("bsa_coarse_score", [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P])
@@ -61,7 +65,8 @@ _sig("bsa_profile_enable", [_P, _I])
 _sig("bsa_profile_read", [_P, _P, _P, _I])
 
 EXPORTED = ("bsa_create", "bsa_destroy", "bsa_status_string", "bsa_last_error", "bsa_set_option",
-            "bsa_workspace_bytes", "bsa_forward", "bsa_forward_budgets", "bsa_fine_forward",
+            "bsa_workspace_bytes", "bsa_forward", "bsa_forward_budgets", "bsa_forward_train",
+            "bsa_backward", "bsa_fine_forward",
             "bsa_block_pool",
             "bsa_coarse_score", "bsa_topk_select", "bsa_forward_static", "bsa_tiles_from_mask",
             "bsa_tiles_window_stride", "bsa_tiles_validate", "bsa_profile_enable",
@@ -180,6 +185,42 @@ def bsa_forward_budgets(h, q, k, v, out, block_idx_out=None, *, head_topk, topk_
     _check(_lib.bsa_forward_budgets(h, pq, pk, pv, po, pi, b, hh, n, d, _dtype_code(q), block,
                                     ks.ctypes.data, int(topk_max), float(scale), int(causal),
                                     _stream(stream, dev)), h)
+
+
+def bsa_forward_train(h, q, k, v, out, block_idx_out, lse_out, *, topk: int, head_topk=None,
+                      block: int = 64, scale: float, causal: bool = False, stream=None) -> None:
+    """bsa_forward that also writes the row log-sum-exp the backward needs;
+    head_topk (optional, one int per head) as in bsa_forward_budgets."""
+    pq, pk, pv, dev = _qkv(q, k, v)
+    b, hh, n, d = q.shape
+    po = _need(out, "out", q.shape, torch.float32, dev)
+    pi = _need(block_idx_out, "block_idx_out", (b, hh, n, topk), torch.int32, dev)
+    pl = _need(lse_out, "lse_out", (b, hh, n), torch.float32, dev)
+    pk_ = None
+    if head_topk is not None:
+        ks = np.ascontiguousarray(np.asarray(head_topk, dtype=np.int32).reshape(-1))
+        if ks.size != hh:
+            raise ValueError(f"head_topk needs {hh} entries, got {ks.size}")
+        pk_ = ks.ctypes.data
+    _check(_lib.bsa_forward_train(h, pq, pk, pv, po, pi, pl, b, hh, n, d, _dtype_code(q), block, pk_,
+                                  int(topk), float(scale), int(causal), _stream(stream, dev)), h)
+
+
+def bsa_backward(h, q, k, v, out, dout, block_idx, lse, dq, dk, dv, *, block: int = 64,
+                 scale: float, causal: bool = False, stream=None) -> None:
+    """Gradients of q, k, v through the fine stage (selection fixed)."""
+    pq, pk, pv, dev = _qkv(q, k, v)
+    b, hh, n, d = q.shape
+    if block_idx.dim() != 4:
+        raise ValueError("block_idx must be [batch, heads, n, topk]")
+    topk = block_idx.shape[-1]
+    f32 = torch.float32
+    args = [_need(out, "out", q.shape, f32, dev), _need(dout, "dout", q.shape, f32, dev),
+            _need(block_idx, "block_idx", (b, hh, n, topk), torch.int32, dev),
+            _need(lse, "lse", (b, hh, n), f32, dev), _need(dq, "dq", q.shape, f32, dev),
+            _need(dk, "dk", q.shape, f32, dev), _need(dv, "dv", q.shape, f32, dev)]
+    _check(_lib.bsa_backward(h, pq, pk, pv, *args, b, hh, n, d, _dtype_code(q), block, topk,
+                             float(scale), int(causal), _stream(stream, dev)), h)
 
 
 def bsa_fine_forward(h, q, k, v, out, block_idx, *, block: int = 64, scale: float,

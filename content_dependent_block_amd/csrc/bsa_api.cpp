@@ -39,6 +39,7 @@ struct bsa_handle_s {
     size_t bytes = 0;
   };
   Buf g_count, g_offsets, g_items, g_item_rec, g_rank, g_list, g_po, g_pml;
+  Buf b_ld, b_dq, b_dkv;  // backward: per-row (lse, delta), per-pair dq, per-item dk/dv
   // timing
   bool profiling = false;
   struct Rec {
@@ -235,7 +236,8 @@ BSA_API bsa_status bsa_destroy(bsa_handle h) {
   if (h->split) (void)hipFree(h->split);
   if (h->panel) (void)hipFree(h->panel);
   if (h->idx) (void)hipFree(h->idx);
-  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml})
+  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml,
+                 &h->b_ld, &h->b_dq, &h->b_dkv})
     if (b->p) (void)hipFree(b->p);
   delete h;
   return BSA_OK;
@@ -270,7 +272,8 @@ BSA_API bsa_status bsa_set_option(bsa_handle h, int option, int64_t value) {
 BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
   if (!h || !bytes) return fail(h, BSA_ERR_INVALID_ARG, "bsa_workspace_bytes: NULL argument");
   *bytes = h->repr_bytes + h->split_bytes + h->panel_bytes + h->idx_bytes;
-  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml})
+  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml,
+                 &h->b_ld, &h->b_dq, &h->b_dkv})
     *bytes += b->bytes;
   return BSA_OK;
 }
@@ -332,11 +335,11 @@ bsa_status grow_buf(bsa_handle h, bsa_handle_s::Buf& b, size_t need, const char*
 
 // Stage 2 for the dynamic path, with the handle's fine strategy.
 bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, float* out,
-                    const int32_t* idx, const Shape& s, bsa_dtype dt, int topk, float scale,
-                    int causal, hipStream_t st) {
+                    float* lse, const int32_t* idx, const Shape& s, bsa_dtype dt, int topk,
+                    float scale, int causal, hipStream_t st) {
   if (h->fine_strategy == BSA_FINE_QUERY_TILE)
     return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
-      return bsa::launch_sparse_flash_dynamic(q, k, v, out, idx, s.bh(), s.n, s.d, topk, scale,
+      return bsa::launch_sparse_flash_dynamic(q, k, v, out, lse, idx, s.bh(), s.n, s.d, topk, scale,
                                               causal, dt, st);
     });
   const int64_t total = s.bh() * s.n;
@@ -353,13 +356,26 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   TRY(grow_buf(h, h->g_count, size_t(buckets) * 4, "bucket counts"));
   TRY(grow_buf(h, h->g_offsets, size_t(buckets + 1) * 4, "bucket offsets"));
   TRY(grow_buf(h, h->g_items, size_t(buckets + 1) * 4, "bucket work items"));
-  TRY(grow_buf(h, h->g_item_rec, size_t(bsa::gather_grid(chunk, topk, buckets)) * 16,
+  TRY(grow_buf(h, h->g_item_rec, size_t(bsa::gather_grid(chunk, topk, buckets, bsa::kGatherItemPairs)) * 16,
                "work-item records"));
   TRY(grow_buf(h, h->g_rank, size_t(pairs) * 4, "pair ranks"));
   TRY(grow_buf(h, h->g_list, size_t(pairs) * 4, "pair lists"));
   TRY(grow_buf(h, h->g_po, size_t(pairs) * s.d * (dt == BSA_BF16 ? 2 : 4), "partial outputs"));
   TRY(grow_buf(h, h->g_pml, size_t(pairs) * 8, "partial max/sum"));
-  bsa::GatherArgs a{q, k, v, out, idx, s.n, s.d, topk, causal, scale, dt, qsegs, {}};
+  bsa::GatherArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.idx = idx;
+  a.n = s.n;
+  a.d = s.d;
+  a.topk = topk;
+  a.causal = causal;
+  a.scale = scale;
+  a.dtype = dt;
+  a.qsegs = qsegs;
   a.ws.count = static_cast<int32_t*>(h->g_count.p);
   a.ws.offsets = static_cast<int32_t*>(h->g_offsets.p);
   a.ws.items = static_cast<int32_t*>(h->g_items.p);
@@ -450,7 +466,7 @@ BSA_API bsa_status bsa_fine_forward(bsa_handle h, const void* q, const void* k, 
   TRY(check_ptr(h, fn, "out", out));
   if (!block_idx) return fail(h, BSA_ERR_INVALID_ARG, "%s: block_idx is NULL", fn);
   DeviceGuard dg(h->device);
-  return run_fine(h, q, k, v, out, block_idx, s, dtype, topk, scale, causal,
+  return run_fine(h, q, k, v, out, nullptr, block_idx, s, dtype, topk, scale, causal,
                   static_cast<hipStream_t>(stream));
 }
 
@@ -458,8 +474,9 @@ namespace {
 // bsa_forward and bsa_forward_budgets after their own argument checks;
 // topk = index row length (the largest budget).
 bsa_status forward_impl(bsa_handle h, const char* fn, const void* q, const void* k, const void* v,
-                        float* out, int32_t* block_idx_out, const Shape& s, bsa_dtype dtype,
-                        int topk, const bsa::HeadBudget& hb, float scale, int causal, void* stream) {
+                        float* out, int32_t* block_idx_out, float* lse_out, const Shape& s,
+                        bsa_dtype dtype, int topk, const bsa::HeadBudget& hb, float scale,
+                        int causal, void* stream) {
   TRY(check_scale(h, fn, scale));
   TRY(check_ptr(h, fn, "q", q));
   TRY(check_ptr(h, fn, "k", k));
@@ -488,7 +505,23 @@ bsa_status forward_impl(bsa_handle h, const char* fn, const void* q, const void*
   }
   TRY(run_pool(h, k, repr, split, s, dtype, st));
   TRY(run_select(h, q, repr, split, idx, s, dtype, topk, hb, causal, st));
-  return run_fine(h, q, k, v, out, idx, s, dtype, topk, scale, causal, st);
+  return run_fine(h, q, k, v, out, lse_out, idx, s, dtype, topk, scale, causal, st);
+}
+
+// Per-head budgets from a host array (heads entries, each in [1, topk_max]).
+bsa_status read_budgets(bsa_handle h, const char* fn, const int32_t* head_topk, int heads,
+                        int topk_max, bsa::HeadBudget* hb) {
+  if (heads > bsa::kMaxBudgetHeads)
+    return fail(h, BSA_ERR_UNSUPPORTED, "%s: at most %d heads with per-head budgets (got %d)", fn,
+                bsa::kMaxBudgetHeads, heads);
+  hb->heads = heads;
+  for (int i = 0; i < heads; ++i) {
+    if (head_topk[i] < 1 || head_topk[i] > topk_max)
+      return fail(h, BSA_ERR_INVALID_ARG, "%s: head_topk[%d] = %d is outside [1, topk_max = %d]", fn, i,
+                  head_topk[i], topk_max);
+    hb->k[i] = head_topk[i];
+  }
+  return BSA_OK;
 }
 }  // namespace
 
@@ -501,8 +534,8 @@ BSA_API bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const
   const Shape s{batch, heads, n, d};
   TRY(check_shape(h, fn, s, dtype, block));
   TRY(check_dynamic(h, fn, s, topk, causal));
-  return forward_impl(h, fn, q, k, v, out, block_idx_out, s, dtype, topk, uniform_budget(topk), scale,
-                      causal, stream);
+  return forward_impl(h, fn, q, k, v, out, block_idx_out, nullptr, s, dtype, topk, uniform_budget(topk),
+                      scale, causal, stream);
 }
 
 BSA_API bsa_status bsa_forward_budgets(bsa_handle h, const void* q, const void* k, const void* v,
@@ -516,19 +549,130 @@ BSA_API bsa_status bsa_forward_budgets(bsa_handle h, const void* q, const void* 
   TRY(check_shape(h, fn, s, dtype, block));
   TRY(check_dynamic(h, fn, s, topk_max, causal));
   if (!head_topk) return fail(h, BSA_ERR_INVALID_ARG, "%s: head_topk is NULL", fn);
-  if (heads > bsa::kMaxBudgetHeads)
-    return fail(h, BSA_ERR_UNSUPPORTED, "%s: at most %d heads with per-head budgets (got %d)", fn,
-                bsa::kMaxBudgetHeads, heads);
   bsa::HeadBudget hb;
-  hb.heads = heads;
-  for (int i = 0; i < heads; ++i) {
-    if (head_topk[i] < 1 || head_topk[i] > topk_max)
-      return fail(h, BSA_ERR_INVALID_ARG, "%s: head_topk[%d] = %d is outside [1, topk_max = %d]", fn, i,
-                  head_topk[i], topk_max);
-    hb.k[i] = head_topk[i];
-  }
-  return forward_impl(h, fn, q, k, v, out, block_idx_out, s, dtype, topk_max, hb, scale, causal,
+  TRY(read_budgets(h, fn, head_topk, heads, topk_max, &hb));
+  return forward_impl(h, fn, q, k, v, out, block_idx_out, nullptr, s, dtype, topk_max, hb, scale,
+                      causal, stream);
+}
+
+BSA_API bsa_status bsa_forward_train(bsa_handle h, const void* q, const void* k, const void* v,
+                                     float* out, int32_t* block_idx_out, float* lse_out, int batch,
+                                     int heads, int n, int d, bsa_dtype dtype, int block,
+                                     const int32_t* head_topk, int topk, float scale, int causal,
+                                     void* stream) {
+  const char* fn = "bsa_forward_train";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const Shape s{batch, heads, n, d};
+  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_dynamic(h, fn, s, topk, causal));
+  if (!block_idx_out) return fail(h, BSA_ERR_INVALID_ARG, "%s: block_idx_out is NULL", fn);
+  if (!lse_out) return fail(h, BSA_ERR_INVALID_ARG, "%s: lse_out is NULL", fn);
+  if (reinterpret_cast<uintptr_t>(lse_out) & 3u)
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: lse_out is not 4-byte aligned", fn);
+  bsa::HeadBudget hb = uniform_budget(topk);
+  if (head_topk) TRY(read_budgets(h, fn, head_topk, heads, topk, &hb));
+  return forward_impl(h, fn, q, k, v, out, block_idx_out, lse_out, s, dtype, topk, hb, scale, causal,
                       stream);
+}
+
+BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, const void* v,
+                                const float* out, const float* dout, const int32_t* block_idx,
+                                const float* lse, float* dq, float* dk, float* dv, int batch,
+                                int heads, int n, int d, bsa_dtype dtype, int block, int topk,
+                                float scale, int causal, void* stream) {
+  const char* fn = "bsa_backward";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const Shape s{batch, heads, n, d};
+  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_dynamic(h, fn, s, topk, causal));
+  TRY(check_scale(h, fn, scale));
+  TRY(check_ptr(h, fn, "q", q));
+  TRY(check_ptr(h, fn, "k", k));
+  TRY(check_ptr(h, fn, "v", v));
+  TRY(check_ptr(h, fn, "out", out));
+  TRY(check_ptr(h, fn, "dout", dout));
+  TRY(check_ptr(h, fn, "dq", dq));
+  TRY(check_ptr(h, fn, "dk", dk));
+  TRY(check_ptr(h, fn, "dv", dv));
+  if (!block_idx || (reinterpret_cast<uintptr_t>(block_idx) & 3u))
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: block_idx is NULL or not 4-byte aligned", fn);
+  if (!lse || (reinterpret_cast<uintptr_t>(lse) & 3u))
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: lse is NULL or not 4-byte aligned", fn);
+  DeviceGuard dg(h->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t total = s.bh() * s.n;
+  const int64_t align = (s.n % 256 == 0) ? 256 : 64;  // keeps bucketing workgroups inside one head
+  const size_t per_row = size_t(topk) * (size_t(s.d) * 4 + 8);
+  int64_t chunk = h->fine_chunk_bytes / int64_t(per_row) / align * align;
+  if (chunk < align) chunk = align;
+  if (chunk > total) chunk = total;
+  const int64_t pairs = chunk * topk;
+  const int64_t nb = s.n / 64;
+  const int qsegs = bsa::gather_segments(s.n, s.d, topk, dtype);
+  const int64_t heads_spanned = s.bh() < (chunk + s.n - 1) / s.n + 1 ? s.bh() : (chunk + s.n - 1) / s.n + 1;
+  const int64_t buckets = heads_spanned * qsegs * nb;
+  const int64_t slots = bsa::gather_grid(chunk, topk, buckets, bsa::kBwdItemPairs);
+  TRY(grow_buf(h, h->g_count, size_t(buckets) * 4, "bucket counts"));
+  TRY(grow_buf(h, h->g_offsets, size_t(buckets + 1) * 4, "bucket offsets"));
+  TRY(grow_buf(h, h->g_items, size_t(buckets + 1) * 4, "bucket work items"));
+  TRY(grow_buf(h, h->g_item_rec, size_t(slots) * 16, "work-item records"));
+  TRY(grow_buf(h, h->g_rank, size_t(pairs) * 4, "pair ranks"));
+  TRY(grow_buf(h, h->g_list, size_t(pairs) * 4, "pair lists"));
+  TRY(grow_buf(h, h->b_ld, size_t(total) * 8, "backward row statistics"));
+  TRY(grow_buf(h, h->b_dq, size_t(pairs) * s.d * 4, "backward dq contributions"));
+  TRY(grow_buf(h, h->b_dkv, size_t(slots) * 2 * 64 * s.d * 4, "backward dk/dv contributions"));
+  bsa::BackwardArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.dout = dout;
+  a.lse = lse;
+  a.idx = block_idx;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.n = s.n;
+  a.d = s.d;
+  a.topk = topk;
+  a.causal = causal;
+  a.scale = scale;
+  a.dtype = dtype;
+  a.qsegs = qsegs;
+  a.ld = static_cast<float2*>(h->b_ld.p);
+  a.dq_part = static_cast<float*>(h->b_dq.p);
+  a.dkv_part = static_cast<float*>(h->b_dkv.p);
+  a.ws.count = static_cast<int32_t*>(h->g_count.p);
+  a.ws.offsets = static_cast<int32_t*>(h->g_offsets.p);
+  a.ws.items = static_cast<int32_t*>(h->g_items.p);
+  a.ws.item_rec = static_cast<int4*>(h->g_item_rec.p);
+  a.ws.rank = static_cast<int32_t*>(h->g_rank.p);
+  a.ws.list = static_cast<int32_t*>(h->g_list.p);
+  bsa::GatherArgs gi;  // the bucketing of the forward, with backward-sized work items
+  gi.q = q;
+  gi.idx = block_idx;
+  gi.n = s.n;
+  gi.d = s.d;
+  gi.topk = topk;
+  gi.causal = causal;
+  gi.dtype = dtype;
+  gi.qsegs = qsegs;
+  gi.item_pairs = bsa::kBwdItemPairs;
+  gi.ws = a.ws;
+  TRY(timed_launch(h, BSA_STAGE_BWD_PREP, st, "backward row statistics",
+                   [&] { return bsa::launch_bwd_prep(a, total, st); }));
+  for (int64_t r0 = 0; r0 < total; r0 += chunk) {
+    const int64_t rows = (total - r0) < chunk ? (total - r0) : chunk;
+    TRY(timed_launch(h, BSA_STAGE_BWD_INDEX, st, "backward bucketing",
+                     [&] { return bsa::launch_gather_index(gi, r0, rows, st); }));
+    TRY(timed_launch(h, BSA_STAGE_BWD_PAIRS, st, "backward pair kernel",
+                     [&] { return bsa::launch_bwd_pairs(a, r0, rows, st); }));
+    TRY(timed_launch(h, BSA_STAGE_BWD_REDUCE, st, "backward dq reduction",
+                     [&] { return bsa::launch_bwd_dq(a, r0, rows, st); }));
+    TRY(timed_launch(h, BSA_STAGE_BWD_REDUCE, st, "backward dk/dv reduction",
+                     [&] { return bsa::launch_bwd_dkv(a, r0, rows, st); }));
+  }
+  return BSA_OK;
 }
 
 BSA_API bsa_status bsa_forward_static(bsa_handle h, const void* q, const void* k, const void* v,

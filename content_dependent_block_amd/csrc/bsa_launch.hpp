@@ -47,10 +47,11 @@ hipError_t launch_topk_select(const float* panel, int32_t* idx, int64_t row0, in
                               int topk, const HeadBudget& budget, int causal, hipStream_t stream);
 
 // sparse_flash_fwd, dynamic: per 64-query tile the union of its rows'
-// selected blocks, each row masked to its own selection.
+// selected blocks, each row masked to its own selection.  lse (nullable):
+// per row log-sum-exp of the scaled scores, natural log.
 hipError_t launch_sparse_flash_dynamic(const void* q, const void* k, const void* v, float* out,
-                                       const int32_t* idx, int64_t bh, int n, int d, int topk,
-                                       float scale, int causal, bsa_dtype dtype,
+                                       float* lse, const int32_t* idx, int64_t bh, int n, int d,
+                                       int topk, float scale, int causal, bsa_dtype dtype,
                                        hipStream_t stream);
 
 // sparse_flash_fwd, static tile list.
@@ -73,16 +74,21 @@ struct GatherWorkspace {
   float2* partial_ml = nullptr;  // [chunk pairs]  (log2-domain max, sum)
 };
 
+// Pairs per work item of the forward attention kernel.
+constexpr int kGatherItemPairs = 256;
+
 struct GatherArgs {
-  const void* q;
-  const void* k;
-  const void* v;
-  float* out;
-  const int32_t* idx;
-  int n, d, topk, causal;
-  float scale;
-  bsa_dtype dtype;
-  int qsegs;  // query segments per head (gather_segments); buckets = heads x qsegs x n/64
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  float* out = nullptr;
+  float* lse = nullptr;  // nullable: per row log-sum-exp (natural log), from the combine
+  const int32_t* idx = nullptr;
+  int n = 0, d = 0, topk = 0, causal = 0;
+  float scale = 0.f;
+  bsa_dtype dtype = BSA_FP32;
+  int qsegs = 1;  // query segments per head (gather_segments); buckets = heads x qsegs x n/64
+  int item_pairs = kGatherItemPairs;  // pairs per work item made by the bucketing
   GatherWorkspace ws;
 };
 
@@ -92,9 +98,46 @@ struct GatherArgs {
 int gather_segments(int n, int d, int topk, bsa_dtype dtype);
 
 size_t gather_pair_bytes(int d, bsa_dtype dtype);  // partial bytes per (query, block) pair
-int64_t gather_grid(int64_t rows, int topk, int64_t nbuckets);  // attention-kernel workgroups
+// Work-item slots (workgroups of the kernels that run the items).
+int64_t gather_grid(int64_t rows, int topk, int64_t nbuckets, int item_pairs);
 hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s);
 hipError_t launch_gather_partial(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s);
 hipError_t launch_gather_combine(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s);
+
+// Backward of the fine stage with the selection held fixed, on the same
+// bucketing as the block-gather forward (one work item = up to
+// kBwdItemPairs pairs of one (head, query segment, key block) bucket).
+constexpr int kBwdItemPairs = 512;
+
+struct BackwardArgs {
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  const float* out = nullptr;   // forward output [bh][n][d]
+  const float* dout = nullptr;  // incoming gradient [bh][n][d]
+  const float* lse = nullptr;   // forward log-sum-exp [bh][n]
+  const int32_t* idx = nullptr;
+  float* dq = nullptr;
+  float* dk = nullptr;
+  float* dv = nullptr;
+  int n = 0, d = 0, topk = 0, causal = 0;
+  float scale = 0.f;
+  bsa_dtype dtype = BSA_FP32;
+  int qsegs = 1;
+  float2* ld = nullptr;      // [bh * n] (lse * log2(e), sum_d dout * out)
+  float* dq_part = nullptr;  // [chunk pairs][d]  per-pair dq contributions
+  float* dkv_part = nullptr; // [work items][2][64][d]  per-item dk, dv contributions
+  GatherWorkspace ws;        // bucketing (count .. list); partial_o / partial_ml unused
+};
+
+// ld for all `rows` query rows.
+hipError_t launch_bwd_prep(const BackwardArgs& a, int64_t rows, hipStream_t s);
+// Per chunk of query rows [row0, row0 + rows), after launch_gather_index on
+// the chunk: the pair kernel, then dq of the chunk's rows and dk, dv of the
+// key blocks of the heads the chunk spans (added to what an earlier chunk
+// wrote for the head when the head began before row0).
+hipError_t launch_bwd_pairs(const BackwardArgs& a, int64_t row0, int64_t rows, hipStream_t s);
+hipError_t launch_bwd_dq(const BackwardArgs& a, int64_t row0, int64_t rows, hipStream_t s);
+hipError_t launch_bwd_dkv(const BackwardArgs& a, int64_t row0, int64_t rows, hipStream_t s);
 
 }  // namespace bsa

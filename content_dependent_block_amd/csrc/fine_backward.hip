@@ -1,0 +1,579 @@
+// fine_backward.hip -- backward of the fine stage with the selection held
+// fixed (nishantmodi.me "sparse-attention-triton-bench", section "What's
+// next": a backward pass through the softmax-weighted sum over the selected
+// blocks, FlashAttention-2's recomputing backward as the dense model).
+//
+// With z_ij = scale * q_i.k_j over query i's visible keys J(i), the forward's
+// per-row log-sum-exp lse_i, and the incoming gradient dO:
+//   p_ij  = exp(z_ij - lse_i)                (recomputed, never stored)
+//   dp_ij = dO_i . v_j,  delta_i = dO_i . o_i  (= sum_j p_ij dp_ij)
+//   ds_ij = p_ij (dp_ij - delta_i)
+//   dq_i  = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+//   dv_j  = sum_i p_ij dO_i.
+//
+// The work runs on the block-gather bucketing of the forward: one work item
+// is up to kBwdItemPairs (query, block) pairs that share key block beta, so
+// K and V of the block are staged once and every pair reuses them.  Per tile
+// of 64 pairs (16 per wave, one pair per MFMA column):
+//   S^T = K Q^T and dP^T = V dO^T on MFMA (64 keys x 16 pairs per wave),
+//   P^T, dS^T in registers,
+//   dQ^T = K^T dS^T on MFMA: the pair's dq contribution from this block, one
+//         row per pair, summed per query by bwd_dq in slot order (the same
+//         bits on every call);
+//   dV += P^T dO and dK += dS^T Q on MFMA, each wave owning 16 keys of the
+//         block and summing over all 64 pairs of the tile (P^T, dS^T, dO,
+//         Q pass through LDS).
+// At the end of the item its dk, dv (64 keys x d each) go to a per-item
+// buffer; bwd_dkv sums the items of every (head, block) in item order.  No
+// floating-point atomics anywhere; dk and dv still depend in their last bits
+// on the order the bucketing's integer atomics give a block's pairs.
+//
+// bf16 inputs: MFMA operands in bf16 (P, dS and dO rounded to bf16 as the
+// forward rounds P), fp32 accumulation and outputs.  fp32 inputs: fp32 MFMA
+// throughout.
+#include "bsa_device.hpp"
+#include "bsa_launch.hpp"
+
+namespace bsa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kXcds = 8;
+constexpr int kItem = kBwdItemPairs;
+
+__device__ __forceinline__ bool pair_valid(int beta, int nb, int64_t row, int n, int causal) {
+  if (beta < 0 || beta >= nb) return false;
+  return !causal || beta <= static_cast<int>(row % n) / kTile;
+}
+
+// ---------------------------------------------------------------- prep --
+// ld[row] = (lse * log2 e, sum_d dout * out): 16 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ out,
+                                                       const float* __restrict__ dout,
+                                                       const float* __restrict__ lse,
+                                                       float2* __restrict__ ld, int64_t rows) {
+  constexpr int E = D / 16;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  float s = 0.f;
+  if (r < rows) {
+    const float* o = out + r * D + c * E;
+    const float* g = dout + r * D + c * E;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const float4 a = *reinterpret_cast<const float4*>(o + e);
+      const float4 b = *reinterpret_cast<const float4*>(g + e);
+      s += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+    }
+  }
+#pragma unroll
+  for (int off = 8; off >= 1; off >>= 1) s += __shfl_xor(s, off, 16);
+  if (r < rows && c == 0) ld[r] = make_float2(lse[r] * kLog2e, s);
+}
+
+// -------------------------------------------------------- LDS layout --
+template <typename T, int D>
+struct BwdLayout {
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  // K, V natural [64 keys][KP]; bf16 also K^T [D][KTP keys].
+  static constexpr int KP = D + (kBf16 ? 16 : 4);
+  static constexpr int KTP = kTile + 4;
+  // P^T or dS^T [64 keys][PP pairs].
+  static constexpr int PP = kTile + (kBf16 ? 16 : 4);
+  // bf16: dO^T or Q^T [D][PP pairs]; fp32: dO or Q natural [64 pairs][KP].
+  static constexpr int K_BYTES = kTile * KP * sizeof(T);
+  static constexpr int KT_BYTES = kBf16 ? D * KTP * 2 : 0;
+  static constexpr int P_BYTES = kTile * PP * sizeof(T);
+  static constexpr int O_BYTES = kBf16 ? D * PP * 2 : kTile * KP * 4;
+  static constexpr int OFF_V = K_BYTES;
+  static constexpr int OFF_KT = 2 * K_BYTES;
+  static constexpr int OFF_P = OFF_KT + KT_BYTES;
+  static constexpr int OFF_O = OFF_P + P_BYTES;
+  static constexpr int BYTES = OFF_O + O_BYTES;
+};
+
+// K and V of one key block into LDS (K natural and, for bf16, transposed;
+// V natural).  bf16: every thread moves keys (2p, 2p+1) x 8 dims, so K^T gets
+// two keys per 32-bit LDS write.  fp32: 16-byte pieces of key rows.
+template <typename T, int D>
+__device__ __forceinline__ void stage_kv(const T* __restrict__ kb, const T* __restrict__ vb, T* ks,
+                                         T* vs, T* kt, int tid) {
+  using L = BwdLayout<T, D>;
+  if constexpr (L::kBf16) {
+#pragma unroll
+    for (int u = 0; u < D / 64; ++u) {
+      const int it = tid + 256 * u, c8 = it % (D / 8), p = it / (D / 8);
+      const uint4 k0 = ld16(kb + (2 * p) * D + c8 * 8), k1 = ld16(kb + (2 * p + 1) * D + c8 * 8);
+      const uint4 v0 = ld16(vb + (2 * p) * D + c8 * 8), v1 = ld16(vb + (2 * p + 1) * D + c8 * 8);
+      *reinterpret_cast<uint4*>(ks + (2 * p) * L::KP + c8 * 8) = k0;
+      *reinterpret_cast<uint4*>(ks + (2 * p + 1) * L::KP + c8 * 8) = k1;
+      *reinterpret_cast<uint4*>(vs + (2 * p) * L::KP + c8 * 8) = v0;
+      *reinterpret_cast<uint4*>(vs + (2 * p + 1) * L::KP + c8 * 8) = v1;
+      const uint32_t a[4] = {k0.x, k0.y, k0.z, k0.w};
+      const uint32_t b[4] = {k1.x, k1.y, k1.z, k1.w};
+      uint32_t* dst = reinterpret_cast<uint32_t*>(kt + (c8 * 8) * L::KTP + 2 * p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // dim c8*8 + 2e (low halves) and + 2e + 1 (high halves); keys 2p, 2p+1
+        dst[(2 * e) * (L::KTP / 2)] = (a[e] & 0xFFFFu) | (b[e] << 16);
+        dst[(2 * e + 1) * (L::KTP / 2)] = (a[e] >> 16) | (b[e] & 0xFFFF0000u);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < D / 16; ++u) {
+      const int c = tid + 256 * u, c4 = c % (D / 4), row = c / (D / 4);
+      *reinterpret_cast<uint4*>(ks + row * L::KP + c4 * 4) = ld16(kb + row * D + c4 * 4);
+      *reinterpret_cast<uint4*>(vs + row * L::KP + c4 * 4) = ld16(vb + row * D + c4 * 4);
+    }
+  }
+}
+
+// The pair's query row and incoming-gradient row as MFMA B operands.
+// bf16: slot group g = lane/16 holds dims 32kk + 8g .. +7 of k-step kk.
+// fp32: group g holds dims (D/4) g .. (D/4) g + D/4 - 1, one per k-step.
+template <typename T, int D>
+struct PairRows {
+  static constexpr bool kBf16 = sizeof(T) == 2;
+  bf16x8 qb[kBf16 ? D / 32 : 1];
+  bf16x8 ob[kBf16 ? D / 32 : 1];
+  float qf[kBf16 ? 1 : D / 4];
+  float of[kBf16 ? 1 : D / 4];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void load_rows(PairRows<T, D>& pr, const T* __restrict__ q,
+                                          const float* __restrict__ dout, int64_t row, bool live,
+                                          int g) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      const int d0 = 32 * kk + 8 * g;
+      pr.qb[kk] = live ? as_bf16x8(ld16(q + row * D + d0)) : bf16x8{};
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      if (live) {
+        a = *reinterpret_cast<const float4*>(dout + row * D + d0);
+        b = *reinterpret_cast<const float4*>(dout + row * D + d0 + 4);
+      }
+      pr.ob[kk] = bf16x8{f32_to_bf16(a.x), f32_to_bf16(a.y), f32_to_bf16(a.z), f32_to_bf16(a.w),
+                         f32_to_bf16(b.x), f32_to_bf16(b.y), f32_to_bf16(b.z), f32_to_bf16(b.w)};
+    }
+  } else {
+    constexpr int KS = D / 4;
+#pragma unroll
+    for (int e = 0; e < KS; e += 4) {
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+      if (live) {
+        a = *reinterpret_cast<const float4*>(q + row * D + KS * g + e);
+        b = *reinterpret_cast<const float4*>(dout + row * D + KS * g + e);
+      }
+      pr.qf[e] = a.x;
+      pr.qf[e + 1] = a.y;
+      pr.qf[e + 2] = a.z;
+      pr.qf[e + 3] = a.w;
+      pr.of[e] = b.x;
+      pr.of[e + 1] = b.y;
+      pr.of[e + 2] = b.z;
+      pr.of[e + 3] = b.w;
+    }
+  }
+}
+
+// Output dim carried by row m of output tile dt in dQ^T = K^T dS^T (bf16):
+// the K^T rows are permuted so that lane group g ends up with 8 consecutive
+// dims per pair of tiles (32u + 8g .. +7 for tiles 2u, 2u + 1).
+__device__ __forceinline__ int dq_dim(int dt, int m) {
+  return 32 * (dt / 2) + 8 * (m / 4) + 4 * (dt % 2) + (m % 4);
+}
+
+// One wave's 64 keys x 16 pairs: S^T = K Q^T and dP^T = V dO^T.
+template <typename T, int D>
+__device__ __forceinline__ void scores(const T* ks, const T* vs, const PairRows<T, D>& pr, f32x4 (&s)[4],
+                                       f32x4 (&dp)[4], int g, int c16) {
+  using L = BwdLayout<T, D>;
+#pragma unroll
+  for (int tt = 0; tt < 4; ++tt) {
+    s[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (L::kBf16) {
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const int off = (16 * tt + c16) * L::KP + 8 * g + 32 * kk;
+        s[tt] = mfma_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(ks + off), pr.qb[kk], s[tt]);
+        dp[tt] = mfma_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(vs + off), pr.ob[kk], dp[tt]);
+      }
+    } else {
+      constexpr int KS = D / 4;
+      const T* kr = ks + (16 * tt + c16) * L::KP + KS * g;
+      const T* vr = vs + (16 * tt + c16) * L::KP + KS * g;
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) {
+        s[tt] = mfma_16x16x4_f32(kr[kk], pr.qf[kk], s[tt]);
+        dp[tt] = mfma_16x16x4_f32(vr[kk], pr.of[kk], dp[tt]);
+      }
+    }
+  }
+}
+
+// One work item.  Workgroup = 4 waves; tiles of 64 pairs, wave w takes pairs
+// 16w .. 16w + 15 of the tile (lane%16 = its pair), and owns keys
+// 16w .. 16w + 15 of the block for dK and dV.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void bwd_pair_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    const float* __restrict__ dout, const float2* __restrict__ ld,
+    const int32_t* __restrict__ list, const int32_t* __restrict__ items,
+    const int4* __restrict__ item_rec, int nbuckets, int64_t row0, int64_t npairs, int n,
+    uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, float scale, float scale_log2,
+    float* __restrict__ dq_part, float* __restrict__ dkv_part) {
+  using L = BwdLayout<T, D>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  T* ks = reinterpret_cast<T*>(smem);
+  T* vs = reinterpret_cast<T*>(smem + L::OFF_V);
+  T* kt = reinterpret_cast<T*>(smem + L::OFF_KT);
+  T* pt = reinterpret_cast<T*>(smem + L::OFF_P);
+  T* ot = reinterpret_cast<T*>(smem + L::OFF_O);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+
+  const int total = items[nbuckets];
+  const int4 rec = item_rec[blockIdx.x];
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int slot = static_cast<int>(blockIdx.x) / kXcds;
+  const int item = (static_cast<int>(blockIdx.x) % kXcds) * per_xcd + slot;
+  if (slot >= per_xcd || item >= total) return;  // whole workgroup: no item here
+  const int b = rec.x;
+  if (b < 0 || b >= nbuckets) return;
+  const int64_t first = rec.y;
+  int cnt = rec.z;
+  if (cnt > kItem) cnt = kItem;
+  if (first + cnt > npairs) cnt = first < npairs ? static_cast<int>(npairs - first) : 0;
+  const int nb = n / kTile;
+  const int beta = b % nb;
+  const int64_t bh = bh0 + b / (nb * qsegs);
+
+  stage_kv<T, D>(k + (bh * n + static_cast<int64_t>(beta) * kTile) * D,
+                 v + (bh * n + static_cast<int64_t>(beta) * kTile) * D, ks, vs, kt, tid);
+
+  f32x4 dk[D / 16], dv[D / 16];
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    dk[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __syncthreads();
+
+  const int ntiles = (cnt + 63) / 64;  // workgroup-uniform
+  for (int it = 0; it < ntiles; ++it) {
+    const int t = it * 64 + 16 * wave + c16;
+    bool live = t < cnt;
+    int32_t pair = live ? list[first + t] : 0;
+    if (pair < 0 || pair >= npairs) {
+      pair = 0;
+      live = false;
+    }
+    const int64_t row = row0 + static_cast<int64_t>((static_cast<uint64_t>(pair) * div_magic) >> div_shift);
+    PairRows<T, D> pr;
+    load_rows<T, D>(pr, q, dout, row, live, g);
+    const float2 lr = live ? ld[row] : make_float2(0.f, 0.f);
+
+    f32x4 s[4], dp[4];
+    scores<T, D>(ks, vs, pr, s, dp, g, c16);
+
+    // P^T and dS^T of the lane's pair: keys 16tt + 4g + jj.
+    const int qlocal = static_cast<int>(row % n) - beta * kTile;  // < 64 only on the diagonal
+    float pv[4][4], dsv[4][4];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const bool vis = live && (!CAUSAL || 16 * tt + 4 * g + jj <= qlocal);
+        const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][jj], scale_log2, -lr.x)) : 0.f;
+        pv[tt][jj] = p;
+        dsv[tt][jj] = p * (dp[tt][jj] - lr.y);
+      }
+
+    // dQ^T = K^T dS^T: this block's contribution to the pair's dq.
+    f32x4 acc[D / 16];
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (L::kBf16) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        bf16x8 bs;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bs[i] = f32_to_bf16(dsv[2 * kk][i]);
+          bs[4 + i] = f32_to_bf16(dsv[2 * kk + 1][i]);
+        }
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const T* kr = kt + dq_dim(dt, c16) * L::KTP + 32 * kk + 4 * g;
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(kr);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(kr + 16);
+          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[dt] = mfma_16x16x32_bf16(a, bs, acc[dt]);
+        }
+      }
+      if (live) {
+        float* dst = dq_part + static_cast<int64_t>(pair) * D + 8 * g;
+#pragma unroll
+        for (int u = 0; u < D / 32; ++u) {
+          const f32x4 a0 = acc[2 * u] * scale, a1 = acc[2 * u + 1] * scale;
+          *reinterpret_cast<float4*>(dst + 32 * u) = make_float4(a0[0], a0[1], a0[2], a0[3]);
+          *reinterpret_cast<float4*>(dst + 32 * u + 4) = make_float4(a1[0], a1[1], a1[2], a1[3]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const T* kr = ks + (16 * tt + 4 * g + jj) * L::KP + c16;
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma_16x16x4_f32(kr[16 * dt], dsv[tt][jj], acc[dt]);
+        }
+      if (live) {
+        float* dst = dq_part + static_cast<int64_t>(pair) * D + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const f32x4 a = acc[dt] * scale;
+          *reinterpret_cast<float4*>(dst + 16 * dt) = make_float4(a[0], a[1], a[2], a[3]);
+        }
+      }
+    }
+
+    // dV += P^T dO, then dK += dS^T Q, over the tile's 64 pairs.
+#pragma unroll
+    for (int phase = 0; phase < 2; ++phase) {
+      const int col = 16 * wave + c16;  // the lane's pair column in the tile
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float x = phase == 0 ? pv[tt][jj] : dsv[tt][jj];
+          if constexpr (L::kBf16)
+            reinterpret_cast<__bf16*>(pt)[(16 * tt + 4 * g + jj) * L::PP + col] = f32_to_bf16(x);
+          else
+            pt[(16 * tt + 4 * g + jj) * L::PP + col] = x;
+        }
+      if constexpr (L::kBf16) {
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            reinterpret_cast<__bf16*>(ot)[(32 * kk + 8 * g + i) * L::PP + col] =
+                phase == 0 ? pr.ob[kk][i] : pr.qb[kk][i];
+      } else {
+        constexpr int KS = D / 4;
+        float* orow = reinterpret_cast<float*>(ot) + col * L::KP + KS * g;
+#pragma unroll
+        for (int e = 0; e < KS; e += 4) {
+          const float* src = phase == 0 ? pr.of : pr.qf;
+          *reinterpret_cast<float4*>(orow + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
+        }
+      }
+      __syncthreads();
+      f32x4* out = phase == 0 ? dv : dk;
+      if constexpr (L::kBf16) {
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(pt + (16 * wave + c16) * L::PP + 32 * kk + 8 * g);
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt) {
+            const bf16x8 bb = *reinterpret_cast<const bf16x8*>(ot + (16 * dt + c16) * L::PP + 32 * kk + 8 * g);
+            out[dt] = mfma_16x16x32_bf16(a, bb, out[dt]);
+          }
+        }
+      } else {
+        const float* orows = reinterpret_cast<const float*>(ot);
+#pragma unroll 4
+        for (int st = 0; st < 16; ++st) {
+          const float a = pt[(16 * wave + c16) * L::PP + 4 * st + g];
+#pragma unroll
+          for (int dt = 0; dt < D / 16; ++dt)
+            out[dt] = mfma_16x16x4_f32(a, orows[(4 * st + g) * L::KP + 16 * dt + c16], out[dt]);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // The item's dk (scaled) and dv: [item][0 = dk, 1 = dv][64 keys][D].
+  float* dst = dkv_part + static_cast<int64_t>(item) * 2 * kTile * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int key = 16 * wave + 4 * g + e, c = 16 * dt + c16;
+      dst[key * D + c] = dk[dt][e] * scale;
+      dst[(kTile + key) * D + c] = dv[dt][e];
+    }
+}
+
+// dq[row] = sum over the row's valid slots, in slot order, of its pairs'
+// contributions.  16 lanes per row.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__ idx,
+                                                     const float* __restrict__ dq_part,
+                                                     float* __restrict__ dq, int64_t row0,
+                                                     int64_t rows, int n, int topk, int causal) {
+  constexpr int E = D / 16;
+  const int64_t r = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  if (r >= rows) return;
+  const int c = threadIdx.x & 15;
+  const int64_t row = row0 + r;
+  const int nb = n / kTile;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int s = 0; s < topk; ++s) {
+    if (!pair_valid(idx[row * topk + s], nb, row, n, causal)) continue;
+    const float* src = dq_part + (r * topk + s) * D + c * E;
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+      const float4 x = *reinterpret_cast<const float4*>(src + e);
+      acc[e] += x.x;
+      acc[e + 1] += x.y;
+      acc[e + 2] += x.z;
+      acc[e + 3] += x.w;
+    }
+  }
+  float* dst = dq + row * D + c * E;
+#pragma unroll
+  for (int e = 0; e < E; e += 4)
+    *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+}
+
+// dk, dv of one (head, key block): the sum of its work items over the
+// head's query segments, in item order.  Added to the existing values when
+// the head's rows began before this chunk (an earlier chunk wrote them).
+template <int D>
+__global__ __launch_bounds__(256) void bwd_dkv_kernel(const float* __restrict__ dkv_part,
+                                                      const int32_t* __restrict__ items,
+                                                      float* __restrict__ dk, float* __restrict__ dv,
+                                                      int64_t row0, int n, int64_t bh0, int qsegs) {
+  constexpr int V = 2 * kTile * D / 4 / 256;  // float4 per thread
+  const int nb = n / kTile;
+  const int64_t hb = blockIdx.x / nb;  // head relative to bh0
+  const int beta = static_cast<int>(blockIdx.x % nb);
+  const int64_t bh = bh0 + hb;
+  float4 acc[V];
+#pragma unroll
+  for (int u = 0; u < V; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int sg = 0; sg < qsegs; ++sg) {
+    const int64_t b = (hb * qsegs + sg) * nb + beta;
+    for (int i = items[b]; i < items[b + 1]; ++i) {
+      const float4* src = reinterpret_cast<const float4*>(dkv_part + static_cast<int64_t>(i) * 2 * kTile * D);
+#pragma unroll
+      for (int u = 0; u < V; ++u) {
+        const float4 x = src[threadIdx.x + 256 * u];
+        acc[u].x += x.x;
+        acc[u].y += x.y;
+        acc[u].z += x.z;
+        acc[u].w += x.w;
+      }
+    }
+  }
+  const bool add = bh * n < row0;
+#pragma unroll
+  for (int u = 0; u < V; ++u) {
+    const int e4 = threadIdx.x + 256 * u;          // float4 index in [2][64][D]
+    const int which = e4 / (kTile * D / 4);
+    const int rem = e4 % (kTile * D / 4);
+    float4* dst = reinterpret_cast<float4*>((which == 0 ? dk : dv) + (bh * n + static_cast<int64_t>(beta) * kTile) * D) + rem;
+    float4 x = acc[u];
+    if (add) {
+      const float4 y = *dst;
+      x.x += y.x;
+      x.y += y.y;
+      x.z += y.z;
+      x.w += y.w;
+    }
+    *dst = x;
+  }
+}
+
+struct Geom {
+  int nb, nbuckets;
+  int64_t bh0, bh1, npairs;
+  Geom(const BackwardArgs& a, int64_t row0, int64_t rows) {
+    nb = a.n / kTile;
+    bh0 = row0 / a.n;
+    bh1 = (row0 + rows - 1) / a.n;
+    nbuckets = static_cast<int>((bh1 - bh0 + 1) * a.qsegs * nb);
+    npairs = rows * a.topk;
+  }
+};
+
+template <typename T, int D, bool CAUSAL>
+hipError_t pairs_launch(const BackwardArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
+  using L = BwdLayout<T, D>;
+  const Geom c(a, row0, rows);
+  const int64_t grid = gather_grid(rows, a.topk, c.nbuckets, kItem);
+  int lg = 0;
+  while ((1 << lg) < a.topk) ++lg;
+  const int shift = 32 + lg;
+  const uint64_t magic = ((uint64_t(1) << shift) + uint64_t(a.topk) - 1) / uint64_t(a.topk);
+  const auto kern = bwd_pair_kernel<T, D, CAUSAL>;
+  if (L::BYTES > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(256), L::BYTES, s,
+                     static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                     a.dout, a.ld, a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets, row0, c.npairs,
+                     a.n, magic, shift, c.bh0, a.qsegs, a.scale, a.scale * kLog2e, a.dq_part,
+                     a.dkv_part);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t pairs_dispatch(const BackwardArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
+  return a.causal ? pairs_launch<T, D, true>(a, row0, rows, s) : pairs_launch<T, D, false>(a, row0, rows, s);
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep(const BackwardArgs& a, int64_t rows, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((rows + 15) / 16));
+  if (a.d == 64)
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, dim3(256), 0, s, a.out, a.dout, a.lse, a.ld, rows);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, dim3(256), 0, s, a.out, a.dout, a.lse, a.ld, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_pairs(const BackwardArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
+  if (a.dtype == BSA_BF16)
+    return a.d == 64 ? pairs_dispatch<bf16_bits, 64>(a, row0, rows, s)
+                     : pairs_dispatch<bf16_bits, 128>(a, row0, rows, s);
+  return a.d == 64 ? pairs_dispatch<float, 64>(a, row0, rows, s) : pairs_dispatch<float, 128>(a, row0, rows, s);
+}
+
+hipError_t launch_bwd_dq(const BackwardArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((rows + 15) / 16));
+  if (a.d == 64)
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq, row0, rows, a.n,
+                       a.topk, a.causal);
+  else
+    hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq, row0, rows, a.n,
+                       a.topk, a.causal);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkv(const BackwardArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
+  const Geom c(a, row0, rows);
+  const dim3 grid(static_cast<unsigned>((c.bh1 - c.bh0 + 1) * c.nb));
+  if (a.d == 64)
+    hipLaunchKernelGGL(bwd_dkv_kernel<64>, grid, dim3(256), 0, s, a.dkv_part, a.ws.items, a.dk, a.dv, row0,
+                       a.n, c.bh0, a.qsegs);
+  else
+    hipLaunchKernelGGL(bwd_dkv_kernel<128>, grid, dim3(256), 0, s, a.dkv_part, a.ws.items, a.dk, a.dv, row0,
+                       a.n, c.bh0, a.qsegs);
+  return hipGetLastError();
+}
+
+}  // namespace bsa

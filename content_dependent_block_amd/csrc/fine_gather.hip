@@ -23,9 +23,9 @@
 //                     gets its rank inside its bucket (LDS histogram per 64 rows,
 //                     one global atomic per (workgroup, block)).
 //   bucket_scan    -- one workgroup: exclusive prefix of the counts (pair offsets)
-//                     and of ceil(count / 128) (work-item offsets).
+//                     and of ceil(count / item_pairs) (work-item offsets).
 //   bucket_fill    -- pair ids into per-bucket lists.
-//   gather_partial -- one work item = up to 128 pairs of one bucket: K and V^T
+//   gather_partial -- one work item = up to 256 pairs of one bucket: K and V^T
 //                     of the block in LDS, the pairs' query rows gathered into
 //                     MFMA operands, S^T = K Q^T and O^T = V^T P^T on MFMA,
 //                     partial (m, l, o) out.  Work items are laid out so that
@@ -44,7 +44,7 @@
 namespace bsa {
 namespace {
 
-constexpr int kItemPairs = 256;  // pairs per work item (16 groups of 16)
+constexpr int kItemPairs = kGatherItemPairs;  // pairs per work item (16 groups of 16)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kXcds = 8;
 
@@ -121,7 +121,7 @@ constexpr int kScanRun = 16;
 __global__ __launch_bounds__(1024) void bucket_scan_kernel(const int32_t* __restrict__ count,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ items,
-                                                           int nbuckets) {
+                                                           int nbuckets, int item_pairs) {
   constexpr int PASS = 1024 * kScanRun, RP = kScanRun + 1;
   __shared__ int32_t s_c[1024 * RP], s_i[1024 * RP];
   __shared__ int32_t s_wp[16], s_wi[16], s_tot[2];
@@ -139,7 +139,7 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const int32_t* __rest
     for (int j = 0; j < kScanRun; ++j) {
       v[j] = s_c[t * RP + j];
       sp += v[j];
-      si += (v[j] + kItemPairs - 1) / kItemPairs;
+      si += (v[j] + item_pairs - 1) / item_pairs;
     }
     const int32_t ip = wave_incl_scan(sp, lane), ii = wave_incl_scan(si, lane);
     if (lane == 63) {
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const int32_t* __rest
       s_c[t * RP + j] = ep;
       s_i[t * RP + j] = ei;
       ep += v[j];
-      ei += (v[j] + kItemPairs - 1) / kItemPairs;
+      ei += (v[j] + item_pairs - 1) / item_pairs;
     }
     carry_p += s_tot[0];
     carry_i += s_tot[1];
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ items,
     int4* __restrict__ item_rec, int nbuckets, int64_t max_slots, int32_t* __restrict__ list,
-    int64_t row0, int64_t npairs, int n, int topk, int64_t bh0, int qsegs) {
+    int64_t row0, int64_t npairs, int n, int topk, int64_t bh0, int qsegs, int item_pairs) {
   const int64_t p = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (p < nbuckets) {
     const int32_t total = items[nbuckets];
@@ -204,10 +204,10 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(
     const int32_t cnt = offsets[p + 1] - offsets[p];
     for (int32_t i = items[p], u = 0; i < items[p + 1]; ++i, ++u) {
       const int64_t slot = static_cast<int64_t>(i % per_xcd) * kXcds + i / per_xcd;
-      const int32_t left = cnt - u * kItemPairs;
+      const int32_t left = cnt - u * item_pairs;
       if (slot < max_slots)
-        item_rec[slot] = make_int4(static_cast<int32_t>(p), offsets[p] + u * kItemPairs,
-                                   left < kItemPairs ? left : kItemPairs, 0);
+        item_rec[slot] = make_int4(static_cast<int32_t>(p), offsets[p] + u * item_pairs,
+                                   left < item_pairs ? left : item_pairs, 0);
     }
   }
   if (p >= npairs) return;
@@ -497,8 +497,9 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ idx,
                                                       const PartialT<T>* __restrict__ po,
                                                       const float2* __restrict__ pml,
-                                                      float* __restrict__ out, int64_t row0,
-                                                      int64_t rows, int n, int topk, int causal) {
+                                                      float* __restrict__ out, float* __restrict__ lse,
+                                                      int64_t row0, int64_t rows, int n, int topk,
+                                                      int causal) {
   constexpr int E = D / 16;  // dims per lane
   constexpr int V = E / 4;   // 4-element loads per lane and slot
   typedef typename std::conditional<sizeof(T) == 2, f16x4, f32x4>::type Vec;
@@ -550,6 +551,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off, 16);
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  // log-sum-exp of the row's scaled scores, natural log: the partial maxima
+  // are in log2 units, so lse = (M + log2 sum_s w_s) / log2(e).
+  if (lse && c == 0) lse[row] = wsum > 0.f ? (mmax + __log2f(wsum)) * (1.0f / kLog2e) : -INFINITY;
   float* dst = out + row * D + c * E;
 #pragma unroll
   for (int e = 0; e < E; e += 4)
@@ -571,8 +575,9 @@ struct ChunkGeom {
 
 template <typename T, int D>
 hipError_t partial_chunk(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
+  if (a.item_pairs != kItemPairs) return hipErrorInvalidValue;  // items made for another kernel
   const ChunkGeom c(a, row0, rows);
-  const int64_t grid = gather_grid(rows, a.topk, c.nbuckets);
+  const int64_t grid = gather_grid(rows, a.topk, c.nbuckets, kItemPairs);
   const float sl2 = a.scale * kLog2e;
   auto* po = reinterpret_cast<PartialT<T>*>(a.ws.partial_o);
   // pair / topk as (pair * magic) >> shift: shift = 32 + ceil(log2 topk),
@@ -598,14 +603,14 @@ template <typename T, int D>
 hipError_t combine_chunk(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
   auto* po = reinterpret_cast<const PartialT<T>*>(a.ws.partial_o);
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0,
-                     s, a.idx, po, a.ws.partial_ml, a.out, row0, rows, a.n, a.topk, a.causal);
+                     s, a.idx, po, a.ws.partial_ml, a.out, a.lse, row0, rows, a.n, a.topk, a.causal);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int64_t gather_grid(int64_t rows, int topk, int64_t nbuckets) {
-  const int64_t max_items = (rows * topk + kItemPairs - 1) / kItemPairs + nbuckets;
+int64_t gather_grid(int64_t rows, int topk, int64_t nbuckets, int item_pairs) {
+  const int64_t max_items = (rows * topk + item_pairs - 1) / item_pairs + nbuckets;
   return (max_items + kXcds - 1) / kXcds * kXcds;
 }
 
@@ -639,12 +644,12 @@ hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, 
                      dim3(256), static_cast<size_t>(c.nb) * 8, s, a.idx, a.ws.count, a.ws.rank, row0,
                      rows, a.n, a.topk, a.causal, c.bh0, rpw, a.qsegs);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, a.ws.count, a.ws.offsets,
-                     a.ws.items, c.nbuckets);
+                     a.ws.items, c.nbuckets, a.item_pairs);
   const int64_t nthreads = c.npairs > c.nbuckets ? c.npairs : c.nbuckets;
   hipLaunchKernelGGL(bucket_fill_kernel, dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256),
                      0, s, a.idx, a.ws.rank, a.ws.offsets, a.ws.items, a.ws.item_rec, c.nbuckets,
-                     gather_grid(rows, a.topk, c.nbuckets), a.ws.list, row0, c.npairs, a.n, a.topk,
-                     c.bh0, a.qsegs);
+                     gather_grid(rows, a.topk, c.nbuckets, a.item_pairs), a.ws.list, row0, c.npairs,
+                     a.n, a.topk, c.bh0, a.qsegs, a.item_pairs);
   return hipGetLastError();
 }
 

@@ -150,7 +150,7 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const T* ks, const T*
 template <typename T, int D, bool STATIC, bool CAUSAL>
 __global__ __launch_bounds__(256) void sparse_flash_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    float* __restrict__ out, const int32_t* __restrict__ idx, int topk,
+    float* __restrict__ out, float* __restrict__ lse, const int32_t* __restrict__ idx, int topk,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
     const uint64_t* __restrict__ rowmask, int64_t nnz, int n, float scale_log2) {
   using L = KvLayout<T, D>;
@@ -288,6 +288,8 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
   float lt = st.l + __shfl_xor(st.l, 16);
   lt += __shfl_xor(lt, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (lse && g == 0)  // natural-log log-sum-exp; st.m is in log2 units
+    lse[qrow] = lt > 0.f ? (st.m + __log2f(lt)) * (1.0f / kLog2e) : -INFINITY;
   float* op = out + qrow * D + 4 * g;
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) {
@@ -297,8 +299,8 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
 }
 
 template <typename T, int D, bool STATIC, bool CAUSAL>
-hipError_t launch_one(const void* q, const void* k, const void* v, float* out, const int32_t* idx,
-                      int topk, const int32_t* row_ptr, const int32_t* col,
+hipError_t launch_one(const void* q, const void* k, const void* v, float* out, float* lse,
+                      const int32_t* idx, int topk, const int32_t* row_ptr, const int32_t* col,
                       const uint64_t* rowmask, int64_t nnz, int64_t bh, int n, float scale,
                       hipStream_t s) {
   using L = KvLayout<T, D>;
@@ -314,32 +316,32 @@ hipError_t launch_one(const void* q, const void* k, const void* v, float* out, c
   }
   const dim3 grid(static_cast<unsigned>(bh * (n / kTile)));
   hipLaunchKernelGGL(kern, grid, dim3(256), smem, s, static_cast<const T*>(q),
-                     static_cast<const T*>(k), static_cast<const T*>(v), out, idx, topk, row_ptr,
+                     static_cast<const T*>(k), static_cast<const T*>(v), out, lse, idx, topk, row_ptr,
                      col, rowmask, nnz, n, scale * kLog2e);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t dispatch_dynamic(const void* q, const void* k, const void* v, float* out,
+hipError_t dispatch_dynamic(const void* q, const void* k, const void* v, float* out, float* lse,
                             const int32_t* idx, int64_t bh, int n, int topk, float scale,
                             int causal, hipStream_t s) {
-  return causal ? launch_one<T, D, false, true>(q, k, v, out, idx, topk, nullptr, nullptr, nullptr,
-                                                0, bh, n, scale, s)
-                : launch_one<T, D, false, false>(q, k, v, out, idx, topk, nullptr, nullptr,
+  return causal ? launch_one<T, D, false, true>(q, k, v, out, lse, idx, topk, nullptr, nullptr,
+                                                nullptr, 0, bh, n, scale, s)
+                : launch_one<T, D, false, false>(q, k, v, out, lse, idx, topk, nullptr, nullptr,
                                                  nullptr, 0, bh, n, scale, s);
 }
 
 }  // namespace
 
 hipError_t launch_sparse_flash_dynamic(const void* q, const void* k, const void* v, float* out,
-                                       const int32_t* idx, int64_t bh, int n, int d, int topk,
-                                       float scale, int causal, bsa_dtype dtype,
+                                       float* lse, const int32_t* idx, int64_t bh, int n, int d,
+                                       int topk, float scale, int causal, bsa_dtype dtype,
                                        hipStream_t stream) {
   if (dtype == BSA_BF16)
-    return d == 64 ? dispatch_dynamic<bf16_bits, 64>(q, k, v, out, idx, bh, n, topk, scale, causal, stream)
-                   : dispatch_dynamic<bf16_bits, 128>(q, k, v, out, idx, bh, n, topk, scale, causal, stream);
-  return d == 64 ? dispatch_dynamic<float, 64>(q, k, v, out, idx, bh, n, topk, scale, causal, stream)
-                 : dispatch_dynamic<float, 128>(q, k, v, out, idx, bh, n, topk, scale, causal, stream);
+    return d == 64 ? dispatch_dynamic<bf16_bits, 64>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream)
+                   : dispatch_dynamic<bf16_bits, 128>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream);
+  return d == 64 ? dispatch_dynamic<float, 64>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream)
+                 : dispatch_dynamic<float, 128>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream);
 }
 
 hipError_t launch_sparse_flash_static(const void* q, const void* k, const void* v, float* out,
@@ -347,13 +349,13 @@ hipError_t launch_sparse_flash_static(const void* q, const void* k, const void* 
                                       const uint64_t* rowmask, int64_t nnz, int64_t bh, int n,
                                       int d, float scale, bsa_dtype dtype, hipStream_t stream) {
   if (dtype == BSA_BF16)
-    return d == 64 ? launch_one<bf16_bits, 64, true, false>(q, k, v, out, nullptr, 0, row_ptr, col,
+    return d == 64 ? launch_one<bf16_bits, 64, true, false>(q, k, v, out, nullptr, nullptr, 0, row_ptr, col,
                                                             rowmask, nnz, bh, n, scale, stream)
-                   : launch_one<bf16_bits, 128, true, false>(q, k, v, out, nullptr, 0, row_ptr, col,
+                   : launch_one<bf16_bits, 128, true, false>(q, k, v, out, nullptr, nullptr, 0, row_ptr, col,
                                                              rowmask, nnz, bh, n, scale, stream);
-  return d == 64 ? launch_one<float, 64, true, false>(q, k, v, out, nullptr, 0, row_ptr, col,
+  return d == 64 ? launch_one<float, 64, true, false>(q, k, v, out, nullptr, nullptr, 0, row_ptr, col,
                                                       rowmask, nnz, bh, n, scale, stream)
-                 : launch_one<float, 128, true, false>(q, k, v, out, nullptr, 0, row_ptr, col,
+                 : launch_one<float, 128, true, false>(q, k, v, out, nullptr, nullptr, 0, row_ptr, col,
                                                        rowmask, nnz, bh, n, scale, stream);
 }
 

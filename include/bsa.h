@@ -67,7 +67,11 @@ typedef enum {
   BSA_STAGE_GATHER_INDEX = 4,   /* block-gather: bucketing of (query, block) pairs */
   BSA_STAGE_GATHER_COMBINE = 5, /* block-gather: merge of per-block partials       */
   BSA_STAGE_COARSE_TOPK = 6,    /* coarse_score and topk_select fused in one kernel  */
-  BSA_NUM_STAGES = 7
+  BSA_STAGE_BWD_PREP = 7,       /* backward: per-row lse and delta = dout . out      */
+  BSA_STAGE_BWD_INDEX = 8,      /* backward: bucketing of (query, block) pairs       */
+  BSA_STAGE_BWD_PAIRS = 9,      /* backward: the MFMA pair kernel (dq, dk, dv parts) */
+  BSA_STAGE_BWD_REDUCE = 10,    /* backward: sums of the dq and dk/dv contributions  */
+  BSA_NUM_STAGES = 11
 } bsa_stage;
 
 /* How the dynamic fine stage visits the selected blocks. */
@@ -178,6 +182,52 @@ bsa_status bsa_forward_budgets(bsa_handle h, const void* q, const void* k,
                                bsa_dtype dtype, int block,
                                const int32_t* head_topk, int topk_max,
                                float scale, int causal, void* stream);
+
+/* ------------------------------------------------------------ training -- */
+
+/* The forward for training: bsa_forward (or bsa_forward_budgets) that also
+ * stores what bsa_backward needs.
+ *  block_idx_out  device, int32 [batch][heads][n][topk], required.
+ *  lse_out        device, float32 [batch][heads][n], required, 4-byte aligned:
+ *                 per query row log(sum_j exp(scale * q.k_j)) over its visible
+ *                 keys (natural log).
+ *  head_topk      host, int32 [heads], or NULL for topk on every head; as in
+ *                 bsa_forward_budgets with topk_max = topk.
+ * Everything else as for bsa_forward. */
+bsa_status bsa_forward_train(bsa_handle h, const void* q, const void* k,
+                             const void* v, float* out, int32_t* block_idx_out,
+                             float* lse_out, int batch, int heads, int n, int d,
+                             bsa_dtype dtype, int block, const int32_t* head_topk,
+                             int topk, float scale, int causal, void* stream);
+
+/* Backward of the fine stage (nishantmodi.me "sparse-attention-triton-bench",
+ * section "What's next": a backward pass through the softmax-weighted sum over
+ * the selected blocks, FlashAttention-2's backward as the dense model).  The
+ * selection is a discrete choice and gets no gradient: block_idx is held
+ * fixed, and q, k, v get the gradients of softmax attention over each row's
+ * visible keys (its selected blocks; j <= i when causal):
+ *   dq_i = scale sum_j ds_ij k_j,  dk_j = scale sum_i ds_ij q_i,
+ *   dv_j = sum_i p_ij dout_i,  ds_ij = p_ij (dout_i . v_j - dout_i . out_i),
+ * with p_ij = exp(scale q_i.k_j - lse_i) recomputed from lse.
+ *  q, k, v        device, as passed to bsa_forward_train.
+ *  out, lse, block_idx  device, as written by bsa_forward_train for the same
+ *                 q, k, v, topk, scale and causal (row length topk).
+ *  dout           device, float32 [batch][heads][n][d]: gradient of out.
+ *  dq, dk, dv     device, float32 [batch][heads][n][d], written (every
+ *                 element; keys no row sees get 0).
+ * Pointers 16-byte aligned except block_idx and lse (4).  No floating-point
+ * atomics: dq is the same bit for bit on every call (each (query, block)
+ * contribution is computed alone and they are summed in slot order); dk and
+ * dv sum the pairs of a key block in the order the bucketing lists them,
+ * which its integer atomics set, so two calls can differ in the last bits.
+ * Workspace grows with topk * n (bounded by BSA_OPT_FINE_CHUNK_BYTES, the
+ * rows being processed in chunks). */
+bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, const void* v,
+                        const float* out, const float* dout,
+                        const int32_t* block_idx, const float* lse, float* dq,
+                        float* dk, float* dv, int batch, int heads, int n, int d,
+                        bsa_dtype dtype, int block, int topk, float scale,
+                        int causal, void* stream);
 
 /* Stage 2 alone on caller-supplied selections (same layout as block_idx_out;
  * each row must hold distinct indices; entries outside [0, n/block), and in

@@ -14,6 +14,8 @@ Recipe (the same for every workload; all batch = 1):
       off = rng.normal(0, 0.5, [b, h, n/B, d]) -> float32
       k += off repeated over the B keys of each block   (in float32)
   if dtype == bf16: round q, k, v to bf16, nearest-even
+Backward workloads add an incoming gradient of the float32 output:
+  dout = default_rng(seed + 1000).standard_normal([b, h, n, d], float32)
 """
 from __future__ import annotations
 
@@ -125,3 +127,9 @@ def generate(w: Workload | str, *, n: int | None = None, heads: int | None = Non
         v, vb = bf16_round(v)
         return Inputs(q, k, v, qb, kb, vb)
     return Inputs(q, k, v)
+
+
+def grad_output(shape, seed: int) -> np.ndarray:
+    """The incoming gradient dout for a backward workload: float32 N(0, 1)."""
+    rng = np.random.default_rng(seed + 1000)
+    return rng.standard_normal(tuple(shape), dtype=np.float32)
