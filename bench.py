@@ -9,7 +9,12 @@ TFLOP/s, the roofline of the dominant kernel (timed with HIP events on the
 launch stream inside this run) and the fp64 CPU oracle's throughput on a
 bounded sample of the same workload.
 
+With --pass backward a step is one bsa_backward (dq, dk, dv of the fine stage
+for the selection, output and lse of one bsa_forward_train made before the
+timed region) and the line reports backward tokens/s.
+
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--pass forward|backward]
 """
 from __future__ import annotations
 
@@ -27,6 +32,7 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 METRIC = "fwd tokens/s and effective TFLOP/s at N=32k,H=8,D=64,B=64,k=16; % roofline"
+METRIC_BWD = "bwd tokens/s (fine-stage dq, dk, dv; selection fixed) and effective TFLOP/s; % roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
 def visible_pairs(w: W.Workload) -> int:
@@ -73,6 +79,16 @@ def stage_work(w: W.Workload):
         "sparse_flash_fwd": ("mfma", fine_flops, 3 * qkv + idx + partial),
         "gather_index": ("hbm", 0, 2 * idx + 3 * sel_pairs * 4),
         "gather_combine": ("hbm", 0, partial + idx + out_b),
+        # backward: out, dout and lse in, per-row (lse, delta) out
+        "bwd_prep": ("hbm", 0, 2 * out_b + w.bh * w.n * (4 + 8)),
+        "bwd_index": ("hbm", 0, 2 * idx + 3 * sel_pairs * 4),
+        # S, dP, dQ, dK, dV: five products per visible (query, key) pair;
+        # reads Q, K, V, dout (fp32) and the row statistics once, writes the
+        # per-pair dq rows
+        "bwd_pairs": ("mfma", 10 * w.d * visible_pairs(w),
+                      3 * qkv + out_b + w.bh * w.n * 8 + sel_pairs * w.d * 4),
+        # per-pair dq rows in, dq, dk, dv out
+        "bwd_reduce": ("hbm", 0, sel_pairs * w.d * 4 + idx + 3 * out_b),
     }
 
 
@@ -105,6 +121,24 @@ def cpu_baseline(w: W.Workload, inp, positions: int):
                       f"{dt:.2f} s wall"}
 
 
+def cpu_baseline_backward(w: W.Workload, inp, dout):
+    """The oracle's backward over one head (all its rows and key blocks),
+    scaled to all heads."""
+    import oracle
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    r = oracle.pool(inp.k[:, :1], w.block)
+    sc = oracle.scores(inp.q[:, :1], r, w.block)
+    idx, _, _ = oracle.topk(sc, w.n, w.block, w.topk, w.causal)
+    t0 = time.perf_counter()
+    oracle.attend_backward(inp.q[:, :1], inp.k[:, :1], inp.v[:, :1], dout[:, :1], idx, w.block,
+                           w.causal, w.scale)
+    dt = time.perf_counter() - t0
+    return {"value": w.n * w.batch / (dt * w.heads), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"head 0 of {w.heads} (all {w.n} rows, all key blocks): dq, dk, dv, lse in "
+                      f"fp64 on the oracle's own selection; {dt:.2f} s wall, scaled to {w.heads} heads"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +151,7 @@ def main():
     ap.add_argument("--select-strategy", choices=["fused", "panel"], default="fused")
     ap.add_argument("--panel-chunk-mb", type=int, default=0, help="coarse-score panel chunk (0 = default)")
     ap.add_argument("--fine-chunk-mb", type=int, default=0, help="block-gather partial chunk (0 = default)")
+    ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB -> 1 GiB device copy (3 times), the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -163,8 +198,18 @@ def main():
     if args.fine_chunk_mb:
         m.bsa_set_option(h, m.BSA_OPT_FINE_CHUNK_BYTES, args.fine_chunk_mb << 20)
 
-    def step():
-        m.bsa_forward(h, q, k, v, out, idx, topk=w.topk, scale=w.scale, causal=w.causal)
+    if args.which == "forward":
+        def step():
+            m.bsa_forward(h, q, k, v, out, idx, topk=w.topk, scale=w.scale, causal=w.causal)
+    else:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        m.bsa_forward_train(h, q, k, v, out, idx, lse, topk=w.topk, scale=w.scale, causal=w.causal)
+        dout_np = W.grad_output(q.shape, w.seed)
+        dout = torch.from_numpy(dout_np).to(dev)
+        dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+
+        def step():
+            m.bsa_backward(h, q, k, v, out, dout, idx, lse, dq, dk, dv, scale=w.scale, causal=w.causal)
 
     for _ in range(args.warmup):
         step()
@@ -211,7 +256,7 @@ def main():
     total_flops = sum(work[k_][1] for k_ in per_step)  # matmul-only: coarse + fine, stages that ran
     tokens = w.batch * w.n
     result = {
-        "metric": METRIC,
+        "metric": METRIC if args.which == "forward" else METRIC_BWD,
         "value": round(tokens / (ms_per_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -227,14 +272,16 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n": w.n, "d": w.d,
                    "block": w.block, "topk": w.topk, "causal": w.causal,
                    "select_strategy": args.select_strategy, "fine_strategy": args.fine_strategy,
-                   "panel_chunk_mb": args.panel_chunk_mb or 128, "fine_chunk_mb": args.fine_chunk_mb or 1024},
+                   "panel_chunk_mb": args.panel_chunk_mb or 128, "fine_chunk_mb": args.fine_chunk_mb or 1024,
+                   "pass": args.which},
         "effective_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 3),
         "algorithmic_gflop": round(total_flops / 1e9, 3),
         "stage_ms_per_step": {k_: round(v_, 5) for k_, v_ in per_step.items()},
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_positions)
+        result["cpu_baseline"] = (cpu_baseline(w, inp, args.cpu_positions) if args.which == "forward"
+                                  else cpu_baseline_backward(w, inp, dout_np))
     lib.close()
     print(json.dumps(result), flush=True)
 

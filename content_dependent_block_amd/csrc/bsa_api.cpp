@@ -602,7 +602,7 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int64_t total = s.bh() * s.n;
   const int64_t align = (s.n % 256 == 0) ? 256 : 64;  // keeps bucketing workgroups inside one head
-  const size_t per_row = size_t(topk) * (size_t(s.d) * 4 + 8);
+  const size_t per_row = size_t(topk) * size_t(s.d) * 4;  // the per-pair dq rows
   int64_t chunk = h->fine_chunk_bytes / int64_t(per_row) / align * align;
   if (chunk < align) chunk = align;
   if (chunk > total) chunk = total;

@@ -89,8 +89,15 @@ struct BwdLayout {
   static constexpr int OFF_V = K_BYTES;
   static constexpr int OFF_KT = 2 * K_BYTES;
   static constexpr int OFF_P = OFF_KT + KT_BYTES;
-  static constexpr int OFF_O = OFF_P + P_BYTES;
-  static constexpr int BYTES = OFF_O + O_BYTES;
+  // Dual: separate buffers for the dV operands (P^T, dO) and the dK operands
+  // (dS^T, Q), so a tile needs two barriers instead of four; used when both
+  // fit in the 160 KB of a CU's LDS.
+  static constexpr int SINGLE = OFF_P + P_BYTES + O_BYTES;
+  static constexpr bool kDual = SINGLE + P_BYTES + O_BYTES <= 160 * 1024;
+  static constexpr int OFF_P2 = OFF_P + P_BYTES;                   // dual only
+  static constexpr int OFF_O = OFF_P + (kDual ? 2 : 1) * P_BYTES;
+  static constexpr int OFF_O2 = OFF_O + O_BYTES;                   // dual only
+  static constexpr int BYTES = OFF_O + (kDual ? 2 : 1) * O_BYTES;
 };
 
 // K and V of one key block into LDS (K natural and, for bf16, transposed;
@@ -142,40 +149,75 @@ struct PairRows {
   float of[kBf16 ? 1 : D / 4];
 };
 
+// Raw inputs of the lane's pair for one tile, loaded a tile ahead of use:
+// its query row and incoming-gradient row (the lane's dims as above), the
+// row statistics, the row and the pair id.
 template <typename T, int D>
-__device__ __forceinline__ void load_rows(PairRows<T, D>& pr, const T* __restrict__ q,
-                                          const float* __restrict__ dout, int64_t row, bool live,
-                                          int g) {
+struct PairIn {
+  static constexpr int NQ = sizeof(T) == 2 ? D / 32 : D / 16;  // 16-byte pieces of q
+  uint4 q[NQ];
+  float4 o[D / 16];  // bf16: pieces 2kk, 2kk + 1 = dims 32kk + 8g .. +7; fp32: (D/4) g + 4i
+  float2 lr;
+  int64_t row;
+  int32_t pair;
+  bool live;
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void fetch(PairIn<T, D>& x, const T* __restrict__ q,
+                                      const float* __restrict__ dout, const float2* __restrict__ ld,
+                                      int32_t entry, bool live, int64_t row0, int64_t npairs,
+                                      uint64_t div_magic, int div_shift, int g) {
+  if (entry < 0 || entry >= npairs) live = false;
+  x.live = live;
+  x.pair = live ? entry : 0;
+  x.row = row0 + static_cast<int64_t>((static_cast<uint64_t>(x.pair) * div_magic) >> div_shift);
+#pragma unroll
+  for (int i = 0; i < PairIn<T, D>::NQ; ++i) x.q[i] = uint4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < D / 16; ++i) x.o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (live) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int kk = 0; kk < D / 32; ++kk) {
+        const int d0 = 32 * kk + 8 * g;
+        x.q[kk] = ld16(q + x.row * D + d0);
+        x.o[2 * kk] = *reinterpret_cast<const float4*>(dout + x.row * D + d0);
+        x.o[2 * kk + 1] = *reinterpret_cast<const float4*>(dout + x.row * D + d0 + 4);
+      }
+    } else {
+      constexpr int KS = D / 4;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) {
+        x.q[i] = ld16(q + x.row * D + KS * g + 4 * i);
+        x.o[i] = *reinterpret_cast<const float4*>(dout + x.row * D + KS * g + 4 * i);
+      }
+    }
+  }
+  x.lr = live ? ld[x.row] : make_float2(0.f, 0.f);
+}
+
+template <typename T, int D>
+__device__ __forceinline__ void ready(PairRows<T, D>& pr, const PairIn<T, D>& x) {
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-      const int d0 = 32 * kk + 8 * g;
-      pr.qb[kk] = live ? as_bf16x8(ld16(q + row * D + d0)) : bf16x8{};
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-      if (live) {
-        a = *reinterpret_cast<const float4*>(dout + row * D + d0);
-        b = *reinterpret_cast<const float4*>(dout + row * D + d0 + 4);
-      }
+      pr.qb[kk] = as_bf16x8(x.q[kk]);
+      const float4 a = x.o[2 * kk], b = x.o[2 * kk + 1];
       pr.ob[kk] = bf16x8{f32_to_bf16(a.x), f32_to_bf16(a.y), f32_to_bf16(a.z), f32_to_bf16(a.w),
                          f32_to_bf16(b.x), f32_to_bf16(b.y), f32_to_bf16(b.z), f32_to_bf16(b.w)};
     }
   } else {
-    constexpr int KS = D / 4;
 #pragma unroll
-    for (int e = 0; e < KS; e += 4) {
-      float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-      if (live) {
-        a = *reinterpret_cast<const float4*>(q + row * D + KS * g + e);
-        b = *reinterpret_cast<const float4*>(dout + row * D + KS * g + e);
-      }
-      pr.qf[e] = a.x;
-      pr.qf[e + 1] = a.y;
-      pr.qf[e + 2] = a.z;
-      pr.qf[e + 3] = a.w;
-      pr.of[e] = b.x;
-      pr.of[e + 1] = b.y;
-      pr.of[e + 2] = b.z;
-      pr.of[e + 3] = b.w;
+    for (int i = 0; i < D / 16; ++i) {
+      pr.qf[4 * i] = __uint_as_float(x.q[i].x);
+      pr.qf[4 * i + 1] = __uint_as_float(x.q[i].y);
+      pr.qf[4 * i + 2] = __uint_as_float(x.q[i].z);
+      pr.qf[4 * i + 3] = __uint_as_float(x.q[i].w);
+      pr.of[4 * i] = x.o[i].x;
+      pr.of[4 * i + 1] = x.o[i].y;
+      pr.of[4 * i + 2] = x.o[i].z;
+      pr.of[4 * i + 3] = x.o[i].w;
     }
   }
 }
@@ -265,18 +307,24 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
   __syncthreads();
 
   const int ntiles = (cnt + 63) / 64;  // workgroup-uniform
+  // Inputs run one tile ahead of the compute (list entries two tiles ahead),
+  // so the gathered rows of tile it + 1 load while tile it computes.
+  const int tl = 16 * wave + c16;  // the lane's pair position inside a tile
+  int32_t ent = tl + 64 < cnt ? list[first + tl + 64] : 0;
+  PairIn<T, D> cur;
+  fetch<T, D>(cur, q, dout, ld, tl < cnt ? list[first + tl] : 0, tl < cnt, row0, npairs, div_magic,
+              div_shift, g);
   for (int it = 0; it < ntiles; ++it) {
-    const int t = it * 64 + 16 * wave + c16;
-    bool live = t < cnt;
-    int32_t pair = live ? list[first + t] : 0;
-    if (pair < 0 || pair >= npairs) {
-      pair = 0;
-      live = false;
-    }
-    const int64_t row = row0 + static_cast<int64_t>((static_cast<uint64_t>(pair) * div_magic) >> div_shift);
+    PairIn<T, D> nxt;
+    const int tn = (it + 1) * 64 + tl;
+    fetch<T, D>(nxt, q, dout, ld, ent, tn < cnt, row0, npairs, div_magic, div_shift, g);
+    ent = tn + 64 < cnt ? list[first + tn + 64] : 0;
+    const bool live = cur.live;
+    const int32_t pair = cur.pair;
+    const int64_t row = cur.row;
+    const float2 lr = cur.lr;
     PairRows<T, D> pr;
-    load_rows<T, D>(pr, q, dout, row, live, g);
-    const float2 lr = live ? ld[row] : make_float2(0.f, 0.f);
+    ready<T, D>(pr, cur);
 
     f32x4 s[4], dp[4];
     scores<T, D>(ks, vs, pr, s, dp, g, c16);
@@ -344,60 +392,82 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
       }
     }
 
-    // dV += P^T dO, then dK += dS^T Q, over the tile's 64 pairs.
-#pragma unroll
-    for (int phase = 0; phase < 2; ++phase) {
-      const int col = 16 * wave + c16;  // the lane's pair column in the tile
+    // dV += P^T dO and dK += dS^T Q over the tile's 64 pairs: the lane's
+    // column of P^T (or dS^T) and of dO (or Q) into LDS, then each wave's 16
+    // keys against all 64 pairs.
+    const int col = 16 * wave + c16;  // the lane's pair column in the tile
+    auto put = [&](T* pbuf, T* obuf, int phase) {
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           const float x = phase == 0 ? pv[tt][jj] : dsv[tt][jj];
           if constexpr (L::kBf16)
-            reinterpret_cast<__bf16*>(pt)[(16 * tt + 4 * g + jj) * L::PP + col] = f32_to_bf16(x);
+            reinterpret_cast<__bf16*>(pbuf)[(16 * tt + 4 * g + jj) * L::PP + col] = f32_to_bf16(x);
           else
-            pt[(16 * tt + 4 * g + jj) * L::PP + col] = x;
+            pbuf[(16 * tt + 4 * g + jj) * L::PP + col] = x;
         }
       if constexpr (L::kBf16) {
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk)
 #pragma unroll
           for (int i = 0; i < 8; ++i)
-            reinterpret_cast<__bf16*>(ot)[(32 * kk + 8 * g + i) * L::PP + col] =
+            reinterpret_cast<__bf16*>(obuf)[(32 * kk + 8 * g + i) * L::PP + col] =
                 phase == 0 ? pr.ob[kk][i] : pr.qb[kk][i];
       } else {
         constexpr int KS = D / 4;
-        float* orow = reinterpret_cast<float*>(ot) + col * L::KP + KS * g;
+        float* orow = reinterpret_cast<float*>(obuf) + col * L::KP + KS * g;
 #pragma unroll
         for (int e = 0; e < KS; e += 4) {
-          const float* src = phase == 0 ? pr.of : pr.qf;
-          *reinterpret_cast<float4*>(orow + e) = make_float4(src[e], src[e + 1], src[e + 2], src[e + 3]);
+          if (phase == 0)
+            *reinterpret_cast<float4*>(orow + e) = make_float4(pr.of[e], pr.of[e + 1], pr.of[e + 2], pr.of[e + 3]);
+          else
+            *reinterpret_cast<float4*>(orow + e) = make_float4(pr.qf[e], pr.qf[e + 1], pr.qf[e + 2], pr.qf[e + 3]);
         }
       }
-      __syncthreads();
-      f32x4* out = phase == 0 ? dv : dk;
+    };
+    auto mul = [&](const T* pbuf, const T* obuf, f32x4(&acc)[D / 16]) {
       if constexpr (L::kBf16) {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(pt + (16 * wave + c16) * L::PP + 32 * kk + 8 * g);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(pbuf + (16 * wave + c16) * L::PP + 32 * kk + 8 * g);
 #pragma unroll
           for (int dt = 0; dt < D / 16; ++dt) {
-            const bf16x8 bb = *reinterpret_cast<const bf16x8*>(ot + (16 * dt + c16) * L::PP + 32 * kk + 8 * g);
-            out[dt] = mfma_16x16x32_bf16(a, bb, out[dt]);
+            const bf16x8 bb = *reinterpret_cast<const bf16x8*>(obuf + (16 * dt + c16) * L::PP + 32 * kk + 8 * g);
+            acc[dt] = mfma_16x16x32_bf16(a, bb, acc[dt]);
           }
         }
       } else {
-        const float* orows = reinterpret_cast<const float*>(ot);
+        const float* orows = reinterpret_cast<const float*>(obuf);
 #pragma unroll 4
         for (int st = 0; st < 16; ++st) {
-          const float a = pt[(16 * wave + c16) * L::PP + 4 * st + g];
+          const float a = pbuf[(16 * wave + c16) * L::PP + 4 * st + g];
 #pragma unroll
           for (int dt = 0; dt < D / 16; ++dt)
-            out[dt] = mfma_16x16x4_f32(a, orows[(4 * st + g) * L::KP + 16 * dt + c16], out[dt]);
+            acc[dt] = mfma_16x16x4_f32(a, orows[(4 * st + g) * L::KP + 16 * dt + c16], acc[dt]);
         }
       }
+    };
+    if constexpr (L::kDual) {
+      T* pt2 = reinterpret_cast<T*>(smem + L::OFF_P2);
+      T* ot2 = reinterpret_cast<T*>(smem + L::OFF_O2);
+      put(pt, ot, 0);
+      put(pt2, ot2, 1);
+      __syncthreads();
+      mul(pt, ot, dv);
+      mul(pt2, ot2, dk);
+      __syncthreads();
+    } else {
+      put(pt, ot, 0);
+      __syncthreads();
+      mul(pt, ot, dv);
+      __syncthreads();
+      put(pt, ot, 1);
+      __syncthreads();
+      mul(pt, ot, dk);
       __syncthreads();
     }
+    cur = nxt;
   }
 
   // The item's dk (scaled) and dv: [item][0 = dk, 1 = dv][64 keys][D].
@@ -413,37 +483,48 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
 }
 
 // dq[row] = sum over the row's valid slots, in slot order, of its pairs'
-// contributions.  16 lanes per row.
+// contributions.  16 lanes per row; 8 slots at a time, every lane issues the
+// loads of its D/16 dims of all 8 before adding any (slot index clamped into
+// the row so every load is in bounds; slots that are padding were never
+// written and are dropped by a select).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__ idx,
                                                      const float* __restrict__ dq_part,
                                                      float* __restrict__ dq, int64_t row0,
                                                      int64_t rows, int n, int topk, int causal) {
   constexpr int E = D / 16;
+  constexpr int V = E / 4;
+  constexpr int S = 8;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   if (r >= rows) return;
   const int c = threadIdx.x & 15;
   const int64_t row = row0 + r;
   const int nb = n / kTile;
-  float acc[E];
+  f32x4 acc[V];
 #pragma unroll
-  for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int s = 0; s < topk; ++s) {
-    if (!pair_valid(idx[row * topk + s], nb, row, n, causal)) continue;
-    const float* src = dq_part + (r * topk + s) * D + c * E;
+  for (int u = 0; u < V; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const float* src = dq_part + r * topk * D + c * E;
+  for (int s0 = 0; s0 < topk; s0 += S) {
+    f32x4 x[S][V];
+    bool ok[S];
 #pragma unroll
-    for (int e = 0; e < E; e += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(src + e);
-      acc[e] += x.x;
-      acc[e + 1] += x.y;
-      acc[e + 2] += x.z;
-      acc[e + 3] += x.w;
+    for (int t = 0; t < S; ++t) {
+      const int st = s0 + t < topk ? s0 + t : topk - 1;
+      ok[t] = s0 + t < topk && pair_valid(idx[row * topk + st], nb, row, n, causal);
+#pragma unroll
+      for (int u = 0; u < V; ++u)
+        x[t][u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(st) * D) + u);
     }
+#pragma unroll
+    for (int t = 0; t < S; ++t)
+#pragma unroll
+      for (int u = 0; u < V; ++u)
+        acc[u] += ok[t] ? x[t][u] : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   float* dst = dq + row * D + c * E;
 #pragma unroll
-  for (int e = 0; e < E; e += 4)
-    *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  for (int u = 0; u < V; ++u)
+    *reinterpret_cast<float4*>(dst + 4 * u) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
 }
 
 // dk, dv of one (head, key block): the sum of its work items over the
