@@ -70,8 +70,15 @@ __global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, 
   if (i < count) p[i] = 0;
 }
 
+// Pairs per thread the bucketing kernels keep in registers: a workgroup of
+// rpw rows holds rpw * topk <= 256 * kPairRegs pairs that way (all the
+// selection sizes up to 32 at rpw = 256); larger ones go through memory.
+constexpr int kPairRegs = 32;
+
 // One workgroup per `rpw` query rows of one query segment (rpw divides the
-// segment length and row0).
+// segment length and row0).  Each pair's rank inside its bucket is its
+// workgroup's base (one global atomic per (workgroup, block)) plus its rank
+// inside the workgroup (LDS atomics).
 __global__ __launch_bounds__(256) void bucket_count_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ count, int32_t* __restrict__ rank,
     int64_t row0, int64_t rows, int n, int topk, int causal, int64_t bh0, int rpw, int qsegs) {
@@ -83,21 +90,46 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
   const int npairs = static_cast<int>(nrows) * topk;
   const int64_t p_begin = (r_begin - row0) * topk;  // chunk-relative pair id of the first pair
   const int64_t bucket0 = bucket_of(r_begin, 0, n, nb, qsegs, bh0);  // rpw divides the segment
+  const int32_t* sel = idx + r_begin * topk;          // the workgroup's selections, contiguous
   for (int c = threadIdx.x; c < nb; c += 256) hist[c] = 0;
   __syncthreads();
+  if (npairs <= 256 * kPairRegs) {
+    int32_t lr[kPairRegs], bt[kPairRegs];
+#pragma unroll
+    for (int j = 0; j < kPairRegs; ++j) {
+      const int e = threadIdx.x + 256 * j;
+      lr[j] = -1;
+      bt[j] = 0;
+      if (e < npairs) {
+        const int beta = sel[e];
+        if (pair_valid(beta, nb, r_begin + e / topk, n, causal)) {
+          bt[j] = beta;
+          lr[j] = atomicAdd(&hist[beta], 1);
+        }
+      }
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < nb; c += 256)
+      base[c] = hist[c] ? atomicAdd(&count[bucket0 + c], hist[c]) : 0;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < kPairRegs; ++j) {
+      const int e = threadIdx.x + 256 * j;
+      if (e < npairs) rank[p_begin + e] = lr[j] >= 0 ? base[bt[j]] + lr[j] : -1;
+    }
+    return;
+  }
   for (int e = threadIdx.x; e < npairs; e += 256) {
-    const int64_t row = r_begin + e / topk;
-    const int beta = idx[row * topk + (e % topk)];
-    rank[p_begin + e] = pair_valid(beta, nb, row, n, causal) ? atomicAdd(&hist[beta], 1) : -1;
+    const int beta = sel[e];
+    rank[p_begin + e] = pair_valid(beta, nb, r_begin + e / topk, n, causal) ? atomicAdd(&hist[beta], 1) : -1;
   }
   __syncthreads();
   for (int c = threadIdx.x; c < nb; c += 256)
     base[c] = hist[c] ? atomicAdd(&count[bucket0 + c], hist[c]) : 0;
   __syncthreads();
   for (int e = threadIdx.x; e < npairs; e += 256) {
-    const int64_t row = r_begin + e / topk;
     const int32_t rk = rank[p_begin + e];
-    if (rk >= 0) rank[p_begin + e] = base[idx[row * topk + (e % topk)]] + rk;
+    if (rk >= 0) rank[p_begin + e] = base[sel[e]] + rk;
   }
 }
 
@@ -187,38 +219,116 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const int32_t* __rest
   }
 }
 
-// Pair ids into per-bucket lists.  Threads p < nbuckets also write, for each
-// work item of bucket p, the record {bucket, first list position, pair count}
-// at the slot of the workgroup that will run it: items are spread so that
-// consecutive items (one head, neighbouring blocks) go to one XCD, i.e.
-// item = xcd * per_xcd + j runs as workgroup j * 8 + xcd.
+// Exclusive prefix sum, in place, of s[0 .. m) in LDS (m <= 2048) by a
+// 256-thread workgroup; returns the total.  wt: 4 ints of LDS.
+__device__ __forceinline__ int32_t block_excl_scan(int32_t* s, int m, int32_t* wt) {
+  constexpr int P = 8;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int32_t v[P], sum = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    v[j] = t * P + j < m ? s[t * P + j] : 0;
+    sum += v[j];
+  }
+  const int32_t inc = wave_incl_scan(sum, lane);
+  if (lane == 63) wt[wave] = inc;
+  __syncthreads();
+  int32_t run = inc - sum, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) run += wt[w];
+    total += wt[w];
+  }
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    if (t * P + j < m) s[t * P + j] = run;
+    run += v[j];
+  }
+  __syncthreads();
+  return total;
+}
+
+// Pair ids into per-bucket lists, with the geometry of bucket_count (one
+// workgroup per rpw rows).  Within the workgroup the pairs are first ordered
+// by block in LDS, so the pairs of one bucket, whose list positions are
+// consecutive, leave in consecutive lanes of one store.  Workgroup w also
+// writes, for each work item of buckets 256w .. 256w + 255, the record
+// {bucket, first list position, pair count} at the slot of the workgroup
+// that will run it: items are spread so that consecutive items (one head,
+// neighbouring blocks) go to one XCD, i.e. item = xcd * per_xcd + j runs as
+// workgroup j * 8 + xcd.
 __global__ __launch_bounds__(256) void bucket_fill_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
     const int32_t* __restrict__ offsets, const int32_t* __restrict__ items,
     int4* __restrict__ item_rec, int nbuckets, int64_t max_slots, int32_t* __restrict__ list,
-    int64_t row0, int64_t npairs, int n, int topk, int64_t bh0, int qsegs, int item_pairs) {
-  const int64_t p = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (p < nbuckets) {
+    int64_t row0, int64_t rows, int n, int topk, int64_t bh0, int qsegs, int item_pairs, int rpw,
+    int cap) {
+  // LDS: [nb] counts / bases, [4] scan scratch, then the workgroup's pairs
+  // ordered by block: [cap] list positions, [cap] pair ids (cap >= its pairs
+  // whenever they fit the registers).
+  extern __shared__ int32_t sm[];
+  const int64_t pb = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (pb < nbuckets) {
     const int32_t total = items[nbuckets];
     const int32_t per_xcd = (total + kXcds - 1) / kXcds;
-    const int32_t cnt = offsets[p + 1] - offsets[p];
-    for (int32_t i = items[p], u = 0; i < items[p + 1]; ++i, ++u) {
+    const int32_t cnt = offsets[pb + 1] - offsets[pb];
+    for (int32_t i = items[pb], u = 0; i < items[pb + 1]; ++i, ++u) {
       const int64_t slot = static_cast<int64_t>(i % per_xcd) * kXcds + i / per_xcd;
       const int32_t left = cnt - u * item_pairs;
       if (slot < max_slots)
-        item_rec[slot] = make_int4(static_cast<int32_t>(p), offsets[p] + u * item_pairs,
+        item_rec[slot] = make_int4(static_cast<int32_t>(pb), offsets[pb] + u * item_pairs,
                                    left < item_pairs ? left : item_pairs, 0);
     }
   }
-  if (p >= npairs) return;
-  const int32_t rk = rank[p];
-  if (rk < 0) return;
+  const int64_t r_begin = row0 + static_cast<int64_t>(blockIdx.x) * rpw;
+  if (r_begin >= row0 + rows) return;  // workgroup-uniform: no rows here
   const int nb = n / kTile;
-  const int64_t row = row0 + p / topk;
-  const int beta = idx[row * topk + (p % topk)];
-  const int64_t b = bucket_of(row, beta, n, nb, qsegs, bh0);
-  const int64_t pos = static_cast<int64_t>(offsets[b]) + rk;
-  if (pos < npairs) list[pos] = static_cast<int32_t>(p);
+  const int64_t nrows = (row0 + rows - r_begin) < rpw ? (row0 + rows - r_begin) : rpw;
+  const int np = static_cast<int>(nrows) * topk;
+  const int64_t npairs = rows * topk;
+  const int64_t p_begin = (r_begin - row0) * topk;
+  const int32_t* off = offsets + bucket_of(r_begin, 0, n, nb, qsegs, bh0);  // rpw divides the segment
+  const int32_t* sel = idx + r_begin * topk;
+  if (np > 256 * kPairRegs || np > cap) {  // workgroup-uniform: plain scattered stores
+    for (int e = threadIdx.x; e < np; e += 256) {
+      const int32_t rk = rank[p_begin + e];
+      if (rk < 0) continue;
+      const int64_t pos = static_cast<int64_t>(off[sel[e]]) + rk;
+      if (pos < npairs) list[pos] = static_cast<int32_t>(p_begin + e);
+    }
+    return;
+  }
+  int32_t* cnt = sm;
+  int32_t* wt = sm + nb;
+  int32_t* spos = sm + nb + 4;
+  int32_t* spair = spos + cap;
+  for (int c = threadIdx.x; c < nb; c += 256) cnt[c] = 0;
+  __syncthreads();
+  int32_t lr[kPairRegs], bt[kPairRegs];
+#pragma unroll
+  for (int j = 0; j < kPairRegs; ++j) {
+    const int e = threadIdx.x + 256 * j;
+    lr[j] = -1;
+    bt[j] = 0;
+    if (e < np && rank[p_begin + e] >= 0) {
+      bt[j] = sel[e];
+      lr[j] = atomicAdd(&cnt[bt[j]], 1);
+    }
+  }
+  __syncthreads();
+  const int32_t valid = block_excl_scan(cnt, nb, wt);
+#pragma unroll
+  for (int j = 0; j < kPairRegs; ++j) {
+    const int e = threadIdx.x + 256 * j;
+    if (lr[j] >= 0) {
+      const int32_t si = cnt[bt[j]] + lr[j];
+      spos[si] = off[bt[j]] + rank[p_begin + e];
+      spair[si] = static_cast<int32_t>(p_begin + e);
+    }
+  }
+  __syncthreads();
+  for (int si = threadIdx.x; si < valid; si += 256)
+    if (spos[si] < npairs) list[spos[si]] = spair[si];
 }
 
 // bf16 inputs keep partial outputs as fp16 (|o| <= max |v|, relative error
@@ -645,11 +755,21 @@ hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, 
                      rows, a.n, a.topk, a.causal, c.bh0, rpw, a.qsegs);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, a.ws.count, a.ws.offsets,
                      a.ws.items, c.nbuckets, a.item_pairs);
-  const int64_t nthreads = c.npairs > c.nbuckets ? c.npairs : c.nbuckets;
-  hipLaunchKernelGGL(bucket_fill_kernel, dim3(static_cast<unsigned>((nthreads + 255) / 256)), dim3(256),
-                     0, s, a.idx, a.ws.rank, a.ws.offsets, a.ws.items, a.ws.item_rec, c.nbuckets,
-                     gather_grid(rows, a.topk, c.nbuckets, a.item_pairs), a.ws.list, row0, c.npairs,
-                     a.n, a.topk, c.bh0, a.qsegs, a.item_pairs);
+  const int64_t row_groups = (rows + rpw - 1) / rpw;
+  const int64_t bucket_groups = (c.nbuckets + 255) / 256;
+  const int cap = rpw * a.topk < 256 * kPairRegs ? rpw * a.topk : 256 * kPairRegs;
+  const size_t fill_lds = (static_cast<size_t>(c.nb) + 4 + 2 * static_cast<size_t>(cap)) * 4;
+  if (fill_lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bucket_fill_kernel),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             static_cast<int>(fill_lds));
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(bucket_fill_kernel,
+                     dim3(static_cast<unsigned>(row_groups > bucket_groups ? row_groups : bucket_groups)),
+                     dim3(256), fill_lds, s, a.idx, a.ws.rank, a.ws.offsets, a.ws.items, a.ws.item_rec,
+                     c.nbuckets, gather_grid(rows, a.topk, c.nbuckets, a.item_pairs), a.ws.list, row0, rows,
+                     a.n, a.topk, c.bh0, a.qsegs, a.item_pairs, rpw, cap);
   return hipGetLastError();
 }
 
