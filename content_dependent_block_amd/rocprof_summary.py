@@ -39,12 +39,16 @@ STAGE_SOURCES = {
     "sparse_flash_fwd": "fine_gather.hip",
     "gather_index": "fine_gather.hip",
     "gather_combine": "fine_gather.hip",
+    "bwd_prep": "fine_backward.hip",
+    "bwd_index": "fine_gather.hip",
+    "bwd_pairs": "fine_backward.hip",
+    "bwd_reduce": "fine_backward.hip",
 }
 
 _SHORT = re.compile(r"(gather_partial_kernel|combine_kernel|topk_lane_kernel|topk_wave_kernel|"
                     r"coarse_select_kernel|coarse_panel_kernel|bucket_count_kernel|bucket_scan_kernel|"
                     r"bucket_fill_kernel|block_pool_kernel|zero_i32_kernel|sparse_flash_kernel|"
-                    r"elementwise_kernel)")
+                    r"elementwise_kernel|bwd_prep_kernel|bwd_pair_kernel|bwd_dq_kernel|bwd_dkv_kernel)")
 
 
 def short(name: str) -> str:
