@@ -25,9 +25,11 @@ BSA_FP32, BSA_BF16 = 0, 1
 BSA_STAGE_POOL, BSA_STAGE_COARSE, BSA_STAGE_TOPK, BSA_STAGE_FINE = 0, 1, 2, 3
 BSA_STAGE_GATHER_INDEX, BSA_STAGE_GATHER_COMBINE, BSA_STAGE_COARSE_TOPK = 4, 5, 6
 BSA_STAGE_BWD_PREP, BSA_STAGE_BWD_INDEX, BSA_STAGE_BWD_PAIRS, BSA_STAGE_BWD_REDUCE = 7, 8, 9, 10
-BSA_NUM_STAGES = 11
+BSA_STAGE_RAGGED_COPY = 11
+BSA_NUM_STAGES = 12
 STAGE_NAMES = ("block_pool", "coarse_score", "topk_select", "sparse_flash_fwd", "gather_index",
-               "gather_combine", "coarse_select", "bwd_prep", "bwd_index", "bwd_pairs", "bwd_reduce")
+               "gather_combine", "coarse_select", "bwd_prep", "bwd_index", "bwd_pairs", "bwd_reduce",
+               "ragged_copy")
 BSA_OPT_PANEL_CHUNK_BYTES, BSA_OPT_FINE_STRATEGY, BSA_OPT_FINE_CHUNK_BYTES = 0, 1, 2
 BSA_OPT_SELECT_STRATEGY = 3
 BSA_FINE_BLOCK_GATHER, BSA_FINE_QUERY_TILE = 0, 1

@@ -8,6 +8,10 @@
 // kernel reads K exactly once and writes the float32 representatives, so it is
 // bound by HBM bandwidth.
 //
+// When the sequence length is not a multiple of 64 the keys come padded with
+// zero rows to whole blocks, and the last block of each head is the mean of
+// its `last` valid keys (the sum over the padded block, divided by `last`).
+//
 // Optionally it also writes each representative r as three bfloat16 terms
 // hi + mid + lo (hi = bf16(r), mid = bf16(r - hi), lo = bf16(r - hi - mid)),
 // laid out as one plane per term and head, split[bh][term][beta][d], the form
@@ -23,7 +27,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k,
                                                          float* __restrict__ repr,
                                                          bf16_bits* __restrict__ split,
-                                                         int64_t total_blocks, int nb) {
+                                                         int64_t total_blocks, int nb, int last) {
   constexpr int E = 16 / sizeof(T);     // elements per 16-byte chunk
   constexpr int LPR = D / E;            // lanes per key row
   constexpr int RPL = kWave / LPR;      // rows per wave-wide load
@@ -61,9 +65,14 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k
     for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], s);
   }
   if (ro == 0) {
-    constexpr float inv = 1.0f / kTile;  // exact: a power of two
+    if (last < kTile && blk % nb == nb - 1) {  // a partial last block: mean of its valid keys
 #pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] *= inv;
+      for (int e = 0; e < E; ++e) acc[e] = acc[e] / static_cast<float>(last);
+    } else {
+      constexpr float inv = 1.0f / kTile;  // exact: a power of two
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] *= inv;
+    }
     if (repr) {
       float* dst = repr + blk * D + c * E;
 #pragma unroll
@@ -96,25 +105,27 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k
 }
 
 template <typename T, int D>
-hipError_t launch(const void* k, float* repr, bf16_bits* split, int64_t blocks, int nb, hipStream_t s) {
+hipError_t launch(const void* k, float* repr, bf16_bits* split, int64_t blocks, int nb, int last,
+                  hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((blocks + 3) / 4));
   hipLaunchKernelGGL((block_pool_kernel<T, D>), grid, dim3(256), 0, s,
-                     static_cast<const T*>(k), repr, split, blocks, nb);
+                     static_cast<const T*>(k), repr, split, blocks, nb, last);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_block_pool(const void* k, float* repr, uint16_t* split, int64_t bh, int n, int d,
-                             bsa_dtype dtype, hipStream_t stream) {
+                             bsa_dtype dtype, hipStream_t stream, int nv) {
   const int nb = n / kTile;
   const int64_t blocks = bh * nb;
+  const int last = (nv > 0 && nv < n) ? nv - (nb - 1) * kTile : kTile;
   if (dtype == BSA_BF16) {
-    return d == 64 ? launch<bf16_bits, 64>(k, repr, split, blocks, nb, stream)
-                   : launch<bf16_bits, 128>(k, repr, split, blocks, nb, stream);
+    return d == 64 ? launch<bf16_bits, 64>(k, repr, split, blocks, nb, last, stream)
+                   : launch<bf16_bits, 128>(k, repr, split, blocks, nb, last, stream);
   }
-  return d == 64 ? launch<float, 64>(k, repr, split, blocks, nb, stream)
-                 : launch<float, 128>(k, repr, split, blocks, nb, stream);
+  return d == 64 ? launch<float, 64>(k, repr, split, blocks, nb, last, stream)
+                 : launch<float, 128>(k, repr, split, blocks, nb, last, stream);
 }
 
 }  // namespace bsa

@@ -40,6 +40,7 @@ struct bsa_handle_s {
   };
   Buf g_count, g_offsets, g_items, g_item_rec, g_rank, g_list, g_po, g_pml;
   Buf b_ld, b_dq, b_dkv;  // backward: per-row (lse, delta), per-pair dq, per-item dk/dv
+  Buf r_q, r_k, r_v, r_o, r_do, r_lse, r_idx, r_dq, r_dk, r_dv;  // padded copies (ragged n)
   // timing
   bool profiling = false;
   struct Rec {
@@ -136,9 +137,12 @@ struct Shape {
   int batch, heads, n, d;
   int64_t bh() const { return int64_t(batch) * heads; }
   int64_t elems() const { return bh() * n * d; }
+  // The same problem with n rounded up to whole 64-key blocks.
+  Shape padded() const { return Shape{batch, heads, (n + 63) / 64 * 64, d}; }
 };
 
-bsa_status check_shape(bsa_handle h, const char* fn, const Shape& s, bsa_dtype dtype, int block) {
+bsa_status check_shape(bsa_handle h, const char* fn, const Shape& s, bsa_dtype dtype, int block,
+                       bool ragged_ok = false) {
   if (s.batch < 1 || s.heads < 1 || s.n < 1 || s.d < 1)
     return fail(h, BSA_ERR_INVALID_ARG, "%s: batch, heads, n and d must be >= 1 (got %d, %d, %d, %d)",
                 fn, s.batch, s.heads, s.n, s.d);
@@ -148,7 +152,7 @@ bsa_status check_shape(bsa_handle h, const char* fn, const Shape& s, bsa_dtype d
     return fail(h, BSA_ERR_UNSUPPORTED, "%s: block must be 64 (got %d)", fn, block);
   if (s.d != 64 && s.d != 128)
     return fail(h, BSA_ERR_UNSUPPORTED, "%s: d must be 64 or 128 (got %d)", fn, s.d);
-  if (s.n % 64 != 0)
+  if (s.n % 64 != 0 && !ragged_ok)
     return fail(h, BSA_ERR_UNSUPPORTED, "%s: n must be a multiple of 64 (got %d)", fn, s.n);
   if (s.bh() * s.n > (int64_t(1) << 31) / 1 || s.elems() > (int64_t(1) << 40))
     return fail(h, BSA_ERR_UNSUPPORTED, "%s: problem too large (batch*heads*n = %lld)", fn,
@@ -172,8 +176,8 @@ bsa_status check_dynamic(bsa_handle h, const char* fn, const Shape& s, int topk,
   if (topk < 1) return fail(h, BSA_ERR_INVALID_ARG, "%s: topk must be >= 1 (got %d)", fn, topk);
   if (causal != 0 && causal != 1)
     return fail(h, BSA_ERR_INVALID_ARG, "%s: causal must be 0 or 1 (got %d)", fn, causal);
-  if (s.n / 64 > 2048)
-    return fail(h, BSA_ERR_UNSUPPORTED, "%s: n/64 must be <= 2048 (got %d)", fn, s.n / 64);
+  if ((s.n + 63) / 64 > 2048)
+    return fail(h, BSA_ERR_UNSUPPORTED, "%s: ceil(n/64) must be <= 2048 (got %d)", fn, (s.n + 63) / 64);
   return BSA_OK;
 }
 
@@ -237,7 +241,8 @@ BSA_API bsa_status bsa_destroy(bsa_handle h) {
   if (h->panel) (void)hipFree(h->panel);
   if (h->idx) (void)hipFree(h->idx);
   for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml,
-                 &h->b_ld, &h->b_dq, &h->b_dkv})
+                 &h->b_ld, &h->b_dq, &h->b_dkv, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
+                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv})
     if (b->p) (void)hipFree(b->p);
   delete h;
   return BSA_OK;
@@ -273,7 +278,8 @@ BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
   if (!h || !bytes) return fail(h, BSA_ERR_INVALID_ARG, "bsa_workspace_bytes: NULL argument");
   *bytes = h->repr_bytes + h->split_bytes + h->panel_bytes + h->idx_bytes;
   for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_list, &h->g_po, &h->g_pml,
-                 &h->b_ld, &h->b_dq, &h->b_dkv})
+                 &h->b_ld, &h->b_dq, &h->b_dkv, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
+                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv})
     *bytes += b->bytes;
   return BSA_OK;
 }
@@ -283,11 +289,27 @@ BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
 namespace {
 
 bsa_status run_pool(bsa_handle h, const void* k, float* repr, uint16_t* split, const Shape& s,
-                    bsa_dtype dt, hipStream_t st) {
+                    bsa_dtype dt, hipStream_t st, int nv = 0) {
   return timed_launch(h, BSA_STAGE_POOL, st, "block_pool", [&] {
-    return bsa::launch_block_pool(k, repr, split, s.bh(), s.n, s.d, dt, st);
+    return bsa::launch_block_pool(k, repr, split, s.bh(), s.n, s.d, dt, st, nv);
   });
 }
+
+// Ragged n: copies of caller rows into whole-block buffers and back.
+bsa_status pad_rows(bsa_handle h, const void* src, void* dst, const Shape& s, int words, uint32_t fill,
+                    hipStream_t st) {
+  return timed_launch(h, BSA_STAGE_RAGGED_COPY, st, "ragged-n padding copy", [&] {
+    return bsa::launch_pad_rows(src, dst, s.bh(), s.n, s.padded().n, words, fill, st);
+  });
+}
+
+bsa_status unpad_rows(bsa_handle h, const void* src, void* dst, const Shape& s, int words, hipStream_t st) {
+  return timed_launch(h, BSA_STAGE_RAGGED_COPY, st, "ragged-n copy back", [&] {
+    return bsa::launch_unpad_rows(src, dst, s.bh(), s.n, s.padded().n, words, st);
+  });
+}
+
+int elem_bytes(bsa_dtype dt) { return dt == BSA_BF16 ? 2 : 4; }
 
 bool fused_select(bsa_handle h, int topk) {
   return h->select_strategy == BSA_SELECT_FUSED && topk <= bsa::kFusedSelectMaxK;
@@ -336,11 +358,11 @@ bsa_status grow_buf(bsa_handle h, bsa_handle_s::Buf& b, size_t need, const char*
 // Stage 2 for the dynamic path, with the handle's fine strategy.
 bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, float* out,
                     float* lse, const int32_t* idx, const Shape& s, bsa_dtype dt, int topk,
-                    float scale, int causal, hipStream_t st) {
+                    float scale, int causal, hipStream_t st, int nv = 0) {
   if (h->fine_strategy == BSA_FINE_QUERY_TILE)
     return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
       return bsa::launch_sparse_flash_dynamic(q, k, v, out, lse, idx, s.bh(), s.n, s.d, topk, scale,
-                                              causal, dt, st);
+                                              causal, dt, st, nv);
     });
   const int64_t total = s.bh() * s.n;
   const size_t per_row = bsa::gather_pair_bytes(s.d, dt) * size_t(topk);
@@ -376,6 +398,7 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   a.scale = scale;
   a.dtype = dt;
   a.qsegs = qsegs;
+  a.nv = nv;
   a.ws.count = static_cast<int32_t*>(h->g_count.p);
   a.ws.offsets = static_cast<int32_t*>(h->g_offsets.p);
   a.ws.items = static_cast<int32_t*>(h->g_items.p);
@@ -457,7 +480,7 @@ BSA_API bsa_status bsa_fine_forward(bsa_handle h, const void* q, const void* k, 
   const char* fn = "bsa_fine_forward";
   if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
   const Shape s{batch, heads, n, d};
-  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_shape(h, fn, s, dtype, block, true));
   TRY(check_dynamic(h, fn, s, topk, causal));
   TRY(check_scale(h, fn, scale));
   TRY(check_ptr(h, fn, "q", q));
@@ -466,8 +489,24 @@ BSA_API bsa_status bsa_fine_forward(bsa_handle h, const void* q, const void* k, 
   TRY(check_ptr(h, fn, "out", out));
   if (!block_idx) return fail(h, BSA_ERR_INVALID_ARG, "%s: block_idx is NULL", fn);
   DeviceGuard dg(h->device);
-  return run_fine(h, q, k, v, out, nullptr, block_idx, s, dtype, topk, scale, causal,
-                  static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (s.n % 64 == 0) return run_fine(h, q, k, v, out, nullptr, block_idx, s, dtype, topk, scale, causal, st);
+  // ragged n: whole-block copies; the padding rows select nothing
+  const Shape sp = s.padded();
+  const size_t in_bytes = size_t(sp.elems()) * elem_bytes(dtype);
+  const int w = s.d * elem_bytes(dtype) / 4;
+  TRY(grow_buf(h, h->r_q, in_bytes, "padded q"));
+  TRY(grow_buf(h, h->r_k, in_bytes, "padded k"));
+  TRY(grow_buf(h, h->r_v, in_bytes, "padded v"));
+  TRY(grow_buf(h, h->r_o, size_t(sp.elems()) * 4, "padded out"));
+  TRY(grow_buf(h, h->r_idx, size_t(sp.bh() * sp.n * topk) * 4, "padded indices"));
+  TRY(pad_rows(h, q, h->r_q.p, s, w, 0u, st));
+  TRY(pad_rows(h, k, h->r_k.p, s, w, 0u, st));
+  TRY(pad_rows(h, v, h->r_v.p, s, w, 0u, st));
+  TRY(pad_rows(h, block_idx, h->r_idx.p, s, topk, 0xFFFFFFFFu, st));
+  TRY(run_fine(h, h->r_q.p, h->r_k.p, h->r_v.p, static_cast<float*>(h->r_o.p), nullptr,
+               static_cast<const int32_t*>(h->r_idx.p), sp, dtype, topk, scale, causal, st, s.n));
+  return unpad_rows(h, h->r_o.p, out, s, s.d, st);
 }
 
 namespace {
@@ -486,26 +525,57 @@ bsa_status forward_impl(bsa_handle h, const char* fn, const void* q, const void*
     return fail(h, BSA_ERR_INVALID_ARG, "%s: block_idx_out is not 4-byte aligned", fn);
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t nb = s.n / 64;
+  // A ragged n runs on copies padded to whole blocks (sp); the padding keys
+  // are masked, the padding rows' results dropped.
+  const Shape sp = s.padded();
+  const bool ragged = sp.n != s.n;
+  const void *pq = q, *pk = k, *pv = v;
+  float* pout = out;
+  float* plse = lse_out;
+  int32_t* idx = block_idx_out;
+  if (ragged) {
+    const size_t in_bytes = size_t(sp.elems()) * elem_bytes(dtype);
+    const int w = s.d * elem_bytes(dtype) / 4;
+    TRY(grow_buf(h, h->r_q, in_bytes, "padded q"));
+    TRY(grow_buf(h, h->r_k, in_bytes, "padded k"));
+    TRY(grow_buf(h, h->r_v, in_bytes, "padded v"));
+    TRY(grow_buf(h, h->r_o, size_t(sp.elems()) * 4, "padded out"));
+    if (lse_out) TRY(grow_buf(h, h->r_lse, size_t(sp.bh() * sp.n) * 4, "padded lse"));
+    TRY(pad_rows(h, q, h->r_q.p, s, w, 0u, st));
+    TRY(pad_rows(h, k, h->r_k.p, s, w, 0u, st));
+    TRY(pad_rows(h, v, h->r_v.p, s, w, 0u, st));
+    pq = h->r_q.p;
+    pk = h->r_k.p;
+    pv = h->r_v.p;
+    pout = static_cast<float*>(h->r_o.p);
+    plse = lse_out ? static_cast<float*>(h->r_lse.p) : nullptr;
+    idx = nullptr;
+  }
+  const int64_t nb = sp.n / 64;
   // The fused bf16 selection reads the split representatives only.
   const bool want_split = fused_select(h, topk) && dtype == BSA_BF16;
   if (want_split)
     TRY(grow(h, reinterpret_cast<void**>(&h->split), &h->split_bytes,
-             size_t(s.bh() * nb * s.d) * 3 * 2, "split repr workspace"));
+             size_t(sp.bh() * nb * sp.d) * 3 * 2, "split repr workspace"));
   else
-    TRY(grow(h, reinterpret_cast<void**>(&h->repr), &h->repr_bytes, size_t(s.bh() * nb * s.d) * 4,
+    TRY(grow(h, reinterpret_cast<void**>(&h->repr), &h->repr_bytes, size_t(sp.bh() * nb * sp.d) * 4,
              "repr workspace"));
   float* repr = want_split ? nullptr : h->repr;
   uint16_t* split = want_split ? h->split : nullptr;
-  int32_t* idx = block_idx_out;
   if (!idx) {
-    TRY(grow(h, reinterpret_cast<void**>(&h->idx), &h->idx_bytes, size_t(s.bh() * s.n * topk) * 4,
+    TRY(grow(h, reinterpret_cast<void**>(&h->idx), &h->idx_bytes, size_t(sp.bh() * sp.n * topk) * 4,
              "index workspace"));
     idx = h->idx;
   }
-  TRY(run_pool(h, k, repr, split, s, dtype, st));
-  TRY(run_select(h, q, repr, split, idx, s, dtype, topk, hb, causal, st));
-  return run_fine(h, q, k, v, out, lse_out, idx, s, dtype, topk, scale, causal, st);
+  TRY(run_pool(h, pk, repr, split, sp, dtype, st, s.n));
+  TRY(run_select(h, pq, repr, split, idx, sp, dtype, topk, hb, causal, st));
+  TRY(run_fine(h, pq, pk, pv, pout, plse, idx, sp, dtype, topk, scale, causal, st, s.n));
+  if (ragged) {
+    TRY(unpad_rows(h, pout, out, s, s.d, st));
+    if (block_idx_out) TRY(unpad_rows(h, idx, block_idx_out, s, topk, st));
+    if (lse_out) TRY(unpad_rows(h, plse, lse_out, s, 1, st));
+  }
+  return BSA_OK;
 }
 
 // Per-head budgets from a host array (heads entries, each in [1, topk_max]).
@@ -532,7 +602,7 @@ BSA_API bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const
   const char* fn = "bsa_forward";
   if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
   const Shape s{batch, heads, n, d};
-  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_shape(h, fn, s, dtype, block, true));
   TRY(check_dynamic(h, fn, s, topk, causal));
   return forward_impl(h, fn, q, k, v, out, block_idx_out, nullptr, s, dtype, topk, uniform_budget(topk),
                       scale, causal, stream);
@@ -546,7 +616,7 @@ BSA_API bsa_status bsa_forward_budgets(bsa_handle h, const void* q, const void* 
   const char* fn = "bsa_forward_budgets";
   if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
   const Shape s{batch, heads, n, d};
-  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_shape(h, fn, s, dtype, block, true));
   TRY(check_dynamic(h, fn, s, topk_max, causal));
   if (!head_topk) return fail(h, BSA_ERR_INVALID_ARG, "%s: head_topk is NULL", fn);
   bsa::HeadBudget hb;
@@ -563,7 +633,7 @@ BSA_API bsa_status bsa_forward_train(bsa_handle h, const void* q, const void* k,
   const char* fn = "bsa_forward_train";
   if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
   const Shape s{batch, heads, n, d};
-  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_shape(h, fn, s, dtype, block, true));
   TRY(check_dynamic(h, fn, s, topk, causal));
   if (!block_idx_out) return fail(h, BSA_ERR_INVALID_ARG, "%s: block_idx_out is NULL", fn);
   if (!lse_out) return fail(h, BSA_ERR_INVALID_ARG, "%s: lse_out is NULL", fn);
@@ -583,7 +653,7 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   const char* fn = "bsa_backward";
   if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
   const Shape s{batch, heads, n, d};
-  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_shape(h, fn, s, dtype, block, true));
   TRY(check_dynamic(h, fn, s, topk, causal));
   TRY(check_scale(h, fn, scale));
   TRY(check_ptr(h, fn, "q", q));
@@ -600,16 +670,53 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
     return fail(h, BSA_ERR_INVALID_ARG, "%s: lse is NULL or not 4-byte aligned", fn);
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const int64_t total = s.bh() * s.n;
-  const int64_t align = (s.n % 256 == 0) ? 256 : 64;  // keeps bucketing workgroups inside one head
-  const size_t per_row = size_t(topk) * size_t(s.d) * 4;  // the per-pair dq rows
+  // A ragged n runs on copies padded to whole blocks (the padding rows select
+  // nothing, the padding keys are masked) and copies dq, dk, dv back.
+  const Shape sp = s.padded();
+  const bool ragged = sp.n != s.n;
+  float *gq = dq, *gk = dk, *gv = dv;
+  if (ragged) {
+    const size_t in_bytes = size_t(sp.elems()) * elem_bytes(dtype);
+    const size_t f_bytes = size_t(sp.elems()) * 4;
+    const int w = s.d * elem_bytes(dtype) / 4;
+    TRY(grow_buf(h, h->r_q, in_bytes, "padded q"));
+    TRY(grow_buf(h, h->r_k, in_bytes, "padded k"));
+    TRY(grow_buf(h, h->r_v, in_bytes, "padded v"));
+    TRY(grow_buf(h, h->r_o, f_bytes, "padded out"));
+    TRY(grow_buf(h, h->r_do, f_bytes, "padded dout"));
+    TRY(grow_buf(h, h->r_lse, size_t(sp.bh() * sp.n) * 4, "padded lse"));
+    TRY(grow_buf(h, h->r_idx, size_t(sp.bh() * sp.n * topk) * 4, "padded indices"));
+    TRY(grow_buf(h, h->r_dq, f_bytes, "padded dq"));
+    TRY(grow_buf(h, h->r_dk, f_bytes, "padded dk"));
+    TRY(grow_buf(h, h->r_dv, f_bytes, "padded dv"));
+    TRY(pad_rows(h, q, h->r_q.p, s, w, 0u, st));
+    TRY(pad_rows(h, k, h->r_k.p, s, w, 0u, st));
+    TRY(pad_rows(h, v, h->r_v.p, s, w, 0u, st));
+    TRY(pad_rows(h, out, h->r_o.p, s, s.d, 0u, st));
+    TRY(pad_rows(h, dout, h->r_do.p, s, s.d, 0u, st));
+    TRY(pad_rows(h, lse, h->r_lse.p, s, 1, 0u, st));
+    TRY(pad_rows(h, block_idx, h->r_idx.p, s, topk, 0xFFFFFFFFu, st));
+    q = h->r_q.p;
+    k = h->r_k.p;
+    v = h->r_v.p;
+    out = static_cast<const float*>(h->r_o.p);
+    dout = static_cast<const float*>(h->r_do.p);
+    lse = static_cast<const float*>(h->r_lse.p);
+    block_idx = static_cast<const int32_t*>(h->r_idx.p);
+    gq = static_cast<float*>(h->r_dq.p);
+    gk = static_cast<float*>(h->r_dk.p);
+    gv = static_cast<float*>(h->r_dv.p);
+  }
+  const int64_t total = sp.bh() * sp.n;
+  const int64_t align = (sp.n % 256 == 0) ? 256 : 64;  // keeps bucketing workgroups inside one head
+  const size_t per_row = size_t(topk) * size_t(sp.d) * 4;  // the per-pair dq rows
   int64_t chunk = h->fine_chunk_bytes / int64_t(per_row) / align * align;
   if (chunk < align) chunk = align;
   if (chunk > total) chunk = total;
   const int64_t pairs = chunk * topk;
-  const int64_t nb = s.n / 64;
-  const int qsegs = bsa::gather_segments(s.n, s.d, topk, dtype);
-  const int64_t heads_spanned = s.bh() < (chunk + s.n - 1) / s.n + 1 ? s.bh() : (chunk + s.n - 1) / s.n + 1;
+  const int64_t nb = sp.n / 64;
+  const int qsegs = bsa::gather_segments(sp.n, sp.d, topk, dtype);
+  const int64_t heads_spanned = sp.bh() < (chunk + sp.n - 1) / sp.n + 1 ? sp.bh() : (chunk + sp.n - 1) / sp.n + 1;
   const int64_t buckets = heads_spanned * qsegs * nb;
   const int64_t slots = bsa::gather_grid(chunk, topk, buckets, bsa::kBwdItemPairs);
   TRY(grow_buf(h, h->g_count, size_t(buckets) * 4, "bucket counts"));
@@ -619,8 +726,8 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   TRY(grow_buf(h, h->g_rank, size_t(pairs) * 4, "pair ranks"));
   TRY(grow_buf(h, h->g_list, size_t(pairs) * 4, "pair lists"));
   TRY(grow_buf(h, h->b_ld, size_t(total) * 8, "backward row statistics"));
-  TRY(grow_buf(h, h->b_dq, size_t(pairs) * s.d * 4, "backward dq contributions"));
-  TRY(grow_buf(h, h->b_dkv, size_t(slots) * 2 * 64 * s.d * 4, "backward dk/dv contributions"));
+  TRY(grow_buf(h, h->b_dq, size_t(pairs) * sp.d * 4, "backward dq contributions"));
+  TRY(grow_buf(h, h->b_dkv, size_t(slots) * 2 * 64 * sp.d * 4, "backward dk/dv contributions"));
   bsa::BackwardArgs a;
   a.q = q;
   a.k = k;
@@ -629,11 +736,12 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   a.dout = dout;
   a.lse = lse;
   a.idx = block_idx;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.n = s.n;
-  a.d = s.d;
+  a.dq = gq;
+  a.dk = gk;
+  a.dv = gv;
+  a.n = sp.n;
+  a.nv = s.n;
+  a.d = sp.d;
   a.topk = topk;
   a.causal = causal;
   a.scale = scale;
@@ -651,8 +759,8 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   bsa::GatherArgs gi;  // the bucketing of the forward, with backward-sized work items
   gi.q = q;
   gi.idx = block_idx;
-  gi.n = s.n;
-  gi.d = s.d;
+  gi.n = sp.n;
+  gi.d = sp.d;
   gi.topk = topk;
   gi.causal = causal;
   gi.dtype = dtype;
@@ -671,6 +779,11 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
                      [&] { return bsa::launch_bwd_dq(a, r0, rows, st); }));
     TRY(timed_launch(h, BSA_STAGE_BWD_REDUCE, st, "backward dk/dv reduction",
                      [&] { return bsa::launch_bwd_dkv(a, r0, rows, st); }));
+  }
+  if (ragged) {
+    TRY(unpad_rows(h, gq, dq, s, s.d, st));
+    TRY(unpad_rows(h, gk, dk, s, s.d, st));
+    TRY(unpad_rows(h, gv, dv, s, s.d, st));
   }
   return BSA_OK;
 }

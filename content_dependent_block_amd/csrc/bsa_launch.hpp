@@ -13,9 +13,19 @@ namespace bsa {
 
 // block_pool: k [bh][n][d] -> repr float [bh][n/64][d] (if repr != NULL) and
 // the three-term bf16 split of each representative, split [bh][3][n/64][d]
-// (if split != NULL).
+// (if split != NULL).  nv < n: the keys are padded with zero rows from nv to
+// n, and the last block is the mean of its nv - (n - 64) valid keys.
 hipError_t launch_block_pool(const void* k, float* repr, uint16_t* split, int64_t bh, int n, int d,
-                             bsa_dtype dtype, hipStream_t stream);
+                             bsa_dtype dtype, hipStream_t stream, int nv = 0);
+
+// Ragged sequences run on copies padded to whole blocks.  pad: dst[h][r][:] =
+// src[h][r][:] for r < n, = fill (every 32-bit word) for n <= r < n_pad.
+// unpad: dst[h][r][:] = src[h][r][:] for r < n, src rows n_pad apart.  Rows
+// are `words` 32-bit words.
+hipError_t launch_pad_rows(const void* src, void* dst, int64_t bh, int n, int n_pad, int words,
+                           uint32_t fill, hipStream_t stream);
+hipError_t launch_unpad_rows(const void* src, void* dst, int64_t bh, int n, int n_pad, int words,
+                             hipStream_t stream);
 
 // coarse_score over panel rows [row0, row0 + rows) of the flattened
 // [bh * n] query rows; row0 and rows multiples of 64.  panel row r holds
@@ -52,7 +62,7 @@ hipError_t launch_topk_select(const float* panel, int32_t* idx, int64_t row0, in
 hipError_t launch_sparse_flash_dynamic(const void* q, const void* k, const void* v, float* out,
                                        float* lse, const int32_t* idx, int64_t bh, int n, int d,
                                        int topk, float scale, int causal, bsa_dtype dtype,
-                                       hipStream_t stream);
+                                       hipStream_t stream, int nv = 0);
 
 // sparse_flash_fwd, static tile list.
 hipError_t launch_sparse_flash_static(const void* q, const void* k, const void* v, float* out,
@@ -85,6 +95,7 @@ struct GatherArgs {
   float* lse = nullptr;  // nullable: per row log-sum-exp (natural log), from the combine
   const int32_t* idx = nullptr;
   int n = 0, d = 0, topk = 0, causal = 0;
+  int nv = 0;  // keys per head that exist (< n: rows nv .. n-1 are padding and masked); 0 = n
   float scale = 0.f;
   bsa_dtype dtype = BSA_FP32;
   int qsegs = 1;  // query segments per head (gather_segments); buckets = heads x qsegs x n/64
@@ -121,6 +132,7 @@ struct BackwardArgs {
   float* dk = nullptr;
   float* dv = nullptr;
   int n = 0, d = 0, topk = 0, causal = 0;
+  int nv = 0;  // keys per head that exist (< n: padding rows, masked); 0 = n
   float scale = 0.f;
   bsa_dtype dtype = BSA_FP32;
   int qsegs = 1;

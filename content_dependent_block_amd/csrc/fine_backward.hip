@@ -267,8 +267,8 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
     const float* __restrict__ dout, const float2* __restrict__ ld,
     const int32_t* __restrict__ list, const int32_t* __restrict__ items,
     const int4* __restrict__ item_rec, int nbuckets, int64_t row0, int64_t npairs, int n,
-    uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, float scale, float scale_log2,
-    float* __restrict__ dq_part, float* __restrict__ dkv_part) {
+    uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, int klim_last, float scale,
+    float scale_log2, float* __restrict__ dq_part, float* __restrict__ dkv_part) {
   using L = BwdLayout<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   T* ks = reinterpret_cast<T*>(smem);
@@ -294,6 +294,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
   const int nb = n / kTile;
   const int beta = b % nb;
   const int64_t bh = bh0 + b / (nb * qsegs);
+  const int klim = beta == nb - 1 ? klim_last : kTile;  // valid keys of the block (the rest pad)
 
   stage_kv<T, D>(k + (bh * n + static_cast<int64_t>(beta) * kTile) * D,
                  v + (bh * n + static_cast<int64_t>(beta) * kTile) * D, ks, vs, kt, tid);
@@ -336,7 +337,8 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const bool vis = live && (!CAUSAL || 16 * tt + 4 * g + jj <= qlocal);
+        const int key = 16 * tt + 4 * g + jj;
+        const bool vis = live && (!CAUSAL || key <= qlocal) && key < klim;
         const float p = vis ? __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][jj], scale_log2, -lr.x)) : 0.f;
         pv[tt][jj] = p;
         dsv[tt][jj] = p * (dp[tt][jj] - lr.y);
@@ -597,6 +599,7 @@ hipError_t pairs_launch(const BackwardArgs& a, int64_t row0, int64_t rows, hipSt
   while ((1 << lg) < a.topk) ++lg;
   const int shift = 32 + lg;
   const uint64_t magic = ((uint64_t(1) << shift) + uint64_t(a.topk) - 1) / uint64_t(a.topk);
+  const int klim_last = (a.nv > 0 && a.nv < a.n) ? a.nv - (c.nb - 1) * kTile : kTile;
   const auto kern = bwd_pair_kernel<T, D, CAUSAL>;
   if (L::BYTES > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -606,8 +609,8 @@ hipError_t pairs_launch(const BackwardArgs& a, int64_t row0, int64_t rows, hipSt
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(256), L::BYTES, s,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                      a.dout, a.ld, a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets, row0, c.npairs,
-                     a.n, magic, shift, c.bh0, a.qsegs, a.scale, a.scale * kLog2e, a.dq_part,
-                     a.dkv_part);
+                     a.n, magic, shift, c.bh0, a.qsegs, klim_last, a.scale, a.scale * kLog2e,
+                     a.dq_part, a.dkv_part);
   return hipGetLastError();
 }
 

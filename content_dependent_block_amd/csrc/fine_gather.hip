@@ -389,7 +389,7 @@ __device__ __forceinline__ int out_dim(int dt, int m) {
 // probabilities, so l sums exactly the weights that enter o.
 template <typename T, int D, bool CAUSAL>
 __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage, const QOperand<T, D>& qo,
-                                           int64_t row, int beta, int n, bool live, int32_t pair,
+                                           int64_t row, int beta, int n, int klim, bool live, int32_t pair,
                                            float scale_log2, PartialT<T>* __restrict__ po,
                                            float2* __restrict__ pml, int lane) {
   using L = KvLayout<T, D>;
@@ -425,6 +425,13 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
         for (int jj = 0; jj < 4; ++jj)
           if (16 * tt + 4 * g + jj > qlocal) s[tt][jj] = -INFINITY;
     }
+  }
+  if (klim < kTile) {  // a partial last block: keys klim .. 63 are padding
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        if (16 * tt + 4 * g + jj >= klim) s[tt][jj] = -INFINITY;
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -536,7 +543,7 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ list, const int32_t* __restrict__ items,
     const int4* __restrict__ item_rec, int nbuckets, int64_t row0, int64_t npairs, int n,
-    uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, float scale_log2,
+    uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, int klim_last, float scale_log2,
     PartialT<T>* __restrict__ po, float2* __restrict__ pml) {
   using L = KvLayout<T, D>;
   constexpr int GPW = kItemPairs / 16 / 4;  // 16-pair groups per wave
@@ -563,6 +570,7 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
   const int nb = n / kTile;
   const int beta = b % nb;
   const int64_t bh = bh0 + b / (nb * qsegs);
+  const int klim = beta == nb - 1 ? klim_last : kTile;  // valid keys of the block
 
   int32_t pair[GPW];
   bool live[GPW];
@@ -591,8 +599,8 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     if ((wave + 4 * gi) * 16 >= cnt) break;  // wave-uniform
-    pair_group<T, D, CAUSAL>(ks, vs, stage, qo[gi], row[gi], beta, n, live[gi], pair[gi], scale_log2,
-                             po, pml, lane);
+    pair_group<T, D, CAUSAL>(ks, vs, stage, qo[gi], row[gi], beta, n, klim, live[gi], pair[gi],
+                             scale_log2, po, pml, lane);
   }
 }
 
@@ -696,16 +704,19 @@ hipError_t partial_chunk(const GatherArgs& a, int64_t row0, int64_t rows, hipStr
   while ((1 << lg) < a.topk) ++lg;
   const int shift = 32 + lg;
   const uint64_t magic = ((uint64_t(1) << shift) + uint64_t(a.topk) - 1) / uint64_t(a.topk);
+  const int klim_last = (a.nv > 0 && a.nv < a.n) ? a.nv - (c.nb - 1) * kTile : kTile;
   if (a.causal)
     hipLaunchKernelGGL((gather_partial_kernel<T, D, true>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets,
-                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, sl2, po, a.ws.partial_ml);
+                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, klim_last, sl2, po,
+                       a.ws.partial_ml);
   else
     hipLaunchKernelGGL((gather_partial_kernel<T, D, false>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets,
-                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, sl2, po, a.ws.partial_ml);
+                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, klim_last, sl2, po,
+                       a.ws.partial_ml);
   return hipGetLastError();
 }
 

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     float* __restrict__ out, float* __restrict__ lse, const int32_t* __restrict__ idx, int topk,
     const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
-    const uint64_t* __restrict__ rowmask, int64_t nnz, int n, float scale_log2) {
+    const uint64_t* __restrict__ rowmask, int64_t nnz, int n, int klim_last, float scale_log2) {
   using L = KvLayout<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   T* ks = reinterpret_cast<T*>(smem);
@@ -268,6 +268,16 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
               if (16 * t + 4 * g + jj <= qlocal) cm |= 1u << (4 * t + jj);
           vis &= cm;
         }
+        if (cur == nb - 1 && klim_last < kTile) {
+          // a partial last block: keys klim_last .. 63 are padding
+          uint32_t km = 0u;
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+              if (16 * t + 4 * g + jj < klim_last) km |= 1u << (4 * t + jj);
+          vis &= km;
+        }
       } else {
         uint64_t m64 = ~0ull;
         if (rowmask) m64 = rowmask[(list_base + it) * kTile + qlocal];
@@ -300,7 +310,7 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
 
 template <typename T, int D, bool STATIC, bool CAUSAL>
 hipError_t launch_one(const void* q, const void* k, const void* v, float* out, float* lse,
-                      const int32_t* idx, int topk, const int32_t* row_ptr, const int32_t* col,
+                      const int32_t* idx, int topk, int klim_last, const int32_t* row_ptr, const int32_t* col,
                       const uint64_t* rowmask, int64_t nnz, int64_t bh, int n, float scale,
                       hipStream_t s) {
   using L = KvLayout<T, D>;
@@ -317,18 +327,18 @@ hipError_t launch_one(const void* q, const void* k, const void* v, float* out, f
   const dim3 grid(static_cast<unsigned>(bh * (n / kTile)));
   hipLaunchKernelGGL(kern, grid, dim3(256), smem, s, static_cast<const T*>(q),
                      static_cast<const T*>(k), static_cast<const T*>(v), out, lse, idx, topk, row_ptr,
-                     col, rowmask, nnz, n, scale * kLog2e);
+                     col, rowmask, nnz, n, klim_last, scale * kLog2e);
   return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t dispatch_dynamic(const void* q, const void* k, const void* v, float* out, float* lse,
                             const int32_t* idx, int64_t bh, int n, int topk, float scale,
-                            int causal, hipStream_t s) {
-  return causal ? launch_one<T, D, false, true>(q, k, v, out, lse, idx, topk, nullptr, nullptr,
-                                                nullptr, 0, bh, n, scale, s)
-                : launch_one<T, D, false, false>(q, k, v, out, lse, idx, topk, nullptr, nullptr,
-                                                 nullptr, 0, bh, n, scale, s);
+                            int causal, hipStream_t s, int klim_last) {
+  return causal ? launch_one<T, D, false, true>(q, k, v, out, lse, idx, topk, klim_last, nullptr,
+                                                nullptr, nullptr, 0, bh, n, scale, s)
+                : launch_one<T, D, false, false>(q, k, v, out, lse, idx, topk, klim_last, nullptr,
+                                                 nullptr, nullptr, 0, bh, n, scale, s);
 }
 
 }  // namespace
@@ -336,12 +346,13 @@ hipError_t dispatch_dynamic(const void* q, const void* k, const void* v, float* 
 hipError_t launch_sparse_flash_dynamic(const void* q, const void* k, const void* v, float* out,
                                        float* lse, const int32_t* idx, int64_t bh, int n, int d,
                                        int topk, float scale, int causal, bsa_dtype dtype,
-                                       hipStream_t stream) {
+                                       hipStream_t stream, int nv) {
+  const int kl = (nv > 0 && nv < n) ? nv - (n / kTile - 1) * kTile : kTile;
   if (dtype == BSA_BF16)
-    return d == 64 ? dispatch_dynamic<bf16_bits, 64>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream)
-                   : dispatch_dynamic<bf16_bits, 128>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream);
-  return d == 64 ? dispatch_dynamic<float, 64>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream)
-                 : dispatch_dynamic<float, 128>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream);
+    return d == 64 ? dispatch_dynamic<bf16_bits, 64>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl)
+                   : dispatch_dynamic<bf16_bits, 128>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl);
+  return d == 64 ? dispatch_dynamic<float, 64>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl)
+                 : dispatch_dynamic<float, 128>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl);
 }
 
 hipError_t launch_sparse_flash_static(const void* q, const void* k, const void* v, float* out,
@@ -349,13 +360,13 @@ hipError_t launch_sparse_flash_static(const void* q, const void* k, const void* 
                                       const uint64_t* rowmask, int64_t nnz, int64_t bh, int n,
                                       int d, float scale, bsa_dtype dtype, hipStream_t stream) {
   if (dtype == BSA_BF16)
-    return d == 64 ? launch_one<bf16_bits, 64, true, false>(q, k, v, out, nullptr, nullptr, 0, row_ptr, col,
+    return d == 64 ? launch_one<bf16_bits, 64, true, false>(q, k, v, out, nullptr, nullptr, 0, kTile, row_ptr, col,
                                                             rowmask, nnz, bh, n, scale, stream)
-                   : launch_one<bf16_bits, 128, true, false>(q, k, v, out, nullptr, nullptr, 0, row_ptr, col,
+                   : launch_one<bf16_bits, 128, true, false>(q, k, v, out, nullptr, nullptr, 0, kTile, row_ptr, col,
                                                              rowmask, nnz, bh, n, scale, stream);
-  return d == 64 ? launch_one<float, 64, true, false>(q, k, v, out, nullptr, nullptr, 0, row_ptr, col,
+  return d == 64 ? launch_one<float, 64, true, false>(q, k, v, out, nullptr, nullptr, 0, kTile, row_ptr, col,
                                                       rowmask, nnz, bh, n, scale, stream)
-                 : launch_one<float, 128, true, false>(q, k, v, out, nullptr, nullptr, 0, row_ptr, col,
+                 : launch_one<float, 128, true, false>(q, k, v, out, nullptr, nullptr, 0, kTile, row_ptr, col,
                                                        rowmask, nnz, bh, n, scale, stream);
 }
 

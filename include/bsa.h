@@ -31,9 +31,14 @@
  *  - A handle is not thread-safe: use one handle per host thread / stream.
  *    Two calls on one handle that overlap on different streams race on the
  *    handle's workspace.
- *  - Supported today: block (= tile) 64; d in {64, 128}; n a multiple of 64;
- *    n/64 <= 2048 for the dynamic path.  Anything else returns
- *    BSA_ERR_UNSUPPORTED.
+ *  - Supported today: block (= tile) 64; d in {64, 128}; ceil(n/64) <= 2048
+ *    for the dynamic path.  n need not be a multiple of 64 in bsa_forward,
+ *    bsa_forward_budgets, bsa_forward_train, bsa_backward and
+ *    bsa_fine_forward: the last block then holds the n mod 64 remaining keys
+ *    and its representative is their mean (the calls run on copies padded to
+ *    whole blocks, workspace held by the handle, with the padding keys
+ *    masked).  The stage exports and bsa_forward_static need n a multiple of
+ *    64.  Anything else returns BSA_ERR_UNSUPPORTED.
  */
 #ifndef BSA_H
 #define BSA_H
@@ -71,7 +76,8 @@ typedef enum {
   BSA_STAGE_BWD_INDEX = 8,      /* backward: bucketing of (query, block) pairs       */
   BSA_STAGE_BWD_PAIRS = 9,      /* backward: the MFMA pair kernel (dq, dk, dv parts) */
   BSA_STAGE_BWD_REDUCE = 10,    /* backward: sums of the dq and dk/dv contributions  */
-  BSA_NUM_STAGES = 11
+  BSA_STAGE_RAGGED_COPY = 11,   /* n not a multiple of 64: copies to / from padding  */
+  BSA_NUM_STAGES = 12
 } bsa_stage;
 
 /* How the dynamic fine stage visits the selected blocks. */

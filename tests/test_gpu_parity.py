@@ -453,6 +453,74 @@ def test_selection_exact_ties(bsa, select, causal):
     np.testing.assert_array_equal(idx.cpu().numpy().reshape(-1, topk), ref)
 
 
+# ------------------------------------------------------------ ragged n --
+RAGGED = [("tiny_fp32_n1k", 1000, 4, False), ("tiny_fp32_n1k", 1000, 4, True),
+          ("dyn_bf16_n4k", 4100, 16, False), ("dyn_bf16_n4k", 4100, 16, True),
+          ("dyn_bf16_n4k", 65, 16, False), ("dyn_bf16_n4k", 65, 1, True),
+          ("tiny_fp32_n1k", 1, 4, False), ("tiny_fp32_n1k", 1, 4, True),
+          ("dyn_bf16_n4k", 3000, 32, True)]
+
+
+@pytest.mark.parametrize("select,strategy", PATHS)
+@pytest.mark.parametrize("name,n,topk,causal", RAGGED)
+def test_forward_ragged_n(bsa, name, n, topk, causal, select, strategy):
+    """n not a multiple of 64: the last block holds n mod 64 keys, its
+    representative is their mean (the oracle's definition), and no query sees
+    a key beyond n.  Every row checked."""
+    m, lib = bsa
+    use_strategy(m, lib, strategy, select)
+    w = W.WORKLOADS[name]
+    inp = W.generate(w, n=n)
+    rows = np.arange(w.bh * n, dtype=np.int64)
+    end_to_end(m, lib, w, inp, rows, topk=topk, causal=causal)
+
+
+@pytest.mark.parametrize("n,causal", [(1000, False), (4100, True)])
+def test_fine_forward_ragged_n(bsa, n, causal):
+    """Stage 2 alone on the oracle's selection at a ragged n."""
+    m, lib = bsa
+    w = W.WORKLOADS["dyn_bf16_n4k"]
+    inp = W.generate(w, n=n)
+    say(f"[gpu] bsa_fine_forward ragged n={n} causal={causal}")
+    r = oracle.pool(inp.k, w.block)
+    sc = oracle.scores(inp.q, r, w.block)
+    oidx, _, _ = oracle.topk(sc, n, w.block, w.topk, causal)
+    q, k, v = to_dev(inp, w.dtype)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    idx = torch.from_numpy(oidx.reshape(q.shape[:3] + (w.topk,))).cuda()
+    m.bsa_fine_forward(lib.handle, q, k, v, out, idx, scale=w.scale, causal=causal)
+    torch.cuda.synchronize()
+    ref = oracle.attend(inp.q, inp.k, inp.v, oidx, w.block, causal, w.scale)
+    err = np.abs(out.cpu().numpy().reshape(-1, w.d) - ref).max()
+    say(f"    max|err|={err:.3g}")
+    assert err <= TOL[w.dtype]
+
+
+def test_budgets_ragged_n(bsa):
+    m, lib = bsa
+    w = W.WORKLOADS["dyn_bf16_n4k"]
+    n, ks = 2500, [1, 3, 16, 7, 32, 2, 9, 16]
+    inp = W.generate(w, n=n)
+    say(f"[gpu] bsa_forward_budgets ragged n={n}")
+    q, k, v = to_dev(inp, w.dtype)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    idx = torch.empty(q.shape[:3] + (32,), dtype=torch.int32, device="cuda")
+    m.bsa_forward_budgets(lib.handle, q, k, v, out, idx, head_topk=ks, topk_max=32, scale=w.scale,
+                          causal=True)
+    torch.cuda.synchronize()
+    rows = np.arange(w.bh * n, dtype=np.int64)
+    gidx = idx.cpu().numpy().reshape(-1, 32)
+    r = oracle.pool(inp.k, w.block)
+    sc = oracle.scores(inp.q, r, w.block)
+    for hh in range(w.heads):
+        sel = (rows // n) % w.heads == hh
+        oidx, kth, nxt = oracle.topk(sc[sel], n, w.block, ks[hh], True, rows[sel])
+        check_selection(gidx[sel][:, :ks[hh]], oidx, kth, nxt, sc[sel], rows[sel], n, w.block, True)
+        assert (gidx[sel][:, ks[hh]:] == -1).all()
+    ref = oracle.attend(inp.q, inp.k, inp.v, gidx, w.block, True, w.scale)
+    assert np.abs(out.cpu().numpy().reshape(-1, w.d) - ref).max() <= TOL[w.dtype]
+
+
 # ----------------------------------------------------- per-head budgets --
 def run_budgets(m, lib, w, inp, ks, topk_max, causal):
     q, k, v = to_dev(inp, w.dtype)
@@ -568,7 +636,8 @@ def test_validation_statuses(bsa):
     assert fwd(dt=7) == m.BSA_ERR_INVALID_ARG
     assert fwd(d=96) == m.BSA_ERR_UNSUPPORTED
     assert fwd(block=32) == m.BSA_ERR_UNSUPPORTED
-    assert fwd(n=100) == m.BSA_ERR_UNSUPPORTED
+    assert fwd(n=100) == m.BSA_OK                           # ragged n: padded internally
+    assert L.bsa_block_pool(h, P(q), P(out), 1, 1, 100, 64, 1, 64, None) == m.BSA_ERR_UNSUPPORTED
     assert fwd(n=64 * 4096) == m.BSA_ERR_UNSUPPORTED
     assert "d must be 64 or 128" in (fwd(d=96), m.bsa_last_error(h))[1]
     assert L.bsa_forward(None, P(q), P(q), P(q), P(out), None, 1, 1, 128, 64, 1, 64, 2, 0.125, 0,
