@@ -79,6 +79,8 @@ struct GatherWorkspace {
   int32_t* items = nullptr;    // [buckets + 1]
   int4* item_rec = nullptr;    // [gather_grid(...)]  per-workgroup work-item records
   int32_t* rank = nullptr;     // [chunk pairs]  pairs = rows * topk
+  int2* rec = nullptr;         // [chunk pairs]  block-ordered {pair, block << 21 | rank} records
+  int32_t* wg_valid = nullptr; // [chunk rows / 64]  valid pairs per bucketing workgroup
   int32_t* list = nullptr;     // [chunk pairs]
   void* partial_o = nullptr;   // [chunk pairs][d]  fp16 for bf16 inputs, fp32 for fp32 inputs
   float2* partial_ml = nullptr;  // [chunk pairs]  (log2-domain max, sum)

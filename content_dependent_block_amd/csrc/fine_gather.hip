@@ -75,14 +75,63 @@ __global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, 
 // selection sizes up to 32 at rpw = 256); larger ones go through memory.
 constexpr int kPairRegs = 32;
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Exclusive prefix sum, in place, of s[0 .. m) in LDS (m <= 2048) by a
+// 256-thread workgroup; returns the total.  wt: 4 ints of LDS.
+__device__ __forceinline__ int32_t block_excl_scan(int32_t* s, int m, int32_t* wt) {
+  constexpr int P = 8;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int32_t v[P], sum = 0;
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    v[j] = t * P + j < m ? s[t * P + j] : 0;
+    sum += v[j];
+  }
+  const int32_t inc = wave_incl_scan(sum, lane);
+  if (lane == 63) wt[wave] = inc;
+  __syncthreads();
+  int32_t run = inc - sum, total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) run += wt[w];
+    total += wt[w];
+  }
+#pragma unroll
+  for (int j = 0; j < P; ++j) {
+    if (t * P + j < m) s[t * P + j] = run;
+    run += v[j];
+  }
+  __syncthreads();
+  return total;
+}
+
 // One workgroup per `rpw` query rows of one query segment (rpw divides the
 // segment length and row0).  Each pair's rank inside its bucket is its
 // workgroup's base (one global atomic per (workgroup, block)) plus its rank
 // inside the workgroup (LDS atomics).
+//
+// Register path (rpw * topk <= 256 * kPairRegs): the workgroup's valid pairs
+// also leave ordered by block, as records {pair, block << 21 | rank} at
+// rec[first pair of the workgroup + position], with the count of valid pairs
+// in wg_valid[workgroup] (a bucket holds pairs of distinct rows of one head,
+// so rank < n <= 2^17 fits 21 bits and the block 11).  Otherwise each pair's
+// rank goes to rank[pair] (-1 for padding).
 __global__ __launch_bounds__(256) void bucket_count_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ count, int32_t* __restrict__ rank,
-    int64_t row0, int64_t rows, int n, int topk, int causal, int64_t bh0, int rpw, int qsegs) {
-  extern __shared__ int32_t hist[];  // [nb] local counts, then [nb] global bases
+    int2* __restrict__ rec, int32_t* __restrict__ wg_valid, int64_t row0, int64_t rows, int n, int topk,
+    int causal, int64_t bh0, int rpw, int qsegs) {
+  // LDS: [nb] local counts -> local offsets, [nb] global bases, [4] scan
+  // scratch, then (register path) the block-ordered records, 8 bytes each
+  extern __shared__ int32_t hist[];
   const int nb = n / kTile;
   int32_t* base = hist + nb;
   const int64_t r_begin = row0 + static_cast<int64_t>(blockIdx.x) * rpw;
@@ -112,11 +161,21 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
     for (int c = threadIdx.x; c < nb; c += 256)
       base[c] = hist[c] ? atomicAdd(&count[bucket0 + c], hist[c]) : 0;
     __syncthreads();
+    const int32_t valid = block_excl_scan(hist, nb, hist + 2 * nb);
+    if (threadIdx.x == 0) wg_valid[blockIdx.x] = valid;
+    // ordered in LDS, then written out contiguously
+    int2* srec = reinterpret_cast<int2*>(hist + 2 * nb + 4);
 #pragma unroll
     for (int j = 0; j < kPairRegs; ++j) {
       const int e = threadIdx.x + 256 * j;
-      if (e < npairs) rank[p_begin + e] = lr[j] >= 0 ? base[bt[j]] + lr[j] : -1;
+      if (lr[j] >= 0)
+        srec[hist[bt[j]] + lr[j]] =
+            make_int2(static_cast<int32_t>(p_begin + e),
+                      static_cast<int32_t>((static_cast<uint32_t>(bt[j]) << 21) |
+                                           static_cast<uint32_t>(base[bt[j]] + lr[j])));
     }
+    __syncthreads();
+    for (int t = threadIdx.x; t < valid; t += 256) rec[p_begin + t] = srec[t];
     return;
   }
   for (int e = threadIdx.x; e < npairs; e += 256) {
@@ -131,16 +190,6 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
     const int32_t rk = rank[p_begin + e];
     if (rk >= 0) rank[p_begin + e] = base[sel[e]] + rk;
   }
-}
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int32_t wave_incl_scan(int32_t x, int lane) {
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t y = __shfl_up(x, off);
-    if (lane >= off) x += y;
-  }
-  return x;
 }
 
 // Single workgroup of 1024 threads.  offsets[b] / items[b] are exclusive
@@ -219,54 +268,22 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const int32_t* __rest
   }
 }
 
-// Exclusive prefix sum, in place, of s[0 .. m) in LDS (m <= 2048) by a
-// 256-thread workgroup; returns the total.  wt: 4 ints of LDS.
-__device__ __forceinline__ int32_t block_excl_scan(int32_t* s, int m, int32_t* wt) {
-  constexpr int P = 8;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  int32_t v[P], sum = 0;
-#pragma unroll
-  for (int j = 0; j < P; ++j) {
-    v[j] = t * P + j < m ? s[t * P + j] : 0;
-    sum += v[j];
-  }
-  const int32_t inc = wave_incl_scan(sum, lane);
-  if (lane == 63) wt[wave] = inc;
-  __syncthreads();
-  int32_t run = inc - sum, total = 0;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (w < wave) run += wt[w];
-    total += wt[w];
-  }
-#pragma unroll
-  for (int j = 0; j < P; ++j) {
-    if (t * P + j < m) s[t * P + j] = run;
-    run += v[j];
-  }
-  __syncthreads();
-  return total;
-}
-
 // Pair ids into per-bucket lists, with the geometry of bucket_count (one
-// workgroup per rpw rows).  Within the workgroup the pairs are first ordered
-// by block in LDS, so the pairs of one bucket, whose list positions are
-// consecutive, leave in consecutive lanes of one store.  Workgroup w also
+// workgroup per rpw rows).  On the register path it streams the count
+// kernel's block-ordered records, so the pairs of one bucket, whose list
+// positions are consecutive, leave in consecutive lanes of one store; else
+// each pair is stored at its own position.  Workgroup w also
 // writes, for each work item of buckets 256w .. 256w + 255, the record
 // {bucket, first list position, pair count} at the slot of the workgroup
 // that will run it: items are spread so that consecutive items (one head,
 // neighbouring blocks) go to one XCD, i.e. item = xcd * per_xcd + j runs as
 // workgroup j * 8 + xcd.
 __global__ __launch_bounds__(256) void bucket_fill_kernel(
-    const int32_t* __restrict__ idx, const int32_t* __restrict__ rank,
-    const int32_t* __restrict__ offsets, const int32_t* __restrict__ items,
-    int4* __restrict__ item_rec, int nbuckets, int64_t max_slots, int32_t* __restrict__ list,
-    int64_t row0, int64_t rows, int n, int topk, int64_t bh0, int qsegs, int item_pairs, int rpw,
-    int cap) {
-  // LDS: [nb] counts / bases, [4] scan scratch, then the workgroup's pairs
-  // ordered by block: [cap] list positions, [cap] pair ids (cap >= its pairs
-  // whenever they fit the registers).
-  extern __shared__ int32_t sm[];
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ rank, const int2* __restrict__ rec,
+    const int32_t* __restrict__ wg_valid, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ items, int4* __restrict__ item_rec, int nbuckets, int64_t max_slots,
+    int32_t* __restrict__ list, int64_t row0, int64_t rows, int n, int topk, int64_t bh0, int qsegs,
+    int item_pairs, int rpw) {
   const int64_t pb = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (pb < nbuckets) {
     const int32_t total = items[nbuckets];
@@ -288,47 +305,25 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(
   const int64_t npairs = rows * topk;
   const int64_t p_begin = (r_begin - row0) * topk;
   const int32_t* off = offsets + bucket_of(r_begin, 0, n, nb, qsegs, bh0);  // rpw divides the segment
-  const int32_t* sel = idx + r_begin * topk;
-  if (np > 256 * kPairRegs || np > cap) {  // workgroup-uniform: plain scattered stores
-    for (int e = threadIdx.x; e < np; e += 256) {
-      const int32_t rk = rank[p_begin + e];
-      if (rk < 0) continue;
-      const int64_t pos = static_cast<int64_t>(off[sel[e]]) + rk;
-      if (pos < npairs) list[pos] = static_cast<int32_t>(p_begin + e);
+  if (np <= 256 * kPairRegs) {
+    // the count kernel's block-ordered records: consecutive records of one
+    // block have consecutive list positions
+    const int32_t valid = wg_valid[blockIdx.x];
+    for (int t = threadIdx.x; t < valid; t += 256) {
+      const int2 r = rec[p_begin + t];
+      const uint32_t w = static_cast<uint32_t>(r.y);
+      const int64_t pos = static_cast<int64_t>(off[w >> 21]) + (w & 0x1FFFFFu);
+      if (pos < npairs) list[pos] = r.x;
     }
     return;
   }
-  int32_t* cnt = sm;
-  int32_t* wt = sm + nb;
-  int32_t* spos = sm + nb + 4;
-  int32_t* spair = spos + cap;
-  for (int c = threadIdx.x; c < nb; c += 256) cnt[c] = 0;
-  __syncthreads();
-  int32_t lr[kPairRegs], bt[kPairRegs];
-#pragma unroll
-  for (int j = 0; j < kPairRegs; ++j) {
-    const int e = threadIdx.x + 256 * j;
-    lr[j] = -1;
-    bt[j] = 0;
-    if (e < np && rank[p_begin + e] >= 0) {
-      bt[j] = sel[e];
-      lr[j] = atomicAdd(&cnt[bt[j]], 1);
-    }
+  const int32_t* sel = idx + r_begin * topk;
+  for (int e = threadIdx.x; e < np; e += 256) {
+    const int32_t rk = rank[p_begin + e];
+    if (rk < 0) continue;
+    const int64_t pos = static_cast<int64_t>(off[sel[e]]) + rk;
+    if (pos < npairs) list[pos] = static_cast<int32_t>(p_begin + e);
   }
-  __syncthreads();
-  const int32_t valid = block_excl_scan(cnt, nb, wt);
-#pragma unroll
-  for (int j = 0; j < kPairRegs; ++j) {
-    const int e = threadIdx.x + 256 * j;
-    if (lr[j] >= 0) {
-      const int32_t si = cnt[bt[j]] + lr[j];
-      spos[si] = off[bt[j]] + rank[p_begin + e];
-      spair[si] = static_cast<int32_t>(p_begin + e);
-    }
-  }
-  __syncthreads();
-  for (int si = threadIdx.x; si < valid; si += 256)
-    if (spos[si] < npairs) list[spos[si]] = spair[si];
 }
 
 // bf16 inputs keep partial outputs as fp16 (|o| <= max |v|, relative error
@@ -761,26 +756,27 @@ hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, 
                      0, s, a.ws.count, static_cast<int64_t>(c.nbuckets));
   const int seg = a.n / a.qsegs;
   const int rpw = (seg % 256 == 0 && row0 % 256 == 0) ? 256 : kTile;
-  hipLaunchKernelGGL(bucket_count_kernel, dim3(static_cast<unsigned>((rows + rpw - 1) / rpw)),
-                     dim3(256), static_cast<size_t>(c.nb) * 8, s, a.idx, a.ws.count, a.ws.rank, row0,
-                     rows, a.n, a.topk, a.causal, c.bh0, rpw, a.qsegs);
-  hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, a.ws.count, a.ws.offsets,
-                     a.ws.items, c.nbuckets, a.item_pairs);
   const int64_t row_groups = (rows + rpw - 1) / rpw;
-  const int64_t bucket_groups = (c.nbuckets + 255) / 256;
-  const int cap = rpw * a.topk < 256 * kPairRegs ? rpw * a.topk : 256 * kPairRegs;
-  const size_t fill_lds = (static_cast<size_t>(c.nb) + 4 + 2 * static_cast<size_t>(cap)) * 4;
-  if (fill_lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bucket_fill_kernel),
+  const int np = rpw * a.topk;  // pairs per workgroup
+  const size_t count_lds = (2 * static_cast<size_t>(c.nb) + 4) * 4 +
+                           (np <= 256 * kPairRegs ? static_cast<size_t>(np) * 8 : 0);
+  if (count_lds > 64 * 1024) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bucket_count_kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                                             static_cast<int>(fill_lds));
+                                             static_cast<int>(count_lds));
     if (e != hipSuccess) return e;
   }
+  hipLaunchKernelGGL(bucket_count_kernel, dim3(static_cast<unsigned>(row_groups)), dim3(256),
+                     count_lds, s, a.idx, a.ws.count, a.ws.rank, a.ws.rec,
+                     a.ws.wg_valid, row0, rows, a.n, a.topk, a.causal, c.bh0, rpw, a.qsegs);
+  hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, a.ws.count, a.ws.offsets,
+                     a.ws.items, c.nbuckets, a.item_pairs);
+  const int64_t bucket_groups = (c.nbuckets + 255) / 256;
   hipLaunchKernelGGL(bucket_fill_kernel,
                      dim3(static_cast<unsigned>(row_groups > bucket_groups ? row_groups : bucket_groups)),
-                     dim3(256), fill_lds, s, a.idx, a.ws.rank, a.ws.offsets, a.ws.items, a.ws.item_rec,
-                     c.nbuckets, gather_grid(rows, a.topk, c.nbuckets, a.item_pairs), a.ws.list, row0, rows,
-                     a.n, a.topk, c.bh0, a.qsegs, a.item_pairs, rpw, cap);
+                     dim3(256), 0, s, a.idx, a.ws.rank, a.ws.rec, a.ws.wg_valid, a.ws.offsets, a.ws.items,
+                     a.ws.item_rec, c.nbuckets, gather_grid(rows, a.topk, c.nbuckets, a.item_pairs), a.ws.list,
+                     row0, rows, a.n, a.topk, c.bh0, a.qsegs, a.item_pairs, rpw);
   return hipGetLastError();
 }
 
