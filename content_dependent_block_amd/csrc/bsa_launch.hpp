@@ -119,8 +119,11 @@ hipError_t launch_gather_combine(const GatherArgs& a, int64_t row0, int64_t rows
 
 // Backward of the fine stage with the selection held fixed, on the same
 // bucketing as the block-gather forward (one work item = up to
-// kBwdItemPairs pairs of one (head, query segment, key block) bucket).
-constexpr int kBwdItemPairs = 512;
+// bwd_item_pairs(d) pairs of one (head, query segment, key block) bucket).
+// d = 64: 2048 pairs (fewer per-item dk/dv partials; measured best at N =
+// 32k); d = 128: 512 (its pair kernel runs one workgroup per CU, and larger
+// items left long tails on the long causal workload).
+constexpr int bwd_item_pairs(int d) { return d == 64 ? 2048 : 512; }
 
 struct BackwardArgs {
   const void* q = nullptr;
@@ -139,6 +142,7 @@ struct BackwardArgs {
   bsa_dtype dtype = BSA_FP32;
   int qsegs = 1;
   float2* ld = nullptr;      // [bh * n] (lse * log2(e), sum_d dout * out)
+  uint16_t* dout_b = nullptr; // [bh * n][d] dout rounded to bf16 (bf16 inputs only)
   float* dq_part = nullptr;  // [chunk pairs][d]  per-pair dq contributions
   float* dkv_part = nullptr; // [work items][2][64][d]  per-item dk, dv contributions
   GatherWorkspace ws;        // bucketing (count .. list); partial_o / partial_ml unused

@@ -12,7 +12,7 @@
 //   dv_j  = sum_i p_ij dO_i.
 //
 // The work runs on the block-gather bucketing of the forward: one work item
-// is up to kBwdItemPairs (query, block) pairs that share key block beta, so
+// is up to bwd_item_pairs(d) (query, block) pairs that share key block beta, so
 // K and V of the block are staged once and every pair reuses them.  Per tile
 // of 64 pairs (16 per wave, one pair per MFMA column):
 //   S^T = K Q^T and dP^T = V dO^T on MFMA (64 keys x 16 pairs per wave),
@@ -39,7 +39,6 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kXcds = 8;
-constexpr int kItem = kBwdItemPairs;
 
 __device__ __forceinline__ bool pair_valid(int beta, int nb, int64_t row, int n, int causal) {
   if (beta < 0 || beta >= nb) return false;
@@ -48,11 +47,14 @@ __device__ __forceinline__ bool pair_valid(int beta, int nb, int64_t row, int n,
 
 // ---------------------------------------------------------------- prep --
 // ld[row] = (lse * log2 e, sum_d dout * out): 16 lanes per row.
+// For bf16 inputs it also writes dout rounded to bf16 (dout_b, [rows][D]),
+// the operand the pair kernel gathers (half the bytes of the fp32 rows).
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ out,
                                                        const float* __restrict__ dout,
                                                        const float* __restrict__ lse,
-                                                       float2* __restrict__ ld, int64_t rows) {
+                                                       float2* __restrict__ ld,
+                                                       bf16_bits* __restrict__ dout_b, int64_t rows) {
   constexpr int E = D / 16;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
@@ -60,11 +62,23 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
   if (r < rows) {
     const float* o = out + r * D + c * E;
     const float* g = dout + r * D + c * E;
+    uint32_t packed[E / 2];
 #pragma unroll
     for (int e = 0; e < E; e += 4) {
       const float4 a = *reinterpret_cast<const float4*>(o + e);
       const float4 b = *reinterpret_cast<const float4*>(g + e);
       s += a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+      packed[e / 2] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(b.x))) |
+                      (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(b.y))) << 16);
+      packed[e / 2 + 1] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(b.z))) |
+                          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(b.w))) << 16);
+    }
+    if (dout_b) {
+      bf16_bits* dst = dout_b + r * D + c * E;
+      if constexpr (E == 8)
+        *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      else
+        *reinterpret_cast<uint2*>(dst) = make_uint2(packed[0], packed[1]);
     }
   }
 #pragma unroll
@@ -154,9 +168,9 @@ struct PairRows {
 // row statistics, the row and the pair id.
 template <typename T, int D>
 struct PairIn {
-  static constexpr int NQ = sizeof(T) == 2 ? D / 32 : D / 16;  // 16-byte pieces of q
+  static constexpr int NQ = sizeof(T) == 2 ? D / 32 : D / 16;  // 16-byte pieces of q and of dout
   uint4 q[NQ];
-  float4 o[D / 16];  // bf16: pieces 2kk, 2kk + 1 = dims 32kk + 8g .. +7; fp32: (D/4) g + 4i
+  uint4 o[NQ];  // bf16: the bf16 copy of dout, dims 32kk + 8g .. +7; fp32: dims (D/4) g + 4i ..
   float2 lr;
   int64_t row;
   int32_t pair;
@@ -165,7 +179,7 @@ struct PairIn {
 
 template <typename T, int D>
 __device__ __forceinline__ void fetch(PairIn<T, D>& x, const T* __restrict__ q,
-                                      const float* __restrict__ dout, const float2* __restrict__ ld,
+                                      const void* __restrict__ dout, const float2* __restrict__ ld,
                                       int32_t entry, bool live, int64_t row0, int64_t npairs,
                                       uint64_t div_magic, int div_shift, int g) {
   if (entry < 0 || entry >= npairs) live = false;
@@ -173,24 +187,23 @@ __device__ __forceinline__ void fetch(PairIn<T, D>& x, const T* __restrict__ q,
   x.pair = live ? entry : 0;
   x.row = row0 + static_cast<int64_t>((static_cast<uint64_t>(x.pair) * div_magic) >> div_shift);
 #pragma unroll
-  for (int i = 0; i < PairIn<T, D>::NQ; ++i) x.q[i] = uint4{0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int i = 0; i < D / 16; ++i) x.o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int i = 0; i < PairIn<T, D>::NQ; ++i) x.q[i] = x.o[i] = uint4{0u, 0u, 0u, 0u};
   if (live) {
     if constexpr (sizeof(T) == 2) {
+      const bf16_bits* ob = static_cast<const bf16_bits*>(dout);
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
         const int d0 = 32 * kk + 8 * g;
         x.q[kk] = ld16(q + x.row * D + d0);
-        x.o[2 * kk] = *reinterpret_cast<const float4*>(dout + x.row * D + d0);
-        x.o[2 * kk + 1] = *reinterpret_cast<const float4*>(dout + x.row * D + d0 + 4);
+        x.o[kk] = ld16(ob + x.row * D + d0);
       }
     } else {
       constexpr int KS = D / 4;
+      const float* of = static_cast<const float*>(dout);
 #pragma unroll
       for (int i = 0; i < D / 16; ++i) {
         x.q[i] = ld16(q + x.row * D + KS * g + 4 * i);
-        x.o[i] = *reinterpret_cast<const float4*>(dout + x.row * D + KS * g + 4 * i);
+        x.o[i] = ld16(of + x.row * D + KS * g + 4 * i);
       }
     }
   }
@@ -203,9 +216,7 @@ __device__ __forceinline__ void ready(PairRows<T, D>& pr, const PairIn<T, D>& x)
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
       pr.qb[kk] = as_bf16x8(x.q[kk]);
-      const float4 a = x.o[2 * kk], b = x.o[2 * kk + 1];
-      pr.ob[kk] = bf16x8{f32_to_bf16(a.x), f32_to_bf16(a.y), f32_to_bf16(a.z), f32_to_bf16(a.w),
-                         f32_to_bf16(b.x), f32_to_bf16(b.y), f32_to_bf16(b.z), f32_to_bf16(b.w)};
+      pr.ob[kk] = as_bf16x8(x.o[kk]);
     }
   } else {
 #pragma unroll
@@ -214,10 +225,10 @@ __device__ __forceinline__ void ready(PairRows<T, D>& pr, const PairIn<T, D>& x)
       pr.qf[4 * i + 1] = __uint_as_float(x.q[i].y);
       pr.qf[4 * i + 2] = __uint_as_float(x.q[i].z);
       pr.qf[4 * i + 3] = __uint_as_float(x.q[i].w);
-      pr.of[4 * i] = x.o[i].x;
-      pr.of[4 * i + 1] = x.o[i].y;
-      pr.of[4 * i + 2] = x.o[i].z;
-      pr.of[4 * i + 3] = x.o[i].w;
+      pr.of[4 * i] = __uint_as_float(x.o[i].x);
+      pr.of[4 * i + 1] = __uint_as_float(x.o[i].y);
+      pr.of[4 * i + 2] = __uint_as_float(x.o[i].z);
+      pr.of[4 * i + 3] = __uint_as_float(x.o[i].w);
     }
   }
 }
@@ -264,7 +275,7 @@ __device__ __forceinline__ void scores(const T* ks, const T* vs, const PairRows<
 template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void bwd_pair_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
-    const float* __restrict__ dout, const float2* __restrict__ ld,
+    const void* __restrict__ dout, const float2* __restrict__ ld,
     const int32_t* __restrict__ list, const int32_t* __restrict__ items,
     const int4* __restrict__ item_rec, int nbuckets, int64_t row0, int64_t npairs, int n,
     uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, int klim_last, float scale,
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
   if (b < 0 || b >= nbuckets) return;
   const int64_t first = rec.y;
   int cnt = rec.z;
-  if (cnt > kItem) cnt = kItem;
+  if (cnt > bwd_item_pairs(D)) cnt = bwd_item_pairs(D);
   if (first + cnt > npairs) cnt = first < npairs ? static_cast<int>(npairs - first) : 0;
   const int nb = n / kTile;
   const int beta = b % nb;
@@ -594,7 +605,7 @@ template <typename T, int D, bool CAUSAL>
 hipError_t pairs_launch(const BackwardArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
   using L = BwdLayout<T, D>;
   const Geom c(a, row0, rows);
-  const int64_t grid = gather_grid(rows, a.topk, c.nbuckets, kItem);
+  const int64_t grid = gather_grid(rows, a.topk, c.nbuckets, bwd_item_pairs(D));
   int lg = 0;
   while ((1 << lg) < a.topk) ++lg;
   const int shift = 32 + lg;
@@ -608,7 +619,8 @@ hipError_t pairs_launch(const BackwardArgs& a, int64_t row0, int64_t rows, hipSt
   }
   hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(grid)), dim3(256), L::BYTES, s,
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
-                     a.dout, a.ld, a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets, row0, c.npairs,
+                     sizeof(T) == 2 ? static_cast<const void*>(a.dout_b) : static_cast<const void*>(a.dout),
+                     a.ld, a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets, row0, c.npairs,
                      a.n, magic, shift, c.bh0, a.qsegs, klim_last, a.scale, a.scale * kLog2e,
                      a.dq_part, a.dkv_part);
   return hipGetLastError();
@@ -623,10 +635,11 @@ hipError_t pairs_dispatch(const BackwardArgs& a, int64_t row0, int64_t rows, hip
 
 hipError_t launch_bwd_prep(const BackwardArgs& a, int64_t rows, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((rows + 15) / 16));
+  bf16_bits* ob = a.dtype == BSA_BF16 ? a.dout_b : nullptr;
   if (a.d == 64)
-    hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, dim3(256), 0, s, a.out, a.dout, a.lse, a.ld, rows);
+    hipLaunchKernelGGL(bwd_prep_kernel<64>, grid, dim3(256), 0, s, a.out, a.dout, a.lse, a.ld, ob, rows);
   else
-    hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, dim3(256), 0, s, a.out, a.dout, a.lse, a.ld, rows);
+    hipLaunchKernelGGL(bwd_prep_kernel<128>, grid, dim3(256), 0, s, a.out, a.dout, a.lse, a.ld, ob, rows);
   return hipGetLastError();
 }
 
