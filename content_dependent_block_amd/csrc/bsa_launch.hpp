@@ -143,7 +143,8 @@ struct BackwardArgs {
   int qsegs = 1;
   float2* ld = nullptr;      // [bh * n] (lse * log2(e), sum_d dout * out)
   uint16_t* dout_b = nullptr; // [bh * n][d] dout rounded to bf16 (bf16 inputs only)
-  float* dq_part = nullptr;  // [chunk pairs][d]  per-pair dq contributions
+  float* dq_part = nullptr;  // [chunk pairs][d]  per-pair dq contributions (fp16 for bf16 inputs)
+  int32_t* dq_exp = nullptr; // [chunk pairs]  bf16 inputs: the rows' power-of-two scales
   float* dkv_part = nullptr; // [work items][2][64][d]  per-item dk, dv contributions
   GatherWorkspace ws;        // bucketing (count .. list); partial_o / partial_ml unused
 };

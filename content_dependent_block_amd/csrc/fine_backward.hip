@@ -18,8 +18,9 @@
 //   S^T = K Q^T and dP^T = V dO^T on MFMA (64 keys x 16 pairs per wave),
 //   P^T, dS^T in registers,
 //   dQ^T = K^T dS^T on MFMA: the pair's dq contribution from this block, one
-//         row per pair, summed per query by bwd_dq in slot order (the same
-//         bits on every call);
+//         row per pair (bf16 inputs: fp16 with a power-of-two scale per
+//         row), summed per query by bwd_dq in slot order (the same bits on
+//         every call);
 //   dV += P^T dO and dK += dS^T Q on MFMA, each wave owning 16 keys of the
 //         block and summing over all 64 pairs of the tile (P^T, dS^T, dO,
 //         Q pass through LDS).
@@ -279,7 +280,8 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
     const int32_t* __restrict__ list, const int32_t* __restrict__ items,
     const int4* __restrict__ item_rec, int nbuckets, int64_t row0, int64_t npairs, int n,
     uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, int klim_last, float scale,
-    float scale_log2, float* __restrict__ dq_part, float* __restrict__ dkv_part) {
+    float scale_log2, float* __restrict__ dq_part, int32_t* __restrict__ dq_exp,
+    float* __restrict__ dkv_part) {
   using L = BwdLayout<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   T* ks = reinterpret_cast<T*>(smem);
@@ -377,14 +379,33 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
           acc[dt] = mfma_16x16x32_bf16(a, bs, acc[dt]);
         }
       }
+      // The pair's dq row as fp16 with one power-of-two scale per row: the
+      // row is divided by 2^ex, ex the exponent of its largest magnitude,
+      // so every entry is below 1 (no overflow) and keeps 11 bits relative
+      // to the largest.
+      float mx = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(acc[dt][e]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));  // the 4 lanes of the pair's column
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // mx * scale = f * 2^ex with f in [0.5, 1) (v_frexp_exp_i32_f32)
+      const int ex = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx * scale) : 0;
+      const float mul = __builtin_ldexpf(scale, -ex);
       if (live) {
-        float* dst = dq_part + static_cast<int64_t>(pair) * D + 8 * g;
+        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+        _Float16* dst = reinterpret_cast<_Float16*>(dq_part) + static_cast<int64_t>(pair) * D + 8 * g;
 #pragma unroll
         for (int u = 0; u < D / 32; ++u) {
-          const f32x4 a0 = acc[2 * u] * scale, a1 = acc[2 * u + 1] * scale;
-          *reinterpret_cast<float4*>(dst + 32 * u) = make_float4(a0[0], a0[1], a0[2], a0[3]);
-          *reinterpret_cast<float4*>(dst + 32 * u + 4) = make_float4(a1[0], a1[1], a1[2], a1[3]);
+          const f32x4 a0 = acc[2 * u] * mul, a1 = acc[2 * u + 1] * mul;
+          const f16x8 h = {static_cast<_Float16>(a0[0]), static_cast<_Float16>(a0[1]),
+                           static_cast<_Float16>(a0[2]), static_cast<_Float16>(a0[3]),
+                           static_cast<_Float16>(a1[0]), static_cast<_Float16>(a1[1]),
+                           static_cast<_Float16>(a1[2]), static_cast<_Float16>(a1[3])};
+          *reinterpret_cast<f16x8*>(dst + 32 * u) = h;
         }
+        if (g == 0) dq_exp[pair] = ex;
       }
     } else {
 #pragma unroll
@@ -499,15 +520,18 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
 // contributions.  16 lanes per row; 8 slots at a time, every lane issues the
 // loads of its D/16 dims of all 8 before adding any (slot index clamped into
 // the row so every load is in bounds; slots that are padding were never
-// written and are dropped by a select).
-template <int D>
+// written and are dropped by a select).  HALF: the rows are fp16 times
+// 2^dq_exp[pair] (bf16 inputs), else fp32.
+template <int D, bool HALF>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__ idx,
-                                                     const float* __restrict__ dq_part,
+                                                     const void* __restrict__ dq_part,
+                                                     const int32_t* __restrict__ dq_exp,
                                                      float* __restrict__ dq, int64_t row0,
                                                      int64_t rows, int n, int topk, int causal) {
   constexpr int E = D / 16;
   constexpr int V = E / 4;
   constexpr int S = 8;
+  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   if (r >= rows) return;
   const int c = threadIdx.x & 15;
@@ -516,17 +540,28 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__
   f32x4 acc[V];
 #pragma unroll
   for (int u = 0; u < V; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const float* src = dq_part + r * topk * D + c * E;
   for (int s0 = 0; s0 < topk; s0 += S) {
     f32x4 x[S][V];
     bool ok[S];
 #pragma unroll
     for (int t = 0; t < S; ++t) {
       const int st = s0 + t < topk ? s0 + t : topk - 1;
+      const int64_t pr = r * topk + st;
       ok[t] = s0 + t < topk && pair_valid(idx[row * topk + st], nb, row, n, causal);
+      if constexpr (HALF) {
+        const f16x4* src = reinterpret_cast<const f16x4*>(static_cast<const _Float16*>(dq_part) + pr * D + c * E);
+        const int ex = dq_exp[pr];
 #pragma unroll
-      for (int u = 0; u < V; ++u)
-        x[t][u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + static_cast<int64_t>(st) * D) + u);
+        for (int u = 0; u < V; ++u) {
+          const f16x4 h = __builtin_nontemporal_load(src + u);
+          x[t][u] = f32x4{__builtin_ldexpf(static_cast<float>(h[0]), ex), __builtin_ldexpf(static_cast<float>(h[1]), ex),
+                          __builtin_ldexpf(static_cast<float>(h[2]), ex), __builtin_ldexpf(static_cast<float>(h[3]), ex)};
+        }
+      } else {
+        const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(dq_part) + pr * D + c * E);
+#pragma unroll
+        for (int u = 0; u < V; ++u) x[t][u] = __builtin_nontemporal_load(src + u);
+      }
     }
 #pragma unroll
     for (int t = 0; t < S; ++t)
@@ -622,7 +657,7 @@ hipError_t pairs_launch(const BackwardArgs& a, int64_t row0, int64_t rows, hipSt
                      sizeof(T) == 2 ? static_cast<const void*>(a.dout_b) : static_cast<const void*>(a.dout),
                      a.ld, a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets, row0, c.npairs,
                      a.n, magic, shift, c.bh0, a.qsegs, klim_last, a.scale, a.scale * kLog2e,
-                     a.dq_part, a.dkv_part);
+                     a.dq_part, a.dq_exp, a.dkv_part);
   return hipGetLastError();
 }
 
@@ -652,12 +687,22 @@ hipError_t launch_bwd_pairs(const BackwardArgs& a, int64_t row0, int64_t rows, h
 
 hipError_t launch_bwd_dq(const BackwardArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((rows + 15) / 16));
-  if (a.d == 64)
-    hipLaunchKernelGGL(bwd_dq_kernel<64>, grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq, row0, rows, a.n,
-                       a.topk, a.causal);
-  else
-    hipLaunchKernelGGL(bwd_dq_kernel<128>, grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq, row0, rows, a.n,
-                       a.topk, a.causal);
+  const bool half = a.dtype == BSA_BF16;
+  if (a.d == 64) {
+    if (half)
+      hipLaunchKernelGGL((bwd_dq_kernel<64, true>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq_exp, a.dq,
+                         row0, rows, a.n, a.topk, a.causal);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<64, false>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq_exp, a.dq,
+                         row0, rows, a.n, a.topk, a.causal);
+  } else {
+    if (half)
+      hipLaunchKernelGGL((bwd_dq_kernel<128, true>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq_exp, a.dq,
+                         row0, rows, a.n, a.topk, a.causal);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<128, false>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq_exp, a.dq,
+                         row0, rows, a.n, a.topk, a.causal);
+  }
   return hipGetLastError();
 }
 
