@@ -272,6 +272,29 @@ def test_backward_headline_sampled(bsa):
     assert err <= 1e-2 * np.abs(do_sum).max()
 
 
+def test_backward_causal_long_sampled(bsa):
+    """The long causal workload at full size (8 x 131072 x 128, k = 32): the
+    dq rows span eight row chunks, so dk and dv are summed across chunks.
+    dq on sampled rows, dk and dv on sampled key blocks of the later half of
+    the sequence (fewer rows select them, which keeps the oracle short)."""
+    m, lib = bsa
+    w = W.WORKLOADS["causal_bf16_n128k"]
+    inp = W.generate(w)
+    b, h, n, d = inp.q.shape
+    say(f"[gpu] backward causal long n={n} heads={h} d={d} k={w.topk}")
+    qkv, out, idx, lse = forward_train(m, lib, w, inp, w.topk, True)
+    dout = W.grad_output(inp.q.shape, w.seed)
+    g = gpu_backward(m, lib, qkv, out, torch.from_numpy(dout).cuda(), idx, lse, w.scale, True)
+    del qkv, out, lse
+    rng = np.random.default_rng(13)
+    rows = np.sort(rng.choice(b * h * n, 400, replace=False))
+    nb = n // w.block
+    heads = rng.integers(0, b * h, size=3)
+    blocks = np.sort(heads * nb + rng.integers(nb // 2, nb, size=3))
+    compare_grads(w, inp, dout, idx.cpu().numpy().reshape(-1, w.topk), g, True, w.scale,
+                  rows=rows, blocks=blocks)
+
+
 def test_backward_deterministic_and_chunked(bsa):
     """Two calls give identical dq bits and dk, dv equal within rounding (the
     order of a block's pairs comes from the bucketing's atomics); a small row
