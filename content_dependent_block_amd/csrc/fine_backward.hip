@@ -91,9 +91,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
 template <typename T, int D>
 struct BwdLayout {
   static constexpr bool kBf16 = sizeof(T) == 2;
-  // K, V natural [64 keys][KP]; bf16 also K^T [D][KTP keys].
+  // K, V natural [64 keys][KP]; bf16 also K^T [D][KTP key positions], the
+  // keys of each row in the order ktpos gives.
   static constexpr int KP = D + (kBf16 ? 16 : 4);
-  static constexpr int KTP = kTile + 4;
+  static constexpr int KTP = kTile + 16;
   // P^T or dS^T [64 keys][PP pairs].
   static constexpr int PP = kTile + (kBf16 ? 16 : 4);
   // bf16: dO^T or Q^T [D][PP pairs]; fp32: dO or Q natural [64 pairs][KP].
@@ -115,6 +116,15 @@ struct BwdLayout {
   static constexpr int BYTES = OFF_O + (kDual ? 2 : 1) * O_BYTES;
 };
 
+// Position of key k inside a K^T row: within each group of 32 keys, key
+// 16h + 4g + i (h < 2, g < 4, i < 4) sits at 8g + 4h + i, so the eight keys
+// lane group g feeds to one k-step of dQ^T = K^T dS^T (4g .. 4g+3 and
+// 16 + 4g .. 16 + 4g + 3, the order of S^T's C layout) are one aligned
+// 16-byte read.  Keys 2p and 2p + 1 stay adjacent.
+__device__ __forceinline__ int ktpos(int k) {
+  return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
+}
+
 // K and V of one key block into LDS (K natural and, for bf16, transposed;
 // V natural).  bf16: every thread moves keys (2p, 2p+1) x 8 dims, so K^T gets
 // two keys per 32-bit LDS write.  fp32: 16-byte pieces of key rows.
@@ -134,7 +144,7 @@ __device__ __forceinline__ void stage_kv(const T* __restrict__ kb, const T* __re
       *reinterpret_cast<uint4*>(vs + (2 * p + 1) * L::KP + c8 * 8) = v1;
       const uint32_t a[4] = {k0.x, k0.y, k0.z, k0.w};
       const uint32_t b[4] = {k1.x, k1.y, k1.z, k1.w};
-      uint32_t* dst = reinterpret_cast<uint32_t*>(kt + (c8 * 8) * L::KTP + 2 * p);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(kt + (c8 * 8) * L::KTP + ktpos(2 * p));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         // dim c8*8 + 2e (low halves) and + 2e + 1 (high halves); keys 2p, 2p+1
@@ -232,13 +242,6 @@ __device__ __forceinline__ void ready(PairRows<T, D>& pr, const PairIn<T, D>& x)
       pr.of[4 * i + 3] = __uint_as_float(x.o[i].w);
     }
   }
-}
-
-// Output dim carried by row m of output tile dt in dQ^T = K^T dS^T (bf16):
-// the K^T rows are permuted so that lane group g ends up with 8 consecutive
-// dims per pair of tiles (32u + 8g .. +7 for tiles 2u, 2u + 1).
-__device__ __forceinline__ int dq_dim(int dt, int m) {
-  return 32 * (dt / 2) + 8 * (m / 4) + 4 * (dt % 2) + (m % 4);
 }
 
 // One wave's 64 keys x 16 pairs: S^T = K Q^T and dP^T = V dO^T.
@@ -372,10 +375,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
         }
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-          const T* kr = kt + dq_dim(dt, c16) * L::KTP + 32 * kk + 4 * g;
-          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(kr);
-          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(kr + 16);
-          const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + (16 * dt + c16) * L::KTP + 32 * kk + 8 * g);
           acc[dt] = mfma_16x16x32_bf16(a, bs, acc[dt]);
         }
       }
@@ -394,16 +394,15 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
       const int ex = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx * scale) : 0;
       const float mul = __builtin_ldexpf(scale, -ex);
       if (live) {
-        typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-        _Float16* dst = reinterpret_cast<_Float16*>(dq_part) + static_cast<int64_t>(pair) * D + 8 * g;
+        // acc[dt][e] = dq of dim 16 dt + 4g + e (C layout: row 4g + e)
+        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+        _Float16* dst = reinterpret_cast<_Float16*>(dq_part) + static_cast<int64_t>(pair) * D + 4 * g;
 #pragma unroll
-        for (int u = 0; u < D / 32; ++u) {
-          const f32x4 a0 = acc[2 * u] * mul, a1 = acc[2 * u + 1] * mul;
-          const f16x8 h = {static_cast<_Float16>(a0[0]), static_cast<_Float16>(a0[1]),
-                           static_cast<_Float16>(a0[2]), static_cast<_Float16>(a0[3]),
-                           static_cast<_Float16>(a1[0]), static_cast<_Float16>(a1[1]),
-                           static_cast<_Float16>(a1[2]), static_cast<_Float16>(a1[3])};
-          *reinterpret_cast<f16x8*>(dst + 32 * u) = h;
+        for (int dt = 0; dt < D / 16; ++dt) {
+          const f32x4 a = acc[dt] * mul;
+          const f16x4 h = {static_cast<_Float16>(a[0]), static_cast<_Float16>(a[1]),
+                           static_cast<_Float16>(a[2]), static_cast<_Float16>(a[3])};
+          *reinterpret_cast<f16x4*>(dst + 16 * dt) = h;
         }
         if (g == 0) dq_exp[pair] = ex;
       }
