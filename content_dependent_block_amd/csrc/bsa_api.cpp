@@ -39,7 +39,8 @@ struct bsa_handle_s {
     size_t bytes = 0;
   };
   Buf g_count, g_offsets, g_items, g_item_rec, g_rank, g_rec, g_wgv, g_list, g_po, g_pml;
-  Buf b_ld, b_dq, b_dqe, b_dkv, b_dob;  // backward: per-row (lse, delta), per-pair dq, per-item dk/dv, bf16 dout
+  Buf b_ld, b_dq, b_dqe, b_dkv, b_dob;
+  bool counts_zero = false;  // g_count holds zeros (the bucketing's scan leaves it so)  // backward: per-row (lse, delta), per-pair dq, per-item dk/dv, bf16 dout
   Buf r_q, r_k, r_v, r_o, r_do, r_lse, r_idx, r_dq, r_dk, r_dv;  // padded copies (ragged n)
   // timing
   bool profiling = false;
@@ -355,6 +356,27 @@ bsa_status grow_buf(bsa_handle h, bsa_handle_s::Buf& b, size_t need, const char*
   return grow(h, &b.p, &b.bytes, need, what);
 }
 
+// The bucket counts must be zero when a bucketing starts; the scan kernel
+// clears them after use, so only a new buffer or a failed launch needs a
+// clearing kernel.  Returns the words to clear (0 if none) and assumes the
+// bucketing about to be enqueued succeeds; run_gather_index undoes that on
+// failure.
+bsa_status grow_counts(bsa_handle h, size_t buckets, int64_t* clear_words) {
+  void* before = h->g_count.p;
+  TRY(grow_buf(h, h->g_count, buckets * 4, "bucket counts"));
+  if (h->g_count.p != before) h->counts_zero = false;
+  *clear_words = h->counts_zero ? 0 : int64_t(h->g_count.bytes / 4);
+  return BSA_OK;
+}
+
+bsa_status run_gather_index(bsa_handle h, bsa::GatherArgs& a, int64_t r0, int64_t rows, int stage,
+                            const char* what, hipStream_t st) {
+  const bsa_status r = timed_launch(h, stage, st, what, [&] { return bsa::launch_gather_index(a, r0, rows, st); });
+  h->counts_zero = r == BSA_OK;
+  a.ws.count_words = 0;  // cleared by the first bucketing of this call
+  return r;
+}
+
 // Stage 2 for the dynamic path, with the handle's fine strategy.
 bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, float* out,
                     float* lse, const int32_t* idx, const Shape& s, bsa_dtype dt, int topk,
@@ -375,7 +397,8 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   const int qsegs = bsa::gather_segments(s.n, s.d, topk, dt);
   const int64_t heads_spanned = s.bh() < (chunk + s.n - 1) / s.n + 1 ? s.bh() : (chunk + s.n - 1) / s.n + 1;
   const int64_t buckets = heads_spanned * qsegs * nb;
-  TRY(grow_buf(h, h->g_count, size_t(buckets) * 4, "bucket counts"));
+  int64_t clear_words = 0;
+  TRY(grow_counts(h, size_t(buckets), &clear_words));
   TRY(grow_buf(h, h->g_offsets, size_t(buckets + 1) * 4, "bucket offsets"));
   TRY(grow_buf(h, h->g_items, size_t(buckets + 1) * 4, "bucket work items"));
   TRY(grow_buf(h, h->g_item_rec, size_t(bsa::gather_grid(chunk, topk, buckets, bsa::kGatherItemPairs)) * 16,
@@ -402,6 +425,7 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   a.qsegs = qsegs;
   a.nv = nv;
   a.ws.count = static_cast<int32_t*>(h->g_count.p);
+  a.ws.count_words = clear_words;
   a.ws.offsets = static_cast<int32_t*>(h->g_offsets.p);
   a.ws.items = static_cast<int32_t*>(h->g_items.p);
   a.ws.item_rec = static_cast<int4*>(h->g_item_rec.p);
@@ -413,8 +437,7 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   a.ws.partial_ml = static_cast<float2*>(h->g_pml.p);
   for (int64_t r0 = 0; r0 < total; r0 += chunk) {
     const int64_t rows = (total - r0) < chunk ? (total - r0) : chunk;
-    TRY(timed_launch(h, BSA_STAGE_GATHER_INDEX, st, "block-gather bucketing",
-                     [&] { return bsa::launch_gather_index(a, r0, rows, st); }));
+    TRY(run_gather_index(h, a, r0, rows, BSA_STAGE_GATHER_INDEX, "block-gather bucketing", st));
     TRY(timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd",
                      [&] { return bsa::launch_gather_partial(a, r0, rows, st); }));
     TRY(timed_launch(h, BSA_STAGE_GATHER_COMBINE, st, "block-gather combine",
@@ -723,7 +746,8 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   const int64_t heads_spanned = sp.bh() < (chunk + sp.n - 1) / sp.n + 1 ? sp.bh() : (chunk + sp.n - 1) / sp.n + 1;
   const int64_t buckets = heads_spanned * qsegs * nb;
   const int64_t slots = bsa::gather_grid(chunk, topk, buckets, bsa::bwd_item_pairs(sp.d));
-  TRY(grow_buf(h, h->g_count, size_t(buckets) * 4, "bucket counts"));
+  int64_t clear_words = 0;
+  TRY(grow_counts(h, size_t(buckets), &clear_words));
   TRY(grow_buf(h, h->g_offsets, size_t(buckets + 1) * 4, "bucket offsets"));
   TRY(grow_buf(h, h->g_items, size_t(buckets + 1) * 4, "bucket work items"));
   TRY(grow_buf(h, h->g_item_rec, size_t(slots) * 16, "work-item records"));
@@ -761,6 +785,7 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   a.dq_exp = static_cast<int32_t*>(h->b_dqe.p);
   a.dkv_part = static_cast<float*>(h->b_dkv.p);
   a.ws.count = static_cast<int32_t*>(h->g_count.p);
+  a.ws.count_words = clear_words;
   a.ws.offsets = static_cast<int32_t*>(h->g_offsets.p);
   a.ws.items = static_cast<int32_t*>(h->g_items.p);
   a.ws.item_rec = static_cast<int4*>(h->g_item_rec.p);
@@ -783,8 +808,7 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
                    [&] { return bsa::launch_bwd_prep(a, total, st); }));
   for (int64_t r0 = 0; r0 < total; r0 += chunk) {
     const int64_t rows = (total - r0) < chunk ? (total - r0) : chunk;
-    TRY(timed_launch(h, BSA_STAGE_BWD_INDEX, st, "backward bucketing",
-                     [&] { return bsa::launch_gather_index(gi, r0, rows, st); }));
+    TRY(run_gather_index(h, gi, r0, rows, BSA_STAGE_BWD_INDEX, "backward bucketing", st));
     TRY(timed_launch(h, BSA_STAGE_BWD_PAIRS, st, "backward pair kernel",
                      [&] { return bsa::launch_bwd_pairs(a, r0, rows, st); }));
     TRY(timed_launch(h, BSA_STAGE_BWD_REDUCE, st, "backward dq reduction",

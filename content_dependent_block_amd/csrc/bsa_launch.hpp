@@ -74,7 +74,9 @@ hipError_t launch_sparse_flash_static(const void* q, const void* k, const void* 
 // split-softmax partials, merged per query.  Three launch groups per chunk of
 // query rows [row0, row0 + rows) (row0, rows multiples of 64).
 struct GatherWorkspace {
-  int32_t* count = nullptr;    // [buckets]      buckets = heads spanned by a chunk * n/64
+  int32_t* count = nullptr;    // [buckets]      buckets = heads spanned by a chunk * n/64; zero
+                               // between bucketings (the scan kernel clears what it read)
+  int64_t count_words = 0;     // > 0: clear count[0 .. count_words) first (its contents unknown)
   int32_t* offsets = nullptr;  // [buckets + 1]
   int32_t* items = nullptr;    // [buckets + 1]
   int4* item_rec = nullptr;    // [gather_grid(...)]  per-workgroup work-item records

@@ -193,13 +193,14 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
 }
 
 // Single workgroup of 1024 threads.  offsets[b] / items[b] are exclusive
-// prefixes; entry nbuckets holds the totals.  Passes of 1024 x 16 buckets:
+// prefixes; entry nbuckets holds the totals.  It leaves count[] zero, as the
+// next bucketing's count kernel needs it.  Passes of 1024 x 16 buckets:
 // the counts are loaded coalesced into LDS, each thread sums a contiguous run
 // of 16, one block-wide scan of the run sums (waves, then the 16 wave totals)
 // gives every run its base, and the prefixes go back through LDS to
 // coalesced stores.  Runs are padded to 17 words (no bank conflicts).
 constexpr int kScanRun = 16;
-__global__ __launch_bounds__(1024) void bucket_scan_kernel(const int32_t* __restrict__ count,
+__global__ __launch_bounds__(1024) void bucket_scan_kernel(int32_t* __restrict__ count,
                                                            int32_t* __restrict__ offsets,
                                                            int32_t* __restrict__ items,
                                                            int nbuckets, int item_pairs) {
@@ -213,6 +214,7 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(const int32_t* __rest
     for (int j = 0; j < kScanRun; ++j) {
       const int e = j * 1024 + t, b = base + e;  // element e of the pass lives in run e / 16
       s_c[(e / kScanRun) * RP + e % kScanRun] = b < nbuckets ? count[b] : 0;
+      if (b < nbuckets) count[b] = 0;  // the counts start at zero for the next bucketing
     }
     __syncthreads();
     int32_t v[kScanRun], sp = 0, si = 0;
@@ -752,8 +754,9 @@ size_t gather_pair_bytes(int d, bsa_dtype dtype) {
 
 hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
   const ChunkGeom c(a, row0, rows);
-  hipLaunchKernelGGL(zero_i32_kernel, dim3(static_cast<unsigned>((c.nbuckets + 255) / 256)), dim3(256),
-                     0, s, a.ws.count, static_cast<int64_t>(c.nbuckets));
+  if (a.ws.count_words > 0)  // counts not known to be zero (new buffer, or a failed launch)
+    hipLaunchKernelGGL(zero_i32_kernel, dim3(static_cast<unsigned>((a.ws.count_words + 255) / 256)), dim3(256),
+                       0, s, a.ws.count, a.ws.count_words);
   const int seg = a.n / a.qsegs;
   const int rpw = (seg % 256 == 0 && row0 % 256 == 0) ? 256 : kTile;
   const int64_t row_groups = (rows + rpw - 1) / rpw;
