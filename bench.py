@@ -55,7 +55,8 @@ def candidate_pairs(w: W.Workload) -> int:
 
 def stage_work(w: W.Workload):
     """Algorithmic work per launch of each kernel over the whole problem:
-    (bound, flops, bytes).  Bytes count each compulsory read/write once."""
+    (flops, bytes).  Bytes count each compulsory read/write once; a kernel's
+    roofline bound is whichever of the two takes longer at the MI355X peaks."""
     s = 2 if w.dtype == "bf16" else 4
     qkv = w.bh * w.n * w.d * s
     repr_b = w.bh * w.nb * w.d * 4
@@ -69,26 +70,28 @@ def stage_work(w: W.Workload):
         sel_pairs = int(w.bh * np.minimum(w.topk, i // w.block + 1).sum())
     partial = sel_pairs * (w.d * (2 if w.dtype == "bf16" else 4) + 8)
     out_b = w.bh * w.n * w.d * 4
+    rows = w.bh * w.n
+    dq_rows = sel_pairs * (w.d * s + (4 if w.dtype == "bf16" else 0))  # fp16 + scale, or fp32
     return {
-        "block_pool": ("hbm", 0, qkv + repr_b),
-        "coarse_score": ("hbm", 2 * w.d * cand, qkv + repr_b + panel),
-        "topk_select": ("hbm", 0, panel + idx),
+        "block_pool": (0, qkv + repr_b),
+        "coarse_score": (2 * w.d * cand, qkv + repr_b + panel),
+        "topk_select": (0, panel + idx),
         # fused scoring + selection: q and the representatives in, indices out
-        "coarse_select": ("mfma", 2 * w.d * cand, qkv + repr_b + idx),
+        "coarse_select": (2 * w.d * cand, qkv + repr_b + idx),
         # block-gather attention kernel: reads Q, K, V once, writes the partials
-        "sparse_flash_fwd": ("mfma", fine_flops, 3 * qkv + idx + partial),
-        "gather_index": ("hbm", 0, 2 * idx + 3 * sel_pairs * 4),
-        "gather_combine": ("hbm", 0, partial + idx + out_b),
-        # backward: out, dout and lse in, per-row (lse, delta) out
-        "bwd_prep": ("hbm", 0, 2 * out_b + w.bh * w.n * (4 + 8)),
-        "bwd_index": ("hbm", 0, 2 * idx + 3 * sel_pairs * 4),
-        # S, dP, dQ, dK, dV: five products per visible (query, key) pair;
-        # reads Q, K, V, dout (fp32) and the row statistics once, writes the
-        # per-pair dq rows
-        "bwd_pairs": ("mfma", 10 * w.d * visible_pairs(w),
-                      3 * qkv + out_b + w.bh * w.n * 8 + sel_pairs * w.d * 4),
-        # per-pair dq rows in, dq, dk, dv out
-        "bwd_reduce": ("hbm", 0, sel_pairs * w.d * 4 + idx + 3 * out_b),
+        "sparse_flash_fwd": (fine_flops, 3 * qkv + idx + partial),
+        "gather_index": (0, 2 * idx + 3 * sel_pairs * 4),
+        "gather_combine": (0, partial + idx + out_b),
+        # backward: out, dout and lse in; per-row (lse, delta) and (bf16 inputs) bf16 dout out
+        "bwd_prep": (0, 2 * out_b + rows * (4 + 8) + (qkv if w.dtype == "bf16" else 0)),
+        "bwd_index": (0, 2 * idx + 3 * sel_pairs * 4),
+        # S, dP, dQ, dK, dV: five products per visible (query, key) pair; reads
+        # Q, K, V, dout (bf16 copy for bf16 inputs) and the row statistics
+        # once, writes the per-pair dq rows
+        "bwd_pairs": (10 * w.d * visible_pairs(w),
+                      3 * qkv + (qkv if w.dtype == "bf16" else out_b) + rows * 8 + dq_rows),
+        # per-pair dq rows in; dq, dk, dv out
+        "bwd_reduce": (0, dq_rows + idx + 3 * out_b),
     }
 
 
@@ -239,9 +242,14 @@ def main():
 
     work = stage_work(w)
     dom = max(per_step, key=per_step.get)
-    bound, flops, nbytes = work[dom]
+    flops, nbytes = work[dom]
     t_launch = per_launch[dom] * 1e-3
     n_launch = launches_per_step[dom]
+    # the bound is the resource whose peak the kernel's algorithmic work
+    # would take longer on
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    bound = "mfma" if t_mfma >= t_hbm else "hbm"
     if bound == "mfma":
         achieved = flops / n_launch / t_launch / 1e12
         peak, unit = MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
@@ -253,7 +261,7 @@ def main():
                 "kernel": dom, "avg_launch_ms": round(per_launch[dom], 5),
                 "launches_per_step": n_launch}
 
-    total_flops = sum(work[k_][1] for k_ in per_step)  # matmul-only: coarse + fine, stages that ran
+    total_flops = sum(work[k_][0] for k_ in per_step)  # matmul-only: coarse + fine, stages that ran
     tokens = w.batch * w.n
     result = {
         "metric": METRIC if args.which == "forward" else METRIC_BWD,
