@@ -26,7 +26,8 @@
 //   pass 1: every lane keeps the maximum of each of its score groups, group =
 //     beta mod G with G = 64 * GM (16 * GM groups per lane, the 4 lanes of a
 //     query hold them all).  tau = the k_eff-th largest of the G group maxima
-//     (each lane sorts its own, then k_eff rounds of a 4-lane tournament).
+//     (each lane sorts its own; two pairwise bitonic merges between the
+//     query's 4 lanes, over the gfx950 permlane swaps, give all 4 the top).
 //     The k_eff groups whose maxima are >= tau each hold a score >= tau, so at
 //     least k_eff scores are >= tau, and every score of the answer is >= tau.
 //     For bf16 inputs pass 1 multiplies only the hi term of the split; tau is
@@ -35,14 +36,18 @@
 //     it a bound for the exact scores at a third of the MFMA and LDS work.
 //   pass 2: the same scores again; those >= tau (typically k + a few) are
 //     appended to the lane's LDS slots in ascending block order.
-//   The lane offers its slots to an exact register top-KL list (topk_list.hpp,
-//     KL >= k) and k_eff rounds of a cross-lane tournament between the 4
-//     lists take the answer in rank order; it is written in ascending block
-//     order.  Because the answer is ranked from pass 2's scores alone and
-//     pass 2 checks it holds >= k_eff candidates, the result is exact.
+//   The lane reads its slots into registers and sorts a copy of their
+//     scores; two pairwise merges between the query's 4 lanes give each the
+//     query's top scores, so T = the k_eff-th largest candidate.  The answer
+//     is every candidate above T plus the lowest-block ties at T; the 4 lanes
+//     put it in an LDS row, and each sorts the row's block ids and writes its
+//     quarter of the output in ascending block order.  Because the answer is
+//     ranked from pass 2's scores alone and pass 2 checks it holds >= k_eff
+//     candidates, the result is exact.
 //   A workgroup in which some lane has more candidates than slots (or fewer
-//     than k_eff candidates) redoes the walk offering every score to the
-//     lists: the same answer, slower.
+//     than k_eff candidates) redoes the walk offering every score to exact
+//     register top-KL lists (topk_list.hpp) merged the same way: the same
+//     answer, slower.
 // topk_select.hip states the selection semantics.
 //
 // Workgroups are issued XCD-major: consecutive workgroup ids go round-robin
@@ -531,6 +536,27 @@ __device__ __forceinline__ int sum4(int x, int lane) {
   return x + static_cast<int>(lane_xor<32>(static_cast<uint32_t>(x), lane));
 }
 
+// Bitonic sort of N ints, ascending.
+template <int N>
+__device__ __forceinline__ void sort_asc(int (&a)[N]) {
+#pragma unroll
+  for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+    for (int stride = size / 2; stride > 0; stride >>= 1) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const int lo = min(a[i], a[j]), hi = max(a[i], a[j]);
+          const bool up = (i & size) == 0;
+          a[i] = up ? lo : hi;
+          a[j] = up ? hi : lo;
+        }
+      }
+    }
+  }
+}
+
 // Stream the tiles of the workgroup's representatives through LDS, register-
 // prefetching tile bt + 1 while tile bt is computed, and hand each 16-block
 // MFMA tile to fast(h, mt, b0, acc) or slow(...) (b0 = first block of the
@@ -580,10 +606,13 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
   constexpr int MT = TL::TB / 16;     // MFMA tiles per R tile
   constexpr int NS = 16 * GM;         // group slots per lane
   constexpr int NH = NS / (4 * MT);   // R tiles per cycle of slots
-  static_assert(TL::LDS_BYTES >= 64 * 33 * 4, "the R tile buffer also holds the selection lists");
-  static_assert(TL::LDS_BYTES >= 256 * 16 + 128 * 4, "and the scratch of the pass-1 error bound");
+  // The R tile buffer also holds the scratch of the pass-1 error bound and,
+  // at the end, the selection lists (64 rows of 33) and a slot per lane.
+  constexpr int LIST_BYTES = (64 * 33 + 256) * 4;
+  constexpr int RS_BYTES = TL::LDS_BYTES > LIST_BYTES ? TL::LDS_BYTES : LIST_BYTES;
+  static_assert(TL::LDS_BYTES >= 256 * 16 + 128 * 4, "scratch of the pass-1 error bound");
   static_assert(CAP <= 32, "candidate slots are tracked in a 32-bit mask");
-  __shared__ __attribute__((aligned(16))) unsigned char rs[TL::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) unsigned char rs[RS_BYTES];
   // per lane: candidate scores and blocks
   __shared__ float cv[4][CAP][64];
   __shared__ uint16_t cb[4][CAP][64];
@@ -637,70 +666,91 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
   int32_t* dst = idx + ti.qrow * topk;
 
   if (!redo) {
-    // T = the keff-th largest candidate score of the query: every lane sorts
-    // its candidates' scores, two pairwise merges give all 4 lanes the
-    // query's top CAP.
-    int mc = cnt;
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) mc = max(mc, __shfl_xor(mc, m));
-    mc = __builtin_amdgcn_readfirstlane(mc);
+    // The lane's candidates, read once into registers: scores (-inf past
+    // cnt) and blocks, in ascending block order.
     const float(&lv)[CAP][64] = cv[ti.wave];
     const uint16_t(&lb)[CAP][64] = cb[ti.wave];
+    float x[CAP];
+    int bl[CAP];
+#pragma unroll
+    for (int i = 0; i < CAP; ++i) {
+      x[i] = i < cnt ? lv[i][ti.lane] : -INFINITY;
+      bl[i] = lb[i][ti.lane];
+    }
+    // T = the keff-th largest candidate score of the query: every lane sorts
+    // a copy of its scores, two pairwise merges give all 4 lanes the query's
+    // top CAP.
     float c[CAP];
 #pragma unroll
-    for (int i = 0; i < CAP; ++i) c[i] = i < cnt ? lv[i][ti.lane] : -INFINITY;
+    for (int i = 0; i < CAP; ++i) c[i] = x[i];
     sort_desc<CAP>(c);
     merge_top<16, CAP>(c, ti.lane);
     merge_top<32, CAP>(c, ti.lane);
     const float T = kth_desc<CAP>(c, keff);
-    // Selected: scores above T, and the lowest-index `need` of those equal to
-    // T.  A tie's rank among the query's ties = ties before it in its own
-    // lane (ascending blocks) + ties with lower blocks in the other 3 lanes.
+    // Selected: scores above T, and the lowest-block `need` of those equal to
+    // T; when exactly `need` candidates equal T (the usual case) all are.
     int gt = 0, eq = 0;
-    for (int i = 0; i < mc; ++i) {
-      const float x = i < cnt ? lv[i][ti.lane] : -INFINITY;
-      gt += x > T ? 1 : 0;
-      eq += x == T ? 1 : 0;
+#pragma unroll
+    for (int i = 0; i < CAP; ++i) {
+      gt += x[i] > T ? 1 : 0;
+      eq += x[i] == T ? 1 : 0;
     }
     const int need = keff - sum4(gt, ti.lane);
     const bool all_ties = sum4(eq, ti.lane) == need;
+    uint32_t selbits = 0u;
+#pragma unroll
+    for (int i = 0; i < CAP; ++i) selbits |= (x[i] > T || (x[i] == T && all_ties)) ? (1u << i) : 0u;
     const int cnt16 = static_cast<int>(lane_xor<16>(static_cast<uint32_t>(cnt), ti.lane));
     const int cnt32 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(cnt), ti.lane));
     const int cnt48 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(cnt16), ti.lane));
-    uint32_t selbits = 0u;
-    int ties_before = 0;
-    for (int i = 0; i < mc; ++i) {
-      const float x = i < cnt ? lv[i][ti.lane] : -INFINITY;
-      bool s = x > T;
-      if (x == T) {
-        int r = ties_before++;
-        if (!all_ties) {
-          const int beta = lb[i][ti.lane];
+    if (!all_ties) {
+      // A tie's rank among the query's ties = ties before it in its own lane
+      // (ascending blocks) + ties with lower blocks in the other 3 lanes.
+      int ties_before = 0;
+#pragma unroll
+      for (int i = 0; i < CAP; ++i) {
+        if (x[i] == T) {
+          int r = ties_before++;
           for (int m = 1; m < 4; ++m) {
             const int ln = ti.lane ^ (16 * m);
             const int cn = m == 1 ? cnt16 : m == 2 ? cnt32 : cnt48;
-            for (int jj = 0; jj < cn; ++jj) r += (lv[jj][ln] == T && lb[jj][ln] < beta) ? 1 : 0;
+            for (int jj = 0; jj < cn; ++jj) r += (lv[jj][ln] == T && lb[jj][ln] < bl[i]) ? 1 : 0;
           }
+          selbits |= r < need ? (1u << i) : 0u;
         }
-        s = r < need;
       }
-      selbits |= s ? (1u << i) : 0u;
     }
     // The query's selection into its row of an LDS list (the R tile buffer
-    // is free now), this lane's part after those of lanes g' < g.
+    // is free now), this lane's part after those of lanes g' < g; a lane
+    // writes unselected entries to a slot of its own.
     const int ns = __popc(selbits);
     const int n16 = static_cast<int>(lane_xor<16>(static_cast<uint32_t>(ns), ti.lane));
     const int n32 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(ns), ti.lane));
     const int n48 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(n16), ti.lane));
     int p = ((ti.g & 1) ? n16 : 0) + ((ti.g & 2) ? n32 + n48 : 0);
     int* list = reinterpret_cast<int*>(rs) + (ti.wave * 16 + ti.c16) * 33;  // odd pitch: no bank conflicts
-    for (int i = 0; i < mc; ++i)
-      if ((selbits >> i) & 1u) list[p++] = lb[i][ti.lane];
+    int* own = reinterpret_cast<int*>(rs) + 64 * 33 + ti.tid;
+#pragma unroll
+    for (int i = 0; i < CAP; ++i) {
+      const bool s = (selbits >> i) & 1u;
+      *(s ? list + p : own) = bl[i];
+      p += s ? 1 : 0;
+    }
     __syncthreads();
+    // Every lane of the query sorts the query's keff blocks; lane g writes
+    // entries g, g + 4, ..., and -1 from keff up to topk.
     int b[KL];
 #pragma unroll
     for (int u = 0; u < KL; ++u) b[u] = u < keff ? list[u] : 0x7fffffff;
-    emit_selection<KL>(b, ti.g, keff, topk, dst);
+    sort_asc<KL>(b);
+#pragma unroll
+    for (int t0 = 0; t0 < KL; t0 += 4) {
+      int me = b[t0];
+#pragma unroll
+      for (int e = 1; e < 4; ++e) me = ti.g == e ? b[t0 + e] : me;
+      const int t = t0 + ti.g;
+      if (t < topk) dst[t] = t < keff ? me : -1;
+    }
   } else {
     // slots overflowed somewhere in the workgroup: offer every score to
     // exact register lists and merge them pairwise
