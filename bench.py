@@ -71,7 +71,7 @@ def stage_work(w: W.Workload):
     partial = sel_pairs * (w.d * (2 if w.dtype == "bf16" else 4) + 8)
     out_b = w.bh * w.n * w.d * 4
     rows = w.bh * w.n
-    dq_rows = sel_pairs * (w.d * s + (4 if w.dtype == "bf16" else 0))  # fp16 + scale, or fp32
+    dq_rows = sel_pairs * w.d * s  # per-pair dq rows: bf16 (bf16 inputs) or fp32
     return {
         "block_pool": (0, qkv + repr_b),
         "coarse_score": (2 * w.d * cand, qkv + repr_b + panel),

@@ -39,7 +39,7 @@ struct bsa_handle_s {
     size_t bytes = 0;
   };
   Buf g_count, g_offsets, g_items, g_item_rec, g_rank, g_rec, g_wgv, g_list, g_po, g_pml;
-  Buf b_ld, b_dq, b_dqe, b_dkv, b_dob;
+  Buf b_ld, b_dq, b_dkv, b_dob;
   bool counts_zero = false;  // g_count holds zeros (the bucketing's scan leaves it so)  // backward: per-row (lse, delta), per-pair dq, per-item dk/dv, bf16 dout
   Buf r_q, r_k, r_v, r_o, r_do, r_lse, r_idx, r_dq, r_dk, r_dv;  // padded copies (ragged n)
   // timing
@@ -242,7 +242,7 @@ BSA_API bsa_status bsa_destroy(bsa_handle h) {
   if (h->panel) (void)hipFree(h->panel);
   if (h->idx) (void)hipFree(h->idx);
   for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_rec, &h->g_wgv, &h->g_list, &h->g_po, &h->g_pml,
-                 &h->b_ld, &h->b_dq, &h->b_dqe, &h->b_dkv, &h->b_dob, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
+                 &h->b_ld, &h->b_dq, &h->b_dkv, &h->b_dob, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
                  &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv})
     if (b->p) (void)hipFree(b->p);
   delete h;
@@ -279,7 +279,7 @@ BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
   if (!h || !bytes) return fail(h, BSA_ERR_INVALID_ARG, "bsa_workspace_bytes: NULL argument");
   *bytes = h->repr_bytes + h->split_bytes + h->panel_bytes + h->idx_bytes;
   for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_rec, &h->g_wgv, &h->g_list, &h->g_po, &h->g_pml,
-                 &h->b_ld, &h->b_dq, &h->b_dqe, &h->b_dkv, &h->b_dob, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
+                 &h->b_ld, &h->b_dq, &h->b_dkv, &h->b_dob, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
                  &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv})
     *bytes += b->bytes;
   return BSA_OK;
@@ -758,7 +758,6 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   TRY(grow_buf(h, h->b_ld, size_t(total) * 8, "backward row statistics"));
   if (dtype == BSA_BF16) TRY(grow_buf(h, h->b_dob, size_t(total) * sp.d * 2, "backward bf16 dout"));
   TRY(grow_buf(h, h->b_dq, size_t(pairs) * sp.d * elem_bytes(dtype), "backward dq contributions"));
-  TRY(grow_buf(h, h->b_dqe, size_t(pairs) * 4, "backward dq row scales"));
   TRY(grow_buf(h, h->b_dkv, size_t(slots) * 2 * 64 * sp.d * 4, "backward dk/dv contributions"));
   bsa::BackwardArgs a;
   a.q = q;
@@ -782,7 +781,6 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   a.ld = static_cast<float2*>(h->b_ld.p);
   a.dout_b = dtype == BSA_BF16 ? static_cast<uint16_t*>(h->b_dob.p) : nullptr;
   a.dq_part = static_cast<float*>(h->b_dq.p);
-  a.dq_exp = static_cast<int32_t*>(h->b_dqe.p);
   a.dkv_part = static_cast<float*>(h->b_dkv.p);
   a.ws.count = static_cast<int32_t*>(h->g_count.p);
   a.ws.count_words = clear_words;

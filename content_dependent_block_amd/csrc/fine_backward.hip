@@ -18,9 +18,8 @@
 //   S^T = K Q^T and dP^T = V dO^T on MFMA (64 keys x 16 pairs per wave),
 //   P^T, dS^T in registers,
 //   dQ^T = K^T dS^T on MFMA: the pair's dq contribution from this block, one
-//         row per pair (bf16 inputs: fp16 with a power-of-two scale per
-//         row), summed per query by bwd_dq in slot order (the same bits on
-//         every call);
+//         row per pair (rounded to bf16 for bf16 inputs), summed per query
+//         by bwd_dq in slot order (the same bits on every call);
 //   dV += P^T dO and dK += dS^T Q on MFMA, each wave owning 16 keys of the
 //         block and summing over all 64 pairs of the tile (P^T, dS^T, dO,
 //         Q pass through LDS).
@@ -283,7 +282,7 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
     const int32_t* __restrict__ list, const int32_t* __restrict__ items,
     const int4* __restrict__ item_rec, int nbuckets, int64_t row0, int64_t npairs, int n,
     uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, int klim_last, float scale,
-    float scale_log2, float* __restrict__ dq_part, int32_t* __restrict__ dq_exp,
+    float scale_log2, float* __restrict__ dq_part,
     float* __restrict__ dkv_part) {
   using L = BwdLayout<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -379,32 +378,19 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
           acc[dt] = mfma_16x16x32_bf16(a, bs, acc[dt]);
         }
       }
-      // The pair's dq row as fp16 with one power-of-two scale per row: the
-      // row is divided by 2^ex, ex the exponent of its largest magnitude,
-      // so every entry is below 1 (no overflow) and keeps 11 bits relative
-      // to the largest.
-      float mx = 0.f;
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mx = fmaxf(mx, fabsf(acc[dt][e]));
-      mx = fmaxf(mx, __shfl_xor(mx, 16));  // the 4 lanes of the pair's column
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // mx * scale = f * 2^ex with f in [0.5, 1) (v_frexp_exp_i32_f32)
-      const int ex = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx * scale) : 0;
-      const float mul = __builtin_ldexpf(scale, -ex);
+      // The pair's dq row, rounded to bf16 (fp32's range: no scale needed).
       if (live) {
         // acc[dt][e] = dq of dim 16 dt + 4g + e (C layout: row 4g + e)
-        typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-        _Float16* dst = reinterpret_cast<_Float16*>(dq_part) + static_cast<int64_t>(pair) * D + 4 * g;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(dq_part) + static_cast<int64_t>(pair) * D + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) {
-          const f32x4 a = acc[dt] * mul;
-          const f16x4 h = {static_cast<_Float16>(a[0]), static_cast<_Float16>(a[1]),
-                           static_cast<_Float16>(a[2]), static_cast<_Float16>(a[3])};
-          *reinterpret_cast<f16x4*>(dst + 16 * dt) = h;
+          const f32x4 a = acc[dt] * scale;
+          const uint32_t lo = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(a[0]))) |
+                              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(a[1]))) << 16);
+          const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(a[2]))) |
+                              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(a[3]))) << 16);
+          *reinterpret_cast<uint2*>(dst + 16 * dt) = make_uint2(lo, hi);
         }
-        if (g == 0) dq_exp[pair] = ex;
       }
     } else {
 #pragma unroll
@@ -519,18 +505,16 @@ __global__ __launch_bounds__(256) void bwd_pair_kernel(
 // contributions.  16 lanes per row; 8 slots at a time, every lane issues the
 // loads of its D/16 dims of all 8 before adding any (slot index clamped into
 // the row so every load is in bounds; slots that are padding were never
-// written and are dropped by a select).  HALF: the rows are fp16 times
-// 2^dq_exp[pair] (bf16 inputs), else fp32.
+// written and are dropped by a select).  HALF: the rows are bf16 (bf16
+// inputs), else fp32.
 template <int D, bool HALF>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__ idx,
                                                      const void* __restrict__ dq_part,
-                                                     const int32_t* __restrict__ dq_exp,
                                                      float* __restrict__ dq, int64_t row0,
                                                      int64_t rows, int n, int topk, int causal) {
   constexpr int E = D / 16;
   constexpr int V = E / 4;
   constexpr int S = 8;
-  typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   if (r >= rows) return;
   const int c = threadIdx.x & 15;
@@ -548,13 +532,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__
       const int64_t pr = r * topk + st;
       ok[t] = s0 + t < topk && pair_valid(idx[row * topk + st], nb, row, n, causal);
       if constexpr (HALF) {
-        const f16x4* src = reinterpret_cast<const f16x4*>(static_cast<const _Float16*>(dq_part) + pr * D + c * E);
-        const int ex = dq_exp[pr];
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2* src = reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(dq_part) + pr * D + c * E);
 #pragma unroll
         for (int u = 0; u < V; ++u) {
-          const f16x4 h = __builtin_nontemporal_load(src + u);
-          x[t][u] = f32x4{__builtin_ldexpf(static_cast<float>(h[0]), ex), __builtin_ldexpf(static_cast<float>(h[1]), ex),
-                          __builtin_ldexpf(static_cast<float>(h[2]), ex), __builtin_ldexpf(static_cast<float>(h[3]), ex)};
+          const u32x2 h = __builtin_nontemporal_load(src + u);
+          x[t][u] = f32x4{__uint_as_float(h[0] << 16), __uint_as_float(h[0] & 0xFFFF0000u),
+                          __uint_as_float(h[1] << 16), __uint_as_float(h[1] & 0xFFFF0000u)};
         }
       } else {
         const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(dq_part) + pr * D + c * E);
@@ -656,7 +640,7 @@ hipError_t pairs_launch(const BackwardArgs& a, int64_t row0, int64_t rows, hipSt
                      sizeof(T) == 2 ? static_cast<const void*>(a.dout_b) : static_cast<const void*>(a.dout),
                      a.ld, a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets, row0, c.npairs,
                      a.n, magic, shift, c.bh0, a.qsegs, klim_last, a.scale, a.scale * kLog2e,
-                     a.dq_part, a.dq_exp, a.dkv_part);
+                     a.dq_part, a.dkv_part);
   return hipGetLastError();
 }
 
@@ -689,17 +673,17 @@ hipError_t launch_bwd_dq(const BackwardArgs& a, int64_t row0, int64_t rows, hipS
   const bool half = a.dtype == BSA_BF16;
   if (a.d == 64) {
     if (half)
-      hipLaunchKernelGGL((bwd_dq_kernel<64, true>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq_exp, a.dq,
+      hipLaunchKernelGGL((bwd_dq_kernel<64, true>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq,
                          row0, rows, a.n, a.topk, a.causal);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<64, false>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq_exp, a.dq,
+      hipLaunchKernelGGL((bwd_dq_kernel<64, false>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq,
                          row0, rows, a.n, a.topk, a.causal);
   } else {
     if (half)
-      hipLaunchKernelGGL((bwd_dq_kernel<128, true>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq_exp, a.dq,
+      hipLaunchKernelGGL((bwd_dq_kernel<128, true>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq,
                          row0, rows, a.n, a.topk, a.causal);
     else
-      hipLaunchKernelGGL((bwd_dq_kernel<128, false>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq_exp, a.dq,
+      hipLaunchKernelGGL((bwd_dq_kernel<128, false>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq,
                          row0, rows, a.n, a.topk, a.causal);
   }
   return hipGetLastError();
