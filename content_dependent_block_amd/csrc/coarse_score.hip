@@ -666,17 +666,13 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
   int32_t* dst = idx + ti.qrow * topk;
 
   if (!redo) {
-    // The lane's candidates, read once into registers: scores (-inf past
-    // cnt) and blocks, in ascending block order.
+    // The lane's candidate scores, read once into registers (-inf past cnt),
+    // in ascending block order.
     const float(&lv)[CAP][64] = cv[ti.wave];
     const uint16_t(&lb)[CAP][64] = cb[ti.wave];
     float x[CAP];
-    int bl[CAP];
 #pragma unroll
-    for (int i = 0; i < CAP; ++i) {
-      x[i] = i < cnt ? lv[i][ti.lane] : -INFINITY;
-      bl[i] = lb[i][ti.lane];
-    }
+    for (int i = 0; i < CAP; ++i) x[i] = i < cnt ? lv[i][ti.lane] : -INFINITY;
     // T = the keff-th largest candidate score of the query: every lane sorts
     // a copy of its scores, two pairwise merges give all 4 lanes the query's
     // top CAP.
@@ -714,7 +710,7 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
           for (int m = 1; m < 4; ++m) {
             const int ln = ti.lane ^ (16 * m);
             const int cn = m == 1 ? cnt16 : m == 2 ? cnt32 : cnt48;
-            for (int jj = 0; jj < cn; ++jj) r += (lv[jj][ln] == T && lb[jj][ln] < bl[i]) ? 1 : 0;
+            for (int jj = 0; jj < cn; ++jj) r += (lv[jj][ln] == T && lb[jj][ln] < lb[i][ti.lane]) ? 1 : 0;
           }
           selbits |= r < need ? (1u << i) : 0u;
         }
@@ -733,23 +729,43 @@ __global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename
 #pragma unroll
     for (int i = 0; i < CAP; ++i) {
       const bool s = (selbits >> i) & 1u;
-      *(s ? list + p : own) = bl[i];
+      *(s ? list + p : own) = lb[i][ti.lane];
       p += s ? 1 : 0;
     }
     __syncthreads();
-    // Every lane of the query sorts the query's keff blocks; lane g writes
-    // entries g, g + 4, ..., and -1 from keff up to topk.
+    // Every lane of the query sorts the query's keff blocks (-1 from keff up
+    // to topk).  Rows of whole 16-byte chunks: lane g stores chunks g, g + 4,
+    // ..., so one store writes a 64-byte stretch of the row; otherwise lane g
+    // writes entries g, g + 4, ...
     int b[KL];
 #pragma unroll
     for (int u = 0; u < KL; ++u) b[u] = u < keff ? list[u] : 0x7fffffff;
     sort_asc<KL>(b);
 #pragma unroll
-    for (int t0 = 0; t0 < KL; t0 += 4) {
-      int me = b[t0];
+    for (int u = 0; u < KL; ++u) b[u] = u < keff ? b[u] : -1;
+    if (((reinterpret_cast<uintptr_t>(dst) | static_cast<uintptr_t>(topk) * 4u) & 15u) == 0) {
 #pragma unroll
-      for (int e = 1; e < 4; ++e) me = ti.g == e ? b[t0 + e] : me;
-      const int t = t0 + ti.g;
-      if (t < topk) dst[t] = t < keff ? me : -1;
+      for (int c0 = 0; c0 < KL / 4; c0 += 4) {
+        int v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] = b[4 * c0 + i];
+#pragma unroll
+          for (int h = 1; h < 4; ++h)
+            if (4 * (c0 + h) + i < KL) v[i] = ti.g == h ? b[4 * (c0 + h) + i] : v[i];
+        }
+        const int c = c0 + ti.g;
+        if (c < KL / 4 && 4 * c < topk) *reinterpret_cast<int4*>(dst + 4 * c) = make_int4(v[0], v[1], v[2], v[3]);
+      }
+    } else {
+#pragma unroll
+      for (int t0 = 0; t0 < KL; t0 += 4) {
+        int me = b[t0];
+#pragma unroll
+        for (int e = 1; e < 4; ++e) me = ti.g == e ? b[t0 + e] : me;
+        const int t = t0 + ti.g;
+        if (t < topk) dst[t] = me;
+      }
     }
   } else {
     // slots overflowed somewhere in the workgroup: offer every score to
