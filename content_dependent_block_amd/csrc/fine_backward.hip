@@ -90,12 +90,17 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
 template <typename T, int D>
 struct BwdLayout {
   static constexpr bool kBf16 = sizeof(T) == 2;
+  // Workgroups per CU the kernel is sized for (waves per SIMD): bf16 d = 64
+  // runs three (51 KB of LDS single-buffered, <= 168 VGPRs), bf16 d = 128
+  // two (80 KB with 8-element row pads, <= 256 VGPRs); fp32 one or two.
+  static constexpr int kWaves = !kBf16 ? 1 : D == 64 ? 3 : 2;
+  static constexpr int PAD = kBf16 ? (D == 128 ? 8 : 16) : 4;
   // K, V natural [64 keys][KP]; bf16 also K^T [D][KTP key positions], the
   // keys of each row in the order ktpos gives.
-  static constexpr int KP = D + (kBf16 ? 16 : 4);
-  static constexpr int KTP = kTile + 16;
+  static constexpr int KP = D + PAD;
+  static constexpr int KTP = kTile + (kBf16 ? PAD : 16);
   // P^T or dS^T [64 keys][PP pairs].
-  static constexpr int PP = kTile + (kBf16 ? 16 : 4);
+  static constexpr int PP = kTile + PAD;
   // bf16: dO^T or Q^T [D][PP pairs]; fp32: dO or Q natural [64 pairs][KP].
   static constexpr int K_BYTES = kTile * KP * sizeof(T);
   static constexpr int KT_BYTES = kBf16 ? D * KTP * 2 : 0;
@@ -106,13 +111,14 @@ struct BwdLayout {
   static constexpr int OFF_P = OFF_KT + KT_BYTES;
   // Dual: separate buffers for the dV operands (P^T, dO) and the dK operands
   // (dS^T, Q), so a tile needs two barriers instead of four; used when both
-  // fit in the 160 KB of a CU's LDS.
+  // fit in the CU's 160 KB of LDS at kWaves workgroups.
   static constexpr int SINGLE = OFF_P + P_BYTES + O_BYTES;
-  static constexpr bool kDual = SINGLE + P_BYTES + O_BYTES <= 160 * 1024;
+  static constexpr bool kDual = (SINGLE + P_BYTES + O_BYTES) * kWaves <= 160 * 1024;
   static constexpr int OFF_P2 = OFF_P + P_BYTES;                   // dual only
   static constexpr int OFF_O = OFF_P + (kDual ? 2 : 1) * P_BYTES;
   static constexpr int OFF_O2 = OFF_O + O_BYTES;                   // dual only
   static constexpr int BYTES = OFF_O + (kDual ? 2 : 1) * O_BYTES;
+  static_assert(BYTES * kWaves <= 160 * 1024, "kWaves workgroups fit a CU's LDS");
 };
 
 // Position of key k inside a K^T row: within each group of 32 keys, key
@@ -276,7 +282,7 @@ __device__ __forceinline__ void scores(const T* ks, const T* vs, const PairRows<
 // 16w .. 16w + 15 of the tile (lane%16 = its pair), and owns keys
 // 16w .. 16w + 15 of the block for dK and dV.
 template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void bwd_pair_kernel(
+__global__ __launch_bounds__(256, (BwdLayout<T, D>::kWaves)) void bwd_pair_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const void* __restrict__ dout, const float2* __restrict__ ld,
     const int32_t* __restrict__ list, const int32_t* __restrict__ items,
