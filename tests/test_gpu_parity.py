@@ -425,6 +425,31 @@ def test_fused_and_panel_selection_identical(bsa, name, causal, topk):
     assert np.array_equal(i1, i2) and np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
+@pytest.mark.parametrize("topk", [16, 8, 32])
+def test_selection_unaligned_index_output(bsa, topk):
+    """An index output that is 4-byte but not 16-byte aligned (a view one
+    int32 into a buffer) takes the selection kernel's one-entry stores; the
+    indices and outputs equal those written to an aligned buffer."""
+    m, lib = bsa
+    use_strategy(m, lib, "block_gather", "fused")
+    w = W.WORKLOADS["dyn_bf16_n4k"]
+    inp = W.generate(w)
+    q, k, v = to_dev(inp, w.dtype)
+    say(f"[gpu] unaligned index output k={topk}")
+    shape = q.shape[:3] + (topk,)
+    out_a = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    idx_a = torch.empty(shape, dtype=torch.int32, device="cuda")
+    m.bsa_forward(lib.handle, q, k, v, out_a, idx_a, topk=topk, scale=w.scale, causal=True)
+    buf = torch.full((idx_a.numel() + 4,), 7, dtype=torch.int32, device="cuda")
+    idx_u = buf[1:1 + idx_a.numel()].view(shape)
+    assert idx_u.data_ptr() % 16 == 4
+    out_u = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    m.bsa_forward(lib.handle, q, k, v, out_u, idx_u, topk=topk, scale=w.scale, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(idx_a, idx_u) and torch.equal(out_a, out_u)
+    assert int(buf[0]) == 7 and bool((buf[1 + idx_a.numel():] == 7).all())   # nothing outside the view
+
+
 @pytest.mark.parametrize("select", ["fused", "panel"])
 @pytest.mark.parametrize("causal", [False, True])
 def test_selection_exact_ties(bsa, select, causal):
