@@ -742,7 +742,10 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   if (chunk > total) chunk = total;
   const int64_t pairs = chunk * topk;
   const int64_t nb = sp.n / 64;
-  const int qsegs = bsa::gather_segments(sp.n, sp.d, topk, dtype);
+  // One query segment per head: the backward's gathered rows (Q and dO) get
+  // little L2 reuse at any segment size, and fewer segments mean fewer
+  // per-item dk, dv partials to write and sum.
+  const int qsegs = 1;
   const int64_t heads_spanned = sp.bh() < (chunk + sp.n - 1) / sp.n + 1 ? sp.bh() : (chunk + sp.n - 1) / sp.n + 1;
   const int64_t buckets = heads_spanned * qsegs * nb;
   const int64_t slots = bsa::gather_grid(chunk, topk, buckets, bsa::bwd_item_pairs(sp.d));

@@ -109,9 +109,11 @@ struct GatherArgs {
 
 // Query segments per head for the bucketing: the pairs of one (head, key
 // block) are split by query range so that the work items of one segment,
-// which run together, gather query rows from at most 2 MB of Q.  The
-// backward uses the same segments (halving them for its Q + dO rows cost
-// more in per-item dk, dv partials than it saved: 0.80 -> 0.93 ms at N = 32k).
+// which run together, gather query rows from at most 2 MB of Q.  Forward
+// only: the backward buckets by (head, block) (measured at N = 32k: 0.69 ms
+// with one segment per head, 0.73 with the forward's two, 0.93 with four;
+// its per-item dk, dv partials grow with the segments while its gathered Q
+// and dO rows hit little in L2 at any of these sizes).
 int gather_segments(int n, int d, int topk, bsa_dtype dtype);
 
 size_t gather_pair_bytes(int d, bsa_dtype dtype);  // partial bytes per (query, block) pair
@@ -121,13 +123,13 @@ hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, 
 hipError_t launch_gather_partial(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s);
 hipError_t launch_gather_combine(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s);
 
-// Backward of the fine stage with the selection held fixed, on the same
-// bucketing as the block-gather forward (one work item = up to
-// bwd_item_pairs(d) pairs of one (head, query segment, key block) bucket).
-// d = 64: 2048 pairs (fewer per-item dk/dv partials; measured best at N =
-// 32k); d = 128: 512 (its pair kernel runs one workgroup per CU, and larger
-// items left long tails on the long causal workload).
-constexpr int bwd_item_pairs(int d) { return d == 64 ? 2048 : 512; }
+// Backward of the fine stage with the selection held fixed, on the
+// bucketing of the block-gather forward with one query segment per head (one
+// work item = up to bwd_item_pairs(d) pairs of one (head, key block) bucket).
+// d = 64: 2048 pairs, so a bucket at N = 32k is one item (fewest per-item
+// dk, dv partials); d = 128: 1024 (measured on the long causal workload:
+// 11.8 ms at 512, 11.2 at 1024, 12.3 at 2048, where long items leave tails).
+constexpr int bwd_item_pairs(int d) { return d == 64 ? 2048 : 1024; }
 
 struct BackwardArgs {
   const void* q = nullptr;
