@@ -68,7 +68,7 @@ def stage_work(w: W.Workload):
     if sel_pairs is None:
         i = np.arange(w.n, dtype=np.int64)
         sel_pairs = int(w.bh * np.minimum(w.topk, i // w.block + 1).sum())
-    partial = sel_pairs * (w.d * (2 if w.dtype == "bf16" else 4) + 8)
+    partial = sel_pairs * w.d * (2 if w.dtype == "bf16" else 4)
     out_b = w.bh * w.n * w.d * 4
     rows = w.bh * w.n
     dq_rows = sel_pairs * w.d * s  # per-pair dq rows: bf16 (bf16 inputs) or fp32

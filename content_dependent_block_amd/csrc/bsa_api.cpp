@@ -38,7 +38,7 @@ struct bsa_handle_s {
     void* p = nullptr;
     size_t bytes = 0;
   };
-  Buf g_count, g_offsets, g_items, g_item_rec, g_rank, g_rec, g_wgv, g_list, g_po, g_pml;
+  Buf g_count, g_offsets, g_items, g_item_rec, g_rank, g_rec, g_wgv, g_list, g_po;
   Buf b_ld, b_dq, b_dkv, b_dob;
   bool counts_zero = false;  // g_count holds zeros (the bucketing's scan leaves it so)  // backward: per-row (lse, delta), per-pair dq, per-item dk/dv, bf16 dout
   Buf r_q, r_k, r_v, r_o, r_do, r_lse, r_idx, r_dq, r_dk, r_dv;  // padded copies (ragged n)
@@ -241,7 +241,7 @@ BSA_API bsa_status bsa_destroy(bsa_handle h) {
   if (h->split) (void)hipFree(h->split);
   if (h->panel) (void)hipFree(h->panel);
   if (h->idx) (void)hipFree(h->idx);
-  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_rec, &h->g_wgv, &h->g_list, &h->g_po, &h->g_pml,
+  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_rec, &h->g_wgv, &h->g_list, &h->g_po,
                  &h->b_ld, &h->b_dq, &h->b_dkv, &h->b_dob, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
                  &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv})
     if (b->p) (void)hipFree(b->p);
@@ -278,7 +278,7 @@ BSA_API bsa_status bsa_set_option(bsa_handle h, int option, int64_t value) {
 BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
   if (!h || !bytes) return fail(h, BSA_ERR_INVALID_ARG, "bsa_workspace_bytes: NULL argument");
   *bytes = h->repr_bytes + h->split_bytes + h->panel_bytes + h->idx_bytes;
-  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_rec, &h->g_wgv, &h->g_list, &h->g_po, &h->g_pml,
+  for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_rec, &h->g_wgv, &h->g_list, &h->g_po,
                  &h->b_ld, &h->b_dq, &h->b_dkv, &h->b_dob, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
                  &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv})
     *bytes += b->bytes;
@@ -406,7 +406,6 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   TRY(grow_buf(h, h->g_rank, size_t(pairs) * 4, "pair ranks"));
   TRY(grow_buf(h, h->g_list, size_t(pairs) * 4, "pair lists"));
   TRY(grow_buf(h, h->g_po, size_t(pairs) * s.d * (dt == BSA_BF16 ? 2 : 4), "partial outputs"));
-  TRY(grow_buf(h, h->g_pml, size_t(pairs) * 8, "partial max/sum"));
   TRY(grow_buf(h, h->g_rec, size_t(pairs) * 8, "block-ordered pair records"));
   TRY(grow_buf(h, h->g_wgv, size_t(chunk / 64 + 1) * 4, "pairs per bucketing workgroup"));
   bsa::GatherArgs a;
@@ -434,7 +433,6 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   a.ws.wg_valid = static_cast<int32_t*>(h->g_wgv.p);
   a.ws.list = static_cast<int32_t*>(h->g_list.p);
   a.ws.partial_o = h->g_po.p;
-  a.ws.partial_ml = static_cast<float2*>(h->g_pml.p);
   for (int64_t r0 = 0; r0 < total; r0 += chunk) {
     const int64_t rows = (total - r0) < chunk ? (total - r0) : chunk;
     TRY(run_gather_index(h, a, r0, rows, BSA_STAGE_GATHER_INDEX, "block-gather bucketing", st));

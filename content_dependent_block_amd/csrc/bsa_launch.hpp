@@ -84,8 +84,9 @@ struct GatherWorkspace {
   int2* rec = nullptr;         // [chunk pairs]  block-ordered {pair, block << 21 | rank} records
   int32_t* wg_valid = nullptr; // [chunk rows / 64]  valid pairs per bucketing workgroup
   int32_t* list = nullptr;     // [chunk pairs]
-  void* partial_o = nullptr;   // [chunk pairs][d]  fp16 for bf16 inputs, fp32 for fp32 inputs
-  float2* partial_ml = nullptr;  // [chunk pairs]  (log2-domain max, sum)
+  // [chunk pairs][d]  fp16 for bf16 inputs, fp32 for fp32 inputs; the low bits of
+  // elements 0 .. 31 of a row hold the pair's log2-domain log-sum-exp (fp32 bits)
+  void* partial_o = nullptr;
 };
 
 // Pairs per work item of the forward attention kernel.
@@ -151,7 +152,7 @@ struct BackwardArgs {
   uint16_t* dout_b = nullptr; // [bh * n][d] dout rounded to bf16 (bf16 inputs only)
   float* dq_part = nullptr;  // [chunk pairs][d]  per-pair dq contributions (bf16 for bf16 inputs)
   float* dkv_part = nullptr; // [work items][2][64][d]  per-item dk, dv contributions
-  GatherWorkspace ws;        // bucketing (count .. list); partial_o / partial_ml unused
+  GatherWorkspace ws;        // bucketing (count .. list); partial_o unused
 };
 
 // ld for all `rows` query rows.

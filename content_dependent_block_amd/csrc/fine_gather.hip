@@ -387,8 +387,7 @@ __device__ __forceinline__ int out_dim(int dt, int m) {
 template <typename T, int D, bool CAUSAL>
 __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage, const QOperand<T, D>& qo,
                                            int64_t row, int beta, int n, int klim, bool live, int32_t pair,
-                                           float scale_log2, PartialT<T>* __restrict__ po,
-                                           float2* __restrict__ pml, int lane) {
+                                           float scale_log2, PartialT<T>* __restrict__ po, int lane) {
   using L = KvLayout<T, D>;
   const int g = lane >> 4, c16 = lane & 15;
   f32x4 s[4];
@@ -489,6 +488,10 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
     lt += __shfl_xor(lt, 32);
   }
   const float inv = 1.0f / lt;
+  // The pair's log2-domain log-sum-exp, m + log2 l (l >= 1: the maximum's own
+  // weight is 1), rides in the row itself: bit e of its fp32 pattern replaces
+  // the least significant bit of element e, e < 32.
+  const uint32_t lse_bits = __float_as_uint(m + __builtin_amdgcn_logf(lt));
   if constexpr (L::kBf16) {
     // Through the wave's LDS staging rows (16 pairs x D fp16) so that every
     // partial row leaves as whole 128-byte lines: CPR lanes write one row's
@@ -514,8 +517,16 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
       const int r = i * RPI + lane / CPR, ch = lane % CPR;
       const int32_t pr = __shfl(pair, r);
       const bool lv = __shfl(static_cast<int>(live), r) != 0;
-      const f16x8 h = *reinterpret_cast<const f16x8*>(stage + r * kStagePitch<D> + ch * 8);
-      if (lv) __builtin_nontemporal_store(h, reinterpret_cast<f16x8*>(po + static_cast<int64_t>(pr) * D) + ch);
+      const uint32_t bits = __shfl(lse_bits, r) >> (8 * ch);  // elements 8 ch .. 8 ch + 7
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      u32x4 h = *reinterpret_cast<const u32x4*>(stage + r * kStagePitch<D> + ch * 8);
+      if (ch < 4) {
+        h[0] = (h[0] & 0xFFFEFFFEu) | (bits & 1u) | ((bits << 15) & 0x10000u);
+        h[1] = (h[1] & 0xFFFEFFFEu) | ((bits >> 2) & 1u) | ((bits << 13) & 0x10000u);
+        h[2] = (h[2] & 0xFFFEFFFEu) | ((bits >> 4) & 1u) | ((bits << 11) & 0x10000u);
+        h[3] = (h[3] & 0xFFFEFFFEu) | ((bits >> 6) & 1u) | ((bits << 9) & 0x10000u);
+      }
+      if (lv) __builtin_nontemporal_store(h, reinterpret_cast<u32x4*>(po + static_cast<int64_t>(pr) * D) + ch);
     }
   } else {
     if (!live) return;
@@ -523,10 +534,16 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
 #pragma unroll
     for (int dt = 0; dt < D / 16; ++dt) {
       const f32x4 a = acc[dt] * inv;
-      *reinterpret_cast<float4*>(op + 16 * dt + 4 * g) = make_float4(a[0], a[1], a[2], a[3]);
+      uint32_t u[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 16 * dt + 4 * g + i;  // element of the row
+        u[i] = __float_as_uint(a[i]);
+        if (e < 32) u[i] = (u[i] & ~1u) | ((lse_bits >> e) & 1u);
+      }
+      *reinterpret_cast<uint4*>(op + 16 * dt + 4 * g) = make_uint4(u[0], u[1], u[2], u[3]);
     }
   }
-  if (live && g == 0) pml[pair] = make_float2(m, lt);
 }
 
 // One work item = up to kItemPairs pairs of one bucket (head, key block),
@@ -541,7 +558,7 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
     const int32_t* __restrict__ list, const int32_t* __restrict__ items,
     const int4* __restrict__ item_rec, int nbuckets, int64_t row0, int64_t npairs, int n,
     uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, int klim_last, float scale_log2,
-    PartialT<T>* __restrict__ po, float2* __restrict__ pml) {
+    PartialT<T>* __restrict__ po) {
   using L = KvLayout<T, D>;
   constexpr int GPW = kItemPairs / 16 / 4;  // 16-pair groups per wave
   constexpr int STAGE_BYTES = L::kBf16 ? 16 * kStagePitch<D> * 2 : 0;  // per wave
@@ -597,21 +614,48 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
   for (int gi = 0; gi < GPW; ++gi) {
     if ((wave + 4 * gi) * 16 >= cnt) break;  // wave-uniform
     pair_group<T, D, CAUSAL>(ks, vs, stage, qo[gi], row[gi], beta, n, klim, live[gi], pair[gi],
-                             scale_log2, po, pml, lane);
+                             scale_log2, po, lane);
   }
 }
 
-// One group of 16 lanes per query row.  Lane c reads the (m, l) of slots
-// c, c + 16, ... so a row's partial headers arrive together; the row max and
-// the weight sum are 16-lane shuffle reductions.  Then, 16 slots at a time,
-// every lane issues the loads of its D/16 dims of all 16 partials before
-// using any (slot index clamped into the row, so every load is in bounds;
-// padding slots carry weight 0 and are zeroed by a select, since their buffer
-// entries were never written), and accumulates in slot order.  Any topk.
+// Least significant bit of a partial element's bit pattern.
+__device__ __forceinline__ uint32_t low_bit(f16 x) { return __builtin_bit_cast(uint16_t, x) & 1u; }
+__device__ __forceinline__ uint32_t low_bit(float x) { return __float_as_uint(x) & 1u; }
+
+// Reduce-scatter by OR over a group of 16 lanes: lane c holds v[t] for
+// t = 0 .. 15 and gets back the OR of every lane's v[c].  Recursive halving:
+// at distance M a lane keeps the half of its 2M live entries whose bit M
+// matches its own lane bit and sends the other half to lane c ^ M; after the
+// steps M = 8, 4, 2, 1 (15 shuffles) entry 0 is the lane's own slot.
+template <int M>
+__device__ __forceinline__ void or_halve(uint32_t (&v)[16], int c) {
+  const bool hi = (c & M) != 0;
+#pragma unroll
+  for (int j = 0; j < M; ++j) {
+    const uint32_t keep = hi ? v[j + M] : v[j];
+    const uint32_t give = hi ? v[j] : v[j + M];
+    v[j] = keep | static_cast<uint32_t>(__shfl_xor(static_cast<int>(give), M, 16));
+  }
+}
+__device__ __forceinline__ uint32_t or_scatter16(uint32_t (&v)[16], int c) {
+  or_halve<8>(v, c);
+  or_halve<4>(v, c);
+  or_halve<2>(v, c);
+  or_halve<1>(v, c);
+  return v[0];
+}
+
+// One group of 16 lanes per query row, 16 slots at a time: every lane issues
+// the loads of its D/16 dims of all 16 partial rows before using any (slot
+// index clamped into the row, so every load is in bounds; padding slots carry
+// weight 0 and are zeroed by a select, since their rows were never written).
+// Each row carries its pair's log2-domain log-sum-exp in the low bits of its
+// first 32 elements; lane c collects the bits it holds and a reduce-scatter
+// hands lane c the value of slot c.  Rows are merged in slot order against a
+// running maximum (rescaled when a later batch of 16 raises it).  Any topk.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict__ idx,
                                                       const PartialT<T>* __restrict__ po,
-                                                      const float2* __restrict__ pml,
                                                       float* __restrict__ out, float* __restrict__ lse,
                                                       int64_t row0, int64_t rows, int n, int topk,
                                                       int causal) {
@@ -625,16 +669,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   const int64_t row = row0 + r;
   const int nb = n / kTile;
   const int32_t* sel = idx + row * topk;
-  const float2* ml = pml + r * topk;
-  float mmax = -INFINITY;
-  for (int s = c; s < topk; s += 16)
-    if (pair_valid(sel[s], nb, row, n, causal)) mmax = fmaxf(mmax, ml[s].x);
-#pragma unroll
-  for (int off = 8; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off, 16));
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  float wsum = 0.f;
+  float wsum = 0.f, mrun = -INFINITY;
   const PartialT<T>* src = po + r * topk * D + c * E;
   for (int s0 = 0; s0 < topk; s0 += 16) {
     Vec x[16][V];
@@ -645,11 +683,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
       for (int u = 0; u < V; ++u)
         x[t][u] = __builtin_nontemporal_load(reinterpret_cast<const Vec*>(src + static_cast<int64_t>(st) * D) + u);
     }
-    float wl = 0.f;  // weight of slot s0 + c
-    if (s0 + c < topk && pair_valid(sel[s0 + c], nb, row, n, causal)) {
-      const float2 v = ml[s0 + c];
-      wl = v.y * __builtin_amdgcn_exp2f(v.x - mmax);
+    // bits c E .. c E + E - 1 of each slot's log-sum-exp (lanes c < 32 / E)
+    uint32_t part[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      uint32_t b = 0u;
+#pragma unroll
+      for (int u = 0; u < V; ++u)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) b |= low_bit(x[t][u][q4]) << (4 * u + q4);
+      part[t] = c * E < 32 ? b << (c * E) : 0u;
     }
+    const uint32_t bits = or_scatter16(part, c);  // slot s0 + c
+    const bool valid = s0 + c < topk && pair_valid(sel[s0 + c], nb, row, n, causal);
+    const float ls = valid ? __uint_as_float(bits) : -INFINITY;
+    float mb = ls;
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) mb = fmaxf(mb, __shfl_xor(mb, off, 16));
+    const float mnew = fmaxf(mrun, mb);
+    if (mnew > mrun && mrun > -INFINITY) {  // a later batch raised the maximum
+      const float sc = __builtin_amdgcn_exp2f(mrun - mnew);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] *= sc;
+      wsum *= sc;
+    }
+    mrun = mnew;
+    const float wl = valid ? __builtin_amdgcn_exp2f(ls - mrun) : 0.f;  // weight of slot s0 + c
     wsum += wl;
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -666,9 +725,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off, 16);
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
-  // log-sum-exp of the row's scaled scores, natural log: the partial maxima
+  // log-sum-exp of the row's scaled scores, natural log: the partial values
   // are in log2 units, so lse = (M + log2 sum_s w_s) / log2(e).
-  if (lse && c == 0) lse[row] = wsum > 0.f ? (mmax + __log2f(wsum)) * (1.0f / kLog2e) : -INFINITY;
+  if (lse && c == 0) lse[row] = wsum > 0.f ? (mrun + __log2f(wsum)) * (1.0f / kLog2e) : -INFINITY;
   float* dst = out + row * D + c * E;
 #pragma unroll
   for (int e = 0; e < E; e += 4)
@@ -706,14 +765,12 @@ hipError_t partial_chunk(const GatherArgs& a, int64_t row0, int64_t rows, hipStr
     hipLaunchKernelGGL((gather_partial_kernel<T, D, true>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets,
-                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, klim_last, sl2, po,
-                       a.ws.partial_ml);
+                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, klim_last, sl2, po);
   else
     hipLaunchKernelGGL((gather_partial_kernel<T, D, false>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets,
-                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, klim_last, sl2, po,
-                       a.ws.partial_ml);
+                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, klim_last, sl2, po);
   return hipGetLastError();
 }
 
@@ -721,7 +778,7 @@ template <typename T, int D>
 hipError_t combine_chunk(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
   auto* po = reinterpret_cast<const PartialT<T>*>(a.ws.partial_o);
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0,
-                     s, a.idx, po, a.ws.partial_ml, a.out, a.lse, row0, rows, a.n, a.topk, a.causal);
+                     s, a.idx, po, a.out, a.lse, row0, rows, a.n, a.topk, a.causal);
   return hipGetLastError();
 }
 
@@ -749,7 +806,7 @@ int gather_segments(int n, int d, int topk, bsa_dtype dtype) {
 }
 
 size_t gather_pair_bytes(int d, bsa_dtype dtype) {
-  return static_cast<size_t>(d) * (dtype == BSA_BF16 ? 2 : 4) + sizeof(float2);
+  return static_cast<size_t>(d) * (dtype == BSA_BF16 ? 2 : 4);
 }
 
 hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s) {

@@ -83,8 +83,9 @@ typedef enum {
 /* How the dynamic fine stage visits the selected blocks. */
 typedef enum {
   /* Group the (query, block) pairs by key block, run 16 pairs per MFMA tile,
-   * write split-softmax partials (m, l, o) and merge them per query.  Every
-   * selected pair is computed once.  Default. */
+   * write split-softmax partials (a normalised output row that also carries
+   * the pair's log-sum-exp) and merge them per query.  Every selected pair is
+   * computed once.  Default. */
   BSA_FINE_BLOCK_GATHER = 0,
   /* Per 64-query tile, walk the union of the rows' selected blocks with the
    * online softmax in registers, masking each row to its own selection. */
