@@ -569,27 +569,42 @@ __device__ __forceinline__ void walk(TL& sc, unsigned char* rs, const typename T
                                      const TileInfo& ti, FF&& fast, FS&& slow) {
   constexpr int MT = TL::TB / 16;
   sc.template fetch<NT>(rbase, ti.nb, 0, ti.tid);
-  for (int bt0 = 0; bt0 < ti.nbt; bt0 += NH) {
+  // Steady state: NH tiles per iteration, none of them the last, so the body
+  // has no branches and the slot index h stays a compile-time value.
+  int bt0 = 0;
+  for (; bt0 + NH < ti.nbt; bt0 += NH) {
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
       const int bt = bt0 + h;
-      if (bt < ti.nbt) {
-        __syncthreads();
-        sc.template put<NT>(rs, ti.tid);
-        const bool last = bt + 1 == ti.nbt;
-        if (!last) sc.template fetch<NT>(rbase, ti.nb, bt + 1, ti.tid);
-        __syncthreads();
-        if (!last) {
+      __syncthreads();
+      sc.template put<NT>(rs, ti.tid);
+      sc.template fetch<NT>(rbase, ti.nb, bt + 1, ti.tid);
+      __syncthreads();
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            fast(h, mt, bt * TL::TB + mt * 16, sc.template tile<NT>(rs, mt, ti.g, ti.c16));
-        } else {
+      for (int mt = 0; mt < MT; ++mt)
+        fast(h, mt, bt * TL::TB + mt * 16, sc.template tile<NT>(rs, mt, ti.g, ti.c16));
+    }
+  }
+  // The remaining 1 .. NH tiles; the last one takes the checked slow().
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            const int b0 = bt * TL::TB + mt * 16;
-            if (b0 >= ti.nb) break;
-            slow(h, mt, b0, sc.template tile<NT>(rs, mt, ti.g, ti.c16));
-          }
+  for (int h = 0; h < NH; ++h) {
+    const int bt = bt0 + h;
+    if (bt < ti.nbt) {
+      __syncthreads();
+      sc.template put<NT>(rs, ti.tid);
+      const bool last = bt + 1 == ti.nbt;
+      if (!last) sc.template fetch<NT>(rbase, ti.nb, bt + 1, ti.tid);
+      __syncthreads();
+      if (!last) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          fast(h, mt, bt * TL::TB + mt * 16, sc.template tile<NT>(rs, mt, ti.g, ti.c16));
+      } else {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int b0 = bt * TL::TB + mt * 16;
+          if (b0 >= ti.nb) break;
+          slow(h, mt, b0, sc.template tile<NT>(rs, mt, ti.g, ti.c16));
         }
       }
     }
