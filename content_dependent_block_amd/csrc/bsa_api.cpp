@@ -361,10 +361,12 @@ bsa_status grow_buf(bsa_handle h, bsa_handle_s::Buf& b, size_t need, const char*
 // clearing kernel.  Returns the words to clear (0 if none) and assumes the
 // bucketing about to be enqueued succeeds; run_gather_index undoes that on
 // failure.
+// A buffer that has to grow is new memory whatever its address (a free
+// followed by an allocation can return the same pointer), so growth itself
+// marks the counts as not known to be zero.
 bsa_status grow_counts(bsa_handle h, size_t buckets, int64_t* clear_words) {
-  void* before = h->g_count.p;
+  if (h->g_count.bytes < buckets * 4) h->counts_zero = false;
   TRY(grow_buf(h, h->g_count, buckets * 4, "bucket counts"));
-  if (h->g_count.p != before) h->counts_zero = false;
   *clear_words = h->counts_zero ? 0 : int64_t(h->g_count.bytes / 4);
   return BSA_OK;
 }

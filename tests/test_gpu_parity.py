@@ -373,12 +373,35 @@ def test_fine_chunking_does_not_change_results(bsa, n):
     inp = W.generate(w)
     o1, i1 = run_forward(m, lib, w, inp)
     say("[gpu] small fine chunks")
-    m.bsa_set_option(lib.handle, m.BSA_OPT_FINE_CHUNK_BYTES, 3 * 64 * w.topk * (w.d * 2 + 8))
+    m.bsa_set_option(lib.handle, m.BSA_OPT_FINE_CHUNK_BYTES, 3 * 64 * w.topk * w.d * 2)
     try:
         o2, i2 = run_forward(m, lib, w, inp)
     finally:
         m.bsa_set_option(lib.handle, m.BSA_OPT_FINE_CHUNK_BYTES, 1 << 30)
     assert np.array_equal(i1, i2) and np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
+
+
+def test_growing_workspace_on_reused_memory():
+    """A handle whose bucket-count buffer grows between calls gives the same
+    output as a fresh handle, also when the grown buffer lands on device
+    memory that held nonzero data (a free and a new allocation may even
+    return the same address, so growth alone must mark the counts as dirty)."""
+    import content_dependent_block_amd as m
+    small = W.Workload("grow_small", 1, 1, 1024, 64, "bf16", seed=21, topk=4, key_offsets=True)
+    big = W.Workload("grow_big", 1, 8, 4096, 64, "bf16", seed=22, topk=16, key_offsets=True)
+    ins, inb = W.generate(small), W.generate(big)
+    with m.BlockSparseAttention(0) as fresh:
+        ref_o, ref_i = run_forward(m, fresh, big, inb)
+    with m.BlockSparseAttention(0) as lib:
+        say("[gpu] small call, then garbage in freed memory, then a larger call on the same handle")
+        run_forward(m, lib, small, ins)
+        junk = torch.full((64 << 20,), -1, dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        del junk
+        torch.cuda.empty_cache()
+        got_o, got_i = run_forward(m, lib, big, inb)
+    assert np.array_equal(got_i, ref_i)
+    assert np.array_equal(got_o.view(np.uint32), ref_o.view(np.uint32))
 
 
 @pytest.mark.parametrize("strategy", STRATEGIES)
