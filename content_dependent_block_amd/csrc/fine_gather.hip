@@ -7,10 +7,13 @@
 // "The Triton kernel"): o_i = softmax over the keys of query i's selected
 // blocks, applied to V.  Instead of one online-softmax pass per query, the
 // softmax is split by block (a standard split-softmax identity): each pair
-// (i, beta) yields m = max of its log2-scaled scores, l = sum 2^(z - m), and
-// o = (sum 2^(z - m) v) / l; the pairs of a query are then merged as
-//   M = max m_s,  w_s = l_s 2^(m_s - M),  o_i = sum w_s o_s / sum w_s.
-// No score leaves the chip; only the per-pair (m, l, o) do.
+// (i, beta) yields m = max of its log2-scaled scores, l = sum 2^(z - m),
+// o = (sum 2^(z - m) v) / l and its log-sum-exp L = m + log2 l; the pairs of
+// a query are then merged as
+//   M = max L_s,  w_s = 2^(L_s - M),  o_i = sum w_s o_s / sum w_s.
+// No score leaves the chip; only the per-pair rows o do, each carrying its L
+// in the least significant bits of its first 32 elements (one 128-byte line
+// per pair for bf16 inputs, and no separate record to scatter).
 //
 // Why: with content-dependent selections, queries that sit next to each other
 // share few blocks, so a query tile's union of blocks is mostly work for one
@@ -28,10 +31,10 @@
 //   gather_partial -- one work item = up to 256 pairs of one bucket: K and V^T
 //                     of the block in LDS, the pairs' query rows gathered into
 //                     MFMA operands, S^T = K Q^T and O^T = V^T P^T on MFMA,
-//                     partial (m, l, o) out.  Work items are laid out so that
+//                     partial rows out.  Work items are laid out so that
 //                     consecutive items (one head, one query segment,
 //                     neighbouring blocks) land on one XCD, whose L2 then holds
-//                     the segment's query rows (at most 2 MB, gather_segments).
+//                     the segment's query rows (at most 4 MB, gather_segments).
 //   combine        -- per query row, merge its partials in slot order.
 // The order of pairs inside a bucket (set by atomics) does not affect any
 // result: every MFMA column is computed independently of the others.
@@ -378,8 +381,9 @@ __device__ __forceinline__ int out_dim(int dt, int m) {
 }
 
 // One group of 16 pairs sharing key block `beta` (K, V^T in LDS): the lane
-// computes column lane%16 (its pair) and writes the pair's partial
-// (m in log2 units, l, o = sum 2^(z-m) v / l).  The softmax scale is folded
+// computes column lane%16 (its pair) and writes the pair's partial row
+// o = sum 2^(z-m) v / l with m + log2 l in its low bits (m in log2 units,
+// l = sum 2^(z-m)).  The softmax scale is folded
 // into the exp2 argument (the max is taken on raw scores; the scale is > 0),
 // and for bf16 inputs l comes out of the PV MFMA itself: one more 16-row
 // output tile whose A operand is a row of ones multiplies the same rounded
@@ -517,10 +521,11 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
       const int r = i * RPI + lane / CPR, ch = lane % CPR;
       const int32_t pr = __shfl(pair, r);
       const bool lv = __shfl(static_cast<int>(live), r) != 0;
-      const uint32_t bits = __shfl(lse_bits, r) >> (8 * ch);  // elements 8 ch .. 8 ch + 7
+      const uint32_t lb = __shfl(lse_bits, r);
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       u32x4 h = *reinterpret_cast<const u32x4*>(stage + r * kStagePitch<D> + ch * 8);
       if (ch < 4) {
+        const uint32_t bits = lb >> (8 * ch);  // elements 8 ch .. 8 ch + 7
         h[0] = (h[0] & 0xFFFEFFFEu) | (bits & 1u) | ((bits << 15) & 0x10000u);
         h[1] = (h[1] & 0xFFFEFFFEu) | ((bits >> 2) & 1u) | ((bits << 13) & 0x10000u);
         h[2] = (h[2] & 0xFFFEFFFEu) | ((bits >> 4) & 1u) | ((bits << 11) & 0x10000u);
@@ -794,12 +799,15 @@ int gather_segments(int n, int d, int topk, bsa_dtype dtype) {
   const int nb = n / kTile;
   const int64_t qbytes = static_cast<int64_t>(n) * d * (dtype == BSA_BF16 ? 2 : 4);
   int qs = 1;
-  // halve the segment while its Q is over 2 MB, its length stays a multiple
-  // of 256 rows, and a (segment, block) bucket still averages >= 256 pairs.
-  // (Measured at N = 32k, d = 64: 4 MB segments fetch 554 MB per launch,
-  // 2 MB 434 MB, 1 MB 451 MB with twice the buckets, 512 KB 792 MB: smaller
-  // segments trade query-row misses for re-reads of the key blocks.)
-  while (n % (qs * 2 * 256) == 0 && qbytes / qs > (int64_t(2) << 20) &&
+  // halve the segment while its Q is over 4 MB (one XCD's L2), its length
+  // stays a multiple of 256 rows, and a (segment, block) bucket still
+  // averages >= 256 pairs.  Smaller segments trade query-row misses for
+  // re-reads of the key blocks; at N = 32k, d = 64 the attention kernel took
+  // 0.160 ms with one 4 MB segment per head, 0.163 with 2 MB and 0.169 with
+  // 1 MB.  (Before the partial rows carried their own log-sum-exp, the
+  // scattered 8-byte (m, l) stores evicted query rows from L2 and 2 MB
+  // segments were best.)
+  while (n % (qs * 2 * 256) == 0 && qbytes / qs > (int64_t(4) << 20) &&
          static_cast<int64_t>(n / (qs * 2)) * topk / nb >= 256)
     qs *= 2;
   return qs;
