@@ -6,8 +6,9 @@ block_pool -> coarse_select (coarse scores and top-k in one kernel) ->
 block-gather sparse_flash_fwd (gather_index, attention, gather_combine).
 Prints ONE JSON line: forward tokens/s (batch * n / step time), effective
 TFLOP/s, the roofline of the dominant kernel (timed with HIP events on the
-launch stream inside this run) and the fp64 CPU oracle's throughput on a
-bounded sample of the same workload.
+launch stream inside this run), the bound and fraction of every stage
+(`stage_rooflines`, longest first) and the fp64 CPU oracle's throughput on
+a bounded sample of the same workload.
 
 With --pass backward a step is one bsa_backward (dq, dk, dv of the fine stage
 for the selection, output and lse of one bsa_forward_train made before the
@@ -241,25 +242,29 @@ def main():
                          if launches[i]}
 
     work = stage_work(w)
+
+    def stage_roofline(name):
+        """The roofline of one stage: its algorithmic flops (MFMA-bound) or
+        bytes (HBM-bound) per launch over its average launch time; the bound
+        is the resource whose peak the algorithmic work would take longer on."""
+        flops, nbytes = work[name]
+        t_launch = per_launch[name] * 1e-3
+        n_launch = launches_per_step[name]
+        t_mfma = flops / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)
+        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+        if t_mfma >= t_hbm:
+            achieved, peak, unit = flops / n_launch / t_launch / 1e12, MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
+        else:
+            achieved, peak, unit = nbytes / n_launch / t_launch / 1e9, HBM_PEAK_GBS, "GB/s"
+        return {"bound": "mfma" if t_mfma >= t_hbm else "hbm", "achieved": round(achieved, 3), "peak": peak,
+                "unit": unit, "frac": round(achieved / peak, 5)}
+
     dom = max(per_step, key=per_step.get)
-    flops, nbytes = work[dom]
-    t_launch = per_launch[dom] * 1e-3
-    n_launch = launches_per_step[dom]
-    # the bound is the resource whose peak the kernel's algorithmic work
-    # would take longer on
-    t_mfma = flops / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)
-    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
-    bound = "mfma" if t_mfma >= t_hbm else "hbm"
-    if bound == "mfma":
-        achieved = flops / n_launch / t_launch / 1e12
-        peak, unit = MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
-    else:
-        achieved = nbytes / n_launch / t_launch / 1e9
-        peak, unit = HBM_PEAK_GBS, "GB/s"
-    roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 5), "traffic": measured_traffic(dom, w.name),
-                "kernel": dom, "avg_launch_ms": round(per_launch[dom], 5),
-                "launches_per_step": n_launch}
+    roofline = dict(stage_roofline(dom), traffic=measured_traffic(dom, w.name), kernel=dom,
+                    avg_launch_ms=round(per_launch[dom], 5), launches_per_step=launches_per_step[dom])
+    # every stage's bound and fraction, longest first (the first is `roofline`)
+    stage_rooflines = {k_: {f: stage_roofline(k_)[f] for f in ("bound", "achieved", "unit", "frac")}
+                       for k_ in sorted(per_step, key=per_step.get, reverse=True)}
 
     total_flops = sum(work[k_][0] for k_ in per_step)  # matmul-only: coarse + fine, stages that ran
     tokens = w.batch * w.n
@@ -286,6 +291,7 @@ def main():
         "algorithmic_gflop": round(total_flops / 1e9, 3),
         "stage_ms_per_step": {k_: round(v_, 5) for k_, v_ in per_step.items()},
         "roofline": roofline,
+        "stage_rooflines": stage_rooflines,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = (cpu_baseline(w, inp, args.cpu_positions) if args.which == "forward"
