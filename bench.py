@@ -7,8 +7,9 @@ block-gather sparse_flash_fwd (gather_index, attention, gather_combine).
 Prints ONE JSON line: forward tokens/s (batch * n / step time), effective
 TFLOP/s, the roofline of the dominant kernel (timed with HIP events on the
 launch stream inside this run), the bound and fraction of every stage
-(`stage_rooflines`, longest first) and the fp64 CPU oracle's throughput on
-a bounded sample of the same workload.
+(`stage_rooflines`, longest first), the median and minimum of single steps
+run after a cache-flushing 1 GiB write (`cold`), and the fp64 CPU oracle's
+throughput on a bounded sample of the same workload.
 
 With --pass backward a step is one bsa_backward (dq, dk, dv of the fine stage
 for the selection, output and lse of one bsa_forward_train made before the
@@ -151,6 +152,8 @@ def main():
     ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-positions", type=int, default=32768)
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra steps timed one by one after a cache-flushing 1 GiB write (0 = none)")
     ap.add_argument("--fine-strategy", choices=["block_gather", "query_tile"], default="block_gather")
     ap.add_argument("--select-strategy", choices=["fused", "panel"], default="fused")
     ap.add_argument("--panel-chunk-mb", type=int, default=0, help="coarse-score panel chunk (0 = default)")
@@ -228,6 +231,26 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
 
+    # Cold steps (after the timed region, not part of `value`): before each
+    # step a 1 GiB scratch buffer is written, which evicts the inputs from
+    # the 256 MB Infinity Cache; each step is timed alone with HIP events.
+    cold = None
+    if args.cold_steps > 0:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        times = []
+        for i in range(args.cold_steps):
+            scratch.fill_(float(i))
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            step()
+            c1.record(stream)
+            torch.cuda.synchronize()
+            times.append(c0.elapsed_time(c1))
+        del scratch
+        cold = {"steps": args.cold_steps, "ms_median": round(float(np.median(times)), 5),
+                "ms_min": round(float(np.min(times)), 5),
+                "flush": "1 GiB scratch written before each step"}
+
     # Second pass: per-kernel HIP events on the launch stream.
     m.bsa_profile_read(h, reset=True)
     m.bsa_profile_enable(h, True)
@@ -293,6 +316,8 @@ def main():
         "roofline": roofline,
         "stage_rooflines": stage_rooflines,
     }
+    if cold is not None:
+        result["cold"] = cold
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = (cpu_baseline(w, inp, args.cpu_positions) if args.which == "forward"
                                   else cpu_baseline_backward(w, inp, dout_np))
