@@ -164,7 +164,12 @@ bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes);
  *                 (as one of the k), and inside kept blocks only keys j <= i
  *                 are visible.
  * Coarse scores are q . mean(block keys), unscaled; equal scores go to the
- * lower block index, and -0 equals +0. */
+ * lower block index, and -0 equals +0.
+ * Range: with bf16 inputs the block-gather fine stage (the default) keeps
+ * each (query, block) partial output in fp16, so every |v| must stay below
+ * 65504; a larger value makes the affected output rows non-finite (never a
+ * finite wrong value).  The same holds for every entry point below that runs
+ * the dynamic fine stage on bf16 inputs. */
 bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const void* v,
                        float* out, int32_t* block_idx_out, int batch, int heads,
                        int n, int d, bsa_dtype dtype, int block, int topk,

@@ -381,6 +381,31 @@ def test_fine_chunking_does_not_change_results(bsa, n):
     assert np.array_equal(i1, i2) and np.array_equal(o1.view(np.uint32), o2.view(np.uint32))
 
 
+def test_bf16_value_beyond_fp16_range_is_never_finite_and_wrong(bsa):
+    """bf16 inputs keep the per-(query, block) partial rows in fp16: a value
+    of v beyond the fp16 range must leave the affected outputs non-finite,
+    and every finite output must still match the oracle (relative 1e-2, the
+    values are large)."""
+    m, lib = bsa
+    w = W.Workload("big_v", 1, 1, 1024, 64, "bf16", seed=31, topk=4, key_offsets=True)
+    inp = W.generate(w)
+    v = inp.v.copy()
+    v[0, 0, 70, :] = 3.0e7  # key 70 of block 1, every dim
+    v, vbits = W.bf16_round(v.astype(np.float32))
+    inp = W.Inputs(q=inp.q, k=inp.k, v=v, q_bits=inp.q_bits, k_bits=inp.k_bits, v_bits=vbits)
+    say("[gpu] bsa_forward with one v row at 3e7 (beyond fp16)")
+    out, idx = run_forward(m, lib, w, inp)
+    out = out.reshape(-1, w.d)
+    gidx = idx.reshape(-1, w.topk)
+    rows = np.arange(w.n, dtype=np.int64)
+    ref = oracle.attend(inp.q, inp.k, inp.v, gidx, w.block, False, w.scale, rows)
+    fin = np.isfinite(out)
+    assert (~fin).any(), "the overflow case was not reached"
+    assert not (~fin[~(gidx == 1).any(axis=1)]).any(), "rows that did not select block 1 must stay finite"
+    err = np.abs(out - ref) / np.maximum(1.0, np.abs(ref))
+    assert err[fin].max() <= TOL["bf16"]
+
+
 def test_growing_workspace_on_reused_memory():
     """A handle whose bucket-count buffer grows between calls gives the same
     output as a fresh handle, also when the grown buffer lands on device
