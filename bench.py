@@ -7,7 +7,8 @@ block-gather sparse_flash_fwd (gather_index, attention, gather_combine).
 Prints ONE JSON line: forward tokens/s (batch * n / step time), effective
 TFLOP/s, the roofline of the dominant kernel (timed with HIP events on the
 launch stream inside this run), the bound and fraction of every stage
-(`stage_rooflines`, longest first), the median and minimum of single steps
+(`stage_rooflines`, longest first), the step against the sum of the stages'
+ideal times (`path_roofline`), the median and minimum of single steps
 run after a cache-flushing 1 GiB write (`cold`), and the fp64 CPU oracle's
 throughput on a bounded sample of the same workload.
 
@@ -285,6 +286,12 @@ def main():
     dom = max(per_step, key=per_step.get)
     roofline = dict(stage_roofline(dom), traffic=measured_traffic(dom, w.name), kernel=dom,
                     avg_launch_ms=round(per_launch[dom], 5), launches_per_step=launches_per_step[dom])
+    # the whole step against the sum of every stage's ideal time (the longer of
+    # its algorithmic flops at the MFMA peak and its algorithmic bytes at the
+    # HBM peak)
+    ideal_ms = sum(max(work[k_][0] / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12), work[k_][1] / (HBM_PEAK_GBS * 1e9))
+                   for k_ in per_step) * 1e3
+    path_roofline = {"ideal_ms": round(ideal_ms, 5), "frac": round(ideal_ms / ms_per_step, 5)}
     # every stage's bound and fraction, longest first (the first is `roofline`)
     stage_rooflines = {k_: {f: stage_roofline(k_)[f] for f in ("bound", "achieved", "unit", "frac")}
                        for k_ in sorted(per_step, key=per_step.get, reverse=True)}
@@ -315,6 +322,7 @@ def main():
         "stage_ms_per_step": {k_: round(v_, 5) for k_, v_ in per_step.items()},
         "roofline": roofline,
         "stage_rooflines": stage_rooflines,
+        "path_roofline": path_roofline,
     }
     if cold is not None:
         result["cold"] = cold
