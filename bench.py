@@ -165,8 +165,8 @@ def main():
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only; multi-GPU runs are not part of it "
-              "(heads shard with no communication; see the sharding notes).", file=sys.stderr)
+        print("bench.py: the library runs on one GPU; there is no multi-GPU mode "
+              "(heads would shard across GPUs with no communication).", file=sys.stderr)
         sys.exit(2)
 
     import torch
