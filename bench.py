@@ -292,6 +292,22 @@ def main():
     ideal_ms = sum(max(work[k_][0] / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12), work[k_][1] / (HBM_PEAK_GBS * 1e9))
                    for k_ in per_step) * 1e3
     path_roofline = {"ideal_ms": round(ideal_ms, 5), "frac": round(ideal_ms / ms_per_step, 5)}
+    if args.which == "forward":
+        # strict: the method's three steps with compulsory bytes only (Q, K, V
+        # read once, O written, representatives and indices written and read
+        # once; no score panel, no split-softmax partials)
+        s_ = 2 if w.dtype == "bf16" else 4
+        qkv_b = w.bh * w.n * w.d * s_
+        repr_b = w.bh * w.nb * w.d * 4
+        idx_b = w.bh * w.n * w.topk * 4
+        out_b = w.bh * w.n * w.d * 4
+        peak_f = MFMA_PEAK_TFLOPS[w.dtype] * 1e12
+        peak_b = HBM_PEAK_GBS * 1e9
+        strict_s = (max(0.0, (qkv_b + repr_b) / peak_b)
+                    + max(work["coarse_select"][0] / peak_f, (qkv_b + repr_b + idx_b) / peak_b)
+                    + max(4 * w.d * visible_pairs(w) / peak_f, (3 * qkv_b + idx_b + out_b) / peak_b))
+        path_roofline["strict_ideal_ms"] = round(strict_s * 1e3, 5)
+        path_roofline["strict_frac"] = round(strict_s * 1e3 / ms_per_step, 5)
     # every stage's bound and fraction, longest first (the first is `roofline`)
     stage_rooflines = {k_: {f: stage_roofline(k_)[f] for f in ("bound", "achieved", "unit", "frac")}
                        for k_ in sorted(per_step, key=per_step.get, reverse=True)}
