@@ -3,21 +3,29 @@
 
 One step = one full forward over one batch of resident synthetic inputs:
 block_pool -> coarse_select (coarse scores and top-k in one kernel) ->
-block-gather sparse_flash_fwd (gather_index, attention, gather_combine).
-Prints ONE JSON line: forward tokens/s (batch * n / step time), effective
-TFLOP/s, the roofline of the dominant kernel (timed with HIP events on the
-launch stream inside this run), the bound and fraction of every stage
-(`stage_rooflines`, longest first), the step against the sum of the stages'
-ideal times (`path_roofline`), the median and minimum of single steps
-run after a cache-flushing 1 GiB write (`cold`), and the fp64 CPU oracle's
-throughput on a bounded sample of the same workload.
+block-gather sparse_flash_fwd (gather_index, attention, gather_combine); for
+the static workload one bsa_forward_static over its tile list.
+
+Timing protocol: W untimed warm-up steps; then K cold steps, each after a
+1 GiB scratch write that evicts the inputs from the 256 MB Infinity Cache,
+each bracketed by a device synchronisation and timed with HIP events on the
+launch stream.  `value` is tokens/s at the MEDIAN cold step; the warm figure
+(K steps back to back) is reported beside it.  Per-kernel times come from a
+second cold pass with per-stage HIP events on the launch stream (the
+roofline of the dominant kernel is computed from those).
+
+Prints ONE JSON line: the headline workload's tokens/s, effective TFLOP/s,
+the roofline of the dominant kernel, every stage's bound and fraction, the
+step against the sum of the stages' ideal times, the fp64 CPU oracle's
+throughput on the host cores (plus a one-thread time of the small workload),
+and (unless --only) the same timings for every other workload.
 
 With --pass backward a step is one bsa_backward (dq, dk, dv of the fine stage
 for the selection, output and lse of one bsa_forward_train made before the
 timed region) and the line reports backward tokens/s.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--pass forward|backward]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--only]
+                    [--no-cpu-baseline] [--pass forward|backward]
 """
 from __future__ import annotations
 
@@ -38,8 +46,12 @@ METRIC = "fwd tokens/s and effective TFLOP/s at N=32k,H=8,D=64,B=64,k=16; % roof
 METRIC_BWD = "bwd tokens/s (fine-stage dq, dk, dv; selection fixed) and effective TFLOP/s; % roofline"
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
+
+
 def visible_pairs(w: W.Workload) -> int:
     """Closed form of the (query, key) pairs the fine stage visits."""
+    if w.static:
+        return static_visible_pairs(w)
     nb = w.nb
     if not w.causal:
         return w.bh * w.n * min(w.topk, nb) * w.block
@@ -49,6 +61,19 @@ def visible_pairs(w: W.Workload) -> int:
     return int(w.bh * ((keff - 1) * w.block + (i % w.block) + 1).sum())
 
 
+def static_visible_pairs(w: W.Workload) -> int:
+    """Pairs with |i - j| <= window or j mod stride == 0, counted per row."""
+    i = np.arange(w.n, dtype=np.int64)
+    lo = np.maximum(0, i - w.window)
+    hi = np.minimum(w.n - 1, i + w.window)
+    band = hi - lo + 1
+    glob_all = (w.n - 1) // w.stride + 1
+    # global keys inside the band are counted once
+    glob_in_band = hi // w.stride - (lo - 1) // w.stride
+    glob_in_band = np.where(lo == 0, hi // w.stride + 1, glob_in_band)
+    return int(w.bh * (band + glob_all - glob_in_band).sum())
+
+
 def candidate_pairs(w: W.Workload) -> int:
     if not w.causal:
         return w.bh * w.n * w.nb
@@ -56,23 +81,28 @@ def candidate_pairs(w: W.Workload) -> int:
     return int(w.bh * (i // w.block + 1).sum())
 
 
-def stage_work(w: W.Workload):
-    """Algorithmic work per launch of each kernel over the whole problem:
+def stage_work(w: W.Workload, nnz: int = 0):
+    """Algorithmic work per step of each kernel over the whole problem:
     (flops, bytes).  Bytes count each compulsory read/write once; a kernel's
     roofline bound is whichever of the two takes longer at the MI355X peaks."""
     s = 2 if w.dtype == "bf16" else 4
     qkv = w.bh * w.n * w.d * s
+    out_b = w.bh * w.n * w.d * 4
+    fine_flops = 4 * w.d * visible_pairs(w)
+    if w.static:
+        lst = nnz * 4 + nnz * 64 * 8  # key-tile ids and row masks
+        return {"sparse_flash_fwd": (fine_flops, 3 * qkv + lst + out_b),
+                "static_combine": (0, 0)}
     repr_b = w.bh * w.nb * w.d * 4
     cand = candidate_pairs(w)
     panel = cand * 4
     idx = w.bh * w.n * w.topk * 4
-    fine_flops = 4 * w.d * visible_pairs(w)
-    sel_pairs = w.bh * w.n * min(w.topk, w.nb) if not w.causal else None
-    if sel_pairs is None:
+    if not w.causal:
+        sel_pairs = w.bh * w.n * min(w.topk, w.nb)
+    else:
         i = np.arange(w.n, dtype=np.int64)
         sel_pairs = int(w.bh * np.minimum(w.topk, i // w.block + 1).sum())
     partial = sel_pairs * w.d * (2 if w.dtype == "bf16" else 4)
-    out_b = w.bh * w.n * w.d * 4
     rows = w.bh * w.n
     dq_rows = sel_pairs * w.d * s  # per-pair dq rows: bf16 (bf16 inputs) or fp32
     return {
@@ -95,7 +125,27 @@ def stage_work(w: W.Workload):
                       3 * qkv + (qkv if w.dtype == "bf16" else out_b) + rows * 8 + dq_rows),
         # per-pair dq rows in; dq, dk, dv out
         "bwd_reduce": (0, dq_rows + idx + 3 * out_b),
+        "ragged_copy": (0, 0),
     }
+
+
+def strict_ideal_s(w: W.Workload, nnz: int = 0) -> float:
+    """The method's steps with compulsory bytes only: Q, K, V read once, O
+    written, representatives and indices written and read once; no score
+    panel and no split-softmax partials."""
+    peak_f = MFMA_PEAK_TFLOPS[w.dtype] * 1e12
+    peak_b = HBM_PEAK_GBS * 1e9
+    s_ = 2 if w.dtype == "bf16" else 4
+    qkv_b = w.bh * w.n * w.d * s_
+    out_b = w.bh * w.n * w.d * 4
+    fine_f = 4 * w.d * visible_pairs(w)
+    if w.static:
+        return max(fine_f / peak_f, (3 * qkv_b + out_b + nnz * (4 + 512)) / peak_b)
+    repr_b = w.bh * w.nb * w.d * 4
+    idx_b = w.bh * w.n * w.topk * 4
+    return ((qkv_b + repr_b) / peak_b
+            + max(2 * w.d * candidate_pairs(w) / peak_f, (qkv_b + repr_b + idx_b) / peak_b)
+            + max(fine_f / peak_f, (3 * qkv_b + idx_b + out_b) / peak_b))
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -112,26 +162,57 @@ def measured_traffic(kernel: str, workload: str):
     return c.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w: W.Workload, inp, positions: int):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w: W.Workload, inp, positions: int, static_mask=None):
+    """The fp64 oracle on the host cores over a bounded sample of the same
+    workload (all heads, evenly spaced query positions), plus the whole
+    small workload on one thread."""
     import oracle
+    threads = oracle.threads()
     n_pos = min(positions, w.n)
     pos = np.linspace(0, w.n - 1, n_pos).astype(np.int64)
     rows = (np.arange(w.bh, dtype=np.int64)[:, None] * w.n + pos[None, :]).ravel()
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     t0 = time.perf_counter()
-    oracle.forward(inp.q, inp.k, inp.v, w.block, w.topk, w.causal, w.scale, rows)
+    if w.static:
+        oracle.attend_mask(inp.q, inp.k, inp.v, static_mask, w.scale, rows)
+        what = "masked softmax attention in fp64"
+    else:
+        oracle.forward(inp.q, inp.k, inp.v, w.block, w.topk, w.causal, w.scale, rows)
+        what = "pool + coarse scores + top-k + two-pass softmax attention in fp64"
     dt = time.perf_counter() - t0
-    return {"value": n_pos * w.batch / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n_pos} of {w.n} query positions (evenly spaced) x all {w.bh} heads; "
-                      f"pool + coarse scores + top-k + two-pass softmax attention in fp64; "
-                      f"{dt:.2f} s wall"}
+    res = {"value": round(n_pos * w.batch / dt, 1), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "sample": f"{n_pos} of {w.n} query positions (evenly spaced) x all {w.bh} heads; {what}; "
+                     f"{dt:.2f} s wall", "cpu_model": cpu_model(), "host_cpus": os.cpu_count()}
+    # the small workload in full on one thread
+    ws = W.WORKLOADS[W.SMALL]
+    si = W.generate(ws)
+    before = oracle.set_threads(1)
+    try:
+        t0 = time.perf_counter()
+        oracle.forward(si.q, si.k, si.v, ws.block, ws.topk, ws.causal, ws.scale)
+        dt1 = time.perf_counter() - t0
+    finally:
+        oracle.set_threads(before)
+    res["one_thread_small"] = {"workload": ws.name, "seconds": round(dt1, 4),
+                               "tokens_per_s": round(ws.n * ws.batch / dt1, 1), "cores": 1}
+    return res
 
 
 def cpu_baseline_backward(w: W.Workload, inp, dout):
     """The oracle's backward over one head (all its rows and key blocks),
     scaled to all heads."""
     import oracle
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle.threads()
     r = oracle.pool(inp.k[:, :1], w.block)
     sc = oracle.scores(inp.q[:, :1], r, w.block)
     idx, _, _ = oracle.topk(sc, w.n, w.block, w.topk, w.causal)
@@ -139,10 +220,162 @@ def cpu_baseline_backward(w: W.Workload, inp, dout):
     oracle.attend_backward(inp.q[:, :1], inp.k[:, :1], inp.v[:, :1], dout[:, :1], idx, w.block,
                            w.causal, w.scale)
     dt = time.perf_counter() - t0
-    return {"value": w.n * w.batch / (dt * w.heads), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+    return {"value": round(w.n * w.batch / (dt * w.heads), 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"head 0 of {w.heads} (all {w.n} rows, all key blocks): dq, dk, dv, lse in "
                       f"fp64 on the oracle's own selection; {dt:.2f} s wall, scaled to {w.heads} heads"}
+
+
+class Runner:
+    """Inputs of one workload resident on the device and its step function."""
+
+    def __init__(self, m, lib, w: W.Workload, which: str, args):
+        import torch
+        self.torch, self.m, self.lib, self.w = torch, m, lib, w
+        self.inp = W.generate(w)
+        dev = torch.device("cuda:0")
+        inp = self.inp
+        if w.dtype == "bf16":
+            q, k, v = (torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+                       for b in (inp.q_bits, inp.k_bits, inp.v_bits))
+        else:
+            q, k, v = (torch.from_numpy(x).to(dev) for x in (inp.q, inp.k, inp.v))
+        out = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        h = lib.handle
+        self.nnz = 0
+        self.mask = None
+        self.tiles = None
+        self.dout_np = None
+        if w.static:
+            rp, col, rm = m.bsa_tiles_window_stride(w.n, w.window, w.stride)
+            self.nnz = int(col.size)
+            self.tiles = m.bsa_tiles_create(h, w.n, rp, col, rm)
+            tiles = self.tiles
+
+            def step():
+                m.bsa_forward_static(h, q, k, v, out, tiles, scale=w.scale)
+        elif which == "forward":
+            idx = torch.empty(q.shape[:3] + (w.topk,), dtype=torch.int32, device=dev)
+
+            def step():
+                m.bsa_forward(h, q, k, v, out, idx, topk=w.topk, scale=w.scale, causal=w.causal)
+        else:
+            idx = torch.empty(q.shape[:3] + (w.topk,), dtype=torch.int32, device=dev)
+            lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+            m.bsa_forward_train(h, q, k, v, out, idx, lse, topk=w.topk, scale=w.scale, causal=w.causal)
+            self.dout_np = W.grad_output(q.shape, w.seed)
+            dout = torch.from_numpy(self.dout_np).to(dev)
+            dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
+
+            def step():
+                m.bsa_backward(h, q, k, v, out, dout, idx, lse, dq, dk, dv, scale=w.scale, causal=w.causal)
+        self.step = step
+        self.stream = torch.cuda.current_stream(dev)
+        self.tensors = [q, k, v, out]
+
+    def close(self):
+        if self.tiles is not None:
+            self.tiles.close()
+        self.tensors = []
+
+    def warm(self, steps):
+        """Mean milliseconds of `steps` back-to-back steps."""
+        torch = self.torch
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(self.stream)
+        for _ in range(steps):
+            self.step()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def cold(self, steps, scratch, profile=False):
+        """Milliseconds of each of `steps` steps, each after a 1 GiB scratch
+        write; with profile, also the per-stage HIP-event times."""
+        torch, m, h = self.torch, self.m, self.lib.handle
+        if profile:
+            m.bsa_profile_read(h, reset=True)
+            m.bsa_profile_enable(h, True)
+        times = []
+        for i in range(steps):
+            scratch.fill_(float(i))
+            torch.cuda.synchronize()
+            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            c0.record(self.stream)
+            self.step()
+            c1.record(self.stream)
+            torch.cuda.synchronize()
+            times.append(c0.elapsed_time(c1))
+        stages = None
+        if profile:
+            ms, launches = m.bsa_profile_read(h, reset=True)
+            m.bsa_profile_enable(h, False)
+            stages = {name: (ms[i], launches[i]) for i, name in enumerate(m.STAGE_NAMES) if launches[i]}
+        return times, stages
+
+
+def stage_roofline(w, work, name, per_launch_ms, launches_per_step):
+    """The roofline of one stage: its algorithmic flops (MFMA-bound) or bytes
+    (HBM-bound) per launch over its average launch time; the bound is the
+    resource whose peak the algorithmic work would take longer on."""
+    flops, nbytes = work[name]
+    t_launch = per_launch_ms * 1e-3
+    t_mfma = flops / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        achieved, peak, unit = flops / launches_per_step / t_launch / 1e12, MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
+    else:
+        achieved, peak, unit = nbytes / launches_per_step / t_launch / 1e9, HBM_PEAK_GBS, "GB/s"
+    return {"bound": "mfma" if t_mfma >= t_hbm else "hbm", "achieved": round(achieved, 3), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 5)}
+
+
+def measure(r: Runner, args, scratch, steps, warmup):
+    """Warm-up, cold steps (the value), warm steps, cold per-stage times."""
+    w = r.w
+    for _ in range(warmup):
+        r.step()
+    r.torch.cuda.synchronize()
+    cold_t, _ = r.cold(steps, scratch)
+    warm_ms = r.warm(steps)
+    _, stages = r.cold(steps, scratch, profile=True)
+    per_step = {k: v[0] / steps for k, v in stages.items()}
+    per_launch = {k: v[0] / v[1] for k, v in stages.items()}
+    lps = {k: v[1] // steps for k, v in stages.items()}
+    work = stage_work(w, r.nnz)
+    ms_med = float(np.median(cold_t))
+    tokens = w.batch * w.n
+    total_flops = sum(work[k][0] for k in per_step if k in work)
+    res = {
+        "ms_cold_median": round(ms_med, 5), "ms_cold_min": round(float(np.min(cold_t)), 5),
+        "ms_cold_mean": round(float(np.mean(cold_t)), 5), "ms_warm": round(warm_ms, 5),
+        "tokens_per_s": round(tokens / (ms_med * 1e-3), 1),
+        "tokens_per_s_warm": round(tokens / (warm_ms * 1e-3), 1),
+        "effective_tflops": round(total_flops / (ms_med * 1e-3) / 1e12, 3),
+        "algorithmic_gflop": round(total_flops / 1e9, 4),
+        "stage_ms_per_step": {k: round(v, 5) for k, v in per_step.items()},
+    }
+    known = [k for k in per_step if k in work and (work[k][0] or work[k][1])]
+    dom = max(known, key=per_step.get)
+    res["roofline"] = dict(stage_roofline(w, work, dom, per_launch[dom], lps[dom]),
+                           traffic=measured_traffic(dom, w.name) if dom in _TRAFFIC_STAGES else None,
+                           kernel=dom, avg_launch_ms=round(per_launch[dom], 5), launches_per_step=lps[dom])
+    res["stage_rooflines"] = {k: {f: stage_roofline(w, work, k, per_launch[k], lps[k])[f]
+                                  for f in ("bound", "achieved", "unit", "frac")}
+                              for k in sorted(known, key=per_step.get, reverse=True)}
+    ideal_ms = sum(max(work[k][0] / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12), work[k][1] / (HBM_PEAK_GBS * 1e9))
+                   for k in known) * 1e3
+    res["path_roofline"] = {"ideal_ms": round(ideal_ms, 5), "frac": round(ideal_ms / ms_med, 5)}
+    if args.which == "forward":
+        strict_ms = strict_ideal_s(w, r.nnz) * 1e3
+        res["path_roofline"]["strict_ideal_ms"] = round(strict_ms, 5)
+        res["path_roofline"]["strict_frac"] = round(strict_ms / ms_med, 5)
+    return res
+
+
+_TRAFFIC_STAGES = ("block_pool", "coarse_score", "topk_select", "coarse_select", "sparse_flash_fwd",
+                   "gather_index", "gather_combine", "bwd_prep", "bwd_index", "bwd_pairs", "bwd_reduce")
 
 
 def main():
@@ -151,14 +384,15 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=W.HEADLINE, choices=sorted(W.WORKLOADS))
+    ap.add_argument("--only", action="store_true", help="time the chosen workload only")
+    ap.add_argument("--other-steps", type=int, default=20, help="cold steps for each other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-positions", type=int, default=32768)
-    ap.add_argument("--cold-steps", type=int, default=10,
-                    help="extra steps timed one by one after a cache-flushing 1 GiB write (0 = none)")
     ap.add_argument("--fine-strategy", choices=["block_gather", "query_tile"], default="block_gather")
     ap.add_argument("--select-strategy", choices=["fused", "panel"], default="fused")
     ap.add_argument("--panel-chunk-mb", type=int, default=0, help="coarse-score panel chunk (0 = default)")
     ap.add_argument("--fine-chunk-mb", type=int, default=0, help="block-gather partial chunk (0 = default)")
+    ap.add_argument("--static-item-tiles", type=int, default=0, help="static work-item size (0 = per call)")
     ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB -> 1 GiB device copy (3 times), the reference "
@@ -184,17 +418,6 @@ def main():
     import content_dependent_block_amd as m
 
     w = W.WORKLOADS[args.workload]
-    if w.static:
-        raise SystemExit("bench.py times the dynamic two-stage forward; pick a dynamic workload")
-    inp = W.generate(w)
-    dev = torch.device("cuda:0")
-    if w.dtype == "bf16":
-        q, k, v = (torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
-                   for b in (inp.q_bits, inp.k_bits, inp.v_bits))
-    else:
-        q, k, v = (torch.from_numpy(x).to(dev) for x in (inp.q, inp.k, inp.v))
-    out = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    idx = torch.empty(q.shape[:3] + (w.topk,), dtype=torch.int32, device=dev)
     lib = m.BlockSparseAttention(0)
     h = lib.handle
     m.bsa_set_option(h, m.BSA_OPT_FINE_STRATEGY,
@@ -205,146 +428,79 @@ def main():
         m.bsa_set_option(h, m.BSA_OPT_PANEL_CHUNK_BYTES, args.panel_chunk_mb << 20)
     if args.fine_chunk_mb:
         m.bsa_set_option(h, m.BSA_OPT_FINE_CHUNK_BYTES, args.fine_chunk_mb << 20)
+    m.bsa_set_option(h, m.BSA_OPT_STATIC_ITEM_TILES, args.static_item_tiles)
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB cache flush
 
-    if args.which == "forward":
-        def step():
-            m.bsa_forward(h, q, k, v, out, idx, topk=w.topk, scale=w.scale, causal=w.causal)
+    r = Runner(m, lib, w, args.which, args)
+    res = measure(r, args, scratch, args.steps, args.warmup)
+    inp, dout_np = r.inp, r.dout_np
+    static_mask = None
+    if w.static and not args.no_cpu_baseline:
+        import oracle
+        static_mask = oracle.window_stride_mask(w.n, w.window, w.stride)
+    r.close()
+    del r
+    torch.cuda.empty_cache()
+
+    others = {}
+    if not args.only and args.which == "forward":
+        for name, ow in W.WORKLOADS.items():
+            if name == w.name:
+                continue
+            print(f"[bench] {name}", file=sys.stderr, flush=True)
+            ro = Runner(m, lib, ow, "forward", args)
+            o = measure(ro, args, scratch, args.other_steps, 3)
+            ro.close()
+            del ro
+            torch.cuda.empty_cache()
+            others[name] = {k: o[k] for k in ("ms_cold_median", "ms_cold_min", "ms_warm", "tokens_per_s",
+                                              "tokens_per_s_warm", "effective_tflops", "algorithmic_gflop",
+                                              "stage_ms_per_step", "path_roofline")}
+            others[name]["roofline"] = {k: o["roofline"][k] for k in ("kernel", "bound", "achieved", "unit",
+                                                                      "frac", "avg_launch_ms")}
+            others[name]["config"] = {"batch": ow.batch, "heads": ow.heads, "n": ow.n, "d": ow.d,
+                                      "dtype": ow.dtype, "topk": ow.topk, "causal": ow.causal,
+                                      "static": ow.static}
+    del scratch
+
+    cfg = {"workload": w.name, "batch": w.batch, "heads": w.heads, "n": w.n, "d": w.d, "pass": args.which}
+    if w.static:
+        cfg.update(window=w.window, stride=w.stride, tile=64, static_item_tiles=args.static_item_tiles or "auto")
     else:
-        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-        m.bsa_forward_train(h, q, k, v, out, idx, lse, topk=w.topk, scale=w.scale, causal=w.causal)
-        dout_np = W.grad_output(q.shape, w.seed)
-        dout = torch.from_numpy(dout_np).to(dev)
-        dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3))
-
-        def step():
-            m.bsa_backward(h, q, k, v, out, dout, idx, lse, dq, dk, dv, scale=w.scale, causal=w.causal)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-
-    # Cold steps (after the timed region, not part of `value`): before each
-    # step a 1 GiB scratch buffer is written, which evicts the inputs from
-    # the 256 MB Infinity Cache; each step is timed alone with HIP events.
-    cold = None
-    if args.cold_steps > 0:
-        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        times = []
-        for i in range(args.cold_steps):
-            scratch.fill_(float(i))
-            c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            c0.record(stream)
-            step()
-            c1.record(stream)
-            torch.cuda.synchronize()
-            times.append(c0.elapsed_time(c1))
-        del scratch
-        cold = {"steps": args.cold_steps, "ms_median": round(float(np.median(times)), 5),
-                "ms_min": round(float(np.min(times)), 5),
-                "flush": "1 GiB scratch written before each step"}
-
-    # Second pass: per-kernel HIP events on the launch stream.
-    m.bsa_profile_read(h, reset=True)
-    m.bsa_profile_enable(h, True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms, launches = m.bsa_profile_read(h, reset=True)
-    m.bsa_profile_enable(h, False)
-    per_step = {name: ms[i] / args.steps for i, name in enumerate(m.STAGE_NAMES) if launches[i]}
-    per_launch = {name: ms[i] / launches[i] for i, name in enumerate(m.STAGE_NAMES) if launches[i]}
-    launches_per_step = {name: launches[i] // args.steps for i, name in enumerate(m.STAGE_NAMES)
-                         if launches[i]}
-
-    work = stage_work(w)
-
-    def stage_roofline(name):
-        """The roofline of one stage: its algorithmic flops (MFMA-bound) or
-        bytes (HBM-bound) per launch over its average launch time; the bound
-        is the resource whose peak the algorithmic work would take longer on."""
-        flops, nbytes = work[name]
-        t_launch = per_launch[name] * 1e-3
-        n_launch = launches_per_step[name]
-        t_mfma = flops / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12)
-        t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
-        if t_mfma >= t_hbm:
-            achieved, peak, unit = flops / n_launch / t_launch / 1e12, MFMA_PEAK_TFLOPS[w.dtype], "TFLOP/s"
-        else:
-            achieved, peak, unit = nbytes / n_launch / t_launch / 1e9, HBM_PEAK_GBS, "GB/s"
-        return {"bound": "mfma" if t_mfma >= t_hbm else "hbm", "achieved": round(achieved, 3), "peak": peak,
-                "unit": unit, "frac": round(achieved / peak, 5)}
-
-    dom = max(per_step, key=per_step.get)
-    roofline = dict(stage_roofline(dom), traffic=measured_traffic(dom, w.name), kernel=dom,
-                    avg_launch_ms=round(per_launch[dom], 5), launches_per_step=launches_per_step[dom])
-    # the whole step against the sum of every stage's ideal time (the longer of
-    # its algorithmic flops at the MFMA peak and its algorithmic bytes at the
-    # HBM peak)
-    ideal_ms = sum(max(work[k_][0] / (MFMA_PEAK_TFLOPS[w.dtype] * 1e12), work[k_][1] / (HBM_PEAK_GBS * 1e9))
-                   for k_ in per_step) * 1e3
-    path_roofline = {"ideal_ms": round(ideal_ms, 5), "frac": round(ideal_ms / ms_per_step, 5)}
-    if args.which == "forward":
-        # strict: the method's three steps with compulsory bytes only (Q, K, V
-        # read once, O written, representatives and indices written and read
-        # once; no score panel, no split-softmax partials)
-        s_ = 2 if w.dtype == "bf16" else 4
-        qkv_b = w.bh * w.n * w.d * s_
-        repr_b = w.bh * w.nb * w.d * 4
-        idx_b = w.bh * w.n * w.topk * 4
-        out_b = w.bh * w.n * w.d * 4
-        peak_f = MFMA_PEAK_TFLOPS[w.dtype] * 1e12
-        peak_b = HBM_PEAK_GBS * 1e9
-        strict_s = (max(0.0, (qkv_b + repr_b) / peak_b)
-                    + max(work["coarse_select"][0] / peak_f, (qkv_b + repr_b + idx_b) / peak_b)
-                    + max(4 * w.d * visible_pairs(w) / peak_f, (3 * qkv_b + idx_b + out_b) / peak_b))
-        path_roofline["strict_ideal_ms"] = round(strict_s * 1e3, 5)
-        path_roofline["strict_frac"] = round(strict_s * 1e3 / ms_per_step, 5)
-    # every stage's bound and fraction, longest first (the first is `roofline`)
-    stage_rooflines = {k_: {f: stage_roofline(k_)[f] for f in ("bound", "achieved", "unit", "frac")}
-                       for k_ in sorted(per_step, key=per_step.get, reverse=True)}
-
-    total_flops = sum(work[k_][0] for k_ in per_step)  # matmul-only: coarse + fine, stages that ran
-    tokens = w.batch * w.n
+        cfg.update(block=w.block, topk=w.topk, causal=w.causal, select_strategy=args.select_strategy,
+                   fine_strategy=args.fine_strategy, panel_chunk_mb=args.panel_chunk_mb or 128,
+                   fine_chunk_mb=args.fine_chunk_mb or 1024)
     result = {
         "metric": METRIC if args.which == "forward" else METRIC_BWD,
-        "value": round(tokens / (ms_per_step * 1e-3), 1),
+        "value": res["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": res["ms_cold_median"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic: seeded N(0,1) q/k/v plus per-block key offsets N(0,0.5^2), "
-                "rounded to bf16 (no dataset)" if w.key_offsets else "synthetic: seeded N(0,1)",
-        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "n": w.n, "d": w.d,
-                   "block": w.block, "topk": w.topk, "causal": w.causal,
-                   "select_strategy": args.select_strategy, "fine_strategy": args.fine_strategy,
-                   "panel_chunk_mb": args.panel_chunk_mb or 128, "fine_chunk_mb": args.fine_chunk_mb or 1024,
-                   "pass": args.which},
-        "effective_tflops": round(total_flops / (ms_per_step * 1e-3) / 1e12, 3),
-        "algorithmic_gflop": round(total_flops / 1e9, 3),
-        "stage_ms_per_step": {k_: round(v_, 5) for k_, v_ in per_step.items()},
-        "roofline": roofline,
-        "stage_rooflines": stage_rooflines,
-        "path_roofline": path_roofline,
+        "data": ("synthetic: seeded N(0,1) q/k/v plus per-block key offsets N(0,0.5^2), rounded to bf16 "
+                 "(no dataset)") if w.key_offsets else "synthetic: seeded N(0,1) (no dataset)",
+        "config": cfg,
+        "timing": {"value_from": "median of the cold steps (each after a 1 GiB scratch write; HIP events)",
+                   "ms_cold_median": res["ms_cold_median"], "ms_cold_min": res["ms_cold_min"],
+                   "ms_cold_mean": res["ms_cold_mean"], "ms_warm": res["ms_warm"],
+                   "tokens_per_s_warm": res["tokens_per_s_warm"]},
+        "effective_tflops": res["effective_tflops"],
+        "algorithmic_gflop": res["algorithmic_gflop"],
+        "stage_ms_per_step": res["stage_ms_per_step"],
+        "roofline": res["roofline"],
+        "stage_rooflines": res["stage_rooflines"],
+        "path_roofline": res["path_roofline"],
     }
-    if cold is not None:
-        result["cold"] = cold
+    if others:
+        result["workloads"] = others
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = (cpu_baseline(w, inp, args.cpu_positions) if args.which == "forward"
-                                  else cpu_baseline_backward(w, inp, dout_np))
+        result["cpu_baseline"] = (cpu_baseline(w, inp, args.cpu_positions, static_mask)
+                                  if args.which == "forward" else cpu_baseline_backward(w, inp, dout_np))
     lib.close()
     print(json.dumps(result), flush=True)
 

@@ -16,7 +16,8 @@ import torch
 
 from ._binding import *  # noqa: F401,F403  (bsa_* functions and constants)
 from ._binding import (EXPORTED, STAGE_NAMES, BsaError, bsa_backward, bsa_create, bsa_destroy,
-                       bsa_forward, bsa_forward_budgets, bsa_forward_static, bsa_forward_train)
+                       bsa_forward, bsa_forward_budgets, bsa_forward_static, bsa_forward_train,
+                       bsa_tiles_create)
 
 
 class BlockSparseAttention:
@@ -63,13 +64,15 @@ class BlockSparseAttention:
                         causal=causal, stream=stream)
         return (out, idx) if return_indices else out
 
-    def forward_static(self, q, k, v, tile_row_ptr, tile_col, tile_rowmask=None, *,
-                       scale: float | None = None, stream=None):
+    def tiles(self, n: int, row_ptr, col, rowmask=None):
+        """A device tile list (validated on the host) for forward_static."""
+        return bsa_tiles_create(self.handle, n, row_ptr, col, rowmask)
+
+    def forward_static(self, q, k, v, tiles, *, scale: float | None = None, stream=None):
         d = q.shape[-1]
         scale = 1.0 / math.sqrt(d) if scale is None else scale
         out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-        bsa_forward_static(self.handle, q, k, v, out, tile_row_ptr, tile_col, tile_rowmask,
-                           scale=scale, stream=stream)
+        bsa_forward_static(self.handle, q, k, v, out, tiles, scale=scale, stream=stream)
         return out
 
 

@@ -26,12 +26,14 @@ BSA_STAGE_POOL, BSA_STAGE_COARSE, BSA_STAGE_TOPK, BSA_STAGE_FINE = 0, 1, 2, 3
 BSA_STAGE_GATHER_INDEX, BSA_STAGE_GATHER_COMBINE, BSA_STAGE_COARSE_TOPK = 4, 5, 6
 BSA_STAGE_BWD_PREP, BSA_STAGE_BWD_INDEX, BSA_STAGE_BWD_PAIRS, BSA_STAGE_BWD_REDUCE = 7, 8, 9, 10
 BSA_STAGE_RAGGED_COPY = 11
-BSA_NUM_STAGES = 12
+BSA_STAGE_STATIC_COMBINE = 12
+BSA_NUM_STAGES = 13
 STAGE_NAMES = ("block_pool", "coarse_score", "topk_select", "sparse_flash_fwd", "gather_index",
                "gather_combine", "coarse_select", "bwd_prep", "bwd_index", "bwd_pairs", "bwd_reduce",
-               "ragged_copy")
+               "ragged_copy", "static_combine")
 BSA_OPT_PANEL_CHUNK_BYTES, BSA_OPT_FINE_STRATEGY, BSA_OPT_FINE_CHUNK_BYTES = 0, 1, 2
 BSA_OPT_SELECT_STRATEGY = 3
+BSA_OPT_STATIC_ITEM_TILES = 4
 BSA_FINE_BLOCK_GATHER, BSA_FINE_QUERY_TILE = 0, 1
 BSA_SELECT_FUSED, BSA_SELECT_PANEL = 0, 1
 
@@ -59,7 +61,9 @@ _sig("bsa_fine_forward", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F
 _sig("bsa_block_pool", [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P])
 _sig("bsa_coarse_score", [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P])
 _sig("bsa_topk_select", [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P])
-_sig("bsa_forward_static", [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _I64, _F, _P])
+_sig("bsa_tiles_create", [_P, _I, _I, _P, _P, _P, _I64, ctypes.POINTER(_P)])
+_sig("bsa_tiles_destroy", [_P])
+_sig("bsa_forward_static", [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _F, _P])
 _sig("bsa_tiles_from_mask", [_P, _I, _I, _P, _P, _P, ctypes.POINTER(_I64)])
 _sig("bsa_tiles_window_stride", [_I, _I, _I, _I, _P, _P, _P, ctypes.POINTER(_I64)])
 _sig("bsa_tiles_validate", [_P, _P, _I64, _I, _I])
@@ -70,7 +74,8 @@ EXPORTED = ("bsa_create", "bsa_destroy", "bsa_status_string", "bsa_last_error", 
             "bsa_workspace_bytes", "bsa_forward", "bsa_forward_budgets", "bsa_forward_train",
             "bsa_backward", "bsa_fine_forward",
             "bsa_block_pool",
-            "bsa_coarse_score", "bsa_topk_select", "bsa_forward_static", "bsa_tiles_from_mask",
+            "bsa_coarse_score", "bsa_topk_select", "bsa_tiles_create", "bsa_tiles_destroy",
+            "bsa_forward_static", "bsa_tiles_from_mask",
             "bsa_tiles_window_stride", "bsa_tiles_validate", "bsa_profile_enable",
             "bsa_profile_read")
 
@@ -276,25 +281,64 @@ def bsa_topk_select(h, panel, block_idx_out, *, block: int = 64, causal: bool = 
 
 
 # --------------------------------------------------------------- static --
-def bsa_forward_static(h, q, k, v, out, tile_row_ptr, tile_col, tile_rowmask=None, *,
-                       scale: float, stream=None) -> None:
+class TileList:
+    """A validated tile list in device memory (bsa_tiles_create); free it with
+    close() or use it as a context manager."""
+
+    def __init__(self, h, n: int, row_ptr, col, rowmask=None, tile: int = 64):
+        row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
+        col = np.ascontiguousarray(col, dtype=np.int32)
+        if row_ptr.size != -(-n // tile) + 1:
+            raise ValueError(f"row_ptr needs {-(-n // tile) + 1} entries, got {row_ptr.size}")
+        pm = None
+        if rowmask is not None:
+            rowmask = np.ascontiguousarray(rowmask).view(np.uint64).reshape(-1, tile)
+            if rowmask.shape[0] != col.size:
+                raise ValueError(f"rowmask needs {col.size} rows of {tile}, got {rowmask.shape[0]}")
+            pm = rowmask.ctypes.data
+        self.n, self.nnz = n, int(col.size)
+        self.ptr = ctypes.c_void_p()
+        _check(_lib.bsa_tiles_create(h, n, tile, row_ptr.ctypes.data, col.ctypes.data if col.size else None,
+                                     pm, col.size, ctypes.byref(self.ptr)), h)
+
+    def close(self) -> None:
+        if self.ptr:
+            _check(_lib.bsa_tiles_destroy(self.ptr))
+            self.ptr = ctypes.c_void_p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def bsa_tiles_create(h, n: int, row_ptr, col, rowmask=None, tile: int = 64) -> TileList:
+    """Validate a host tile list and copy it to the device (a TileList)."""
+    return TileList(h, n, row_ptr, col, rowmask, tile)
+
+
+def bsa_tiles_destroy(tiles: TileList) -> None:
+    tiles.close()
+
+
+def bsa_forward_static(h, q, k, v, out, tiles: TileList, *, scale: float, tile: int = 64,
+                       stream=None) -> None:
     pq, pk, pv, dev = _qkv(q, k, v)
     b, hh, n, d = q.shape
     po = _need(out, "out", q.shape, torch.float32, dev)
-    prp = _need(tile_row_ptr, "tile_row_ptr", (n // 64 + 1,), torch.int32, dev)
-    nnz = int(tile_col.numel())
-    pc = _need(tile_col, "tile_col", (nnz,), torch.int32, dev)
-    pm = None
-    if tile_rowmask is not None:
-        pm = _need(tile_rowmask, "tile_rowmask", (nnz, 64), None, dev)
-        if tile_rowmask.element_size() != 8:
-            raise TypeError("tile_rowmask must hold 64-bit masks")
-    _check(_lib.bsa_forward_static(h, pq, pk, pv, po, b, hh, n, d, _dtype_code(q), prp, pc, pm,
-                                   nnz, float(scale), _stream(stream, dev)), h)
+    _check(_lib.bsa_forward_static(h, pq, pk, pv, po, b, hh, n, d, _dtype_code(q), tile, tiles.ptr,
+                                   float(scale), _stream(stream, dev)), h)
 
 
 def _tiles(fn, n, *head_args):
-    row_ptr = np.zeros(n // 64 + 1, dtype=np.int32)
+    row_ptr = np.zeros(-(-n // 64) + 1, dtype=np.int32)
     nnz = ctypes.c_int64(0)
     _check(fn(*head_args, row_ptr.ctypes.data, None, None, ctypes.byref(nnz)))
     col = np.zeros(max(nnz.value, 1), dtype=np.int32)
@@ -321,7 +365,7 @@ def bsa_tiles_window_stride(n: int, window: int, stride: int, tile: int = 64):
 def bsa_tiles_validate(row_ptr: np.ndarray, col: np.ndarray, n: int, tile: int = 64) -> bool:
     row_ptr = np.ascontiguousarray(row_ptr, dtype=np.int32)
     col = np.ascontiguousarray(col, dtype=np.int32)
-    if row_ptr.size != n // tile + 1:
+    if row_ptr.size != -(-n // tile) + 1:
         return False
     return _lib.bsa_tiles_validate(row_ptr.ctypes.data, col.ctypes.data if col.size else None,
                                    col.size, n, tile) == BSA_OK

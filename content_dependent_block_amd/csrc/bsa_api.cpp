@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <new>
 #include <string>
@@ -42,6 +43,8 @@ struct bsa_handle_s {
   Buf b_ld, b_dq, b_dkv, b_dob;
   bool counts_zero = false;  // g_count holds zeros (the bucketing's scan leaves it so)  // backward: per-row (lse, delta), per-pair dq, per-item dk/dv, bf16 dout
   Buf r_q, r_k, r_v, r_o, r_do, r_lse, r_idx, r_dq, r_dk, r_dv;  // padded copies (ragged n)
+  Buf s_part, s_lse;  // static mode: partial rows of split query tiles and their log-sum-exp
+  int64_t static_item_tiles = 0;  // 0: chosen per call; else the most key tiles per work item
   // timing
   bool profiling = false;
   struct Rec {
@@ -51,6 +54,30 @@ struct bsa_handle_s {
   std::vector<Rec> recs;
   std::vector<hipEvent_t> free_events;
 };
+
+// A validated static tile list in device memory (bsa_tiles_create), with the
+// work-item schedules made from it so far (one per item size).
+struct bsa_tiles_s {
+  int device = 0;
+  int n = 0, nt = 0;
+  int64_t nnz = 0;
+  std::vector<int32_t> row_ptr;   // host copy [nt + 1]
+  int32_t* col = nullptr;         // device [nnz]
+  uint64_t* rowmask = nullptr;    // device [nnz][64], or NULL
+  struct Schedule {
+    int64_t S = 0;                // most key tiles per item
+    std::vector<int4> items, split;  // host copies (kept while the device copies may be read)
+    int nslots = 0;
+    int4* d_items = nullptr;
+    int4* d_split = nullptr;
+  };
+  std::vector<Schedule> schedules;
+};
+
+namespace bsa {
+bsa_status tiles_check(const int32_t* row_ptr, const int32_t* col, const uint64_t* rowmask, int64_t nnz,
+                       int n, int tile, char* why, size_t why_len);
+}
 
 namespace {
 
@@ -243,7 +270,7 @@ BSA_API bsa_status bsa_destroy(bsa_handle h) {
   if (h->idx) (void)hipFree(h->idx);
   for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_rec, &h->g_wgv, &h->g_list, &h->g_po,
                  &h->b_ld, &h->b_dq, &h->b_dkv, &h->b_dob, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
-                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv})
+                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv, &h->s_part, &h->s_lse})
     if (b->p) (void)hipFree(b->p);
   delete h;
   return BSA_OK;
@@ -270,6 +297,10 @@ BSA_API bsa_status bsa_set_option(bsa_handle h, int option, int64_t value) {
       if (value < 1) return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: fine chunk must be > 0");
       h->fine_chunk_bytes = value;
       return BSA_OK;
+    case BSA_OPT_STATIC_ITEM_TILES:
+      if (value < 0) return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: static item tiles must be >= 0");
+      h->static_item_tiles = value;
+      return BSA_OK;
     default:
       return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: unknown option %d", option);
   }
@@ -280,7 +311,7 @@ BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
   *bytes = h->repr_bytes + h->split_bytes + h->panel_bytes + h->idx_bytes;
   for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_rec, &h->g_wgv, &h->g_list, &h->g_po,
                  &h->b_ld, &h->b_dq, &h->b_dkv, &h->b_dob, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
-                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv})
+                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv, &h->s_part, &h->s_lse})
     *bytes += b->bytes;
   return BSA_OK;
 }
@@ -825,31 +856,196 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   return BSA_OK;
 }
 
+// ------------------------------------------------------ static forward --
+
+BSA_API bsa_status bsa_tiles_create(bsa_handle h, int n, int tile, const int32_t* row_ptr,
+                                    const int32_t* col, const uint64_t* rowmask, int64_t nnz,
+                                    bsa_tiles* out) {
+  const char* fn = "bsa_tiles_create";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  if (!out) return fail(h, BSA_ERR_INVALID_ARG, "%s: out is NULL", fn);
+  *out = nullptr;
+  char why[256] = {0};
+  const bsa_status st = bsa::tiles_check(row_ptr, col, rowmask, nnz, n, tile, why, sizeof why);
+  if (st != BSA_OK) return fail(h, st, "%s: %s", fn, why);
+  if (nnz > (int64_t(1) << 31) - 1)
+    return fail(h, BSA_ERR_UNSUPPORTED, "%s: at most 2^31 - 1 list entries (got %lld)", fn, (long long)nnz);
+  DeviceGuard dg(h->device);
+  bsa_tiles t = new (std::nothrow) bsa_tiles_s();
+  if (!t) return fail(h, BSA_ERR_OUT_OF_MEMORY, "%s: host allocation failed", fn);
+  t->device = h->device;
+  t->n = n;
+  t->nt = (n + 63) / 64;
+  t->nnz = nnz;
+  t->row_ptr.assign(row_ptr, row_ptr + t->nt + 1);
+  size_t have = 0;
+  bsa_status r = BSA_OK;
+  if (nnz > 0) {
+    r = grow(h, reinterpret_cast<void**>(&t->col), &have, size_t(nnz) * 4, "tile list");
+    if (r == BSA_OK && hipMemcpy(t->col, col, size_t(nnz) * 4, hipMemcpyHostToDevice) != hipSuccess)
+      r = fail(h, BSA_ERR_LAUNCH, "%s: copy of the tile list failed", fn);
+    if (r == BSA_OK && rowmask) {
+      have = 0;
+      r = grow(h, reinterpret_cast<void**>(&t->rowmask), &have, size_t(nnz) * 64 * 8, "tile row masks");
+      if (r == BSA_OK &&
+          hipMemcpy(t->rowmask, rowmask, size_t(nnz) * 64 * 8, hipMemcpyHostToDevice) != hipSuccess)
+        r = fail(h, BSA_ERR_LAUNCH, "%s: copy of the row masks failed", fn);
+    }
+  }
+  if (r != BSA_OK) {
+    (void)bsa_tiles_destroy(t);
+    return r;
+  }
+  *out = t;
+  return BSA_OK;
+}
+
+BSA_API bsa_status bsa_tiles_destroy(bsa_tiles t) {
+  if (!t) return BSA_OK;
+  DeviceGuard dg(t->device);
+  if (t->col) (void)hipFree(t->col);
+  if (t->rowmask) (void)hipFree(t->rowmask);
+  for (auto& sc : t->schedules) {
+    if (sc.d_items) (void)hipFree(sc.d_items);
+    if (sc.d_split) (void)hipFree(sc.d_split);
+  }
+  delete t;
+  return BSA_OK;
+}
+
+namespace {
+
+// Work items of at most S key tiles (a longer query-tile list is cut into
+// ceil(count / S) items of near-equal length that write partials), ordered
+// heaviest first; empty query tiles get an item of length 0 (it writes zeros).
+int64_t count_items(const bsa_tiles_s& t, int64_t S) {
+  int64_t items = 0;
+  for (int q = 0; q < t.nt; ++q) {
+    const int64_t c = t.row_ptr[q + 1] - t.row_ptr[q];
+    items += c <= S ? 1 : (c + S - 1) / S;
+  }
+  return items;
+}
+
+bsa_status tiles_schedule(bsa_handle h, bsa_tiles t, int64_t S, const bsa_tiles_s::Schedule** out) {
+  for (const auto& sc : t->schedules)
+    if (sc.S == S) {
+      *out = &sc;
+      return BSA_OK;
+    }
+  bsa_tiles_s::Schedule sc;
+  sc.S = S;
+  for (int q = 0; q < t->nt; ++q) {
+    const int p0 = t->row_ptr[q], c = t->row_ptr[q + 1] - p0;
+    if (c <= S) {
+      sc.items.push_back(make_int4(q, p0, c, -1));
+      continue;
+    }
+    const int m = static_cast<int>((c + S - 1) / S);
+    sc.split.push_back(make_int4(q, sc.nslots, m, 0));
+    for (int j = 0, p = p0; j < m; ++j) {
+      const int len = c / m + (j < c % m ? 1 : 0);
+      sc.items.push_back(make_int4(q, p, len, sc.nslots + j));
+      p += len;
+    }
+    sc.nslots += m;
+  }
+  std::stable_sort(sc.items.begin(), sc.items.end(), [](const int4& a, const int4& b) { return a.z > b.z; });
+  size_t have = 0;
+  TRY(grow(h, reinterpret_cast<void**>(&sc.d_items), &have, sc.items.size() * sizeof(int4), "static work items"));
+  if (!sc.split.empty()) {
+    have = 0;
+    const bsa_status r = grow(h, reinterpret_cast<void**>(&sc.d_split), &have, sc.split.size() * sizeof(int4),
+                              "static split list");
+    if (r != BSA_OK) {
+      (void)hipFree(sc.d_items);
+      return r;
+    }
+  }
+  if (hipMemcpy(sc.d_items, sc.items.data(), sc.items.size() * sizeof(int4), hipMemcpyHostToDevice) != hipSuccess ||
+      (!sc.split.empty() &&
+       hipMemcpy(sc.d_split, sc.split.data(), sc.split.size() * sizeof(int4), hipMemcpyHostToDevice) != hipSuccess)) {
+    (void)hipFree(sc.d_items);
+    if (sc.d_split) (void)hipFree(sc.d_split);
+    return fail(h, BSA_ERR_LAUNCH, "bsa_forward_static: copy of the work-item schedule failed");
+  }
+  t->schedules.push_back(std::move(sc));
+  *out = &t->schedules.back();
+  return BSA_OK;
+}
+
+// Item size: enough items for about four workgroups per CU (halving from one
+// item per query tile), and no item longer than about twice the mean list.
+int64_t pick_item_tiles(const bsa_tiles_s& t, int64_t bh) {
+  int64_t maxc = 1, total = 0;
+  for (int q = 0; q < t.nt; ++q) {
+    const int64_t c = t.row_ptr[q + 1] - t.row_ptr[q];
+    maxc = c > maxc ? c : maxc;
+    total += c;
+  }
+  int64_t S = 1;
+  while (S < maxc) S <<= 1;
+  while (S > 2 && bh * count_items(t, S) < 1024) S >>= 1;
+  int64_t bal = 4;
+  while (bal < 2 * total / t.nt) bal <<= 1;
+  return S < bal ? S : bal;
+}
+
+}  // namespace
+
 BSA_API bsa_status bsa_forward_static(bsa_handle h, const void* q, const void* k, const void* v,
                                       float* out, int batch, int heads, int n, int d,
-                                      bsa_dtype dtype, const int32_t* tile_row_ptr,
-                                      const int32_t* tile_col, const uint64_t* tile_rowmask,
-                                      int64_t nnz, float scale, void* stream) {
+                                      bsa_dtype dtype, int tile, bsa_tiles tiles, float scale,
+                                      void* stream) {
   const char* fn = "bsa_forward_static";
   if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
   const Shape s{batch, heads, n, d};
-  TRY(check_shape(h, fn, s, dtype, 64));
+  TRY(check_shape(h, fn, s, dtype, tile, true));
   TRY(check_scale(h, fn, scale));
   TRY(check_ptr(h, fn, "q", q));
   TRY(check_ptr(h, fn, "k", k));
   TRY(check_ptr(h, fn, "v", v));
   TRY(check_ptr(h, fn, "out", out));
-  if (!tile_row_ptr) return fail(h, BSA_ERR_INVALID_ARG, "%s: tile_row_ptr is NULL", fn);
-  if (nnz < 0) return fail(h, BSA_ERR_INVALID_ARG, "%s: nnz must be >= 0", fn);
-  if (nnz > 0 && !tile_col) return fail(h, BSA_ERR_INVALID_ARG, "%s: tile_col is NULL", fn);
-  if (tile_rowmask && (reinterpret_cast<uintptr_t>(tile_rowmask) & 7u))
-    return fail(h, BSA_ERR_INVALID_ARG, "%s: tile_rowmask is not 8-byte aligned", fn);
+  if (!tiles) return fail(h, BSA_ERR_INVALID_ARG, "%s: tiles is NULL", fn);
+  if (tiles->n != n)
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: the tile list was made for n = %d, not %d", fn, tiles->n, n);
+  if (tiles->device != h->device)
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: the tile list lives on device %d, the handle on %d", fn,
+                tiles->device, h->device);
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
-    return bsa::launch_sparse_flash_static(q, k, v, out, tile_row_ptr, tile_col, tile_rowmask, nnz,
-                                           s.bh(), s.n, s.d, scale, dtype, st);
-  });
+  const int64_t S = h->static_item_tiles > 0 ? h->static_item_tiles : pick_item_tiles(*tiles, s.bh());
+  const bsa_tiles_s::Schedule* sc = nullptr;
+  TRY(tiles_schedule(h, tiles, S, &sc));
+  bsa::StaticLaunch a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.bh = s.bh();
+  a.n = n;
+  a.d = d;
+  a.dtype = dtype;
+  a.scale = scale;
+  a.col = tiles->col;
+  a.rowmask = tiles->rowmask;
+  a.items = sc->d_items;
+  a.nitems = int64_t(sc->items.size());
+  a.split = sc->d_split;
+  a.nsplit = int64_t(sc->split.size());
+  a.nslots = sc->nslots;
+  if (sc->nslots > 0) {
+    const size_t rows = size_t(s.bh()) * sc->nslots * 64;
+    TRY(grow_buf(h, h->s_part, rows * d * 4, "static partial rows"));
+    TRY(grow_buf(h, h->s_lse, rows * 4, "static partial log-sum-exp"));
+    a.part = static_cast<float*>(h->s_part.p);
+    a.part_lse = static_cast<float*>(h->s_lse.p);
+  }
+  TRY(timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd (static)",
+                   [&] { return bsa::launch_sparse_flash_static(a, st); }));
+  if (a.nsplit == 0) return BSA_OK;
+  return timed_launch(h, BSA_STAGE_STATIC_COMBINE, st, "static partial merge",
+                      [&] { return bsa::launch_static_combine(a, st); });
 }
 
 // ------------------------------------------------------------- timing ---

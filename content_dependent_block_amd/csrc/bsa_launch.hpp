@@ -64,11 +64,30 @@ hipError_t launch_sparse_flash_dynamic(const void* q, const void* k, const void*
                                        int topk, float scale, int causal, bsa_dtype dtype,
                                        hipStream_t stream, int nv = 0);
 
-// sparse_flash_fwd, static tile list.
-hipError_t launch_sparse_flash_static(const void* q, const void* k, const void* v, float* out,
-                                      const int32_t* row_ptr, const int32_t* col,
-                                      const uint64_t* rowmask, int64_t nnz, int64_t bh, int n,
-                                      int d, float scale, bsa_dtype dtype, hipStream_t stream);
+// sparse_flash_fwd, static tile list, run as host-scheduled work items (each
+// at most S key tiles of one query tile, heaviest first), then a merge of the
+// query tiles whose list was cut into several items.
+struct StaticLaunch {
+  const void* q = nullptr;
+  const void* k = nullptr;
+  const void* v = nullptr;
+  float* out = nullptr;
+  int64_t bh = 0;               // batch * heads (the list is the same for each)
+  int n = 0, d = 0;             // n: rows per head (need not be a multiple of 64)
+  bsa_dtype dtype = BSA_FP32;
+  float scale = 0.f;
+  const int32_t* col = nullptr;       // [nnz] key tile of each list entry
+  const uint64_t* rowmask = nullptr;  // [nnz][64] or NULL (every listed tile fully visible)
+  const int4* items = nullptr;  // [nitems] {query tile, first entry, entries, slot or -1}
+  int64_t nitems = 0;
+  const int4* split = nullptr;  // [nsplit] {query tile, first slot, slots}
+  int64_t nsplit = 0;
+  int nslots = 0;               // partial slots per (batch, head)
+  float* part = nullptr;        // [bh][nslots][64][d]  normalised partial rows
+  float* part_lse = nullptr;    // [bh][nslots][64]     their log2-domain log-sum-exp
+};
+hipError_t launch_sparse_flash_static(const StaticLaunch& a, hipStream_t stream);
+hipError_t launch_static_combine(const StaticLaunch& a, hipStream_t stream);  // no-op when nothing is split
 
 // sparse_flash_fwd, block-gather strategy: pairs grouped by key block,
 // split-softmax partials, merged per query.  Three launch groups per chunk of

@@ -38,30 +38,34 @@ struct KvRegs {
   uint4 vr[KvLayout<T, D>::VCH];
 };
 
-// Global loads of key tile `kt` (keys 64*kt .. 64*kt+63) of one head.
+// Global loads of key tile `kt` (keys 64*kt .. 64*kt+63) of one head.  A
+// tile with only `klim` < 64 keys in memory (the last tile of a sequence
+// whose length is not a multiple of 64) reads key klim - 1 in place of the
+// missing ones; the caller masks those keys.
 template <typename T, int D>
 __device__ __forceinline__ void kv_load(KvRegs<T, D>& r, const T* __restrict__ kb,
-                                        const T* __restrict__ vb, int kt, int tid) {
+                                        const T* __restrict__ vb, int kt, int tid, int klim = kTile) {
   using L = KvLayout<T, D>;
   const int64_t key0 = static_cast<int64_t>(kt) * kTile;
+  auto key = [&](int row) -> int64_t { return key0 + (row < klim ? row : klim - 1); };
   if constexpr (L::kBf16) {
 #pragma unroll
     for (int u = 0; u < L::KCH; ++u) {
       const int c = tid + 256 * u, c8 = c % (D / 8), row = c / (D / 8);
-      r.kr[u] = ld16(kb + (key0 + row) * D + c8 * 8);
+      r.kr[u] = ld16(kb + key(row) * D + c8 * 8);
     }
 #pragma unroll
     for (int u = 0; u < L::VCH / 2; ++u) {
       const int it = tid + 256 * u, c8 = it % (D / 8), p = it / (D / 8);
-      r.vr[2 * u] = ld16(vb + (key0 + 2 * p) * D + c8 * 8);
-      r.vr[2 * u + 1] = ld16(vb + (key0 + 2 * p + 1) * D + c8 * 8);
+      r.vr[2 * u] = ld16(vb + key(2 * p) * D + c8 * 8);
+      r.vr[2 * u + 1] = ld16(vb + key(2 * p + 1) * D + c8 * 8);
     }
   } else {
 #pragma unroll
     for (int u = 0; u < L::KCH; ++u) {
       const int c = tid + 256 * u, c4 = c % (D / 4), row = c / (D / 4);
-      r.kr[u] = ld16(kb + (key0 + row) * D + c4 * 4);
-      r.vr[u] = ld16(vb + (key0 + row) * D + c4 * 4);
+      r.kr[u] = ld16(kb + key(row) * D + c4 * 4);
+      r.vr[u] = ld16(vb + key(row) * D + c4 * 4);
     }
   }
 }

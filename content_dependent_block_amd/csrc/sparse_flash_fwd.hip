@@ -18,6 +18,12 @@
 //     64-bit key masks, built on the host (the README's plan of precomputing
 //     the active (row tile, column tile) list; infra.bea.ai "Block-Sparse &
 //     Linear Attention Kernels", the loop over K/V blocks where the mask is set).
+//     The list is cut on the host into work items of at most S key tiles of
+//     one query tile, heaviest first (infra.bea.ai, section 4, the challenges
+//     table: load imbalance answered by dynamic block scheduling).  A query
+//     tile whose list fits one item is written directly; the items of a
+//     longer list each write a split-softmax partial (the normalised rows and
+//     their log-sum-exp), and static_combine merges them.
 //
 // Work layout (gfx950): a 256-thread workgroup owns 64 queries, 16 per wave.
 // Each key tile (64 keys) is staged once into LDS for all four waves: K in its
@@ -147,12 +153,11 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const T* ks, const T*
   st.l = st.l * alpha + lsum;
 }
 
-template <typename T, int D, bool STATIC, bool CAUSAL>
+template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void sparse_flash_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     float* __restrict__ out, float* __restrict__ lse, const int32_t* __restrict__ idx, int topk,
-    const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
-    const uint64_t* __restrict__ rowmask, int64_t nnz, int n, int klim_last, float scale_log2) {
+    int n, int klim_last, float scale_log2) {
   using L = KvLayout<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   T* ks = reinterpret_cast<T*>(smem);
@@ -170,13 +175,11 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
   const T* kb = k + bh * static_cast<int64_t>(n) * D;
   const T* vb = v + bh * static_cast<int64_t>(n) * D;
 
-  // ---- the tile list
-  int nlist = 0;
-  int64_t list_base = 0;
-  int32_t* list = nullptr;
-  if constexpr (!STATIC) {
+  // ---- the tile list: the union of the rows' selected blocks
+  int32_t* list = reinterpret_cast<int32_t*>(rm + nb);
+  int nlist;
+  {
     const int nbc = CAUSAL ? qt + 1 : nb;  // blocks that can be visible to this tile
-    list = reinterpret_cast<int32_t*>(rm + nb);
     int* count = reinterpret_cast<int*>(list + nb);
     for (int c = tid; c < nbc; c += 256) rm[c] = 0ull;
     __syncthreads();
@@ -199,17 +202,9 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
     }
     __syncthreads();
     nlist = *count;
-  } else {
-    int64_t s0 = row_ptr[qt], s1 = row_ptr[qt + 1];
-    if (s0 < 0) s0 = 0;
-    if (s1 > nnz) s1 = nnz;
-    list_base = s0;
-    nlist = s1 > s0 ? static_cast<int>(s1 - s0) : 0;
   }
   auto tile_at = [&](int it) -> int {
-    int kt;
-    if constexpr (STATIC) kt = col[list_base + it];
-    else kt = list[it];
+    const int kt = list[it];
     return (kt >= 0 && kt < nqt) ? kt : -1;
   };
 
@@ -254,7 +249,7 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
     if (cur >= 0) {
       uint32_t vis;
       bool any;
-      if constexpr (!STATIC) {
+      {
         const uint64_t bits = rm[cur];
         any = ((bits >> (16 * wave)) & 0xFFFFull) != 0ull;
         vis = ((bits >> qlocal) & 1ull) ? 0xFFFFu : 0u;
@@ -278,16 +273,6 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
               if (16 * t + 4 * g + jj < klim_last) km |= 1u << (4 * t + jj);
           vis &= km;
         }
-      } else {
-        uint64_t m64 = ~0ull;
-        if (rowmask) m64 = rowmask[(list_base + it) * kTile + qlocal];
-        any = ballot(m64 != 0ull) != 0ull;
-        vis = 0u;
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj)
-            vis |= static_cast<uint32_t>((m64 >> (16 * t + 4 * g + jj)) & 1ull) << (4 * t + jj);
       }
       if (any) tile_step<T, D>(st, ks, vs, &qreg, vis, scale_log2, lane);
     }
@@ -308,16 +293,171 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
   }
 }
 
-template <typename T, int D, bool STATIC, bool CAUSAL>
-hipError_t launch_one(const void* q, const void* k, const void* v, float* out, float* lse,
-                      const int32_t* idx, int topk, int klim_last, const int32_t* row_ptr, const int32_t* col,
-                      const uint64_t* rowmask, int64_t nnz, int64_t bh, int n, float scale,
-                      hipStream_t s) {
+// The query operand of S^T = K Q^T for one lane: its row, the d slots of
+// MFMA k-group lane / 16.
+template <typename T, int D>
+union QReg {
+  bf16x8 b[D / 32];
+  float f[D / 4];
+};
+
+template <typename T, int D>
+__device__ __forceinline__ void load_qreg(QReg<T, D>& qr, const T* __restrict__ q, int64_t qrow, int g) {
+  if constexpr (sizeof(T) == 2) {
+    const T* qp = q + qrow * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) qr.b[kk] = as_bf16x8(ld16(qp + 32 * kk));
+  } else {
+    const T* qp = q + qrow * D + (D / 4) * g;
+#pragma unroll
+    for (int e = 0; e < D / 4; e += 4) {
+      const uint4 u = ld16(qp + e);
+      qr.f[e] = __uint_as_float(u.x);
+      qr.f[e + 1] = __uint_as_float(u.y);
+      qr.f[e + 2] = __uint_as_float(u.z);
+      qr.f[e + 3] = __uint_as_float(u.w);
+    }
+  }
+}
+
+// Static tile list, one work item per workgroup: item = {query tile, first
+// list entry, number of entries, partial slot (-1: the query tile's whole
+// list, written to out directly)}.  Workgroup w runs item w / bh of head
+// w % bh, so the heaviest items of every head start first.  Rows and keys at
+// or past nv (a sequence whose length is not a multiple of 64) do not exist:
+// their loads are clamped into the sequence, their keys masked, their rows
+// not stored.  Partials: part[(bh * nslots + slot) * 64 + row] is the row's
+// normalised output (D floats), part_lse the matching log2-domain
+// log-sum-exp (-inf for a row that saw no key in the item).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void static_item_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v, float* __restrict__ out,
+    const int4* __restrict__ items, int64_t bh_count, const int32_t* __restrict__ col,
+    const uint64_t* __restrict__ rowmask, float* __restrict__ part, float* __restrict__ part_lse, int nslots,
+    int nv, float scale_log2) {
+  using L = KvLayout<T, D>;
+  __shared__ __align__(16) unsigned char smem[L::BYTES];
+  T* ks = reinterpret_cast<T*>(smem);
+  T* vs = reinterpret_cast<T*>(smem + L::K_BYTES);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int nt = (nv + kTile - 1) / kTile;
+  const int klast = nv - (nt - 1) * kTile;  // keys of the last tile
+  const int4 it = items[blockIdx.x / bh_count];
+  const int64_t bh = blockIdx.x % bh_count;
+  const int qt = it.x, p0 = it.y, cnt = it.z, slot = it.w;
+  const int64_t head = bh * static_cast<int64_t>(nv);
+  const T* kb = k + head * D;
+  const T* vb = v + head * D;
+  const int qlocal = wave * 16 + c16;
+  const int qi = qt * kTile + qlocal;  // row inside the sequence
+  const bool row_ok = qi < nv;
+
+  QReg<T, D> qreg;
+  load_qreg<T, D>(qreg, q, head + (row_ok ? qi : nv - 1), g);
+  RowState<D> st;
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) st.acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m = -INFINITY;
+  st.l = 0.f;
+
+  auto tile_at = [&](int e) -> int { return col[p0 + e]; };
+  KvRegs<T, D> regs;
+  int cur = cnt > 0 ? tile_at(0) : -1;
+  if (cur >= 0) kv_load<T, D>(regs, kb, vb, cur, tid, cur == nt - 1 ? klast : kTile);
+  for (int e = 0; e < cnt; ++e) {
+    __syncthreads();
+    kv_store<T, D>(regs, ks, vs, tid);
+    __syncthreads();
+    const int nxt = e + 1 < cnt ? tile_at(e + 1) : -1;
+    if (nxt >= 0) kv_load<T, D>(regs, kb, vb, nxt, tid, nxt == nt - 1 ? klast : kTile);
+    uint64_t m64 = rowmask ? rowmask[static_cast<int64_t>(p0 + e) * kTile + qlocal] : ~0ull;
+    if (cur == nt - 1 && klast < kTile) m64 &= (1ull << klast) - 1ull;  // keys past the sequence
+    if (!row_ok) m64 = 0ull;
+    const bool any = ballot(m64 != 0ull) != 0ull;
+    uint32_t vis = 0u;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj)
+        vis |= static_cast<uint32_t>((m64 >> (16 * t + 4 * g + jj)) & 1ull) << (4 * t + jj);
+    if (any) tile_step<T, D>(st, ks, vs, &qreg, vis, scale_log2, lane);
+    cur = nxt;
+  }
+
+  float lt = st.l + __shfl_xor(st.l, 16);
+  lt += __shfl_xor(lt, 32);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (!row_ok) return;
+  float* op;
+  if (slot < 0) {
+    op = out + (head + qi) * D + 4 * g;
+  } else {
+    const int64_t prow = (bh * nslots + slot) * kTile + qlocal;
+    op = part + prow * D + 4 * g;
+    if (g == 0) part_lse[prow] = lt > 0.f ? st.m + __log2f(lt) : -INFINITY;
+  }
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) {
+    const f32x4 a = st.acc[dt] * inv;
+    *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(a[0], a[1], a[2], a[3]);
+  }
+}
+
+// Merge the partials of the query tiles whose list was split: split entry s
+// = {query tile, first slot, number of slots}.  Four lanes per row, D/4 dims
+// each; weights 2^(L_s - max L) in slot order.
+template <int D>
+__global__ __launch_bounds__(256) void static_combine_kernel(const int4* __restrict__ split, int64_t bh_count,
+                                                             const float* __restrict__ part,
+                                                             const float* __restrict__ part_lse, int nslots,
+                                                             float* __restrict__ out, int nv) {
+  constexpr int E = D / 4;
+  const int4 sp = split[blockIdx.x / bh_count];
+  const int64_t bh = blockIdx.x % bh_count;
+  const int r = threadIdx.x >> 2, c = threadIdx.x & 3;
+  const int qi = sp.x * kTile + r;
+  if (qi >= nv) return;
+  float mx = -INFINITY;
+  for (int s = 0; s < sp.z; ++s) mx = fmaxf(mx, part_lse[(bh * nslots + sp.y + s) * kTile + r]);
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float wsum = 0.f;
+  if (mx > -INFINITY) {
+    for (int s = 0; s < sp.z; ++s) {
+      const int64_t prow = (bh * nslots + sp.y + s) * kTile + r;
+      const float ls = part_lse[prow];
+      if (ls == -INFINITY) continue;
+      const float w = __builtin_amdgcn_exp2f(ls - mx);
+      wsum += w;
+      const float* src = part + prow * D + c * E;
+#pragma unroll
+      for (int e = 0; e < E; e += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(src + e);
+        acc[e] += w * x.x;
+        acc[e + 1] += w * x.y;
+        acc[e + 2] += w * x.z;
+        acc[e + 3] += w * x.w;
+      }
+    }
+  }
+  const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
+  float* dst = out + (bh * static_cast<int64_t>(nv) + qi) * D + c * E;
+#pragma unroll
+  for (int e = 0; e < E; e += 4)
+    *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv,
+                                                      acc[e + 3] * inv);
+}
+
+template <typename T, int D, bool CAUSAL>
+hipError_t launch_union(const void* q, const void* k, const void* v, float* out, float* lse,
+                        const int32_t* idx, int topk, int klim_last, int64_t bh, int n, float scale,
+                        hipStream_t s) {
   using L = KvLayout<T, D>;
   const int nb = n / kTile;
-  size_t smem = L::BYTES;
-  if (!STATIC) smem += static_cast<size_t>(nb) * 8 + static_cast<size_t>(nb) * 4 + 16;
-  const auto kern = sparse_flash_kernel<T, D, STATIC, CAUSAL>;
+  const size_t smem = L::BYTES + static_cast<size_t>(nb) * 8 + static_cast<size_t>(nb) * 4 + 16;
+  const auto kern = sparse_flash_kernel<T, D, CAUSAL>;
   if (smem > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -326,8 +466,8 @@ hipError_t launch_one(const void* q, const void* k, const void* v, float* out, f
   }
   const dim3 grid(static_cast<unsigned>(bh * (n / kTile)));
   hipLaunchKernelGGL(kern, grid, dim3(256), smem, s, static_cast<const T*>(q),
-                     static_cast<const T*>(k), static_cast<const T*>(v), out, lse, idx, topk, row_ptr,
-                     col, rowmask, nnz, n, klim_last, scale * kLog2e);
+                     static_cast<const T*>(k), static_cast<const T*>(v), out, lse, idx, topk, n, klim_last,
+                     scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -335,10 +475,18 @@ template <typename T, int D>
 hipError_t dispatch_dynamic(const void* q, const void* k, const void* v, float* out, float* lse,
                             const int32_t* idx, int64_t bh, int n, int topk, float scale,
                             int causal, hipStream_t s, int klim_last) {
-  return causal ? launch_one<T, D, false, true>(q, k, v, out, lse, idx, topk, klim_last, nullptr,
-                                                nullptr, nullptr, 0, bh, n, scale, s)
-                : launch_one<T, D, false, false>(q, k, v, out, lse, idx, topk, klim_last, nullptr,
-                                                 nullptr, nullptr, 0, bh, n, scale, s);
+  return causal ? launch_union<T, D, true>(q, k, v, out, lse, idx, topk, klim_last, bh, n, scale, s)
+                : launch_union<T, D, false>(q, k, v, out, lse, idx, topk, klim_last, bh, n, scale, s);
+}
+
+template <typename T, int D>
+hipError_t launch_static_t(const StaticLaunch& a, hipStream_t s) {
+  if (a.nitems > 0)
+    hipLaunchKernelGGL((static_item_kernel<T, D>), dim3(static_cast<unsigned>(a.nitems * a.bh)), dim3(256), 0,
+                       s, static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
+                       a.out, a.items, a.bh, a.col, a.rowmask, a.part, a.part_lse, a.nslots, a.n,
+                       a.scale * kLog2e);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -355,19 +503,22 @@ hipError_t launch_sparse_flash_dynamic(const void* q, const void* k, const void*
                  : dispatch_dynamic<float, 128>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl);
 }
 
-hipError_t launch_sparse_flash_static(const void* q, const void* k, const void* v, float* out,
-                                      const int32_t* row_ptr, const int32_t* col,
-                                      const uint64_t* rowmask, int64_t nnz, int64_t bh, int n,
-                                      int d, float scale, bsa_dtype dtype, hipStream_t stream) {
-  if (dtype == BSA_BF16)
-    return d == 64 ? launch_one<bf16_bits, 64, true, false>(q, k, v, out, nullptr, nullptr, 0, kTile, row_ptr, col,
-                                                            rowmask, nnz, bh, n, scale, stream)
-                   : launch_one<bf16_bits, 128, true, false>(q, k, v, out, nullptr, nullptr, 0, kTile, row_ptr, col,
-                                                             rowmask, nnz, bh, n, scale, stream);
-  return d == 64 ? launch_one<float, 64, true, false>(q, k, v, out, nullptr, nullptr, 0, kTile, row_ptr, col,
-                                                      rowmask, nnz, bh, n, scale, stream)
-                 : launch_one<float, 128, true, false>(q, k, v, out, nullptr, nullptr, 0, kTile, row_ptr, col,
-                                                       rowmask, nnz, bh, n, scale, stream);
+hipError_t launch_sparse_flash_static(const StaticLaunch& a, hipStream_t stream) {
+  if (a.dtype == BSA_BF16)
+    return a.d == 64 ? launch_static_t<bf16_bits, 64>(a, stream) : launch_static_t<bf16_bits, 128>(a, stream);
+  return a.d == 64 ? launch_static_t<float, 64>(a, stream) : launch_static_t<float, 128>(a, stream);
+}
+
+hipError_t launch_static_combine(const StaticLaunch& a, hipStream_t stream) {
+  if (a.nsplit <= 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(a.nsplit * a.bh));
+  if (a.d == 64)
+    hipLaunchKernelGGL((static_combine_kernel<64>), grid, dim3(256), 0, stream, a.split, a.bh, a.part, a.part_lse,
+                       a.nslots, a.out, a.n);
+  else
+    hipLaunchKernelGGL((static_combine_kernel<128>), grid, dim3(256), 0, stream, a.split, a.bh, a.part,
+                       a.part_lse, a.nslots, a.out, a.n);
+  return hipGetLastError();
 }
 
 }  // namespace bsa

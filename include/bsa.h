@@ -33,12 +33,13 @@
  *    handle's workspace.
  *  - Supported today: block (= tile) 64; d in {64, 128}; ceil(n/64) <= 2048
  *    for the dynamic path.  n need not be a multiple of 64 in bsa_forward,
- *    bsa_forward_budgets, bsa_forward_train, bsa_backward and
- *    bsa_fine_forward: the last block then holds the n mod 64 remaining keys
- *    and its representative is their mean (the calls run on copies padded to
- *    whole blocks, workspace held by the handle, with the padding keys
- *    masked).  The stage exports and bsa_forward_static need n a multiple of
- *    64.  Anything else returns BSA_ERR_UNSUPPORTED.
+ *    bsa_forward_budgets, bsa_forward_train, bsa_backward, bsa_fine_forward
+ *    and bsa_forward_static: the last block then holds the n mod 64
+ *    remaining keys and its representative is their mean (the dynamic calls
+ *    run on copies padded to whole blocks, workspace held by the handle,
+ *    with the padding keys masked; the static mode reads the sequence in
+ *    place).  The stage exports need n a multiple of 64.  Anything else
+ *    returns BSA_ERR_UNSUPPORTED.
  */
 #ifndef BSA_H
 #define BSA_H
@@ -51,6 +52,11 @@ extern "C" {
 #endif
 
 typedef struct bsa_handle_s* bsa_handle;
+
+/* A static tile list validated on the host and copied to device memory
+ * (bsa_tiles_create).  It belongs to the device of the handle it was made
+ * with and stays valid until bsa_tiles_destroy. */
+typedef struct bsa_tiles_s* bsa_tiles;
 
 typedef enum {
   BSA_OK = 0,
@@ -77,7 +83,8 @@ typedef enum {
   BSA_STAGE_BWD_PAIRS = 9,      /* backward: the MFMA pair kernel (dq, dk, dv parts) */
   BSA_STAGE_BWD_REDUCE = 10,    /* backward: sums of the dq and dk/dv contributions  */
   BSA_STAGE_RAGGED_COPY = 11,   /* n not a multiple of 64: copies to / from padding  */
-  BSA_NUM_STAGES = 12
+  BSA_STAGE_STATIC_COMBINE = 12, /* static mode: merge of the items of a cut list     */
+  BSA_NUM_STAGES = 13
 } bsa_stage;
 
 /* How the dynamic fine stage visits the selected blocks. */
@@ -116,10 +123,24 @@ typedef enum {
    * processed in chunks that fit.  Default 1 GiB.  Minimum one 64-query tile. */
   BSA_OPT_FINE_CHUNK_BYTES = 2,
   /* bsa_select_strategy for stage 1 of bsa_forward.  Default BSA_SELECT_FUSED. */
-  BSA_OPT_SELECT_STRATEGY = 3
+  BSA_OPT_SELECT_STRATEGY = 3,
+  /* bsa_forward_static: the most key tiles one work item (one workgroup)
+   * takes from a query tile's list; a longer list is cut into several items
+   * whose partial results are merged.  0 (default): chosen per call so that
+   * there are about four items per compute unit and none is longer than
+   * about twice the mean list; a value >= every list length gives one item
+   * per query tile. */
+  BSA_OPT_STATIC_ITEM_TILES = 4
 } bsa_option;
 
 /* ----------------------------------------------------------- lifetime -- */
+
+/* The lifetime, option, workspace and timing calls are this library's own
+ * plumbing: no page defines them.  The pages' interface is the two-stage
+ * call with block size B and top-k (nishantmodi.me "sparse-attention-triton-
+ * bench", section "Two-stage block indexer") and the README's call on Q, K, V
+ * and a mask (yayme/CUDA-kernel README, the usage example); bsa_forward and
+ * bsa_forward_static below are those. */
 
 /* Create a handle bound to HIP device `device`.  *out receives the handle.
  * BSA_ERR_NO_DEVICE if there is no HIP device, `device` is out of range, or
@@ -241,10 +262,17 @@ bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, const void* 
                         bsa_dtype dtype, int block, int topk, float scale,
                         int causal, void* stream);
 
-/* Stage 2 alone on caller-supplied selections (same layout as block_idx_out;
- * each row must hold distinct indices; entries outside [0, n/block), and in
- * causal mode blocks after the query's own block, count as padding).  Useful
- * to test or reuse a selection. */
+/* Stage 2 alone on caller-supplied selections (nishantmodi.me
+ * "sparse-attention-triton-bench", sections "Stage 2: fine attention" and "The
+ * Triton kernel": each query attends only to the keys of the blocks it
+ * selected, with an online softmax; the block ids are int32, section "Two
+ * things I wish I knew").
+ *  block_idx      device, int32 [batch][heads][n][topk] (the layout of
+ *                 block_idx_out above); each row must hold distinct indices;
+ *                 entries outside [0, ceil(n/block)), and in causal mode
+ *                 blocks after the query's own block, count as padding.
+ * Everything else as for bsa_forward; the output is the same as
+ * bsa_forward's for that selection.  Useful to test or reuse a selection. */
 bsa_status bsa_fine_forward(bsa_handle h, const void* q, const void* k,
                             const void* v, float* out, const int32_t* block_idx,
                             int batch, int heads, int n, int d, bsa_dtype dtype,
@@ -253,70 +281,125 @@ bsa_status bsa_fine_forward(bsa_handle h, const void* q, const void* k,
 
 /* ---------------------------------------------------- stage 1 pieces -- */
 
-/* block_pool: repr_out[b][h][beta][:] = mean of keys beta*B .. beta*B+B-1, as
- * float32 [batch][heads][n/B][d]. */
+/* block_pool alone (nishantmodi.me "sparse-attention-triton-bench", section
+ * "Stage 1: coarse scoring": the keys are split into blocks of B and each
+ * block is mean-pooled into one representative vector).
+ *  k              device, [batch][heads][n][d], dtype.
+ *  repr_out       device, float32 [batch][heads][n/B][d], 16-byte aligned:
+ *                 repr_out[b][h][beta][:] = mean of keys beta*B .. beta*B+B-1,
+ *                 summed in float32.
+ *  n              a multiple of 64 (BSA_ERR_UNSUPPORTED otherwise); other
+ *                 arguments as for bsa_forward. */
 bsa_status bsa_block_pool(bsa_handle h, const void* k, float* repr_out,
                           int batch, int heads, int n, int d, bsa_dtype dtype,
                           int block, void* stream);
 
-/* coarse_score: the float32 score panel, stored block-major: with
- * rows = batch*heads*n and row = (b*heads + h)*n + i,
- * panel_out[beta * rows + row] = q_i . repr[b][h][beta]  (beta < n/B).
- * repr is float32 as produced by bsa_block_pool.  In causal mode entries with
- * beta > i/B are unspecified. */
+/* coarse_score alone (nishantmodi.me "sparse-attention-triton-bench", section
+ * "Stage 1: coarse scoring": every query is scored against every block
+ * representative, Q times the transposed representatives, O(N * N/B)).
+ *  q              device, [batch][heads][n][d], dtype.
+ *  repr           device, float32 [batch][heads][n/B][d] as bsa_block_pool
+ *                 writes it.
+ *  panel_out      device, float32, block-major: with rows = batch*heads*n and
+ *                 row = (b*heads + h)*n + i,
+ *                 panel_out[beta * rows + row] = q_i . repr[b][h][beta]
+ *                 (beta < n/B), unscaled.  In causal mode entries with
+ *                 beta > i/B are unspecified.
+ * n a multiple of 64; errors as for bsa_forward.  The caller owns the panel
+ * (batch*heads*n*(n/64)*4 bytes). */
 bsa_status bsa_coarse_score(bsa_handle h, const void* q, const float* repr,
                             float* panel_out, int batch, int heads, int n, int d,
                             bsa_dtype dtype, int block, int causal, void* stream);
 
-/* topk_select: per row of the block-major float32 panel laid out as
- * bsa_coarse_score writes it, the selection exactly as described for
- * bsa_forward, into block_idx_out int32 [batch][heads][n][topk]. */
+/* topk_select alone (nishantmodi.me "sparse-attention-triton-bench", section
+ * "Stage 2: fine attention": each query keeps its top-k highest-scoring
+ * blocks; the ids are int32, section "Two things I wish I knew").
+ *  panel          device, float32, block-major as bsa_coarse_score writes it.
+ *  block_idx_out  device, int32 [batch][heads][n][topk]: per row the selection
+ *                 exactly as described for bsa_forward (ties to the lower
+ *                 block, -0 equal to +0, ascending, -1 padded; causal: the own
+ *                 block kept, later blocks not candidates).
+ * n a multiple of 64; errors as for bsa_forward. */
 bsa_status bsa_topk_select(bsa_handle h, const float* panel,
                            int32_t* block_idx_out, int batch, int heads, int n,
                            int block, int topk, int causal, void* stream);
 
 /* ------------------------------------------------------ static forward -- */
 
-/* Fine attention over a precomputed tile list, the same for every batch and
- * head.  Query tile t (rows 64t .. 64t+63) visits key tiles
- * tile_col[tile_row_ptr[t] .. tile_row_ptr[t+1]) in that order.
- *  tile_row_ptr  device int32 [n/64 + 1], non-decreasing, tile_row_ptr[0] = 0.
- *  tile_col      device int32 [nnz], key-tile ids in [0, n/64).
- *  tile_rowmask  device uint64 [nnz][64] or NULL: bit c of entry (p, r) says
- *                whether query row r of the tile sees key c of tile p.  NULL
- *                means every listed tile is fully visible.
- *  nnz           number of listed tiles (= tile_row_ptr[n/64]).
- * Device-side list content is not read on the host; the kernel skips entries
- * outside the stated ranges instead of reading out of bounds.  Use
- * bsa_tiles_validate on the host copy to check a list.  A row that sees no
- * key gets zeros. */
+/* The static mode runs the fine attention of bsa_fine_forward over a fixed
+ * list of active (64-query tile, 64-key tile) pairs instead of a selection
+ * (yayme/CUDA-kernel README: precompute the active tile list on the CPU and
+ * skip inactive tiles instead of scanning the mask in the kernel; infra.bea.ai
+ * "Block-Sparse & Linear Attention Kernels", section 4: a compressed list of
+ * active blocks per row as the mask representation).  Format: CSR over query
+ * tiles.  With nt = ceil(n/64):
+ *  row_ptr   int32 [nt + 1]: row_ptr[0] = 0, non-decreasing, row_ptr[nt] = nnz;
+ *            query tile t (rows 64t .. min(64t+63, n-1)) visits key tiles
+ *            col[row_ptr[t] .. row_ptr[t+1]).
+ *  col       int32 [nnz]: key-tile ids in [0, nt), strictly increasing inside
+ *            each query tile's range.
+ *  rowmask   uint64 [nnz][64] or NULL: bit c of entry (p, r) says whether
+ *            query row r of the tile sees key c of tile col[p]; bits of keys
+ *            at or past n must be clear.  NULL means every listed tile is
+ *            fully visible (keys past n excepted).
+ * A key that is not visible takes no part in the softmax (score -inf, the
+ * README's note on its v1 bug); a row that sees no key gets zeros. */
+
+/* Validate a tile list held in HOST memory and copy it to the device of h.
+ *  n, tile   sequence length (>= 1, need not be a multiple of 64) and tile
+ *            size (must be 64: BSA_ERR_UNSUPPORTED otherwise).
+ *  row_ptr, col, rowmask, nnz   as above, host memory, read during the call
+ *            only.
+ *  out       receives the list; free it with bsa_tiles_destroy.
+ * Every rule above is checked: a malformed list returns BSA_ERR_INVALID_ARG
+ * (bsa_last_error(h) names the first broken rule) and creates nothing.
+ * BSA_ERR_OUT_OF_MEMORY if the device copy cannot be allocated.  Blocks
+ * until the copy is done. */
+bsa_status bsa_tiles_create(bsa_handle h, int n, int tile, const int32_t* row_ptr,
+                            const int32_t* col, const uint64_t* rowmask, int64_t nnz,
+                            bsa_tiles* out);
+
+/* Free a tile list.  No work that uses it may still be running.  NULL is
+ * accepted. */
+bsa_status bsa_tiles_destroy(bsa_tiles t);
+
+/* Fine attention over a tile list, the same list for every batch and head.
+ *  q, k, v, out, batch, heads, n, d, dtype, scale   as for bsa_forward; n
+ *            must equal the n the list was made for (BSA_ERR_INVALID_ARG).
+ *  tile      must be 64 (BSA_ERR_UNSUPPORTED otherwise).
+ *  tiles     from bsa_tiles_create with the same handle's device.
+ * Work: query tiles whose list is longer than the item size (see
+ * BSA_OPT_STATIC_ITEM_TILES) are cut into several work items, heaviest first
+ * (infra.bea.ai, section 4, the challenges table: load imbalance answered by
+ * dynamic block scheduling); their partials go to handle workspace and are
+ * merged.  The first call with a new item size builds that schedule on the
+ * host and copies it to the device (synchronously, once). */
 bsa_status bsa_forward_static(bsa_handle h, const void* q, const void* k,
                               const void* v, float* out, int batch, int heads,
-                              int n, int d, bsa_dtype dtype,
-                              const int32_t* tile_row_ptr,
-                              const int32_t* tile_col,
-                              const uint64_t* tile_rowmask, int64_t nnz,
-                              float scale, void* stream);
+                              int n, int d, bsa_dtype dtype, int tile,
+                              bsa_tiles tiles, float scale, void* stream);
 
-/* Host helper: tile list of a dense element mask.  mask is host uint8 [n][n]
- * (nonzero = visible).  row_ptr: host int32 [n/tile + 1].  col: host int32
- * [*nnz_inout] or NULL; rowmask: host uint64 [*nnz_inout][tile] or NULL.
- * With col == NULL only counts: *nnz_inout receives the number of active tiles.
- * Otherwise *nnz_inout must be >= that number on entry and receives it on
- * return.  tile must be 64; n a multiple of 64. */
+/* Host helper: tile list of a dense element mask (same source as above).
+ * mask is host uint8 [n][n] (nonzero = visible).  row_ptr: host int32
+ * [ceil(n/64) + 1].  col: host int32 [*nnz_inout] or NULL; rowmask: host
+ * uint64 [*nnz_inout][64] or NULL.  With col == NULL only counts: *nnz_inout
+ * receives the number of active tiles.  Otherwise *nnz_inout must be >= that
+ * number on entry (BSA_ERR_INVALID_ARG) and receives it on return.  tile must
+ * be 64; any n >= 1. */
 bsa_status bsa_tiles_from_mask(const uint8_t* mask, int n, int tile,
                                int32_t* row_ptr, int32_t* col,
                                uint64_t* rowmask, int64_t* nnz_inout);
 
-/* Host helper: the same for the window+stride pattern (query i sees key j iff
- * |i-j| <= window or j mod stride == 0) without materialising the mask. */
+/* Host helper: the same for the window+stride pattern (yayme/CUDA-kernel
+ * README, the sparsity pattern: query i sees key j iff |i-j| <= window or
+ * j mod stride == 0) without materialising the mask. */
 bsa_status bsa_tiles_window_stride(int n, int window, int stride, int tile,
                                    int32_t* row_ptr, int32_t* col,
                                    uint64_t* rowmask, int64_t* nnz_inout);
 
-/* Host helper: BSA_OK iff (row_ptr, col) is a well-formed list for n and tile:
- * row_ptr[0] == 0, non-decreasing, row_ptr[n/tile] == nnz, every col in
- * [0, n/tile). */
+/* Host helper: BSA_OK iff (row_ptr, col) satisfies the rules above for n and
+ * tile (the row masks are not looked at); else the status bsa_tiles_create
+ * would return. */
 bsa_status bsa_tiles_validate(const int32_t* row_ptr, const int32_t* col,
                               int64_t nnz, int n, int tile);
 

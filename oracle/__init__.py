@@ -62,6 +62,20 @@ def _load():
     return lib
 
 
+def set_threads(count: int) -> int:
+    """Use `count` OpenMP threads in later calls (the OpenMP runtime the
+    library links); returns the count in effect before."""
+    lib = _load()
+    before = int(lib.omp_get_max_threads())
+    lib.omp_set_num_threads(int(count))
+    return before
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().omp_get_max_threads())
+
+
 def _f32(a):
     a = np.ascontiguousarray(a, dtype=np.float32)
     return a, a.ctypes.data

@@ -62,11 +62,13 @@ def test_null_handle_is_rejected(m):
 
 def _brute_tiles(mask, t=64):
     n = mask.shape[0]
-    nt = n // t
+    nt = -(-n // t)
     row_ptr, col, rm = [0], [], []
     for qt in range(nt):
         for kt in range(nt):
-            blk = mask[qt * t:(qt + 1) * t, kt * t:(kt + 1) * t]
+            blk = np.zeros((t, t), np.uint8)
+            part = mask[qt * t:(qt + 1) * t, kt * t:(kt + 1) * t]
+            blk[:part.shape[0], :part.shape[1]] = part
             if blk.any():
                 col.append(kt)
                 rm.append([int(sum(int(b) << c for c, b in enumerate(row))) for row in blk])
@@ -75,10 +77,11 @@ def _brute_tiles(mask, t=64):
             np.array(rm, np.uint64).reshape(-1, t))
 
 
-@pytest.mark.parametrize("density,seed", [(0.0, 0), (0.002, 1), (0.05, 2), (1.0, 3)])
-def test_tiles_from_mask_matches_brute_force(m, density, seed):
+@pytest.mark.parametrize("n,density,seed", [(256, 0.0, 0), (256, 0.002, 1), (256, 0.05, 2), (256, 1.0, 3),
+                                             (200, 0.05, 4), (65, 1.0, 5), (1, 1.0, 6)])
+def test_tiles_from_mask_matches_brute_force(m, n, density, seed):
+    """n not a multiple of 64 too: the last tile holds n mod 64 rows / keys."""
     rng = np.random.default_rng(seed)
-    n = 256
     mask = (rng.random((n, n)) < density).astype(np.uint8)
     rp, col, rm = m.bsa_tiles_from_mask(mask)
     brp, bcol, brm = _brute_tiles(mask)
@@ -89,7 +92,8 @@ def test_tiles_from_mask_matches_brute_force(m, density, seed):
 
 
 def test_window_stride_builder_matches_mask(m):
-    for n, w, s in [(8192, 32, 512), (1024, 8, 300), (512, 0, 64), (640, 100, 7)]:
+    for n, w, s in [(8192, 32, 512), (1024, 8, 300), (512, 0, 64), (640, 100, 7), (1000, 32, 512),
+                    (65, 3, 20), (8200, 32, 512)]:
         a = m.bsa_tiles_window_stride(n, w, s)
         b = m.bsa_tiles_from_mask(oracle.window_stride_mask(n, w, s))
         for x, y in zip(a, b):
@@ -105,6 +109,18 @@ def test_tiles_validate_rejects_bad_lists(m):
     assert not m.bsa_tiles_validate(rp, np.array([0, 1, 2, 4], np.int32), n)       # col out of range
     assert not m.bsa_tiles_validate(np.array([0, 1, 2, 3, 3], np.int32), col, n)   # last != nnz
     assert not m.bsa_tiles_validate(np.array([1, 1, 2, 3, 4], np.int32), col, n)   # first != 0
+    # strictly increasing inside a query tile: no repeat, no descent
+    assert m.bsa_tiles_validate(np.array([0, 2, 2, 2, 4], np.int32), np.array([0, 3, 1, 2], np.int32), n)
+    assert not m.bsa_tiles_validate(np.array([0, 2, 2, 2, 4], np.int32), np.array([3, 0, 1, 2], np.int32), n)
+    assert not m.bsa_tiles_validate(np.array([0, 2, 2, 2, 4], np.int32), np.array([1, 1, 1, 2], np.int32), n)
+    # n = 200: four query tiles, key tiles 0 .. 3
+    assert m.bsa_tiles_validate(rp, np.array([0, 1, 2, 3], np.int32), 200)
+    assert not m.bsa_tiles_validate(np.array([0, 1, 2, 3], np.int32), col[:3], 200)  # row_ptr too short for n
+    L = m._binding._lib
+    assert L.bsa_tiles_validate(rp.ctypes.data, col.ctypes.data, 4, n, 32) == m.BSA_ERR_UNSUPPORTED
+    assert L.bsa_tiles_validate(None, col.ctypes.data, 4, n, 64) == m.BSA_ERR_INVALID_ARG
+    assert L.bsa_tiles_create(None, n, 64, rp.ctypes.data, col.ctypes.data, None, 4,
+                              ctypes.byref(ctypes.c_void_p())) == m.BSA_ERR_INVALID_ARG
 
 
 def test_tiles_buffer_too_small_is_an_error(m):
@@ -121,4 +137,7 @@ def test_tiles_buffer_too_small_is_an_error(m):
                                  ctypes.byref(nnz)) == m.BSA_OK
     assert nnz.value == 4
     assert L.bsa_tiles_from_mask(mask.ctypes.data, 100, 64, rp.ctypes.data, None, None,
+                                 ctypes.byref(nnz)) == m.BSA_OK   # n = 100: 2 x 2 tiles
+    assert nnz.value == 4
+    assert L.bsa_tiles_from_mask(mask.ctypes.data, 128, 32, rp.ctypes.data, None, None,
                                  ctypes.byref(nnz)) == m.BSA_ERR_UNSUPPORTED

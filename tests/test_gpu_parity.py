@@ -10,6 +10,7 @@ Acceptance (per query row):
   * outputs within 1e-2 (bf16 inputs) / 1e-4 (fp32 inputs) max abs of the
     oracle's fine attention over the GPU's own selection.
 """
+import ctypes
 import math
 import sys
 
@@ -114,14 +115,14 @@ def run_forward(m, lib, w, inp, *, topk=None, causal=None, n=None):
     return out.cpu().numpy(), idx.cpu().numpy()
 
 
-def end_to_end(m, lib, w, inp, rows, *, topk=None, causal=None):
+def end_to_end(m, lib, w, inp, rows, *, topk=None, causal=None, return_all=False):
     topk = topk or w.topk
     causal = w.causal if causal is None else causal
     b, h, n, d = inp.q.shape
     say(f"[gpu] bsa_forward {w.name} b={b} h={h} n={n} d={d} k={topk} causal={causal} dtype={w.dtype}")
-    out, idx = run_forward(m, lib, w, inp, topk=topk, causal=causal)
+    out, idx_all = run_forward(m, lib, w, inp, topk=topk, causal=causal)
     out = out.reshape(-1, d)[rows]
-    gidx = idx.reshape(-1, topk)[rows]
+    gidx = idx_all.reshape(-1, topk)[rows]
     r = oracle.pool(inp.k, w.block)
     s = oracle.scores(inp.q, r, w.block, rows)
     oidx, kth, nxt = oracle.topk(s, n, w.block, topk, causal, rows)
@@ -131,6 +132,8 @@ def end_to_end(m, lib, w, inp, rows, *, topk=None, causal=None):
     say(f"    rows={rows.size} tie-band rows={int(band.sum())} "
         f"index mismatches={int((gidx != oidx).any(axis=1).sum())} max|err|={err:.3g}")
     assert err <= TOL[w.dtype]
+    if return_all:
+        return out, idx_all, band
     return out, gidx, band
 
 
@@ -249,11 +252,21 @@ def test_forward_small_workloads_all_rows(bsa, name, select, strategy):
     end_to_end(m, lib, w, inp, np.arange(w.bh * w.n, dtype=np.int64))
 
 
-@pytest.mark.parametrize("select,strategy", PATHS)
-def test_forward_headline_sampled(bsa, select, strategy):
+def test_forward_headline_all_rows(bsa):
     """N=32768, 8 heads, bf16, k=16 in the launch configuration the benchmark
-    times (fused selection, block_gather); sampled rows against the oracle,
-    plus properties of every row."""
+    times (fused selection, block_gather): every one of the 262,144 query rows
+    against the oracle, indices and outputs."""
+    m, lib = bsa
+    use_strategy(m, lib, "block_gather", "fused")
+    w = W.WORKLOADS["dyn_bf16_n32k"]
+    inp = W.generate(w)
+    end_to_end(m, lib, w, inp, np.arange(w.bh * w.n, dtype=np.int64))
+
+
+@pytest.mark.parametrize("select,strategy", [p for p in PATHS if p != ("fused", "block_gather")])
+def test_forward_headline_sampled(bsa, select, strategy):
+    """The same workload through the other stage-1 / fine strategies: sampled
+    rows against the oracle, plus properties of every row."""
     m, lib = bsa
     use_strategy(m, lib, strategy, select)
     w = W.WORKLOADS["dyn_bf16_n32k"]
@@ -265,43 +278,223 @@ def test_forward_headline_sampled(bsa, select, strategy):
     assert (np.diff(idx, axis=1) > 0).all() and idx.min() >= 0 and idx.max() < w.nb
 
 
-def test_forward_causal_long_sampled(bsa):
-    """N=131072, 8 heads, D=128, bf16, k=32, causal: all rows of the first 32
-    query blocks of two heads plus random rows; every row's properties."""
+def test_forward_causal_long_all_rows(bsa):
+    """N=131072, 8 heads, D=128, bf16, k=32, causal: the selection of every
+    one of the 1,048,576 query rows against the oracle (head by head, in
+    chunks of rows); outputs against the oracle on all rows of the first 32
+    query blocks of two heads plus random rows."""
     m, lib = bsa
     w = W.WORKLOADS["causal_bf16_n128k"]
     inp = W.generate(w)
     early = np.concatenate([h * w.n + np.arange(32 * 64) for h in (0, 5)])
     rows = sample_rows(w, 1500, seed=4, extra=early)
-    end_to_end(m, lib, w, inp, rows)
-    _, idx = run_forward(m, lib, w, inp)
-    idx = idx.reshape(w.bh, w.n, w.topk)
-    qb = np.arange(w.n) // 64
-    keff = np.minimum(w.topk, qb + 1)
+    out, gidx_all, _ = end_to_end(m, lib, w, inp, rows, return_all=True)
+    gidx_all = gidx_all.reshape(-1, w.topk)
+    r = oracle.pool(inp.k, w.block)
+    chunk = 16384
+    mismatched = banded = 0
     for h in range(w.bh):
-        valid = idx[h] >= 0
-        assert (valid.sum(axis=1) == keff).all()
-        assert ((idx[h] == qb[:, None]).any(axis=1)).all()   # own block kept
-        assert (np.where(valid, idx[h], 0) <= qb[:, None]).all()
+        for r0 in range(0, w.n, chunk):
+            rr = np.arange(h * w.n + r0, h * w.n + min(w.n, r0 + chunk), dtype=np.int64)
+            s = oracle.scores(inp.q, r, w.block, rr)
+            oidx, kth, nxt = oracle.topk(s, w.n, w.block, w.topk, True, rr)
+            band = check_selection(gidx_all[rr], oidx, kth, nxt, s, rr, w.n, w.block, True)
+            mismatched += int((gidx_all[rr] != oidx).any(axis=1).sum())
+            banded += int(band.sum())
+        say(f"    head {h}: all {w.n} rows checked (so far {mismatched} tie-band mismatches, "
+            f"{banded} tie-band rows)")
 
 
-def test_static_window_stride(bsa):
+def run_static(m, lib, inp, dtype, tiles, scale, item_tiles=0):
+    q, k, v = to_dev(inp, dtype)
+    out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    m.bsa_set_option(lib.handle, m.BSA_OPT_STATIC_ITEM_TILES, item_tiles)
+    try:
+        m.bsa_forward_static(lib.handle, q, k, v, out, tiles, scale=scale)
+        torch.cuda.synchronize()
+    finally:
+        m.bsa_set_option(lib.handle, m.BSA_OPT_STATIC_ITEM_TILES, 0)
+    return out.cpu().numpy().reshape(-1, q.shape[-1])
+
+
+@pytest.mark.parametrize("item_tiles", [0, 1 << 20, 1, 3])
+def test_static_window_stride(bsa, item_tiles):
+    """The 8192-row window+stride pattern, every row against the oracle's
+    masked attention; item sizes: chosen per call, one item per query tile,
+    single-tile items and 3-tile items (lists cut and merged)."""
     m, lib = bsa
     w = W.WORKLOADS["static_fp32_n8k"]
     inp = W.generate(w)
     rp, col, rm = m.bsa_tiles_window_stride(w.n, w.window, w.stride)
-    say(f"[gpu] bsa_forward_static {w.name} nnz={col.size}")
-    q, k, v = to_dev(inp, w.dtype)
-    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
-    m.bsa_forward_static(lib.handle, q, k, v, out, torch.from_numpy(rp).cuda(),
-                         torch.from_numpy(col).cuda(), torch.from_numpy(rm.view(np.int64)).cuda(),
-                         scale=w.scale)
-    torch.cuda.synchronize()
+    say(f"[gpu] bsa_forward_static {w.name} nnz={col.size} item_tiles={item_tiles}")
+    with m.bsa_tiles_create(lib.handle, w.n, rp, col, rm) as tl:
+        got = run_static(m, lib, inp, w.dtype, tl, w.scale, item_tiles)
     mask = oracle.window_stride_mask(w.n, w.window, w.stride)
     ref = oracle.attend_mask(inp.q, inp.k, inp.v, mask, w.scale)
-    err = np.abs(out.cpu().numpy().reshape(-1, w.d) - ref).max()
+    err = np.abs(got - ref).max()
     say(f"    max|err|={err:.3g}")
     assert err <= TOL["fp32"]
+
+
+@pytest.mark.parametrize("n,dtype,d", [(1000, "fp32", 64), (8200, "bf16", 128), (65, "fp32", 128),
+                                       (1, "bf16", 64)])
+def test_static_ragged_n(bsa, n, dtype, d):
+    """n not a multiple of 64: the last query tile has n mod 64 rows and the
+    last key tile n mod 64 keys; nothing past n is read as a key or written."""
+    m, lib = bsa
+    w = W.Workload("static_ragged", 1, 2, n, d, dtype, seed=41, window=32, stride=512)
+    inp = W.generate(w)
+    rp, col, rm = m.bsa_tiles_window_stride(n, w.window, w.stride)
+    say(f"[gpu] bsa_forward_static ragged n={n} dtype={dtype} d={d} nnz={col.size}")
+    mask = oracle.window_stride_mask(n, w.window, w.stride)
+    ref = oracle.attend_mask(inp.q, inp.k, inp.v, mask, w.scale)
+    with m.bsa_tiles_create(lib.handle, n, rp, col, rm) as tl:
+        for item_tiles in (0, 2):
+            got = run_static(m, lib, inp, dtype, tl, w.scale, item_tiles)
+            assert np.abs(got - ref).max() <= TOL[dtype]
+        # no row masks: whole tiles visible, but never the keys past n
+        full = np.zeros((n, n), np.uint8)
+        for t in range(rp.size - 1):
+            for kt in col[rp[t]:rp[t + 1]]:
+                full[t * 64:(t + 1) * 64, kt * 64:(kt + 1) * 64] = 1
+    with m.bsa_tiles_create(lib.handle, n, rp, col) as tl:
+        got = run_static(m, lib, inp, dtype, tl, w.scale, 1)
+    ref = oracle.attend_mask(inp.q, inp.k, inp.v, full, w.scale)
+    assert np.abs(got - ref).max() <= TOL[dtype]
+
+
+def skewed_mask(n, band_tiles, global_cols):
+    """A dense causal band of `band_tiles` key tiles behind each query tile,
+    plus dense global key columns (every query sees key tiles in
+    global_cols, causally): query-tile lists from 1 to band + len(globals)
+    tiles long, the longest at the end."""
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    band = (j <= i) & (j // 64 >= i // 64 - band_tiles + 1)
+    glob = np.isin(j // 64, global_cols) & (j <= i)
+    skew = (i // 64 >= (n // 64) * 3 // 4) & (j <= i)      # the last quarter of the tiles is dense causal
+    return (band | glob | skew).astype(np.uint8)
+
+
+def test_static_skewed_lists_balanced(bsa):
+    """Query-tile lists of very different lengths (1 .. 96 tiles): the cut,
+    heaviest-first items give the oracle's output, equal within rounding to
+    one workgroup per query tile, and the two are timed side by side."""
+    m, lib = bsa
+    n, d = 8192, 64
+    w = W.Workload("static_skew", 1, 2, n, d, "bf16", seed=43, window=0, stride=1)
+    inp = W.generate(w)
+    mask = skewed_mask(n, 2, np.arange(0, 128, 16))
+    rp, col, rm = m.bsa_tiles_from_mask(mask)
+    lens = np.diff(rp)
+    say(f"[gpu] skewed static list n={n} nnz={col.size} list lengths {lens.min()}..{lens.max()}")
+    ref = oracle.attend_mask(inp.q, inp.k, inp.v, mask, 0.125)
+    times = {}
+    outs = {}
+    with m.bsa_tiles_create(lib.handle, n, rp, col, rm) as tl:
+        q, k, v = to_dev(inp, "bf16")
+        for label, it in (("balanced", 0), ("one item per query tile", 1 << 20)):
+            m.bsa_set_option(lib.handle, m.BSA_OPT_STATIC_ITEM_TILES, it)
+            out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+            for _ in range(3):
+                m.bsa_forward_static(lib.handle, q, k, v, out, tl, scale=0.125)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                m.bsa_forward_static(lib.handle, q, k, v, out, tl, scale=0.125)
+            e1.record()
+            torch.cuda.synchronize()
+            times[label] = e0.elapsed_time(e1) / 20
+            outs[label] = out.cpu().numpy().reshape(-1, d)
+        m.bsa_set_option(lib.handle, m.BSA_OPT_STATIC_ITEM_TILES, 0)
+    say("    " + ", ".join(f"{k_}: {v_ * 1e3:.1f} us" for k_, v_ in times.items()))
+    for label, got in outs.items():
+        err = np.abs(got - ref).max()
+        say(f"    {label}: max|err|={err:.3g}")
+        assert err <= TOL["bf16"]
+    # not bit-identical for bf16: each item rounds P to bf16 against its own
+    # running maximum, so a cut list rounds some weights differently (2^-9
+    # relative per weight)
+    assert np.abs(outs["balanced"] - outs["one item per query tile"]).max() <= 2e-3
+
+
+def test_static_tile_list_validation(bsa):
+    """Malformed lists are refused when the list is made (BSA_ERR_INVALID_ARG,
+    nothing created); a list for another n, or tile != 64, is refused by the
+    forward."""
+    m, lib = bsa
+    h = lib.handle
+    L = m._binding._lib
+    n = 256
+    rp = np.array([0, 1, 2, 3, 4], np.int32)
+    col = np.array([0, 1, 2, 3], np.int32)
+    say("[gpu] tile-list validation statuses")
+
+    def create(rp_, col_, rm_=None, nn=n, tile=64):
+        out = ctypes.c_void_p()
+        rp_ = np.ascontiguousarray(rp_, np.int32)
+        col_ = np.ascontiguousarray(col_, np.int32)
+        st = L.bsa_tiles_create(h, nn, tile, rp_.ctypes.data, col_.ctypes.data if col_.size else None,
+                                None if rm_ is None else rm_.ctypes.data, col_.size, ctypes.byref(out))
+        if st == m.BSA_OK:
+            L.bsa_tiles_destroy(out)
+        else:
+            assert not out.value
+        return st
+
+    assert create(rp, col) == m.BSA_OK
+    assert create([0, 2, 1, 3, 4], col) == m.BSA_ERR_INVALID_ARG          # row_ptr decreases
+    assert create(rp, [0, 1, 2, 4]) == m.BSA_ERR_INVALID_ARG              # key tile out of range
+    assert create(rp, [0, 1, -1, 3]) == m.BSA_ERR_INVALID_ARG             # negative key tile
+    assert create([0, 1, 2, 3, 3], col) == m.BSA_ERR_INVALID_ARG          # last != nnz
+    assert create([0, 2, 2, 2, 4], [1, 1, 2, 3]) == m.BSA_ERR_INVALID_ARG  # repeated tile in a row
+    assert create([0, 2, 2, 2, 4], [3, 0, 2, 3]) == m.BSA_ERR_INVALID_ARG  # descending in a row
+    assert "row_ptr" in m.bsa_last_error(h) or "col" in m.bsa_last_error(h)
+    assert create(rp, col, tile=32) == m.BSA_ERR_UNSUPPORTED
+    # n = 200: the last key tile holds 8 keys; a row mask bit for key 8 of it is refused
+    rm = np.zeros((4, 64), np.uint64)
+    rm[:, 0] = 1
+    assert create(rp, col, rm, nn=200) == m.BSA_OK
+    rm[3, 5] = np.uint64(1 << 8)
+    assert create(rp, col, rm, nn=200) == m.BSA_ERR_INVALID_ARG
+    q = torch.zeros((1, 1, n, 64), dtype=torch.float32, device="cuda")
+    out = torch.zeros_like(q)
+    with m.bsa_tiles_create(h, n, rp, col) as tl:
+        P = lambda t: t.data_ptr()
+        fs = lambda nn=n, tile=64: L.bsa_forward_static(h, P(q), P(q), P(q), P(out), 1, 1, nn, 64, 0, tile,
+                                                       tl.ptr, 0.125, None)
+        assert fs() == m.BSA_OK
+        assert fs(tile=32) == m.BSA_ERR_UNSUPPORTED
+        assert fs(nn=192) == m.BSA_ERR_INVALID_ARG                       # list made for another n
+        assert L.bsa_forward_static(h, P(q), P(q), P(q), P(out), 1, 1, n, 64, 0, 64, None, 0.125,
+                                    None) == m.BSA_ERR_INVALID_ARG
+        torch.cuda.synchronize()
+
+
+def test_out_of_memory_status_and_recovery(bsa, monkeypatch):
+    """A workspace allocation that fails (forced from the host with
+    BSA_TEST_FAIL_ALLOC=1) returns BSA_ERR_OUT_OF_MEMORY, enqueues nothing,
+    and the handle works normally once allocation succeeds again."""
+    import content_dependent_block_amd as m
+    w = W.Workload("oom", 1, 2, 2048, 64, "bf16", seed=51, topk=8, key_offsets=True)
+    inp = W.generate(w)
+    q, k, v = to_dev(inp, "bf16")
+    say("[gpu] forced allocation failure on a fresh handle")
+    with m.BlockSparseAttention(0) as lib:
+        out = torch.full(q.shape, 7.0, dtype=torch.float32, device="cuda")
+        monkeypatch.setenv("BSA_TEST_FAIL_ALLOC", "1")
+        with pytest.raises(m.BsaError) as e:
+            m.bsa_forward(lib.handle, q, k, v, out, None, topk=w.topk, scale=w.scale)
+        assert e.value.status == m.BSA_ERR_OUT_OF_MEMORY
+        assert "allocation" in m.bsa_last_error(lib.handle)
+        torch.cuda.synchronize()
+        assert bool((out == 7.0).all())           # nothing was enqueued
+        monkeypatch.delenv("BSA_TEST_FAIL_ALLOC")
+        got_o, got_i = run_forward(m, lib, w, inp)
+    with m.BlockSparseAttention(0) as fresh:
+        ref_o, ref_i = run_forward(m, fresh, w, inp)
+    assert np.array_equal(got_i, ref_i)
+    assert np.array_equal(got_o.view(np.uint32), ref_o.view(np.uint32))
 
 
 # ------------------------------------------------------------- edge cases --
@@ -338,28 +531,23 @@ def test_static_edge_cases(bsa):
     mask[512:576, 64:128] = 1               # one fully visible tile
     rp, col, rm = m.bsa_tiles_from_mask(mask)
     assert m.bsa_tiles_validate(rp, col, n)
-    q, k, v = to_dev(inp, "bf16")
-    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
     say(f"[gpu] bsa_forward_static random mask n={n} nnz={col.size}")
-    m.bsa_forward_static(lib.handle, q, k, v, out, torch.from_numpy(rp).cuda(),
-                         torch.from_numpy(col).cuda(), torch.from_numpy(rm.view(np.int64)).cuda(),
-                         scale=0.125)
-    torch.cuda.synchronize()
-    ref = oracle.attend_mask(inp.q, inp.k, inp.v, mask, 0.125)
-    got = out.cpu().numpy().reshape(-1, d)
-    assert np.abs(got - ref).max() <= TOL["bf16"]
-    assert (got.reshape(2, n, d)[:, 128:256] == 0).all()
+    with m.bsa_tiles_create(lib.handle, n, rp, col, rm) as tl:
+        for item_tiles in (0, 1, 1 << 20):
+            got = run_static(m, lib, inp, "bf16", tl, 0.125, item_tiles)
+            ref = oracle.attend_mask(inp.q, inp.k, inp.v, mask, 0.125)
+            assert np.abs(got - ref).max() <= TOL["bf16"]
+            assert (got.reshape(2, n, d)[:, 128:256] == 0).all()
     # no rowmask: every listed tile fully visible
     full = np.zeros((n, n), dtype=np.uint8)
     for t in range(n // 64):
         for kt in col[rp[t]:rp[t + 1]]:
             full[t * 64:(t + 1) * 64, kt * 64:(kt + 1) * 64] = 1
     say("[gpu] bsa_forward_static without rowmask")
-    m.bsa_forward_static(lib.handle, q, k, v, out, torch.from_numpy(rp).cuda(),
-                         torch.from_numpy(col).cuda(), None, scale=0.125)
-    torch.cuda.synchronize()
+    with m.bsa_tiles_create(lib.handle, n, rp, col) as tl:
+        got = run_static(m, lib, inp, "bf16", tl, 0.125)
     ref = oracle.attend_mask(inp.q, inp.k, inp.v, full, 0.125)
-    assert np.abs(out.cpu().numpy().reshape(-1, d) - ref).max() <= TOL["bf16"]
+    assert np.abs(got - ref).max() <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("n", [4096, 4160])
