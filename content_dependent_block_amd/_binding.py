@@ -53,6 +53,7 @@ _sig("bsa_last_error", [_P], ctypes.c_char_p)
 _sig("bsa_set_option", [_P, _I, _I64])
 _sig("bsa_workspace_bytes", [_P, ctypes.POINTER(ctypes.c_size_t)])
 _sig("bsa_forward", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P])
+_sig("bsa_forward_noalloc", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P])
 _sig("bsa_forward_budgets", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _F, _I, _P])
 _sig("bsa_forward_train", [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _F, _I, _P])
 _sig("bsa_backward", [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
@@ -71,7 +72,8 @@ _sig("bsa_profile_enable", [_P, _I])
 _sig("bsa_profile_read", [_P, _P, _P, _I])
 
 EXPORTED = ("bsa_create", "bsa_destroy", "bsa_status_string", "bsa_last_error", "bsa_set_option",
-            "bsa_workspace_bytes", "bsa_forward", "bsa_forward_budgets", "bsa_forward_train",
+            "bsa_workspace_bytes", "bsa_forward", "bsa_forward_noalloc", "bsa_forward_budgets",
+            "bsa_forward_train",
             "bsa_backward", "bsa_fine_forward",
             "bsa_block_pool",
             "bsa_coarse_score", "bsa_topk_select", "bsa_tiles_create", "bsa_tiles_destroy",
@@ -173,6 +175,18 @@ def bsa_forward(h, q, k, v, out, block_idx_out=None, *, block: int = 64, topk: i
         pi = _need(block_idx_out, "block_idx_out", (b, hh, n, topk), torch.int32, dev)
     _check(_lib.bsa_forward(h, pq, pk, pv, po, pi, b, hh, n, d, _dtype_code(q), block, topk,
                             float(scale), int(causal), _stream(stream, dev)), h)
+
+
+def bsa_forward_noalloc(h, q, k, v, out, block_idx_out, *, block: int = 64, topk: int,
+                        scale: float, causal: bool = False, stream=None) -> None:
+    """bsa_forward with no device allocation: the workspace is the library's
+    fixed per-device array (calls that overlap on one device race)."""
+    pq, pk, pv, dev = _qkv(q, k, v)
+    b, hh, n, d = q.shape
+    po = _need(out, "out", q.shape, torch.float32, dev)
+    pi = _need(block_idx_out, "block_idx_out", (b, hh, n, topk), torch.int32, dev)
+    _check(_lib.bsa_forward_noalloc(h, pq, pk, pv, po, pi, b, hh, n, d, _dtype_code(q), block, topk,
+                                    float(scale), int(causal), _stream(stream, dev)), h)
 
 
 def bsa_forward_budgets(h, q, k, v, out, block_idx_out=None, *, head_topk, topk_max: int = None,

@@ -21,7 +21,7 @@ LIB = PKG / "libbsa.so"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["block_pool.hip", "coarse_score.hip", "topk_select.hip", "sparse_flash_fwd.hip",
-           "fine_gather.hip", "fine_backward.hip", "ragged.hip", "bsa_api.cpp", "tiles.cpp"]
+           "fine_gather.hip", "fine_backward.hip", "ragged.hip", "noalloc.hip", "bsa_api.cpp", "tiles.cpp"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "--offload-arch=gfx950",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -20,6 +20,7 @@
 
 struct bsa_handle_s {
   int device = 0;
+  void* noalloc = nullptr;  // device address of the fixed workspace on this device
   char err[512] = {0};
   // workspace
   float* repr = nullptr;
@@ -249,9 +250,18 @@ BSA_API bsa_status bsa_create(int device, bsa_handle* out) {
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
     return fail(nullptr, BSA_ERR_NO_DEVICE, "bsa_create: device %d is %s, not gfx950", device,
                 prop.gcnArchName);
+  void* arena = nullptr;
+  {
+    DeviceGuard dg(device);
+    const hipError_t e = bsa::noalloc_scratch(device, &arena);
+    if (e != hipSuccess)
+      return fail(nullptr, BSA_ERR_NO_DEVICE, "bsa_create: cannot locate the fixed workspace on device %d: %s",
+                  device, hipGetErrorString(e));
+  }
   bsa_handle h = new (std::nothrow) bsa_handle_s();
   if (!h) return fail(nullptr, BSA_ERR_OUT_OF_MEMORY, "bsa_create: host allocation failed");
   h->device = device;
+  h->noalloc = arena;
   *out = h;
   return BSA_OK;
 }
@@ -354,12 +364,36 @@ bsa::HeadBudget uniform_budget(int topk) {
   return hb;
 }
 
+// A fixed region of device memory handed out front to back (256-byte
+// aligned pieces); the workspace of the no-allocation entry point.
+struct Arena {
+  unsigned char* base = nullptr;
+  size_t cap = 0, used = 0;
+  size_t avail() const { return cap > align(used) ? cap - align(used) : 0; }
+  static size_t align(size_t x) { return (x + 255) & ~size_t(255); }
+  void* take(size_t bytes) {
+    const size_t off = align(used);
+    if (off + bytes > cap) return nullptr;
+    used = off + bytes;
+    return base + off;
+  }
+};
+
+bsa_status take(bsa_handle h, Arena* arena, void** out, size_t bytes, const char* what) {
+  *out = arena->take(bytes);
+  if (!*out)
+    return fail(h, BSA_ERR_UNSUPPORTED, "%s: %zu bytes do not fit the %zu bytes left of the fixed workspace",
+                what, bytes, arena->avail());
+  return BSA_OK;
+}
+
 // Stage 1 selection over all rows: one fused coarse_score + topk_select
 // kernel (k <= 32, fused strategy), else coarse_score and topk_select through
-// a panel, in chunks of at most panel_chunk_bytes of panel.
+// a panel, in chunks of at most panel_chunk_bytes of panel (with an arena: of
+// what is left of it).
 bsa_status run_select(bsa_handle h, const void* q, const float* repr, const uint16_t* split,
                       int32_t* idx, const Shape& s, bsa_dtype dt, int topk,
-                      const bsa::HeadBudget& hb, int causal, hipStream_t st) {
+                      const bsa::HeadBudget& hb, int causal, hipStream_t st, Arena* arena = nullptr) {
   const int64_t nb = s.n / 64;
   const int64_t total = s.bh() * s.n;
   if (fused_select(h, topk))
@@ -367,17 +401,28 @@ bsa_status run_select(bsa_handle h, const void* q, const float* repr, const uint
       return bsa::launch_coarse_select(q, repr, split, idx, total, s.n, s.d, dt, topk, hb, causal, st);
     });
   int64_t chunk = h->panel_chunk_bytes / (nb * 4) / 64 * 64;
+  if (arena) {
+    const int64_t fit = int64_t(arena->avail() / size_t(nb * 4)) / 64 * 64;
+    if (fit < 64) return fail(h, BSA_ERR_UNSUPPORTED, "score panel: one 64-row chunk does not fit the fixed workspace");
+    if (chunk > fit) chunk = fit;
+  }
   if (chunk < 64) chunk = 64;
   if (chunk > total) chunk = total;
-  TRY(grow(h, reinterpret_cast<void**>(&h->panel), &h->panel_bytes, size_t(chunk) * nb * 4,
-           "panel workspace"));
+  float* panel = nullptr;
+  if (arena) {
+    TRY(take(h, arena, reinterpret_cast<void**>(&panel), size_t(chunk) * nb * 4, "score panel"));
+  } else {
+    TRY(grow(h, reinterpret_cast<void**>(&h->panel), &h->panel_bytes, size_t(chunk) * nb * 4,
+             "panel workspace"));
+    panel = h->panel;
+  }
   for (int64_t r0 = 0; r0 < total; r0 += chunk) {
     const int64_t rows = (total - r0) < chunk ? (total - r0) : chunk;
     TRY(timed_launch(h, BSA_STAGE_COARSE, st, "coarse_score", [&] {
-      return bsa::launch_coarse_score(q, repr, h->panel, r0, rows, s.n, s.d, dt, causal, st);
+      return bsa::launch_coarse_score(q, repr, panel, r0, rows, s.n, s.d, dt, causal, st);
     }));
     TRY(timed_launch(h, BSA_STAGE_TOPK, st, "topk_select", [&] {
-      return bsa::launch_topk_select(h->panel, idx, r0, rows, s.n, topk, hb, causal, st);
+      return bsa::launch_topk_select(panel, idx, r0, rows, s.n, topk, hb, causal, st);
     }));
   }
   return BSA_OK;
@@ -403,17 +448,102 @@ bsa_status grow_counts(bsa_handle h, size_t buckets, int64_t* clear_words) {
 }
 
 bsa_status run_gather_index(bsa_handle h, bsa::GatherArgs& a, int64_t r0, int64_t rows, int stage,
-                            const char* what, hipStream_t st) {
+                            const char* what, hipStream_t st, bool handle_counts = true) {
   const bsa_status r = timed_launch(h, stage, st, what, [&] { return bsa::launch_gather_index(a, r0, rows, st); });
-  h->counts_zero = r == BSA_OK;
+  if (handle_counts) h->counts_zero = r == BSA_OK;
   a.ws.count_words = 0;  // cleared by the first bucketing of this call
   return r;
+}
+
+// Device bytes the block-gather fine stage needs for a chunk of `chunk`
+// query rows (each piece 256-byte aligned, as an Arena hands them out).
+struct FineGeom {
+  int64_t chunk, pairs, buckets, slots;
+  int qsegs;
+  size_t bytes;
+};
+FineGeom fine_geom(const Shape& s, bsa_dtype dt, int topk, int64_t chunk) {
+  FineGeom g;
+  g.chunk = chunk;
+  g.pairs = chunk * topk;
+  g.qsegs = bsa::gather_segments(s.n, s.d, topk, dt);
+  const int64_t nb = s.n / 64;
+  const int64_t heads_spanned = s.bh() < (chunk + s.n - 1) / s.n + 1 ? s.bh() : (chunk + s.n - 1) / s.n + 1;
+  g.buckets = heads_spanned * g.qsegs * nb;
+  g.slots = bsa::gather_grid(chunk, topk, g.buckets, bsa::kGatherItemPairs);
+  const size_t pieces[] = {size_t(g.buckets) * 4, size_t(g.buckets + 1) * 4, size_t(g.buckets + 1) * 4,
+                           size_t(g.slots) * 16, size_t(g.pairs) * 4, size_t(g.pairs) * 4,
+                           size_t(g.pairs) * s.d * (dt == BSA_BF16 ? 2 : 4), size_t(g.pairs) * 8,
+                           size_t(chunk / 64 + 1) * 4};
+  g.bytes = 0;
+  for (size_t b : pieces) g.bytes += Arena::align(b);
+  return g;
+}
+
+// The block-gather fine stage with every buffer carved from `arena`: the
+// largest row chunk whose buffers fit is used; the bucket counts are cleared
+// by a kernel at the start of every call (the arena keeps what the last call
+// left).
+bsa_status run_fine_arena(bsa_handle h, const void* q, const void* k, const void* v, float* out, float* lse,
+                          const int32_t* idx, const Shape& s, bsa_dtype dt, int topk, float scale, int causal,
+                          hipStream_t st, Arena& arena) {
+  const int64_t total = s.bh() * s.n;
+  const int64_t align = (s.n % 256 == 0) ? 256 : 64;
+  int64_t chunk = (total + align - 1) / align * align;
+  while (chunk > align && fine_geom(s, dt, topk, chunk).bytes > arena.avail())
+    chunk = (chunk / 2 + align - 1) / align * align;
+  if (chunk > total) chunk = total;
+  const FineGeom g = fine_geom(s, dt, topk, chunk);
+  if (g.bytes > arena.avail())
+    return fail(h, BSA_ERR_UNSUPPORTED, "fine stage: one chunk of %lld rows needs %zu bytes, the fixed workspace "
+                "has %zu left", (long long)chunk, g.bytes, arena.avail());
+  bsa::GatherArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.lse = lse;
+  a.idx = idx;
+  a.n = s.n;
+  a.d = s.d;
+  a.topk = topk;
+  a.causal = causal;
+  a.scale = scale;
+  a.dtype = dt;
+  a.qsegs = g.qsegs;
+  void* p[9];
+  const size_t sizes[] = {size_t(g.buckets) * 4, size_t(g.buckets + 1) * 4, size_t(g.buckets + 1) * 4,
+                          size_t(g.slots) * 16, size_t(g.pairs) * 4, size_t(g.pairs) * 4,
+                          size_t(g.pairs) * s.d * (dt == BSA_BF16 ? 2 : 4), size_t(g.pairs) * 8,
+                          size_t(chunk / 64 + 1) * 4};
+  for (int i = 0; i < 9; ++i) TRY(take(h, &arena, &p[i], sizes[i], "fine-stage workspace"));
+  a.ws.count = static_cast<int32_t*>(p[0]);
+  a.ws.count_words = g.buckets;
+  a.ws.offsets = static_cast<int32_t*>(p[1]);
+  a.ws.items = static_cast<int32_t*>(p[2]);
+  a.ws.item_rec = static_cast<int4*>(p[3]);
+  a.ws.rank = static_cast<int32_t*>(p[4]);
+  a.ws.list = static_cast<int32_t*>(p[5]);
+  a.ws.partial_o = p[6];
+  a.ws.rec = static_cast<int2*>(p[7]);
+  a.ws.wg_valid = static_cast<int32_t*>(p[8]);
+  for (int64_t r0 = 0; r0 < total; r0 += chunk) {
+    const int64_t rows = (total - r0) < chunk ? (total - r0) : chunk;
+    TRY(run_gather_index(h, a, r0, rows, BSA_STAGE_GATHER_INDEX, "block-gather bucketing", st, false));
+    TRY(timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd",
+                     [&] { return bsa::launch_gather_partial(a, r0, rows, st); }));
+    TRY(timed_launch(h, BSA_STAGE_GATHER_COMBINE, st, "block-gather combine",
+                     [&] { return bsa::launch_gather_combine(a, r0, rows, st); }));
+  }
+  return BSA_OK;
 }
 
 // Stage 2 for the dynamic path, with the handle's fine strategy.
 bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, float* out,
                     float* lse, const int32_t* idx, const Shape& s, bsa_dtype dt, int topk,
-                    float scale, int causal, hipStream_t st, int nv = 0) {
+                    float scale, int causal, hipStream_t st, int nv = 0, Arena* arena = nullptr) {
+  if (arena && h->fine_strategy == BSA_FINE_BLOCK_GATHER)
+    return run_fine_arena(h, q, k, v, out, lse, idx, s, dt, topk, scale, causal, st, *arena);
   if (h->fine_strategy == BSA_FINE_QUERY_TILE)
     return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
       return bsa::launch_sparse_flash_dynamic(q, k, v, out, lse, idx, s.bh(), s.n, s.d, topk, scale,
@@ -664,6 +794,48 @@ BSA_API bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const
   TRY(check_dynamic(h, fn, s, topk, causal));
   return forward_impl(h, fn, q, k, v, out, block_idx_out, nullptr, s, dtype, topk, uniform_budget(topk),
                       scale, causal, stream);
+}
+
+BSA_API bsa_status bsa_forward_noalloc(bsa_handle h, const void* q, const void* k, const void* v,
+                                       float* out, int32_t* block_idx_out, int batch, int heads, int n,
+                                       int d, bsa_dtype dtype, int block, int topk, float scale,
+                                       int causal, void* stream) {
+  const char* fn = "bsa_forward_noalloc";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const Shape s{batch, heads, n, d};
+  TRY(check_shape(h, fn, s, dtype, block));
+  TRY(check_dynamic(h, fn, s, topk, causal));
+  TRY(check_scale(h, fn, scale));
+  TRY(check_ptr(h, fn, "q", q));
+  TRY(check_ptr(h, fn, "k", k));
+  TRY(check_ptr(h, fn, "v", v));
+  TRY(check_ptr(h, fn, "out", out));
+  if (!block_idx_out || (reinterpret_cast<uintptr_t>(block_idx_out) & 3u))
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: block_idx_out is NULL or not 4-byte aligned", fn);
+  if (!h->noalloc) return fail(h, BSA_ERR_NO_DEVICE, "%s: no fixed workspace on device %d", fn, h->device);
+  DeviceGuard dg(h->device);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Arena arena;
+  arena.base = static_cast<unsigned char*>(h->noalloc);
+  arena.cap = bsa::kNoAllocScratchBytes;
+  const int64_t nb = s.n / 64;
+  const bool want_split = fused_select(h, topk) && dtype == BSA_BF16;
+  float* repr = nullptr;
+  uint16_t* split = nullptr;
+  if (want_split)
+    TRY(take(h, &arena, reinterpret_cast<void**>(&split), size_t(s.bh() * nb * s.d) * 3 * 2, "split representatives"));
+  else
+    TRY(take(h, &arena, reinterpret_cast<void**>(&repr), size_t(s.bh() * nb * s.d) * 4, "representatives"));
+  // no events either: per-stage timing is off for this call
+  const bool profiling = h->profiling;
+  h->profiling = false;
+  bsa_status r = run_pool(h, k, repr, split, s, dtype, st);
+  if (r == BSA_OK)
+    r = run_select(h, q, repr, split, block_idx_out, s, dtype, topk, uniform_budget(topk), causal, st, &arena);
+  if (r == BSA_OK)
+    r = run_fine(h, q, k, v, out, nullptr, block_idx_out, s, dtype, topk, scale, causal, st, 0, &arena);
+  h->profiling = profiling;
+  return r;
 }
 
 BSA_API bsa_status bsa_forward_budgets(bsa_handle h, const void* q, const void* k, const void* v,

@@ -184,4 +184,11 @@ hipError_t launch_bwd_pairs(const BackwardArgs& a, int64_t row0, int64_t rows, h
 hipError_t launch_bwd_dq(const BackwardArgs& a, int64_t row0, int64_t rows, hipStream_t s);
 hipError_t launch_bwd_dkv(const BackwardArgs& a, int64_t row0, int64_t rows, hipStream_t s);
 
+// The fixed workspace of bsa_forward_noalloc: a device array of
+// kNoAllocScratchBytes per device (noalloc.hip).  noalloc_scratch returns its
+// device address on `device`, which must be the current device on the first
+// call for that device (the address is looked up once and kept).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(int device, void** out);
+
 }  // namespace bsa

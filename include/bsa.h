@@ -196,6 +196,28 @@ bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const void* v
                        int n, int d, bsa_dtype dtype, int block, int topk,
                        float scale, int causal, void* stream);
 
+/* bsa_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * call makes no hipMalloc, hipFree or other allocation: all its workspace
+ * (block representatives, score-panel chunks, the fine stage's bucketing
+ * buffers and partial rows) comes from one fixed device array of
+ * BSA_NOALLOC_WORKSPACE_BYTES per device, held by the library until the
+ * process ends.  The fine stage processes query rows in the largest chunks
+ * whose buffers fit.  Results equal bsa_forward's with the same arguments.
+ *  block_idx_out  required (the caller provides the index buffer).
+ *  n              a multiple of 64 (BSA_ERR_UNSUPPORTED otherwise).
+ * A problem whose representatives, or whose smallest fine-stage chunk, do
+ * not fit the fixed array returns BSA_ERR_UNSUPPORTED and enqueues nothing.
+ * Every call on a device shares that device's array: calls that overlap on
+ * one device (different streams, threads or handles) race and give wrong
+ * results.  Per-stage timing is not recorded for this call.  Everything else
+ * as for bsa_forward. */
+#define BSA_NOALLOC_WORKSPACE_BYTES (64u << 20)
+bsa_status bsa_forward_noalloc(bsa_handle h, const void* q, const void* k, const void* v,
+                               float* out, int32_t* block_idx_out, int batch, int heads,
+                               int n, int d, bsa_dtype dtype, int block, int topk,
+                               float scale, int causal, void* stream);
+
 /* Like bsa_forward with a top-k budget per head (nishantmodi.me
  * "sparse-attention-triton-bench", section "What's next": each head keeps
  * its own number of blocks, chosen at run time).
