@@ -65,6 +65,11 @@ namespace {
 
 constexpr int kTerms = 3;
 
+// R tiles in flight ahead of the one computed in the hi-only pass, and blocks
+// per R tile of that pass (bf16 planes).
+constexpr int kSelectPrefetch = 1;
+constexpr int kPass1Blocks = 64;
+
 __device__ __forceinline__ int64_t xcd_tile(int causal) {
   const int64_t nwg = gridDim.x, bid = blockIdx.x;
   if (nwg % 8 != 0) return bid;
@@ -176,38 +181,66 @@ struct Bf16Tiles {
 // repeat the last block (their scores are never used).  NT = number of terms
 // staged and multiplied: 3 (exact scores) or 1 (hi only, for the selection
 // bound; put<1>() also tracks max |hi| per column for its error bound).
-template <int D>
+// QG query groups of 16 share each A-operand read from LDS: one read feeds
+// QG MFMAs.  NTH = threads of the workgroup that stage the tile.
+template <int D, int QG = 1, int NTH = 256, int TB_ = 32, int NTS = kTerms>
 struct Bf16PlaneTiles {
   using QT = bf16_bits;
   using Src = bf16_bits;
-  static constexpr int TB = 32;
+  static constexpr int TB = TB_;                        // blocks per R tile
   static constexpr int PITCH = kRPitch<D>;
-  static constexpr int LDS_BYTES = kTerms * TB * PITCH * 2;
+  static constexpr int LDS_BYTES = NTS * TB * PITCH * 2;  // NTS: terms staged at most
   static constexpr int CPR = D / 8;             // 16-byte chunks per block row
-  static constexpr int PER = TB * CPR / 256;    // chunks per thread and term
-  static_assert(256 % CPR == 0, "a thread keeps one column chunk");
+  static constexpr int PER = TB * CPR / NTH;    // chunks per thread and term
+  static_assert(PER >= 1 && (TB * CPR) % NTH == 0, "whole chunks per thread");
+  static_assert(NTH % CPR == 0, "a thread keeps one column chunk");
   typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-  bf16x8 qb[D / 32];
+  static constexpr int PFD = kSelectPrefetch;  // R tiles in flight ahead of the one computed (hi-only walk)
+  bf16x8 qb[QG][D / 32];
   uint4 pf[kTerms][PER];
+  uint4 pf1[PFD > 1 ? PFD - 1 : 1][PER];  // further hi-only tiles in flight
   u16x2 amax[4];  // max |hi| bit patterns of this thread's 8 columns
 
-  __device__ __forceinline__ void load_q(const QT* __restrict__ q, int64_t qrow, int g) {
-    load_q_bf16<D>(qb, q, qrow, g);
+  // Query group gq of this lane: row qrow0 + 16 gq.
+  __device__ __forceinline__ void load_q(const QT* __restrict__ q, int64_t qrow0, int g) {
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) load_q_bf16<D>(qb[gq], q, qrow0 + 16 * gq, g);
 #pragma unroll
     for (int i = 0; i < 4; ++i) amax[i] = u16x2{0, 0};
   }
   __device__ __forceinline__ static const Src* head_base(const Src* r, int64_t bh, int nb) {
     return r + bh * kTerms * nb * D;
   }
+  // Loads of tile bt (all NT terms) into registers.  The hi-only walk keeps
+  // PFD tiles in flight: fetch() then fills the last slot, and put() takes
+  // the oldest and moves the others up.
   template <int NT>
   __device__ __forceinline__ void fetch(const Src* __restrict__ rbase, int nb, int bt, int tid) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 8;
+      const int c = tid + NTH * u, r = c / CPR, col = (c % CPR) * 8;
       const int beta = min(bt * TB + r, nb - 1);
+      if constexpr (NT == 1 && PFD > 1) {
+        pf1[PFD - 2][u] = ld16(rbase + static_cast<uint32_t>(beta * D + col));
+      } else {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        pf[t][u] = ld16(rbase + static_cast<uint32_t>((t * nb + beta) * D + col));
+        for (int t = 0; t < NT; ++t)
+          pf[t][u] = ld16(rbase + static_cast<uint32_t>((t * nb + beta) * D + col));
+      }
+    }
+  }
+  template <int NT>
+  __device__ __forceinline__ void prime(const Src* __restrict__ rbase, int nb, int tid) {
+    fetch<NT>(rbase, nb, 0, tid);
+    if constexpr (NT == 1 && PFD > 1) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) pf[0][u] = pf1[PFD - 2][u];
+#pragma unroll
+      for (int i = 1; i < PFD; ++i) {
+        fetch<NT>(rbase, nb, i, tid);
+#pragma unroll
+        for (int u = 0; u < PER; ++u) pf1[i - 1][u] = pf1[PFD - 2][u];
+      }
     }
   }
   template <int NT>
@@ -215,7 +248,7 @@ struct Bf16PlaneTiles {
     __bf16* rs = reinterpret_cast<__bf16*>(lds);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 8;
+      const int c = tid + NTH * u, r = c / CPR, col = (c % CPR) * 8;
 #pragma unroll
       for (int t = 0; t < NT; ++t) *reinterpret_cast<uint4*>(rs + (t * TB + r) * PITCH + col) = pf[t][u];
       if constexpr (NT == 1) {
@@ -223,21 +256,63 @@ struct Bf16PlaneTiles {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           amax[i] = __builtin_elementwise_max(amax[i], __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
+        if constexpr (PFD > 1) {
+          pf[0][u] = pf1[0][u];
+#pragma unroll
+          for (int i = 0; i + 1 < PFD - 1; ++i) pf1[i][u] = pf1[i + 1][u];
+        }
       }
     }
   }
-  template <int NT>
-  __device__ __forceinline__ f32x4 tile(const unsigned char* lds, int mt, int g, int c16) const {
-    return bf16_tile<D, TB, NT>(lds, qb, mt, g, c16);
+  // One lane's 4 scores of every MFMA tile of the R tile for each of its QG
+  // query groups; the MT tiles' accumulation chains are interleaved (each
+  // chain keeps the order of tiles(), so the scores are the same bits).
+  template <int NT, int MT>
+  __device__ __forceinline__ void tiles_all(const unsigned char* lds, int g, int c16, f32x4 (&acc)[MT][QG]) const {
+    const __bf16* rs = reinterpret_cast<const __bf16*>(lds);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) acc[mt][gq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const bf16x8 a =
+              *reinterpret_cast<const bf16x8*>(rs + (t * TB + mt * 16 + c16) * PITCH + 8 * g + 32 * ks);
+#pragma unroll
+          for (int gq = 0; gq < QG; ++gq) acc[mt][gq] = mfma_16x16x32_bf16(a, qb[gq][ks], acc[mt][gq]);
+        }
+      }
+    }
   }
-  // E >= |exact score - hi-only score| for this lane's query and every block
-  // of the head: (2^-8 + 2^-15) sum_d |q_d| R_d with R_d >= max_beta |r_beta,d|
-  // (hi is r rounded to 8 significant bits, |r - hi| <= 2^-8 |r|; 2^-15 covers
-  // the fp32 rounding of both sums).  The query's 4 lanes return the same E.
-  // lds: at least 256 * 16 + D * 4 bytes, free; a barrier precedes reuse.
-  __device__ __forceinline__ float pass1_error(unsigned char* lds, int tid, int lane, int g) const {
-    uint32_t* part = reinterpret_cast<uint32_t*>(lds);              // [256][4]
-    float* rmax = reinterpret_cast<float*>(lds + 256 * 16);         // [D]
+  // One lane's 4 scores of MFMA tile mt for each of its QG query groups.
+  template <int NT>
+  __device__ __forceinline__ void tiles(const unsigned char* lds, int mt, int g, int c16, f32x4 (&acc)[QG]) const {
+    const __bf16* rs = reinterpret_cast<const __bf16*>(lds);
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) acc[gq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(rs + (t * TB + mt * 16 + c16) * PITCH + 8 * g + 32 * ks);
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) acc[gq] = mfma_16x16x32_bf16(a, qb[gq][ks], acc[gq]);
+      }
+    }
+  }
+  // E >= |exact score - hi-only score| for each of this lane's queries and
+  // every block of the head: (2^-8 + 2^-15) sum_d |q_d| R_d with R_d >=
+  // max_beta |r_beta,d| (hi is r rounded to 8 significant bits,
+  // |r - hi| <= 2^-8 |r|; 2^-15 covers the fp32 rounding of both sums).  The
+  // query's 4 lanes return the same E.  lds: at least NTH * 16 + D * 4 bytes,
+  // free; a barrier precedes reuse.
+  __device__ __forceinline__ void pass1_error(unsigned char* lds, int tid, int lane, int g, float (&err)[QG]) const {
+    uint32_t* part = reinterpret_cast<uint32_t*>(lds);              // [NTH][4]
+    float* rmax = reinterpret_cast<float*>(lds + NTH * 16);         // [D]
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i) part[tid * 4 + i] = __builtin_bit_cast(uint32_t, amax[i]);
@@ -245,28 +320,32 @@ struct Bf16PlaneTiles {
     if (tid < D) {
       const int cc = tid / 8, e = tid % 8;  // column chunk, element in it
       uint32_t m = 0u;
-      for (int t = cc; t < 256; t += CPR) {
+      for (int t = cc; t < NTH; t += CPR) {
         const uint32_t w = part[t * 4 + e / 2];
         m = max(m, (e & 1) ? (w >> 16) : (w & 0xffffu));
       }
       rmax[tid] = __uint_as_float(m << 16) * (1.0f + 0x1.0p-8f);
     }
     __syncthreads();
-    float sum = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks)
+    for (int gq = 0; gq < QG; ++gq) {
+      float sum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        sum += fabsf(static_cast<float>(qb[ks][e])) * rmax[8 * g + 32 * ks + e];
-    sum += __uint_as_float(lane_xor<16>(__float_as_uint(sum), lane));
-    sum += __uint_as_float(lane_xor<32>(__float_as_uint(sum), lane));
-    return sum * (0x1.0p-8f + 0x1.0p-15f);
+      for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          sum += fabsf(static_cast<float>(qb[gq][ks][e])) * rmax[8 * g + 32 * ks + e];
+      sum += __uint_as_float(lane_xor<16>(__float_as_uint(sum), lane));
+      sum += __uint_as_float(lane_xor<32>(__float_as_uint(sum), lane));
+      err[gq] = sum * (0x1.0p-8f + 0x1.0p-15f);
+    }
   }
 };
 
 // fp32 inputs: v_mfma_f32_16x16x4_f32; slot (ks, g) carries d = KS*g + ks.
-// stage() for the panel kernel; fetch()/put() as for Bf16PlaneTiles.
-template <int D, int TB_>
+// stage() and tile() (one query group) for the panel kernel; fetch()/put()/
+// tiles() as for Bf16PlaneTiles.
+template <int D, int TB_, int QG = 1, int NTH = 256>
 struct F32Tiles {
   using QT = float;
   using Src = float;
@@ -275,16 +354,20 @@ struct F32Tiles {
   static constexpr int PITCH = D + 4;
   static constexpr int LDS_BYTES = TB * PITCH * 4;
   static constexpr int CPR = D / 4;             // 16-byte chunks per block row
-  static constexpr int PER = TB * CPR / 256;
-  float qf[KS];
+  static constexpr int PER = TB * CPR / NTH;
+  static_assert(PER >= 1 && (TB * CPR) % NTH == 0, "whole chunks per thread");
+  float qf[QG][KS];
   float4 pf[PER];
 
-  __device__ __forceinline__ void load_q(const QT* __restrict__ q, int64_t qrow, int g) {
-    const float* qr = q + qrow * D + KS * g;
+  __device__ __forceinline__ void load_q(const QT* __restrict__ q, int64_t qrow0, int g) {
 #pragma unroll
-    for (int e = 0; e < KS; e += 4) {
-      const float4 x = *reinterpret_cast<const float4*>(qr + e);
-      qf[e] = x.x; qf[e + 1] = x.y; qf[e + 2] = x.z; qf[e + 3] = x.w;
+    for (int gq = 0; gq < QG; ++gq) {
+      const float* qr = q + (qrow0 + 16 * gq) * D + KS * g;
+#pragma unroll
+      for (int e = 0; e < KS; e += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(qr + e);
+        qf[gq][e] = x.x; qf[gq][e + 1] = x.y; qf[gq][e + 2] = x.z; qf[gq][e + 3] = x.w;
+      }
     }
   }
   __device__ __forceinline__ static const Src* head_base(const Src* r, int64_t bh, int nb) {
@@ -305,30 +388,64 @@ struct F32Tiles {
   __device__ __forceinline__ void fetch(const Src* __restrict__ rbase, int nb, int bt, int tid) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 4;
+      const int c = tid + NTH * u, r = c / CPR, col = (c % CPR) * 4;
       const int beta = min(bt * TB + r, nb - 1);
       pf[u] = *reinterpret_cast<const float4*>(rbase + static_cast<uint32_t>(beta * D + col));
     }
   }
   template <int NT>
+  __device__ __forceinline__ void prime(const Src* __restrict__ rbase, int nb, int tid) {
+    fetch<NT>(rbase, nb, 0, tid);
+  }
+  static constexpr int PFD = 1;
+  template <int NT>
   __device__ __forceinline__ void put(unsigned char* lds, int tid) {
     float* rs = reinterpret_cast<float*>(lds);
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int c = tid + 256 * u, r = c / CPR, col = (c % CPR) * 4;
+      const int c = tid + NTH * u, r = c / CPR, col = (c % CPR) * 4;
       *reinterpret_cast<float4*>(rs + r * PITCH + col) = pf[u];
     }
   }
   template <int NT>
   __device__ __forceinline__ f32x4 tile(const unsigned char* lds, int mt, int g, int c16) const {
+    f32x4 acc[QG];
+    tiles<NT>(lds, mt, g, c16, acc);
+    return acc[0];
+  }
+  template <int NT>
+  __device__ __forceinline__ void tiles(const unsigned char* lds, int mt, int g, int c16, f32x4 (&acc)[QG]) const {
     const float* rr = reinterpret_cast<const float*>(lds) + (mt * 16 + c16) * PITCH + KS * g;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc = mfma_16x16x4_f32(rr[ks], qf[ks], acc);
-    return acc;
+    for (int gq = 0; gq < QG; ++gq) acc[gq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const float a = rr[ks];
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) acc[gq] = mfma_16x16x4_f32(a, qf[gq][ks], acc[gq]);
+    }
+  }
+  template <int NT, int MT>
+  __device__ __forceinline__ void tiles_all(const unsigned char* lds, int g, int c16, f32x4 (&acc)[MT][QG]) const {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq) acc[mt][gq] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const float a = reinterpret_cast<const float*>(lds)[(mt * 16 + c16) * PITCH + KS * g + ks];
+#pragma unroll
+        for (int gq = 0; gq < QG; ++gq) acc[mt][gq] = mfma_16x16x4_f32(a, qf[gq][ks], acc[mt][gq]);
+      }
+    }
   }
   // Pass 1 computes the same scores as pass 2 here.
-  __device__ __forceinline__ float pass1_error(unsigned char*, int, int, int) const { return 0.f; }
+  __device__ __forceinline__ void pass1_error(unsigned char*, int, int, int, float (&err)[QG]) const {
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) err[gq] = 0.f;
+  }
 };
 
 // Where a workgroup's 64 query rows sit, and which blocks they may select;
@@ -557,18 +674,60 @@ __device__ __forceinline__ void sort_asc(int (&a)[N]) {
   }
 }
 
+// Where a select workgroup's queries sit: NW waves x QG query groups of 16
+// rows; lane (g, c16) of wave w holds, for group gq, query row
+// tile_row + 16 (w QG + gq) + c16.  All rows of a workgroup belong to one
+// (batch, head), and (64-row query blocks being aligned to the 32-block R
+// tiles) their query blocks lie in one R tile, the last one walked.
+template <int QG>
+struct SelInfo {
+  int64_t tile_row, bh, qrow0;
+  int nb, nbt;
+  int nvalid[QG], forced[QG];
+  int tid, lane, wave, g, c16;
+  __device__ __forceinline__ SelInfo(int n, int causal, int TB, int NW) {
+    const int rows = 16 * QG * NW;
+    nb = n / kTile;
+    tid = threadIdx.x;
+    lane = tid & 63;
+    wave = tid >> 6;
+    g = lane >> 4;
+    c16 = lane & 15;
+    tile_row = xcd_tile(causal) * rows;
+    bh = tile_row / n;
+    const int i0 = static_cast<int>(tile_row % n);
+    qrow0 = tile_row + 16 * QG * wave + c16;
+    const int qlast = (i0 + rows - 1) / kTile;  // query block of the workgroup's last row
+    nbt = causal ? qlast / TB + 1 : (nb + TB - 1) / TB;
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) {
+      const int qblk = (i0 + 16 * (QG * wave + gq)) / kTile;
+      nvalid[gq] = causal ? qblk + 1 : nb;
+      forced[gq] = causal ? qblk : -1;
+    }
+  }
+  // The score as the selection sees it: -inf for a block that is not a
+  // candidate, +inf for the causal own block.
+  __device__ __forceinline__ float cand(int gq, float s, int beta) const {
+    const float x = beta == forced[gq] ? INFINITY : s;
+    return beta < nvalid[gq] ? x : -INFINITY;
+  }
+};
+
 // Stream the tiles of the workgroup's representatives through LDS, register-
 // prefetching tile bt + 1 while tile bt is computed, and hand each 16-block
-// MFMA tile to fast(h, mt, b0, acc) or slow(...) (b0 = first block of the
-// MFMA tile, h = bt mod NH as a compile-time value: the loop is unrolled by
-// NH).  Every block of a tile before the last is an ordinary candidate (below
-// the last candidate and not the causal own block, which both lie in the
-// last tile), so only the last tile takes the checked slow().
-template <int NH, int NT, typename TL, typename FF, typename FS>
+// MFMA tile (its QG accumulators) to fast(h, mt, b0, acc) or slow(...) (b0 =
+// first block of the MFMA tile, h = bt mod NH as a compile-time value: the
+// loop is unrolled by NH).  Every block of a tile before the last is an
+// ordinary candidate for every query group (below each group's own block),
+// so only the last tile takes the checked slow().
+template <int NH, int NT, int QG, int NTH, typename TL, typename FF, typename FS>
 __device__ __forceinline__ void walk(TL& sc, unsigned char* rs, const typename TL::Src* rbase,
-                                     const TileInfo& ti, FF&& fast, FS&& slow) {
+                                     const SelInfo<QG>& ti, FF&& fast, FS&& slow) {
   constexpr int MT = TL::TB / 16;
-  sc.template fetch<NT>(rbase, ti.nb, 0, ti.tid);
+  constexpr int PF = NT == 1 ? TL::PFD : 1;  // tiles loaded ahead
+  sc.template prime<NT>(rbase, ti.nb, ti.tid);
+  f32x4 acc[MT][QG];
   // Steady state: NH tiles per iteration, none of them the last, so the body
   // has no branches and the slot index h stays a compile-time value.
   int bt0 = 0;
@@ -578,11 +737,11 @@ __device__ __forceinline__ void walk(TL& sc, unsigned char* rs, const typename T
       const int bt = bt0 + h;
       __syncthreads();
       sc.template put<NT>(rs, ti.tid);
-      sc.template fetch<NT>(rbase, ti.nb, bt + 1, ti.tid);
+      sc.template fetch<NT>(rbase, ti.nb, bt + PF, ti.tid);
       __syncthreads();
+      sc.template tiles_all<NT, MT>(rs, ti.g, ti.c16, acc);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        fast(h, mt, bt * TL::TB + mt * 16, sc.template tile<NT>(rs, mt, ti.g, ti.c16));
+      for (int mt = 0; mt < MT; ++mt) fast(h, mt, bt * TL::TB + mt * 16, acc[mt]);
     }
   }
   // The remaining 1 .. NH tiles; the last one takes the checked slow().
@@ -593,212 +752,274 @@ __device__ __forceinline__ void walk(TL& sc, unsigned char* rs, const typename T
       __syncthreads();
       sc.template put<NT>(rs, ti.tid);
       const bool last = bt + 1 == ti.nbt;
-      if (!last) sc.template fetch<NT>(rbase, ti.nb, bt + 1, ti.tid);
+      if (bt + PF < ti.nbt) sc.template fetch<NT>(rbase, ti.nb, bt + PF, ti.tid);
       __syncthreads();
+      sc.template tiles_all<NT, MT>(rs, ti.g, ti.c16, acc);
       if (!last) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          fast(h, mt, bt * TL::TB + mt * 16, sc.template tile<NT>(rs, mt, ti.g, ti.c16));
+        for (int mt = 0; mt < MT; ++mt) fast(h, mt, bt * TL::TB + mt * 16, acc[mt]);
       } else {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int b0 = bt * TL::TB + mt * 16;
           if (b0 >= ti.nb) break;
-          slow(h, mt, b0, sc.template tile<NT>(rs, mt, ti.g, ti.c16));
+          slow(h, mt, b0, acc[mt]);
         }
       }
     }
   }
 }
 
-// MINW: waves per SIMD the register budget is sized for.
-template <typename TL, int KL, int GM, int CAP, int MINW>
-__global__ __launch_bounds__(256, MINW) void coarse_select_kernel(const typename TL::QT* __restrict__ q,
-                                                                  const typename TL::Src* __restrict__ rsrc,
-                                                                  int32_t* __restrict__ idx, int n,
-                                                                  int topk, const HeadBudget budget,
-                                                                  int causal) {
-  constexpr int MT = TL::TB / 16;     // MFMA tiles per R tile
+// MINW: waves per SIMD the register budget is sized for.  NW waves per
+// workgroup, QG query groups of 16 per wave.
+// The tile type of the hi-only first pass: bf16 planes take 64-block R tiles
+// there (one staged term fits the LDS the 32-block three-term tiles use, and
+// each tile gives four independent MFMA chains); fp32 keeps its tiles.
+template <typename TL>
+struct Pass1Tiles {
+  using type = TL;
+};
+template <int D, int QG, int NTH, int TB_, int NTS>
+struct Pass1Tiles<Bf16PlaneTiles<D, QG, NTH, TB_, NTS>> {
+  using type = Bf16PlaneTiles<D, QG, NTH, kPass1Blocks, 1>;
+};
+
+template <typename TL, int KL, int GM, int CAP, int MINW, int QG, int NW>
+__global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const typename TL::QT* __restrict__ q,
+                                                                      const typename TL::Src* __restrict__ rsrc,
+                                                                      int32_t* __restrict__ idx, int n,
+                                                                      int topk, const HeadBudget budget,
+                                                                      int causal) {
+  using TL1 = typename Pass1Tiles<TL>::type;
+  constexpr int NTH = 64 * NW;
+  constexpr int MT = TL1::TB / 16;    // MFMA tiles per R tile of pass 1
   constexpr int NS = 16 * GM;         // group slots per lane
-  constexpr int NH = NS / (4 * MT);   // R tiles per cycle of slots
+  constexpr int NH = NS / (4 * MT) > 0 ? NS / (4 * MT) : 1;  // R tiles per cycle of slots
+  static_assert(NS % (4 * MT) == 0, "a cycle of slots covers whole R tiles");
+  constexpr int ROWS = 16 * QG * NW;  // queries per workgroup
   // The R tile buffer also holds the scratch of the pass-1 error bound and,
-  // at the end, the selection lists (64 rows of 33) and a slot per lane.
-  constexpr int LIST_BYTES = (64 * 33 + 256) * 4;
-  constexpr int RS_BYTES = TL::LDS_BYTES > LIST_BYTES ? TL::LDS_BYTES : LIST_BYTES;
-  static_assert(TL::LDS_BYTES >= 256 * 16 + 128 * 4, "scratch of the pass-1 error bound");
+  // at the end, the selection lists (a row of 33 per query) and a slot per
+  // lane.
+  constexpr int LIST_BYTES = (ROWS * 33 + NTH) * 4;
+  constexpr int ERR_BYTES = NTH * 16 + 128 * 4;
+  constexpr int RS_T = TL::LDS_BYTES > TL1::LDS_BYTES ? TL::LDS_BYTES : TL1::LDS_BYTES;
+  constexpr int RS0 = RS_T > LIST_BYTES ? RS_T : LIST_BYTES;
+  constexpr int RS_BYTES = RS0 > ERR_BYTES ? RS0 : ERR_BYTES;
   static_assert(CAP <= 32, "candidate slots are tracked in a 32-bit mask");
   __shared__ __attribute__((aligned(16))) unsigned char rs[RS_BYTES];
-  // per lane: candidate scores and blocks
-  __shared__ float cv[4][CAP][64];
-  __shared__ uint16_t cb[4][CAP][64];
-  const TileInfo ti(0, n, causal, TL::TB);
-  TL sc;
-  sc.load_q(q, ti.qrow, ti.g);
+  // per lane and query group: candidate scores and blocks
+  __shared__ float cv[NW][QG][CAP][64];
+  __shared__ uint16_t cb[NW][QG][CAP][64];
+  const SelInfo<QG> ti(n, causal, TL::TB, NW);
+  const SelInfo<QG> ti1(n, causal, TL1::TB, NW);  // the same rows, walked in pass-1 tiles
   const auto* rbase = TL::head_base(rsrc, ti.bh, ti.nb);
   const int kh = budget.k[ti.bh % budget.heads];  // this head's budget (<= topk <= KL)
-  const int keff = kh < ti.nvalid ? kh : ti.nvalid;
+  int keff[QG];
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq) keff[gq] = kh < ti.nvalid[gq] ? kh : ti.nvalid[gq];
 
   // pass 1: group maxima.  The lane's block 16 (MT bt + mt) + 4 g + j goes to
   // slot 4 ((MT bt + mt) mod 4 GM) + j: G = 64 GM groups over the 4 lanes.
-  float a[NS];
+  float a[QG][NS];
 #pragma unroll
-  for (int u = 0; u < NS; ++u) a[u] = -INFINITY;
-  auto group_max = [&](bool checked, int h, int mt, int b0, const f32x4& acc) {
+  for (int gq = 0; gq < QG; ++gq)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float x = checked ? ti.cand(acc[j], b0 + 4 * ti.g + j) : acc[j];
-      a[4 * (MT * h + mt) + j] = fmaxf(a[4 * (MT * h + mt) + j], x);
-    }
+    for (int u = 0; u < NS; ++u) a[gq][u] = -INFINITY;
+  auto group_max = [&](bool checked, int h, int mt, int b0, const f32x4 (&acc)[QG]) {
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = checked ? ti.cand(gq, acc[gq][j], b0 + 4 * ti.g + j) : acc[gq][j];
+        a[gq][4 * (MT * h + mt) + j] = fmaxf(a[gq][4 * (MT * h + mt) + j], x);
+      }
   };
-  walk<NH, 1>(sc, rs, rbase, ti,
-              [&](int h, int mt, int b0, const f32x4& acc) { group_max(false, h, mt, b0, acc); },
-              [&](int h, int mt, int b0, const f32x4& acc) { group_max(true, h, mt, b0, acc); });
-  sort_desc<NS>(a);
-  // pass 1 may run on approximate scores (bf16: the hi term alone); lowering
-  // the bound by their error keeps it a bound for the exact scores
-  const float err = sc.pass1_error(rs, ti.tid, ti.lane, ti.g);
-  const float tau = kth_of_lanes<NS>(a, keff, ti.lane) - err;
+  float err[QG], tau[QG];
+  {
+    TL1 sc1;
+    sc1.load_q(q, ti.qrow0, ti.g);
+    walk<NH, 1, QG, NTH>(sc1, rs, rbase, ti1,
+                         [&](int h, int mt, int b0, const f32x4 (&acc)[QG]) { group_max(false, h, mt, b0, acc); },
+                         [&](int h, int mt, int b0, const f32x4 (&acc)[QG]) { group_max(true, h, mt, b0, acc); });
+    // pass 1 may run on approximate scores (bf16: the hi term alone); lowering
+    // the bound by their error keeps it a bound for the exact scores
+    sc1.pass1_error(rs, ti.tid, ti.lane, ti.g, err);
+  }
+  TL sc;
+  sc.load_q(q, ti.qrow0, ti.g);
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq) {
+    sort_desc<NS>(a[gq]);
+    tau[gq] = kth_of_lanes<NS>(a[gq], keff[gq], ti.lane) - err[gq];
+  }
 
   // pass 2: the candidates >= tau, in ascending block order
-  int cnt = 0;
-  auto append = [&](bool checked, int b0, const f32x4& acc) {
+  int cnt[QG];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int beta = b0 + 4 * ti.g + j;
-      const float x = checked ? ti.cand(acc[j], beta) : acc[j];
-      if (x >= tau) {
-        if (cnt < CAP) {
-          cv[ti.wave][cnt][ti.lane] = x;
-          cb[ti.wave][cnt][ti.lane] = static_cast<uint16_t>(beta);
+  for (int gq = 0; gq < QG; ++gq) cnt[gq] = 0;
+  auto append = [&](bool checked, int b0, const f32x4 (&acc)[QG]) {
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int beta = b0 + 4 * ti.g + j;
+        const float x = checked ? ti.cand(gq, acc[gq][j], beta) : acc[gq][j];
+        // past CAP candidates the lane overwrites its last slot: the count
+        // still grows, and a count above CAP sends the workgroup to the
+        // exact redo below
+        const int slot = cnt[gq] < CAP ? cnt[gq] : CAP - 1;
+        if (x >= tau[gq]) {
+          cv[ti.wave][gq][slot][ti.lane] = x;
+          cb[ti.wave][gq][slot][ti.lane] = static_cast<uint16_t>(beta);
+          ++cnt[gq];
         }
-        ++cnt;
       }
-    }
   };
-  walk<1, kTerms>(sc, rs, rbase, ti, [&](int, int, int b0, const f32x4& acc) { append(false, b0, acc); },
-                  [&](int, int, int b0, const f32x4& acc) { append(true, b0, acc); });
-  const int redo = __syncthreads_or(cnt > CAP || sum4(cnt, ti.lane) < keff);
-  int32_t* dst = idx + ti.qrow * topk;
+  walk<1, kTerms, QG, NTH>(sc, rs, rbase, ti,
+                           [&](int, int, int b0, const f32x4 (&acc)[QG]) { append(false, b0, acc); },
+                           [&](int, int, int b0, const f32x4 (&acc)[QG]) { append(true, b0, acc); });
+  bool bad = false;
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq) bad = bad || cnt[gq] > CAP || sum4(cnt[gq], ti.lane) < keff[gq];
+  const int redo = __syncthreads_or(bad);
 
   if (!redo) {
-    // The lane's candidate scores, read once into registers (-inf past cnt),
-    // in ascending block order.
-    const float(&lv)[CAP][64] = cv[ti.wave];
-    const uint16_t(&lb)[CAP][64] = cb[ti.wave];
-    float x[CAP];
 #pragma unroll
-    for (int i = 0; i < CAP; ++i) x[i] = i < cnt ? lv[i][ti.lane] : -INFINITY;
-    // T = the keff-th largest candidate score of the query: every lane sorts
-    // a copy of its scores, two pairwise merges give all 4 lanes the query's
-    // top CAP.
-    float c[CAP];
+    for (int gq = 0; gq < QG; ++gq) {
+      int32_t* dst = idx + (ti.qrow0 + 16 * gq) * topk;
+      const int kq = keff[gq];
+      // The lane's candidate scores, read once into registers (-inf past cnt),
+      // in ascending block order.
+      const float(&lv)[CAP][64] = cv[ti.wave][gq];
+      const uint16_t(&lb)[CAP][64] = cb[ti.wave][gq];
+      float x[CAP];
 #pragma unroll
-    for (int i = 0; i < CAP; ++i) c[i] = x[i];
-    sort_desc<CAP>(c);
-    merge_top<16, CAP>(c, ti.lane);
-    merge_top<32, CAP>(c, ti.lane);
-    const float T = kth_desc<CAP>(c, keff);
-    // Selected: scores above T, and the lowest-block `need` of those equal to
-    // T; when exactly `need` candidates equal T (the usual case) all are.
-    int gt = 0, eq = 0;
+      for (int i = 0; i < CAP; ++i) x[i] = i < cnt[gq] ? lv[i][ti.lane] : -INFINITY;
+      // T = the keff-th largest candidate score of the query: every lane sorts
+      // a copy of its scores, two pairwise merges give all 4 lanes the query's
+      // top CAP.
+      float c[CAP];
 #pragma unroll
-    for (int i = 0; i < CAP; ++i) {
-      gt += x[i] > T ? 1 : 0;
-      eq += x[i] == T ? 1 : 0;
-    }
-    const int need = keff - sum4(gt, ti.lane);
-    const bool all_ties = sum4(eq, ti.lane) == need;
-    uint32_t selbits = 0u;
-#pragma unroll
-    for (int i = 0; i < CAP; ++i) selbits |= (x[i] > T || (x[i] == T && all_ties)) ? (1u << i) : 0u;
-    const int cnt16 = static_cast<int>(lane_xor<16>(static_cast<uint32_t>(cnt), ti.lane));
-    const int cnt32 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(cnt), ti.lane));
-    const int cnt48 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(cnt16), ti.lane));
-    if (!all_ties) {
-      // A tie's rank among the query's ties = ties before it in its own lane
-      // (ascending blocks) + ties with lower blocks in the other 3 lanes.
-      int ties_before = 0;
+      for (int i = 0; i < CAP; ++i) c[i] = x[i];
+      sort_desc<CAP>(c);
+      merge_top<16, CAP>(c, ti.lane);
+      merge_top<32, CAP>(c, ti.lane);
+      const float T = kth_desc<CAP>(c, kq);
+      // Selected: scores above T, and the lowest-block `need` of those equal
+      // to T; when exactly `need` candidates equal T (the usual case) all are.
+      int gt = 0, eq = 0;
 #pragma unroll
       for (int i = 0; i < CAP; ++i) {
-        if (x[i] == T) {
-          int r = ties_before++;
-          for (int m = 1; m < 4; ++m) {
-            const int ln = ti.lane ^ (16 * m);
-            const int cn = m == 1 ? cnt16 : m == 2 ? cnt32 : cnt48;
-            for (int jj = 0; jj < cn; ++jj) r += (lv[jj][ln] == T && lb[jj][ln] < lb[i][ti.lane]) ? 1 : 0;
+        gt += x[i] > T ? 1 : 0;
+        eq += x[i] == T ? 1 : 0;
+      }
+      const int need = kq - sum4(gt, ti.lane);
+      const bool all_ties = sum4(eq, ti.lane) == need;
+      uint32_t selbits = 0u;
+#pragma unroll
+      for (int i = 0; i < CAP; ++i) selbits |= (x[i] > T || (x[i] == T && all_ties)) ? (1u << i) : 0u;
+      const int cn = cnt[gq];
+      const int cnt16 = static_cast<int>(lane_xor<16>(static_cast<uint32_t>(cn), ti.lane));
+      const int cnt32 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(cn), ti.lane));
+      const int cnt48 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(cnt16), ti.lane));
+      if (!all_ties) {
+        // A tie's rank among the query's ties = ties before it in its own lane
+        // (ascending blocks) + ties with lower blocks in the other 3 lanes.
+        int ties_before = 0;
+#pragma unroll
+        for (int i = 0; i < CAP; ++i) {
+          if (x[i] == T) {
+            int r = ties_before++;
+            for (int m = 1; m < 4; ++m) {
+              const int ln = ti.lane ^ (16 * m);
+              const int cm = m == 1 ? cnt16 : m == 2 ? cnt32 : cnt48;
+              for (int jj = 0; jj < cm; ++jj) r += (lv[jj][ln] == T && lb[jj][ln] < lb[i][ti.lane]) ? 1 : 0;
+            }
+            selbits |= r < need ? (1u << i) : 0u;
           }
-          selbits |= r < need ? (1u << i) : 0u;
         }
       }
-    }
-    // The query's selection into its row of an LDS list (the R tile buffer
-    // is free now), this lane's part after those of lanes g' < g; a lane
-    // writes unselected entries to a slot of its own.
-    const int ns = __popc(selbits);
-    const int n16 = static_cast<int>(lane_xor<16>(static_cast<uint32_t>(ns), ti.lane));
-    const int n32 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(ns), ti.lane));
-    const int n48 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(n16), ti.lane));
-    int p = ((ti.g & 1) ? n16 : 0) + ((ti.g & 2) ? n32 + n48 : 0);
-    int* list = reinterpret_cast<int*>(rs) + (ti.wave * 16 + ti.c16) * 33;  // odd pitch: no bank conflicts
-    int* own = reinterpret_cast<int*>(rs) + 64 * 33 + ti.tid;
+      // The query's selection into its row of an LDS list (the R tile buffer
+      // is free now), this lane's part after those of lanes g' < g; a lane
+      // writes unselected entries to a slot of its own.
+      const int ns = __popc(selbits);
+      const int n16 = static_cast<int>(lane_xor<16>(static_cast<uint32_t>(ns), ti.lane));
+      const int n32 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(ns), ti.lane));
+      const int n48 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(n16), ti.lane));
+      int p = ((ti.g & 1) ? n16 : 0) + ((ti.g & 2) ? n32 + n48 : 0);
+      const int qslot = 16 * (QG * ti.wave + gq) + ti.c16;
+      int* list = reinterpret_cast<int*>(rs) + qslot * 33;  // odd pitch: no bank conflicts
+      int* own = reinterpret_cast<int*>(rs) + ROWS * 33 + ti.tid;
 #pragma unroll
-    for (int i = 0; i < CAP; ++i) {
-      const bool s = (selbits >> i) & 1u;
-      *(s ? list + p : own) = lb[i][ti.lane];
-      p += s ? 1 : 0;
-    }
-    __syncthreads();
-    // Every lane of the query sorts the query's keff blocks (-1 from keff up
-    // to topk).  Rows of whole 16-byte chunks: lane g stores chunks g, g + 4,
-    // ..., so one store writes a 64-byte stretch of the row; otherwise lane g
-    // writes entries g, g + 4, ...
-    int b[KL];
-#pragma unroll
-    for (int u = 0; u < KL; ++u) b[u] = u < keff ? list[u] : 0x7fffffff;
-    sort_asc<KL>(b);
-#pragma unroll
-    for (int u = 0; u < KL; ++u) b[u] = u < keff ? b[u] : -1;
-    if (((reinterpret_cast<uintptr_t>(dst) | static_cast<uintptr_t>(topk) * 4u) & 15u) == 0) {
-#pragma unroll
-      for (int c0 = 0; c0 < KL / 4; c0 += 4) {
-        int v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = b[4 * c0 + i];
-#pragma unroll
-          for (int h = 1; h < 4; ++h)
-            if (4 * (c0 + h) + i < KL) v[i] = ti.g == h ? b[4 * (c0 + h) + i] : v[i];
-        }
-        const int c = c0 + ti.g;
-        if (c < KL / 4 && 4 * c < topk) *reinterpret_cast<int4*>(dst + 4 * c) = make_int4(v[0], v[1], v[2], v[3]);
+      for (int i = 0; i < CAP; ++i) {
+        const bool sel = (selbits >> i) & 1u;
+        *(sel ? list + p : own) = lb[i][ti.lane];
+        p += sel ? 1 : 0;
       }
-    } else {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      // Every lane of the query sorts the query's keff blocks (-1 from keff
+      // up to topk).  Rows of whole 16-byte chunks: lane g stores chunks g,
+      // g + 4, ..., so one store writes a 64-byte stretch of the row;
+      // otherwise lane g writes entries g, g + 4, ...
+      int b[KL];
 #pragma unroll
-      for (int t0 = 0; t0 < KL; t0 += 4) {
-        int me = b[t0];
+      for (int u = 0; u < KL; ++u) b[u] = u < kq ? list[u] : 0x7fffffff;
+      sort_asc<KL>(b);
 #pragma unroll
-        for (int e = 1; e < 4; ++e) me = ti.g == e ? b[t0 + e] : me;
-        const int t = t0 + ti.g;
-        if (t < topk) dst[t] = me;
+      for (int u = 0; u < KL; ++u) b[u] = u < kq ? b[u] : -1;
+      if (((reinterpret_cast<uintptr_t>(dst) | static_cast<uintptr_t>(topk) * 4u) & 15u) == 0) {
+#pragma unroll
+        for (int c0 = 0; c0 < KL / 4; c0 += 4) {
+          int v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] = b[4 * c0 + i];
+#pragma unroll
+            for (int hh = 1; hh < 4; ++hh)
+              if (4 * (c0 + hh) + i < KL) v[i] = ti.g == hh ? b[4 * (c0 + hh) + i] : v[i];
+          }
+          const int cc = c0 + ti.g;
+          if (cc < KL / 4 && 4 * cc < topk) *reinterpret_cast<int4*>(dst + 4 * cc) = make_int4(v[0], v[1], v[2], v[3]);
+        }
+      } else {
+#pragma unroll
+        for (int t0 = 0; t0 < KL; t0 += 4) {
+          int me = b[t0];
+#pragma unroll
+          for (int e = 1; e < 4; ++e) me = ti.g == e ? b[t0 + e] : me;
+          const int t = t0 + ti.g;
+          if (t < topk) dst[t] = me;
+        }
       }
     }
   } else {
     // slots overflowed somewhere in the workgroup: offer every score to
-    // exact register lists and merge them pairwise
-    TopList<KL> l;
-    l.init();
-    walk<1, kTerms>(sc, rs, rbase, ti,
-         [&](int, int, int b0, const f32x4& acc) {
+    // exact register lists and merge them pairwise, one query group at a time
 #pragma unroll
-           for (int j = 0; j < 4; ++j) l.offer(acc[j], b0 + 4 * ti.g + j);
-         },
-         [&](int, int, int b0, const f32x4& acc) {
+    for (int gq = 0; gq < QG; ++gq) {
+      TopList<KL> l;
+      l.init();
+      walk<1, kTerms, QG, NTH>(sc, rs, rbase, ti,
+           [&](int, int, int b0, const f32x4 (&acc)[QG]) {
+             f32x4 v = acc[0];
 #pragma unroll
-           for (int j = 0; j < 4; ++j) l.offer(ti.cand(acc[j], b0 + 4 * ti.g + j), b0 + 4 * ti.g + j);
-         });
-    merge_top<16, KL>(l.v, l.b, ti.lane);
-    merge_top<32, KL>(l.v, l.b, ti.lane);
-    emit_selection<KL>(l.b, ti.g, keff, topk, dst);
+             for (int e = 1; e < QG; ++e) v = gq == e ? acc[e] : v;
+#pragma unroll
+             for (int j = 0; j < 4; ++j) l.offer(v[j], b0 + 4 * ti.g + j);
+           },
+           [&](int, int, int b0, const f32x4 (&acc)[QG]) {
+             f32x4 v = acc[0];
+#pragma unroll
+             for (int e = 1; e < QG; ++e) v = gq == e ? acc[e] : v;
+#pragma unroll
+             for (int j = 0; j < 4; ++j) l.offer(ti.cand(gq, v[j], b0 + 4 * ti.g + j), b0 + 4 * ti.g + j);
+           });
+      merge_top<16, KL>(l.v, l.b, ti.lane);
+      merge_top<32, KL>(l.v, l.b, ti.lane);
+      emit_selection<KL>(l.b, ti.g, keff[gq], topk, idx + (ti.qrow0 + 16 * gq) * topk);
+    }
   }
 }
 
@@ -811,21 +1032,31 @@ void launch_panel(const void* q, const void* rsrc, float* panel, int64_t row0, i
                      panel, row0, rows, n, causal);
 }
 
-template <typename TL, int KL, int GM, int CAP, int MINW>
+template <typename TL, int KL, int GM, int CAP, int MINW, int QG, int NW>
 void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
                    const HeadBudget& hb, int causal, hipStream_t s) {
-  hipLaunchKernelGGL((coarse_select_kernel<TL, KL, GM, CAP, MINW>), dim3(static_cast<unsigned>(rows / kTile)),
-                     dim3(256), 0, s, static_cast<const typename TL::QT*>(q),
+  constexpr int ROWS = 16 * QG * NW;
+  hipLaunchKernelGGL((coarse_select_kernel<TL, KL, GM, CAP, MINW, QG, NW>), dim3(static_cast<unsigned>(rows / ROWS)),
+                     dim3(64 * NW), 0, s, static_cast<const typename TL::QT*>(q),
                      static_cast<const typename TL::Src*>(rsrc), idx, n, topk, hb, causal);
 }
 
-template <typename TL>
+// One 16-query group per wave, four waves per workgroup; the register budget
+// allows 4 waves per SIMD for bf16 d = 64 and k <= 16, else 3 (2 for k > 16,
+// whose candidate lists are twice as long).
+template <template <int, int, int> class TLT, int D>
 void launch_select_k(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
                      const HeadBudget& hb, int causal, hipStream_t s) {
-  if (topk <= 8) launch_select<TL, 8, 1, 8, 4>(q, rsrc, idx, rows, n, topk, hb, causal, s);
-  else if (topk <= 16) launch_select<TL, 16, 1, 16, 4>(q, rsrc, idx, rows, n, topk, hb, causal, s);
-  else launch_select<TL, 32, 2, 32, 2>(q, rsrc, idx, rows, n, topk, hb, causal, s);
+  constexpr int M1 = (D == 64 && std::is_same<typename TLT<D, 1, 256>::QT, bf16_bits>::value) ? 4 : 3;
+  if (topk <= 8) launch_select<TLT<D, 1, 256>, 8, 1, 8, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, s);
+  else if (topk <= 16) launch_select<TLT<D, 1, 256>, 16, 1, 16, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, s);
+  else launch_select<TLT<D, 1, 256>, 32, 2, 32, 2, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, s);
 }
+
+template <int D, int QG, int NTH>
+using PlaneT = Bf16PlaneTiles<D, QG, NTH>;
+template <int D, int QG, int NTH>
+using F32T = F32Tiles<D, 32, QG, NTH>;
 
 }  // namespace
 
@@ -846,11 +1077,11 @@ hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t
                                 int32_t* idx, int64_t rows, int n, int d, bsa_dtype dtype,
                                 int topk, const HeadBudget& hb, int causal, hipStream_t stream) {
   if (dtype == BSA_BF16) {
-    if (d == 64) launch_select_k<Bf16PlaneTiles<64>>(q, repr_split, idx, rows, n, topk, hb, causal, stream);
-    else launch_select_k<Bf16PlaneTiles<128>>(q, repr_split, idx, rows, n, topk, hb, causal, stream);
+    if (d == 64) launch_select_k<PlaneT, 64>(q, repr_split, idx, rows, n, topk, hb, causal, stream);
+    else launch_select_k<PlaneT, 128>(q, repr_split, idx, rows, n, topk, hb, causal, stream);
   } else {
-    if (d == 64) launch_select_k<F32Tiles<64, 32>>(q, repr, idx, rows, n, topk, hb, causal, stream);
-    else launch_select_k<F32Tiles<128, 32>>(q, repr, idx, rows, n, topk, hb, causal, stream);
+    if (d == 64) launch_select_k<F32T, 64>(q, repr, idx, rows, n, topk, hb, causal, stream);
+    else launch_select_k<F32T, 128>(q, repr, idx, rows, n, topk, hb, causal, stream);
   }
   return hipGetLastError();
 }
