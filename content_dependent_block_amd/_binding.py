@@ -58,6 +58,9 @@ _sig("bsa_forward_budgets", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P,
 _sig("bsa_forward_train", [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _I, _F, _I, _P])
 _sig("bsa_backward", [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                       _P])
+_sig("bsa_forward_varlen", [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _I, _F, _I, _P])
+_sig("bsa_backward_varlen", [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _F, _I,
+                             _P])
 _sig("bsa_fine_forward", [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P])
 _sig("bsa_block_pool", [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P])
 _sig("bsa_coarse_score", [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _P])
@@ -74,7 +77,7 @@ _sig("bsa_profile_read", [_P, _P, _P, _I])
 EXPORTED = ("bsa_create", "bsa_destroy", "bsa_status_string", "bsa_last_error", "bsa_set_option",
             "bsa_workspace_bytes", "bsa_forward", "bsa_forward_noalloc", "bsa_forward_budgets",
             "bsa_forward_train",
-            "bsa_backward", "bsa_fine_forward",
+            "bsa_backward", "bsa_forward_varlen", "bsa_backward_varlen", "bsa_fine_forward",
             "bsa_block_pool",
             "bsa_coarse_score", "bsa_topk_select", "bsa_tiles_create", "bsa_tiles_destroy",
             "bsa_forward_static", "bsa_tiles_from_mask",
@@ -242,6 +245,69 @@ def bsa_backward(h, q, k, v, out, dout, block_idx, lse, dq, dk, dv, *, block: in
             _need(dk, "dk", q.shape, f32, dev), _need(dv, "dv", q.shape, f32, dev)]
     _check(_lib.bsa_backward(h, pq, pk, pv, *args, b, hh, n, d, _dtype_code(q), block, topk,
                              float(scale), int(causal), _stream(stream, dev)), h)
+
+
+def _cu_seqlens(cu_seqlens):
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int32).reshape(-1))
+    if cu.size < 2:
+        raise ValueError("cu_seqlens needs nseq + 1 >= 2 entries")
+    return cu, cu.size - 1, int(cu[-1])
+
+
+def _qkv_varlen(q, k, v, total):
+    if q.dim() != 3:
+        raise ValueError("q must be [heads, total, d] for a variable-length batch")
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on a HIP device")
+    if q.shape[1] != total:
+        raise ValueError(f"q has {q.shape[1]} rows per head, cu_seqlens ends at {total}")
+    pq = _need(q, "q", q.shape, None, dev)
+    pk = _need(k, "k", q.shape, q.dtype, dev)
+    pv = _need(v, "v", q.shape, q.dtype, dev)
+    return pq, pk, pv, dev
+
+
+def bsa_forward_varlen(h, q, k, v, out, cu_seqlens, block_idx_out=None, lse_out=None, *, topk: int,
+                       head_topk=None, block: int = 64, scale: float, causal: bool = False,
+                       stream=None) -> None:
+    """Both stages over a batch of sequences of different lengths: q, k, v
+    [heads, total, d], sequence i = rows cu_seqlens[i] .. cu_seqlens[i+1]-1 of
+    every head; block_idx_out [heads, total, topk] (block numbers from each
+    sequence's first block), lse_out [heads, total] (both optional)."""
+    cu, nseq, total = _cu_seqlens(cu_seqlens)
+    pq, pk, pv, dev = _qkv_varlen(q, k, v, total)
+    hh, _, d = q.shape
+    po = _need(out, "out", q.shape, torch.float32, dev)
+    pi = None if block_idx_out is None else _need(block_idx_out, "block_idx_out", (hh, total, topk),
+                                                  torch.int32, dev)
+    pl = None if lse_out is None else _need(lse_out, "lse_out", (hh, total), torch.float32, dev)
+    pk_ = None
+    if head_topk is not None:
+        ks = np.ascontiguousarray(np.asarray(head_topk, dtype=np.int32).reshape(-1))
+        if ks.size != hh:
+            raise ValueError(f"head_topk needs {hh} entries, got {ks.size}")
+        pk_ = ks.ctypes.data
+    _check(_lib.bsa_forward_varlen(h, pq, pk, pv, po, pi, pl, cu.ctypes.data, nseq, hh, d, _dtype_code(q),
+                                   block, pk_, int(topk), float(scale), int(causal), _stream(stream, dev)), h)
+
+
+def bsa_backward_varlen(h, q, k, v, out, dout, block_idx, lse, dq, dk, dv, cu_seqlens, *, block: int = 64,
+                        scale: float, causal: bool = False, stream=None) -> None:
+    """Gradients of q, k, v for a batch laid out as for bsa_forward_varlen."""
+    cu, nseq, total = _cu_seqlens(cu_seqlens)
+    pq, pk, pv, dev = _qkv_varlen(q, k, v, total)
+    hh, _, d = q.shape
+    if block_idx.dim() != 3:
+        raise ValueError("block_idx must be [heads, total, topk]")
+    topk = block_idx.shape[-1]
+    f32 = torch.float32
+    args = [_need(out, "out", q.shape, f32, dev), _need(dout, "dout", q.shape, f32, dev),
+            _need(block_idx, "block_idx", (hh, total, topk), torch.int32, dev),
+            _need(lse, "lse", (hh, total), f32, dev), _need(dq, "dq", q.shape, f32, dev),
+            _need(dk, "dk", q.shape, f32, dev), _need(dv, "dv", q.shape, f32, dev)]
+    _check(_lib.bsa_backward_varlen(h, pq, pk, pv, *args, cu.ctypes.data, nseq, hh, d, _dtype_code(q), block,
+                                    topk, float(scale), int(causal), _stream(stream, dev)), h)
 
 
 def bsa_fine_forward(h, q, k, v, out, block_idx, *, block: int = 64, scale: float,

@@ -8,9 +8,10 @@
 // kernel reads K exactly once and writes the float32 representatives, so it is
 // bound by HBM bandwidth.
 //
-// When the sequence length is not a multiple of 64 the keys come padded with
-// zero rows to whole blocks, and the last block of each head is the mean of
-// its `last` valid keys (the sum over the padded block, divided by `last`).
+// When a sequence's length is not a multiple of 64 its keys come padded with
+// zero rows to whole blocks, and its last block is the mean of the keys that
+// exist (the sum over the padded block, divided by their count, which the
+// block table gives).
 //
 // Optionally it also writes each representative r as three bfloat16 terms
 // hi + mid + lo (hi = bf16(r), mid = bf16(r - hi), lo = bf16(r - hi - mid)),
@@ -27,7 +28,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k,
                                                          float* __restrict__ repr,
                                                          bf16_bits* __restrict__ split,
-                                                         int64_t total_blocks, int nb, int last) {
+                                                         int64_t total_blocks, int nb,
+                                                         const int4* __restrict__ seqtab) {
   constexpr int E = 16 / sizeof(T);     // elements per 16-byte chunk
   constexpr int LPR = D / E;            // lanes per key row
   constexpr int RPL = kWave / LPR;      // rows per wave-wide load
@@ -65,9 +67,10 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k
     for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], s);
   }
   if (ro == 0) {
-    if (last < kTile && blk % nb == nb - 1) {  // a partial last block: mean of its valid keys
+    const int keys = block_keys(seqtab, static_cast<int>(blk % nb));
+    if (keys < kTile) {  // a sequence's partial last block: mean of the keys that exist
 #pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] = acc[e] / static_cast<float>(last);
+      for (int e = 0; e < E; ++e) acc[e] = acc[e] / static_cast<float>(keys);
     } else {
       constexpr float inv = 1.0f / kTile;  // exact: a power of two
 #pragma unroll
@@ -105,27 +108,26 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k
 }
 
 template <typename T, int D>
-hipError_t launch(const void* k, float* repr, bf16_bits* split, int64_t blocks, int nb, int last,
-                  hipStream_t s) {
+hipError_t launch(const void* k, float* repr, bf16_bits* split, int64_t blocks, int nb,
+                  const int4* seqtab, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((blocks + 3) / 4));
   hipLaunchKernelGGL((block_pool_kernel<T, D>), grid, dim3(256), 0, s,
-                     static_cast<const T*>(k), repr, split, blocks, nb, last);
+                     static_cast<const T*>(k), repr, split, blocks, nb, seqtab);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_block_pool(const void* k, float* repr, uint16_t* split, int64_t bh, int n, int d,
-                             bsa_dtype dtype, hipStream_t stream, int nv) {
+                             bsa_dtype dtype, hipStream_t stream, const int4* seqtab) {
   const int nb = n / kTile;
   const int64_t blocks = bh * nb;
-  const int last = (nv > 0 && nv < n) ? nv - (nb - 1) * kTile : kTile;
   if (dtype == BSA_BF16) {
-    return d == 64 ? launch<bf16_bits, 64>(k, repr, split, blocks, nb, last, stream)
-                   : launch<bf16_bits, 128>(k, repr, split, blocks, nb, last, stream);
+    return d == 64 ? launch<bf16_bits, 64>(k, repr, split, blocks, nb, seqtab, stream)
+                   : launch<bf16_bits, 128>(k, repr, split, blocks, nb, seqtab, stream);
   }
-  return d == 64 ? launch<float, 64>(k, repr, split, blocks, nb, last, stream)
-                 : launch<float, 128>(k, repr, split, blocks, nb, last, stream);
+  return d == 64 ? launch<float, 64>(k, repr, split, blocks, nb, seqtab, stream)
+                 : launch<float, 128>(k, repr, split, blocks, nb, seqtab, stream);
 }
 
 }  // namespace bsa

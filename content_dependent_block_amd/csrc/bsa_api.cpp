@@ -43,7 +43,14 @@ struct bsa_handle_s {
   Buf g_count, g_offsets, g_items, g_item_rec, g_rank, g_rec, g_wgv, g_list, g_po;
   Buf b_ld, b_dq, b_dkv, b_dob;
   bool counts_zero = false;  // g_count holds zeros (the bucketing's scan leaves it so)  // backward: per-row (lse, delta), per-pair dq, per-item dk/dv, bf16 dout
-  Buf r_q, r_k, r_v, r_o, r_do, r_lse, r_idx, r_dq, r_dk, r_dv;  // padded copies (ragged n)
+  Buf r_q, r_k, r_v, r_o, r_do, r_lse, r_idx, r_dq, r_dk, r_dv;  // padded copies (ragged lengths)
+  // block table of sequences padded to whole blocks: device copy, pinned
+  // staging copy, and an event on the last upload from the staging copy
+  Buf tab;
+  void* tab_host = nullptr;
+  size_t tab_host_bytes = 0;
+  hipEvent_t tab_ev = nullptr;
+  bool tab_ev_live = false;
   Buf s_part, s_lse;  // static mode: partial rows of split query tiles and their log-sum-exp
   int64_t static_item_tiles = 0;  // 0: chosen per call; else the most key tiles per work item
   // timing
@@ -274,13 +281,15 @@ BSA_API bsa_status bsa_destroy(bsa_handle h) {
     (void)hipEventDestroy(r.b);
   }
   for (auto e : h->free_events) (void)hipEventDestroy(e);
+  if (h->tab_ev) (void)hipEventDestroy(h->tab_ev);
+  if (h->tab_host) (void)hipHostFree(h->tab_host);
   if (h->repr) (void)hipFree(h->repr);
   if (h->split) (void)hipFree(h->split);
   if (h->panel) (void)hipFree(h->panel);
   if (h->idx) (void)hipFree(h->idx);
   for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_rec, &h->g_wgv, &h->g_list, &h->g_po,
                  &h->b_ld, &h->b_dq, &h->b_dkv, &h->b_dob, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
-                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv, &h->s_part, &h->s_lse})
+                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv, &h->s_part, &h->s_lse, &h->tab})
     if (b->p) (void)hipFree(b->p);
   delete h;
   return BSA_OK;
@@ -321,7 +330,7 @@ BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
   *bytes = h->repr_bytes + h->split_bytes + h->panel_bytes + h->idx_bytes;
   for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_rec, &h->g_wgv, &h->g_list, &h->g_po,
                  &h->b_ld, &h->b_dq, &h->b_dkv, &h->b_dob, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
-                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv, &h->s_part, &h->s_lse})
+                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv, &h->s_part, &h->s_lse, &h->tab})
     *bytes += b->bytes;
   return BSA_OK;
 }
@@ -331,23 +340,119 @@ BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
 namespace {
 
 bsa_status run_pool(bsa_handle h, const void* k, float* repr, uint16_t* split, const Shape& s,
-                    bsa_dtype dt, hipStream_t st, int nv = 0) {
+                    bsa_dtype dt, hipStream_t st, const int4* tab = nullptr) {
   return timed_launch(h, BSA_STAGE_POOL, st, "block_pool", [&] {
-    return bsa::launch_block_pool(k, repr, split, s.bh(), s.n, s.d, dt, st, nv);
+    return bsa::launch_block_pool(k, repr, split, s.bh(), s.n, s.d, dt, st, tab);
   });
 }
 
-// Ragged n: copies of caller rows into whole-block buffers and back.
-bsa_status pad_rows(bsa_handle h, const void* src, void* dst, const Shape& s, int words, uint32_t fill,
-                    hipStream_t st) {
-  return timed_launch(h, BSA_STAGE_RAGGED_COPY, st, "ragged-n padding copy", [&] {
-    return bsa::launch_pad_rows(src, dst, s.bh(), s.n, s.padded().n, words, fill, st);
+// The layout the kernels run on: ks.bh() slices (batch x heads, or heads for
+// a variable-length batch) of ks.n rows, ks.n a multiple of 64, every
+// sequence starting on a block boundary.  tab: the block table when a slice
+// is not one sequence of whole blocks (empty otherwise).  copy: the caller's
+// rows (src_rows per slice) must be copied into that layout, some sequence
+// not being whole blocks, and the results copied back.
+struct Plan {
+  Shape ks;
+  int src_rows = 0;
+  bool copy = false;
+  std::vector<int4> tab;
+};
+
+// One sequence of s.n rows per (batch, head).
+Plan plan_dense(const Shape& s) {
+  Plan p;
+  p.ks = s.padded();
+  p.src_rows = s.n;
+  p.copy = p.ks.n != s.n;
+  if (p.copy) {
+    const int nb = p.ks.n / 64;
+    p.tab.resize(size_t(nb));
+    for (int b = 0; b < nb; ++b) p.tab[size_t(b)] = make_int4(0, nb, std::min(64, s.n - 64 * b), 64 * b);
+  }
+  return p;
+}
+
+// Sequences cu[i] .. cu[i + 1] - 1 of the caller's rows of every head.
+bsa_status plan_varlen(bsa_handle h, const char* fn, const int32_t* cu, int nseq, int heads, int d, Plan* p) {
+  if (!cu) return fail(h, BSA_ERR_INVALID_ARG, "%s: cu_seqlens is NULL", fn);
+  if (nseq < 1 || heads < 1)
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: nseq and heads must be >= 1 (got %d, %d)", fn, nseq, heads);
+  if (cu[0] != 0) return fail(h, BSA_ERR_INVALID_ARG, "%s: cu_seqlens[0] must be 0 (got %d)", fn, cu[0]);
+  int64_t blocks = 0;
+  for (int i = 0; i < nseq; ++i) {
+    if (cu[i + 1] < cu[i])
+      return fail(h, BSA_ERR_INVALID_ARG, "%s: cu_seqlens decreases at %d (%d -> %d)", fn, i, cu[i], cu[i + 1]);
+    blocks += (int64_t(cu[i + 1]) - cu[i] + 63) / 64;
+  }
+  if (cu[nseq] < 1) return fail(h, BSA_ERR_INVALID_ARG, "%s: the batch has no rows", fn);
+  if (blocks > 2048)
+    return fail(h, BSA_ERR_UNSUPPORTED, "%s: the sequences take %lld blocks of 64 rows per head; at most 2048",
+                fn, (long long)blocks);
+  p->ks = Shape{1, heads, int(blocks * 64), d};
+  p->src_rows = cu[nseq];
+  p->copy = false;
+  p->tab.assign(size_t(blocks), make_int4(0, 0, 0, 0));
+  int b0 = 0;
+  for (int i = 0; i < nseq; ++i) {
+    const int len = cu[i + 1] - cu[i], nbs = (len + 63) / 64;
+    if (len % 64 != 0) p->copy = true;
+    for (int j = 0; j < nbs; ++j)
+      p->tab[size_t(b0 + j)] = make_int4(b0, b0 + nbs, std::min(64, len - 64 * j), cu[i] + 64 * j);
+    b0 += nbs;
+  }
+  return BSA_OK;
+}
+
+// The plan's block table on the device (NULL when it has none), copied on
+// the stream from a pinned staging buffer; the staging buffer is rewritten
+// only once the previous copy from it has finished.
+bsa_status upload_tab(bsa_handle h, const Plan& p, hipStream_t st, const int4** out) {
+  *out = nullptr;
+  if (p.tab.empty()) return BSA_OK;
+  const size_t bytes = p.tab.size() * sizeof(int4);
+  TRY(grow(h, &h->tab.p, &h->tab.bytes, bytes, "block table"));
+  if (h->tab_ev_live && hipEventSynchronize(h->tab_ev) != hipSuccess)
+    return fail(h, BSA_ERR_LAUNCH, "block table: waiting for the previous upload failed");
+  h->tab_ev_live = false;
+  if (h->tab_host_bytes < bytes) {
+    if (h->tab_host) (void)hipHostFree(h->tab_host);
+    h->tab_host = nullptr;
+    h->tab_host_bytes = 0;
+    if (hipHostMalloc(&h->tab_host, bytes, hipHostMallocDefault) != hipSuccess) {
+      (void)hipGetLastError();
+      h->tab_host = nullptr;
+      return fail(h, BSA_ERR_OUT_OF_MEMORY, "block table: pinned host allocation of %zu bytes failed", bytes);
+    }
+    h->tab_host_bytes = bytes;
+  }
+  std::memcpy(h->tab_host, p.tab.data(), bytes);
+  if (!h->tab_ev && hipEventCreateWithFlags(&h->tab_ev, hipEventDisableTiming) != hipSuccess) {
+    h->tab_ev = nullptr;
+    return fail(h, BSA_ERR_LAUNCH, "block table: could not create an event");
+  }
+  if (hipMemcpyAsync(h->tab.p, h->tab_host, bytes, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipEventRecord(h->tab_ev, st) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(h, BSA_ERR_LAUNCH, "block table: upload failed");
+  }
+  h->tab_ev_live = true;
+  *out = static_cast<const int4*>(h->tab.p);
+  return BSA_OK;
+}
+
+// Copies of caller rows into the plan's layout and back.
+bsa_status pad_rows(bsa_handle h, const void* src, void* dst, const Plan& p, const int4* tab, int words,
+                    uint32_t fill, hipStream_t st) {
+  return timed_launch(h, BSA_STAGE_RAGGED_COPY, st, "padding copy", [&] {
+    return bsa::launch_pad_rows(src, dst, p.ks.bh(), p.src_rows, p.ks.n, words, fill, tab, st);
   });
 }
 
-bsa_status unpad_rows(bsa_handle h, const void* src, void* dst, const Shape& s, int words, hipStream_t st) {
-  return timed_launch(h, BSA_STAGE_RAGGED_COPY, st, "ragged-n copy back", [&] {
-    return bsa::launch_unpad_rows(src, dst, s.bh(), s.n, s.padded().n, words, st);
+bsa_status unpad_rows(bsa_handle h, const void* src, void* dst, const Plan& p, const int4* tab, int words,
+                      hipStream_t st) {
+  return timed_launch(h, BSA_STAGE_RAGGED_COPY, st, "copy back", [&] {
+    return bsa::launch_unpad_rows(src, dst, p.ks.bh(), p.src_rows, p.ks.n, words, tab, st);
   });
 }
 
@@ -393,12 +498,13 @@ bsa_status take(bsa_handle h, Arena* arena, void** out, size_t bytes, const char
 // what is left of it).
 bsa_status run_select(bsa_handle h, const void* q, const float* repr, const uint16_t* split,
                       int32_t* idx, const Shape& s, bsa_dtype dt, int topk,
-                      const bsa::HeadBudget& hb, int causal, hipStream_t st, Arena* arena = nullptr) {
+                      const bsa::HeadBudget& hb, int causal, hipStream_t st, Arena* arena = nullptr,
+                      const int4* tab = nullptr) {
   const int64_t nb = s.n / 64;
   const int64_t total = s.bh() * s.n;
   if (fused_select(h, topk))
     return timed_launch(h, BSA_STAGE_COARSE_TOPK, st, "coarse_select", [&] {
-      return bsa::launch_coarse_select(q, repr, split, idx, total, s.n, s.d, dt, topk, hb, causal, st);
+      return bsa::launch_coarse_select(q, repr, split, idx, total, s.n, s.d, dt, topk, hb, causal, st, tab);
     });
   int64_t chunk = h->panel_chunk_bytes / (nb * 4) / 64 * 64;
   if (arena) {
@@ -422,7 +528,7 @@ bsa_status run_select(bsa_handle h, const void* q, const float* repr, const uint
       return bsa::launch_coarse_score(q, repr, panel, r0, rows, s.n, s.d, dt, causal, st);
     }));
     TRY(timed_launch(h, BSA_STAGE_TOPK, st, "topk_select", [&] {
-      return bsa::launch_topk_select(panel, idx, r0, rows, s.n, topk, hb, causal, st);
+      return bsa::launch_topk_select(panel, idx, r0, rows, s.n, topk, hb, causal, st, tab);
     }));
   }
   return BSA_OK;
@@ -541,13 +647,13 @@ bsa_status run_fine_arena(bsa_handle h, const void* q, const void* k, const void
 // Stage 2 for the dynamic path, with the handle's fine strategy.
 bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, float* out,
                     float* lse, const int32_t* idx, const Shape& s, bsa_dtype dt, int topk,
-                    float scale, int causal, hipStream_t st, int nv = 0, Arena* arena = nullptr) {
-  if (arena && h->fine_strategy == BSA_FINE_BLOCK_GATHER)
+                    float scale, int causal, hipStream_t st, const int4* tab = nullptr, Arena* arena = nullptr) {
+  if (arena && h->fine_strategy == BSA_FINE_BLOCK_GATHER)  // whole-block sequences only (no table)
     return run_fine_arena(h, q, k, v, out, lse, idx, s, dt, topk, scale, causal, st, *arena);
   if (h->fine_strategy == BSA_FINE_QUERY_TILE)
     return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
       return bsa::launch_sparse_flash_dynamic(q, k, v, out, lse, idx, s.bh(), s.n, s.d, topk, scale,
-                                              causal, dt, st, nv);
+                                              causal, dt, st, tab);
     });
   const int64_t total = s.bh() * s.n;
   const size_t per_row = bsa::gather_pair_bytes(s.d, dt) * size_t(topk);
@@ -585,7 +691,7 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   a.scale = scale;
   a.dtype = dt;
   a.qsegs = qsegs;
-  a.nv = nv;
+  a.seqtab = tab;
   a.ws.count = static_cast<int32_t*>(h->g_count.p);
   a.ws.count_words = clear_words;
   a.ws.offsets = static_cast<int32_t*>(h->g_offsets.p);
@@ -680,7 +786,10 @@ BSA_API bsa_status bsa_fine_forward(bsa_handle h, const void* q, const void* k, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (s.n % 64 == 0) return run_fine(h, q, k, v, out, nullptr, block_idx, s, dtype, topk, scale, causal, st);
   // ragged n: whole-block copies; the padding rows select nothing
-  const Shape sp = s.padded();
+  const Plan p = plan_dense(s);
+  const Shape& sp = p.ks;
+  const int4* tab = nullptr;
+  TRY(upload_tab(h, p, st, &tab));
   const size_t in_bytes = size_t(sp.elems()) * elem_bytes(dtype);
   const int w = s.d * elem_bytes(dtype) / 4;
   TRY(grow_buf(h, h->r_q, in_bytes, "padded q"));
@@ -688,20 +797,20 @@ BSA_API bsa_status bsa_fine_forward(bsa_handle h, const void* q, const void* k, 
   TRY(grow_buf(h, h->r_v, in_bytes, "padded v"));
   TRY(grow_buf(h, h->r_o, size_t(sp.elems()) * 4, "padded out"));
   TRY(grow_buf(h, h->r_idx, size_t(sp.bh() * sp.n * topk) * 4, "padded indices"));
-  TRY(pad_rows(h, q, h->r_q.p, s, w, 0u, st));
-  TRY(pad_rows(h, k, h->r_k.p, s, w, 0u, st));
-  TRY(pad_rows(h, v, h->r_v.p, s, w, 0u, st));
-  TRY(pad_rows(h, block_idx, h->r_idx.p, s, topk, 0xFFFFFFFFu, st));
+  TRY(pad_rows(h, q, h->r_q.p, p, tab, w, 0u, st));
+  TRY(pad_rows(h, k, h->r_k.p, p, tab, w, 0u, st));
+  TRY(pad_rows(h, v, h->r_v.p, p, tab, w, 0u, st));
+  TRY(pad_rows(h, block_idx, h->r_idx.p, p, tab, topk, 0xFFFFFFFFu, st));
   TRY(run_fine(h, h->r_q.p, h->r_k.p, h->r_v.p, static_cast<float*>(h->r_o.p), nullptr,
-               static_cast<const int32_t*>(h->r_idx.p), sp, dtype, topk, scale, causal, st, s.n));
-  return unpad_rows(h, h->r_o.p, out, s, s.d, st);
+               static_cast<const int32_t*>(h->r_idx.p), sp, dtype, topk, scale, causal, st, tab));
+  return unpad_rows(h, h->r_o.p, out, p, tab, s.d, st);
 }
 
 namespace {
-// bsa_forward and bsa_forward_budgets after their own argument checks;
-// topk = index row length (the largest budget).
+// The forward entry points after their own argument checks, on the layout
+// of plan p; topk = index row length (the largest budget).
 bsa_status forward_impl(bsa_handle h, const char* fn, const void* q, const void* k, const void* v,
-                        float* out, int32_t* block_idx_out, float* lse_out, const Shape& s,
+                        float* out, int32_t* block_idx_out, float* lse_out, const Plan& p,
                         bsa_dtype dtype, int topk, const bsa::HeadBudget& hb, float scale,
                         int causal, void* stream) {
   TRY(check_scale(h, fn, scale));
@@ -713,25 +822,26 @@ bsa_status forward_impl(bsa_handle h, const char* fn, const void* q, const void*
     return fail(h, BSA_ERR_INVALID_ARG, "%s: block_idx_out is not 4-byte aligned", fn);
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // A ragged n runs on copies padded to whole blocks (sp); the padding keys
-  // are masked, the padding rows' results dropped.
-  const Shape sp = s.padded();
-  const bool ragged = sp.n != s.n;
+  // Sequences that are not whole blocks run on copies padded to whole blocks
+  // (sp); the padding keys are masked, the padding rows' results dropped.
+  const Shape& sp = p.ks;
+  const int4* tab = nullptr;
+  TRY(upload_tab(h, p, st, &tab));
   const void *pq = q, *pk = k, *pv = v;
   float* pout = out;
   float* plse = lse_out;
   int32_t* idx = block_idx_out;
-  if (ragged) {
+  if (p.copy) {
     const size_t in_bytes = size_t(sp.elems()) * elem_bytes(dtype);
-    const int w = s.d * elem_bytes(dtype) / 4;
+    const int w = sp.d * elem_bytes(dtype) / 4;
     TRY(grow_buf(h, h->r_q, in_bytes, "padded q"));
     TRY(grow_buf(h, h->r_k, in_bytes, "padded k"));
     TRY(grow_buf(h, h->r_v, in_bytes, "padded v"));
     TRY(grow_buf(h, h->r_o, size_t(sp.elems()) * 4, "padded out"));
     if (lse_out) TRY(grow_buf(h, h->r_lse, size_t(sp.bh() * sp.n) * 4, "padded lse"));
-    TRY(pad_rows(h, q, h->r_q.p, s, w, 0u, st));
-    TRY(pad_rows(h, k, h->r_k.p, s, w, 0u, st));
-    TRY(pad_rows(h, v, h->r_v.p, s, w, 0u, st));
+    TRY(pad_rows(h, q, h->r_q.p, p, tab, w, 0u, st));
+    TRY(pad_rows(h, k, h->r_k.p, p, tab, w, 0u, st));
+    TRY(pad_rows(h, v, h->r_v.p, p, tab, w, 0u, st));
     pq = h->r_q.p;
     pk = h->r_k.p;
     pv = h->r_v.p;
@@ -755,13 +865,13 @@ bsa_status forward_impl(bsa_handle h, const char* fn, const void* q, const void*
              "index workspace"));
     idx = h->idx;
   }
-  TRY(run_pool(h, pk, repr, split, sp, dtype, st, s.n));
-  TRY(run_select(h, pq, repr, split, idx, sp, dtype, topk, hb, causal, st));
-  TRY(run_fine(h, pq, pk, pv, pout, plse, idx, sp, dtype, topk, scale, causal, st, s.n));
-  if (ragged) {
-    TRY(unpad_rows(h, pout, out, s, s.d, st));
-    if (block_idx_out) TRY(unpad_rows(h, idx, block_idx_out, s, topk, st));
-    if (lse_out) TRY(unpad_rows(h, plse, lse_out, s, 1, st));
+  TRY(run_pool(h, pk, repr, split, sp, dtype, st, tab));
+  TRY(run_select(h, pq, repr, split, idx, sp, dtype, topk, hb, causal, st, nullptr, tab));
+  TRY(run_fine(h, pq, pk, pv, pout, plse, idx, sp, dtype, topk, scale, causal, st, tab));
+  if (p.copy) {
+    TRY(unpad_rows(h, pout, out, p, tab, sp.d, st));
+    if (block_idx_out) TRY(unpad_rows(h, idx, block_idx_out, p, tab, topk, st));
+    if (lse_out) TRY(unpad_rows(h, plse, lse_out, p, tab, 1, st));
   }
   return BSA_OK;
 }
@@ -792,8 +902,8 @@ BSA_API bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const
   const Shape s{batch, heads, n, d};
   TRY(check_shape(h, fn, s, dtype, block, true));
   TRY(check_dynamic(h, fn, s, topk, causal));
-  return forward_impl(h, fn, q, k, v, out, block_idx_out, nullptr, s, dtype, topk, uniform_budget(topk),
-                      scale, causal, stream);
+  return forward_impl(h, fn, q, k, v, out, block_idx_out, nullptr, plan_dense(s), dtype, topk,
+                      uniform_budget(topk), scale, causal, stream);
 }
 
 BSA_API bsa_status bsa_forward_noalloc(bsa_handle h, const void* q, const void* k, const void* v,
@@ -833,7 +943,7 @@ BSA_API bsa_status bsa_forward_noalloc(bsa_handle h, const void* q, const void* 
   if (r == BSA_OK)
     r = run_select(h, q, repr, split, block_idx_out, s, dtype, topk, uniform_budget(topk), causal, st, &arena);
   if (r == BSA_OK)
-    r = run_fine(h, q, k, v, out, nullptr, block_idx_out, s, dtype, topk, scale, causal, st, 0, &arena);
+    r = run_fine(h, q, k, v, out, nullptr, block_idx_out, s, dtype, topk, scale, causal, st, nullptr, &arena);
   h->profiling = profiling;
   return r;
 }
@@ -851,7 +961,7 @@ BSA_API bsa_status bsa_forward_budgets(bsa_handle h, const void* q, const void* 
   if (!head_topk) return fail(h, BSA_ERR_INVALID_ARG, "%s: head_topk is NULL", fn);
   bsa::HeadBudget hb;
   TRY(read_budgets(h, fn, head_topk, heads, topk_max, &hb));
-  return forward_impl(h, fn, q, k, v, out, block_idx_out, nullptr, s, dtype, topk_max, hb, scale,
+  return forward_impl(h, fn, q, k, v, out, block_idx_out, nullptr, plan_dense(s), dtype, topk_max, hb, scale,
                       causal, stream);
 }
 
@@ -871,20 +981,16 @@ BSA_API bsa_status bsa_forward_train(bsa_handle h, const void* q, const void* k,
     return fail(h, BSA_ERR_INVALID_ARG, "%s: lse_out is not 4-byte aligned", fn);
   bsa::HeadBudget hb = uniform_budget(topk);
   if (head_topk) TRY(read_budgets(h, fn, head_topk, heads, topk, &hb));
-  return forward_impl(h, fn, q, k, v, out, block_idx_out, lse_out, s, dtype, topk, hb, scale, causal,
-                      stream);
+  return forward_impl(h, fn, q, k, v, out, block_idx_out, lse_out, plan_dense(s), dtype, topk, hb, scale,
+                      causal, stream);
 }
 
-BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, const void* v,
-                                const float* out, const float* dout, const int32_t* block_idx,
-                                const float* lse, float* dq, float* dk, float* dv, int batch,
-                                int heads, int n, int d, bsa_dtype dtype, int block, int topk,
-                                float scale, int causal, void* stream) {
-  const char* fn = "bsa_backward";
-  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
-  const Shape s{batch, heads, n, d};
-  TRY(check_shape(h, fn, s, dtype, block, true));
-  TRY(check_dynamic(h, fn, s, topk, causal));
+namespace {
+// The backward entry points after their shape checks, on the layout of plan p.
+bsa_status backward_impl(bsa_handle h, const char* fn, const void* q, const void* k, const void* v,
+                         const float* out, const float* dout, const int32_t* block_idx, const float* lse,
+                         float* dq, float* dk, float* dv, const Plan& p, bsa_dtype dtype, int topk,
+                         float scale, int causal, void* stream) {
   TRY(check_scale(h, fn, scale));
   TRY(check_ptr(h, fn, "q", q));
   TRY(check_ptr(h, fn, "k", k));
@@ -900,15 +1006,17 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
     return fail(h, BSA_ERR_INVALID_ARG, "%s: lse is NULL or not 4-byte aligned", fn);
   DeviceGuard dg(h->device);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  // A ragged n runs on copies padded to whole blocks (the padding rows select
-  // nothing, the padding keys are masked) and copies dq, dk, dv back.
-  const Shape sp = s.padded();
-  const bool ragged = sp.n != s.n;
+  // Sequences that are not whole blocks run on copies padded to whole
+  // blocks (the padding rows select nothing, the padding keys are masked),
+  // and dq, dk, dv are copied back.
+  const Shape& sp = p.ks;
+  const int4* tab = nullptr;
+  TRY(upload_tab(h, p, st, &tab));
   float *gq = dq, *gk = dk, *gv = dv;
-  if (ragged) {
+  if (p.copy) {
     const size_t in_bytes = size_t(sp.elems()) * elem_bytes(dtype);
     const size_t f_bytes = size_t(sp.elems()) * 4;
-    const int w = s.d * elem_bytes(dtype) / 4;
+    const int w = sp.d * elem_bytes(dtype) / 4;
     TRY(grow_buf(h, h->r_q, in_bytes, "padded q"));
     TRY(grow_buf(h, h->r_k, in_bytes, "padded k"));
     TRY(grow_buf(h, h->r_v, in_bytes, "padded v"));
@@ -919,13 +1027,13 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
     TRY(grow_buf(h, h->r_dq, f_bytes, "padded dq"));
     TRY(grow_buf(h, h->r_dk, f_bytes, "padded dk"));
     TRY(grow_buf(h, h->r_dv, f_bytes, "padded dv"));
-    TRY(pad_rows(h, q, h->r_q.p, s, w, 0u, st));
-    TRY(pad_rows(h, k, h->r_k.p, s, w, 0u, st));
-    TRY(pad_rows(h, v, h->r_v.p, s, w, 0u, st));
-    TRY(pad_rows(h, out, h->r_o.p, s, s.d, 0u, st));
-    TRY(pad_rows(h, dout, h->r_do.p, s, s.d, 0u, st));
-    TRY(pad_rows(h, lse, h->r_lse.p, s, 1, 0u, st));
-    TRY(pad_rows(h, block_idx, h->r_idx.p, s, topk, 0xFFFFFFFFu, st));
+    TRY(pad_rows(h, q, h->r_q.p, p, tab, w, 0u, st));
+    TRY(pad_rows(h, k, h->r_k.p, p, tab, w, 0u, st));
+    TRY(pad_rows(h, v, h->r_v.p, p, tab, w, 0u, st));
+    TRY(pad_rows(h, out, h->r_o.p, p, tab, sp.d, 0u, st));
+    TRY(pad_rows(h, dout, h->r_do.p, p, tab, sp.d, 0u, st));
+    TRY(pad_rows(h, lse, h->r_lse.p, p, tab, 1, 0u, st));
+    TRY(pad_rows(h, block_idx, h->r_idx.p, p, tab, topk, 0xFFFFFFFFu, st));
     q = h->r_q.p;
     k = h->r_k.p;
     v = h->r_v.p;
@@ -977,7 +1085,7 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   a.dk = gk;
   a.dv = gv;
   a.n = sp.n;
-  a.nv = s.n;
+  a.seqtab = tab;
   a.d = sp.d;
   a.topk = topk;
   a.causal = causal;
@@ -1001,6 +1109,7 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
   gi.q = q;
   gi.idx = block_idx;
   gi.n = sp.n;
+  gi.seqtab = tab;
   gi.d = sp.d;
   gi.topk = topk;
   gi.causal = causal;
@@ -1020,12 +1129,86 @@ BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, cons
     TRY(timed_launch(h, BSA_STAGE_BWD_REDUCE, st, "backward dk/dv reduction",
                      [&] { return bsa::launch_bwd_dkv(a, r0, rows, st); }));
   }
-  if (ragged) {
-    TRY(unpad_rows(h, gq, dq, s, s.d, st));
-    TRY(unpad_rows(h, gk, dk, s, s.d, st));
-    TRY(unpad_rows(h, gv, dv, s, s.d, st));
+  if (p.copy) {
+    TRY(unpad_rows(h, gq, dq, p, tab, sp.d, st));
+    TRY(unpad_rows(h, gk, dk, p, tab, sp.d, st));
+    TRY(unpad_rows(h, gv, dv, p, tab, sp.d, st));
   }
   return BSA_OK;
+}
+}  // namespace
+
+BSA_API bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, const void* v,
+                                const float* out, const float* dout, const int32_t* block_idx,
+                                const float* lse, float* dq, float* dk, float* dv, int batch,
+                                int heads, int n, int d, bsa_dtype dtype, int block, int topk,
+                                float scale, int causal, void* stream) {
+  const char* fn = "bsa_backward";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  const Shape s{batch, heads, n, d};
+  TRY(check_shape(h, fn, s, dtype, block, true));
+  TRY(check_dynamic(h, fn, s, topk, causal));
+  return backward_impl(h, fn, q, k, v, out, dout, block_idx, lse, dq, dk, dv, plan_dense(s), dtype, topk,
+                       scale, causal, stream);
+}
+
+
+
+// ------------------------------------------------- variable lengths --
+
+namespace {
+bsa_status check_varlen(bsa_handle h, const char* fn, int heads, int d, bsa_dtype dtype, int block, int topk,
+                        int causal) {
+  if (dtype != BSA_FP32 && dtype != BSA_BF16)
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, int(dtype));
+  if (block != 64) return fail(h, BSA_ERR_UNSUPPORTED, "%s: block must be 64 (got %d)", fn, block);
+  if (d != 64 && d != 128) return fail(h, BSA_ERR_UNSUPPORTED, "%s: d must be 64 or 128 (got %d)", fn, d);
+  if (heads < 1) return fail(h, BSA_ERR_INVALID_ARG, "%s: heads must be >= 1 (got %d)", fn, heads);
+  if (topk < 1) return fail(h, BSA_ERR_INVALID_ARG, "%s: topk must be >= 1 (got %d)", fn, topk);
+  if (causal != 0 && causal != 1)
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: causal must be 0 or 1 (got %d)", fn, causal);
+  return BSA_OK;
+}
+
+bsa_status check_plan_size(bsa_handle h, const char* fn, const Plan& p) {
+  if (p.ks.bh() * p.ks.n > (int64_t(1) << 31))
+    return fail(h, BSA_ERR_UNSUPPORTED, "%s: problem too large (heads * padded rows = %lld)", fn,
+                (long long)(p.ks.bh() * p.ks.n));
+  return BSA_OK;
+}
+}  // namespace
+
+BSA_API bsa_status bsa_forward_varlen(bsa_handle h, const void* q, const void* k, const void* v, float* out,
+                                      int32_t* block_idx_out, float* lse_out, const int32_t* cu_seqlens,
+                                      int nseq, int heads, int d, bsa_dtype dtype, int block,
+                                      const int32_t* head_topk, int topk, float scale, int causal,
+                                      void* stream) {
+  const char* fn = "bsa_forward_varlen";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  TRY(check_varlen(h, fn, heads, d, dtype, block, topk, causal));
+  Plan p;
+  TRY(plan_varlen(h, fn, cu_seqlens, nseq, heads, d, &p));
+  TRY(check_plan_size(h, fn, p));
+  if (lse_out && (reinterpret_cast<uintptr_t>(lse_out) & 3u))
+    return fail(h, BSA_ERR_INVALID_ARG, "%s: lse_out is not 4-byte aligned", fn);
+  bsa::HeadBudget hb = uniform_budget(topk);
+  if (head_topk) TRY(read_budgets(h, fn, head_topk, heads, topk, &hb));
+  return forward_impl(h, fn, q, k, v, out, block_idx_out, lse_out, p, dtype, topk, hb, scale, causal, stream);
+}
+
+BSA_API bsa_status bsa_backward_varlen(bsa_handle h, const void* q, const void* k, const void* v,
+                                       const float* out, const float* dout, const int32_t* block_idx,
+                                       const float* lse, float* dq, float* dk, float* dv,
+                                       const int32_t* cu_seqlens, int nseq, int heads, int d, bsa_dtype dtype,
+                                       int block, int topk, float scale, int causal, void* stream) {
+  const char* fn = "bsa_backward_varlen";
+  if (!h) return fail(nullptr, BSA_ERR_INVALID_ARG, "%s: handle is NULL", fn);
+  TRY(check_varlen(h, fn, heads, d, dtype, block, topk, causal));
+  Plan p;
+  TRY(plan_varlen(h, fn, cu_seqlens, nseq, heads, d, &p));
+  TRY(check_plan_size(h, fn, p));
+  return backward_impl(h, fn, q, k, v, out, dout, block_idx, lse, dq, dk, dv, p, dtype, topk, scale, causal,
+                       stream);
 }
 
 // ------------------------------------------------------ static forward --

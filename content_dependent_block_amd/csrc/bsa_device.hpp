@@ -57,4 +57,44 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// Sequences of different lengths.  The rows of a head hold one or more
+// sequences one after the other, each padded with zero rows to whole 64-row
+// blocks.  Entry beta of the block table describes block beta of that layout
+// (the same for every head): {first block of its sequence, one past the
+// sequence's last block, keys of the block that exist (1 .. 64), first caller
+// row of the block}.  A NULL table means one sequence of n / 64 whole blocks
+// per head.  Selections hold block numbers relative to the sequence's first
+// block.
+struct RowBlocks {
+  int lo, hi;  // candidate blocks [lo, hi) of the row's head
+  int own;     // the row's own block
+};
+
+__device__ __forceinline__ RowBlocks row_blocks(const int4* __restrict__ seqtab, int64_t row, int n,
+                                                int causal) {
+  RowBlocks r;
+  r.own = static_cast<int>(row % n) / kTile;
+  r.lo = 0;
+  r.hi = n / kTile;
+  if (seqtab) {
+    const int4 e = seqtab[r.own];
+    r.lo = e.x;
+    r.hi = e.y;
+  }
+  if (causal) r.hi = r.own + 1;
+  return r;
+}
+
+// The head-level block of selection entry `sel`, or -1 when the entry does
+// not count (padding, outside the row's sequence, after its own block in the
+// causal variant).
+__device__ __forceinline__ int sel_block(int sel, const RowBlocks& r) {
+  return (sel >= 0 && sel < r.hi - r.lo) ? r.lo + sel : -1;
+}
+
+// Keys of block beta that exist.
+__device__ __forceinline__ int block_keys(const int4* __restrict__ seqtab, int beta) {
+  return seqtab ? seqtab[beta].z : kTile;
+}
+
 }  // namespace bsa

@@ -13,19 +13,24 @@ namespace bsa {
 
 // block_pool: k [bh][n][d] -> repr float [bh][n/64][d] (if repr != NULL) and
 // the three-term bf16 split of each representative, split [bh][3][n/64][d]
-// (if split != NULL).  nv < n: the keys are padded with zero rows from nv to
-// n, and the last block is the mean of its nv - (n - 64) valid keys.
+// (if split != NULL).  seqtab (nullable): the block table of sequences
+// padded to whole blocks (bsa_device.hpp); a block with fewer than 64 keys
+// is the mean of those.
+//
+// Every `seqtab` below is that table: n / 64 entries in device memory, or
+// NULL for one sequence of n whole-block rows per head.
 hipError_t launch_block_pool(const void* k, float* repr, uint16_t* split, int64_t bh, int n, int d,
-                             bsa_dtype dtype, hipStream_t stream, int nv = 0);
+                             bsa_dtype dtype, hipStream_t stream, const int4* seqtab = nullptr);
 
-// Ragged sequences run on copies padded to whole blocks.  pad: dst[h][r][:] =
-// src[h][r][:] for r < n, = fill (every 32-bit word) for n <= r < n_pad.
-// unpad: dst[h][r][:] = src[h][r][:] for r < n, src rows n_pad apart.  Rows
-// are `words` 32-bit words.
-hipError_t launch_pad_rows(const void* src, void* dst, int64_t bh, int n, int n_pad, int words,
-                           uint32_t fill, hipStream_t stream);
-hipError_t launch_unpad_rows(const void* src, void* dst, int64_t bh, int n, int n_pad, int words,
-                             hipStream_t stream);
+// Sequences whose lengths are not multiples of 64 run on copies padded to
+// whole blocks.  pad: dst [slices][n_pad] rows from src [slices][src_rows]
+// rows, row r of a slice taking caller row seqtab[r / 64].w + r % 64 when
+// r % 64 < seqtab[r / 64].z, else `fill` in every 32-bit word.  unpad: the
+// inverse, for the rows that exist.  Rows are `words` 32-bit words.
+hipError_t launch_pad_rows(const void* src, void* dst, int64_t slices, int src_rows, int n_pad, int words,
+                           uint32_t fill, const int4* seqtab, hipStream_t stream);
+hipError_t launch_unpad_rows(const void* src, void* dst, int64_t slices, int src_rows, int n_pad, int words,
+                             const int4* seqtab, hipStream_t stream);
 
 // coarse_score over panel rows [row0, row0 + rows) of the flattened
 // [bh * n] query rows; row0 and rows multiples of 64.  panel row r holds
@@ -46,15 +51,18 @@ struct HeadBudget {
 // coarse_score and topk_select in one kernel (topk <= 32) over all `rows`
 // query rows: idx[row * topk + t], no panel.  Representatives: for bf16
 // inputs the split form from block_pool (repr_split), for fp32 inputs the
-// float32 repr.
+// float32 repr.  Candidates: the blocks of the query's sequence; indices
+// relative to its first block.
 hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t* repr_split,
                                 int32_t* idx, int64_t rows, int n, int d, bsa_dtype dtype,
-                                int topk, const HeadBudget& budget, int causal, hipStream_t stream);
+                                int topk, const HeadBudget& budget, int causal, hipStream_t stream,
+                                const int4* seqtab = nullptr);
 constexpr int kFusedSelectMaxK = 32;
 
 // topk_select over panel rows [row0, row0 + rows): idx[(row0 + r) * topk + t].
 hipError_t launch_topk_select(const float* panel, int32_t* idx, int64_t row0, int64_t rows, int n,
-                              int topk, const HeadBudget& budget, int causal, hipStream_t stream);
+                              int topk, const HeadBudget& budget, int causal, hipStream_t stream,
+                              const int4* seqtab = nullptr);
 
 // sparse_flash_fwd, dynamic: per 64-query tile the union of its rows'
 // selected blocks, each row masked to its own selection.  lse (nullable):
@@ -62,7 +70,7 @@ hipError_t launch_topk_select(const float* panel, int32_t* idx, int64_t row0, in
 hipError_t launch_sparse_flash_dynamic(const void* q, const void* k, const void* v, float* out,
                                        float* lse, const int32_t* idx, int64_t bh, int n, int d,
                                        int topk, float scale, int causal, bsa_dtype dtype,
-                                       hipStream_t stream, int nv = 0);
+                                       hipStream_t stream, const int4* seqtab = nullptr);
 
 // sparse_flash_fwd, static tile list, run as host-scheduled work items (each
 // at most S key tiles of one query tile, heaviest first), then a merge of the
@@ -119,7 +127,7 @@ struct GatherArgs {
   float* lse = nullptr;  // nullable: per row log-sum-exp (natural log), from the combine
   const int32_t* idx = nullptr;
   int n = 0, d = 0, topk = 0, causal = 0;
-  int nv = 0;  // keys per head that exist (< n: rows nv .. n-1 are padding and masked); 0 = n
+  const int4* seqtab = nullptr;  // block table (sequences padded to whole blocks) or NULL
   float scale = 0.f;
   bsa_dtype dtype = BSA_FP32;
   int qsegs = 1;  // query segments per head (gather_segments); buckets = heads x qsegs x n/64
@@ -163,7 +171,7 @@ struct BackwardArgs {
   float* dk = nullptr;
   float* dv = nullptr;
   int n = 0, d = 0, topk = 0, causal = 0;
-  int nv = 0;  // keys per head that exist (< n: padding rows, masked); 0 = n
+  const int4* seqtab = nullptr;  // block table (sequences padded to whole blocks) or NULL
   float scale = 0.f;
   bsa_dtype dtype = BSA_FP32;
   int qsegs = 1;

@@ -230,14 +230,14 @@ struct Bf16PlaneTiles {
     }
   }
   template <int NT>
-  __device__ __forceinline__ void prime(const Src* __restrict__ rbase, int nb, int tid) {
-    fetch<NT>(rbase, nb, 0, tid);
+  __device__ __forceinline__ void prime(const Src* __restrict__ rbase, int nb, int bt0, int tid) {
+    fetch<NT>(rbase, nb, bt0, tid);
     if constexpr (NT == 1 && PFD > 1) {
 #pragma unroll
       for (int u = 0; u < PER; ++u) pf[0][u] = pf1[PFD - 2][u];
 #pragma unroll
       for (int i = 1; i < PFD; ++i) {
-        fetch<NT>(rbase, nb, i, tid);
+        fetch<NT>(rbase, nb, bt0 + i, tid);
 #pragma unroll
         for (int u = 0; u < PER; ++u) pf1[i - 1][u] = pf1[PFD - 2][u];
       }
@@ -394,8 +394,8 @@ struct F32Tiles {
     }
   }
   template <int NT>
-  __device__ __forceinline__ void prime(const Src* __restrict__ rbase, int nb, int tid) {
-    fetch<NT>(rbase, nb, 0, tid);
+  __device__ __forceinline__ void prime(const Src* __restrict__ rbase, int nb, int bt0, int tid) {
+    fetch<NT>(rbase, nb, bt0, tid);
   }
   static constexpr int PFD = 1;
   template <int NT>
@@ -631,7 +631,7 @@ __device__ __forceinline__ float kth_of_lanes(float (&a)[N], int keff, int lane)
 // up to topk.
 template <int KL>
 __device__ __forceinline__ void emit_selection(const int (&b)[KL], int g, int keff, int topk,
-                                               int32_t* __restrict__ dst) {
+                                               int32_t* __restrict__ dst, int base) {
 #pragma unroll
   for (int t0 = 0; t0 < KL; t0 += 4) {
     if (t0 + g < keff) {
@@ -641,7 +641,7 @@ __device__ __forceinline__ void emit_selection(const int (&b)[KL], int g, int ke
       int pos = 0;
 #pragma unroll
       for (int u = 0; u < KL; ++u) pos += (u < keff && b[u] < me) ? 1 : 0;
-      dst[pos] = me;
+      dst[pos] = me - base;
     }
   }
   for (int t = keff + g; t < topk; t += 4) dst[t] = -1;
@@ -679,13 +679,16 @@ __device__ __forceinline__ void sort_asc(int (&a)[N]) {
 // tile_row + 16 (w QG + gq) + c16.  All rows of a workgroup belong to one
 // (batch, head), and (64-row query blocks being aligned to the 32-block R
 // tiles) their query blocks lie in one R tile, the last one walked.
+// With a block table (several sequences per head), the candidates start at
+// the sequence's first block lo: the walk runs over tiles bt0 = lo / TB ..
+// nbt - 1, and all rows of a workgroup (one 64-row query block) share lo.
 template <int QG>
 struct SelInfo {
   int64_t tile_row, bh, qrow0;
-  int nb, nbt;
+  int nb, nbt, bt0, lo;
   int nvalid[QG], forced[QG];
   int tid, lane, wave, g, c16;
-  __device__ __forceinline__ SelInfo(int n, int causal, int TB, int NW) {
+  __device__ __forceinline__ SelInfo(int n, int causal, int TB, int NW, const int4* __restrict__ seqtab) {
     const int rows = 16 * QG * NW;
     nb = n / kTile;
     tid = threadIdx.x;
@@ -697,12 +700,20 @@ struct SelInfo {
     bh = tile_row / n;
     const int i0 = static_cast<int>(tile_row % n);
     qrow0 = tile_row + 16 * QG * wave + c16;
+    int hi = nb;
+    lo = 0;
+    if (seqtab) {
+      const int4 e = seqtab[i0 / kTile];
+      lo = e.x;
+      hi = e.y;
+    }
     const int qlast = (i0 + rows - 1) / kTile;  // query block of the workgroup's last row
-    nbt = causal ? qlast / TB + 1 : (nb + TB - 1) / TB;
+    nbt = causal ? qlast / TB + 1 : (hi + TB - 1) / TB;
+    bt0 = lo / TB;
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
       const int qblk = (i0 + 16 * (QG * wave + gq)) / kTile;
-      nvalid[gq] = causal ? qblk + 1 : nb;
+      nvalid[gq] = causal ? qblk + 1 : hi;
       forced[gq] = causal ? qblk : -1;
     }
   }
@@ -710,7 +721,7 @@ struct SelInfo {
   // candidate, +inf for the causal own block.
   __device__ __forceinline__ float cand(int gq, float s, int beta) const {
     const float x = beta == forced[gq] ? INFINITY : s;
-    return beta < nvalid[gq] ? x : -INFINITY;
+    return (beta < nvalid[gq] && beta >= lo) ? x : -INFINITY;
   }
 };
 
@@ -726,11 +737,23 @@ __device__ __forceinline__ void walk(TL& sc, unsigned char* rs, const typename T
                                      const SelInfo<QG>& ti, FF&& fast, FS&& slow) {
   constexpr int MT = TL::TB / 16;
   constexpr int PF = NT == 1 ? TL::PFD : 1;  // tiles loaded ahead
-  sc.template prime<NT>(rbase, ti.nb, ti.tid);
+  sc.template prime<NT>(rbase, ti.nb, ti.bt0, ti.tid);
   f32x4 acc[MT][QG];
+  int bt0 = ti.bt0;
+  // A first tile that starts before the sequence's first block (and is not
+  // the last) is checked too.
+  if (ti.lo % TL::TB != 0 && bt0 + 1 < ti.nbt) {
+    __syncthreads();
+    sc.template put<NT>(rs, ti.tid);
+    sc.template fetch<NT>(rbase, ti.nb, bt0 + PF, ti.tid);
+    __syncthreads();
+    sc.template tiles_all<NT, MT>(rs, ti.g, ti.c16, acc);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) slow(0, mt, bt0 * TL::TB + mt * 16, acc[mt]);
+    ++bt0;
+  }
   // Steady state: NH tiles per iteration, none of them the last, so the body
   // has no branches and the slot index h stays a compile-time value.
-  int bt0 = 0;
   for (; bt0 + NH < ti.nbt; bt0 += NH) {
 #pragma unroll
     for (int h = 0; h < NH; ++h) {
@@ -789,7 +812,8 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
                                                                       const typename TL::Src* __restrict__ rsrc,
                                                                       int32_t* __restrict__ idx, int n,
                                                                       int topk, const HeadBudget budget,
-                                                                      int causal) {
+                                                                      int causal,
+                                                                      const int4* __restrict__ seqtab) {
   using TL1 = typename Pass1Tiles<TL>::type;
   constexpr int NTH = 64 * NW;
   constexpr int MT = TL1::TB / 16;    // MFMA tiles per R tile of pass 1
@@ -810,13 +834,14 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
   // per lane and query group: candidate scores and blocks
   __shared__ float cv[NW][QG][CAP][64];
   __shared__ uint16_t cb[NW][QG][CAP][64];
-  const SelInfo<QG> ti(n, causal, TL::TB, NW);
-  const SelInfo<QG> ti1(n, causal, TL1::TB, NW);  // the same rows, walked in pass-1 tiles
+  static_assert(ROWS == kTile, "a workgroup's rows are one query block, so one sequence");
+  const SelInfo<QG> ti(n, causal, TL::TB, NW, seqtab);
+  const SelInfo<QG> ti1(n, causal, TL1::TB, NW, seqtab);  // the same rows, walked in pass-1 tiles
   const auto* rbase = TL::head_base(rsrc, ti.bh, ti.nb);
   const int kh = budget.k[ti.bh % budget.heads];  // this head's budget (<= topk <= KL)
   int keff[QG];
 #pragma unroll
-  for (int gq = 0; gq < QG; ++gq) keff[gq] = kh < ti.nvalid[gq] ? kh : ti.nvalid[gq];
+  for (int gq = 0; gq < QG; ++gq) keff[gq] = kh < ti.nvalid[gq] - ti.lo ? kh : ti.nvalid[gq] - ti.lo;
 
   // pass 1: group maxima.  The lane's block 16 (MT bt + mt) + 4 g + j goes to
   // slot 4 ((MT bt + mt) mod 4 GM) + j: G = 64 GM groups over the 4 lanes.
@@ -968,7 +993,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
       for (int u = 0; u < KL; ++u) b[u] = u < kq ? list[u] : 0x7fffffff;
       sort_asc<KL>(b);
 #pragma unroll
-      for (int u = 0; u < KL; ++u) b[u] = u < kq ? b[u] : -1;
+      for (int u = 0; u < KL; ++u) b[u] = u < kq ? b[u] - ti.lo : -1;
       if (((reinterpret_cast<uintptr_t>(dst) | static_cast<uintptr_t>(topk) * 4u) & 15u) == 0) {
 #pragma unroll
         for (int c0 = 0; c0 < KL / 4; c0 += 4) {
@@ -1018,7 +1043,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
            });
       merge_top<16, KL>(l.v, l.b, ti.lane);
       merge_top<32, KL>(l.v, l.b, ti.lane);
-      emit_selection<KL>(l.b, ti.g, keff[gq], topk, idx + (ti.qrow0 + 16 * gq) * topk);
+      emit_selection<KL>(l.b, ti.g, keff[gq], topk, idx + (ti.qrow0 + 16 * gq) * topk, ti.lo);
     }
   }
 }
@@ -1034,11 +1059,11 @@ void launch_panel(const void* q, const void* rsrc, float* panel, int64_t row0, i
 
 template <typename TL, int KL, int GM, int CAP, int MINW, int QG, int NW>
 void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
-                   const HeadBudget& hb, int causal, hipStream_t s) {
+                   const HeadBudget& hb, int causal, const int4* seqtab, hipStream_t s) {
   constexpr int ROWS = 16 * QG * NW;
   hipLaunchKernelGGL((coarse_select_kernel<TL, KL, GM, CAP, MINW, QG, NW>), dim3(static_cast<unsigned>(rows / ROWS)),
                      dim3(64 * NW), 0, s, static_cast<const typename TL::QT*>(q),
-                     static_cast<const typename TL::Src*>(rsrc), idx, n, topk, hb, causal);
+                     static_cast<const typename TL::Src*>(rsrc), idx, n, topk, hb, causal, seqtab);
 }
 
 // One 16-query group per wave, four waves per workgroup; the register budget
@@ -1046,11 +1071,11 @@ void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, 
 // whose candidate lists are twice as long).
 template <template <int, int, int> class TLT, int D>
 void launch_select_k(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
-                     const HeadBudget& hb, int causal, hipStream_t s) {
+                     const HeadBudget& hb, int causal, const int4* seqtab, hipStream_t s) {
   constexpr int M1 = (D == 64 && std::is_same<typename TLT<D, 1, 256>::QT, bf16_bits>::value) ? 4 : 3;
-  if (topk <= 8) launch_select<TLT<D, 1, 256>, 8, 1, 8, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, s);
-  else if (topk <= 16) launch_select<TLT<D, 1, 256>, 16, 1, 16, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, s);
-  else launch_select<TLT<D, 1, 256>, 32, 2, 32, 2, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, s);
+  if (topk <= 8) launch_select<TLT<D, 1, 256>, 8, 1, 8, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, s);
+  else if (topk <= 16) launch_select<TLT<D, 1, 256>, 16, 1, 16, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, s);
+  else launch_select<TLT<D, 1, 256>, 32, 2, 32, 2, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, s);
 }
 
 template <int D, int QG, int NTH>
@@ -1075,13 +1100,14 @@ hipError_t launch_coarse_score(const void* q, const float* repr, float* panel, i
 
 hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t* repr_split,
                                 int32_t* idx, int64_t rows, int n, int d, bsa_dtype dtype,
-                                int topk, const HeadBudget& hb, int causal, hipStream_t stream) {
+                                int topk, const HeadBudget& hb, int causal, hipStream_t stream,
+                                const int4* seqtab) {
   if (dtype == BSA_BF16) {
-    if (d == 64) launch_select_k<PlaneT, 64>(q, repr_split, idx, rows, n, topk, hb, causal, stream);
-    else launch_select_k<PlaneT, 128>(q, repr_split, idx, rows, n, topk, hb, causal, stream);
+    if (d == 64) launch_select_k<PlaneT, 64>(q, repr_split, idx, rows, n, topk, hb, causal, seqtab, stream);
+    else launch_select_k<PlaneT, 128>(q, repr_split, idx, rows, n, topk, hb, causal, seqtab, stream);
   } else {
-    if (d == 64) launch_select_k<F32T, 64>(q, repr, idx, rows, n, topk, hb, causal, stream);
-    else launch_select_k<F32T, 128>(q, repr, idx, rows, n, topk, hb, causal, stream);
+    if (d == 64) launch_select_k<F32T, 64>(q, repr, idx, rows, n, topk, hb, causal, seqtab, stream);
+    else launch_select_k<F32T, 128>(q, repr, idx, rows, n, topk, hb, causal, seqtab, stream);
   }
   return hipGetLastError();
 }

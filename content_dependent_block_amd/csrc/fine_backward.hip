@@ -40,11 +40,6 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kXcds = 8;
 
-__device__ __forceinline__ bool pair_valid(int beta, int nb, int64_t row, int n, int causal) {
-  if (beta < 0 || beta >= nb) return false;
-  return !causal || beta <= static_cast<int>(row % n) / kTile;
-}
-
 // ---------------------------------------------------------------- prep --
 // ld[row] = (lse * log2 e, sum_d dout * out): 16 lanes per row.
 // For bf16 inputs it also writes dout rounded to bf16 (dout_b, [rows][D]),
@@ -287,7 +282,7 @@ __global__ __launch_bounds__(256, (BwdLayout<T, D>::kWaves)) void bwd_pair_kerne
     const void* __restrict__ dout, const float2* __restrict__ ld,
     const int32_t* __restrict__ list, const int32_t* __restrict__ items,
     const int4* __restrict__ item_rec, int nbuckets, int64_t row0, int64_t npairs, int n,
-    uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, int klim_last, float scale,
+    uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, const int4* __restrict__ seqtab, float scale,
     float scale_log2, float* __restrict__ dq_part,
     float* __restrict__ dkv_part) {
   using L = BwdLayout<T, D>;
@@ -315,7 +310,7 @@ __global__ __launch_bounds__(256, (BwdLayout<T, D>::kWaves)) void bwd_pair_kerne
   const int nb = n / kTile;
   const int beta = b % nb;
   const int64_t bh = bh0 + b / (nb * qsegs);
-  const int klim = beta == nb - 1 ? klim_last : kTile;  // valid keys of the block (the rest pad)
+  const int klim = block_keys(seqtab, beta);  // keys of the block that exist (the rest pad)
 
   stage_kv<T, D>(k + (bh * n + static_cast<int64_t>(beta) * kTile) * D,
                  v + (bh * n + static_cast<int64_t>(beta) * kTile) * D, ks, vs, kt, tid);
@@ -517,7 +512,8 @@ template <int D, bool HALF>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__ idx,
                                                      const void* __restrict__ dq_part,
                                                      float* __restrict__ dq, int64_t row0,
-                                                     int64_t rows, int n, int topk, int causal) {
+                                                     int64_t rows, int n, int topk, int causal,
+                                                     const int4* __restrict__ seqtab) {
   constexpr int E = D / 16;
   constexpr int V = E / 4;
   constexpr int S = 8;
@@ -525,7 +521,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__
   if (r >= rows) return;
   const int c = threadIdx.x & 15;
   const int64_t row = row0 + r;
-  const int nb = n / kTile;
+  const RowBlocks rb = row_blocks(seqtab, row, n, causal);
   f32x4 acc[V];
 #pragma unroll
   for (int u = 0; u < V; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -536,7 +532,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__
     for (int t = 0; t < S; ++t) {
       const int st = s0 + t < topk ? s0 + t : topk - 1;
       const int64_t pr = r * topk + st;
-      ok[t] = s0 + t < topk && pair_valid(idx[row * topk + st], nb, row, n, causal);
+      ok[t] = s0 + t < topk && sel_block(idx[row * topk + st], rb) >= 0;
       if constexpr (HALF) {
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         const u32x2* src = reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(dq_part) + pr * D + c * E);
@@ -634,7 +630,6 @@ hipError_t pairs_launch(const BackwardArgs& a, int64_t row0, int64_t rows, hipSt
   while ((1 << lg) < a.topk) ++lg;
   const int shift = 32 + lg;
   const uint64_t magic = ((uint64_t(1) << shift) + uint64_t(a.topk) - 1) / uint64_t(a.topk);
-  const int klim_last = (a.nv > 0 && a.nv < a.n) ? a.nv - (c.nb - 1) * kTile : kTile;
   const auto kern = bwd_pair_kernel<T, D, CAUSAL>;
   if (L::BYTES > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -645,7 +640,7 @@ hipError_t pairs_launch(const BackwardArgs& a, int64_t row0, int64_t rows, hipSt
                      static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v),
                      sizeof(T) == 2 ? static_cast<const void*>(a.dout_b) : static_cast<const void*>(a.dout),
                      a.ld, a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets, row0, c.npairs,
-                     a.n, magic, shift, c.bh0, a.qsegs, klim_last, a.scale, a.scale * kLog2e,
+                     a.n, magic, shift, c.bh0, a.qsegs, a.seqtab, a.scale, a.scale * kLog2e,
                      a.dq_part, a.dkv_part);
   return hipGetLastError();
 }
@@ -680,17 +675,17 @@ hipError_t launch_bwd_dq(const BackwardArgs& a, int64_t row0, int64_t rows, hipS
   if (a.d == 64) {
     if (half)
       hipLaunchKernelGGL((bwd_dq_kernel<64, true>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq,
-                         row0, rows, a.n, a.topk, a.causal);
+                         row0, rows, a.n, a.topk, a.causal, a.seqtab);
     else
       hipLaunchKernelGGL((bwd_dq_kernel<64, false>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq,
-                         row0, rows, a.n, a.topk, a.causal);
+                         row0, rows, a.n, a.topk, a.causal, a.seqtab);
   } else {
     if (half)
       hipLaunchKernelGGL((bwd_dq_kernel<128, true>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq,
-                         row0, rows, a.n, a.topk, a.causal);
+                         row0, rows, a.n, a.topk, a.causal, a.seqtab);
     else
       hipLaunchKernelGGL((bwd_dq_kernel<128, false>), grid, dim3(256), 0, s, a.idx, a.dq_part, a.dq,
-                         row0, rows, a.n, a.topk, a.causal);
+                         row0, rows, a.n, a.topk, a.causal, a.seqtab);
   }
   return hipGetLastError();
 }

@@ -54,13 +54,6 @@ constexpr int kXcds = 8;
 typedef _Float16 f16;
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
-// A selection entry counts iff it names a real block and, in the causal
-// variant, a block that is not after the query's own block.
-__device__ __forceinline__ bool pair_valid(int beta, int nb, int64_t row, int n, int causal) {
-  if (beta < 0 || beta >= nb) return false;
-  return !causal || beta <= static_cast<int>(row % n) / kTile;
-}
-
 // Bucket of pair (row, beta): (head, query segment, key block), so that the
 // buckets of one segment of one head are consecutive.
 __device__ __forceinline__ int64_t bucket_of(int64_t row, int beta, int n, int nb, int qsegs, int64_t bh0) {
@@ -131,7 +124,7 @@ __device__ __forceinline__ int32_t block_excl_scan(int32_t* s, int m, int32_t* w
 __global__ __launch_bounds__(256) void bucket_count_kernel(
     const int32_t* __restrict__ idx, int32_t* __restrict__ count, int32_t* __restrict__ rank,
     int2* __restrict__ rec, int32_t* __restrict__ wg_valid, int64_t row0, int64_t rows, int n, int topk,
-    int causal, int64_t bh0, int rpw, int qsegs) {
+    int causal, int64_t bh0, int rpw, int qsegs, const int4* __restrict__ seqtab) {
   // LDS: [nb] local counts -> local offsets, [nb] global bases, [4] scan
   // scratch, then (register path) the block-ordered records, 8 bytes each
   extern __shared__ int32_t hist[];
@@ -153,8 +146,8 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
       lr[j] = -1;
       bt[j] = 0;
       if (e < npairs) {
-        const int beta = sel[e];
-        if (pair_valid(beta, nb, r_begin + e / topk, n, causal)) {
+        const int beta = sel_block(sel[e], row_blocks(seqtab, r_begin + e / topk, n, causal));
+        if (beta >= 0) {
           bt[j] = beta;
           lr[j] = atomicAdd(&hist[beta], 1);
         }
@@ -182,8 +175,8 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
     return;
   }
   for (int e = threadIdx.x; e < npairs; e += 256) {
-    const int beta = sel[e];
-    rank[p_begin + e] = pair_valid(beta, nb, r_begin + e / topk, n, causal) ? atomicAdd(&hist[beta], 1) : -1;
+    const int beta = sel_block(sel[e], row_blocks(seqtab, r_begin + e / topk, n, causal));
+    rank[p_begin + e] = beta >= 0 ? atomicAdd(&hist[beta], 1) : -1;
   }
   __syncthreads();
   for (int c = threadIdx.x; c < nb; c += 256)
@@ -191,7 +184,7 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
   __syncthreads();
   for (int e = threadIdx.x; e < npairs; e += 256) {
     const int32_t rk = rank[p_begin + e];
-    if (rk >= 0) rank[p_begin + e] = base[sel[e]] + rk;
+    if (rk >= 0) rank[p_begin + e] = base[sel_block(sel[e], row_blocks(seqtab, r_begin + e / topk, n, 0))] + rk;
   }
 }
 
@@ -288,7 +281,7 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(
     const int32_t* __restrict__ wg_valid, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ items, int4* __restrict__ item_rec, int nbuckets, int64_t max_slots,
     int32_t* __restrict__ list, int64_t row0, int64_t rows, int n, int topk, int64_t bh0, int qsegs,
-    int item_pairs, int rpw) {
+    int item_pairs, int rpw, const int4* __restrict__ seqtab) {
   const int64_t pb = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (pb < nbuckets) {
     const int32_t total = items[nbuckets];
@@ -326,7 +319,7 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(
   for (int e = threadIdx.x; e < np; e += 256) {
     const int32_t rk = rank[p_begin + e];
     if (rk < 0) continue;
-    const int64_t pos = static_cast<int64_t>(off[sel[e]]) + rk;
+    const int64_t pos = static_cast<int64_t>(off[sel_block(sel[e], row_blocks(seqtab, r_begin + e / topk, n, 0))]) + rk;
     if (pos < npairs) list[pos] = static_cast<int32_t>(p_begin + e);
   }
 }
@@ -562,8 +555,8 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ list, const int32_t* __restrict__ items,
     const int4* __restrict__ item_rec, int nbuckets, int64_t row0, int64_t npairs, int n,
-    uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, int klim_last, float scale_log2,
-    PartialT<T>* __restrict__ po) {
+    uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, const int4* __restrict__ seqtab,
+    float scale_log2, PartialT<T>* __restrict__ po) {
   using L = KvLayout<T, D>;
   constexpr int GPW = kItemPairs / 16 / 4;  // 16-pair groups per wave
   constexpr int STAGE_BYTES = L::kBf16 ? 16 * kStagePitch<D> * 2 : 0;  // per wave
@@ -589,7 +582,7 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
   const int nb = n / kTile;
   const int beta = b % nb;
   const int64_t bh = bh0 + b / (nb * qsegs);
-  const int klim = beta == nb - 1 ? klim_last : kTile;  // valid keys of the block
+  const int klim = block_keys(seqtab, beta);  // keys of the block that exist
 
   int32_t pair[GPW];
   bool live[GPW];
@@ -663,7 +656,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
                                                       const PartialT<T>* __restrict__ po,
                                                       float* __restrict__ out, float* __restrict__ lse,
                                                       int64_t row0, int64_t rows, int n, int topk,
-                                                      int causal) {
+                                                      int causal, const int4* __restrict__ seqtab) {
   constexpr int E = D / 16;  // dims per lane
   constexpr int V = E / 4;   // 4-element loads per lane and slot
   typedef typename std::conditional<sizeof(T) == 2, f16x4, f32x4>::type Vec;
@@ -672,7 +665,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   const int c = threadIdx.x & 15;
   const int gbase = (threadIdx.x & 63) & ~15;
   const int64_t row = row0 + r;
-  const int nb = n / kTile;
+  const RowBlocks rb = row_blocks(seqtab, row, n, causal);
   const int32_t* sel = idx + row * topk;
   float acc[E];
 #pragma unroll
@@ -700,7 +693,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
       part[t] = c * E < 32 ? b << (c * E) : 0u;
     }
     const uint32_t bits = or_scatter16(part, c);  // slot s0 + c
-    const bool valid = s0 + c < topk && pair_valid(sel[s0 + c], nb, row, n, causal);
+    const bool valid = s0 + c < topk && sel_block(sel[s0 + c], rb) >= 0;
     const float ls = valid ? __uint_as_float(bits) : -INFINITY;
     float mb = ls;
 #pragma unroll
@@ -765,17 +758,16 @@ hipError_t partial_chunk(const GatherArgs& a, int64_t row0, int64_t rows, hipStr
   while ((1 << lg) < a.topk) ++lg;
   const int shift = 32 + lg;
   const uint64_t magic = ((uint64_t(1) << shift) + uint64_t(a.topk) - 1) / uint64_t(a.topk);
-  const int klim_last = (a.nv > 0 && a.nv < a.n) ? a.nv - (c.nb - 1) * kTile : kTile;
   if (a.causal)
     hipLaunchKernelGGL((gather_partial_kernel<T, D, true>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets,
-                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, klim_last, sl2, po);
+                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, a.seqtab, sl2, po);
   else
     hipLaunchKernelGGL((gather_partial_kernel<T, D, false>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets,
-                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, klim_last, sl2, po);
+                       row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, a.seqtab, sl2, po);
   return hipGetLastError();
 }
 
@@ -783,7 +775,7 @@ template <typename T, int D>
 hipError_t combine_chunk(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
   auto* po = reinterpret_cast<const PartialT<T>*>(a.ws.partial_o);
   hipLaunchKernelGGL((combine_kernel<T, D>), dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0,
-                     s, a.idx, po, a.out, a.lse, row0, rows, a.n, a.topk, a.causal);
+                     s, a.idx, po, a.out, a.lse, row0, rows, a.n, a.topk, a.causal, a.seqtab);
   return hipGetLastError();
 }
 
@@ -839,7 +831,7 @@ hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, 
   }
   hipLaunchKernelGGL(bucket_count_kernel, dim3(static_cast<unsigned>(row_groups)), dim3(256),
                      count_lds, s, a.idx, a.ws.count, a.ws.rank, a.ws.rec,
-                     a.ws.wg_valid, row0, rows, a.n, a.topk, a.causal, c.bh0, rpw, a.qsegs);
+                     a.ws.wg_valid, row0, rows, a.n, a.topk, a.causal, c.bh0, rpw, a.qsegs, a.seqtab);
   hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, a.ws.count, a.ws.offsets,
                      a.ws.items, c.nbuckets, a.item_pairs);
   const int64_t bucket_groups = (c.nbuckets + 255) / 256;
@@ -847,7 +839,7 @@ hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, 
                      dim3(static_cast<unsigned>(row_groups > bucket_groups ? row_groups : bucket_groups)),
                      dim3(256), 0, s, a.idx, a.ws.rank, a.ws.rec, a.ws.wg_valid, a.ws.offsets, a.ws.items,
                      a.ws.item_rec, c.nbuckets, gather_grid(rows, a.topk, c.nbuckets, a.item_pairs), a.ws.list,
-                     row0, rows, a.n, a.topk, c.bh0, a.qsegs, a.item_pairs, rpw);
+                     row0, rows, a.n, a.topk, c.bh0, a.qsegs, a.item_pairs, rpw, a.seqtab);
   return hipGetLastError();
 }
 

@@ -157,7 +157,7 @@ template <typename T, int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void sparse_flash_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     float* __restrict__ out, float* __restrict__ lse, const int32_t* __restrict__ idx, int topk,
-    int n, int klim_last, float scale_log2) {
+    int n, const int4* __restrict__ seqtab, float scale_log2) {
   using L = KvLayout<T, D>;
   extern __shared__ __align__(16) unsigned char smem[];
   T* ks = reinterpret_cast<T*>(smem);
@@ -175,23 +175,30 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
   const T* kb = k + bh * static_cast<int64_t>(n) * D;
   const T* vb = v + bh * static_cast<int64_t>(n) * D;
 
-  // ---- the tile list: the union of the rows' selected blocks
+  // ---- the tile list: the union of the rows' selected blocks (entries are
+  // relative to the first block lo of the tile's sequence)
   int32_t* list = reinterpret_cast<int32_t*>(rm + nb);
   int nlist;
   {
-    const int nbc = CAUSAL ? qt + 1 : nb;  // blocks that can be visible to this tile
+    int lo = 0, hi = nb;
+    if (seqtab) {
+      const int4 e = seqtab[qt];
+      lo = e.x;
+      hi = e.y;
+    }
+    const int nbc = CAUSAL ? qt + 1 : hi;  // blocks lo .. nbc - 1 can be visible to this tile
     int* count = reinterpret_cast<int*>(list + nb);
-    for (int c = tid; c < nbc; c += 256) rm[c] = 0ull;
+    for (int c = lo + tid; c < nbc; c += 256) rm[c] = 0ull;
     __syncthreads();
     const int32_t* ib = idx + tile_row * topk;
     for (int e = tid; e < kTile * topk; e += 256) {
       const int b = ib[e];
-      if (b >= 0 && b < nbc) atomicOr(reinterpret_cast<unsigned long long*>(&rm[b]), 1ull << (e / topk));
+      if (b >= 0 && b < nbc - lo) atomicOr(reinterpret_cast<unsigned long long*>(&rm[lo + b]), 1ull << (e / topk));
     }
     __syncthreads();
     if (wave == 0) {
       int cnt = 0;
-      for (int c0 = 0; c0 < nbc; c0 += 64) {
+      for (int c0 = lo; c0 < nbc; c0 += 64) {
         const int c = c0 + lane;
         const bool f = c < nbc && rm[c] != 0ull;
         const uint64_t m = ballot(f);
@@ -263,14 +270,15 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
               if (16 * t + 4 * g + jj <= qlocal) cm |= 1u << (4 * t + jj);
           vis &= cm;
         }
-        if (cur == nb - 1 && klim_last < kTile) {
-          // a partial last block: keys klim_last .. 63 are padding
+        const int klim = block_keys(seqtab, cur);
+        if (klim < kTile) {
+          // a sequence's partial last block: keys klim .. 63 are padding
           uint32_t km = 0u;
 #pragma unroll
           for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-              if (16 * t + 4 * g + jj < klim_last) km |= 1u << (4 * t + jj);
+              if (16 * t + 4 * g + jj < klim) km |= 1u << (4 * t + jj);
           vis &= km;
         }
       }
@@ -452,7 +460,7 @@ __global__ __launch_bounds__(256) void static_combine_kernel(const int4* __restr
 
 template <typename T, int D, bool CAUSAL>
 hipError_t launch_union(const void* q, const void* k, const void* v, float* out, float* lse,
-                        const int32_t* idx, int topk, int klim_last, int64_t bh, int n, float scale,
+                        const int32_t* idx, int topk, const int4* seqtab, int64_t bh, int n, float scale,
                         hipStream_t s) {
   using L = KvLayout<T, D>;
   const int nb = n / kTile;
@@ -466,7 +474,7 @@ hipError_t launch_union(const void* q, const void* k, const void* v, float* out,
   }
   const dim3 grid(static_cast<unsigned>(bh * (n / kTile)));
   hipLaunchKernelGGL(kern, grid, dim3(256), smem, s, static_cast<const T*>(q),
-                     static_cast<const T*>(k), static_cast<const T*>(v), out, lse, idx, topk, n, klim_last,
+                     static_cast<const T*>(k), static_cast<const T*>(v), out, lse, idx, topk, n, seqtab,
                      scale * kLog2e);
   return hipGetLastError();
 }
@@ -474,9 +482,9 @@ hipError_t launch_union(const void* q, const void* k, const void* v, float* out,
 template <typename T, int D>
 hipError_t dispatch_dynamic(const void* q, const void* k, const void* v, float* out, float* lse,
                             const int32_t* idx, int64_t bh, int n, int topk, float scale,
-                            int causal, hipStream_t s, int klim_last) {
-  return causal ? launch_union<T, D, true>(q, k, v, out, lse, idx, topk, klim_last, bh, n, scale, s)
-                : launch_union<T, D, false>(q, k, v, out, lse, idx, topk, klim_last, bh, n, scale, s);
+                            int causal, hipStream_t s, const int4* seqtab) {
+  return causal ? launch_union<T, D, true>(q, k, v, out, lse, idx, topk, seqtab, bh, n, scale, s)
+                : launch_union<T, D, false>(q, k, v, out, lse, idx, topk, seqtab, bh, n, scale, s);
 }
 
 template <typename T, int D>
@@ -494,8 +502,7 @@ hipError_t launch_static_t(const StaticLaunch& a, hipStream_t s) {
 hipError_t launch_sparse_flash_dynamic(const void* q, const void* k, const void* v, float* out,
                                        float* lse, const int32_t* idx, int64_t bh, int n, int d,
                                        int topk, float scale, int causal, bsa_dtype dtype,
-                                       hipStream_t stream, int nv) {
-  const int kl = (nv > 0 && nv < n) ? nv - (n / kTile - 1) * kTile : kTile;
+                                       hipStream_t stream, const int4* kl) {
   if (dtype == BSA_BF16)
     return d == 64 ? dispatch_dynamic<bf16_bits, 64>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl)
                    : dispatch_dynamic<bf16_bits, 128>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl);

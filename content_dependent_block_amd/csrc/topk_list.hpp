@@ -47,19 +47,20 @@ struct TopList {
   }
 };
 
-// Write the first `keff` blocks of a sorted list in ascending block order to
-// dst[0 .. keff), then -1 up to dst[topk - 1].  Position of an entry =
-// number of selected entries with a smaller block index.
+// Write the first `keff` blocks of a sorted list, less `base` (the first
+// block of the query's sequence), in ascending order to dst[0 .. keff), then
+// -1 up to dst[topk - 1].  Position of an entry = number of selected entries
+// with a smaller block index.
 template <int KL>
 __device__ __forceinline__ void emit_ascending(const TopList<KL>& l, int keff, int topk,
-                                               int32_t* __restrict__ dst) {
+                                               int32_t* __restrict__ dst, int base = 0) {
 #pragma unroll
   for (int j = 0; j < KL; ++j) {
     if (j < keff) {
       int pos = 0;
 #pragma unroll
       for (int t = 0; t < KL; ++t) pos += (t < keff && l.b[t] < l.b[j]) ? 1 : 0;
-      dst[pos] = l.b[j];
+      dst[pos] = l.b[j] - base;
     }
   }
   for (int t = keff; t < topk; ++t) dst[t] = -1;

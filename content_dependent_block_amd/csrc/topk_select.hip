@@ -6,8 +6,10 @@
 // scoring kernel instead (coarse_score.hip); this kernel serves the
 // stage-level entry point and the panel strategy.
 //
-// Semantics: candidates are all n/64 blocks, or in the causal variant the
-// blocks up to the query's own block, which is always kept.  k_eff =
+// Semantics: candidates are all blocks of the query's sequence (all n/64
+// blocks of the head unless a block table splits the head into several
+// sequences), or in the causal variant those up to the query's own block,
+// which is always kept; indices are relative to the sequence's first block.  k_eff =
 // min(k, #candidates), where k is the head's budget (one k for all heads
 // unless per-head budgets are given; nishantmodi.me
 // "sparse-attention-triton-bench", section "What's next": per-head sparsity
@@ -40,21 +42,21 @@ template <int KL>
 __global__ __launch_bounds__(64) void topk_lane_kernel(const float* __restrict__ panel,
                                                        int32_t* __restrict__ idx, int64_t row0,
                                                        int64_t prows, int n, int topk,
-                                                       const HeadBudget budget, int causal) {
+                                                       const HeadBudget budget, int causal,
+                                                       const int4* __restrict__ seqtab) {
   const int lane = threadIdx.x;
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 64 + lane;  // prows % 64 == 0
-  const int nb = n / kTile;
   const int64_t grow = row0 + r;
-  const int qb = static_cast<int>(grow % n) / kTile;  // the same in all 64 rows
-  const int nvalid = causal ? qb + 1 : nb;
+  const RowBlocks rb = row_blocks(seqtab, grow, n, causal);  // the same in all 64 rows
+  const int nvalid = rb.hi;
   const int kh = budget.k[(grow / n) % budget.heads];  // the same in all 64 rows
-  const int keff = kh < nvalid ? kh : nvalid;
+  const int keff = kh < rb.hi - rb.lo ? kh : rb.hi - rb.lo;
   const float* col = panel + r;
-  const int forced = causal ? qb : -1;
+  const int forced = causal ? rb.own : -1;
 
   TopList<KL> l;
   l.init();
-  int beta = 0;
+  int beta = rb.lo;
   for (; beta + 8 <= nvalid; beta += 8) {
     float v[8];
 #pragma unroll
@@ -66,7 +68,7 @@ __global__ __launch_bounds__(64) void topk_lane_kernel(const float* __restrict__
     const float v = col[static_cast<int64_t>(beta) * prows];
     l.offer(beta == forced ? INFINITY : v, beta);
   }
-  emit_ascending<KL>(l, keff, topk, idx + grow * topk);
+  emit_ascending<KL>(l, keff, topk, idx + grow * topk, rb.lo);
 }
 
 // Binary radix search for the k-th largest key over NV keys per lane.
@@ -97,24 +99,23 @@ template <int NPER>
 __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict__ panel,
                                                         int32_t* __restrict__ idx, int64_t row0,
                                                         int64_t prows, int n, int topk,
-                                                        const HeadBudget budget, int causal) {
+                                                        const HeadBudget budget, int causal,
+                                                        const int4* __restrict__ seqtab) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nb = n / kTile;
   for (int rr = 0; rr < 16; ++rr) {
     const int64_t r = static_cast<int64_t>(blockIdx.x) * 64 + wave * 16 + rr;
     const int64_t grow = row0 + r;
-    const int qb = static_cast<int>(grow % n) / kTile;
-    const int nvalid = causal ? qb + 1 : nb;
+    const RowBlocks rb = row_blocks(seqtab, grow, n, causal);
     const int kh = budget.k[(grow / n) % budget.heads];
-    const int keff = kh < nvalid ? kh : nvalid;
+    const int keff = kh < rb.hi - rb.lo ? kh : rb.hi - rb.lo;
     int32_t* dst = idx + grow * topk;
     uint32_t key[NPER];
 #pragma unroll
     for (int j = 0; j < NPER; ++j) {
       const int e = lane + 64 * j;
       uint32_t kk = 0u;  // not a candidate: below every score
-      if (e < nvalid)
-        kk = (causal && e == qb) ? 0xffffffffu : order_key(panel[static_cast<int64_t>(e) * prows + r]);
+      if (e >= rb.lo && e < rb.hi)
+        kk = (causal && e == rb.own) ? 0xffffffffu : order_key(panel[static_cast<int64_t>(e) * prows + r]);
       key[j] = kk;
     }
     bool early;
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
       const int eq_rank = eq_base + static_cast<int>(lanes_below(eqm));
       const bool sel = key[j] > thr || (is_eq && eq_rank < need);
       const uint64_t selm = ballot(sel);
-      if (sel) dst[out_base + static_cast<int>(lanes_below(selm))] = lane + 64 * j;
+      if (sel) dst[out_base + static_cast<int>(lanes_below(selm))] = lane + 64 * j - rb.lo;
       out_base += __popcll(selm);
       eq_base += __popcll(eqm);
     }
@@ -142,30 +143,31 @@ __global__ __launch_bounds__(256) void topk_wave_kernel(const float* __restrict_
 
 template <int NPER>
 void launch_wave(const float* panel, int32_t* idx, int64_t row0, int64_t rows, int n, int topk,
-                 const HeadBudget& hb, int causal, hipStream_t s) {
+                 const HeadBudget& hb, int causal, const int4* seqtab, hipStream_t s) {
   hipLaunchKernelGGL((topk_wave_kernel<NPER>), dim3(static_cast<unsigned>(rows / 64)), dim3(256), 0, s,
-                     panel, idx, row0, rows, n, topk, hb, causal);
+                     panel, idx, row0, rows, n, topk, hb, causal, seqtab);
 }
 
 }  // namespace
 
 hipError_t launch_topk_select(const float* panel, int32_t* idx, int64_t row0, int64_t rows, int n,
-                              int topk, const HeadBudget& hb, int causal, hipStream_t s) {
+                              int topk, const HeadBudget& hb, int causal, hipStream_t s,
+                              const int4* seqtab) {
   const dim3 grid(static_cast<unsigned>(rows / 64));
   if (topk <= 8) {
-    hipLaunchKernelGGL((topk_lane_kernel<8>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, hb, causal);
+    hipLaunchKernelGGL((topk_lane_kernel<8>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, hb, causal, seqtab);
   } else if (topk <= 16) {
-    hipLaunchKernelGGL((topk_lane_kernel<16>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, hb, causal);
+    hipLaunchKernelGGL((topk_lane_kernel<16>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, hb, causal, seqtab);
   } else if (topk <= 32) {
-    hipLaunchKernelGGL((topk_lane_kernel<32>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, hb, causal);
+    hipLaunchKernelGGL((topk_lane_kernel<32>), grid, dim3(64), 0, s, panel, idx, row0, rows, n, topk, hb, causal, seqtab);
   } else {
     const int nb = n / kTile;
-    if (nb <= 64) launch_wave<1>(panel, idx, row0, rows, n, topk, hb, causal, s);
-    else if (nb <= 128) launch_wave<2>(panel, idx, row0, rows, n, topk, hb, causal, s);
-    else if (nb <= 256) launch_wave<4>(panel, idx, row0, rows, n, topk, hb, causal, s);
-    else if (nb <= 512) launch_wave<8>(panel, idx, row0, rows, n, topk, hb, causal, s);
-    else if (nb <= 1024) launch_wave<16>(panel, idx, row0, rows, n, topk, hb, causal, s);
-    else launch_wave<32>(panel, idx, row0, rows, n, topk, hb, causal, s);
+    if (nb <= 64) launch_wave<1>(panel, idx, row0, rows, n, topk, hb, causal, seqtab, s);
+    else if (nb <= 128) launch_wave<2>(panel, idx, row0, rows, n, topk, hb, causal, seqtab, s);
+    else if (nb <= 256) launch_wave<4>(panel, idx, row0, rows, n, topk, hb, causal, seqtab, s);
+    else if (nb <= 512) launch_wave<8>(panel, idx, row0, rows, n, topk, hb, causal, seqtab, s);
+    else if (nb <= 1024) launch_wave<16>(panel, idx, row0, rows, n, topk, hb, causal, seqtab, s);
+    else launch_wave<32>(panel, idx, row0, rows, n, topk, hb, causal, seqtab, s);
   }
   return hipGetLastError();
 }

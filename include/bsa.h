@@ -284,6 +284,53 @@ bsa_status bsa_backward(bsa_handle h, const void* q, const void* k, const void* 
                         bsa_dtype dtype, int block, int topk, float scale,
                         int causal, void* stream);
 
+/* --------------------------------------------------- variable lengths -- */
+
+/* A batch of sequences of different lengths (yayme/CUDA-kernel README, file
+ * table: the correctness tests include lengths that are not a multiple of
+ * the tile; nishantmodi.me "sparse-attention-triton-bench", section "Stage 1:
+ * coarse scoring": the blocks are those of each sequence's own keys).
+ * Sequence i is rows cu_seqlens[i] .. cu_seqlens[i + 1] - 1 of every head,
+ * and it is attended to on its own: its key blocks start at its first row
+ * (the last one may be partial and is then pooled over the keys it has), a
+ * query's candidates are the blocks of its sequence only, and in the causal
+ * variant position j <= i counts within the sequence.
+ *  q, k, v        device, [heads][total][d], dtype, total = cu_seqlens[nseq]
+ *                 (each head's rows of all sequences, one after the other).
+ *  out            device, float32 [heads][total][d].
+ *  block_idx_out  device, int32 [heads][total][topk] or NULL: each query's
+ *                 selected blocks numbered from its sequence's first block
+ *                 (0 = rows cu_seqlens[i] .. cu_seqlens[i] + 63), ascending,
+ *                 -1 padded; k_eff = min(budget, blocks of the sequence up to
+ *                 the query's own block when causal).
+ *  lse_out        device, float32 [heads][total] or NULL: as for
+ *                 bsa_forward_train (what bsa_backward_varlen needs).
+ *  cu_seqlens     host, int32 [nseq + 1]: cu_seqlens[0] = 0, non-decreasing
+ *                 (empty sequences allowed), total >= 1; read during the call
+ *                 only.  Else BSA_ERR_INVALID_ARG.
+ *  head_topk      host, int32 [heads] or NULL: per-head budgets as for
+ *                 bsa_forward_budgets, with topk the index row length.
+ * The sequences padded to whole 64-row blocks may take at most 2048 blocks
+ * per head (BSA_ERR_UNSUPPORTED).  Everything else as for bsa_forward; each
+ * sequence's result equals bsa_forward's on that sequence alone. */
+bsa_status bsa_forward_varlen(bsa_handle h, const void* q, const void* k,
+                              const void* v, float* out, int32_t* block_idx_out,
+                              float* lse_out, const int32_t* cu_seqlens, int nseq,
+                              int heads, int d, bsa_dtype dtype, int block,
+                              const int32_t* head_topk, int topk, float scale,
+                              int causal, void* stream);
+
+/* bsa_backward for a batch laid out as for bsa_forward_varlen: out, lse and
+ * block_idx as that call wrote them (lse_out and block_idx_out given), dout,
+ * dq, dk, dv float32 [heads][total][d].  Everything else as for
+ * bsa_backward. */
+bsa_status bsa_backward_varlen(bsa_handle h, const void* q, const void* k,
+                               const void* v, const float* out, const float* dout,
+                               const int32_t* block_idx, const float* lse, float* dq,
+                               float* dk, float* dv, const int32_t* cu_seqlens,
+                               int nseq, int heads, int d, bsa_dtype dtype, int block,
+                               int topk, float scale, int causal, void* stream);
+
 /* Stage 2 alone on caller-supplied selections (nishantmodi.me
  * "sparse-attention-triton-bench", sections "Stage 2: fine attention" and "The
  * Triton kernel": each query attends only to the keys of the blocks it

@@ -55,6 +55,10 @@ def test_null_handle_is_rejected(m):
     L = m._binding._lib
     assert L.bsa_forward(None, None, None, None, None, None, 1, 1, 64, 64, 1, 64, 1, 0.1, 0,
                          None) == m.BSA_ERR_INVALID_ARG
+    assert L.bsa_forward_varlen(None, None, None, None, None, None, None, None, 1, 1, 64, 1, 64, None, 1, 0.1,
+                                0, None) == m.BSA_ERR_INVALID_ARG
+    assert L.bsa_backward_varlen(None, None, None, None, None, None, None, None, None, None, None, None, 1, 1,
+                                 64, 1, 64, 1, 0.1, 0, None) == m.BSA_ERR_INVALID_ARG
     assert L.bsa_set_option(None, 0, 1) == m.BSA_ERR_INVALID_ARG
     assert L.bsa_profile_enable(None, 1) == m.BSA_ERR_INVALID_ARG
     assert L.bsa_destroy(None) == m.BSA_OK

@@ -16,6 +16,10 @@ Recipe (the same for every workload; all batch = 1):
   if dtype == bf16: round q, k, v to bf16, nearest-even
 Backward workloads add an incoming gradient of the float32 output:
   dout = default_rng(seed + 1000).standard_normal([b, h, n, d], float32)
+A batch of sequences of different lengths draws sequence i by the same recipe
+with n = lengths[i] and seed + i (its key blocks, and offsets, start at its own
+first row) and lays the batch out [heads, total, d]: each head's rows of all
+sequences one after the other.
 """
 from __future__ import annotations
 
@@ -133,3 +137,18 @@ def grad_output(shape, seed: int) -> np.ndarray:
     """The incoming gradient dout for a backward workload: float32 N(0, 1)."""
     rng = np.random.default_rng(seed + 1000)
     return rng.standard_normal(tuple(shape), dtype=np.float32)
+
+
+def generate_varlen(w: Workload | str, lengths, *, heads: int | None = None,
+                    seed: int | None = None) -> tuple[Inputs, np.ndarray]:
+    """A batch of sequences of the given lengths (see the module docstring).
+    Returns (inputs as [1, heads, total, d] arrays, cu_seqlens int32)."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    s0 = w.seed if seed is None else seed
+    parts = [generate(w, n=int(n), heads=heads, batch=1, seed=s0 + i) for i, n in enumerate(lengths)]
+    cat = lambda name: (None if getattr(parts[0], name) is None
+                        else np.ascontiguousarray(np.concatenate([getattr(p, name) for p in parts], axis=2)))
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return Inputs(cat("q"), cat("k"), cat("v"), cat("q_bits"), cat("k_bits"), cat("v_bits")), cu
