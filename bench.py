@@ -83,8 +83,14 @@ def candidate_pairs(w: W.Workload) -> int:
 
 def stage_work(w: W.Workload, nnz: int = 0):
     """Algorithmic work per step of each kernel over the whole problem:
-    (flops, bytes).  Bytes count each compulsory read/write once; a kernel's
-    roofline bound is whichever of the two takes longer at the MI355X peaks."""
+    (flops, bytes).  Only the method's own work counts: the matmul flops of
+    scoring and of attention over the visible pairs, and each compulsory
+    tensor (Q, K, V, representatives, indices, output; for the backward dout,
+    out, lse and the gradients) read or written once.  Buffers that are this
+    implementation's choice (score panel, bucket lists, per-pair partial and
+    dq rows) count nothing, so a kernel's fraction says how far it is from the
+    method's bound.  A kernel's roofline bound is whichever of flops and bytes
+    takes longer at the MI355X peaks."""
     s = 2 if w.dtype == "bf16" else 4
     qkv = w.bh * w.n * w.d * s
     out_b = w.bh * w.n * w.d * 4
@@ -95,36 +101,27 @@ def stage_work(w: W.Workload, nnz: int = 0):
                 "static_combine": (0, 0)}
     repr_b = w.bh * w.nb * w.d * 4
     cand = candidate_pairs(w)
-    panel = cand * 4
     idx = w.bh * w.n * w.topk * 4
-    if not w.causal:
-        sel_pairs = w.bh * w.n * min(w.topk, w.nb)
-    else:
-        i = np.arange(w.n, dtype=np.int64)
-        sel_pairs = int(w.bh * np.minimum(w.topk, i // w.block + 1).sum())
-    partial = sel_pairs * w.d * (2 if w.dtype == "bf16" else 4)
     rows = w.bh * w.n
-    dq_rows = sel_pairs * w.d * s  # per-pair dq rows: bf16 (bf16 inputs) or fp32
     return {
         "block_pool": (0, qkv + repr_b),
-        "coarse_score": (2 * w.d * cand, qkv + repr_b + panel),
-        "topk_select": (0, panel + idx),
+        "coarse_score": (2 * w.d * cand, qkv + repr_b),
+        "topk_select": (0, idx),
         # fused scoring + selection: q and the representatives in, indices out
         "coarse_select": (2 * w.d * cand, qkv + repr_b + idx),
-        # block-gather attention kernel: reads Q, K, V once, writes the partials
-        "sparse_flash_fwd": (fine_flops, 3 * qkv + idx + partial),
-        "gather_index": (0, 2 * idx + 3 * sel_pairs * 4),
-        "gather_combine": (0, partial + idx + out_b),
-        # backward: out, dout and lse in; per-row (lse, delta) and (bf16 inputs) bf16 dout out
-        "bwd_prep": (0, 2 * out_b + rows * (4 + 8) + (qkv if w.dtype == "bf16" else 0)),
-        "bwd_index": (0, 2 * idx + 3 * sel_pairs * 4),
-        # S, dP, dQ, dK, dV: five products per visible (query, key) pair; reads
-        # Q, K, V, dout (bf16 copy for bf16 inputs) and the row statistics
-        # once, writes the per-pair dq rows
-        "bwd_pairs": (10 * w.d * visible_pairs(w),
-                      3 * qkv + (qkv if w.dtype == "bf16" else out_b) + rows * 8 + dq_rows),
-        # per-pair dq rows in; dq, dk, dv out
-        "bwd_reduce": (0, dq_rows + idx + 3 * out_b),
+        # block-gather attention: the fine flops; Q, K, V and the indices read once
+        "sparse_flash_fwd": (fine_flops, 3 * qkv + idx),
+        "gather_index": (0, 0),
+        # the merge writes the output once
+        "gather_combine": (0, out_b),
+        # backward: out, dout and lse read once
+        "bwd_prep": (0, 2 * out_b + rows * 4),
+        "bwd_index": (0, 0),
+        # S, dP, dQ, dK, dV: five products per visible (query, key) pair; Q, K,
+        # V and the indices read once, dk and dv written once
+        "bwd_pairs": (10 * w.d * visible_pairs(w), 3 * qkv + idx + 2 * out_b),
+        # dq written once
+        "bwd_reduce": (0, out_b),
         "ragged_copy": (0, 0),
     }
 
