@@ -360,54 +360,67 @@ __global__ __launch_bounds__(256, (BwdLayout<T, D>::kWaves)) void bwd_pair_kerne
         dsv[tt][jj] = p * (dp[tt][jj] - lr.y);
       }
 
-    // dQ^T = K^T dS^T: this block's contribution to the pair's dq.
-    f32x4 acc[D / 16];
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // dQ^T = K^T dS^T: this block's contribution to the pair's dq, in two
+    // halves of the output dims (half the accumulators live at a time).
+    constexpr int DH = D / 32;  // 16-dim output tiles per half
     if constexpr (L::kBf16) {
+      bf16x8 bs[2];
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        bf16x8 bs;
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          bs[i] = f32_to_bf16(dsv[2 * kk][i]);
-          bs[4 + i] = f32_to_bf16(dsv[2 * kk + 1][i]);
+          bs[kk][i] = f32_to_bf16(dsv[2 * kk][i]);
+          bs[kk][4 + i] = f32_to_bf16(dsv[2 * kk + 1][i]);
         }
+      // The pair's dq row, rounded to bf16 (fp32's range: no scale needed);
+      // acc[t][e] = dq of dim 16 (DH h + t) + 4g + e (C layout: row 4g + e).
+      uint16_t* dst = reinterpret_cast<uint16_t*>(dq_part) + static_cast<int64_t>(pair) * D + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + (16 * dt + c16) * L::KTP + 32 * kk + 8 * g);
-          acc[dt] = mfma_16x16x32_bf16(a, bs, acc[dt]);
-        }
-      }
-      // The pair's dq row, rounded to bf16 (fp32's range: no scale needed).
-      if (live) {
-        // acc[dt][e] = dq of dim 16 dt + 4g + e (C layout: row 4g + e)
-        uint16_t* dst = reinterpret_cast<uint16_t*>(dq_part) + static_cast<int64_t>(pair) * D + 4 * g;
+      for (int h = 0; h < 2; ++h) {
+        f32x4 acc[DH];
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const f32x4 a = acc[dt] * scale;
-          const uint32_t lo = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(a[0]))) |
-                              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(a[1]))) << 16);
-          const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(a[2]))) |
-                              (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(a[3]))) << 16);
-          *reinterpret_cast<uint2*>(dst + 16 * dt) = make_uint2(lo, hi);
+        for (int t = 0; t < DH; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int t = 0; t < DH; ++t) {
+            const int dt = DH * h + t;
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + (16 * dt + c16) * L::KTP + 32 * kk + 8 * g);
+            acc[t] = mfma_16x16x32_bf16(a, bs[kk], acc[t]);
+          }
+        if (live) {
+#pragma unroll
+          for (int t = 0; t < DH; ++t) {
+            const f32x4 a = acc[t] * scale;
+            const uint32_t lo = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(a[0]))) |
+                                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(a[1]))) << 16);
+            const uint32_t hi = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(a[2]))) |
+                                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, f32_to_bf16(a[3]))) << 16);
+            *reinterpret_cast<uint2*>(dst + 16 * (DH * h + t)) = make_uint2(lo, hi);
+          }
         }
       }
     } else {
+      float* dst = dq_part + static_cast<int64_t>(pair) * D + 4 * g;
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
+      for (int h = 0; h < 2; ++h) {
+        f32x4 acc[DH];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const T* kr = ks + (16 * tt + 4 * g + jj) * L::KP + c16;
+        for (int t = 0; t < DH; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma_16x16x4_f32(kr[16 * dt], dsv[tt][jj], acc[dt]);
-        }
-      if (live) {
-        float* dst = dq_part + static_cast<int64_t>(pair) * D + 4 * g;
+        for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-        for (int dt = 0; dt < D / 16; ++dt) {
-          const f32x4 a = acc[dt] * scale;
-          *reinterpret_cast<float4*>(dst + 16 * dt) = make_float4(a[0], a[1], a[2], a[3]);
+          for (int jj = 0; jj < 4; ++jj) {
+            const T* kr = ks + (16 * tt + 4 * g + jj) * L::KP + c16;
+#pragma unroll
+            for (int t = 0; t < DH; ++t) acc[t] = mfma_16x16x4_f32(kr[16 * (DH * h + t)], dsv[tt][jj], acc[t]);
+          }
+        if (live) {
+#pragma unroll
+          for (int t = 0; t < DH; ++t) {
+            const f32x4 a = acc[t] * scale;
+            *reinterpret_cast<float4*>(dst + 16 * (DH * h + t)) = make_float4(a[0], a[1], a[2], a[3]);
+          }
         }
       }
     }
