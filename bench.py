@@ -223,6 +223,25 @@ def cpu_baseline_backward(w: W.Workload, inp, dout):
                       f"fp64 on the oracle's own selection; {dt:.2f} s wall, scaled to {w.heads} heads"}
 
 
+def union_stats(idx, w: W.Workload):
+    """For query tiles of 16, 32 and 64 rows: the mean number of distinct
+    blocks the tile's rows selected (the blocks a query-tile union visits),
+    and the flops a union kernel issues when every row of the tile meets
+    every block of the union (S = Q K^T and O = P V over 64 keys each)."""
+    import torch
+    bh, n, k = idx.shape[0] * idx.shape[1], idx.shape[2], idx.shape[3]
+    sel = idx.reshape(bh, n, k).long()
+    out = {}
+    for tq in (16, 32, 64):
+        t = sel.reshape(bh, n // tq, tq * k)
+        hit = torch.zeros((bh, n // tq, w.nb + 1), dtype=torch.bool, device=idx.device)
+        hit.scatter_(2, torch.where(t >= 0, t, torch.full_like(t, w.nb)), True)
+        per_tile = hit[:, :, :w.nb].sum(dim=2).double()
+        out[str(tq)] = {"blocks_per_tile": round(float(per_tile.mean()), 2),
+                        "issued_tflop": round(float(per_tile.sum()) * tq * 64 * 4 * w.d / 1e12, 4)}
+    return out
+
+
 class Runner:
     """Inputs of one workload resident on the device and its step function."""
 
@@ -243,6 +262,7 @@ class Runner:
         self.mask = None
         self.tiles = None
         self.dout_np = None
+        self.idx = None
         if w.static:
             rp, col, rm = m.bsa_tiles_window_stride(w.n, w.window, w.stride)
             self.nnz = int(col.size)
@@ -256,6 +276,7 @@ class Runner:
 
             def step():
                 m.bsa_forward(h, q, k, v, out, idx, topk=w.topk, scale=w.scale, causal=w.causal)
+            self.idx = idx
         else:
             idx = torch.empty(q.shape[:3] + (w.topk,), dtype=torch.int32, device=dev)
             lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
@@ -385,7 +406,11 @@ def main():
     ap.add_argument("--other-steps", type=int, default=20, help="cold steps for each other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-positions", type=int, default=32768)
-    ap.add_argument("--fine-strategy", choices=["block_gather", "query_tile"], default="block_gather")
+    ap.add_argument("--fine-strategy", choices=["block_gather", "query_tile", "per_query"], default="block_gather")
+    ap.add_argument("--union-rows", type=int, choices=[16, 32, 64], default=64,
+                    help="query-tile rows of the query_tile fine strategy")
+    ap.add_argument("--union-stats", action="store_true",
+                    help="report the query-tile unions of the selection (16, 32 and 64 rows)")
     ap.add_argument("--select-strategy", choices=["fused", "panel"], default="fused")
     ap.add_argument("--panel-chunk-mb", type=int, default=0, help="coarse-score panel chunk (0 = default)")
     ap.add_argument("--fine-chunk-mb", type=int, default=0, help="block-gather partial chunk (0 = default)")
@@ -418,7 +443,9 @@ def main():
     lib = m.BlockSparseAttention(0)
     h = lib.handle
     m.bsa_set_option(h, m.BSA_OPT_FINE_STRATEGY,
-                     m.BSA_FINE_BLOCK_GATHER if args.fine_strategy == "block_gather" else m.BSA_FINE_QUERY_TILE)
+                     {"block_gather": m.BSA_FINE_BLOCK_GATHER, "query_tile": m.BSA_FINE_QUERY_TILE,
+                      "per_query": m.BSA_FINE_PER_QUERY}[args.fine_strategy])
+    m.bsa_set_option(h, m.BSA_OPT_UNION_ROWS, args.union_rows)
     m.bsa_set_option(h, m.BSA_OPT_SELECT_STRATEGY,
                      m.BSA_SELECT_FUSED if args.select_strategy == "fused" else m.BSA_SELECT_PANEL)
     if args.panel_chunk_mb:
@@ -430,6 +457,7 @@ def main():
 
     r = Runner(m, lib, w, args.which, args)
     res = measure(r, args, scratch, args.steps, args.warmup)
+    unions = union_stats(r.idx, w) if args.union_stats and args.which == "forward" and not w.static else None
     inp, dout_np = r.inp, r.dout_np
     static_mask = None
     if w.static and not args.no_cpu_baseline:
@@ -466,6 +494,7 @@ def main():
     else:
         cfg.update(block=w.block, topk=w.topk, causal=w.causal, select_strategy=args.select_strategy,
                    fine_strategy=args.fine_strategy, panel_chunk_mb=args.panel_chunk_mb or 128,
+                   union_rows=args.union_rows,
                    fine_chunk_mb=args.fine_chunk_mb or 1024)
     result = {
         "metric": METRIC if args.which == "forward" else METRIC_BWD,
@@ -495,6 +524,8 @@ def main():
     }
     if others:
         result["workloads"] = others
+    if unions:
+        result["query_tile_unions"] = unions
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = (cpu_baseline(w, inp, args.cpu_positions, static_mask)
                                   if args.which == "forward" else cpu_baseline_backward(w, inp, dout_np))

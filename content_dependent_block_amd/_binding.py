@@ -34,7 +34,8 @@ STAGE_NAMES = ("block_pool", "coarse_score", "topk_select", "sparse_flash_fwd", 
 BSA_OPT_PANEL_CHUNK_BYTES, BSA_OPT_FINE_STRATEGY, BSA_OPT_FINE_CHUNK_BYTES = 0, 1, 2
 BSA_OPT_SELECT_STRATEGY = 3
 BSA_OPT_STATIC_ITEM_TILES = 4
-BSA_FINE_BLOCK_GATHER, BSA_FINE_QUERY_TILE = 0, 1
+BSA_OPT_UNION_ROWS = 5
+BSA_FINE_BLOCK_GATHER, BSA_FINE_QUERY_TILE, BSA_FINE_PER_QUERY = 0, 1, 2
 BSA_SELECT_FUSED, BSA_SELECT_PANEL = 0, 1
 
 _P, _I, _I64, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float

@@ -53,6 +53,7 @@ struct bsa_handle_s {
   bool tab_ev_live = false;
   Buf s_part, s_lse;  // static mode: partial rows of split query tiles and their log-sum-exp
   int64_t static_item_tiles = 0;  // 0: chosen per call; else the most key tiles per work item
+  int union_rows = 64;            // query-tile rows of the query-tile union fine stage
   // timing
   bool profiling = false;
   struct Rec {
@@ -303,7 +304,7 @@ BSA_API bsa_status bsa_set_option(bsa_handle h, int option, int64_t value) {
       h->panel_chunk_bytes = value;
       return BSA_OK;
     case BSA_OPT_FINE_STRATEGY:
-      if (value != BSA_FINE_BLOCK_GATHER && value != BSA_FINE_QUERY_TILE)
+      if (value != BSA_FINE_BLOCK_GATHER && value != BSA_FINE_QUERY_TILE && value != BSA_FINE_PER_QUERY)
         return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: unknown fine strategy %lld", (long long)value);
       h->fine_strategy = static_cast<int>(value);
       return BSA_OK;
@@ -319,6 +320,12 @@ BSA_API bsa_status bsa_set_option(bsa_handle h, int option, int64_t value) {
     case BSA_OPT_STATIC_ITEM_TILES:
       if (value < 0) return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: static item tiles must be >= 0");
       h->static_item_tiles = value;
+      return BSA_OK;
+    case BSA_OPT_UNION_ROWS:
+      if (value != 16 && value != 32 && value != 64)
+        return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: union rows must be 16, 32 or 64 (got %lld)",
+                    (long long)value);
+      h->union_rows = static_cast<int>(value);
       return BSA_OK;
     default:
       return fail(h, BSA_ERR_INVALID_ARG, "bsa_set_option: unknown option %d", option);
@@ -653,7 +660,12 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   if (h->fine_strategy == BSA_FINE_QUERY_TILE)
     return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
       return bsa::launch_sparse_flash_dynamic(q, k, v, out, lse, idx, s.bh(), s.n, s.d, topk, scale,
-                                              causal, dt, st, tab);
+                                              causal, dt, st, tab, h->union_rows);
+    });
+  if (h->fine_strategy == BSA_FINE_PER_QUERY)
+    return timed_launch(h, BSA_STAGE_FINE, st, "sparse_flash_fwd", [&] {
+      return bsa::launch_sparse_flash_per_query(q, k, v, out, lse, idx, s.bh() * s.n, s.n, s.d, topk, scale,
+                                                causal, dt, st, tab);
     });
   const int64_t total = s.bh() * s.n;
   const size_t per_row = bsa::gather_pair_bytes(s.d, dt) * size_t(topk);

@@ -64,13 +64,22 @@ hipError_t launch_topk_select(const float* panel, int32_t* idx, int64_t row0, in
                               int topk, const HeadBudget& budget, int causal, hipStream_t stream,
                               const int4* seqtab = nullptr);
 
-// sparse_flash_fwd, dynamic: per 64-query tile the union of its rows'
-// selected blocks, each row masked to its own selection.  lse (nullable):
-// per row log-sum-exp of the scaled scores, natural log.
+// sparse_flash_fwd, dynamic: per query tile of `rows` rows (16, 32 or 64)
+// the union of its rows' selected blocks, each row masked to its own
+// selection.  lse (nullable): per row log-sum-exp of the scaled scores,
+// natural log.
 hipError_t launch_sparse_flash_dynamic(const void* q, const void* k, const void* v, float* out,
                                        float* lse, const int32_t* idx, int64_t bh, int n, int d,
                                        int topk, float scale, int causal, bsa_dtype dtype,
-                                       hipStream_t stream, const int4* seqtab = nullptr);
+                                       hipStream_t stream, const int4* seqtab = nullptr, int rows = 64);
+
+// sparse_flash_fwd, per query: one wave per query row walks the row's
+// selected blocks in slot order with an online softmax on the vector units
+// (no tile sharing between queries).  lse as above.
+hipError_t launch_sparse_flash_per_query(const void* q, const void* k, const void* v, float* out,
+                                         float* lse, const int32_t* idx, int64_t rows, int n, int d,
+                                         int topk, float scale, int causal, bsa_dtype dtype,
+                                         hipStream_t stream, const int4* seqtab = nullptr);
 
 // sparse_flash_fwd, static tile list, run as host-scheduled work items (each
 // at most S key tiles of one query tile, heaviest first), then a merge of the

@@ -153,12 +153,15 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const T* ks, const T*
   st.l = st.l * alpha + lsum;
 }
 
-template <typename T, int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void sparse_flash_kernel(
+// W waves per workgroup own a query tile of TQ = 16 W rows (W = 4: one
+// 64-row block; W = 1, 2: part of one).
+template <typename T, int D, bool CAUSAL, int W>
+__global__ __launch_bounds__(64 * W) void sparse_flash_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     float* __restrict__ out, float* __restrict__ lse, const int32_t* __restrict__ idx, int topk,
     int n, const int4* __restrict__ seqtab, float scale_log2) {
-  using L = KvLayout<T, D>;
+  constexpr int NTH = 64 * W, TQ = 16 * W;
+  using L = KvLayout<T, D, NTH>;
   extern __shared__ __align__(16) unsigned char smem[];
   T* ks = reinterpret_cast<T*>(smem);
   T* vs = reinterpret_cast<T*>(smem + L::K_BYTES);
@@ -166,12 +169,14 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c16 = lane & 15;
-  const int nqt = n / kTile;
-  const int nb = nqt;
+  const int nqt = n / TQ;
+  const int nb = n / kTile;
   const int64_t bh = blockIdx.x / nqt;
   int qt = static_cast<int>(blockIdx.x % nqt);
   if (CAUSAL) qt = nqt - 1 - qt;  // heaviest query tiles first
-  const int64_t tile_row = bh * n + static_cast<int64_t>(qt) * kTile;
+  const int64_t tile_row = bh * n + static_cast<int64_t>(qt) * TQ;
+  const int qblk = qt * TQ / kTile;  // the 64-row block holding the tile
+  const int qoff = qt * TQ % kTile;  // the tile's first row inside that block
   const T* kb = k + bh * static_cast<int64_t>(n) * D;
   const T* vb = v + bh * static_cast<int64_t>(n) * D;
 
@@ -182,16 +187,16 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
   {
     int lo = 0, hi = nb;
     if (seqtab) {
-      const int4 e = seqtab[qt];
+      const int4 e = seqtab[qblk];
       lo = e.x;
       hi = e.y;
     }
-    const int nbc = CAUSAL ? qt + 1 : hi;  // blocks lo .. nbc - 1 can be visible to this tile
+    const int nbc = CAUSAL ? qblk + 1 : hi;  // blocks lo .. nbc - 1 can be visible to this tile
     int* count = reinterpret_cast<int*>(list + nb);
-    for (int c = lo + tid; c < nbc; c += 256) rm[c] = 0ull;
+    for (int c = lo + tid; c < nbc; c += NTH) rm[c] = 0ull;
     __syncthreads();
     const int32_t* ib = idx + tile_row * topk;
-    for (int e = tid; e < kTile * topk; e += 256) {
+    for (int e = tid; e < TQ * topk; e += NTH) {
       const int b = ib[e];
       if (b >= 0 && b < nbc - lo) atomicOr(reinterpret_cast<unsigned long long*>(&rm[lo + b]), 1ull << (e / topk));
     }
@@ -212,7 +217,7 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
   }
   auto tile_at = [&](int it) -> int {
     const int kt = list[it];
-    return (kt >= 0 && kt < nqt) ? kt : -1;
+    return (kt >= 0 && kt < nb) ? kt : -1;
   };
 
   // ---- this lane's query row in registers (B operand of S^T = K Q^T)
@@ -244,15 +249,15 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
   st.m = -INFINITY;
   st.l = 0.f;
 
-  KvRegs<T, D> regs;
+  KvRegs<T, D, NTH> regs;
   int cur = nlist > 0 ? tile_at(0) : -1;
-  if (cur >= 0) kv_load<T, D>(regs, kb, vb, cur, tid);
+  if (cur >= 0) kv_load<T, D, NTH>(regs, kb, vb, cur, tid);
   for (int it = 0; it < nlist; ++it) {
     __syncthreads();
-    if (cur >= 0) kv_store<T, D>(regs, ks, vs, tid);
+    if (cur >= 0) kv_store<T, D, NTH>(regs, ks, vs, tid);
     __syncthreads();
     const int nxt = it + 1 < nlist ? tile_at(it + 1) : -1;
-    if (nxt >= 0) kv_load<T, D>(regs, kb, vb, nxt, tid);
+    if (nxt >= 0) kv_load<T, D, NTH>(regs, kb, vb, nxt, tid);
     if (cur >= 0) {
       uint32_t vis;
       bool any;
@@ -260,14 +265,14 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
         const uint64_t bits = rm[cur];
         any = ((bits >> (16 * wave)) & 0xFFFFull) != 0ull;
         vis = ((bits >> qlocal) & 1ull) ? 0xFFFFu : 0u;
-        if (CAUSAL && cur == qt) {
-          // diagonal tile: key 16t + 4g + jj visible iff it is <= the query
+        if (CAUSAL && cur == qblk) {
+          // diagonal block: key 16t + 4g + jj visible iff it is <= the query
           uint32_t cm = 0u;
 #pragma unroll
           for (int t = 0; t < 4; ++t)
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj)
-              if (16 * t + 4 * g + jj <= qlocal) cm |= 1u << (4 * t + jj);
+              if (16 * t + 4 * g + jj <= qoff + qlocal) cm |= 1u << (4 * t + jj);
           vis &= cm;
         }
         const int klim = block_keys(seqtab, cur);
@@ -298,6 +303,120 @@ __global__ __launch_bounds__(256) void sparse_flash_kernel(
   for (int dt = 0; dt < D / 16; ++dt) {
     const f32x4 a = st.acc[dt] * inv;
     *reinterpret_cast<float4*>(op + 16 * dt) = make_float4(a[0], a[1], a[2], a[3]);
+  }
+}
+
+// Per-query gathering (nishantmodi.me "sparse-attention-triton-bench", "The
+// Triton kernel": one program per (batch, head, query) that loads each
+// selected block's keys and values and runs the online softmax over them).
+// One wave per query row, four rows per workgroup, no MFMA and no sharing of
+// a key block between queries: every (query, block) pair reads its block's
+// K and V again (through L2).  Lane (r, c) of the wave takes the 16-byte
+// column chunk c (CH chunks per row) of rows r, r + RG, ... of a block (RG =
+// 64 / CH row groups): its partial dot products are summed over the CH
+// lanes of its row group, each lane then holds the scores (and
+// probabilities) of its own rows, multiplies them into its chunk of those
+// V rows, and the output's chunks are summed over the row groups once at
+// the end.
+template <typename T, int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void per_query_kernel(
+    const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
+    float* __restrict__ out, float* __restrict__ lse, const int32_t* __restrict__ idx, int64_t rows,
+    int topk, int n, const int4* __restrict__ seqtab, float scale_log2) {
+  constexpr int E = 16 / sizeof(T);  // elements per chunk
+  constexpr int CH = D / E;          // chunks per row
+  constexpr int RG = 64 / CH;        // row groups
+  constexpr int RPL = 64 / RG;       // rows per lane
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;  // wave-uniform
+  const int c = lane % CH, r = lane / CH;
+  const int64_t bh = row / n;
+  const int qi = static_cast<int>(row % n);
+  const RowBlocks rb = row_blocks(seqtab, row, n, CAUSAL);
+  auto to_f = [](const uint4& u, float (&x)[E]) {
+    if constexpr (sizeof(T) == 2) {
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(w[i] << 16);
+        x[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      }
+    } else {
+      x[0] = __uint_as_float(u.x);
+      x[1] = __uint_as_float(u.y);
+      x[2] = __uint_as_float(u.z);
+      x[3] = __uint_as_float(u.w);
+    }
+  };
+  float qv[E];
+  to_f(ld16(q + row * D + c * E), qv);
+  const T* kb = k + bh * static_cast<int64_t>(n) * D;
+  const T* vb = v + bh * static_cast<int64_t>(n) * D;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  float m = -INFINITY, l = 0.f;  // log2-domain running max; the row group's share of the sum
+  const int32_t* sel = idx + row * topk;
+  for (int t = 0; t < topk; ++t) {
+    const int beta = sel_block(sel[t], rb);
+    if (beta < 0) continue;  // wave-uniform
+    const int klim = block_keys(seqtab, beta);
+    const int kmax = CAUSAL && beta == rb.own ? qi % kTile : kTile - 1;  // last visible key
+    float s[RPL];
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int j = r + RG * i;
+      float kx[E];
+      to_f(ld16(kb + (static_cast<int64_t>(beta) * kTile + j) * D + c * E), kx);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) d = __builtin_fmaf(qv[e], kx[e], d);
+      s[i] = d;
+    }
+#pragma unroll
+    for (int off = 1; off < CH; off <<= 1)
+#pragma unroll
+      for (int i = 0; i < RPL; ++i) s[i] += __shfl_xor(s[i], off);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int j = r + RG * i;
+      s[i] = (j < klim && j <= kmax) ? s[i] * scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[i]);
+    }
+#pragma unroll
+    for (int off = CH; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float m_new = fmaxf(m, mx);  // finite: every live block has a visible key
+    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    m = m_new;
+    l *= alpha;
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int i = 0; i < RPL; ++i) {
+      const int j = r + RG * i;
+      const float p = __builtin_amdgcn_exp2f(s[i] - m);
+      l += p;  // the same in the CH lanes of the row group
+      float vx[E];
+      to_f(ld16(vb + (static_cast<int64_t>(beta) * kTile + j) * D + c * E), vx);
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc[e] = __builtin_fmaf(p, vx[e], acc[e]);
+    }
+  }
+#pragma unroll
+  for (int off = CH; off < 64; off <<= 1) {
+    l += __shfl_xor(l, off);
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], off);
+  }
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  if (r == 0) {
+    float* dst = out + row * D + c * E;
+#pragma unroll
+    for (int e = 0; e < E; e += 4)
+      *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv);
+    if (lse && c == 0) lse[row] = l > 0.f ? (m + __log2f(l)) * (1.0f / kLog2e) : -INFINITY;
   }
 }
 
@@ -458,33 +577,42 @@ __global__ __launch_bounds__(256) void static_combine_kernel(const int4* __restr
                                                       acc[e + 3] * inv);
 }
 
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int W>
 hipError_t launch_union(const void* q, const void* k, const void* v, float* out, float* lse,
                         const int32_t* idx, int topk, const int4* seqtab, int64_t bh, int n, float scale,
                         hipStream_t s) {
-  using L = KvLayout<T, D>;
+  using L = KvLayout<T, D, 64 * W>;
   const int nb = n / kTile;
   const size_t smem = L::BYTES + static_cast<size_t>(nb) * 8 + static_cast<size_t>(nb) * 4 + 16;
-  const auto kern = sparse_flash_kernel<T, D, CAUSAL>;
+  const auto kern = sparse_flash_kernel<T, D, CAUSAL, W>;
   if (smem > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              static_cast<int>(smem));
     if (e != hipSuccess) return e;
   }
-  const dim3 grid(static_cast<unsigned>(bh * (n / kTile)));
-  hipLaunchKernelGGL(kern, grid, dim3(256), smem, s, static_cast<const T*>(q),
+  const dim3 grid(static_cast<unsigned>(bh * (n / (16 * W))));
+  hipLaunchKernelGGL(kern, grid, dim3(64 * W), smem, s, static_cast<const T*>(q),
                      static_cast<const T*>(k), static_cast<const T*>(v), out, lse, idx, topk, n, seqtab,
                      scale * kLog2e);
   return hipGetLastError();
 }
 
+template <typename T, int D, int W>
+hipError_t dispatch_w(const void* q, const void* k, const void* v, float* out, float* lse,
+                      const int32_t* idx, int64_t bh, int n, int topk, float scale,
+                      int causal, hipStream_t s, const int4* seqtab) {
+  return causal ? launch_union<T, D, true, W>(q, k, v, out, lse, idx, topk, seqtab, bh, n, scale, s)
+                : launch_union<T, D, false, W>(q, k, v, out, lse, idx, topk, seqtab, bh, n, scale, s);
+}
+
 template <typename T, int D>
 hipError_t dispatch_dynamic(const void* q, const void* k, const void* v, float* out, float* lse,
                             const int32_t* idx, int64_t bh, int n, int topk, float scale,
-                            int causal, hipStream_t s, const int4* seqtab) {
-  return causal ? launch_union<T, D, true>(q, k, v, out, lse, idx, topk, seqtab, bh, n, scale, s)
-                : launch_union<T, D, false>(q, k, v, out, lse, idx, topk, seqtab, bh, n, scale, s);
+                            int causal, hipStream_t s, const int4* seqtab, int rows) {
+  if (rows == 16) return dispatch_w<T, D, 1>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, s, seqtab);
+  if (rows == 32) return dispatch_w<T, D, 2>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, s, seqtab);
+  return dispatch_w<T, D, 4>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, s, seqtab);
 }
 
 template <typename T, int D>
@@ -502,12 +630,33 @@ hipError_t launch_static_t(const StaticLaunch& a, hipStream_t s) {
 hipError_t launch_sparse_flash_dynamic(const void* q, const void* k, const void* v, float* out,
                                        float* lse, const int32_t* idx, int64_t bh, int n, int d,
                                        int topk, float scale, int causal, bsa_dtype dtype,
-                                       hipStream_t stream, const int4* kl) {
+                                       hipStream_t stream, const int4* kl, int rows) {
   if (dtype == BSA_BF16)
-    return d == 64 ? dispatch_dynamic<bf16_bits, 64>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl)
-                   : dispatch_dynamic<bf16_bits, 128>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl);
-  return d == 64 ? dispatch_dynamic<float, 64>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl)
-                 : dispatch_dynamic<float, 128>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl);
+    return d == 64 ? dispatch_dynamic<bf16_bits, 64>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl, rows)
+                   : dispatch_dynamic<bf16_bits, 128>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl, rows);
+  return d == 64 ? dispatch_dynamic<float, 64>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl, rows)
+                 : dispatch_dynamic<float, 128>(q, k, v, out, lse, idx, bh, n, topk, scale, causal, stream, kl, rows);
+}
+
+hipError_t launch_sparse_flash_per_query(const void* q, const void* k, const void* v, float* out,
+                                         float* lse, const int32_t* idx, int64_t rows, int n, int d,
+                                         int topk, float scale, int causal, bsa_dtype dtype,
+                                         hipStream_t stream, const int4* seqtab) {
+  const dim3 grid(static_cast<unsigned>((rows + 3) / 4));
+  const float sl2 = scale * kLog2e;
+#define BSA_PQ(T, DD, C)                                                                                     \
+  hipLaunchKernelGGL((per_query_kernel<T, DD, C>), grid, dim3(256), 0, stream, static_cast<const T*>(q),     \
+                     static_cast<const T*>(k), static_cast<const T*>(v), out, lse, idx, rows, topk, n, seqtab, \
+                     sl2)
+  if (dtype == BSA_BF16) {
+    if (d == 64) { if (causal) BSA_PQ(bf16_bits, 64, true); else BSA_PQ(bf16_bits, 64, false); }
+    else { if (causal) BSA_PQ(bf16_bits, 128, true); else BSA_PQ(bf16_bits, 128, false); }
+  } else {
+    if (d == 64) { if (causal) BSA_PQ(float, 64, true); else BSA_PQ(float, 64, false); }
+    else { if (causal) BSA_PQ(float, 128, true); else BSA_PQ(float, 128, false); }
+  }
+#undef BSA_PQ
+  return hipGetLastError();
 }
 
 hipError_t launch_sparse_flash_static(const StaticLaunch& a, hipStream_t stream) {

@@ -94,9 +94,16 @@ typedef enum {
    * the pair's log-sum-exp) and merge them per query.  Every selected pair is
    * computed once.  Default. */
   BSA_FINE_BLOCK_GATHER = 0,
-  /* Per 64-query tile, walk the union of the rows' selected blocks with the
-   * online softmax in registers, masking each row to its own selection. */
-  BSA_FINE_QUERY_TILE = 1
+  /* Per query tile (64 rows; 16 or 32 with BSA_OPT_UNION_ROWS), walk the
+   * union of the rows' selected blocks with the online softmax in registers,
+   * masking each row to its own selection. */
+  BSA_FINE_QUERY_TILE = 1,
+  /* One wave per query walks the query's own selected blocks with the online
+   * softmax on the vector units (nishantmodi.me
+   * "sparse-attention-triton-bench", "The Triton kernel": one program per
+   * (batch, head, query)); every (query, block) pair reads its block again.
+   * For comparison; the slowest of the three on large problems. */
+  BSA_FINE_PER_QUERY = 2
 } bsa_fine_strategy;
 
 /* How bsa_forward runs stage 1 (the selection is the same either way). */
@@ -130,7 +137,9 @@ typedef enum {
    * there are about four items per compute unit and none is longer than
    * about twice the mean list; a value >= every list length gives one item
    * per query tile. */
-  BSA_OPT_STATIC_ITEM_TILES = 4
+  BSA_OPT_STATIC_ITEM_TILES = 4,
+  /* Rows per query tile of BSA_FINE_QUERY_TILE: 16, 32 or 64 (default 64). */
+  BSA_OPT_UNION_ROWS = 5
 } bsa_option;
 
 /* ----------------------------------------------------------- lifetime -- */

@@ -197,7 +197,7 @@ def check_selection(gidx, oidx, kth, nxt):
     assert not bad.any(), f"{bad.sum()} rows select other blocks outside the tie band"
 
 
-@pytest.mark.parametrize("fine", ["block_gather", "query_tile"])
+@pytest.mark.parametrize("fine", ["block_gather", "query_tile", "per_query"])
 @pytest.mark.parametrize("name,causal,topk,head_topk", [
     ("tiny_fp32_n1k", False, 4, None), ("tiny_fp32_n1k", True, 4, None),
     ("dyn_bf16_n4k", False, 16, None), ("dyn_bf16_n4k", True, 16, None),
@@ -208,7 +208,8 @@ def test_forward_train_and_backward(bsa, fine, name, causal, topk, head_topk):
     lse against the oracle, then bsa_backward's gradients on that selection."""
     m, lib = bsa
     m.bsa_set_option(lib.handle, m.BSA_OPT_FINE_STRATEGY,
-                     m.BSA_FINE_BLOCK_GATHER if fine == "block_gather" else m.BSA_FINE_QUERY_TILE)
+                     {"block_gather": m.BSA_FINE_BLOCK_GATHER, "query_tile": m.BSA_FINE_QUERY_TILE,
+                      "per_query": m.BSA_FINE_PER_QUERY}[fine])
     w = W.WORKLOADS[name]
     inp = W.generate(w)
     b, h, n, d = inp.q.shape

@@ -32,9 +32,10 @@ def say(*a):
     sys.stdout.flush()
 
 
-STRATEGIES = ["block_gather", "query_tile"]
+# fine-stage strategies; query_tile16 / 32: the union over 16- or 32-row query tiles
+STRATEGIES = ["block_gather", "query_tile", "query_tile16", "query_tile32", "per_query"]
 # (stage-1 strategy, fine strategy) combinations run end to end
-PATHS = [("fused", "block_gather"), ("panel", "block_gather"), ("fused", "query_tile")]
+PATHS = [("fused", "block_gather"), ("panel", "block_gather"), ("fused", "query_tile"), ("fused", "per_query")]
 
 
 @pytest.fixture(scope="module")
@@ -46,8 +47,13 @@ def bsa():
 
 
 def use_strategy(m, lib, strategy, select="fused"):
-    code = {"block_gather": m.BSA_FINE_BLOCK_GATHER, "query_tile": m.BSA_FINE_QUERY_TILE}[strategy]
+    rows = 64
+    if strategy.startswith("query_tile") and strategy != "query_tile":
+        strategy, rows = "query_tile", int(strategy[len("query_tile"):])
+    code = {"block_gather": m.BSA_FINE_BLOCK_GATHER, "query_tile": m.BSA_FINE_QUERY_TILE,
+            "per_query": m.BSA_FINE_PER_QUERY}[strategy]
     m.bsa_set_option(lib.handle, m.BSA_OPT_FINE_STRATEGY, code)
+    m.bsa_set_option(lib.handle, m.BSA_OPT_UNION_ROWS, rows)
     code = {"fused": m.BSA_SELECT_FUSED, "panel": m.BSA_SELECT_PANEL}[select]
     m.bsa_set_option(lib.handle, m.BSA_OPT_SELECT_STRATEGY, code)
 

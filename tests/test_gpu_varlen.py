@@ -15,7 +15,7 @@ import pytest
 
 import oracle
 import workloads as W
-from test_gpu_parity import TOL, check_selection, say
+from test_gpu_parity import TOL, check_selection, say, use_strategy
 from test_gpu_backward import TOLG, TOLL, close, single_key_rows
 
 torch = pytest.importorskip("torch")
@@ -37,15 +37,11 @@ def bsa():
 def _defaults(bsa):
     yield
     m, lib = bsa
-    m.bsa_set_option(lib.handle, m.BSA_OPT_FINE_STRATEGY, m.BSA_FINE_BLOCK_GATHER)
-    m.bsa_set_option(lib.handle, m.BSA_OPT_SELECT_STRATEGY, m.BSA_SELECT_FUSED)
+    use_strategy(m, lib, "block_gather", "fused")
 
 
 def strategy(m, lib, select, fine):
-    m.bsa_set_option(lib.handle, m.BSA_OPT_SELECT_STRATEGY,
-                     {"fused": m.BSA_SELECT_FUSED, "panel": m.BSA_SELECT_PANEL}[select])
-    m.bsa_set_option(lib.handle, m.BSA_OPT_FINE_STRATEGY,
-                     {"block_gather": m.BSA_FINE_BLOCK_GATHER, "query_tile": m.BSA_FINE_QUERY_TILE}[fine])
+    use_strategy(m, lib, fine, select)
 
 
 def dev_qkv(inp, dtype):
@@ -99,7 +95,8 @@ def check_sequences(w, inp, cu, out, idx, topk, causal, head_topk=None):
     return worst
 
 
-PATHS = [("fused", "block_gather"), ("panel", "block_gather"), ("fused", "query_tile")]
+PATHS = [("fused", "block_gather"), ("panel", "block_gather"), ("fused", "query_tile"), ("fused", "query_tile16"),
+         ("fused", "per_query")]
 
 
 @pytest.mark.parametrize("select,fine", PATHS)
