@@ -484,10 +484,12 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
     lt = lsum + __shfl_xor(lsum, 16);
     lt += __shfl_xor(lt, 32);
   }
-  const float inv = 1.0f / lt;
-  // The pair's log2-domain log-sum-exp, m + log2 l (l >= 1: the maximum's own
-  // weight is 1), rides in the row itself: bit e of its fp32 pattern replaces
-  // the least significant bit of element e, e < 32.
+  // l >= 1 (the maximum's own weight is 1): the hardware reciprocal (1 ulp)
+  // is far inside the fp16 rounding of the row it scales.
+  const float inv = __builtin_amdgcn_rcpf(lt);
+  // The pair's log2-domain log-sum-exp, m + log2 l, rides in the row itself:
+  // bit e of its fp32 pattern replaces the least significant bit of element
+  // e, e < 32.
   const uint32_t lse_bits = __float_as_uint(m + __builtin_amdgcn_logf(lt));
   if constexpr (L::kBf16) {
     // Through the wave's LDS staging rows (16 pairs x D fp16) so that every
@@ -509,22 +511,25 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     constexpr int CPR = D * 2 / 16;  // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;    // rows per store instruction
+    const int32_t pl = live ? pair : -1;  // the row's pair, or -1 for a dead row
 #pragma unroll
     for (int i = 0; i < 16 / RPI; ++i) {
       const int r = i * RPI + lane / CPR, ch = lane % CPR;
-      const int32_t pr = __shfl(pair, r);
-      const bool lv = __shfl(static_cast<int>(live), r) != 0;
+      const int32_t pr = __shfl(pl, r);
       const uint32_t lb = __shfl(lse_bits, r);
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       u32x4 h = *reinterpret_cast<const u32x4*>(stage + r * kStagePitch<D> + ch * 8);
       if (ch < 4) {
-        const uint32_t bits = lb >> (8 * ch);  // elements 8 ch .. 8 ch + 7
-        h[0] = (h[0] & 0xFFFEFFFEu) | (bits & 1u) | ((bits << 15) & 0x10000u);
-        h[1] = (h[1] & 0xFFFEFFFEu) | ((bits >> 2) & 1u) | ((bits << 13) & 0x10000u);
-        h[2] = (h[2] & 0xFFFEFFFEu) | ((bits >> 4) & 1u) | ((bits << 11) & 0x10000u);
-        h[3] = (h[3] & 0xFFFEFFFEu) | ((bits >> 6) & 1u) | ((bits << 9) & 0x10000u);
+        // elements 8 ch + 2 j (low half of word j) and + 1 (high half) take
+        // bits 8 ch + 2 j and + 1: with t those two bits, t | t << 15 holds
+        // them at bits 0 and 16
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t t = (lb >> (8 * ch + 2 * j)) & 3u;
+          h[j] = ((t | (t << 15)) & 0x00010001u) | (h[j] & 0xFFFEFFFEu);
+        }
       }
-      if (lv) __builtin_nontemporal_store(h, reinterpret_cast<u32x4*>(po + static_cast<int64_t>(pr) * D) + ch);
+      if (pr >= 0) __builtin_nontemporal_store(h, reinterpret_cast<u32x4*>(po + static_cast<int64_t>(pr) * D) + ch);
     }
   } else {
     if (!live) return;
@@ -616,10 +621,6 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
   }
 }
 
-// Least significant bit of a partial element's bit pattern.
-__device__ __forceinline__ uint32_t low_bit(f16 x) { return __builtin_bit_cast(uint16_t, x) & 1u; }
-__device__ __forceinline__ uint32_t low_bit(float x) { return __float_as_uint(x) & 1u; }
-
 // Reduce-scatter by OR over a group of 16 lanes: lane c holds v[t] for
 // t = 0 .. 15 and gets back the OR of every lane's v[c].  Recursive halving:
 // at distance M a lane keeps the half of its 2M live entries whose bit M
@@ -645,9 +646,11 @@ __device__ __forceinline__ uint32_t or_scatter16(uint32_t (&v)[16], int c) {
 
 // One group of 16 lanes per query row, 16 slots at a time: every lane issues
 // the loads of its D/16 dims of all 16 partial rows before using any (slot
-// index clamped into the row, so every load is in bounds; padding slots carry
-// weight 0 and are zeroed by a select, since their rows were never written).
-// Each row carries its pair's log2-domain log-sum-exp in the low bits of its
+// index clamped into the row, so every load is in bounds).  Lane c decides
+// whether slot s0 + c counts, a ballot shares the 16 answers with the row's
+// lanes, and the words of a slot that does not count (its row was never
+// written) are zeroed, so the weighted sum needs no select per element.  Each
+// row carries its pair's log2-domain log-sum-exp in the low bits of its
 // first 32 elements; lane c collects the bits it holds and a reduce-scatter
 // hands lane c the value of slot c.  Rows are merged in slot order against a
 // running maximum (rescaled when a later batch of 16 raises it).  Any topk.
@@ -657,43 +660,66 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
                                                       float* __restrict__ out, float* __restrict__ lse,
                                                       int64_t row0, int64_t rows, int n, int topk,
                                                       int causal, const int4* __restrict__ seqtab) {
-  constexpr int E = D / 16;  // dims per lane
-  constexpr int V = E / 4;   // 4-element loads per lane and slot
-  typedef typename std::conditional<sizeof(T) == 2, f16x4, f32x4>::type Vec;
+  constexpr int E = D / 16;                         // dims per lane
+  constexpr int LW = E * sizeof(PartialT<T>) / 4;   // 32-bit words per lane and slot
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  if (r >= rows) return;
   const int c = threadIdx.x & 15;
   const int gbase = (threadIdx.x & 63) & ~15;
-  const int64_t row = row0 + r;
+  const bool row_ok = r < rows;  // lanes of a missing row still take part in the ballot
+  const int64_t rc = row_ok ? r : rows - 1;
+  const int64_t row = row0 + rc;
   const RowBlocks rb = row_blocks(seqtab, row, n, causal);
   const int32_t* sel = idx + row * topk;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   float wsum = 0.f, mrun = -INFINITY;
-  const PartialT<T>* src = po + r * topk * D + c * E;
+  const PartialT<T>* src = po + rc * topk * D + c * E;
   for (int s0 = 0; s0 < topk; s0 += 16) {
-    Vec x[16][V];
+    uint32_t w[16][LW];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const int st = s0 + t < topk ? s0 + t : topk - 1;
+      const PartialT<T>* p = src + static_cast<int64_t>(st) * D;
+      if constexpr (LW == 2) {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        w[t][0] = v.x;
+        w[t][1] = v.y;
+      } else {
 #pragma unroll
-      for (int u = 0; u < V; ++u)
-        x[t][u] = __builtin_nontemporal_load(reinterpret_cast<const Vec*>(src + static_cast<int64_t>(st) * D) + u);
+        for (int h = 0; h < LW / 4; ++h) {
+          const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + h);
+          w[t][4 * h] = v.x;
+          w[t][4 * h + 1] = v.y;
+          w[t][4 * h + 2] = v.z;
+          w[t][4 * h + 3] = v.w;
+        }
+      }
     }
-    // bits c E .. c E + E - 1 of each slot's log-sum-exp (lanes c < 32 / E)
+    const bool valid = row_ok && s0 + c < topk && sel_block(sel[s0 + c], rb) >= 0;
+    const uint32_t vmask = static_cast<uint32_t>(ballot(valid) >> gbase) & 0xFFFFu;
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+#pragma unroll
+      for (int k2 = 0; k2 < LW; ++k2) w[t][k2] = ((vmask >> t) & 1u) ? w[t][k2] : 0u;
+    // bits c E .. c E + E - 1 of each slot's log-sum-exp (lanes c < 32 / E):
+    // element e's least significant bit
     uint32_t part[16];
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       uint32_t b = 0u;
+      if constexpr (sizeof(PartialT<T>) == 2) {
 #pragma unroll
-      for (int u = 0; u < V; ++u)
+        for (int k2 = 0; k2 < LW; ++k2) b |= ((w[t][k2] & 1u) << (2 * k2)) | (((w[t][k2] >> 16) & 1u) << (2 * k2 + 1));
+      } else {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) b |= low_bit(x[t][u][q4]) << (4 * u + q4);
+        for (int k2 = 0; k2 < LW; ++k2) b |= (w[t][k2] & 1u) << k2;
+      }
       part[t] = c * E < 32 ? b << (c * E) : 0u;
     }
     const uint32_t bits = or_scatter16(part, c);  // slot s0 + c
-    const bool valid = s0 + c < topk && sel_block(sel[s0 + c], rb) >= 0;
     const float ls = valid ? __uint_as_float(bits) : -INFINITY;
     float mb = ls;
 #pragma unroll
@@ -711,15 +737,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const float ws = __shfl(wl, gbase + t);
+      if constexpr (sizeof(PartialT<T>) == 2) {
+        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-      for (int u = 0; u < V; ++u)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const float xv = static_cast<float>(x[t][u][q4]);
-          acc[4 * u + q4] += ws != 0.f ? ws * xv : 0.f;
+        for (int k2 = 0; k2 < LW; ++k2) {
+          const h2 hv = __builtin_bit_cast(h2, w[t][k2]);
+          acc[2 * k2] = __builtin_fmaf(static_cast<float>(hv[0]), ws, acc[2 * k2]);
+          acc[2 * k2 + 1] = __builtin_fmaf(static_cast<float>(hv[1]), ws, acc[2 * k2 + 1]);
         }
+      } else {
+#pragma unroll
+        for (int k2 = 0; k2 < LW; ++k2) acc[k2] = __builtin_fmaf(__uint_as_float(w[t][k2]), ws, acc[k2]);
+      }
     }
   }
+  if (!row_ok) return;
 #pragma unroll
   for (int off = 8; off >= 1; off >>= 1) wsum += __shfl_xor(wsum, off, 16);
   const float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
