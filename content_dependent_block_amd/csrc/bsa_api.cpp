@@ -583,7 +583,7 @@ FineGeom fine_geom(const Shape& s, bsa_dtype dt, int topk, int64_t chunk) {
   const int64_t nb = s.n / 64;
   const int64_t heads_spanned = s.bh() < (chunk + s.n - 1) / s.n + 1 ? s.bh() : (chunk + s.n - 1) / s.n + 1;
   g.buckets = heads_spanned * g.qsegs * nb;
-  g.slots = bsa::gather_grid(chunk, topk, g.buckets, bsa::kGatherItemPairs);
+  g.slots = bsa::gather_grid(chunk, topk, g.buckets, bsa::gather_item_pairs(s.d, dt));
   const size_t pieces[] = {size_t(g.buckets) * 4, size_t(g.buckets + 1) * 4, size_t(g.buckets + 1) * 4,
                            size_t(g.slots) * 16, size_t(g.pairs) * 4, size_t(g.pairs) * 4,
                            size_t(g.pairs) * s.d * (dt == BSA_BF16 ? 2 : 4), size_t(g.pairs) * 8,
@@ -624,6 +624,7 @@ bsa_status run_fine_arena(bsa_handle h, const void* q, const void* k, const void
   a.scale = scale;
   a.dtype = dt;
   a.qsegs = g.qsegs;
+  a.item_pairs = bsa::gather_item_pairs(s.d, dt);
   void* p[9];
   const size_t sizes[] = {size_t(g.buckets) * 4, size_t(g.buckets + 1) * 4, size_t(g.buckets + 1) * 4,
                           size_t(g.slots) * 16, size_t(g.pairs) * 4, size_t(g.pairs) * 4,
@@ -682,7 +683,8 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   TRY(grow_counts(h, size_t(buckets), &clear_words));
   TRY(grow_buf(h, h->g_offsets, size_t(buckets + 1) * 4, "bucket offsets"));
   TRY(grow_buf(h, h->g_items, size_t(buckets + 1) * 4, "bucket work items"));
-  TRY(grow_buf(h, h->g_item_rec, size_t(bsa::gather_grid(chunk, topk, buckets, bsa::kGatherItemPairs)) * 16,
+  const int item_pairs = bsa::gather_item_pairs(s.d, dt);
+  TRY(grow_buf(h, h->g_item_rec, size_t(bsa::gather_grid(chunk, topk, buckets, item_pairs)) * 16,
                "work-item records"));
   TRY(grow_buf(h, h->g_rank, size_t(pairs) * 4, "pair ranks"));
   TRY(grow_buf(h, h->g_list, size_t(pairs) * 4, "pair lists"));
@@ -703,6 +705,7 @@ bsa_status run_fine(bsa_handle h, const void* q, const void* k, const void* v, f
   a.scale = scale;
   a.dtype = dt;
   a.qsegs = qsegs;
+  a.item_pairs = item_pairs;
   a.seqtab = tab;
   a.ws.count = static_cast<int32_t*>(h->g_count.p);
   a.ws.count_words = clear_words;

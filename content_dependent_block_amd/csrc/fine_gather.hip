@@ -47,7 +47,6 @@
 namespace bsa {
 namespace {
 
-constexpr int kItemPairs = kGatherItemPairs;  // pairs per work item (16 groups of 16)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kXcds = 8;
 
@@ -324,8 +323,11 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(
   }
 }
 
-// bf16 inputs keep partial outputs as fp16 (|o| <= max |v|, relative error
-// 2^-11), fp32 inputs as fp32.
+// bf16 inputs keep partial outputs as fp16, fp32 inputs as fp32.  An fp16
+// row (|o| <= max |v|) is rounded once (half an ulp) and its first 32
+// elements lose their last mantissa bit to the log-sum-exp (up to one ulp
+// more): at most 1.5 ulp, 1.5 * 2^-10 relative, so an absolute error of up
+// to 1.5 * 2^-10 * max |v| per element.
 template <typename T>
 using PartialT = typename std::conditional<sizeof(T) == 2, f16, float>::type;
 
@@ -549,13 +551,13 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
   }
 }
 
-// One work item = up to kItemPairs pairs of one bucket (head, key block),
+// One work item = up to IP pairs of one bucket (head, key block),
 // described by the record the fill kernel left at this workgroup's slot.
 // Every load the item needs is issued before any is waited on: the wave's
 // list entries, the block's K/V into registers, then (as the list entries
 // arrive) the pairs' query rows; then K/V go to LDS and the MFMA work runs.
 // row = pair / topk uses a precomputed multiply-shift (exact for pair < 2^31).
-template <typename T, int D, bool CAUSAL>
+template <typename T, int D, bool CAUSAL, int IP>
 __global__ __launch_bounds__(256) void gather_partial_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const int32_t* __restrict__ list, const int32_t* __restrict__ items,
@@ -563,7 +565,7 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
     uint64_t div_magic, int div_shift, int64_t bh0, int qsegs, const int4* __restrict__ seqtab,
     float scale_log2, PartialT<T>* __restrict__ po) {
   using L = KvLayout<T, D>;
-  constexpr int GPW = kItemPairs / 16 / 4;  // 16-pair groups per wave
+  constexpr int GPW = IP / 16 / 4;  // 16-pair groups per wave
   constexpr int STAGE_BYTES = L::kBf16 ? 16 * kStagePitch<D> * 2 : 0;  // per wave
   __shared__ __align__(16) unsigned char smem[L::BYTES + 4 * STAGE_BYTES];
   T* ks = reinterpret_cast<T*>(smem);
@@ -582,7 +584,7 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
   if (b < 0 || b >= nbuckets) return;
   const int64_t first = rec.y;
   int cnt = rec.z;
-  if (cnt > kItemPairs) cnt = kItemPairs;
+  if (cnt > IP) cnt = IP;
   if (first + cnt > npairs) cnt = first < npairs ? static_cast<int>(npairs - first) : 0;
   const int nb = n / kTile;
   const int beta = b % nb;
@@ -779,9 +781,10 @@ struct ChunkGeom {
 
 template <typename T, int D>
 hipError_t partial_chunk(const GatherArgs& a, int64_t row0, int64_t rows, hipStream_t s) {
-  if (a.item_pairs != kItemPairs) return hipErrorInvalidValue;  // items made for another kernel
+  constexpr int IP = gather_item_pairs(D, std::is_same<T, float>::value ? BSA_FP32 : BSA_BF16);
+  if (a.item_pairs != IP) return hipErrorInvalidValue;  // items made for another kernel
   const ChunkGeom c(a, row0, rows);
-  const int64_t grid = gather_grid(rows, a.topk, c.nbuckets, kItemPairs);
+  const int64_t grid = gather_grid(rows, a.topk, c.nbuckets, IP);
   const float sl2 = a.scale * kLog2e;
   auto* po = reinterpret_cast<PartialT<T>*>(a.ws.partial_o);
   // pair / topk as (pair * magic) >> shift: shift = 32 + ceil(log2 topk),
@@ -791,12 +794,12 @@ hipError_t partial_chunk(const GatherArgs& a, int64_t row0, int64_t rows, hipStr
   const int shift = 32 + lg;
   const uint64_t magic = ((uint64_t(1) << shift) + uint64_t(a.topk) - 1) / uint64_t(a.topk);
   if (a.causal)
-    hipLaunchKernelGGL((gather_partial_kernel<T, D, true>), dim3(static_cast<unsigned>(grid)), dim3(256),
+    hipLaunchKernelGGL((gather_partial_kernel<T, D, true, IP>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets,
                        row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, a.seqtab, sl2, po);
   else
-    hipLaunchKernelGGL((gather_partial_kernel<T, D, false>), dim3(static_cast<unsigned>(grid)), dim3(256),
+    hipLaunchKernelGGL((gather_partial_kernel<T, D, false, IP>), dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const T*>(a.q), static_cast<const T*>(a.k),
                        static_cast<const T*>(a.v), a.ws.list, a.ws.items, a.ws.item_rec, c.nbuckets,
                        row0, c.npairs, a.n, magic, shift, c.bh0, a.qsegs, a.seqtab, sl2, po);

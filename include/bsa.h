@@ -195,11 +195,15 @@ bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes);
  *                 are visible.
  * Coarse scores are q . mean(block keys), unscaled; equal scores go to the
  * lower block index, and -0 equals +0.
- * Range: with bf16 inputs the block-gather fine stage (the default) keeps
- * each (query, block) partial output in fp16, so every |v| must stay below
- * 65504; a larger value makes the affected output rows non-finite (never a
- * finite wrong value).  The same holds for every entry point below that runs
- * the dynamic fine stage on bf16 inputs. */
+ * Range and precision: with bf16 inputs the block-gather fine stage (the
+ * default) keeps each (query, block) partial output in fp16, so every |v|
+ * must stay below 65504; a larger value makes the affected output rows
+ * non-finite (never a finite wrong value).  The fp16 rows (at most 1.5 ulp
+ * each, the last mantissa bit of 32 elements carrying the pair's
+ * log-sum-exp) and the bf16 probabilities give outputs an absolute error of
+ * order 2^-9 * max |v| (about 1e-4 * max |v| measured); for fp32 inputs all
+ * of it is fp32.  The same holds for every entry point below that runs the
+ * dynamic fine stage on bf16 inputs. */
 bsa_status bsa_forward(bsa_handle h, const void* q, const void* k, const void* v,
                        float* out, int32_t* block_idx_out, int batch, int heads,
                        int n, int d, bsa_dtype dtype, int block, int topk,

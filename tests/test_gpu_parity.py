@@ -742,6 +742,26 @@ def test_forward_ragged_n(bsa, name, n, topk, causal, select, strategy):
     end_to_end(m, lib, w, inp, rows, topk=topk, causal=causal)
 
 
+@pytest.mark.parametrize("select,strategy", PATHS)
+def test_large_values_error_bound(bsa, select, strategy):
+    """Values far from unit size (v scaled by 37.3, |v| up to about 200, then
+    rounded to bf16): the output error stays within the stated 2^-9 * max|v|
+    (fp16 partial rows, bf16 probabilities), at full size and on every row."""
+    m, lib = bsa
+    use_strategy(m, lib, strategy, select)
+    w = W.WORKLOADS["dyn_bf16_n4k"]
+    inp = W.generate(w)
+    inp.v, inp.v_bits = W.bf16_round(inp.v * np.float32(37.3))
+    vmax = float(np.abs(inp.v).max())
+    say(f"[gpu] large values dyn_bf16_n4k max|v|={vmax:.1f} {select}/{strategy}")
+    out, idx = run_forward(m, lib, w, inp)
+    gidx = idx.reshape(-1, w.topk)
+    ref = oracle.attend(inp.q, inp.k, inp.v, gidx, w.block, w.causal, w.scale)
+    err = float(np.abs(out.reshape(-1, w.d) - ref).max())
+    say(f"    max|err| = {err:.3g} = {err / vmax:.3g} max|v|")
+    assert 10 < vmax and err <= 2.0 ** -9 * vmax
+
+
 @pytest.mark.parametrize("n,causal", [(1000, False), (4100, True)])
 def test_fine_forward_ragged_n(bsa, n, causal):
     """Stage 2 alone on the oracle's selection at a ragged n."""
