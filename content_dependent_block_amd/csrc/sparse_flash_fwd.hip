@@ -63,12 +63,19 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const T* ks, const T*
                                           int lane) {
   using L = KvLayout<T, D>;
   const int g = lane >> 4, c16 = lane & 15;
+  // Keys 16 t .. 16 t + 15 that no row of the wave sees (a sparse static
+  // tile: often one visible key column) cost no MFMA work: their scores are
+  // masked below whatever they hold, and their probabilities are 0.
+  bool sub[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) sub[t] = ballot(((vis >> (4 * t)) & 0xFu) != 0u) != 0ull;
   f32x4 s[4];
   if constexpr (L::kBf16) {
     const bf16x8* qb = static_cast<const bf16x8*>(qreg);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (!sub[t]) continue;
 #pragma unroll
       for (int kk = 0; kk < D / 32; ++kk) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(ks + (16 * t + c16) * L::KPITCH + 8 * g + 32 * kk);
@@ -81,6 +88,7 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const T* ks, const T*
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       s[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (!sub[t]) continue;
       const float* kr = ks + (16 * t + c16) * L::KPITCH + KS * g;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) s[t] = mfma_16x16x4_f32(kr[kk], qf[kk], s[t]);
@@ -116,6 +124,7 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const T* ks, const T*
       }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
+      if (!sub[2 * kk] && !sub[2 * kk + 1]) continue;  // keys 32 kk .. 32 kk + 31: all p = 0
       bf16x8 bp;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -141,14 +150,18 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const T* ks, const T*
         lsum += p[t][jj];
       }
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 4; ++t) {
+      if (!sub[t]) continue;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
+        // one MFMA step covers keys 16 t + 4 g' + jj of the four lane groups
+        if (ballot(((vis >> (4 * t + jj)) & 1u) != 0u) == 0ull) continue;
         const T* vr = vs + (16 * t + 4 * g + jj) * L::VPITCH + c16;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
           st.acc[dt] = mfma_16x16x4_f32(vr[16 * dt], p[t][jj], st.acc[dt]);
       }
+    }
   }
   st.l = st.l * alpha + lsum;
 }

@@ -134,7 +134,7 @@ typedef enum {
   /* bsa_forward_static: the most key tiles one work item (one workgroup)
    * takes from a query tile's list; a longer list is cut into several items
    * whose partial results are merged.  0 (default): chosen per call so that
-   * there are about four items per compute unit and none is longer than
+   * there are about two items per compute unit and none is longer than
    * about twice the mean list; a value >= every list length gives one item
    * per query tile. */
   BSA_OPT_STATIC_ITEM_TILES = 4,
