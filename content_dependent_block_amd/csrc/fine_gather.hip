@@ -13,7 +13,9 @@
 //   M = max L_s,  w_s = 2^(L_s - M),  o_i = sum w_s o_s / sum w_s.
 // No score leaves the chip; only the per-pair rows o do, each carrying its L
 // in the least significant bits of its first 32 elements (one 128-byte line
-// per pair for bf16 inputs, and no separate record to scatter).
+// per pair for bf16 inputs, and no separate record to scatter): for fp16 rows
+// the two halves of 32-bit word p (p < 16) carry bits p and p + 16 of L, for
+// fp32 rows element e carries bit e.
 //
 // Why: with content-dependent selections, queries that sit next to each other
 // share few blocks, so a query tile's union of blocks is mostly work for one
@@ -489,9 +491,7 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
   // l >= 1 (the maximum's own weight is 1): the hardware reciprocal (1 ulp)
   // is far inside the fp16 rounding of the row it scales.
   const float inv = __builtin_amdgcn_rcpf(lt);
-  // The pair's log2-domain log-sum-exp, m + log2 l, rides in the row itself:
-  // bit e of its fp32 pattern replaces the least significant bit of element
-  // e, e < 32.
+  // The pair's log2-domain log-sum-exp, m + log2 l, rides in the row itself.
   const uint32_t lse_bits = __float_as_uint(m + __builtin_amdgcn_logf(lt));
   if constexpr (L::kBf16) {
     // Through the wave's LDS staging rows (16 pairs x D fp16) so that every
@@ -500,13 +500,25 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
     // are read back only by the combine, and keeping them out of L2 leaves
     // it to the gathered query rows.
     typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
     for (int u = 0; u < D / 32; ++u) {
       const f32x4 a0 = acc[2 * u] * inv, a1 = acc[2 * u + 1] * inv;
       const f16x8 h = {static_cast<f16>(a0[0]), static_cast<f16>(a0[1]), static_cast<f16>(a0[2]),
                        static_cast<f16>(a0[3]), static_cast<f16>(a1[0]), static_cast<f16>(a1[1]),
                        static_cast<f16>(a1[2]), static_cast<f16>(a1[3])};
-      *reinterpret_cast<f16x8*>(stage + c16 * kStagePitch<D> + out_dim<D>(2 * u, 4 * g)) = h;
+      u32x4 w = __builtin_bit_cast(u32x4, h);
+      if (u == 0) {
+        // The lane holds elements 8 g .. 8 g + 7, i.e. 32-bit words 4 g + j of
+        // the row; word p takes bits p and p + 16 of the log-sum-exp in the
+        // least significant bits of its two halves.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t t = lse_bits >> (4 * g + j);
+          w[j] = (t & 0x00010001u) | (w[j] & 0xFFFEFFFEu);
+        }
+      }
+      *reinterpret_cast<u32x4*>(stage + c16 * kStagePitch<D> + out_dim<D>(2 * u, 4 * g)) = w;
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -518,19 +530,7 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
     for (int i = 0; i < 16 / RPI; ++i) {
       const int r = i * RPI + lane / CPR, ch = lane % CPR;
       const int32_t pr = __shfl(pl, r);
-      const uint32_t lb = __shfl(lse_bits, r);
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      u32x4 h = *reinterpret_cast<const u32x4*>(stage + r * kStagePitch<D> + ch * 8);
-      if (ch < 4) {
-        // elements 8 ch + 2 j (low half of word j) and + 1 (high half) take
-        // bits 8 ch + 2 j and + 1: with t those two bits, t | t << 15 holds
-        // them at bits 0 and 16
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t t = (lb >> (8 * ch + 2 * j)) & 3u;
-          h[j] = ((t | (t << 15)) & 0x00010001u) | (h[j] & 0xFFFEFFFEu);
-        }
-      }
+      const u32x4 h = *reinterpret_cast<const u32x4*>(stage + r * kStagePitch<D> + ch * 8);
       if (pr >= 0) __builtin_nontemporal_store(h, reinterpret_cast<u32x4*>(po + static_cast<int64_t>(pr) * D) + ch);
     }
   } else {
@@ -706,20 +706,29 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
     for (int t = 0; t < 16; ++t)
 #pragma unroll
       for (int k2 = 0; k2 < LW; ++k2) w[t][k2] = ((vmask >> t) & 1u) ? w[t][k2] : 0u;
-    // bits c E .. c E + E - 1 of each slot's log-sum-exp (lanes c < 32 / E):
-    // element e's least significant bit
+    // The bits of each slot's log-sum-exp that this lane holds (lanes
+    // c < 32 / E).  fp16 rows: its word k is row word p = c E / 2 + k, whose
+    // halves carry bits p and p + 16; fp32 rows: element c E + k carries bit
+    // c E + k.
     uint32_t part[16];
+    if constexpr (sizeof(PartialT<T>) == 2) {
+      const uint32_t msk = c * E < 32 ? 0x00010001u : 0u;
+      const int sh = c * E / 2;
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      uint32_t b = 0u;
-      if constexpr (sizeof(PartialT<T>) == 2) {
+      for (int t = 0; t < 16; ++t) {
+        uint32_t b = 0u;
 #pragma unroll
-        for (int k2 = 0; k2 < LW; ++k2) b |= ((w[t][k2] & 1u) << (2 * k2)) | (((w[t][k2] >> 16) & 1u) << (2 * k2 + 1));
-      } else {
+        for (int k2 = 0; k2 < LW; ++k2) b |= (w[t][k2] & msk) << k2;
+        part[t] = b << sh;
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        uint32_t b = 0u;
 #pragma unroll
         for (int k2 = 0; k2 < LW; ++k2) b |= (w[t][k2] & 1u) << k2;
+        part[t] = c * E < 32 ? b << (c * E) : 0u;
       }
-      part[t] = c * E < 32 ? b << (c * E) : 0u;
     }
     const uint32_t bits = or_scatter16(part, c);  // slot s0 + c
     const float ls = valid ? __uint_as_float(bits) : -INFINITY;
