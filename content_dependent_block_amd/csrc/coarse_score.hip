@@ -575,7 +575,7 @@ __device__ __forceinline__ void bitonic_clean(float (&v)[N], int (&b)[N]) {
 // N-1-i are done together, before either is overwritten in both lanes, so no
 // copy of the lists is needed.
 template <int M, int N>
-__device__ __forceinline__ void merge_top(float (&a)[N], int lane) {
+__device__ __forceinline__ void merge_top_unsorted(float (&a)[N], int lane) {
 #pragma unroll
   for (int i = 0; i < N / 2; ++i) {
     const float pi = __uint_as_float(lane_xor<M>(__float_as_uint(a[N - 1 - i]), lane));
@@ -583,6 +583,10 @@ __device__ __forceinline__ void merge_top(float (&a)[N], int lane) {
     a[i] = fmaxf(a[i], pi);
     a[N - 1 - i] = fmaxf(a[N - 1 - i], pj);
   }
+}
+template <int M, int N>
+__device__ __forceinline__ void merge_top(float (&a)[N], int lane) {
+  merge_top_unsorted<M, N>(a, lane);
   bitonic_clean<N>(a);
 }
 template <int M, int N>
@@ -617,11 +621,20 @@ __device__ __forceinline__ float kth_desc(const float (&a)[N], int t) {
 
 // The keff-th largest of the values held by the 4 lanes g = 0..3 of one
 // query (lanes c16 + 16 g), each sorted descending: after two pairwise
-// merges every lane holds the N largest of the 4 N, sorted.  keff <= N.
+// merges every lane holds the N largest of the 4 N.  keff <= N, the same in
+// every lane of the wave.  For keff = N the answer is the smallest of the N
+// (the last merge is left unsorted); otherwise the list is sorted first.
 template <int N>
 __device__ __forceinline__ float kth_of_lanes(float (&a)[N], int keff, int lane) {
   merge_top<16, N>(a, lane);
-  merge_top<32, N>(a, lane);
+  merge_top_unsorted<32, N>(a, lane);
+  if (keff == N) {
+    float r = a[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) r = fminf(r, a[i]);
+    return r;
+  }
+  bitonic_clean<N>(a);
   return kth_desc<N>(a, keff);
 }
 
@@ -653,21 +666,38 @@ __device__ __forceinline__ int sum4(int x, int lane) {
   return x + static_cast<int>(lane_xor<32>(static_cast<uint32_t>(x), lane));
 }
 
-// Bitonic sort of N ints, ascending.
-template <int N>
-__device__ __forceinline__ void sort_asc(int (&a)[N]) {
+// Ascending bitonic sort of the 4 E values held by the query's 4 lanes
+// (lane g holds entries g E .. g E + E - 1): compare-exchanges at distances
+// below E run inside the lane, the others between lanes g and g ^ (d / E)
+// over the permlane swaps.  Afterwards lane g holds entries g E .. of the
+// sorted order.
+template <int E>
+__device__ __forceinline__ void sort_asc_lanes(int (&b)[E], int g, int lane) {
+  constexpr int N = 4 * E;
 #pragma unroll
   for (int size = 2; size <= N; size <<= 1) {
 #pragma unroll
     for (int stride = size / 2; stride > 0; stride >>= 1) {
+      if (stride >= E) {
+        const int m = stride / E;  // partner g ^ m: lane ^ 16 m
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int j = i ^ stride;
-        if (j > i) {
-          const int lo = min(a[i], a[j]), hi = max(a[i], a[j]);
-          const bool up = (i & size) == 0;
-          a[i] = up ? lo : hi;
-          a[j] = up ? hi : lo;
+        for (int i = 0; i < E; ++i) {
+          const int o = static_cast<int>(m == 1 ? lane_xor<16>(static_cast<uint32_t>(b[i]), lane)
+                                                : lane_xor<32>(static_cast<uint32_t>(b[i]), lane));
+          const bool up = ((g * E + i) & size) == 0;
+          const bool lower = (g & m) == 0;
+          b[i] = up == lower ? min(b[i], o) : max(b[i], o);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < E; ++i) {
+          const int j = i ^ stride;
+          if (j > i) {
+            const int lo = min(b[i], b[j]), hi = max(b[i], b[j]);
+            const bool up = ((g * E + i) & size) == 0;
+            b[i] = up ? lo : hi;
+            b[j] = up ? hi : lo;
+          }
         }
       }
     }
@@ -927,22 +957,18 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
 #pragma unroll
       for (int i = 0; i < CAP; ++i) c[i] = x[i];
       sort_desc<CAP>(c);
-      merge_top<16, CAP>(c, ti.lane);
-      merge_top<32, CAP>(c, ti.lane);
-      const float T = kth_desc<CAP>(c, kq);
+      const float T = kth_of_lanes<CAP>(c, kq, ti.lane);
       // Selected: scores above T, and the lowest-block `need` of those equal
       // to T; when exactly `need` candidates equal T (the usual case) all are.
-      int gt = 0, eq = 0;
+      uint32_t gtb = 0u, eqb = 0u;
 #pragma unroll
       for (int i = 0; i < CAP; ++i) {
-        gt += x[i] > T ? 1 : 0;
-        eq += x[i] == T ? 1 : 0;
+        gtb |= x[i] > T ? (1u << i) : 0u;
+        eqb |= x[i] == T ? (1u << i) : 0u;
       }
-      const int need = kq - sum4(gt, ti.lane);
-      const bool all_ties = sum4(eq, ti.lane) == need;
-      uint32_t selbits = 0u;
-#pragma unroll
-      for (int i = 0; i < CAP; ++i) selbits |= (x[i] > T || (x[i] == T && all_ties)) ? (1u << i) : 0u;
+      const int need = kq - sum4(__popc(gtb), ti.lane);
+      const bool all_ties = sum4(__popc(eqb), ti.lane) == need;
+      uint32_t selbits = gtb | (all_ties ? eqb : 0u);
       const int cn = cnt[gq];
       const int cnt16 = static_cast<int>(lane_xor<16>(static_cast<uint32_t>(cn), ti.lane));
       const int cnt32 = static_cast<int>(lane_xor<32>(static_cast<uint32_t>(cn), ti.lane));
@@ -984,38 +1010,28 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       __syncthreads();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      // Every lane of the query sorts the query's keff blocks (-1 from keff
-      // up to topk).  Rows of whole 16-byte chunks: lane g stores chunks g,
-      // g + 4, ..., so one store writes a 64-byte stretch of the row;
-      // otherwise lane g writes entries g, g + 4, ...
-      int b[KL];
+      // The query's 4 lanes sort its keff blocks together, lane g taking
+      // entries g E .. g E + E - 1 of the row (E = KL / 4; padding past keff
+      // sorts last and becomes -1), and store them: whole 16-byte chunks
+      // when the row allows, else entry by entry.
+      constexpr int E = KL / 4;
+      int b[E];
 #pragma unroll
-      for (int u = 0; u < KL; ++u) b[u] = u < kq ? list[u] : 0x7fffffff;
-      sort_asc<KL>(b);
+      for (int i = 0; i < E; ++i) b[i] = ti.g * E + i < kq ? list[ti.g * E + i] : 0x7fffffff;
+      sort_asc_lanes<E>(b, ti.g, ti.lane);
 #pragma unroll
-      for (int u = 0; u < KL; ++u) b[u] = u < kq ? b[u] - ti.lo : -1;
-      if (((reinterpret_cast<uintptr_t>(dst) | static_cast<uintptr_t>(topk) * 4u) & 15u) == 0) {
+      for (int i = 0; i < E; ++i) b[i] = ti.g * E + i < kq ? b[i] - ti.lo : -1;
+      if (E % 4 == 0 && ((reinterpret_cast<uintptr_t>(dst) | static_cast<uintptr_t>(topk) * 4u) & 15u) == 0) {
 #pragma unroll
-        for (int c0 = 0; c0 < KL / 4; c0 += 4) {
-          int v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[i] = b[4 * c0 + i];
-#pragma unroll
-            for (int hh = 1; hh < 4; ++hh)
-              if (4 * (c0 + hh) + i < KL) v[i] = ti.g == hh ? b[4 * (c0 + hh) + i] : v[i];
-          }
-          const int cc = c0 + ti.g;
-          if (cc < KL / 4 && 4 * cc < topk) *reinterpret_cast<int4*>(dst + 4 * cc) = make_int4(v[0], v[1], v[2], v[3]);
+        for (int c0 = 0; c0 < E; c0 += 4) {
+          const int t = ti.g * E + c0;
+          if (t < topk) *reinterpret_cast<int4*>(dst + t) = make_int4(b[c0], b[c0 + 1], b[c0 + 2], b[c0 + 3]);
         }
       } else {
 #pragma unroll
-        for (int t0 = 0; t0 < KL; t0 += 4) {
-          int me = b[t0];
-#pragma unroll
-          for (int e = 1; e < 4; ++e) me = ti.g == e ? b[t0 + e] : me;
-          const int t = t0 + ti.g;
-          if (t < topk) dst[t] = me;
+        for (int i = 0; i < E; ++i) {
+          const int t = ti.g * E + i;
+          if (t < topk) dst[t] = b[i];
         }
       }
     }
