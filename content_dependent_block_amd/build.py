@@ -29,10 +29,13 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "--offload-arch=gf
          "-Wno-unused-result", f"-I{ROOT / 'include'}", f"-I{CSRC}"]
 
 
-# Per-source extras.  coarse_score: its scores are never NaN for finite
-# inputs, and without NaN semantics a max of MFMA results needs no
-# canonicalising instruction in front of it.
-EXTRA = {"coarse_score.hip": ["-fno-honor-nans"]}
+# Per-source extras.  coarse_score and fine_gather: their scores are never
+# NaN for finite inputs, and without NaN semantics a max of MFMA results
+# needs no canonicalising instruction in front of it.  (fine_gather's one
+# documented non-finite case, a bf16 value beyond the fp16 range, reaches the
+# output through the combine's multiply-adds, which propagate inf and NaN
+# whatever the flag.)
+EXTRA = {"coarse_score.hip": ["-fno-honor-nans"], "fine_gather.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str) -> Path:

@@ -382,9 +382,10 @@ __device__ __forceinline__ int out_dim(int dt, int m) {
 // o = sum 2^(z-m) v / l with m + log2 l in its low bits (m in log2 units,
 // l = sum 2^(z-m)).  The softmax scale is folded
 // into the exp2 argument (the max is taken on raw scores; the scale is > 0),
-// and for bf16 inputs l comes out of the PV MFMA itself: one more 16-row
-// output tile whose A operand is a row of ones multiplies the same rounded
-// probabilities, so l sums exactly the weights that enter o.
+// and for bf16 inputs l comes out of the PV MFMA itself: one more output
+// tile whose A operand is all ones multiplies the same rounded
+// probabilities, so l sums exactly the weights that enter o, and every row
+// of that tile, hence every lane of the pair's column, holds it.
 template <typename T, int D, bool CAUSAL>
 __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage, const QOperand<T, D>& qo,
                                            int64_t row, int beta, int n, int klim, bool live, int32_t pair,
@@ -434,9 +435,8 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
 #pragma unroll
   for (int tt = 0; tt < 4; ++tt)
     mx = fmaxf(mx, fmaxf(fmaxf(s[tt][0], s[tt][1]), fmaxf(s[tt][2], s[tt][3])));
-  mx = fmaxf(mx, __shfl_xor(mx, 16));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));  // a live pair has >= 1 visible key: finite
-  const float m = mx * scale_log2;     // log2-domain max
+  mx = max_over_groups(mx);         // a live pair has >= 1 visible key: finite
+  const float m = mx * scale_log2;  // log2-domain max
   f32x4 acc[D / 16];
 #pragma unroll
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -450,7 +450,7 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
         bp[kk][i] = f32_to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * kk][i], scale_log2, -m)));
         bp[kk][4 + i] = f32_to_bf16(__builtin_amdgcn_exp2f(__builtin_fmaf(s[2 * kk + 1][i], scale_log2, -m)));
       }
-    const __bf16 one = static_cast<__bf16>(c16 == 0 ? 1.0f : 0.0f);
+    const __bf16 one = static_cast<__bf16>(1.0f);
     const bf16x8 ones = {one, one, one, one, one, one, one, one};
     f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -465,8 +465,7 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
       }
       lacc = mfma_16x16x32_bf16(ones, bp[kk], lacc);
     }
-    // row 0 of the ones tile (lane c16, element 0) holds l of query c16
-    lt = __shfl(lacc[0], c16);
+    lt = lacc[0];  // C[m][c16] = l of pair c16 for every row m
   } else {
     float p[4][4];
     float lsum = 0.f;
@@ -485,8 +484,7 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) acc[dt] = mfma_16x16x4_f32(vr[16 * dt], p[tt][jj], acc[dt]);
       }
-    lt = lsum + __shfl_xor(lsum, 16);
-    lt += __shfl_xor(lt, 32);
+    lt = sum_over_groups(lsum);
   }
   // l >= 1 (the maximum's own weight is 1): the hardware reciprocal (1 ulp)
   // is far inside the fp16 rounding of the row it scales.
