@@ -549,11 +549,17 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
   }
 }
 
+// Query operands in flight ahead of the 16-pair group being computed: two
+// keeps the d = 64 kernel at 88 VGPRs (5 waves per SIMD; all eight groups'
+// rows at once took 120 VGPRs, 4 waves) and was faster than three or four.
+constexpr int kQueryAhead = 2;
+
 // One work item = up to IP pairs of one bucket (head, key block),
 // described by the record the fill kernel left at this workgroup's slot.
-// Every load the item needs is issued before any is waited on: the wave's
-// list entries, the block's K/V into registers, then (as the list entries
-// arrive) the pairs' query rows; then K/V go to LDS and the MFMA work runs.
+// The loads the item needs are issued before the first is waited on: the
+// wave's list entries, the block's K/V into registers, and the query rows of
+// its first kQueryAhead groups; then K/V go to LDS and the MFMA work runs,
+// each group issuing the query rows of the group kQueryAhead after it.
 // row = pair / topk uses a precomputed multiply-shift (exact for pair < 2^31).
 template <typename T, int D, bool CAUSAL, int IP>
 __global__ __launch_bounds__(256) void gather_partial_kernel(
@@ -609,13 +615,15 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
       live[gi] = false;
     }
     row[gi] = row0 + static_cast<int64_t>((static_cast<uint64_t>(pair[gi]) * div_magic) >> div_shift);
-    load_q<T, D>(qo[gi], q, row[gi], live[gi], g);
+    if (gi < kQueryAhead) load_q<T, D>(qo[gi], q, row[gi], live[gi], g);
   }
   kv_store<T, D>(kv, ks, vs, tid);
   __syncthreads();
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     if ((wave + 4 * gi) * 16 >= cnt) break;  // wave-uniform
+    if (gi + kQueryAhead < GPW)
+      load_q<T, D>(qo[gi + kQueryAhead], q, row[gi + kQueryAhead], live[gi + kQueryAhead], g);
     pair_group<T, D, CAUSAL>(ks, vs, stage, qo[gi], row[gi], beta, n, klim, live[gi], pair[gi],
                              scale_log2, po, lane);
   }
