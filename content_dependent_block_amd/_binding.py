@@ -74,6 +74,7 @@ _sig("bsa_tiles_window_stride", [_I, _I, _I, _I, _P, _P, _P, ctypes.POINTER(_I64
 _sig("bsa_tiles_validate", [_P, _P, _I64, _I, _I])
 _sig("bsa_profile_enable", [_P, _I])
 _sig("bsa_profile_read", [_P, _P, _P, _I])
+_sig("bsa_select_fallbacks", [_P, _P, _I])
 
 EXPORTED = ("bsa_create", "bsa_destroy", "bsa_status_string", "bsa_last_error", "bsa_set_option",
             "bsa_workspace_bytes", "bsa_forward", "bsa_forward_noalloc", "bsa_forward_budgets",
@@ -83,7 +84,7 @@ EXPORTED = ("bsa_create", "bsa_destroy", "bsa_status_string", "bsa_last_error", 
             "bsa_coarse_score", "bsa_topk_select", "bsa_tiles_create", "bsa_tiles_destroy",
             "bsa_forward_static", "bsa_tiles_from_mask",
             "bsa_tiles_window_stride", "bsa_tiles_validate", "bsa_profile_enable",
-            "bsa_profile_read")
+            "bsa_profile_read", "bsa_select_fallbacks")
 
 
 class BsaError(RuntimeError):
@@ -463,3 +464,11 @@ def bsa_profile_read(h, reset: bool = True):
     launches = (ctypes.c_int64 * BSA_NUM_STAGES)()
     _check(_lib.bsa_profile_read(h, ms, launches, int(reset)), h)
     return list(ms), list(launches)
+
+
+def bsa_select_fallbacks(h, reset: bool = False) -> int:
+    """Fused-selection workgroups that took the exact fallback on this handle
+    (waits for the device)."""
+    c = ctypes.c_int64(0)
+    _check(_lib.bsa_select_fallbacks(h, ctypes.byref(c), int(reset)), h)
+    return int(c.value)

@@ -54,6 +54,7 @@ struct bsa_handle_s {
   Buf s_part, s_lse;  // static mode: partial rows of split query tiles and their log-sum-exp
   int64_t static_item_tiles = 0;  // 0: chosen per call; else the most key tiles per work item
   int union_rows = 64;            // query-tile rows of the query-tile union fine stage
+  int32_t* fallbacks = nullptr;   // device counter: fused-selection workgroups that took the exact fallback
   // timing
   bool profiling = false;
   struct Rec {
@@ -270,6 +271,16 @@ BSA_API bsa_status bsa_create(int device, bsa_handle* out) {
   if (!h) return fail(nullptr, BSA_ERR_OUT_OF_MEMORY, "bsa_create: host allocation failed");
   h->device = device;
   h->noalloc = arena;
+  {
+    DeviceGuard dg(device);
+    if (hipMalloc(reinterpret_cast<void**>(&h->fallbacks), sizeof(int32_t)) != hipSuccess ||
+        hipMemset(h->fallbacks, 0, sizeof(int32_t)) != hipSuccess) {
+      (void)hipGetLastError();
+      if (h->fallbacks) (void)hipFree(h->fallbacks);
+      delete h;
+      return fail(nullptr, BSA_ERR_OUT_OF_MEMORY, "bsa_create: cannot allocate the handle's counter");
+    }
+  }
   *out = h;
   return BSA_OK;
 }
@@ -284,6 +295,7 @@ BSA_API bsa_status bsa_destroy(bsa_handle h) {
   for (auto e : h->free_events) (void)hipEventDestroy(e);
   if (h->tab_ev) (void)hipEventDestroy(h->tab_ev);
   if (h->tab_host) (void)hipHostFree(h->tab_host);
+  if (h->fallbacks) (void)hipFree(h->fallbacks);
   if (h->repr) (void)hipFree(h->repr);
   if (h->split) (void)hipFree(h->split);
   if (h->panel) (void)hipFree(h->panel);
@@ -511,7 +523,8 @@ bsa_status run_select(bsa_handle h, const void* q, const float* repr, const uint
   const int64_t total = s.bh() * s.n;
   if (fused_select(h, topk))
     return timed_launch(h, BSA_STAGE_COARSE_TOPK, st, "coarse_select", [&] {
-      return bsa::launch_coarse_select(q, repr, split, idx, total, s.n, s.d, dt, topk, hb, causal, st, tab);
+      return bsa::launch_coarse_select(q, repr, split, idx, total, s.n, s.d, dt, topk, hb, causal, st, tab,
+                                       h->fallbacks);
     });
   int64_t chunk = h->panel_chunk_bytes / (nb * 4) / 64 * 64;
   if (arena) {
@@ -1454,5 +1467,19 @@ BSA_API bsa_status bsa_profile_read(bsa_handle h, double* ms, int64_t* launches,
     }
     h->recs.clear();
   }
+  return BSA_OK;
+}
+
+BSA_API bsa_status bsa_select_fallbacks(bsa_handle h, int64_t* count, int reset) {
+  if (!h || !count) return fail(h, BSA_ERR_INVALID_ARG, "bsa_select_fallbacks: NULL argument");
+  DeviceGuard dg(h->device);
+  int32_t c = 0;
+  if (hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpy(&c, h->fallbacks, sizeof(c), hipMemcpyDeviceToHost) != hipSuccess ||
+      (reset && hipMemset(h->fallbacks, 0, sizeof(int32_t)) != hipSuccess)) {
+    (void)hipGetLastError();
+    return fail(h, BSA_ERR_LAUNCH, "bsa_select_fallbacks: reading the counter failed");
+  }
+  *count = c;
   return BSA_OK;
 }

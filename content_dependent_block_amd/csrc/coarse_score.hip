@@ -843,7 +843,8 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
                                                                       int32_t* __restrict__ idx, int n,
                                                                       int topk, const HeadBudget budget,
                                                                       int causal,
-                                                                      const int4* __restrict__ seqtab) {
+                                                                      const int4* __restrict__ seqtab,
+                                                                      int32_t* __restrict__ fallbacks) {
   using TL1 = typename Pass1Tiles<TL>::type;
   constexpr int NTH = 64 * NW;
   constexpr int MT = TL1::TB / 16;    // MFMA tiles per R tile of pass 1
@@ -1038,6 +1039,8 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
   } else {
     // slots overflowed somewhere in the workgroup: offer every score to
     // exact register lists and merge them pairwise, one query group at a time
+    // (counted, one vector atomic per such workgroup, when asked)
+    if (fallbacks && threadIdx.x == 0) atomicAdd(fallbacks, 1);
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
       TopList<KL> l;
@@ -1075,11 +1078,11 @@ void launch_panel(const void* q, const void* rsrc, float* panel, int64_t row0, i
 
 template <typename TL, int KL, int GM, int CAP, int MINW, int QG, int NW>
 void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
-                   const HeadBudget& hb, int causal, const int4* seqtab, hipStream_t s) {
+                   const HeadBudget& hb, int causal, const int4* seqtab, int32_t* fallbacks, hipStream_t s) {
   constexpr int ROWS = 16 * QG * NW;
   hipLaunchKernelGGL((coarse_select_kernel<TL, KL, GM, CAP, MINW, QG, NW>), dim3(static_cast<unsigned>(rows / ROWS)),
                      dim3(64 * NW), 0, s, static_cast<const typename TL::QT*>(q),
-                     static_cast<const typename TL::Src*>(rsrc), idx, n, topk, hb, causal, seqtab);
+                     static_cast<const typename TL::Src*>(rsrc), idx, n, topk, hb, causal, seqtab, fallbacks);
 }
 
 // One 16-query group per wave, four waves per workgroup; the register budget
@@ -1087,11 +1090,11 @@ void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, 
 // whose candidate lists are twice as long).
 template <template <int, int, int> class TLT, int D>
 void launch_select_k(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
-                     const HeadBudget& hb, int causal, const int4* seqtab, hipStream_t s) {
+                     const HeadBudget& hb, int causal, const int4* seqtab, int32_t* fb, hipStream_t s) {
   constexpr int M1 = (D == 64 && std::is_same<typename TLT<D, 1, 256>::QT, bf16_bits>::value) ? 4 : 3;
-  if (topk <= 8) launch_select<TLT<D, 1, 256>, 8, 1, 8, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, s);
-  else if (topk <= 16) launch_select<TLT<D, 1, 256>, 16, 1, 16, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, s);
-  else launch_select<TLT<D, 1, 256>, 32, 2, 32, 2, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, s);
+  if (topk <= 8) launch_select<TLT<D, 1, 256>, 8, 1, 8, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, fb, s);
+  else if (topk <= 16) launch_select<TLT<D, 1, 256>, 16, 1, 16, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, fb, s);
+  else launch_select<TLT<D, 1, 256>, 32, 2, 32, 2, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, fb, s);
 }
 
 template <int D, int QG, int NTH>
@@ -1117,13 +1120,13 @@ hipError_t launch_coarse_score(const void* q, const float* repr, float* panel, i
 hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t* repr_split,
                                 int32_t* idx, int64_t rows, int n, int d, bsa_dtype dtype,
                                 int topk, const HeadBudget& hb, int causal, hipStream_t stream,
-                                const int4* seqtab) {
+                                const int4* seqtab, int32_t* fallbacks) {
   if (dtype == BSA_BF16) {
-    if (d == 64) launch_select_k<PlaneT, 64>(q, repr_split, idx, rows, n, topk, hb, causal, seqtab, stream);
-    else launch_select_k<PlaneT, 128>(q, repr_split, idx, rows, n, topk, hb, causal, seqtab, stream);
+    if (d == 64) launch_select_k<PlaneT, 64>(q, repr_split, idx, rows, n, topk, hb, causal, seqtab, fallbacks, stream);
+    else launch_select_k<PlaneT, 128>(q, repr_split, idx, rows, n, topk, hb, causal, seqtab, fallbacks, stream);
   } else {
-    if (d == 64) launch_select_k<F32T, 64>(q, repr, idx, rows, n, topk, hb, causal, seqtab, stream);
-    else launch_select_k<F32T, 128>(q, repr, idx, rows, n, topk, hb, causal, seqtab, stream);
+    if (d == 64) launch_select_k<F32T, 64>(q, repr, idx, rows, n, topk, hb, causal, seqtab, fallbacks, stream);
+    else launch_select_k<F32T, 128>(q, repr, idx, rows, n, topk, hb, causal, seqtab, fallbacks, stream);
   }
   return hipGetLastError();
 }

@@ -61,6 +61,7 @@ def test_null_handle_is_rejected(m):
                                  64, 1, 64, 1, 0.1, 0, None) == m.BSA_ERR_INVALID_ARG
     assert L.bsa_set_option(None, 0, 1) == m.BSA_ERR_INVALID_ARG
     assert L.bsa_profile_enable(None, 1) == m.BSA_ERR_INVALID_ARG
+    assert L.bsa_select_fallbacks(None, None, 0) == m.BSA_ERR_INVALID_ARG
     assert L.bsa_destroy(None) == m.BSA_OK
 
 

@@ -720,6 +720,57 @@ def test_selection_exact_ties(bsa, select, causal):
     np.testing.assert_array_equal(idx.cpu().numpy().reshape(-1, topk), ref)
 
 
+def fallback_workgroups(nb, topk, causal):
+    """Workgroups of one head whose fused selection must take the exact
+    fallback when every score of a query is equal: a lane of a 64-query
+    workgroup holds, of each 16-block tile, the blocks 4 g .. 4 g + 3, and its
+    candidates (every block, up to its own when causal) overflow its slots."""
+    cap = 8 if topk <= 8 else 16 if topk <= 16 else 32
+    count = 0
+    for qb in range(nb):
+        cand = np.arange(qb + 1 if causal else nb)
+        per_lane = np.bincount((cand // 4) % 4, minlength=4)
+        count += int(per_lane.max() > cap)
+    return count
+
+
+@pytest.mark.parametrize("dtype,d,topk,causal,n", [("bf16", 64, 16, False, 8192), ("bf16", 64, 16, True, 8192),
+                                                   ("bf16", 128, 32, True, 16384), ("fp32", 64, 8, False, 4096)])
+def test_selection_fallback_runs(bsa, dtype, d, topk, causal, n):
+    """Every key row is the same vector, so all block representatives are
+    equal and so are all of a query's scores: every one is a candidate, lanes
+    hold more candidates than slots, and the workgroups that must take the
+    exact fallback are known in advance.  The count from
+    bsa_select_fallbacks must match, and the selection (all ties, so the
+    lowest blocks, plus the own block when causal) must equal the oracle's."""
+    m, lib = bsa
+    use_strategy(m, lib, "block_gather", "fused")
+    rng = np.random.default_rng(77)
+    q = rng.standard_normal((1, 1, n, d), dtype=np.float32)
+    k = np.repeat(rng.standard_normal((1, 1, 1, d), dtype=np.float32), n, axis=2)
+    v = rng.standard_normal((1, 1, n, d), dtype=np.float32)
+    if dtype == "bf16":
+        (q, qb), (k, kb), (v, vb) = W.bf16_round(q), W.bf16_round(k), W.bf16_round(v)
+        inp = W.Inputs(q, k, v, qb, kb, vb)
+    else:
+        inp = W.Inputs(q, k, v)
+    nb = n // 64
+    expected = fallback_workgroups(nb, topk, causal)
+    say(f"[gpu] selection fallback {dtype} d={d} k={topk} causal={causal} n={n}: {expected} workgroups expected")
+    assert expected > 0
+    dq, dk, dv = to_dev(inp, dtype)
+    out = torch.empty(dq.shape, dtype=torch.float32, device="cuda")
+    idx = torch.empty((1, 1, n, topk), dtype=torch.int32, device="cuda")
+    m.bsa_select_fallbacks(lib.handle, reset=True)
+    m.bsa_forward(lib.handle, dq, dk, dv, out, idx, topk=topk, scale=1.0 / np.sqrt(d), causal=causal)
+    got = m.bsa_select_fallbacks(lib.handle, reset=True)
+    assert got == expected, f"{got} workgroups took the fallback, {expected} expected"
+    r = oracle.pool(inp.k.astype(np.float64), 64)
+    sc = oracle.scores(inp.q.astype(np.float64), r, 64)
+    ref, _, _ = oracle.topk(sc, n, 64, topk, causal)
+    np.testing.assert_array_equal(idx.cpu().numpy().reshape(-1, topk), ref)
+
+
 # ------------------------------------------------------------ ragged n --
 RAGGED = [("tiny_fp32_n1k", 1000, 4, False), ("tiny_fp32_n1k", 1000, 4, True),
           ("dyn_bf16_n4k", 4100, 16, False), ("dyn_bf16_n4k", 4100, 16, True),
