@@ -458,6 +458,15 @@ def main():
     r = Runner(m, lib, w, args.which, args)
     res = measure(r, args, scratch, args.steps, args.warmup)
     unions = union_stats(r.idx, w) if args.union_stats and args.which == "forward" and not w.static else None
+    fallbacks = None
+    if args.which == "forward" and not w.static and args.select_strategy == "fused":
+        # one more (untimed) step: how many 64-query selection workgroups
+        # walked their candidates twice / took the exact fallback on this data
+        m.bsa_select_fallbacks(h, reset=True)
+        r.step()
+        second, exact = m.bsa_select_fallbacks(h, reset=True)
+        fallbacks = {"second_walk": second, "exact_redo": exact,
+                     "workgroups": w.batch * w.heads * (-(-w.n // 64))}
     inp, dout_np = r.inp, r.dout_np
     static_mask = None
     if w.static and not args.no_cpu_baseline:
@@ -526,6 +535,8 @@ def main():
         result["workloads"] = others
     if unions:
         result["query_tile_unions"] = unions
+    if fallbacks is not None:
+        result["select_fallbacks_per_step"] = fallbacks
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = (cpu_baseline(w, inp, args.cpu_positions, static_mask)
                                   if args.which == "forward" else cpu_baseline_backward(w, inp, dout_np))

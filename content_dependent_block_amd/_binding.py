@@ -466,9 +466,10 @@ def bsa_profile_read(h, reset: bool = True):
     return list(ms), list(launches)
 
 
-def bsa_select_fallbacks(h, reset: bool = False) -> int:
-    """Fused-selection workgroups that took the exact fallback on this handle
+def bsa_select_fallbacks(h, reset: bool = False):
+    """(second walks, exact redos): fused-selection workgroups that walked
+    their candidates a second time / took the exact fallback on this handle
     (waits for the device)."""
-    c = ctypes.c_int64(0)
-    _check(_lib.bsa_select_fallbacks(h, ctypes.byref(c), int(reset)), h)
-    return int(c.value)
+    c = (ctypes.c_int64 * 2)()
+    _check(_lib.bsa_select_fallbacks(h, c, int(reset)), h)
+    return int(c[0]), int(c[1])

@@ -54,7 +54,7 @@ struct bsa_handle_s {
   Buf s_part, s_lse;  // static mode: partial rows of split query tiles and their log-sum-exp
   int64_t static_item_tiles = 0;  // 0: chosen per call; else the most key tiles per work item
   int union_rows = 64;            // query-tile rows of the query-tile union fine stage
-  int32_t* fallbacks = nullptr;   // device counter: fused-selection workgroups that took the exact fallback
+  int32_t* fallbacks = nullptr;   // device counters [2]: fused-selection second walks, exact fallbacks
   // timing
   bool profiling = false;
   struct Rec {
@@ -273,8 +273,8 @@ BSA_API bsa_status bsa_create(int device, bsa_handle* out) {
   h->noalloc = arena;
   {
     DeviceGuard dg(device);
-    if (hipMalloc(reinterpret_cast<void**>(&h->fallbacks), sizeof(int32_t)) != hipSuccess ||
-        hipMemset(h->fallbacks, 0, sizeof(int32_t)) != hipSuccess) {
+    if (hipMalloc(reinterpret_cast<void**>(&h->fallbacks), 2 * sizeof(int32_t)) != hipSuccess ||
+        hipMemset(h->fallbacks, 0, 2 * sizeof(int32_t)) != hipSuccess) {
       (void)hipGetLastError();
       if (h->fallbacks) (void)hipFree(h->fallbacks);
       delete h;
@@ -1470,16 +1470,17 @@ BSA_API bsa_status bsa_profile_read(bsa_handle h, double* ms, int64_t* launches,
   return BSA_OK;
 }
 
-BSA_API bsa_status bsa_select_fallbacks(bsa_handle h, int64_t* count, int reset) {
-  if (!h || !count) return fail(h, BSA_ERR_INVALID_ARG, "bsa_select_fallbacks: NULL argument");
+BSA_API bsa_status bsa_select_fallbacks(bsa_handle h, int64_t* counts, int reset) {
+  if (!h || !counts) return fail(h, BSA_ERR_INVALID_ARG, "bsa_select_fallbacks: NULL argument");
   DeviceGuard dg(h->device);
-  int32_t c = 0;
+  int32_t c[2] = {0, 0};
   if (hipDeviceSynchronize() != hipSuccess ||
-      hipMemcpy(&c, h->fallbacks, sizeof(c), hipMemcpyDeviceToHost) != hipSuccess ||
-      (reset && hipMemset(h->fallbacks, 0, sizeof(int32_t)) != hipSuccess)) {
+      hipMemcpy(c, h->fallbacks, sizeof(c), hipMemcpyDeviceToHost) != hipSuccess ||
+      (reset && hipMemset(h->fallbacks, 0, sizeof(c)) != hipSuccess)) {
     (void)hipGetLastError();
-    return fail(h, BSA_ERR_LAUNCH, "bsa_select_fallbacks: reading the counter failed");
+    return fail(h, BSA_ERR_LAUNCH, "bsa_select_fallbacks: reading the counters failed");
   }
-  *count = c;
+  counts[0] = c[0];
+  counts[1] = c[1];
   return BSA_OK;
 }

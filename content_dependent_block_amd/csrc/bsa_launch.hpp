@@ -52,8 +52,9 @@ struct HeadBudget {
 // query rows: idx[row * topk + t], no panel.  Representatives: for bf16
 // inputs the split form from block_pool (repr_split), for fp32 inputs the
 // float32 repr.  Candidates: the blocks of the query's sequence; indices
-// relative to its first block.  fallbacks (may be null): a device counter to
-// which every workgroup that took the exact fallback adds 1.
+// relative to its first block.  fallbacks (may be null): two device counters;
+// a workgroup adds 1 to [0] when it walks the candidates a second time and to
+// [1] when it takes the exact fallback.
 hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t* repr_split,
                                 int32_t* idx, int64_t rows, int n, int d, bsa_dtype dtype,
                                 int topk, const HeadBudget& budget, int causal, hipStream_t stream,

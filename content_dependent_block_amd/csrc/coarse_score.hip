@@ -44,10 +44,12 @@
 //     quarter of the output in ascending block order.  Because the answer is
 //     ranked from pass 2's scores alone and pass 2 checks it holds >= k_eff
 //     candidates, the result is exact.
-//   A workgroup in which some lane has more candidates than slots (or fewer
-//     than k_eff candidates) redoes the walk offering every score to exact
-//     register top-KL lists (topk_list.hpp) merged the same way: the same
-//     answer, slower.
+//   A workgroup in which some lane has more candidates than slots walks
+//     pass 2 again with tau raised to the k_eff-th largest candidate its lanes
+//     kept; one in which that also overflows (or that has fewer than k_eff
+//     candidates) redoes the walk offering every score to exact register
+//     top-KL lists (topk_list.hpp) merged the same way: the same answer,
+//     slower.
 // topk_select.hip states the selection semantics.
 //
 // Workgroups are issued XCD-major: consecutive workgroup ids go round-robin
@@ -931,13 +933,37 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
         }
       }
   };
+  // A workgroup in which some lane's candidates overflowed its slots walks a
+  // second time with a higher bound: tau2 = the k_eff-th largest of the
+  // candidates its lanes did keep (real scores, so at least k_eff scores are
+  // >= tau2, and every score of the answer is).  Only if that also overflows
+  // does it take the exact redo below.
   walk<1, kTerms, QG, NTH>(sc, rs, rbase, ti,
                            [&](int, int, int b0, const f32x4 (&acc)[QG]) { append(false, b0, acc); },
                            [&](int, int, int b0, const f32x4 (&acc)[QG]) { append(true, b0, acc); });
   bool bad = false;
 #pragma unroll
   for (int gq = 0; gq < QG; ++gq) bad = bad || cnt[gq] > CAP || sum4(cnt[gq], ti.lane) < keff[gq];
-  const int redo = __syncthreads_or(bad);
+  int redo = __syncthreads_or(bad);
+  if (redo) {  // rare: its own copy of the walk keeps the common path's code as it was
+    if (fallbacks && threadIdx.x == 0) atomicAdd(fallbacks, 1);
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) {
+      float c[CAP];
+#pragma unroll
+      for (int i = 0; i < CAP; ++i) c[i] = i < cnt[gq] ? cv[ti.wave][gq][i][ti.lane] : -INFINITY;
+      sort_desc<CAP>(c);
+      tau[gq] = fmaxf(tau[gq], kth_of_lanes<CAP>(c, keff[gq], ti.lane));
+      cnt[gq] = 0;
+    }
+    walk<1, kTerms, QG, NTH>(sc, rs, rbase, ti,
+                             [&](int, int, int b0, const f32x4 (&acc)[QG]) { append(false, b0, acc); },
+                             [&](int, int, int b0, const f32x4 (&acc)[QG]) { append(true, b0, acc); });
+    bad = false;
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) bad = bad || cnt[gq] > CAP || sum4(cnt[gq], ti.lane) < keff[gq];
+    redo = __syncthreads_or(bad);
+  }
 
   if (!redo) {
 #pragma unroll
@@ -1040,7 +1066,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
     // slots overflowed somewhere in the workgroup: offer every score to
     // exact register lists and merge them pairwise, one query group at a time
     // (counted, one vector atomic per such workgroup, when asked)
-    if (fallbacks && threadIdx.x == 0) atomicAdd(fallbacks, 1);
+    if (fallbacks && threadIdx.x == 0) atomicAdd(fallbacks + 1, 1);
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
       TopList<KL> l;

@@ -499,14 +499,17 @@ bsa_status bsa_profile_read(bsa_handle h, double* ms, int64_t* launches,
 
 /* The fused selection (bsa_forward and the entry points built on it, with
  * BSA_SELECT_FUSED and k <= 32) keeps each query's candidates in a fixed
- * number of slots per lane (16 for k <= 16, 8 for k <= 8, 32 for k <= 32);
- * a 64-query workgroup in which some lane has more candidates redoes its walk
- * with exact per-lane top-k lists (the same answer, slower).  This returns in
- * *count how many workgroups took that fallback on this handle since it was
- * created or last reset (reset != 0 clears it after reading).  It waits for
- * all work on the handle's device.  Errors: INVALID_ARG for a NULL argument,
- * LAUNCH if the device reports an error. */
-bsa_status bsa_select_fallbacks(bsa_handle h, int64_t* count, int reset);
+ * number of slots per lane (8 for k <= 8, 16 for k <= 16, 32 for k <= 32).
+ * A 64-query workgroup in which some lane has more candidates walks the
+ * scores a second time with a higher bound; if a lane overflows again, it
+ * redoes the walk with exact per-lane top-k lists.  Every path gives the same
+ * answer; the later ones are slower.  This writes, for this handle since it
+ * was created or last reset, counts[0] = workgroups that walked a second
+ * time and counts[1] = workgroups that took the exact redo (reset != 0
+ * clears both after reading).  It waits for all work on the handle's device.
+ * Errors: INVALID_ARG for a NULL argument, LAUNCH if the device reports an
+ * error. */
+bsa_status bsa_select_fallbacks(bsa_handle h, int64_t* counts, int reset);
 
 #ifdef __cplusplus
 }

@@ -739,10 +739,11 @@ def fallback_workgroups(nb, topk, causal):
 def test_selection_fallback_runs(bsa, dtype, d, topk, causal, n):
     """Every key row is the same vector, so all block representatives are
     equal and so are all of a query's scores: every one is a candidate, lanes
-    hold more candidates than slots, and the workgroups that must take the
-    exact fallback are known in advance.  The count from
-    bsa_select_fallbacks must match, and the selection (all ties, so the
-    lowest blocks, plus the own block when causal) must equal the oracle's."""
+    hold more candidates than slots (also on the second walk, whose bound is
+    that same score), and the workgroups that must take the exact fallback
+    are known in advance.  Both counts from bsa_select_fallbacks must match,
+    and the selection (all ties, so the lowest blocks, plus the own block when
+    causal) must equal the oracle's."""
     m, lib = bsa
     use_strategy(m, lib, "block_gather", "fused")
     rng = np.random.default_rng(77)
@@ -764,7 +765,7 @@ def test_selection_fallback_runs(bsa, dtype, d, topk, causal, n):
     m.bsa_select_fallbacks(lib.handle, reset=True)
     m.bsa_forward(lib.handle, dq, dk, dv, out, idx, topk=topk, scale=1.0 / np.sqrt(d), causal=causal)
     got = m.bsa_select_fallbacks(lib.handle, reset=True)
-    assert got == expected, f"{got} workgroups took the fallback, {expected} expected"
+    assert got == (expected, expected), f"(second walks, exact redos) = {got}, {expected} each expected"
     r = oracle.pool(inp.k.astype(np.float64), 64)
     sc = oracle.scores(inp.q.astype(np.float64), r, 64)
     ref, _, _ = oracle.topk(sc, n, 64, topk, causal)
