@@ -865,14 +865,25 @@ hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, 
     hipLaunchKernelGGL(zero_i32_kernel, dim3(static_cast<unsigned>((a.ws.count_words + 255) / 256)), dim3(256),
                        0, s, a.ws.count, a.ws.count_words);
   const int seg = a.n / a.qsegs;
-  // 256 rows per bucketing workgroup (fewer global atomics) once that still
-  // gives >= 512 workgroups (two per CU); smaller chunks use 64 rows so the
-  // whole GPU takes part (N = 4096, 8 heads: bucketing 32 -> 24.5 us).
-  const int rpw = (seg % 256 == 0 && row0 % 256 == 0 && rows >= int64_t(512) * 256) ? 256 : kTile;
+  // Rows per bucketing workgroup: 256 (fewer global atomics) when that still
+  // gives >= 512 workgroups and its LDS (histogram, bases and the ordered
+  // records) lets two of them share a CU, else 128 under the same
+  // conditions, else 64, so the whole GPU takes part.  (N = 4096, 8 heads:
+  // bucketing 32 -> 24.5 us at 64 rows; N = 128k causal, 2048 blocks, k = 32:
+  // 0.70 -> 0.56 ms per step at 128 rows, where 256 rows took 82 KB, one
+  // workgroup per CU.)
+  auto lds_for = [&](int r) {
+    const int np_r = r * a.topk;
+    return (2 * static_cast<size_t>(c.nb) + 4) * 4 + (np_r <= 256 * kPairRegs ? static_cast<size_t>(np_r) * 8 : 0);
+  };
+  int rpw = kTile;
+  for (const int r : {256, 128})
+    if (seg % r == 0 && row0 % r == 0 && rows >= int64_t(512) * r && lds_for(r) <= 80 * 1024) {
+      rpw = r;
+      break;
+    }
   const int64_t row_groups = (rows + rpw - 1) / rpw;
-  const int np = rpw * a.topk;  // pairs per workgroup
-  const size_t count_lds = (2 * static_cast<size_t>(c.nb) + 4) * 4 +
-                           (np <= 256 * kPairRegs ? static_cast<size_t>(np) * 8 : 0);
+  const size_t count_lds = lds_for(rpw);
   if (count_lds > 64 * 1024) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(bucket_count_kernel),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
