@@ -1301,15 +1301,6 @@ namespace {
 // Work items of at most S key tiles (a longer query-tile list is cut into
 // ceil(count / S) items of near-equal length that write partials), ordered
 // heaviest first; empty query tiles get an item of length 0 (it writes zeros).
-int64_t count_items(const bsa_tiles_s& t, int64_t S) {
-  int64_t items = 0;
-  for (int q = 0; q < t.nt; ++q) {
-    const int64_t c = t.row_ptr[q + 1] - t.row_ptr[q];
-    items += c <= S ? 1 : (c + S - 1) / S;
-  }
-  return items;
-}
-
 bsa_status tiles_schedule(bsa_handle h, bsa_tiles t, int64_t S, const bsa_tiles_s::Schedule** out) {
   for (const auto& sc : t->schedules)
     if (sc.S == S) {
