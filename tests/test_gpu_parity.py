@@ -261,12 +261,19 @@ def test_forward_small_workloads_all_rows(bsa, name, select, strategy):
 def test_forward_headline_all_rows(bsa):
     """N=32768, 8 heads, bf16, k=16 in the launch configuration the benchmark
     times (fused selection, block_gather): every one of the 262,144 query rows
-    against the oracle, indices and outputs."""
+    against the oracle, indices and outputs.  On this data a few selection
+    workgroups overflow their candidate slots and finish with the second walk
+    (its raised bound), so that path is checked here too; none needs the
+    exact redo."""
     m, lib = bsa
     use_strategy(m, lib, "block_gather", "fused")
     w = W.WORKLOADS["dyn_bf16_n32k"]
     inp = W.generate(w)
+    m.bsa_select_fallbacks(lib.handle, reset=True)
     end_to_end(m, lib, w, inp, np.arange(w.bh * w.n, dtype=np.int64))
+    second, exact = m.bsa_select_fallbacks(lib.handle, reset=True)
+    say(f"    selection workgroups that walked twice: {second}, took the exact redo: {exact}")
+    assert second >= 1 and exact == 0
 
 
 @pytest.mark.parametrize("select,strategy", [p for p in PATHS if p != ("fused", "block_gather")])
