@@ -67,10 +67,8 @@ namespace {
 
 constexpr int kTerms = 3;
 
-// R tiles in flight ahead of the one computed in the hi-only pass, and blocks
-// per R tile of that pass (bf16 planes).
+// R tiles in flight ahead of the one computed in the hi-only pass.
 constexpr int kSelectPrefetch = 1;
-constexpr int kPass1Blocks = 64;
 
 __device__ __forceinline__ int64_t xcd_tile(int causal) {
   const int64_t nwg = gridDim.x, bid = blockIdx.x;
@@ -827,16 +825,17 @@ __device__ __forceinline__ void walk(TL& sc, unsigned char* rs, const typename T
 
 // MINW: waves per SIMD the register budget is sized for.  NW waves per
 // workgroup, QG query groups of 16 per wave.
-// The tile type of the hi-only first pass: bf16 planes take 64-block R tiles
-// there (one staged term fits the LDS the 32-block three-term tiles use, and
-// each tile gives four independent MFMA chains); fp32 keeps its tiles.
+// The tile type of the hi-only first pass: bf16 planes take R tiles of twice
+// the three-term tiles' blocks there (one staged term fits the LDS those
+// use; at 64 blocks each tile gives four independent MFMA chains); fp32 keeps
+// its tiles.
 template <typename TL>
 struct Pass1Tiles {
   using type = TL;
 };
 template <int D, int QG, int NTH, int TB_, int NTS>
 struct Pass1Tiles<Bf16PlaneTiles<D, QG, NTH, TB_, NTS>> {
-  using type = Bf16PlaneTiles<D, QG, NTH, kPass1Blocks, 1>;
+  using type = Bf16PlaneTiles<D, QG, NTH, 2 * TB_, 1>;
 };
 
 template <typename TL, int KL, int GM, int CAP, int MINW, int QG, int NW>
@@ -862,7 +861,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
   constexpr int RS_T = TL::LDS_BYTES > TL1::LDS_BYTES ? TL::LDS_BYTES : TL1::LDS_BYTES;
   constexpr int RS0 = RS_T > LIST_BYTES ? RS_T : LIST_BYTES;
   constexpr int RS_BYTES = RS0 > ERR_BYTES ? RS0 : ERR_BYTES;
-  static_assert(CAP <= 32, "candidate slots are tracked in a 32-bit mask");
+  static_assert(CAP <= KL && KL <= 32, "candidate slots are tracked in a 32-bit mask");
   __shared__ __attribute__((aligned(16))) unsigned char rs[RS_BYTES];
   // per lane and query group: candidate scores and blocks
   __shared__ float cv[NW][QG][CAP][64];
@@ -949,11 +948,11 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
     if (fallbacks && threadIdx.x == 0) atomicAdd(fallbacks, 1);
 #pragma unroll
     for (int gq = 0; gq < QG; ++gq) {
-      float c[CAP];
+      float c[KL];
 #pragma unroll
-      for (int i = 0; i < CAP; ++i) c[i] = i < cnt[gq] ? cv[ti.wave][gq][i][ti.lane] : -INFINITY;
-      sort_desc<CAP>(c);
-      tau[gq] = fmaxf(tau[gq], kth_of_lanes<CAP>(c, keff[gq], ti.lane));
+      for (int i = 0; i < KL; ++i) c[i] = (i < CAP && i < cnt[gq]) ? cv[ti.wave][gq][i < CAP ? i : 0][ti.lane] : -INFINITY;
+      sort_desc<KL>(c);
+      tau[gq] = fmaxf(tau[gq], kth_of_lanes<KL>(c, keff[gq], ti.lane));
       cnt[gq] = 0;
     }
     walk<1, kTerms, QG, NTH>(sc, rs, rbase, ti,
@@ -970,21 +969,22 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
     for (int gq = 0; gq < QG; ++gq) {
       int32_t* dst = idx + (ti.qrow0 + 16 * gq) * topk;
       const int kq = keff[gq];
-      // The lane's candidate scores, read once into registers (-inf past cnt),
-      // in ascending block order.
+      // The lane's candidate scores, read once into registers (-inf past cnt
+      // and past the CAP stored slots, up to the list length KL), in ascending
+      // block order.
       const float(&lv)[CAP][64] = cv[ti.wave][gq];
       const uint16_t(&lb)[CAP][64] = cb[ti.wave][gq];
-      float x[CAP];
+      float x[KL];
 #pragma unroll
-      for (int i = 0; i < CAP; ++i) x[i] = i < cnt[gq] ? lv[i][ti.lane] : -INFINITY;
+      for (int i = 0; i < KL; ++i) x[i] = (i < CAP && i < cnt[gq]) ? lv[i < CAP ? i : 0][ti.lane] : -INFINITY;
       // T = the keff-th largest candidate score of the query: every lane sorts
       // a copy of its scores, two pairwise merges give all 4 lanes the query's
       // top CAP.
-      float c[CAP];
+      float c[KL];
 #pragma unroll
-      for (int i = 0; i < CAP; ++i) c[i] = x[i];
-      sort_desc<CAP>(c);
-      const float T = kth_of_lanes<CAP>(c, kq, ti.lane);
+      for (int i = 0; i < KL; ++i) c[i] = x[i];
+      sort_desc<KL>(c);
+      const float T = kth_of_lanes<KL>(c, kq, ti.lane);
       // Selected: scores above T, and the lowest-block `need` of those equal
       // to T; when exactly `need` candidates equal T (the usual case) all are.
       uint32_t gtb = 0u, eqb = 0u;
@@ -1113,13 +1113,20 @@ void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, 
 
 // One 16-query group per wave, four waves per workgroup; the register budget
 // allows 4 waves per SIMD for bf16 d = 64 and k <= 16, else 3 (2 for k > 16,
-// whose candidate lists are twice as long).
+// whose candidate lists are twice as long).  bf16 at d = 128 and k > 16 (the
+// long causal workload) runs 3 workgroups per CU instead of 2: 24 candidate
+// slots per lane (lists still sorted 32 long; a lane with more candidates
+// takes the second walk, 3.5 % of its workgroups), three-term R tiles of 16
+// blocks and hi-only tiles of 32, 51 KB of LDS (selection 2.00 -> 1.82 ms).
 template <template <int, int, int> class TLT, int D>
 void launch_select_k(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
                      const HeadBudget& hb, int causal, const int4* seqtab, int32_t* fb, hipStream_t s) {
   constexpr int M1 = (D == 64 && std::is_same<typename TLT<D, 1, 256>::QT, bf16_bits>::value) ? 4 : 3;
   if (topk <= 8) launch_select<TLT<D, 1, 256>, 8, 1, 8, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, fb, s);
   else if (topk <= 16) launch_select<TLT<D, 1, 256>, 16, 1, 16, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, fb, s);
+  else if constexpr (D == 128 && std::is_same<typename TLT<D, 1, 256>::QT, bf16_bits>::value)
+    launch_select<Bf16PlaneTiles<D, 1, 256, 16, kTerms>, 32, 2, 24, 3, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal,
+                                                                            seqtab, fb, s);
   else launch_select<TLT<D, 1, 256>, 32, 2, 32, 2, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, fb, s);
 }
 

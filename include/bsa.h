@@ -499,7 +499,8 @@ bsa_status bsa_profile_read(bsa_handle h, double* ms, int64_t* launches,
 
 /* The fused selection (bsa_forward and the entry points built on it, with
  * BSA_SELECT_FUSED and k <= 32) keeps each query's candidates in a fixed
- * number of slots per lane (8 for k <= 8, 16 for k <= 16, 32 for k <= 32).
+ * number of slots per lane (8 for k <= 8, 16 for k <= 16, 32 for k <= 32,
+ * except 24 for bf16 inputs at d = 128).
  * A 64-query workgroup in which some lane has more candidates walks the
  * scores a second time with a higher bound; if a lane overflows again, it
  * redoes the walk with exact per-lane top-k lists.  Every path gives the same

@@ -727,12 +727,12 @@ def test_selection_exact_ties(bsa, select, causal):
     np.testing.assert_array_equal(idx.cpu().numpy().reshape(-1, topk), ref)
 
 
-def fallback_workgroups(nb, topk, causal):
+def fallback_workgroups(nb, topk, causal, cap):
     """Workgroups of one head whose fused selection must take the exact
     fallback when every score of a query is equal: a lane of a 64-query
     workgroup holds, of each 16-block tile, the blocks 4 g .. 4 g + 3, and its
-    candidates (every block, up to its own when causal) overflow its slots."""
-    cap = 8 if topk <= 8 else 16 if topk <= 16 else 32
+    candidates (every block, up to its own when causal) overflow its `cap`
+    slots."""
     count = 0
     for qb in range(nb):
         cand = np.arange(qb + 1 if causal else nb)
@@ -741,9 +741,14 @@ def fallback_workgroups(nb, topk, causal):
     return count
 
 
-@pytest.mark.parametrize("dtype,d,topk,causal,n", [("bf16", 64, 16, False, 8192), ("bf16", 64, 16, True, 8192),
-                                                   ("bf16", 128, 32, True, 16384), ("fp32", 64, 8, False, 4096)])
-def test_selection_fallback_runs(bsa, dtype, d, topk, causal, n):
+# (slots per lane: 8 for k <= 8, 16 for k <= 16, 32 for k <= 32 except 24 for
+# bf16 at d = 128)
+@pytest.mark.parametrize("dtype,d,topk,causal,n,cap", [("bf16", 64, 16, False, 8192, 16),
+                                                       ("bf16", 64, 16, True, 8192, 16),
+                                                       ("bf16", 128, 32, True, 16384, 24),
+                                                       ("bf16", 64, 32, False, 16384, 32),
+                                                       ("fp32", 64, 8, False, 4096, 8)])
+def test_selection_fallback_runs(bsa, dtype, d, topk, causal, n, cap):
     """Every key row is the same vector, so all block representatives are
     equal and so are all of a query's scores: every one is a candidate, lanes
     hold more candidates than slots (also on the second walk, whose bound is
@@ -763,7 +768,7 @@ def test_selection_fallback_runs(bsa, dtype, d, topk, causal, n):
     else:
         inp = W.Inputs(q, k, v)
     nb = n // 64
-    expected = fallback_workgroups(nb, topk, causal)
+    expected = fallback_workgroups(nb, topk, causal, cap)
     say(f"[gpu] selection fallback {dtype} d={d} k={topk} causal={causal} n={n}: {expected} workgroups expected")
     assert expected > 0
     dq, dk, dv = to_dev(inp, dtype)
