@@ -54,7 +54,10 @@ struct bsa_handle_s {
   Buf s_part, s_lse;  // static mode: partial rows of split query tiles and their log-sum-exp
   int64_t static_item_tiles = 0;  // 0: chosen per call; else the most key tiles per work item
   int union_rows = 64;            // query-tile rows of the query-tile union fine stage
-  int32_t* fallbacks = nullptr;   // device counters [2]: fused-selection second walks, exact fallbacks
+  int32_t* fallbacks = nullptr;   // device counters [4]: fused-selection second walks, exact fallbacks,
+                                  // and the repair list's counters (one per call parity)
+  int repair_parity = 0;          // parity of the next call of the selection's split instance
+  Buf sel_repair;                 // the split instance's repair list, one int per select workgroup
   // timing
   bool profiling = false;
   struct Rec {
@@ -273,8 +276,8 @@ BSA_API bsa_status bsa_create(int device, bsa_handle* out) {
   h->noalloc = arena;
   {
     DeviceGuard dg(device);
-    if (hipMalloc(reinterpret_cast<void**>(&h->fallbacks), 2 * sizeof(int32_t)) != hipSuccess ||
-        hipMemset(h->fallbacks, 0, 2 * sizeof(int32_t)) != hipSuccess) {
+    if (hipMalloc(reinterpret_cast<void**>(&h->fallbacks), 4 * sizeof(int32_t)) != hipSuccess ||
+        hipMemset(h->fallbacks, 0, 4 * sizeof(int32_t)) != hipSuccess) {
       (void)hipGetLastError();
       if (h->fallbacks) (void)hipFree(h->fallbacks);
       delete h;
@@ -302,7 +305,7 @@ BSA_API bsa_status bsa_destroy(bsa_handle h) {
   if (h->idx) (void)hipFree(h->idx);
   for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_rec, &h->g_wgv, &h->g_list, &h->g_po,
                  &h->b_ld, &h->b_dq, &h->b_dkv, &h->b_dob, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
-                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv, &h->s_part, &h->s_lse, &h->tab})
+                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv, &h->s_part, &h->s_lse, &h->tab, &h->sel_repair})
     if (b->p) (void)hipFree(b->p);
   delete h;
   return BSA_OK;
@@ -349,7 +352,7 @@ BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
   *bytes = h->repr_bytes + h->split_bytes + h->panel_bytes + h->idx_bytes;
   for (auto* b : {&h->g_count, &h->g_offsets, &h->g_items, &h->g_item_rec, &h->g_rank, &h->g_rec, &h->g_wgv, &h->g_list, &h->g_po,
                  &h->b_ld, &h->b_dq, &h->b_dkv, &h->b_dob, &h->r_q, &h->r_k, &h->r_v, &h->r_o, &h->r_do, &h->r_lse,
-                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv, &h->s_part, &h->s_lse, &h->tab})
+                 &h->r_idx, &h->r_dq, &h->r_dk, &h->r_dv, &h->s_part, &h->s_lse, &h->tab, &h->sel_repair})
     *bytes += b->bytes;
   return BSA_OK;
 }
@@ -521,11 +524,26 @@ bsa_status run_select(bsa_handle h, const void* q, const float* repr, const uint
                       const int4* tab = nullptr) {
   const int64_t nb = s.n / 64;
   const int64_t total = s.bh() * s.n;
-  if (fused_select(h, topk))
-    return timed_launch(h, BSA_STAGE_COARSE_TOPK, st, "coarse_select", [&] {
+  if (fused_select(h, topk)) {
+    int32_t* repair_list = nullptr;
+    const bool repair = bsa::select_uses_repair(s.d, dt, topk);
+    if (repair) {
+      const size_t bytes = size_t(total / 64) * sizeof(int32_t);
+      if (arena) {
+        TRY(take(h, arena, reinterpret_cast<void**>(&repair_list), bytes, "selection repair list"));
+      } else {
+        TRY(grow(h, &h->sel_repair.p, &h->sel_repair.bytes, bytes, "selection repair list"));
+        repair_list = static_cast<int32_t*>(h->sel_repair.p);
+      }
+    }
+    const int parity = h->repair_parity;
+    TRY(timed_launch(h, BSA_STAGE_COARSE_TOPK, st, "coarse_select", [&] {
       return bsa::launch_coarse_select(q, repr, split, idx, total, s.n, s.d, dt, topk, hb, causal, st, tab,
-                                       h->fallbacks);
-    });
+                                       h->fallbacks, h->fallbacks + 2, repair_list, parity);
+    }));
+    if (repair) h->repair_parity ^= 1;  // the next such call lists at the counter this one cleared
+    return BSA_OK;
+  }
   int64_t chunk = h->panel_chunk_bytes / (nb * 4) / 64 * 64;
   if (arena) {
     const int64_t fit = int64_t(arena->avail() / size_t(nb * 4)) / 64 * 64;

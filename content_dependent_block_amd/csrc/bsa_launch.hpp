@@ -54,11 +54,21 @@ struct HeadBudget {
 // float32 repr.  Candidates: the blocks of the query's sequence; indices
 // relative to its first block.  fallbacks (may be null): two device counters;
 // a workgroup adds 1 to [0] when it walks the candidates a second time and to
-// [1] when it takes the exact fallback.
+// [1] when it takes the exact fallback.  When select_uses_repair(d, dtype,
+// topk), the exact fallback runs in a second kernel launched after the first
+// and needs repair_counters (two device ints, zero when the handle was made,
+// owned by the caller, the same for every call of a handle), repair_list
+// (rows / 64 ints of workspace) and the call's parity (0/1, flipped by the
+// caller for every such call; calls must not overlap).
+inline bool select_uses_repair(int d, bsa_dtype dtype, int topk) {
+  return d == 128 && dtype == BSA_BF16 && topk > 16;
+}
 hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t* repr_split,
                                 int32_t* idx, int64_t rows, int n, int d, bsa_dtype dtype,
                                 int topk, const HeadBudget& budget, int causal, hipStream_t stream,
-                                const int4* seqtab = nullptr, int32_t* fallbacks = nullptr);
+                                const int4* seqtab = nullptr, int32_t* fallbacks = nullptr,
+                                int32_t* repair_counters = nullptr, int32_t* repair_list = nullptr,
+                                int repair_parity = 0);
 constexpr int kFusedSelectMaxK = 32;
 
 // topk_select over panel rows [row0, row0 + rows): idx[(row0 + r) * topk + t].

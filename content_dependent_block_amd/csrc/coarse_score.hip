@@ -718,7 +718,8 @@ struct SelInfo {
   int nb, nbt, bt0, lo;
   int nvalid[QG], forced[QG];
   int tid, lane, wave, g, c16;
-  __device__ __forceinline__ SelInfo(int n, int causal, int TB, int NW, const int4* __restrict__ seqtab) {
+  __device__ __forceinline__ SelInfo(int n, int causal, int TB, int NW, const int4* __restrict__ seqtab,
+                                      int64_t tile) {
     const int rows = 16 * QG * NW;
     nb = n / kTile;
     tid = threadIdx.x;
@@ -726,7 +727,7 @@ struct SelInfo {
     wave = tid >> 6;
     g = lane >> 4;
     c16 = lane & 15;
-    tile_row = xcd_tile(causal) * rows;
+    tile_row = tile * rows;
     bh = tile_row / n;
     const int i0 = static_cast<int>(tile_row % n);
     qrow0 = tile_row + 16 * QG * wave + c16;
@@ -823,6 +824,39 @@ __device__ __forceinline__ void walk(TL& sc, unsigned char* rs, const typename T
   }
 }
 
+// Exact selection of a workgroup's queries: every score offered to exact
+// register top-KL lists (topk_list.hpp), merged over the query's 4 lanes and
+// written in ascending block order.  The slow path behind the candidate
+// slots, taken only when they overflow twice.
+template <typename TL, int KL, int QG, int NTH>
+__device__ __forceinline__ void exact_select(TL& sc, unsigned char* rs, const typename TL::Src* rbase,
+                                             const SelInfo<QG>& ti, const int (&keff)[QG], int topk,
+                                             int32_t* __restrict__ idx) {
+#pragma unroll
+  for (int gq = 0; gq < QG; ++gq) {
+    TopList<KL> l;
+    l.init();
+    walk<1, kTerms, QG, NTH>(sc, rs, rbase, ti,
+         [&](int, int, int b0, const f32x4 (&acc)[QG]) {
+           f32x4 v = acc[0];
+#pragma unroll
+           for (int e = 1; e < QG; ++e) v = gq == e ? acc[e] : v;
+#pragma unroll
+           for (int j = 0; j < 4; ++j) l.offer(v[j], b0 + 4 * ti.g + j);
+         },
+         [&](int, int, int b0, const f32x4 (&acc)[QG]) {
+           f32x4 v = acc[0];
+#pragma unroll
+           for (int e = 1; e < QG; ++e) v = gq == e ? acc[e] : v;
+#pragma unroll
+           for (int j = 0; j < 4; ++j) l.offer(ti.cand(gq, v[j], b0 + 4 * ti.g + j), b0 + 4 * ti.g + j);
+         });
+    merge_top<16, KL>(l.v, l.b, ti.lane);
+    merge_top<32, KL>(l.v, l.b, ti.lane);
+    emit_selection<KL>(l.b, ti.g, keff[gq], topk, idx + (ti.qrow0 + 16 * gq) * topk, ti.lo);
+  }
+}
+
 // MINW: waves per SIMD the register budget is sized for.  NW waves per
 // workgroup, QG query groups of 16 per wave.
 // The tile type of the hi-only first pass: bf16 planes take R tiles of twice
@@ -838,15 +872,22 @@ struct Pass1Tiles<Bf16PlaneTiles<D, QG, NTH, TB_, NTS>> {
   using type = Bf16PlaneTiles<D, QG, NTH, 2 * TB_, 1>;
 };
 
-template <typename TL, int KL, int GM, int CAP, int MINW, int QG, int NW>
+template <typename TL, int KL, int GM, int CAP, int MINW, int QG, int NW, bool SPLIT>
 __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const typename TL::QT* __restrict__ q,
                                                                       const typename TL::Src* __restrict__ rsrc,
                                                                       int32_t* __restrict__ idx, int n,
                                                                       int topk, const HeadBudget budget,
                                                                       int causal,
                                                                       const int4* __restrict__ seqtab,
-                                                                      int32_t* __restrict__ fallbacks) {
+                                                                      int32_t* __restrict__ fallbacks,
+                                                                      int32_t* __restrict__ repair_count,
+                                                                      int32_t* __restrict__ repair_clear,
+                                                                      int32_t* __restrict__ repair_list) {
   using TL1 = typename Pass1Tiles<TL>::type;
+  // split instance: this call lists its exact redos at repair_count, and
+  // clears the other counter for the next call (no kernel of this call uses
+  // it)
+  if (SPLIT && blockIdx.x == 0 && threadIdx.x == 0) *repair_clear = 0;
   constexpr int NTH = 64 * NW;
   constexpr int MT = TL1::TB / 16;    // MFMA tiles per R tile of pass 1
   constexpr int NS = 16 * GM;         // group slots per lane
@@ -867,8 +908,9 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
   __shared__ float cv[NW][QG][CAP][64];
   __shared__ uint16_t cb[NW][QG][CAP][64];
   static_assert(ROWS == kTile, "a workgroup's rows are one query block, so one sequence");
-  const SelInfo<QG> ti(n, causal, TL::TB, NW, seqtab);
-  const SelInfo<QG> ti1(n, causal, TL1::TB, NW, seqtab);  // the same rows, walked in pass-1 tiles
+  const int64_t tile = xcd_tile(causal);
+  const SelInfo<QG> ti(n, causal, TL::TB, NW, seqtab, tile);
+  const SelInfo<QG> ti1(n, causal, TL1::TB, NW, seqtab, tile);  // the same rows, walked in pass-1 tiles
   const auto* rbase = TL::head_base(rsrc, ti.bh, ti.nb);
   const int kh = budget.k[ti.bh % budget.heads];  // this head's budget (<= topk <= KL)
   int keff[QG];
@@ -1063,33 +1105,53 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
       }
     }
   } else {
-    // slots overflowed somewhere in the workgroup: offer every score to
-    // exact register lists and merge them pairwise, one query group at a time
-    // (counted, one vector atomic per such workgroup, when asked)
-    if (fallbacks && threadIdx.x == 0) atomicAdd(fallbacks + 1, 1);
-#pragma unroll
-    for (int gq = 0; gq < QG; ++gq) {
-      TopList<KL> l;
-      l.init();
-      walk<1, kTerms, QG, NTH>(sc, rs, rbase, ti,
-           [&](int, int, int b0, const f32x4 (&acc)[QG]) {
-             f32x4 v = acc[0];
-#pragma unroll
-             for (int e = 1; e < QG; ++e) v = gq == e ? acc[e] : v;
-#pragma unroll
-             for (int j = 0; j < 4; ++j) l.offer(v[j], b0 + 4 * ti.g + j);
-           },
-           [&](int, int, int b0, const f32x4 (&acc)[QG]) {
-             f32x4 v = acc[0];
-#pragma unroll
-             for (int e = 1; e < QG; ++e) v = gq == e ? acc[e] : v;
-#pragma unroll
-             for (int j = 0; j < 4; ++j) l.offer(ti.cand(gq, v[j], b0 + 4 * ti.g + j), b0 + 4 * ti.g + j);
-           });
-      merge_top<16, KL>(l.v, l.b, ti.lane);
-      merge_top<32, KL>(l.v, l.b, ti.lane);
-      emit_selection<KL>(l.b, ti.g, keff[gq], topk, idx + (ti.qrow0 + 16 * gq) * topk, ti.lo);
+    // slots overflowed again somewhere in the workgroup: the exact walk,
+    // here or, for the split instance, in the repair kernel (counted when
+    // asked, one vector atomic per such workgroup)
+    if constexpr (SPLIT) {
+      if (threadIdx.x == 0) {
+        const int32_t i = atomicAdd(repair_count, 1);
+        if (i < static_cast<int32_t>(gridDim.x)) repair_list[i] = static_cast<int32_t>(tile);
+      }
+    } else {
+      if (fallbacks && threadIdx.x == 0) atomicAdd(fallbacks + 1, 1);
+      exact_select<TL, KL, QG, NTH>(sc, rs, rbase, ti, keff, topk, idx);
     }
+  }
+}
+
+// The exact redo of a workgroup's selection for a tile listed by the split
+// instance of the select kernel (bf16, d = 128, k > 16): without the
+// register lists of the exact walk the select kernel fits in 152 VGPRs, so 3
+// workgroups per CU run it without spilling.  count[0] tiles are listed
+// (any tile number outside this call's tiles is skipped); a grid-stride loop
+// over them, every workgroup leaving when the list is done.
+template <typename TL, int KL, int QG, int NW>
+__global__ __launch_bounds__(64 * NW) void coarse_repair_kernel(const typename TL::QT* __restrict__ q,
+                                                                const typename TL::Src* __restrict__ rsrc,
+                                                                int32_t* __restrict__ idx, int n, int topk,
+                                                                const HeadBudget budget, int causal,
+                                                                const int4* __restrict__ seqtab,
+                                                                const int32_t* __restrict__ repair_count,
+                                                                const int32_t* __restrict__ repair_list,
+                                                                int32_t ntiles, int32_t* __restrict__ fallbacks) {
+  constexpr int NTH = 64 * NW;
+  __shared__ __attribute__((aligned(16))) unsigned char rs[TL::LDS_BYTES];
+  const int32_t listed = *repair_count;
+  const int32_t total = listed < ntiles ? listed : ntiles;
+  for (int32_t i = blockIdx.x; i < total; i += gridDim.x) {
+    const int32_t tile = repair_list[i];
+    if (tile < 0 || tile >= ntiles) continue;  // workgroup-uniform
+    const SelInfo<QG> ti(n, causal, TL::TB, NW, seqtab, tile);
+    const auto* rbase = TL::head_base(rsrc, ti.bh, ti.nb);
+    const int kh = budget.k[ti.bh % budget.heads];
+    int keff[QG];
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq) keff[gq] = kh < ti.nvalid[gq] - ti.lo ? kh : ti.nvalid[gq] - ti.lo;
+    TL sc;
+    sc.load_q(q, ti.qrow0, ti.g);
+    if (fallbacks && threadIdx.x == 0) atomicAdd(fallbacks + 1, 1);
+    exact_select<TL, KL, QG, NTH>(sc, rs, rbase, ti, keff, topk, idx);
   }
 }
 
@@ -1102,13 +1164,32 @@ void launch_panel(const void* q, const void* rsrc, float* panel, int64_t row0, i
                      panel, row0, rows, n, causal);
 }
 
-template <typename TL, int KL, int GM, int CAP, int MINW, int QG, int NW>
+// Repair state of the split instance: two counters (one per call parity) and
+// a list of one entry per select workgroup.
+struct Repair {
+  int32_t* counters = nullptr;
+  int32_t* list = nullptr;
+  int parity = 0;
+};
+
+template <typename TL, int KL, int GM, int CAP, int MINW, int QG, int NW, bool SPLIT = false>
 void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
-                   const HeadBudget& hb, int causal, const int4* seqtab, int32_t* fallbacks, hipStream_t s) {
+                   const HeadBudget& hb, int causal, const int4* seqtab, int32_t* fallbacks, const Repair& rp,
+                   hipStream_t s) {
   constexpr int ROWS = 16 * QG * NW;
-  hipLaunchKernelGGL((coarse_select_kernel<TL, KL, GM, CAP, MINW, QG, NW>), dim3(static_cast<unsigned>(rows / ROWS)),
+  const int64_t tiles = rows / ROWS;
+  int32_t* count = SPLIT ? rp.counters + rp.parity : nullptr;
+  int32_t* clear = SPLIT ? rp.counters + (1 - rp.parity) : nullptr;
+  hipLaunchKernelGGL((coarse_select_kernel<TL, KL, GM, CAP, MINW, QG, NW, SPLIT>), dim3(static_cast<unsigned>(tiles)),
                      dim3(64 * NW), 0, s, static_cast<const typename TL::QT*>(q),
-                     static_cast<const typename TL::Src*>(rsrc), idx, n, topk, hb, causal, seqtab, fallbacks);
+                     static_cast<const typename TL::Src*>(rsrc), idx, n, topk, hb, causal, seqtab, fallbacks, count,
+                     clear, SPLIT ? rp.list : nullptr);
+  if constexpr (SPLIT) {
+    const int64_t grid = tiles < 1024 ? tiles : 1024;
+    hipLaunchKernelGGL((coarse_repair_kernel<TL, KL, QG, NW>), dim3(static_cast<unsigned>(grid)), dim3(64 * NW), 0, s,
+                       static_cast<const typename TL::QT*>(q), static_cast<const typename TL::Src*>(rsrc), idx, n,
+                       topk, hb, causal, seqtab, count, rp.list, static_cast<int32_t>(tiles), fallbacks);
+  }
 }
 
 // One 16-query group per wave, four waves per workgroup; the register budget
@@ -1120,14 +1201,15 @@ void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, 
 // blocks and hi-only tiles of 32, 51 KB of LDS (selection 2.00 -> 1.82 ms).
 template <template <int, int, int> class TLT, int D>
 void launch_select_k(const void* q, const void* rsrc, int32_t* idx, int64_t rows, int n, int topk,
-                     const HeadBudget& hb, int causal, const int4* seqtab, int32_t* fb, hipStream_t s) {
+                     const HeadBudget& hb, int causal, const int4* seqtab, int32_t* fb, const Repair& rp,
+                     hipStream_t s) {
   constexpr int M1 = (D == 64 && std::is_same<typename TLT<D, 1, 256>::QT, bf16_bits>::value) ? 4 : 3;
-  if (topk <= 8) launch_select<TLT<D, 1, 256>, 8, 1, 8, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, fb, s);
-  else if (topk <= 16) launch_select<TLT<D, 1, 256>, 16, 1, 16, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, fb, s);
+  if (topk <= 8) launch_select<TLT<D, 1, 256>, 8, 1, 8, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, fb, rp, s);
+  else if (topk <= 16) launch_select<TLT<D, 1, 256>, 16, 1, 16, M1, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, fb, rp, s);
   else if constexpr (D == 128 && std::is_same<typename TLT<D, 1, 256>::QT, bf16_bits>::value)
-    launch_select<Bf16PlaneTiles<D, 1, 256, 16, kTerms>, 32, 2, 24, 3, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal,
-                                                                            seqtab, fb, s);
-  else launch_select<TLT<D, 1, 256>, 32, 2, 32, 2, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, fb, s);
+    launch_select<Bf16PlaneTiles<D, 1, 256, 16, kTerms>, 32, 2, 24, 3, 1, 4, true>(q, rsrc, idx, rows, n, topk, hb,
+                                                                                  causal, seqtab, fb, rp, s);
+  else launch_select<TLT<D, 1, 256>, 32, 2, 32, 2, 1, 4>(q, rsrc, idx, rows, n, topk, hb, causal, seqtab, fb, rp, s);
 }
 
 template <int D, int QG, int NTH>
@@ -1153,13 +1235,19 @@ hipError_t launch_coarse_score(const void* q, const float* repr, float* panel, i
 hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t* repr_split,
                                 int32_t* idx, int64_t rows, int n, int d, bsa_dtype dtype,
                                 int topk, const HeadBudget& hb, int causal, hipStream_t stream,
-                                const int4* seqtab, int32_t* fallbacks) {
+                                const int4* seqtab, int32_t* fallbacks, int32_t* repair_counters,
+                                int32_t* repair_list, int repair_parity) {
+  Repair rp;
+  rp.counters = repair_counters;
+  rp.list = repair_list;
+  rp.parity = repair_parity;
+  if (select_uses_repair(d, dtype, topk) && (!repair_counters || !repair_list)) return hipErrorInvalidValue;
   if (dtype == BSA_BF16) {
-    if (d == 64) launch_select_k<PlaneT, 64>(q, repr_split, idx, rows, n, topk, hb, causal, seqtab, fallbacks, stream);
-    else launch_select_k<PlaneT, 128>(q, repr_split, idx, rows, n, topk, hb, causal, seqtab, fallbacks, stream);
+    if (d == 64) launch_select_k<PlaneT, 64>(q, repr_split, idx, rows, n, topk, hb, causal, seqtab, fallbacks, rp, stream);
+    else launch_select_k<PlaneT, 128>(q, repr_split, idx, rows, n, topk, hb, causal, seqtab, fallbacks, rp, stream);
   } else {
-    if (d == 64) launch_select_k<F32T, 64>(q, repr, idx, rows, n, topk, hb, causal, seqtab, fallbacks, stream);
-    else launch_select_k<F32T, 128>(q, repr, idx, rows, n, topk, hb, causal, seqtab, fallbacks, stream);
+    if (d == 64) launch_select_k<F32T, 64>(q, repr, idx, rows, n, topk, hb, causal, seqtab, fallbacks, rp, stream);
+    else launch_select_k<F32T, 128>(q, repr, idx, rows, n, topk, hb, causal, seqtab, fallbacks, rp, stream);
   }
   return hipGetLastError();
 }
