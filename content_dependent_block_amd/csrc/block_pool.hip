@@ -17,7 +17,8 @@
 // hi + mid + lo (hi = bf16(r), mid = bf16(r - hi), lo = bf16(r - hi - mid)),
 // laid out as one plane per term and head, split[bh][term][beta][d], the form
 // the fused scoring kernel feeds to the bf16 MFMA (coarse_score.hip explains
-// the split).
+// the split), and the 2-norm of each block's hi term (rounded up), with which
+// that kernel bounds the error of its hi-only first pass per block.
 #include "bsa_device.hpp"
 #include "bsa_launch.hpp"
 
@@ -28,6 +29,7 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k,
                                                          float* __restrict__ repr,
                                                          bf16_bits* __restrict__ split,
+                                                         float* __restrict__ hinorm,
                                                          int64_t total_blocks, int nb,
                                                          const int4* __restrict__ seqtab) {
   constexpr int E = 16 / sizeof(T);     // elements per 16-byte chunk
@@ -86,12 +88,17 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k
       // E consecutive d per lane; the planes of one head are nb * D apart.
       const int64_t bhi = blk / nb;
       bf16_bits* dst = split + (blk + 2 * bhi * nb) * D + c * E;
+      float ss = 0.f;  // sum of squares of this lane's hi elements
 #pragma unroll
       for (int t = 0; t < 3; ++t) {
         uint32_t w[E / 2];
 #pragma unroll
         for (int e = 0; e < E; e += 2) {
           const __bf16 h0 = f32_to_bf16(acc[e]), h1 = f32_to_bf16(acc[e + 1]);
+          if (t == 0) {
+            ss = __builtin_fmaf(static_cast<float>(h0), static_cast<float>(h0), ss);
+            ss = __builtin_fmaf(static_cast<float>(h1), static_cast<float>(h1), ss);
+          }
           acc[e] -= static_cast<float>(h0);
           acc[e + 1] -= static_cast<float>(h1);
           w[e / 2] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, h0)) |
@@ -103,6 +110,11 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k
           *reinterpret_cast<uint2*>(dst + static_cast<int64_t>(t) * nb * D) = make_uint2(w[0], w[1]);
         }
       }
+      // the row's LPR lanes (all with ro == 0) add their parts; rounded up by
+      // 2^-16, more than the relative error of the fp32 sum and square root
+#pragma unroll
+      for (int s = 1; s < LPR; s <<= 1) ss += __shfl_xor(ss, s);
+      if (c == 0) hinorm[blk] = __builtin_sqrtf(ss) * (1.0f + 0x1.0p-16f);
     }
   }
 }
@@ -111,8 +123,9 @@ template <typename T, int D>
 hipError_t launch(const void* k, float* repr, bf16_bits* split, int64_t blocks, int nb,
                   const int4* seqtab, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((blocks + 3) / 4));
+  float* hinorm = split ? split_norms(split, blocks / nb, nb, D) : nullptr;
   hipLaunchKernelGGL((block_pool_kernel<T, D>), grid, dim3(256), 0, s,
-                     static_cast<const T*>(k), repr, split, blocks, nb, seqtab);
+                     static_cast<const T*>(k), repr, split, hinorm, blocks, nb, seqtab);
   return hipGetLastError();
 }
 

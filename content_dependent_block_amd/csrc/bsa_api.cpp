@@ -899,8 +899,8 @@ bsa_status forward_impl(bsa_handle h, const char* fn, const void* q, const void*
   // The fused bf16 selection reads the split representatives only.
   const bool want_split = fused_select(h, topk) && dtype == BSA_BF16;
   if (want_split)
-    TRY(grow(h, reinterpret_cast<void**>(&h->split), &h->split_bytes,
-             size_t(sp.bh() * nb * sp.d) * 3 * 2, "split repr workspace"));
+    TRY(grow(h, reinterpret_cast<void**>(&h->split), &h->split_bytes, bsa::split_buffer_bytes(sp.bh(), int(nb), sp.d),
+             "split repr workspace"));
   else
     TRY(grow(h, reinterpret_cast<void**>(&h->repr), &h->repr_bytes, size_t(sp.bh() * nb * sp.d) * 4,
              "repr workspace"));
@@ -979,7 +979,8 @@ BSA_API bsa_status bsa_forward_noalloc(bsa_handle h, const void* q, const void* 
   float* repr = nullptr;
   uint16_t* split = nullptr;
   if (want_split)
-    TRY(take(h, &arena, reinterpret_cast<void**>(&split), size_t(s.bh() * nb * s.d) * 3 * 2, "split representatives"));
+    TRY(take(h, &arena, reinterpret_cast<void**>(&split), bsa::split_buffer_bytes(s.bh(), int(nb), s.d),
+             "split representatives"));
   else
     TRY(take(h, &arena, reinterpret_cast<void**>(&repr), size_t(s.bh() * nb * s.d) * 4, "representatives"));
   // no events either: per-stage timing is off for this call

@@ -22,6 +22,16 @@ namespace bsa {
 hipError_t launch_block_pool(const void* k, float* repr, uint16_t* split, int64_t bh, int n, int d,
                              bsa_dtype dtype, hipStream_t stream, const int4* seqtab = nullptr);
 
+// The split buffer: the three bf16 planes [bh][3][n/64][d], then per block
+// the 2-norm of its hi term [bh][n/64] (fp32, rounded up), which the fused
+// selection's first pass uses to bound its error block by block.
+inline size_t split_buffer_bytes(int64_t bh, int nb, int d) {
+  return static_cast<size_t>(bh) * nb * d * 3 * 2 + static_cast<size_t>(bh) * nb * 4;
+}
+inline float* split_norms(uint16_t* split, int64_t bh, int nb, int d) {
+  return reinterpret_cast<float*>(split + static_cast<size_t>(bh) * nb * d * 3);
+}
+
 // Sequences whose lengths are not multiples of 64 run on copies padded to
 // whole blocks.  pad: dst [slices][n_pad] rows from src [slices][src_rows]
 // rows, row r of a slice taking caller row seqtab[r / 64].w + r % 64 when

@@ -30,10 +30,12 @@
 //     query's 4 lanes, over the gfx950 permlane swaps, give all 4 the top).
 //     The k_eff groups whose maxima are >= tau each hold a score >= tau, so at
 //     least k_eff scores are >= tau, and every score of the answer is >= tau.
-//     For bf16 inputs pass 1 multiplies only the hi term of the split; tau is
-//     then lowered by a bound E on |exact - hi-only| (relative 2^-8 per
-//     representative element, plus rounding; see pass1_error), which keeps
-//     it a bound for the exact scores at a third of the MFMA and LDS work.
+//     For bf16 inputs pass 1 multiplies only the hi term of the split, at a
+//     third of the MFMA and LDS work, and every score enters as a lower bound
+//     of its exact score: the hi-only score less (2^-8 + 2^-13) |q|_2 |hi|_2
+//     (hi is r rounded to 8 significant bits; Cauchy-Schwarz; the block's
+//     norm comes from block_pool), which keeps tau a bound for the exact
+//     scores.
 //   pass 2: the same scores again; those >= tau (typically k + a few) are
 //     appended to the lane's LDS slots in ascending block order.
 //   The lane reads its slots into registers and sorts a copy of their
@@ -189,24 +191,45 @@ struct Bf16PlaneTiles {
   using Src = bf16_bits;
   static constexpr int TB = TB_;                        // blocks per R tile
   static constexpr int PITCH = kRPitch<D>;
-  static constexpr int LDS_BYTES = NTS * TB * PITCH * 2;  // NTS: terms staged at most
+  // The hi-only tile type (NTS = 1) also stages its blocks' hi-term norms
+  // after the plane.
+  static constexpr bool kNorms = NTS == 1;
+  static constexpr int NORM_OFF = NTS * TB * PITCH * 2;
+  static constexpr int LDS_BYTES = NORM_OFF + (kNorms ? TB * 4 : 0);  // NTS: terms staged at most
   static constexpr int CPR = D / 8;             // 16-byte chunks per block row
   static constexpr int PER = TB * CPR / NTH;    // chunks per thread and term
   static_assert(PER >= 1 && (TB * CPR) % NTH == 0, "whole chunks per thread");
   static_assert(NTH % CPR == 0, "a thread keeps one column chunk");
-  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
   static constexpr int PFD = kSelectPrefetch;  // R tiles in flight ahead of the one computed (hi-only walk)
   bf16x8 qb[QG][D / 32];
   uint4 pf[kTerms][PER];
   uint4 pf1[PFD > 1 ? PFD - 1 : 1][PER];  // further hi-only tiles in flight
-  u16x2 amax[4];  // max |hi| bit patterns of this thread's 8 columns
+  float pfn[4];                           // the next tile's norms (threads tid < TB / 4)
+  const float* hn = nullptr;              // this head's hi-term norms [nb]
+  int nbk = 0;
+  // c |q|_2 for each of this lane's queries, c = 2^-8 + 2^-13: with |hi|_2
+  // of a block it bounds |exact score - hi-only score| (see norms4).
+  float qn[QG];
 
   // Query group gq of this lane: row qrow0 + 16 gq.
   __device__ __forceinline__ void load_q(const QT* __restrict__ q, int64_t qrow0, int g) {
 #pragma unroll
-    for (int gq = 0; gq < QG; ++gq) load_q_bf16<D>(qb[gq], q, qrow0 + 16 * gq, g);
+    for (int gq = 0; gq < QG; ++gq) {
+      load_q_bf16<D>(qb[gq], q, qrow0 + 16 * gq, g);
+      float ss = 0.f;  // this lane's D / 4 elements, then the query's 4 lanes
 #pragma unroll
-    for (int i = 0; i < 4; ++i) amax[i] = u16x2{0, 0};
+      for (int ks = 0; ks < D / 32; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = static_cast<float>(qb[gq][ks][e]);
+          ss = __builtin_fmaf(x, x, ss);
+        }
+      qn[gq] = __builtin_sqrtf(sum_over_groups(ss)) * ((1.0f + 0x1.0p-16f) * (0x1.0p-8f + 0x1.0p-13f));
+    }
+  }
+  __device__ __forceinline__ void set_norms(const float* __restrict__ all, int64_t bh, int nb) {
+    hn = all + bh * nb;
+    nbk = nb;
   }
   __device__ __forceinline__ static const Src* head_base(const Src* r, int64_t bh, int nb) {
     return r + bh * kTerms * nb * D;
@@ -216,6 +239,12 @@ struct Bf16PlaneTiles {
   // the oldest and moves the others up.
   template <int NT>
   __device__ __forceinline__ void fetch(const Src* __restrict__ rbase, int nb, int bt, int tid) {
+    if constexpr (NT == 1 && kNorms) {
+      if (tid < TB / 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pfn[i] = hn[min(bt * TB + 4 * tid + i, nbk - 1)];
+      }
+    }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int c = tid + NTH * u, r = c / CPR, col = (c % CPR) * 8;
@@ -246,16 +275,16 @@ struct Bf16PlaneTiles {
   template <int NT>
   __device__ __forceinline__ void put(unsigned char* lds, int tid) {
     __bf16* rs = reinterpret_cast<__bf16*>(lds);
+    if constexpr (NT == 1 && kNorms) {
+      if (tid < TB / 4)
+        *reinterpret_cast<f32x4*>(lds + NORM_OFF + 16 * tid) = f32x4{pfn[0], pfn[1], pfn[2], pfn[3]};
+    }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int c = tid + NTH * u, r = c / CPR, col = (c % CPR) * 8;
 #pragma unroll
       for (int t = 0; t < NT; ++t) *reinterpret_cast<uint4*>(rs + (t * TB + r) * PITCH + col) = pf[t][u];
       if constexpr (NT == 1) {
-        const uint32_t w[4] = {pf[0][u].x, pf[0][u].y, pf[0][u].z, pf[0][u].w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          amax[i] = __builtin_elementwise_max(amax[i], __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu));
         if constexpr (PFD > 1) {
           pf[0][u] = pf1[0][u];
 #pragma unroll
@@ -304,41 +333,14 @@ struct Bf16PlaneTiles {
       }
     }
   }
-  // E >= |exact score - hi-only score| for each of this lane's queries and
-  // every block of the head: (2^-8 + 2^-15) sum_d |q_d| R_d with R_d >=
-  // max_beta |r_beta,d| (hi is r rounded to 8 significant bits,
-  // |r - hi| <= 2^-8 |r|; 2^-15 covers the fp32 rounding of both sums).  The
-  // query's 4 lanes return the same E.  lds: at least NTH * 16 + D * 4 bytes,
-  // free; a barrier precedes reuse.
-  __device__ __forceinline__ void pass1_error(unsigned char* lds, int tid, int lane, int g, float (&err)[QG]) const {
-    uint32_t* part = reinterpret_cast<uint32_t*>(lds);              // [NTH][4]
-    float* rmax = reinterpret_cast<float*>(lds + NTH * 16);         // [D]
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) part[tid * 4 + i] = __builtin_bit_cast(uint32_t, amax[i]);
-    __syncthreads();
-    if (tid < D) {
-      const int cc = tid / 8, e = tid % 8;  // column chunk, element in it
-      uint32_t m = 0u;
-      for (int t = cc; t < NTH; t += CPR) {
-        const uint32_t w = part[t * 4 + e / 2];
-        m = max(m, (e & 1) ? (w >> 16) : (w & 0xffffu));
-      }
-      rmax[tid] = __uint_as_float(m << 16) * (1.0f + 0x1.0p-8f);
-    }
-    __syncthreads();
-#pragma unroll
-    for (int gq = 0; gq < QG; ++gq) {
-      float sum = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          sum += fabsf(static_cast<float>(qb[gq][ks][e])) * rmax[8 * g + 32 * ks + e];
-      sum += __uint_as_float(lane_xor<16>(__float_as_uint(sum), lane));
-      sum += __uint_as_float(lane_xor<32>(__float_as_uint(sum), lane));
-      err[gq] = sum * (0x1.0p-8f + 0x1.0p-15f);
-    }
+  // The staged hi-only tile's norms |hi_beta|_2 of this lane's 4 blocks of
+  // MFMA tile mt.  For a block, |exact score - hi-only score| <= sum_d |q_d|
+  // |r_d - hi_d| + the fp32 rounding of both sums <= (2^-8 + 2^-13) |q|_2
+  // |hi|_2 (hi is r rounded to 8 significant bits, |r - hi| <= 2^-8 |hi|;
+  // Cauchy-Schwarz; 2^-13 covers the roundings, and both norms are rounded
+  // up), so score_hi - qn * norm is a lower bound of the exact score.
+  __device__ __forceinline__ f32x4 norms4(const unsigned char* lds, int mt, int g) const {
+    return *reinterpret_cast<const f32x4*>(lds + NORM_OFF + 4 * (mt * 16 + 4 * g));
   }
 };
 
@@ -441,11 +443,10 @@ struct F32Tiles {
       }
     }
   }
-  // Pass 1 computes the same scores as pass 2 here.
-  __device__ __forceinline__ void pass1_error(unsigned char*, int, int, int, float (&err)[QG]) const {
-#pragma unroll
-    for (int gq = 0; gq < QG; ++gq) err[gq] = 0.f;
-  }
+  // Pass 1 computes the same scores as pass 2 here: no error to bound.
+  float qn[QG] = {};
+  __device__ __forceinline__ void set_norms(const float*, int64_t, int) {}
+  __device__ __forceinline__ f32x4 norms4(const unsigned char*, int, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 };
 
 // Where a workgroup's 64 query rows sit, and which blocks they may select;
@@ -879,6 +880,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
                                                                       int topk, const HeadBudget budget,
                                                                       int causal,
                                                                       const int4* __restrict__ seqtab,
+                                                                      const float* __restrict__ hinorm,
                                                                       int32_t* __restrict__ fallbacks,
                                                                       int32_t* __restrict__ repair_count,
                                                                       int32_t* __restrict__ repair_clear,
@@ -894,14 +896,12 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
   constexpr int NH = NS / (4 * MT) > 0 ? NS / (4 * MT) : 1;  // R tiles per cycle of slots
   static_assert(NS % (4 * MT) == 0, "a cycle of slots covers whole R tiles");
   constexpr int ROWS = 16 * QG * NW;  // queries per workgroup
-  // The R tile buffer also holds the scratch of the pass-1 error bound and,
-  // at the end, the selection lists (a row of 33 per query) and a slot per
-  // lane.
+  // The R tile buffer (the hi-only tiles with their norms, or the three-term
+  // tiles) also holds, at the end, the selection lists (a row of 33 per
+  // query) and a slot per lane.
   constexpr int LIST_BYTES = (ROWS * 33 + NTH) * 4;
-  constexpr int ERR_BYTES = NTH * 16 + 128 * 4;
   constexpr int RS_T = TL::LDS_BYTES > TL1::LDS_BYTES ? TL::LDS_BYTES : TL1::LDS_BYTES;
-  constexpr int RS0 = RS_T > LIST_BYTES ? RS_T : LIST_BYTES;
-  constexpr int RS_BYTES = RS0 > ERR_BYTES ? RS0 : ERR_BYTES;
+  constexpr int RS_BYTES = RS_T > LIST_BYTES ? RS_T : LIST_BYTES;
   static_assert(CAP <= KL && KL <= 32, "candidate slots are tracked in a 32-bit mask");
   __shared__ __attribute__((aligned(16))) unsigned char rs[RS_BYTES];
   // per lane and query group: candidate scores and blocks
@@ -924,32 +924,35 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
   for (int gq = 0; gq < QG; ++gq)
 #pragma unroll
     for (int u = 0; u < NS; ++u) a[gq][u] = -INFINITY;
-  auto group_max = [&](bool checked, int h, int mt, int b0, const f32x4 (&acc)[QG]) {
-#pragma unroll
-    for (int gq = 0; gq < QG; ++gq)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float x = checked ? ti.cand(gq, acc[gq][j], b0 + 4 * ti.g + j) : acc[gq][j];
-        a[gq][4 * (MT * h + mt) + j] = fmaxf(a[gq][4 * (MT * h + mt) + j], x);
-      }
-  };
-  float err[QG], tau[QG];
+  // Pass 1 may run on approximate scores (bf16: the hi term alone): each
+  // enters as a lower bound of its exact score, the hi-only score less the
+  // block's error bound (norms4), so tau stays a bound for the exact scores.
+  float tau[QG];
   {
     TL1 sc1;
+    sc1.set_norms(hinorm, ti.bh, ti.nb);
     sc1.load_q(q, ti.qrow0, ti.g);
+    auto group_max = [&](bool checked, int h, int mt, int b0, const f32x4 (&acc)[QG]) {
+      const f32x4 nrm = sc1.norms4(rs, mt, ti.g);
+#pragma unroll
+      for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float lb = __builtin_fmaf(-sc1.qn[gq], nrm[j], acc[gq][j]);
+          const float x = checked ? ti.cand(gq, lb, b0 + 4 * ti.g + j) : lb;
+          a[gq][4 * (MT * h + mt) + j] = fmaxf(a[gq][4 * (MT * h + mt) + j], x);
+        }
+    };
     walk<NH, 1, QG, NTH>(sc1, rs, rbase, ti1,
                          [&](int h, int mt, int b0, const f32x4 (&acc)[QG]) { group_max(false, h, mt, b0, acc); },
                          [&](int h, int mt, int b0, const f32x4 (&acc)[QG]) { group_max(true, h, mt, b0, acc); });
-    // pass 1 may run on approximate scores (bf16: the hi term alone); lowering
-    // the bound by their error keeps it a bound for the exact scores
-    sc1.pass1_error(rs, ti.tid, ti.lane, ti.g, err);
   }
   TL sc;
   sc.load_q(q, ti.qrow0, ti.g);
 #pragma unroll
   for (int gq = 0; gq < QG; ++gq) {
     sort_desc<NS>(a[gq]);
-    tau[gq] = kth_of_lanes<NS>(a[gq], keff[gq], ti.lane) - err[gq];
+    tau[gq] = kth_of_lanes<NS>(a[gq], keff[gq], ti.lane);
   }
 
   // pass 2: the candidates >= tau, in ascending block order
@@ -1170,6 +1173,7 @@ struct Repair {
   int32_t* counters = nullptr;
   int32_t* list = nullptr;
   int parity = 0;
+  const float* hinorm = nullptr;  // bf16: the blocks' hi-term norms (after the split planes)
 };
 
 template <typename TL, int KL, int GM, int CAP, int MINW, int QG, int NW, bool SPLIT = false>
@@ -1182,8 +1186,8 @@ void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, 
   int32_t* clear = SPLIT ? rp.counters + (1 - rp.parity) : nullptr;
   hipLaunchKernelGGL((coarse_select_kernel<TL, KL, GM, CAP, MINW, QG, NW, SPLIT>), dim3(static_cast<unsigned>(tiles)),
                      dim3(64 * NW), 0, s, static_cast<const typename TL::QT*>(q),
-                     static_cast<const typename TL::Src*>(rsrc), idx, n, topk, hb, causal, seqtab, fallbacks, count,
-                     clear, SPLIT ? rp.list : nullptr);
+                     static_cast<const typename TL::Src*>(rsrc), idx, n, topk, hb, causal, seqtab, rp.hinorm, fallbacks,
+                     count, clear, SPLIT ? rp.list : nullptr);
   if constexpr (SPLIT) {
     const int64_t grid = tiles < 1024 ? tiles : 1024;
     hipLaunchKernelGGL((coarse_repair_kernel<TL, KL, QG, NW>), dim3(static_cast<unsigned>(grid)), dim3(64 * NW), 0, s,
@@ -1241,6 +1245,7 @@ hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t
   rp.counters = repair_counters;
   rp.list = repair_list;
   rp.parity = repair_parity;
+  if (dtype == BSA_BF16) rp.hinorm = split_norms(const_cast<uint16_t*>(repr_split), rows / n, n / kTile, d);
   if (select_uses_repair(d, dtype, topk) && (!repair_counters || !repair_list)) return hipErrorInvalidValue;
   if (dtype == BSA_BF16) {
     if (d == 64) launch_select_k<PlaneT, 64>(q, repr_split, idx, rows, n, topk, hb, causal, seqtab, fallbacks, rp, stream);
