@@ -57,18 +57,20 @@ struct RowState {
 
 // One key tile for one wave.  `vis` gives the visibility of the lane's 16
 // keys (bit 4*t + jj for key 16*t + 4*(lane/16) + jj).
-template <typename T, int D>
+template <typename T, int D, bool SKIP>
 __device__ __forceinline__ void tile_step(RowState<D>& st, const T* ks, const T* vs,
                                           const void* qreg, uint32_t vis, float scale_log2,
                                           int lane) {
   using L = KvLayout<T, D>;
   const int g = lane >> 4, c16 = lane & 15;
-  // Keys 16 t .. 16 t + 15 that no row of the wave sees (a sparse static
-  // tile: often one visible key column) cost no MFMA work: their scores are
-  // masked below whatever they hold, and their probabilities are 0.
+  // SKIP (the static tile lists): keys 16 t .. 16 t + 15 that no row of the
+  // wave sees (a sparse static tile: often one visible key column) cost no
+  // MFMA work: their scores are masked below whatever they hold, and their
+  // probabilities are 0.  The query-tile union sees whole blocks or none,
+  // and its caller already skips blocks no row of the wave selected.
   bool sub[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) sub[t] = ballot(((vis >> (4 * t)) & 0xFu) != 0u) != 0ull;
+  for (int t = 0; t < 4; ++t) sub[t] = !SKIP || ballot(((vis >> (4 * t)) & 0xFu) != 0u) != 0ull;
   f32x4 s[4];
   if constexpr (L::kBf16) {
     const bf16x8* qb = static_cast<const bf16x8*>(qreg);
@@ -155,7 +157,7 @@ __device__ __forceinline__ void tile_step(RowState<D>& st, const T* ks, const T*
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         // one MFMA step covers keys 16 t + 4 g' + jj of the four lane groups
-        if (ballot(((vis >> (4 * t + jj)) & 1u) != 0u) == 0ull) continue;
+        if (SKIP && ballot(((vis >> (4 * t + jj)) & 1u) != 0u) == 0ull) continue;
         const T* vr = vs + (16 * t + 4 * g + jj) * L::VPITCH + c16;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt)
@@ -300,7 +302,7 @@ __global__ __launch_bounds__(64 * W) void sparse_flash_kernel(
           vis &= km;
         }
       }
-      if (any) tile_step<T, D>(st, ks, vs, &qreg, vis, scale_log2, lane);
+      if (any) tile_step<T, D, false>(st, ks, vs, &qreg, vis, scale_log2, lane);
     }
     cur = nxt;
   }
@@ -521,7 +523,7 @@ __global__ __launch_bounds__(256) void static_item_kernel(
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj)
         vis |= static_cast<uint32_t>((m64 >> (16 * t + 4 * g + jj)) & 1ull) << (4 * t + jj);
-    if (any) tile_step<T, D>(st, ks, vs, &qreg, vis, scale_log2, lane);
+    if (any) tile_step<T, D, true>(st, ks, vs, &qreg, vis, scale_log2, lane);
     cur = nxt;
   }
 
