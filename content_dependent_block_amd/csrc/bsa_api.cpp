@@ -361,10 +361,12 @@ BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
 
 namespace {
 
+// v (nullable): the V the fine stage will read, which the pooling kernel
+// may read ahead (launch_block_pool).
 bsa_status run_pool(bsa_handle h, const void* k, float* repr, uint16_t* split, const Shape& s,
-                    bsa_dtype dt, hipStream_t st, const int4* tab = nullptr) {
+                    bsa_dtype dt, hipStream_t st, const int4* tab = nullptr, const void* v = nullptr) {
   return timed_launch(h, BSA_STAGE_POOL, st, "block_pool", [&] {
-    return bsa::launch_block_pool(k, repr, split, s.bh(), s.n, s.d, dt, st, tab);
+    return bsa::launch_block_pool(k, repr, split, s.bh(), s.n, s.d, dt, st, tab, v);
   });
 }
 
@@ -911,7 +913,7 @@ bsa_status forward_impl(bsa_handle h, const char* fn, const void* q, const void*
              "index workspace"));
     idx = h->idx;
   }
-  TRY(run_pool(h, pk, repr, split, sp, dtype, st, tab));
+  TRY(run_pool(h, pk, repr, split, sp, dtype, st, tab, pv));
   TRY(run_select(h, pq, repr, split, idx, sp, dtype, topk, hb, causal, st, nullptr, tab));
   TRY(run_fine(h, pq, pk, pv, pout, plse, idx, sp, dtype, topk, scale, causal, st, tab));
   if (p.copy) {
@@ -986,7 +988,7 @@ BSA_API bsa_status bsa_forward_noalloc(bsa_handle h, const void* q, const void* 
   // no events either: per-stage timing is off for this call
   const bool profiling = h->profiling;
   h->profiling = false;
-  bsa_status r = run_pool(h, k, repr, split, s, dtype, st);
+  bsa_status r = run_pool(h, k, repr, split, s, dtype, st, nullptr, v);
   if (r == BSA_OK)
     r = run_select(h, q, repr, split, block_idx_out, s, dtype, topk, uniform_budget(topk), causal, st, &arena);
   if (r == BSA_OK)

@@ -17,10 +17,16 @@ namespace bsa {
 // padded to whole blocks (bsa_device.hpp); a block with fewer than 64 keys
 // is the mean of those.
 //
+// warm (nullable): V, laid out like K.  When it is small enough to stay in
+// the Infinity Cache until the fine stage reads it, the kernel also reads it
+// once, so that read comes while the selection leaves HBM idle instead of
+// in the attention kernel's first touch.
+//
 // Every `seqtab` below is that table: n / 64 entries in device memory, or
 // NULL for one sequence of n whole-block rows per head.
 hipError_t launch_block_pool(const void* k, float* repr, uint16_t* split, int64_t bh, int n, int d,
-                             bsa_dtype dtype, hipStream_t stream, const int4* seqtab = nullptr);
+                             bsa_dtype dtype, hipStream_t stream, const int4* seqtab = nullptr,
+                             const void* warm = nullptr);
 
 // The split buffer: the three bf16 planes [bh][3][n/64][d], then per block
 // the 2-norm of its hi term [bh][n/64] (fp32, rounded up), which the fused
