@@ -19,12 +19,6 @@
 // the fused scoring kernel feeds to the bf16 MFMA (coarse_score.hip explains
 // the split), and the 2-norm of each block's hi term (rounded up), with which
 // that kernel bounds the error of its hi-only first pass per block.
-//
-// It can also read V once (`warm`), with the same addressing as K, and
-// discard it.  The selection that follows is bound by its vector ALU work
-// and leaves HBM nearly idle; a V that fits the 256 MB Infinity Cache with
-// room to spare is then still there when the attention kernel reads it,
-// instead of coming from HBM on that kernel's first touch.
 #include "bsa_device.hpp"
 #include "bsa_launch.hpp"
 
@@ -37,8 +31,7 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k
                                                          bf16_bits* __restrict__ split,
                                                          float* __restrict__ hinorm,
                                                          int64_t total_blocks, int nb,
-                                                         const int4* __restrict__ seqtab,
-                                                         const T* __restrict__ warm) {
+                                                         const int4* __restrict__ seqtab) {
   constexpr int E = 16 / sizeof(T);     // elements per 16-byte chunk
   constexpr int LPR = D / E;            // lanes per key row
   constexpr int RPL = kWave / LPR;      // rows per wave-wide load
@@ -70,21 +63,11 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k
       acc[3] += __uint_as_float(u.w);
     }
   }
-  uint32_t seen = 0;  // the XOR of the V words read, so the reads are kept
-  if (warm) {
-    const T* wb = warm + (blk * kTile + ro) * D + c * E;
-#pragma unroll
-    for (int it = 0; it < ITERS; ++it) {
-      const uint4 u = ld16(wb + static_cast<int64_t>(it) * RPL * D);
-      seen ^= u.x ^ u.y ^ u.z ^ u.w;
-    }
-  }
 #pragma unroll
   for (int s = LPR; s < kWave; s <<= 1) {
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], s);
   }
-  asm volatile("" ::"v"(seen));  // an empty use: the V reads cannot be dropped
   if (ro == 0) {
     const int keys = block_keys(seqtab, static_cast<int>(blk % nb));
     if (keys < kTile) {  // a sequence's partial last block: mean of the keys that exist
@@ -136,35 +119,28 @@ __global__ __launch_bounds__(256) void block_pool_kernel(const T* __restrict__ k
   }
 }
 
-// V is read ahead only up to this size: Q and K (as large) and the
-// bucketing's pair lists also pass through the 256 MB cache before the
-// attention kernel runs, and would evict a larger V again first.
-constexpr int64_t kWarmMaxBytes = int64_t(64) << 20;
-
 template <typename T, int D>
 hipError_t launch(const void* k, float* repr, bf16_bits* split, int64_t blocks, int nb,
-                  const int4* seqtab, const void* warm, hipStream_t s) {
+                  const int4* seqtab, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>((blocks + 3) / 4));
   float* hinorm = split ? split_norms(split, blocks / nb, nb, D) : nullptr;
-  const bool ahead = warm && blocks * kTile * D * static_cast<int64_t>(sizeof(T)) <= kWarmMaxBytes;
   hipLaunchKernelGGL((block_pool_kernel<T, D>), grid, dim3(256), 0, s,
-                     static_cast<const T*>(k), repr, split, hinorm, blocks, nb, seqtab,
-                     ahead ? static_cast<const T*>(warm) : nullptr);
+                     static_cast<const T*>(k), repr, split, hinorm, blocks, nb, seqtab);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_block_pool(const void* k, float* repr, uint16_t* split, int64_t bh, int n, int d,
-                             bsa_dtype dtype, hipStream_t stream, const int4* seqtab, const void* warm) {
+                             bsa_dtype dtype, hipStream_t stream, const int4* seqtab) {
   const int nb = n / kTile;
   const int64_t blocks = bh * nb;
   if (dtype == BSA_BF16) {
-    return d == 64 ? launch<bf16_bits, 64>(k, repr, split, blocks, nb, seqtab, warm, stream)
-                   : launch<bf16_bits, 128>(k, repr, split, blocks, nb, seqtab, warm, stream);
+    return d == 64 ? launch<bf16_bits, 64>(k, repr, split, blocks, nb, seqtab, stream)
+                   : launch<bf16_bits, 128>(k, repr, split, blocks, nb, seqtab, stream);
   }
-  return d == 64 ? launch<float, 64>(k, repr, split, blocks, nb, seqtab, warm, stream)
-                 : launch<float, 128>(k, repr, split, blocks, nb, seqtab, warm, stream);
+  return d == 64 ? launch<float, 64>(k, repr, split, blocks, nb, seqtab, stream)
+                 : launch<float, 128>(k, repr, split, blocks, nb, seqtab, stream);
 }
 
 }  // namespace bsa

@@ -361,12 +361,10 @@ BSA_API bsa_status bsa_workspace_bytes(bsa_handle h, size_t* bytes) {
 
 namespace {
 
-// v (nullable): the V the fine stage will read, which the pooling kernel
-// may read ahead (launch_block_pool).
 bsa_status run_pool(bsa_handle h, const void* k, float* repr, uint16_t* split, const Shape& s,
-                    bsa_dtype dt, hipStream_t st, const int4* tab = nullptr, const void* v = nullptr) {
+                    bsa_dtype dt, hipStream_t st, const int4* tab = nullptr) {
   return timed_launch(h, BSA_STAGE_POOL, st, "block_pool", [&] {
-    return bsa::launch_block_pool(k, repr, split, s.bh(), s.n, s.d, dt, st, tab, v);
+    return bsa::launch_block_pool(k, repr, split, s.bh(), s.n, s.d, dt, st, tab);
   });
 }
 
@@ -519,11 +517,12 @@ bsa_status take(bsa_handle h, Arena* arena, void** out, size_t bytes, const char
 // Stage 1 selection over all rows: one fused coarse_score + topk_select
 // kernel (k <= 32, fused strategy), else coarse_score and topk_select through
 // a panel, in chunks of at most panel_chunk_bytes of panel (with an arena: of
-// what is left of it).
+// what is left of it).  v (nullable): the V the fine stage will read, which
+// the fused kernel may read ahead (launch_coarse_select).
 bsa_status run_select(bsa_handle h, const void* q, const float* repr, const uint16_t* split,
                       int32_t* idx, const Shape& s, bsa_dtype dt, int topk,
                       const bsa::HeadBudget& hb, int causal, hipStream_t st, Arena* arena = nullptr,
-                      const int4* tab = nullptr) {
+                      const int4* tab = nullptr, const void* v = nullptr) {
   const int64_t nb = s.n / 64;
   const int64_t total = s.bh() * s.n;
   if (fused_select(h, topk)) {
@@ -541,7 +540,7 @@ bsa_status run_select(bsa_handle h, const void* q, const float* repr, const uint
     const int parity = h->repair_parity;
     TRY(timed_launch(h, BSA_STAGE_COARSE_TOPK, st, "coarse_select", [&] {
       return bsa::launch_coarse_select(q, repr, split, idx, total, s.n, s.d, dt, topk, hb, causal, st, tab,
-                                       h->fallbacks, h->fallbacks + 2, repair_list, parity);
+                                       h->fallbacks, h->fallbacks + 2, repair_list, parity, v);
     }));
     if (repair) h->repair_parity ^= 1;  // the next such call lists at the counter this one cleared
     return BSA_OK;
@@ -913,8 +912,8 @@ bsa_status forward_impl(bsa_handle h, const char* fn, const void* q, const void*
              "index workspace"));
     idx = h->idx;
   }
-  TRY(run_pool(h, pk, repr, split, sp, dtype, st, tab, pv));
-  TRY(run_select(h, pq, repr, split, idx, sp, dtype, topk, hb, causal, st, nullptr, tab));
+  TRY(run_pool(h, pk, repr, split, sp, dtype, st, tab));
+  TRY(run_select(h, pq, repr, split, idx, sp, dtype, topk, hb, causal, st, nullptr, tab, pv));
   TRY(run_fine(h, pq, pk, pv, pout, plse, idx, sp, dtype, topk, scale, causal, st, tab));
   if (p.copy) {
     TRY(unpad_rows(h, pout, out, p, tab, sp.d, st));
@@ -988,9 +987,10 @@ BSA_API bsa_status bsa_forward_noalloc(bsa_handle h, const void* q, const void* 
   // no events either: per-stage timing is off for this call
   const bool profiling = h->profiling;
   h->profiling = false;
-  bsa_status r = run_pool(h, k, repr, split, s, dtype, st, nullptr, v);
+  bsa_status r = run_pool(h, k, repr, split, s, dtype, st);
   if (r == BSA_OK)
-    r = run_select(h, q, repr, split, block_idx_out, s, dtype, topk, uniform_budget(topk), causal, st, &arena);
+    r = run_select(h, q, repr, split, block_idx_out, s, dtype, topk, uniform_budget(topk), causal, st, &arena,
+                   nullptr, v);
   if (r == BSA_OK)
     r = run_fine(h, q, k, v, out, nullptr, block_idx_out, s, dtype, topk, scale, causal, st, nullptr, &arena);
   h->profiling = profiling;

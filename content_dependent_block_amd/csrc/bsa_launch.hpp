@@ -17,16 +17,10 @@ namespace bsa {
 // padded to whole blocks (bsa_device.hpp); a block with fewer than 64 keys
 // is the mean of those.
 //
-// warm (nullable): V, laid out like K.  When it is small enough to stay in
-// the Infinity Cache until the fine stage reads it, the kernel also reads it
-// once, so that read comes while the selection leaves HBM idle instead of
-// in the attention kernel's first touch.
-//
 // Every `seqtab` below is that table: n / 64 entries in device memory, or
 // NULL for one sequence of n whole-block rows per head.
 hipError_t launch_block_pool(const void* k, float* repr, uint16_t* split, int64_t bh, int n, int d,
-                             bsa_dtype dtype, hipStream_t stream, const int4* seqtab = nullptr,
-                             const void* warm = nullptr);
+                             bsa_dtype dtype, hipStream_t stream, const int4* seqtab = nullptr);
 
 // The split buffer: the three bf16 planes [bh][3][n/64][d], then per block
 // the 2-norm of its hi term [bh][n/64] (fp32, rounded up), which the fused
@@ -75,7 +69,11 @@ struct HeadBudget {
 // and needs repair_counters (two device ints, zero when the handle was made,
 // owned by the caller, the same for every call of a handle), repair_list
 // (rows / 64 ints of workspace) and the call's parity (0/1, flipped by the
-// caller for every such call; calls must not overlap).
+// caller for every such call; calls must not overlap).  warm (nullable): the
+// V the fine stage will read, laid out like q.  When it fits the Infinity
+// Cache with room to spare (kWarmMaxBytes) each workgroup also reads its own
+// rows of it, so V arrives while this kernel leaves HBM nearly idle instead
+// of on the attention kernel's first touch.
 inline bool select_uses_repair(int d, bsa_dtype dtype, int topk) {
   return d == 128 && dtype == BSA_BF16 && topk > 16;
 }
@@ -84,7 +82,11 @@ hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t
                                 int topk, const HeadBudget& budget, int causal, hipStream_t stream,
                                 const int4* seqtab = nullptr, int32_t* fallbacks = nullptr,
                                 int32_t* repair_counters = nullptr, int32_t* repair_list = nullptr,
-                                int repair_parity = 0);
+                                int repair_parity = 0, const void* warm = nullptr);
+// V is read ahead only up to this size: Q and K (as large) and the
+// bucketing's pair lists also pass through the 256 MB cache before the
+// attention kernel runs, and would evict a larger V again first.
+constexpr int64_t kWarmMaxBytes = int64_t(64) << 20;
 constexpr int kFusedSelectMaxK = 32;
 
 // topk_select over panel rows [row0, row0 + rows): idx[(row0 + r) * topk + t].

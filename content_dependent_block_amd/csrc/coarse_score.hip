@@ -189,6 +189,7 @@ template <int D, int QG = 1, int NTH = 256, int TB_ = 32, int NTS = kTerms>
 struct Bf16PlaneTiles {
   using QT = bf16_bits;
   using Src = bf16_bits;
+  static constexpr int DIM = D;
   static constexpr int TB = TB_;                        // blocks per R tile
   static constexpr int PITCH = kRPitch<D>;
   // The hi-only tile type (NTS = 1) also stages its blocks' hi-term norms
@@ -351,6 +352,7 @@ template <int D, int TB_, int QG = 1, int NTH = 256>
 struct F32Tiles {
   using QT = float;
   using Src = float;
+  static constexpr int DIM = D;
   static constexpr int TB = TB_;
   static constexpr int KS = D / 4;
   static constexpr int PITCH = D + 4;
@@ -884,7 +886,8 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
                                                                       int32_t* __restrict__ fallbacks,
                                                                       int32_t* __restrict__ repair_count,
                                                                       int32_t* __restrict__ repair_clear,
-                                                                      int32_t* __restrict__ repair_list) {
+                                                                      int32_t* __restrict__ repair_list,
+                                                                      const typename TL::QT* __restrict__ warm) {
   using TL1 = typename Pass1Tiles<TL>::type;
   // split instance: this call lists its exact redos at repair_count, and
   // clears the other counter for the next call (no kernel of this call uses
@@ -928,10 +931,31 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
   // enters as a lower bound of its exact score, the hi-only score less the
   // block's error bound (norms4), so tau stays a bound for the exact scores.
   float tau[QG];
+  // The V rows of the workgroup's queries (warm, when given), read and
+  // discarded so the attention kernel finds V in the Infinity Cache.  Issued
+  // before the query rows and used (XOR, an empty asm) after them, they add
+  // no wait of their own.
+  constexpr int VCH = kTile * TL::DIM * static_cast<int>(sizeof(typename TL::QT)) / 16;
+  constexpr int VPT = (VCH + NTH - 1) / NTH;
+  uint4 vw[VPT];
+  if (warm) {
+    const uint4* vsrc = reinterpret_cast<const uint4*>(warm + ti.tile_row * TL::DIM);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = threadIdx.x + NTH * i;
+      vw[i] = c < VCH ? vsrc[c] : make_uint4(0, 0, 0, 0);
+    }
+  }
   {
     TL1 sc1;
     sc1.set_norms(hinorm, ti.bh, ti.nb);
     sc1.load_q(q, ti.qrow0, ti.g);
+    if (warm) {
+      uint32_t seen = 0;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) seen ^= vw[i].x ^ vw[i].y ^ vw[i].z ^ vw[i].w;
+      asm volatile("" ::"v"(seen));
+    }
     auto group_max = [&](bool checked, int h, int mt, int b0, const f32x4 (&acc)[QG]) {
       const f32x4 nrm = sc1.norms4(rs, mt, ti.g);
 #pragma unroll
@@ -1167,13 +1191,16 @@ void launch_panel(const void* q, const void* rsrc, float* panel, int64_t row0, i
                      panel, row0, rows, n, causal);
 }
 
-// Repair state of the split instance: two counters (one per call parity) and
-// a list of one entry per select workgroup.
+// Per-call extras of the select launch: the repair state of the split
+// instance (two counters, one per call parity, and a list of one entry per
+// select workgroup), the blocks' hi-term norms (bf16, after the split
+// planes) and the V to read ahead (or null).
 struct Repair {
   int32_t* counters = nullptr;
   int32_t* list = nullptr;
   int parity = 0;
-  const float* hinorm = nullptr;  // bf16: the blocks' hi-term norms (after the split planes)
+  const float* hinorm = nullptr;
+  const void* warm = nullptr;
 };
 
 template <typename TL, int KL, int GM, int CAP, int MINW, int QG, int NW, bool SPLIT = false>
@@ -1187,7 +1214,7 @@ void launch_select(const void* q, const void* rsrc, int32_t* idx, int64_t rows, 
   hipLaunchKernelGGL((coarse_select_kernel<TL, KL, GM, CAP, MINW, QG, NW, SPLIT>), dim3(static_cast<unsigned>(tiles)),
                      dim3(64 * NW), 0, s, static_cast<const typename TL::QT*>(q),
                      static_cast<const typename TL::Src*>(rsrc), idx, n, topk, hb, causal, seqtab, rp.hinorm, fallbacks,
-                     count, clear, SPLIT ? rp.list : nullptr);
+                     count, clear, SPLIT ? rp.list : nullptr, static_cast<const typename TL::QT*>(rp.warm));
   if constexpr (SPLIT) {
     const int64_t grid = tiles < 1024 ? tiles : 1024;
     hipLaunchKernelGGL((coarse_repair_kernel<TL, KL, QG, NW>), dim3(static_cast<unsigned>(grid)), dim3(64 * NW), 0, s,
@@ -1240,11 +1267,12 @@ hipError_t launch_coarse_select(const void* q, const float* repr, const uint16_t
                                 int32_t* idx, int64_t rows, int n, int d, bsa_dtype dtype,
                                 int topk, const HeadBudget& hb, int causal, hipStream_t stream,
                                 const int4* seqtab, int32_t* fallbacks, int32_t* repair_counters,
-                                int32_t* repair_list, int repair_parity) {
+                                int32_t* repair_list, int repair_parity, const void* warm) {
   Repair rp;
   rp.counters = repair_counters;
   rp.list = repair_list;
   rp.parity = repair_parity;
+  if (rows * d * (dtype == BSA_BF16 ? 2 : 4) <= kWarmMaxBytes) rp.warm = warm;
   if (dtype == BSA_BF16) rp.hinorm = split_norms(const_cast<uint16_t*>(repr_split), rows / n, n / kTile, d);
   if (select_uses_repair(d, dtype, topk) && (!repair_counters || !repair_list)) return hipErrorInvalidValue;
   if (dtype == BSA_BF16) {
