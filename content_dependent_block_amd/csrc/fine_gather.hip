@@ -67,6 +67,41 @@ __global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, 
   if (i < count) p[i] = 0;
 }
 
+// The candidate blocks of the rows of one bucketing workgroup.  Its rows
+// start at r_begin and lie in one slice (rpw divides the segment), so the
+// row of its pair e is r_begin + e / topk and its position in the slice
+// i0 + e / topk, i0 = r_begin mod n: no 64-bit division per pair, and none
+// at all unless a block table or the causal limit needs the row.  e / topk
+// comes from a float estimate, which is within one of it for e < 2^22, and
+// one correction each way.
+struct WgRows {
+  int i0, topk, nb, causal;
+  float inv_topk;
+  const int4* seqtab;
+  __device__ __forceinline__ WgRows(int64_t r_begin, int n, int topk_, int causal_, const int4* tab)
+      : i0(static_cast<int>(r_begin % n)), topk(topk_), nb(n / kTile), causal(causal_),
+        inv_topk(1.0f / static_cast<float>(topk_)), seqtab(tab) {}
+  __device__ __forceinline__ RowBlocks of(int e, bool use_causal) const {
+    RowBlocks r;
+    r.lo = 0;
+    r.hi = nb;
+    r.own = 0;
+    if (seqtab || (use_causal && causal)) {
+      int q = static_cast<int>(static_cast<float>(e) * inv_topk);
+      q += (q + 1) * topk <= e ? 1 : 0;
+      q -= q * topk > e ? 1 : 0;
+      r.own = (i0 + q) / kTile;
+      if (seqtab) {
+        const int4 t = seqtab[r.own];
+        r.lo = t.x;
+        r.hi = t.y;
+      }
+      if (use_causal && causal) r.hi = r.own + 1;
+    }
+    return r;
+  }
+};
+
 // Pairs per thread the bucketing kernels keep in registers: a workgroup of
 // rpw rows holds rpw * topk <= 256 * kPairRegs pairs that way (all the
 // selection sizes up to 32 at rpw = 256); larger ones go through memory.
@@ -137,6 +172,7 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
   const int64_t p_begin = (r_begin - row0) * topk;  // chunk-relative pair id of the first pair
   const int64_t bucket0 = bucket_of(r_begin, 0, n, nb, qsegs, bh0);  // rpw divides the segment
   const int32_t* sel = idx + r_begin * topk;          // the workgroup's selections, contiguous
+  const WgRows wr(r_begin, n, topk, causal, seqtab);
   for (int c = threadIdx.x; c < nb; c += 256) hist[c] = 0;
   __syncthreads();
   if (npairs <= 256 * kPairRegs) {
@@ -147,7 +183,7 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
       lr[j] = -1;
       bt[j] = 0;
       if (e < npairs) {
-        const int beta = sel_block(sel[e], row_blocks(seqtab, r_begin + e / topk, n, causal));
+        const int beta = sel_block(sel[e], wr.of(e, true));
         if (beta >= 0) {
           bt[j] = beta;
           lr[j] = atomicAdd(&hist[beta], 1);
@@ -176,7 +212,7 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
     return;
   }
   for (int e = threadIdx.x; e < npairs; e += 256) {
-    const int beta = sel_block(sel[e], row_blocks(seqtab, r_begin + e / topk, n, causal));
+    const int beta = sel_block(sel[e], wr.of(e, true));
     rank[p_begin + e] = beta >= 0 ? atomicAdd(&hist[beta], 1) : -1;
   }
   __syncthreads();
@@ -185,7 +221,7 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
   __syncthreads();
   for (int e = threadIdx.x; e < npairs; e += 256) {
     const int32_t rk = rank[p_begin + e];
-    if (rk >= 0) rank[p_begin + e] = base[sel_block(sel[e], row_blocks(seqtab, r_begin + e / topk, n, 0))] + rk;
+    if (rk >= 0) rank[p_begin + e] = base[sel_block(sel[e], wr.of(e, false))] + rk;
   }
 }
 
@@ -317,10 +353,11 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(
     return;
   }
   const int32_t* sel = idx + r_begin * topk;
+  const WgRows wr(r_begin, n, topk, 0, seqtab);
   for (int e = threadIdx.x; e < np; e += 256) {
     const int32_t rk = rank[p_begin + e];
     if (rk < 0) continue;
-    const int64_t pos = static_cast<int64_t>(off[sel_block(sel[e], row_blocks(seqtab, r_begin + e / topk, n, 0))]) + rk;
+    const int64_t pos = static_cast<int64_t>(off[sel_block(sel[e], wr.of(e, false))]) + rk;
     if (pos < npairs) list[pos] = static_cast<int32_t>(p_begin + e);
   }
 }
