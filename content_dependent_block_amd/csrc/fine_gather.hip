@@ -425,7 +425,7 @@ __device__ __forceinline__ int out_dim(int dt, int m) {
 // of that tile, hence every lane of the pair's column, holds it.
 template <typename T, int D, bool CAUSAL>
 __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage, const QOperand<T, D>& qo,
-                                           int64_t row, int beta, int n, int klim, bool live, int32_t pair,
+                                           int qi, int beta, int klim, bool live, int32_t pair,
                                            float scale_log2, PartialT<T>* __restrict__ po, int lane) {
   using L = KvLayout<T, D>;
   const int g = lane >> 4, c16 = lane & 15;
@@ -451,7 +451,6 @@ __device__ __forceinline__ void pair_group(const T* ks, const T* vs, f16* stage,
     }
   }
   if (CAUSAL) {
-    const int qi = static_cast<int>(row % n);
     if (beta == qi / kTile) {  // diagonal block: keys after the query are hidden
       const int qlocal = qi % kTile;
 #pragma unroll
@@ -661,8 +660,9 @@ __global__ __launch_bounds__(256) void gather_partial_kernel(
     if ((wave + 4 * gi) * 16 >= cnt) break;  // wave-uniform
     if (gi + kQueryAhead < GPW)
       load_q<T, D>(qo[gi + kQueryAhead], q, row[gi + kQueryAhead], live[gi + kQueryAhead], g);
-    pair_group<T, D, CAUSAL>(ks, vs, stage, qo[gi], row[gi], beta, n, klim, live[gi], pair[gi],
-                             scale_log2, po, lane);
+    // the pair's row within its slice: a bucket holds rows of head bh only
+    pair_group<T, D, CAUSAL>(ks, vs, stage, qo[gi], static_cast<int>(row[gi] - bh * n), beta, klim, live[gi],
+                             pair[gi], scale_log2, po, lane);
   }
 }
 
