@@ -41,8 +41,9 @@ struct bsa_handle_s {
     size_t bytes = 0;
   };
   Buf g_count, g_offsets, g_items, g_item_rec, g_rank, g_rec, g_wgv, g_list, g_po;
+  // backward: per-row (lse, delta), per-pair dq, per-item dk/dv, bf16 dout
   Buf b_ld, b_dq, b_dkv, b_dob;
-  bool counts_zero = false;  // g_count holds zeros (the bucketing's scan leaves it so)  // backward: per-row (lse, delta), per-pair dq, per-item dk/dv, bf16 dout
+  bool counts_zero = false;  // g_count holds zeros (the bucketing's scan leaves it so)
   Buf r_q, r_k, r_v, r_o, r_do, r_lse, r_idx, r_dq, r_dk, r_dv;  // padded copies (ragged lengths)
   // block table of sequences padded to whole blocks: device copy, pinned
   // staging copy, and an event on the last upload from the staging copy
