@@ -516,61 +516,80 @@ __global__ __launch_bounds__(256, (BwdLayout<T, D>::kWaves)) void bwd_pair_kerne
 }
 
 // dq[row] = sum over the row's valid slots, in slot order, of its pairs'
-// contributions.  16 lanes per row; 8 slots at a time, every lane issues the
-// loads of its D/16 dims of all 8 before adding any (slot index clamped into
-// the row so every load is in bounds; slots that are padding were never
-// written and are dropped by a select).  HALF: the rows are bf16 (bf16
-// inputs), else fp32.
+// contributions.  16 lanes per row, S slots at a time (16; 8 for fp32 rows
+// at d = 128, whose 8 words per lane and slot would otherwise cost the
+// kernel occupancy): every lane issues the loads of its D/16 dims of all S
+// before adding any (slot index clamped into the row, so every load is in
+// bounds), lane c < S decides whether slot s0 + c counts, and a ballot shares
+// the answers with the row's lanes; slots that are padding were never
+// written, and their words are zeroed before the sum.
+// HALF: the rows are bf16 (bf16 inputs), else fp32.
 template <int D, bool HALF>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(const int32_t* __restrict__ idx,
                                                      const void* __restrict__ dq_part,
                                                      float* __restrict__ dq, int64_t row0,
                                                      int64_t rows, int n, int topk, int causal,
                                                      const int4* __restrict__ seqtab) {
-  constexpr int E = D / 16;
-  constexpr int V = E / 4;
-  constexpr int S = 8;
+  constexpr int E = D / 16;                // dims per lane
+  constexpr int LW = HALF ? E / 2 : E;     // 32-bit words per lane and slot
+  constexpr int WPR = HALF ? D / 2 : D;    // 32-bit words per contribution row
+  constexpr int S = LW >= 8 ? 8 : 16;
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   const int64_t r = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  if (r >= rows) return;
   const int c = threadIdx.x & 15;
-  const int64_t row = row0 + r;
+  const int gbase = (threadIdx.x & 63) & ~15;
+  const bool row_ok = r < rows;  // lanes of a missing row still take part in the ballot
+  const int64_t rc = row_ok ? r : rows - 1;
+  const int64_t row = row0 + rc;
   const RowBlocks rb = row_blocks(seqtab, row, n, causal);
-  f32x4 acc[V];
+  const uint32_t* src = static_cast<const uint32_t*>(dq_part) + rc * topk * WPR + c * LW;
+  float acc[E];
 #pragma unroll
-  for (int u = 0; u < V; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
   for (int s0 = 0; s0 < topk; s0 += S) {
-    f32x4 x[S][V];
-    bool ok[S];
+    uint32_t w[S][LW];
 #pragma unroll
     for (int t = 0; t < S; ++t) {
       const int st = s0 + t < topk ? s0 + t : topk - 1;
-      const int64_t pr = r * topk + st;
-      ok[t] = s0 + t < topk && sel_block(idx[row * topk + st], rb) >= 0;
-      if constexpr (HALF) {
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        const u32x2* src = reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(dq_part) + pr * D + c * E);
-#pragma unroll
-        for (int u = 0; u < V; ++u) {
-          const u32x2 h = __builtin_nontemporal_load(src + u);
-          x[t][u] = f32x4{__uint_as_float(h[0] << 16), __uint_as_float(h[0] & 0xFFFF0000u),
-                          __uint_as_float(h[1] << 16), __uint_as_float(h[1] & 0xFFFF0000u)};
-        }
+      const uint32_t* p = src + static_cast<int64_t>(st) * WPR;
+      if constexpr (LW == 2) {
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+        w[t][0] = v.x;
+        w[t][1] = v.y;
       } else {
-        const f32x4* src = reinterpret_cast<const f32x4*>(static_cast<const float*>(dq_part) + pr * D + c * E);
 #pragma unroll
-        for (int u = 0; u < V; ++u) x[t][u] = __builtin_nontemporal_load(src + u);
+        for (int h = 0; h < LW / 4; ++h) {
+          const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p) + h);
+          w[t][4 * h] = v.x;
+          w[t][4 * h + 1] = v.y;
+          w[t][4 * h + 2] = v.z;
+          w[t][4 * h + 3] = v.w;
+        }
       }
     }
+    const bool valid = row_ok && c < S && s0 + c < topk && sel_block(idx[row * topk + s0 + c], rb) >= 0;
+    const uint32_t vmask = static_cast<uint32_t>(ballot(valid) >> gbase) & 0xFFFFu;
 #pragma unroll
-    for (int t = 0; t < S; ++t)
+    for (int t = 0; t < S; ++t) {
+      const bool on = (vmask >> t) & 1u;
 #pragma unroll
-      for (int u = 0; u < V; ++u)
-        acc[u] += ok[t] ? x[t][u] : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k2 = 0; k2 < LW; ++k2) {
+        const uint32_t x = on ? w[t][k2] : 0u;
+        if constexpr (HALF) {
+          acc[2 * k2] += __uint_as_float(x << 16);
+          acc[2 * k2 + 1] += __uint_as_float(x & 0xFFFF0000u);
+        } else {
+          acc[k2] += __uint_as_float(x);
+        }
+      }
+    }
   }
+  if (!row_ok) return;
   float* dst = dq + row * D + c * E;
 #pragma unroll
-  for (int u = 0; u < V; ++u)
-    *reinterpret_cast<float4*>(dst + 4 * u) = make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+  for (int e = 0; e < E; e += 4)
+    *reinterpret_cast<float4*>(dst + e) = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
 }
 
 // dk, dv of one (head, key block): the sum of its work items over the
