@@ -32,6 +32,7 @@ summed over the 8 XCDs) the kernel's cycles and 1024 SIMDs:
     LDS busy   = 4 SQ_ACTIVE_INST_LDS / (C * 1024)
     bf16 MFMA FLOP = 512 SQ_INSTS_VALU_MFMA_MOPS_BF16
     LDS bank-conflict cycles per LDS instruction = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS
+    L2 hit rate = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)
 """
 from __future__ import annotations
 
@@ -176,6 +177,8 @@ def counters(dirs, kernel_re):
         out["bf16_mfma_flop"] = 512 * c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
     if "SQ_LDS_BANK_CONFLICT" in c and c.get("SQ_INSTS_LDS"):
         out["lds_conflict_cycles_per_lds_inst"] = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_INSTS_LDS"]
+    if c.get("TCC_HIT_sum", 0.0) + c.get("TCC_MISS_sum", 0.0) > 0:
+        out["l2_hit_rate"] = c.get("TCC_HIT_sum", 0.0) / (c.get("TCC_HIT_sum", 0.0) + c.get("TCC_MISS_sum", 0.0))
     return out
 
 
