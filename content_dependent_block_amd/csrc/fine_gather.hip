@@ -225,6 +225,57 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
   }
 }
 
+// The same scan for up to 4096 buckets, in one step: thread t takes buckets
+// 4t .. 4t + 3 (loaded, summed, scanned over the workgroup through the 16
+// wave totals, written back and cleared), with no LDS staging and no passes.
+constexpr int kScanSmallMax = 4096;
+__global__ __launch_bounds__(1024) void bucket_scan_small_kernel(int32_t* __restrict__ count,
+                                                                 int32_t* __restrict__ offsets,
+                                                                 int32_t* __restrict__ items, int nbuckets,
+                                                                 int item_pairs) {
+  __shared__ int32_t s_wp[16], s_wi[16];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int32_t v[4], sp = 0, si = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int b = 4 * t + j;
+    v[j] = b < nbuckets ? count[b] : 0;
+    sp += v[j];
+    si += (v[j] + item_pairs - 1) / item_pairs;
+  }
+  const int32_t ip = wave_incl_scan(sp, lane), ii = wave_incl_scan(si, lane);
+  if (lane == 63) {
+    s_wp[wave] = ip;
+    s_wi[wave] = ii;
+  }
+  __syncthreads();
+  int32_t ep = ip - sp, ei = ii - si, tp = 0, ti = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) {
+      ep += s_wp[w];
+      ei += s_wi[w];
+    }
+    tp += s_wp[w];
+    ti += s_wi[w];
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int b = 4 * t + j;
+    if (b < nbuckets) {
+      offsets[b] = ep;
+      items[b] = ei;
+      count[b] = 0;  // the counts start at zero for the next bucketing
+    }
+    ep += v[j];
+    ei += (v[j] + item_pairs - 1) / item_pairs;
+  }
+  if (t == 0) {
+    offsets[nbuckets] = tp;
+    items[nbuckets] = ti;
+  }
+}
+
 // Single workgroup of 1024 threads.  offsets[b] / items[b] are exclusive
 // prefixes; entry nbuckets holds the totals.  It leaves count[] zero, as the
 // next bucketing's count kernel needs it.  Passes of 1024 x 16 buckets:
@@ -930,8 +981,12 @@ hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, 
   hipLaunchKernelGGL(bucket_count_kernel, dim3(static_cast<unsigned>(row_groups)), dim3(256),
                      count_lds, s, a.idx, a.ws.count, a.ws.rank, a.ws.rec,
                      a.ws.wg_valid, row0, rows, a.n, a.topk, a.causal, c.bh0, rpw, a.qsegs, a.seqtab);
-  hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, a.ws.count, a.ws.offsets,
-                     a.ws.items, c.nbuckets, a.item_pairs);
+  if (c.nbuckets <= kScanSmallMax)
+    hipLaunchKernelGGL(bucket_scan_small_kernel, dim3(1), dim3(1024), 0, s, a.ws.count, a.ws.offsets, a.ws.items,
+                       c.nbuckets, a.item_pairs);
+  else
+    hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, a.ws.count, a.ws.offsets,
+                       a.ws.items, c.nbuckets, a.item_pairs);
   const int64_t bucket_groups = (c.nbuckets + 255) / 256;
   hipLaunchKernelGGL(bucket_fill_kernel,
                      dim3(static_cast<unsigned>(row_groups > bucket_groups ? row_groups : bucket_groups)),
