@@ -358,7 +358,11 @@ __global__ __launch_bounds__(1024) void bucket_scan_kernel(int32_t* __restrict__
 // workgroup per rpw rows).  On the register path it streams the count
 // kernel's block-ordered records, so the pairs of one bucket, whose list
 // positions are consecutive, leave in consecutive lanes of one store; else
-// each pair is stored at its own position.  Workgroup w also
+// each pair is stored at its own position.  The list starts of the
+// workgroup's (head, segment) are staged in LDS first when they fit
+// (stage_off, nb entries), and a thread issues the loads of all its records
+// before storing any, so a record costs one global load rather than a chain
+// of two.  Workgroup w also
 // writes, for each work item of buckets 256w .. 256w + 255, the record
 // {bucket, first list position, pair count} at the slot of the workgroup
 // that will run it: items are spread so that consecutive items (one head,
@@ -369,7 +373,8 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(
     const int32_t* __restrict__ wg_valid, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ items, int4* __restrict__ item_rec, int nbuckets, int64_t max_slots,
     int32_t* __restrict__ list, int64_t row0, int64_t rows, int n, int topk, int64_t bh0, int qsegs,
-    int item_pairs, int rpw, const int4* __restrict__ seqtab) {
+    int item_pairs, int rpw, const int4* __restrict__ seqtab, int stage_off) {
+  extern __shared__ int32_t s_off[];  // [nb] when stage_off
   const int64_t pb = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (pb < nbuckets) {
     const int32_t total = items[nbuckets];
@@ -395,6 +400,26 @@ __global__ __launch_bounds__(256) void bucket_fill_kernel(
     // the count kernel's block-ordered records: consecutive records of one
     // block have consecutive list positions
     const int32_t valid = wg_valid[blockIdx.x];
+    if (stage_off) {  // workgroup-uniform
+      for (int c = threadIdx.x; c < nb; c += 256) s_off[c] = off[c];
+      __syncthreads();
+      int2 r[kPairRegs];
+#pragma unroll
+      for (int j = 0; j < kPairRegs; ++j) {
+        const int t = threadIdx.x + 256 * j;
+        r[j] = t < valid ? rec[p_begin + t] : make_int2(0, -1);
+      }
+#pragma unroll
+      for (int j = 0; j < kPairRegs; ++j) {
+        const int t = threadIdx.x + 256 * j;
+        const uint32_t w = static_cast<uint32_t>(r[j].y);
+        if (t < valid) {
+          const int64_t pos = static_cast<int64_t>(s_off[w >> 21]) + (w & 0x1FFFFFu);
+          if (pos < npairs) list[pos] = r[j].x;
+        }
+      }
+      return;
+    }
     for (int t = threadIdx.x; t < valid; t += 256) {
       const int2 r = rec[p_begin + t];
       const uint32_t w = static_cast<uint32_t>(r.y);
@@ -988,11 +1013,14 @@ hipError_t launch_gather_index(const GatherArgs& a, int64_t row0, int64_t rows, 
     hipLaunchKernelGGL(bucket_scan_kernel, dim3(1), dim3(1024), 0, s, a.ws.count, a.ws.offsets,
                        a.ws.items, c.nbuckets, a.item_pairs);
   const int64_t bucket_groups = (c.nbuckets + 255) / 256;
+  // the list starts of a (head, segment) go to LDS when they fit in 16 KB
+  const int stage_off = c.nb <= 4096 ? 1 : 0;
   hipLaunchKernelGGL(bucket_fill_kernel,
                      dim3(static_cast<unsigned>(row_groups > bucket_groups ? row_groups : bucket_groups)),
-                     dim3(256), 0, s, a.idx, a.ws.rank, a.ws.rec, a.ws.wg_valid, a.ws.offsets, a.ws.items,
-                     a.ws.item_rec, c.nbuckets, gather_grid(rows, a.topk, c.nbuckets, a.item_pairs), a.ws.list,
-                     row0, rows, a.n, a.topk, c.bh0, a.qsegs, a.item_pairs, rpw, a.seqtab);
+                     dim3(256), stage_off ? static_cast<size_t>(c.nb) * 4 : 0, s, a.idx, a.ws.rank, a.ws.rec,
+                     a.ws.wg_valid, a.ws.offsets, a.ws.items, a.ws.item_rec, c.nbuckets,
+                     gather_grid(rows, a.topk, c.nbuckets, a.item_pairs), a.ws.list, row0, rows, a.n, a.topk, c.bh0,
+                     a.qsegs, a.item_pairs, rpw, a.seqtab, stage_off);
   return hipGetLastError();
 }
 
