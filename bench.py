@@ -392,6 +392,16 @@ def measure(r: Runner, args, scratch, steps, warmup):
         page_flops = total_flops + 5 * visible_pairs(w)
         res["page_convention"] = {"gflop": round(page_flops / 1e9, 4),
                                   "tflops": round(page_flops / (ms_med * 1e-3) / 1e12, 3)}
+        if not w.static and "sparse_flash_fwd" in per_step:
+            # The fine stage against HBM bandwidth over per-query gathered
+            # bytes (every visible pair's key and value rows read once per
+            # query): a sanity figure that exceeds 1 whenever caches reuse
+            # key blocks across queries, which block-gather is built on.
+            gathered = visible_pairs(w) * 2 * w.d * (2 if w.dtype == "bf16" else 4)
+            ideal = gathered / (HBM_PEAK_GBS * 1e9) * 1e3
+            res["gather_r2"] = {"per_query_gather_gb": round(gathered / 1e9, 3), "ideal_ms": round(ideal, 4),
+                                "attention_ms": round(per_step["sparse_flash_fwd"], 5),
+                                "frac": round(ideal / per_step["sparse_flash_fwd"], 3)}
         strict_ms = strict_ideal_s(w, r.nnz) * 1e3
         res["path_roofline"]["strict_ideal_ms"] = round(strict_ms, 5)
         res["path_roofline"]["strict_frac"] = round(strict_ms / ms_med, 5)
@@ -533,6 +543,7 @@ def main():
         "effective_tflops": res["effective_tflops"],
         "algorithmic_gflop": res["algorithmic_gflop"],
         **({"page_convention": res["page_convention"]} if "page_convention" in res else {}),
+        **({"gather_r2": res["gather_r2"]} if "gather_r2" in res else {}),
         "stage_ms_per_step": res["stage_ms_per_step"],
         "roofline": res["roofline"],
         "stage_rooflines": res["stage_rooflines"],
