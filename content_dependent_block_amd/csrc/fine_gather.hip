@@ -225,9 +225,10 @@ __global__ __launch_bounds__(256) void bucket_count_kernel(
   }
 }
 
-// The same scan for up to 4096 buckets, in one step: thread t takes buckets
-// 4t .. 4t + 3 (loaded, summed, scanned over the workgroup through the 16
-// wave totals, written back and cleared), with no LDS staging and no passes.
+// The bucket scan (bucket_scan_kernel, below, states what it computes) for
+// up to 4096 buckets, in one step: thread t takes buckets 4t .. 4t + 3
+// (loaded, summed, scanned over the workgroup through the 16 wave totals,
+// written back and cleared), with no LDS staging and no passes.
 constexpr int kScanSmallMax = 4096;
 __global__ __launch_bounds__(1024) void bucket_scan_small_kernel(int32_t* __restrict__ count,
                                                                  int32_t* __restrict__ offsets,
