@@ -7,17 +7,20 @@ block-gather sparse_flash_fwd (gather_index, attention, gather_combine); for
 the static workload one bsa_forward_static over its tile list.
 
 Timing protocol: W untimed warm-up steps; then K cold steps, each after a
-1 GiB scratch write that evicts the inputs from the 256 MB Infinity Cache
+1 GiB scratch read that evicts the inputs from the 256 MB Infinity Cache
 and timed with HIP events on the launch stream.  The step is queued behind
-the scratch write (write, start event, step, end event, then a device
+the scratch read (read, start event, step, end event, then a device
 synchronisation), so the host has issued the step's launches before its
-start event fires, as in a stream of back-to-back calls.  `value` is
-tokens/s at the MEDIAN cold step; beside it the line reports the warm figure
-(K steps back to back) and the cold median with a device synchronisation
-before each start event, which also counts the host's time to issue the
-step's first kernel.  Per-kernel times come from another queued cold pass
-with per-stage HIP events on the launch stream (the roofline of the dominant
-kernel is computed from those).
+start event fires, as in a stream of back-to-back calls.  A read leaves the
+cache holding clean lines; a 1 GiB write would leave up to 256 MB of dirty
+lines whose write-back the next step would pay for (--cache-check measures
+both on a plain tensor read).  `value` is tokens/s at the MEDIAN cold step;
+beside it the line reports the warm figure (K steps back to back), the cold
+median with a device synchronisation before each start event (the host's
+issue of the first kernel then counts too), and the cold median after a
+1 GiB scratch write instead of the read.  Per-kernel times come from
+another queued cold pass with per-stage HIP events on the launch stream
+(the roofline of the dominant kernel is computed from those).
 
 Prints ONE JSON line: the headline workload's tokens/s, effective TFLOP/s,
 the roofline of the dominant kernel, every stage's bound and fraction, the
@@ -313,18 +316,22 @@ class Runner:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    def cold(self, steps, scratch, profile=False, synced=False):
+    def cold(self, steps, scratch, profile=False, synced=False, flush="read"):
         """Milliseconds of each of `steps` steps, each after a 1 GiB scratch
-        write on the same stream; with profile, also the per-stage HIP-event
-        times.  synced: wait for the scratch write before issuing the step,
-        so its time also holds the host's issue of the first kernel."""
+        read (flush="write": a 1 GiB scratch write) on the same stream; with
+        profile, also the per-stage HIP-event times.  synced: wait for the
+        flush before issuing the step, so its time also holds the host's
+        issue of the first kernel."""
         torch, m, h = self.torch, self.m, self.lib.handle
         if profile:
             m.bsa_profile_read(h, reset=True)
             m.bsa_profile_enable(h, True)
         times = []
         for i in range(steps):
-            scratch.fill_(float(i))
+            if flush == "write":
+                scratch.fill_(float(i))
+            else:
+                torch.sum(scratch)
             if synced:
                 torch.cuda.synchronize()
             c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -357,6 +364,37 @@ def stage_roofline(w, work, name, per_launch_ms, launches_per_step):
             "unit": unit, "frac": round(achieved / peak, 5)}
 
 
+def cache_check(torch, reps=15):
+    """Median microseconds of one read of a 200 MB tensor x (it fits the
+    256 MB Infinity Cache), taken right after x was read once more and then
+    after nothing, a 1 GiB read, a 1 GiB write, or a 2 GiB read.  Equal times
+    after the 1 GiB and the 2 GiB read mean a 1 GiB read evicts x; a longer
+    time after the write is the write-back of its dirty lines, paid by the
+    read that follows it."""
+    dev = "cuda:0"
+    x = torch.ones(50 << 20, dtype=torch.float32, device=dev)
+    a1 = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    a2 = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    flushes = {"none": lambda i: None, "read_1gib": lambda i: torch.sum(a1),
+               "write_1gib": lambda i: a1.fill_(float(i)),
+               "read_2gib": lambda i: (torch.sum(a1), torch.sum(a2))}
+    res = {"x_bytes": x.numel() * 4}
+    for name, fl in flushes.items():
+        ts = []
+        for i in range(reps):
+            torch.sum(x)
+            fl(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            torch.sum(x)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        res[f"read_x_after_{name}_us"] = round(float(np.median(ts)), 1)
+    return res
+
+
 def measure(r: Runner, args, scratch, steps, warmup):
     """Warm-up, cold steps (the value), warm steps, cold per-stage times."""
     w = r.w
@@ -365,6 +403,7 @@ def measure(r: Runner, args, scratch, steps, warmup):
     r.torch.cuda.synchronize()
     cold_t, _ = r.cold(steps, scratch)
     synced_t, _ = r.cold(steps, scratch, synced=True)
+    write_t, _ = r.cold(steps, scratch, flush="write")
     warm_ms = r.warm(steps)
     _, stages = r.cold(steps, scratch, profile=True)
     per_step = {k: v[0] / steps for k, v in stages.items()}
@@ -378,6 +417,7 @@ def measure(r: Runner, args, scratch, steps, warmup):
         "ms_cold_median": round(ms_med, 5), "ms_cold_min": round(float(np.min(cold_t)), 5),
         "ms_cold_mean": round(float(np.mean(cold_t)), 5), "ms_warm": round(warm_ms, 5),
         "ms_cold_synced_median": round(float(np.median(synced_t)), 5),
+        "ms_cold_write_flush_median": round(float(np.median(write_t)), 5),
         "tokens_per_s": round(tokens / (ms_med * 1e-3), 1),
         "tokens_per_s_warm": round(tokens / (warm_ms * 1e-3), 1),
         "effective_tflops": round(total_flops / (ms_med * 1e-3) / 1e12, 3),
@@ -442,6 +482,9 @@ def main():
     ap.add_argument("--fine-chunk-mb", type=int, default=0, help="block-gather partial chunk (0 = default)")
     ap.add_argument("--static-item-tiles", type=int, default=0, help="static work-item size (0 = per call)")
     ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward")
+    ap.add_argument("--cache-check", action="store_true",
+                    help="run only the check of the cold-step flush: a 200 MB tensor read after no "
+                         "flush, after a 1 GiB read, a 1 GiB write, and a 2 GiB read")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB -> 1 GiB device copy (3 times), the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -452,6 +495,10 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.cache_check:
+        print(json.dumps(cache_check(torch)))
+        return
 
     if args.copy_calibration:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
@@ -479,7 +526,7 @@ def main():
     if args.fine_chunk_mb:
         m.bsa_set_option(h, m.BSA_OPT_FINE_CHUNK_BYTES, args.fine_chunk_mb << 20)
     m.bsa_set_option(h, m.BSA_OPT_STATIC_ITEM_TILES, args.static_item_tiles)
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB cache flush
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB cache flush
 
     r = Runner(m, lib, w, args.which, args)
     res = measure(r, args, scratch, args.steps, args.warmup)
@@ -514,6 +561,7 @@ def main():
             del ro
             torch.cuda.empty_cache()
             others[name] = {k: o[k] for k in ("ms_cold_median", "ms_cold_min", "ms_cold_synced_median",
+                                              "ms_cold_write_flush_median",
                                               "ms_warm", "tokens_per_s",
                                               "tokens_per_s_warm", "effective_tflops", "algorithmic_gflop",
                                               "page_convention", "stage_ms_per_step", "path_roofline")}
@@ -547,11 +595,12 @@ def main():
         "data": ("synthetic: seeded N(0,1) q/k/v plus per-block key offsets N(0,0.5^2), rounded to bf16 "
                  "(no dataset)") if w.key_offsets else "synthetic: seeded N(0,1) (no dataset)",
         "config": cfg,
-        "timing": {"value_from": "median of the cold steps (each queued behind a 1 GiB scratch write; "
+        "timing": {"value_from": "median of the cold steps (each queued behind a 1 GiB scratch read; "
                                  "HIP events)",
                    "ms_cold_median": res["ms_cold_median"], "ms_cold_min": res["ms_cold_min"],
                    "ms_cold_mean": res["ms_cold_mean"], "ms_warm": res["ms_warm"],
                    "ms_cold_synced_median": res["ms_cold_synced_median"],
+                   "ms_cold_write_flush_median": res["ms_cold_write_flush_median"],
                    "tokens_per_s_warm": res["tokens_per_s_warm"]},
         "effective_tflops": res["effective_tflops"],
         "algorithmic_gflop": res["algorithmic_gflop"],

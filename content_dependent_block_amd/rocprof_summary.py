@@ -69,7 +69,7 @@ _SHORT = re.compile(r"(gather_partial_kernel|static_item_kernel|static_combine_k
                     r"topk_lane_kernel|topk_wave_kernel|coarse_select_kernel|coarse_repair_kernel|coarse_panel_kernel|"
                     r"bucket_count_kernel|bucket_scan_small_kernel|bucket_scan_kernel|bucket_fill_kernel|block_pool_kernel|"
                     r"zero_i32_kernel|sparse_flash_kernel|per_query_kernel|pad_rows_kernel|unpad_rows_kernel|"
-                    r"elementwise_kernel|bwd_prep_kernel|bwd_pair_kernel|bwd_dq_kernel|bwd_dkv_kernel|"
+                    r"elementwise_kernel|reduce_kernel|bwd_prep_kernel|bwd_pair_kernel|bwd_dq_kernel|bwd_dkv_kernel|"
                     r"copyBuffer)")
 
 
