@@ -7,18 +7,18 @@ block-gather sparse_flash_fwd (gather_index, attention, gather_combine); for
 the static workload one bsa_forward_static over its tile list.
 
 Timing protocol: W untimed warm-up steps; then K cold steps, each after a
-1 GiB scratch read that evicts the inputs from the 256 MB Infinity Cache
-and timed with HIP events on the launch stream.  The step is queued behind
-the scratch read (read, start event, step, end event, then a device
-synchronisation), so the host has issued the step's launches before its
-start event fires, as in a stream of back-to-back calls.  A read leaves the
-cache holding clean lines; a 1 GiB write would leave up to 256 MB of dirty
-lines whose write-back the next step would pay for (--cache-check measures
-both on a plain tensor read).  `value` is tokens/s at the MEDIAN cold step;
-beside it the line reports the warm figure (K steps back to back), the cold
-median with a device synchronisation before each start event (the host's
-issue of the first kernel then counts too), and the cold median after a
-1 GiB scratch write instead of the read.  Per-kernel times come from
+1 GiB scratch write that evicts the inputs from the 256 MB Infinity Cache,
+followed by a read of the same buffer, and timed with HIP events on the
+launch stream.  The step is queued behind the flush (write, read, start
+event, step, end event, then a device synchronisation), so the host has
+issued the step's launches before its start event fires, as in a stream of
+back-to-back calls.  The read leaves the cache holding clean lines; after
+the write alone up to 256 MB of dirty lines remain, whose write-back the
+next step would pay for (--cache-check measures every case on a plain
+tensor read).  `value` is tokens/s at the MEDIAN cold step; beside it the
+line reports the warm figure (K steps back to back), the cold median with
+a device synchronisation before each start event (the host's issue of the
+first kernel then counts too), and the cold median after the write alone.  Per-kernel times come from
 another queued cold pass with per-stage HIP events on the launch stream
 (the roofline of the dominant kernel is computed from those).
 
@@ -316,21 +316,20 @@ class Runner:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
-    def cold(self, steps, scratch, profile=False, synced=False, flush="read"):
+    def cold(self, steps, scratch, profile=False, synced=False, flush="write_read"):
         """Milliseconds of each of `steps` steps, each after a 1 GiB scratch
-        read (flush="write": a 1 GiB scratch write) on the same stream; with
-        profile, also the per-stage HIP-event times.  synced: wait for the
-        flush before issuing the step, so its time also holds the host's
-        issue of the first kernel."""
+        write and a read of the same buffer (flush="write": the write alone)
+        on the same stream; with profile, also the per-stage HIP-event times.
+        synced: wait for the flush before issuing the step, so its time also
+        holds the host's issue of the first kernel."""
         torch, m, h = self.torch, self.m, self.lib.handle
         if profile:
             m.bsa_profile_read(h, reset=True)
             m.bsa_profile_enable(h, True)
         times = []
         for i in range(steps):
-            if flush == "write":
-                scratch.fill_(float(i))
-            else:
+            scratch.fill_(float(i))
+            if flush == "write_read":
                 torch.sum(scratch)
             if synced:
                 torch.cuda.synchronize()
@@ -367,16 +366,18 @@ def stage_roofline(w, work, name, per_launch_ms, launches_per_step):
 def cache_check(torch, reps=15):
     """Median microseconds of one read of a 200 MB tensor x (it fits the
     256 MB Infinity Cache), taken right after x was read once more and then
-    after nothing, a 1 GiB read, a 1 GiB write, or a 2 GiB read.  Equal times
-    after the 1 GiB and the 2 GiB read mean a 1 GiB read evicts x; a longer
-    time after the write is the write-back of its dirty lines, paid by the
-    read that follows it."""
+    after nothing, a 1 GiB read, a 1 GiB write, that write followed by a
+    read of the same buffer (the cold steps' flush), or a 2 GiB read.  Equal
+    times after a 1 GiB and a 2 GiB read mean a 1 GiB read evicts x; a
+    longer time after the write alone is the write-back of its dirty lines,
+    paid by the read that follows it."""
     dev = "cuda:0"
     x = torch.ones(50 << 20, dtype=torch.float32, device=dev)
     a1 = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     a2 = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     flushes = {"none": lambda i: None, "read_1gib": lambda i: torch.sum(a1),
                "write_1gib": lambda i: a1.fill_(float(i)),
+               "write_then_read_1gib": lambda i: (a1.fill_(float(i)), torch.sum(a1)),
                "read_2gib": lambda i: (torch.sum(a1), torch.sum(a2))}
     res = {"x_bytes": x.numel() * 4}
     for name, fl in flushes.items():
@@ -484,7 +485,7 @@ def main():
     ap.add_argument("--pass", dest="which", choices=["forward", "backward"], default="forward")
     ap.add_argument("--cache-check", action="store_true",
                     help="run only the check of the cold-step flush: a 200 MB tensor read after no "
-                         "flush, after a 1 GiB read, a 1 GiB write, and a 2 GiB read")
+                         "flush, a 1 GiB read, a 1 GiB write, that write and a read of it, a 2 GiB read")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB -> 1 GiB device copy (3 times), the reference "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -526,7 +527,7 @@ def main():
     if args.fine_chunk_mb:
         m.bsa_set_option(h, m.BSA_OPT_FINE_CHUNK_BYTES, args.fine_chunk_mb << 20)
     m.bsa_set_option(h, m.BSA_OPT_STATIC_ITEM_TILES, args.static_item_tiles)
-    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB cache flush
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")  # 1 GiB cache flush
 
     r = Runner(m, lib, w, args.which, args)
     res = measure(r, args, scratch, args.steps, args.warmup)
@@ -595,8 +596,8 @@ def main():
         "data": ("synthetic: seeded N(0,1) q/k/v plus per-block key offsets N(0,0.5^2), rounded to bf16 "
                  "(no dataset)") if w.key_offsets else "synthetic: seeded N(0,1) (no dataset)",
         "config": cfg,
-        "timing": {"value_from": "median of the cold steps (each queued behind a 1 GiB scratch read; "
-                                 "HIP events)",
+        "timing": {"value_from": "median of the cold steps (each queued behind a 1 GiB scratch write and "
+                                 "a read of it; HIP events)",
                    "ms_cold_median": res["ms_cold_median"], "ms_cold_min": res["ms_cold_min"],
                    "ms_cold_mean": res["ms_cold_mean"], "ms_warm": res["ms_warm"],
                    "ms_cold_synced_median": res["ms_cold_synced_median"],
