@@ -192,11 +192,11 @@ struct Bf16PlaneTiles {
   static constexpr int DIM = D;
   static constexpr int TB = TB_;                        // blocks per R tile
   static constexpr int PITCH = kRPitch<D>;
-  // The hi-only tile type (NTS = 1) also stages its blocks' hi-term norms
-  // after the plane.
+  // The hi-only tile type (NTS = 1) also reserves, after the plane, one
+  // float per wave for set_norms' reduction.
   static constexpr bool kNorms = NTS == 1;
   static constexpr int NORM_OFF = NTS * TB * PITCH * 2;
-  static constexpr int LDS_BYTES = NORM_OFF + (kNorms ? TB * 4 : 0);  // NTS: terms staged at most
+  static constexpr int LDS_BYTES = NORM_OFF + (kNorms ? NTH / 16 : 0);  // NTS: terms staged at most
   static constexpr int CPR = D / 8;             // 16-byte chunks per block row
   static constexpr int PER = TB * CPR / NTH;    // chunks per thread and term
   static_assert(PER >= 1 && (TB * CPR) % NTH == 0, "whole chunks per thread");
@@ -205,12 +205,11 @@ struct Bf16PlaneTiles {
   bf16x8 qb[QG][D / 32];
   uint4 pf[kTerms][PER];
   uint4 pf1[PFD > 1 ? PFD - 1 : 1][PER];  // further hi-only tiles in flight
-  float pfn[4];                           // the next tile's norms (threads tid < TB / 4)
-  const float* hn = nullptr;              // this head's hi-term norms [nb]
-  int nbk = 0;
-  // c |q|_2 for each of this lane's queries, c = 2^-8 + 2^-13: with |hi|_2
-  // of a block it bounds |exact score - hi-only score| (see norms4).
+  // c |q|_2 for each of this lane's queries, c = 2^-8 + 2^-13, and the
+  // largest |hi|_2 of the head's blocks: qn * hmax bounds |exact score -
+  // hi-only score| for every block (see set_norms).
   float qn[QG];
+  float hmax = 0.f;
 
   // Query group gq of this lane: row qrow0 + 16 gq.
   __device__ __forceinline__ void load_q(const QT* __restrict__ q, int64_t qrow0, int g) {
@@ -228,9 +227,29 @@ struct Bf16PlaneTiles {
       qn[gq] = __builtin_sqrtf(sum_over_groups(ss)) * ((1.0f + 0x1.0p-16f) * (0x1.0p-8f + 0x1.0p-13f));
     }
   }
-  __device__ __forceinline__ void set_norms(const float* __restrict__ all, int64_t bh, int nb) {
-    hn = all + bh * nb;
-    nbk = nb;
+  // hmax = the largest hi-term norm |hi_beta|_2 of head bh's nb blocks
+  // (each rounded up by block_pool), by the whole workgroup (NTH threads,
+  // every one calling), through NTH / 64 floats of LDS at NORM_OFF.  For a
+  // block, |exact score - hi-only score| <= sum_d |q_d| |r_d - hi_d| + the
+  // fp32 rounding of both sums <= (2^-8 + 2^-13) |q|_2 |hi|_2 (hi is r
+  // rounded to 8 significant bits, |r - hi| <= 2^-8 |hi|; Cauchy-Schwarz;
+  // 2^-13 covers the roundings, and both norms are rounded up).  So the
+  // largest hi-only score of a set of blocks, less qn * hmax, bounds from
+  // below the largest exact score of the set: the block with the largest
+  // hi-only score has an exact score at least that high.
+  __device__ __forceinline__ void set_norms(const float* __restrict__ all, int64_t bh, int nb, unsigned char* lds) {
+    const float* hn = all + bh * nb;
+    float m = 0.f;
+    for (int i = threadIdx.x; i < nb; i += NTH) m = fmaxf(m, hn[i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    float* red = reinterpret_cast<float*>(lds + NORM_OFF);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = red[0];
+#pragma unroll
+    for (int w = 1; w < NTH / 64; ++w) m = fmaxf(m, red[w]);
+    hmax = m;
   }
   __device__ __forceinline__ static const Src* head_base(const Src* r, int64_t bh, int nb) {
     return r + bh * kTerms * nb * D;
@@ -240,12 +259,6 @@ struct Bf16PlaneTiles {
   // the oldest and moves the others up.
   template <int NT>
   __device__ __forceinline__ void fetch(const Src* __restrict__ rbase, int nb, int bt, int tid) {
-    if constexpr (NT == 1 && kNorms) {
-      if (tid < TB / 4) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pfn[i] = hn[min(bt * TB + 4 * tid + i, nbk - 1)];
-      }
-    }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int c = tid + NTH * u, r = c / CPR, col = (c % CPR) * 8;
@@ -276,10 +289,6 @@ struct Bf16PlaneTiles {
   template <int NT>
   __device__ __forceinline__ void put(unsigned char* lds, int tid) {
     __bf16* rs = reinterpret_cast<__bf16*>(lds);
-    if constexpr (NT == 1 && kNorms) {
-      if (tid < TB / 4)
-        *reinterpret_cast<f32x4*>(lds + NORM_OFF + 16 * tid) = f32x4{pfn[0], pfn[1], pfn[2], pfn[3]};
-    }
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int c = tid + NTH * u, r = c / CPR, col = (c % CPR) * 8;
@@ -333,15 +342,6 @@ struct Bf16PlaneTiles {
         for (int gq = 0; gq < QG; ++gq) acc[gq] = mfma_16x16x32_bf16(a, qb[gq][ks], acc[gq]);
       }
     }
-  }
-  // The staged hi-only tile's norms |hi_beta|_2 of this lane's 4 blocks of
-  // MFMA tile mt.  For a block, |exact score - hi-only score| <= sum_d |q_d|
-  // |r_d - hi_d| + the fp32 rounding of both sums <= (2^-8 + 2^-13) |q|_2
-  // |hi|_2 (hi is r rounded to 8 significant bits, |r - hi| <= 2^-8 |hi|;
-  // Cauchy-Schwarz; 2^-13 covers the roundings, and both norms are rounded
-  // up), so score_hi - qn * norm is a lower bound of the exact score.
-  __device__ __forceinline__ f32x4 norms4(const unsigned char* lds, int mt, int g) const {
-    return *reinterpret_cast<const f32x4*>(lds + NORM_OFF + 4 * (mt * 16 + 4 * g));
   }
 };
 
@@ -447,8 +447,8 @@ struct F32Tiles {
   }
   // Pass 1 computes the same scores as pass 2 here: no error to bound.
   float qn[QG] = {};
-  __device__ __forceinline__ void set_norms(const float*, int64_t, int) {}
-  __device__ __forceinline__ f32x4 norms4(const unsigned char*, int, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+  float hmax = 0.f;
+  __device__ __forceinline__ void set_norms(const float*, int64_t, int, unsigned char*) {}
 };
 
 // Where a workgroup's 64 query rows sit, and which blocks they may select;
@@ -928,8 +928,9 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
 #pragma unroll
     for (int u = 0; u < NS; ++u) a[gq][u] = -INFINITY;
   // Pass 1 may run on approximate scores (bf16: the hi term alone): each
-  // enters as a lower bound of its exact score, the hi-only score less the
-  // block's error bound (norms4), so tau stays a bound for the exact scores.
+  // group's maximum enters less the error bound of the head's blocks
+  // (set_norms), a lower bound of the group's largest exact score, so tau
+  // stays a bound for the exact scores.
   float tau[QG];
   // The V rows of the workgroup's queries (warm, when given), read and
   // discarded so the attention kernel finds V in the Infinity Cache.  Issued
@@ -948,7 +949,7 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
   }
   {
     TL1 sc1;
-    sc1.set_norms(hinorm, ti.bh, ti.nb);
+    sc1.set_norms(hinorm, ti.bh, ti.nb, rs);
     sc1.load_q(q, ti.qrow0, ti.g);
     if (warm) {
       uint32_t seen = 0;
@@ -957,19 +958,22 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
       asm volatile("" ::"v"(seen));
     }
     auto group_max = [&](bool checked, int h, int mt, int b0, const f32x4 (&acc)[QG]) {
-      const f32x4 nrm = sc1.norms4(rs, mt, ti.g);
 #pragma unroll
       for (int gq = 0; gq < QG; ++gq)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float lb = __builtin_fmaf(-sc1.qn[gq], nrm[j], acc[gq][j]);
-          const float x = checked ? ti.cand(gq, lb, b0 + 4 * ti.g + j) : lb;
+          const float x = checked ? ti.cand(gq, acc[gq][j], b0 + 4 * ti.g + j) : acc[gq][j];
           a[gq][4 * (MT * h + mt) + j] = fmaxf(a[gq][4 * (MT * h + mt) + j], x);
         }
     };
     walk<NH, 1, QG, NTH>(sc1, rs, rbase, ti1,
                          [&](int h, int mt, int b0, const f32x4 (&acc)[QG]) { group_max(false, h, mt, b0, acc); },
                          [&](int h, int mt, int b0, const f32x4 (&acc)[QG]) { group_max(true, h, mt, b0, acc); });
+    // the groups' maxima, less the bound (infinite maxima stay infinite)
+#pragma unroll
+    for (int gq = 0; gq < QG; ++gq)
+#pragma unroll
+      for (int u = 0; u < NS; ++u) a[gq][u] = __builtin_fmaf(-sc1.qn[gq], sc1.hmax, a[gq][u]);
   }
   TL sc;
   sc.load_q(q, ti.qrow0, ti.g);
