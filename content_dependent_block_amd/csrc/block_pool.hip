@@ -17,8 +17,8 @@
 // hi + mid + lo (hi = bf16(r), mid = bf16(r - hi), lo = bf16(r - hi - mid)),
 // laid out as one plane per term and head, split[bh][term][beta][d], the form
 // the fused scoring kernel feeds to the bf16 MFMA (coarse_score.hip explains
-// the split), and the 2-norm of each block's hi term (rounded up), with which
-// that kernel bounds the error of its hi-only first pass per block.
+// the split), and the 2-norm of each block's hi term (rounded up), whose
+// largest value over a head bounds that kernel's hi-only first pass error.
 #include "bsa_device.hpp"
 #include "bsa_launch.hpp"
 

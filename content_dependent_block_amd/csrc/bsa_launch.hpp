@@ -23,8 +23,8 @@ hipError_t launch_block_pool(const void* k, float* repr, uint16_t* split, int64_
                              bsa_dtype dtype, hipStream_t stream, const int4* seqtab = nullptr);
 
 // The split buffer: the three bf16 planes [bh][3][n/64][d], then per block
-// the 2-norm of its hi term [bh][n/64] (fp32, rounded up), which the fused
-// selection's first pass uses to bound its error block by block.
+// the 2-norm of its hi term [bh][n/64] (fp32, rounded up), whose largest
+// value over a head the fused selection's first pass uses to bound its error.
 inline size_t split_buffer_bytes(int64_t bh, int nb, int d) {
   return static_cast<size_t>(bh) * nb * d * 3 * 2 + static_cast<size_t>(bh) * nb * 4;
 }

@@ -31,11 +31,11 @@
 //     The k_eff groups whose maxima are >= tau each hold a score >= tau, so at
 //     least k_eff scores are >= tau, and every score of the answer is >= tau.
 //     For bf16 inputs pass 1 multiplies only the hi term of the split, at a
-//     third of the MFMA and LDS work, and every score enters as a lower bound
-//     of its exact score: the hi-only score less (2^-8 + 2^-13) |q|_2 |hi|_2
-//     (hi is r rounded to 8 significant bits; Cauchy-Schwarz; the block's
-//     norm comes from block_pool), which keeps tau a bound for the exact
-//     scores.
+//     third of the MFMA and LDS work, and each group maximum enters less
+//     (2^-8 + 2^-13) |q|_2 max |hi|_2 over the head's blocks (hi is r rounded
+//     to 8 significant bits; Cauchy-Schwarz; the norms come from block_pool):
+//     a lower bound of the group's largest exact score, which keeps tau a
+//     bound for the exact scores.
 //   pass 2: the same scores again; those >= tau (typically k + a few) are
 //     appended to the lane's LDS slots in ascending block order.
 //   The lane reads its slots into registers and sorts a copy of their
@@ -899,8 +899,8 @@ __global__ __launch_bounds__(64 * NW, MINW) void coarse_select_kernel(const type
   constexpr int NH = NS / (4 * MT) > 0 ? NS / (4 * MT) : 1;  // R tiles per cycle of slots
   static_assert(NS % (4 * MT) == 0, "a cycle of slots covers whole R tiles");
   constexpr int ROWS = 16 * QG * NW;  // queries per workgroup
-  // The R tile buffer (the hi-only tiles with their norms, or the three-term
-  // tiles) also holds, at the end, the selection lists (a row of 33 per
+  // The R tile buffer (the hi-only tiles with set_norms' reduction slots, or
+  // the three-term tiles) also holds, at the end, the selection lists (a row of 33 per
   // query) and a slot per lane.
   constexpr int LIST_BYTES = (ROWS * 33 + NTH) * 4;
   constexpr int RS_T = TL::LDS_BYTES > TL1::LDS_BYTES ? TL::LDS_BYTES : TL1::LDS_BYTES;
